@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for causal GQA attention prefill.
+
+This module only synthesises tensors; it holds none of the attention method's
+arithmetic, and both the HIP path's tests/benchmark and the CPU oracle draw
+their inputs from it.
+
+The workloads stand in for Llama-3.2-3B query/key/value activations, which the
+method's description ("APA: sloppy attention, exact where it counts",
+rfriedmann.de, introduction and "Why this can work at all") measures on but
+which are not available here.  They reproduce the structure that section
+describes: an attention sink in the first keys, dominant tiles on the causal
+diagonal, and a thin long middle.
+
+* path mode: a smooth unit-vector path c(t) per (batch, kv-head), each channel
+  a sum of 8 random sinusoids with log-uniform periods in [64, 131072]
+  positions; K[k] = N(0, I)/sqrt(D) + a c(k), Q[h, r] = N(0, I)/sqrt(D)
+  + a c(r + Nkv - Nq) (queries sit at the KV tail), V ~ N(0, 1); softmax
+  scale 1.
+* gauss mode: Q, K, V ~ N(0, 1); softmax scale 1/sqrt(D).
+* sink: keys 0..3 get + delta * u / (scale |u|^2), u the mean rounded query of
+  the kv-head's group, so the mean logit lift over the group's rows is delta
+  nats (the "sink logit lift" parameterisation of the P-Cast abstract on
+  thelatestinai.com).
+"""
+from __future__ import annotations
+
+import hashlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+N_SINES = 8
+PERIOD_MIN, PERIOD_MAX = 64.0, 131072.0
+SINK_KEYS = 4
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest even); returns float32."""
+    x = np.ascontiguousarray(x, np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "fp16":
+        return np.asarray(x, np.float64).astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        return round_bf16(np.asarray(x, np.float64).astype(np.float32))
+    raise ValueError(dtype)
+
+
+@dataclass
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+    dtype: str = "fp16"
+    mode: str = "path"          # "path" or "gauss"
+    a: float = 2.0
+    delta: float = 6.0
+    eps: float = 0.005
+    seed: int = 1
+    causal: int = 1
+    eps_sweep: tuple = field(default_factory=tuple)
+    delta_sweep: tuple = field(default_factory=tuple)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 if self.mode == "path" else float(1.0 / np.sqrt(self.D))
+
+    def shape(self) -> dict:
+        return dict(B=self.B, Hq=self.Hq, Hkv=self.Hkv, Nq=self.Nq, Nkv=self.Nkv, D=self.D)
+
+
+# The five workloads: tiny check, the 3B-shaped short case, the headline long
+# prefill (2048 query rows at 122880 keys), full causal prefill at 32768 with a
+# sink-strength sweep, and large head dim in bf16.
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 2, 1, 256, 1024, 64, seed=1),
+    "short3b": Workload("short3b", 1, 24, 8, 2048, 8192, 128, seed=2),
+    "long3b": Workload("long3b", 1, 24, 8, 2048, 122880, 128, seed=3,
+                       eps_sweep=(0.002, 0.005, 0.02)),
+    "full32k": Workload("full32k", 1, 32, 8, 32768, 32768, 128, seed=4,
+                        delta_sweep=(0.0, 4.0, 8.0, 12.0)),
+    "bigd": Workload("bigd", 1, 32, 8, 1024, 4096, 512, dtype="bf16", mode="gauss", seed=5),
+}
+
+
+def _path(rng, n_pos: int, pos0: int, D: int, amp, per, ph) -> np.ndarray:
+    """Unit path vectors c(t) for t = pos0 .. pos0 + n_pos - 1, shape [n_pos, D]."""
+    out = np.empty((n_pos, D), np.float64)
+    step = 4096
+    w = 2.0 * np.pi / per  # [8, D]
+    for s in range(0, n_pos, step):
+        t = np.arange(pos0 + s, pos0 + min(n_pos, s + step), dtype=np.float64)
+        v = np.zeros((len(t), D))
+        for i in range(N_SINES):
+            v += amp[i] * np.sin(t[:, None] * w[i] + ph[i])
+        out[s:s + len(t)] = v / np.linalg.norm(v, axis=1, keepdims=True)
+    return out
+
+
+def make_inputs(w: Workload, delta: float | None = None):
+    """Returns (Q, K, V) as float32 arrays holding values of w.dtype.
+
+    Q [B, Hq, Nq, D], K and V [B, Hkv, Nkv, D].  Deterministic in w.seed.
+    Draw order per (b, kv-head): path parameters, K noise, V, then the Q noise
+    of each q-head of the group in ascending order.
+    """
+    delta = w.delta if delta is None else delta
+    rng = np.random.default_rng(w.seed)
+    B, Hq, Hkv, Nq, Nkv, D = w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D
+    G = Hq // Hkv
+    off = Nkv - Nq
+    Q = np.empty((B, Hq, Nq, D), np.float32)
+    K = np.empty((B, Hkv, Nkv, D), np.float32)
+    V = np.empty((B, Hkv, Nkv, D), np.float32)
+    for b in range(B):
+        for j in range(Hkv):
+            if w.mode == "path":
+                amp = rng.standard_normal((N_SINES, D))
+                per = np.exp(rng.uniform(np.log(PERIOD_MIN), np.log(PERIOD_MAX), (N_SINES, D)))
+                ph = rng.uniform(0.0, 2.0 * np.pi, (N_SINES, D))
+                kk = rng.standard_normal((Nkv, D)) / np.sqrt(D)
+                kk += w.a * _path(rng, Nkv, 0, D, amp, per, ph)
+                V[b, j] = round_to(rng.standard_normal((Nkv, D)), w.dtype)
+                cq = w.a * _path(rng, Nq, off, D, amp, per, ph)
+                for i in range(G):
+                    Q[b, j * G + i] = round_to(rng.standard_normal((Nq, D)) / np.sqrt(D) + cq,
+                                               w.dtype)
+            else:
+                kk = rng.standard_normal((Nkv, D))
+                V[b, j] = round_to(rng.standard_normal((Nkv, D)), w.dtype)
+                for i in range(G):
+                    Q[b, j * G + i] = round_to(rng.standard_normal((Nq, D)), w.dtype)
+            if delta != 0.0 and Nkv > 0 and Nq > 0:
+                u = Q[b, j * G:(j + 1) * G].astype(np.float64).reshape(-1, D).mean(axis=0)
+                nu = float(u @ u)
+                if nu > 0:
+                    kk[:SINK_KEYS] += delta * u / (w.scale * nu)
+            K[b, j] = round_to(kk, w.dtype)
+    return Q, K, V
+
+
+def small_workload(B=1, Hq=2, Hkv=1, Nq=64, Nkv=256, D=64, dtype="fp16", mode="path", a=2.0,
+                   delta=6.0, eps=0.005, seed=0, causal=1) -> Workload:
+    return Workload("custom", B, Hq, Hkv, Nq, Nkv, D, dtype=dtype, mode=mode, a=a, delta=delta,
+                    eps=eps, seed=seed, causal=causal)
+
+
+def digest(*arrays) -> str:
+    h = hashlib.sha256()
+    for a in arrays:
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()

@@ -1,0 +1,362 @@
+"""Python front end of the CPU oracle (``apa_oracle.c``) for adaptive-precision
+attention prefill.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module; the product path
+(``mixed_precision_long_amd``) never does, and shares no code with it.
+
+The arithmetic lives in ``apa_oracle.c`` (plain scalar C, FP64 where the
+method is exact, every FP32 rounding of the method simulated).  This module
+only builds that library with gcc, marshals numpy arrays, and strings the
+steps together in the order "APA: sloppy attention, exact where it counts"
+(rfriedmann.de) gives them: statistics and quantisation ("Mean-centred K",
+"Pass 1" format paragraph), pass 1 (numbered steps 1-5), pass 2 ("Pass 2:
+exact FP16 on the hot tiles") and the merge ("The merge that makes it exact").
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "apa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+MX, NV = 0, 1
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (no FMA contraction, no fast math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+             "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Params(C.Structure):
+    _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("Nq", C.c_int32),
+                ("Nkv", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32), ("scale", C.c_float),
+                ("fmt", C.c_int32), ("int_frame", C.c_int32), ("tau", C.c_float),
+                ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32)]
+
+
+_P = C.c_void_p
+
+
+class _Job(C.Structure):
+    _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P),
+                ("qc", _P), ("qs", _P), ("kc", _P), ("ks", _P), ("vc", _P), ("vs", _P),
+                ("kbar", _P), ("g_v", _P), ("jq", _P),
+                ("groups", _P), ("ngroups", C.c_int),
+                ("hot", _P), ("margin", _P), ("m1", _P), ("l1", _P), ("lam", _P), ("o1", _P),
+                ("shift", _P), ("m2", _P), ("l2", _P), ("o2", _P), ("cr", _P), ("O", _P),
+                ("lse", _P), ("do_pass2", C.c_int), ("next", C.c_int),
+                ("mu", C.c_int64 * 8)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        _lib = C.CDLL(build())
+        L = _lib
+        L.orc_e2m1_mag.argtypes = [C.c_double]
+        L.orc_e2m1_code.argtypes = [C.c_double]
+        L.orc_e2m1_value.argtypes = [C.c_int]
+        L.orc_e2m1_value.restype = C.c_double
+        L.orc_ue4m3_rn.argtypes = [C.c_double]
+        L.orc_ue4m3_rn.restype = C.c_double
+        L.orc_e8m0_exp.argtypes = [C.c_double]
+        L.orc_scale_value.argtypes = [C.c_uint8, C.c_int]
+        L.orc_scale_value.restype = C.c_double
+        L.orc_key_stats.argtypes = [_P, C.c_int, C.c_int, C.c_int, _P, _P]
+        L.orc_absmax.argtypes = [_P, C.c_size_t]
+        L.orc_absmax.restype = C.c_float
+        L.orc_head_scale.argtypes = [C.c_float, C.c_int, _P, _P]
+        L.orc_q_scale.argtypes = [C.c_float, C.c_float, C.c_float, C.c_int, _P, _P]
+        L.orc_quant_rows.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, C.c_int, _P, _P]
+        L.orc_quant_vt.argtypes = [_P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P]
+        L.orc_sl.argtypes = [_P]
+        L.orc_sl.restype = C.c_float
+        L.orc_visit_order.argtypes = [_P, C.c_int, _P]
+        L.orc_run_groups.argtypes = [_P, C.c_int]
+        L.orc_exact_rows.argtypes = [_P, _P, _P, _P, _P, C.c_int, _P, _P, C.c_int]
+        L.orc_merge_row.argtypes = [C.c_int, C.c_double, C.c_double, _P, C.c_double, C.c_double,
+                                    _P, C.c_double, _P, _P]
+        L.orc_job_size.restype = C.c_size_t
+        L.orc_params_size.restype = C.c_size_t
+        assert L.orc_params_size() == C.sizeof(_Params)
+        assert L.orc_job_size() <= C.sizeof(_Job), (L.orc_job_size(), C.sizeof(_Job))
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+@dataclass
+class Params:
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nkv: int
+    D: int
+    causal: int = 1
+    scale: float = 0.0      # <= 0: 1/sqrt(D)
+    fmt: int = MX
+    int_frame: int = 1
+    tau: float = 4.0
+    hoff: float = 32.0
+    eps: float = 0.005
+    tile: int = 64
+    rg: int = 16
+
+    def c(self) -> _Params:
+        assert self.rg == 16, "the oracle keeps 16-row verdict groups"
+        assert self.Hq % self.Hkv == 0
+        bs = 16 if self.fmt == NV else 32
+        assert self.D % bs == 0
+        return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
+                       self.scale, self.fmt, self.int_frame, self.tau, self.hoff, self.eps,
+                       self.tile, self.rg)
+
+    @property
+    def n_tiles(self) -> int:
+        return (self.Nkv + self.tile - 1) // self.tile
+
+    @property
+    def n_groups(self) -> int:
+        return (self.Nq + self.rg - 1) // self.rg
+
+    @property
+    def block(self) -> int:
+        return 16 if self.fmt == NV else 32
+
+
+# --------------------------------------------------------------------------
+# format helpers (thin wrappers, used by the pins)
+# --------------------------------------------------------------------------
+
+def e2m1_mag(a: float) -> int:
+    return lib().orc_e2m1_mag(float(a))
+
+
+def e2m1_code(x: float) -> int:
+    return lib().orc_e2m1_code(float(x))
+
+
+def e2m1_value(code: int) -> float:
+    return lib().orc_e2m1_value(int(code))
+
+
+def ue4m3_rn(a: float) -> float:
+    return lib().orc_ue4m3_rn(float(a))
+
+
+def e8m0_exp(a: float) -> int:
+    return lib().orc_e8m0_exp(float(a))
+
+
+def scale_value(b: int, fmt: int = MX) -> float:
+    return lib().orc_scale_value(int(b), fmt)
+
+
+def sl(p: Params) -> float:
+    cp = p.c()
+    return lib().orc_sl(C.byref(cp))
+
+
+def visit_order(p: Params, g: int) -> list:
+    cp = p.c()
+    buf = np.zeros(p.n_tiles + 1, np.int32)
+    n = lib().orc_visit_order(C.byref(cp), int(g), _ptr(buf))
+    return buf[:n].tolist()
+
+
+def quant_rows(X: np.ndarray, inv: float, fmt: int = MX, centre=None):
+    """Quantise rows of X [n, D] along D.  Returns (codes [n, D/2], scales [n, D/Bs])."""
+    X = np.ascontiguousarray(X, np.float32)
+    n, D = X.shape
+    bs = 16 if fmt == NV else 32
+    codes = np.zeros((n, D // 2), np.uint8)
+    scales = np.zeros((n, D // bs), np.uint8)
+    c = None if centre is None else np.ascontiguousarray(centre, np.float32)
+    lib().orc_quant_rows(_ptr(X), n, D, _ptr(c), float(inv), fmt, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+# --------------------------------------------------------------------------
+# a1 + a2: statistics, per-head scales, quantisation
+# --------------------------------------------------------------------------
+
+def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
+    """Stats and block-scaled FP4 quantisation of Q, K (centred), V (along keys).
+
+    Q [B,Hq,Nq,D], K/V [B,Hkv,Nkv,D] float32 arrays holding the fp16/bf16
+    input values.  Returns codes, scale bytes and per-head scales.
+    """
+    L = lib()
+    cp = p.c()
+    Q = np.ascontiguousarray(Q, np.float32)
+    K = np.ascontiguousarray(K, np.float32)
+    V = np.ascontiguousarray(V, np.float32)
+    B, Hq, Hkv, Nq, Nkv, D = p.B, p.Hq, p.Hkv, p.Nq, p.Nkv, p.D
+    G = Hq // Hkv
+    bs = p.block
+    NkvP = p.n_tiles * p.tile
+    s_l = L.orc_sl(C.byref(cp))
+    out = dict(
+        kbar=np.zeros((B, Hkv, D), np.float32), amax_k=np.zeros((B, Hkv), np.float32),
+        g_k=np.zeros((B, Hkv), np.float32), inv_k=np.zeros((B, Hkv), np.float32),
+        amax_v=np.zeros((B, Hkv), np.float32), g_v=np.zeros((B, Hkv), np.float32),
+        inv_v=np.zeros((B, Hkv), np.float32), amax_q=np.zeros((B, Hq), np.float32),
+        inv_q=np.zeros((B, Hq), np.float32), jq=np.zeros((B, Hq), np.int32),
+        qc=np.zeros((B, Hq, Nq, D // 2), np.uint8), qs=np.zeros((B, Hq, Nq, D // bs), np.uint8),
+        kc=np.zeros((B, Hkv, Nkv, D // 2), np.uint8),
+        ks=np.zeros((B, Hkv, Nkv, D // bs), np.uint8),
+        vc=np.zeros((B, Hkv, D, NkvP // 2), np.uint8),
+        vs=np.zeros((B, Hkv, D, NkvP // bs), np.uint8), sl=np.float32(s_l))
+    f = np.zeros(2, np.float32)
+    ji = np.zeros(1, np.int32)
+    for b in range(B):
+        for hk in range(Hkv):
+            Kh = np.ascontiguousarray(K[b, hk])
+            Vh = np.ascontiguousarray(V[b, hk])
+            kb = np.zeros(D, np.float32)
+            am = np.zeros(1, np.float32)
+            L.orc_key_stats(_ptr(Kh), Nkv, D, p.tile, _ptr(kb), _ptr(am))
+            out["kbar"][b, hk] = kb
+            out["amax_k"][b, hk] = am[0]
+            L.orc_head_scale(C.c_float(am[0]), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
+            out["g_k"][b, hk], out["inv_k"][b, hk] = f[0], f[1]
+            av = L.orc_absmax(_ptr(Vh), Vh.size)
+            out["amax_v"][b, hk] = av
+            L.orc_head_scale(C.c_float(av), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
+            out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]
+            kc = np.zeros((Nkv, D // 2), np.uint8)
+            ks = np.zeros((Nkv, D // bs), np.uint8)
+            L.orc_quant_rows(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]), p.fmt,
+                             _ptr(kc), _ptr(ks))
+            out["kc"][b, hk], out["ks"][b, hk] = kc, ks
+            vc = np.zeros((D, NkvP // 2), np.uint8)
+            vs = np.zeros((D, NkvP // bs), np.uint8)
+            L.orc_quant_vt(_ptr(Vh), Nkv, NkvP, D, C.c_float(out["inv_v"][b, hk]), p.fmt,
+                           _ptr(vc), _ptr(vs))
+            out["vc"][b, hk], out["vs"][b, hk] = vc, vs
+        for h in range(Hq):
+            Qh = np.ascontiguousarray(Q[b, h])
+            aq = L.orc_absmax(_ptr(Qh), Qh.size)
+            out["amax_q"][b, h] = aq
+            L.orc_q_scale(C.c_float(aq), C.c_float(s_l), C.c_float(out["g_k"][b, h // G]), p.fmt,
+                          _ptr(f[0:1]), _ptr(ji))
+            out["inv_q"][b, h], out["jq"][b, h] = f[0], ji[0]
+            qc = np.zeros((Nq, D // 2), np.uint8)
+            qs = np.zeros((Nq, D // bs), np.uint8)
+            L.orc_quant_rows(_ptr(Qh), Nq, D, None, C.c_float(f[0]), p.fmt, _ptr(qc), _ptr(qs))
+            out["qc"][b, h], out["qs"][b, h] = qc, qs
+    return out
+
+
+def all_groups(p: Params) -> np.ndarray:
+    g = [(b, h, i) for b in range(p.B) for h in range(p.Hq) for i in range(p.n_groups)]
+    return np.array(g, np.int32).reshape(-1, 3)
+
+
+# --------------------------------------------------------------------------
+# a3..a10: pass 1, pass 2, merge for a list of row groups
+# --------------------------------------------------------------------------
+
+def run(p: Params, Q, K, V, prep: dict | None = None, groups=None, nthreads: int | None = None,
+        pass2: bool = True) -> dict:
+    """APA on the CPU.  groups: array [n, 3] of (b, q-head, row group); all if None.
+
+    Returns the pass-1 state (m1 frame, l1, o1 = o * g_v, lambda), the hot
+    cells (one byte per (b, h, group, tile)) with their margins, and, if
+    pass2, the exact pass-2 state, the frame constants c_r and the merged
+    output O (FP64) with LSE (natural log).  Only rows of listed groups are
+    written; others stay NaN.
+    """
+    L = lib()
+    cp = p.c()
+    Q = np.ascontiguousarray(Q, np.float32)
+    K = np.ascontiguousarray(K, np.float32)
+    V = np.ascontiguousarray(V, np.float32)
+    if prep is None:
+        prep = quantize(p, Q, K, V)
+    if groups is None:
+        groups = all_groups(p)
+    groups = np.ascontiguousarray(groups, np.int32).reshape(-1, 3)
+    B, Hq, Nq, D = p.B, p.Hq, p.Nq, p.D
+    NG, NT = p.n_groups, p.n_tiles
+    nan = np.nan
+    res = dict(
+        hot=np.zeros((B, Hq, NG, NT), np.uint8), margin=np.full((B, Hq, NG, NT), nan),
+        m1=np.full((B, Hq, Nq), nan), l1=np.full((B, Hq, Nq), nan, np.float32),
+        lam=np.full((B, Hq, Nq), nan, np.float32), o1=np.full((B, Hq, Nq, D), nan, np.float32),
+        shift=np.full((B, Hq, Nq), nan), m2=np.full((B, Hq, Nq), nan),
+        l2=np.full((B, Hq, Nq), nan), o2=np.full((B, Hq, Nq, D), nan),
+        cr=np.full((B, Hq, Nq), nan), O=np.full((B, Hq, Nq, D), nan),
+        lse=np.full((B, Hq, Nq), nan))
+    keep = [Q, K, V, prep, groups]
+    job = _Job()
+    job.p = C.cast(C.pointer(cp), C.c_void_p)
+    job.Q, job.K, job.V = _ptr(Q), _ptr(K), _ptr(V)
+    for k in ("qc", "qs", "kc", "ks", "vc", "vs", "kbar", "g_v"):
+        setattr(job, k, _ptr(prep[k]))
+    job.jq = _ptr(prep["jq"])
+    job.groups, job.ngroups = _ptr(groups), len(groups)
+    for k in ("hot", "margin", "m1", "l1", "lam", "o1", "shift", "m2", "l2", "o2", "cr", "O",
+              "lse"):
+        setattr(job, k, _ptr(res[k]))
+    job.do_pass2 = 1 if pass2 else 0
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    L.orc_run_groups(C.byref(job), int(nthreads))
+    del keep
+    res["prep"] = prep
+    res["groups"] = groups
+    res["threads"] = int(nthreads)
+    return res
+
+
+def exact(p: Params, Q, K, V, rows=None, nthreads: int | None = None):
+    """Reference attention in FP64 for rows [n, 3] of (b, q-head, r); all if None.
+
+    Returns (O [n, D] float64, lse [n] float64)."""
+    L = lib()
+    cp = p.c()
+    Q = np.ascontiguousarray(Q, np.float32)
+    K = np.ascontiguousarray(K, np.float32)
+    V = np.ascontiguousarray(V, np.float32)
+    if rows is None:
+        rows = np.array([(b, h, r) for b in range(p.B) for h in range(p.Hq) for r in range(p.Nq)],
+                        np.int32).reshape(-1, 3)
+    rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 3)
+    O = np.zeros((len(rows), p.D))
+    lse = np.zeros(len(rows))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    L.orc_exact_rows(C.byref(cp), _ptr(Q), _ptr(K), _ptr(V), _ptr(rows), len(rows), _ptr(O),
+                     _ptr(lse), int(nthreads))
+    return O, lse
+
+
+def merge_row(D, m1, l1, o1, m2, l2, o2, c):
+    """Merge two states of one row (FP64).  Returns (O [D], lse)."""
+    o1 = np.ascontiguousarray(o1, np.float64)
+    o2 = np.ascontiguousarray(o2, np.float64)
+    O = np.zeros(D)
+    lse = np.zeros(1)
+    lib().orc_merge_row(int(D), float(m1), float(l1), _ptr(o1), float(m2), float(l2), _ptr(o2),
+                        float(c), _ptr(O), _ptr(lse))
+    return O, float(lse[0])

@@ -1,0 +1,195 @@
+"""An independent, frame-free numpy brute force of APA's pass 1 for tiny inputs.
+
+It re-derives everything from the raw inputs with different arithmetic than
+the oracle: quantisation by nearest-value search (not threshold counting),
+scores as an FP64 matrix product of dequantised operands, and pass 1 without
+any logit frame.  In MX mode with an integer frame the per-group exponent
+E = ceil(c_g - m - log2 6) shifts by exactly the frame, so every quantity of
+pass 1 (P, the tile row sums, lambda, the cold l and o) is the frame-free
+value times an exact power of two -- the tau/H frame logic only relabels it.
+Agreement with the oracle, bit for bit, therefore pins the lazy maximum, the
+decoupled cold frame and every rescale, as well as the visit order and the
+hot test ("APA: sloppy attention, exact where it counts", "Pass 1" steps 1-5,
+"Tile order", "The bug: a sink that drowned the tail").
+
+Valid while no block exponent reaches the E8M0 floor (2^-127) and nothing
+underflows FP32; the tiny workloads used by the tests stay far from both.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MAGS = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+LOG2E32 = np.float32(np.log2(np.e))
+
+
+def f32(x):
+    return np.asarray(x, np.float64).astype(np.float32)
+
+
+def nearest_mag_code(a: np.ndarray) -> np.ndarray:
+    """3-bit E2M1 magnitude code of |a| by nearest-value search; ties go to the
+    even code; values above 6 saturate."""
+    a = np.minimum(np.abs(np.asarray(a, np.float64)), 6.0)
+    dist = np.abs(a[..., None] - MAGS)
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    # among tied candidates prefer the even code index
+    idx = np.arange(8)
+    score = np.where(cand, (idx % 2) * 16 + idx, 1000)
+    return score.argmin(axis=-1)
+
+
+def block_exp(a: np.ndarray) -> np.ndarray:
+    """Smallest integer e with a <= 6 * 2^e (a > 0), clamped to [-127, 127]."""
+    a = np.asarray(a, np.float64)
+    e = np.full(a.shape, -127, np.int64)
+    pos = a > 0
+    with np.errstate(divide="ignore"):
+        guess = np.floor(np.log2(np.where(pos, a, 1.0) / 6.0)).astype(np.int64) - 1
+    for _ in range(4):  # walk up to the smallest passing exponent
+        ok = 6.0 * np.ldexp(1.0, guess) >= a
+        guess = np.where(ok, guess, guess + 1)
+    e = np.where(pos, guess, -127)
+    return np.clip(e, -127, 127)
+
+
+def quantise_blocks(x: np.ndarray, bs: int = 32):
+    """x [..., n] normalised values -> dequantised values (same shape)."""
+    sh = x.shape
+    xb = np.asarray(x, np.float64).reshape(sh[:-1] + (sh[-1] // bs, bs))
+    e = block_exp(np.abs(xb).max(axis=-1))
+    sc = np.ldexp(1.0, e)[..., None]
+    code = nearest_mag_code(xb / sc)
+    val = np.sign(xb) * MAGS[code] * sc
+    return val.reshape(sh)
+
+
+def prepare(Q, K, V, scale: float):
+    """Per-head scales and dequantised operands (without the per-head factors
+    that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry."""
+    Hq, Nq, D = Q.shape
+    Hkv = K.shape[0]
+    G = Hq // Hkv
+    sl = np.float32(np.float32(scale) * LOG2E32)
+    out = []
+    for hk in range(Hkv):
+        Kh = K[hk].astype(np.float32)
+        kbar = f32(Kh.astype(np.float64).sum(axis=0) / Kh.shape[0])
+        kc = (Kh - kbar).astype(np.float32)              # fl32 subtraction
+        amax_k = np.abs(kc).max() if kc.size else np.float32(0)
+        g_k = f32(amax_k / 6.0) if amax_k > 0 else np.float32(1)
+        inv_k = f32(6.0 / amax_k) if amax_k > 0 else np.float32(1)
+        kn = np.clip((kc * inv_k).astype(np.float32), -6, 6)
+        kd = quantise_blocks(kn)
+        Vh = V[hk].astype(np.float32)
+        amax_v = np.abs(Vh).max()
+        g_v = f32(amax_v / 6.0) if amax_v > 0 else np.float32(1)
+        inv_v = f32(6.0 / amax_v) if amax_v > 0 else np.float32(1)
+        vn = np.clip((Vh * inv_v).astype(np.float32), -6, 6)
+        Nkv = Vh.shape[0]
+        NkvP = -(-Nkv // 64) * 64
+        vpad = np.zeros((NkvP, D), np.float32)
+        vpad[:Nkv] = vn
+        vd = quantise_blocks(vpad.T).T[:Nkv]              # blocks of 32 keys per channel
+        w = np.float32(sl * g_k)
+        heads = []
+        for i in range(G):
+            Qh = Q[hk * G + i].astype(np.float32)
+            amax_q = np.abs(Qh).max()
+            j = 0
+            if amax_q > 0:
+                prod = float(amax_q) * float(w)
+                j = int(np.ceil(np.log2(prod / 6.0))) - 1
+                while 6.0 * 2.0 ** j < prod:
+                    j += 1
+            inv_q = np.float32(np.ldexp(np.float64(w), -j))
+            qn = np.clip((Qh * inv_q).astype(np.float32), -6, 6)
+            heads.append(dict(qd=quantise_blocks(qn), alpha=2.0 ** j, Qh=Qh))
+        out.append(dict(kd=kd, vd=vd, g_v=g_v, heads=heads, kbar=kbar, sl=sl))
+    return out
+
+
+def visit_order(last_row: int, off: int, Nkv: int, causal: bool, tile: int = 64):
+    nt = -(-Nkv // tile)
+    d = min(Nkv - 1, last_row + off) // tile if causal else nt - 1
+    return [0] + list(range(d, 0, -1))
+
+
+def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray, off: int,
+                Nkv: int, causal: bool):
+    """Frame-free pass 1 of one row group.
+
+    scores: [R, Nkv] FP4 scores in log2 units (fl32), vd: [Nkv, D] dequantised
+    V'.  Returns (hot [NT] bool, l [R], o [R, D], lam [R]) in frame-free units.
+    """
+    R = scores.shape[0]
+    D = vd.shape[1]
+    nt = -(-Nkv // 64)
+    hot = np.zeros(nt, bool)
+    lam = np.zeros(R, np.float32)
+    lsum = np.zeros(R, np.float32)
+    o = np.zeros((R, D), np.float32)
+    keys = np.arange(Nkv)
+    vis = (keys[None, :] <= rows[:, None] + off) if causal else np.ones((R, Nkv), bool)
+    s = np.where(vis, scores.astype(np.float64), -np.inf)
+    eps32 = np.float32(eps)
+    for t in visit_order(int(rows[-1]), off, Nkv, causal):
+        k0, k1 = 64 * t, min(Nkv, 64 * t + 64)
+        st = np.full((R, 64), -np.inf)
+        st[:, :k1 - k0] = s[:, k0:k1]
+        ph = np.zeros((R, 64))
+        for q0 in (0, 32):
+            g = st[:, q0:q0 + 32]
+            cg = g.max(axis=1)
+            E = np.where(np.isfinite(cg), np.ceil(cg - np.log2(6.0)), 0).astype(np.int64)
+            # exact adjustment of the ceiling
+            E = np.where(np.exp2(cg - E) > 6.0, E + 1, E)
+            E = np.where(np.exp2(cg - (E - 1)) <= 6.0, E - 1, E)
+            with np.errstate(invalid="ignore", over="ignore"):
+                code = nearest_mag_code(np.exp2(g - E[:, None]))
+            ph[:, q0:q0 + 32] = np.where(np.isfinite(g), MAGS[code] * np.ldexp(1.0, E)[:, None], 0)
+        ell = f32(ph.sum(axis=1))
+        lam = (lam + ell).astype(np.float32)
+        thr = (eps32 * lam).astype(np.float32)
+        h = (eps == 0.0) or bool(np.any(ell > thr))
+        hot[t] = h
+        if not h:
+            vt = np.zeros((64, D))
+            vt[:k1 - k0] = vd[k0:k1]
+            pv = f32(ph @ vt)
+            o = (o + pv).astype(np.float32)
+            lsum = (lsum + ell).astype(np.float32)
+    return hot, lsum, o, lam
+
+
+def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True):
+    """Frame-free pass 1 for every row group of a batch-1 problem.
+
+    Returns dict with hot [Hq, NG, NT], l [Hq, Nq], o [Hq, Nq, D] (o already
+    times g_v), lam [Hq, Nq], all frame-free."""
+    Q, K, V = Q[0], K[0], V[0]
+    Hq, Nq, D = Q.shape
+    Nkv = K.shape[1]
+    G = Hq // K.shape[0]
+    off = Nkv - Nq
+    nt = -(-Nkv // 64)
+    ng = -(-Nq // 16)
+    ops = prepare(Q, K, V, scale)
+    hot = np.zeros((Hq, ng, nt), bool)
+    lo = np.zeros((Hq, Nq), np.float32)
+    oo = np.zeros((Hq, Nq, D), np.float32)
+    la = np.zeros((Hq, Nq), np.float32)
+    for h in range(Hq):
+        kv = ops[h // G]
+        hd = kv["heads"][h % G]
+        dot = f32(hd["qd"].astype(np.float64) @ kv["kd"].astype(np.float64).T)
+        scores = f32(hd["alpha"] * dot.astype(np.float64))
+        for g in range(ng):
+            rows = np.arange(16 * g, min(Nq, 16 * g + 16))
+            hh, l, o, lam = pass1_group(scores[rows], kv["vd"], eps, rows, off, Nkv, causal)
+            hot[h, g] = hh
+            lo[h, rows] = l
+            oo[h, rows] = (o * kv["g_v"]).astype(np.float32)
+            la[h, rows] = lam
+    return dict(hot=hot, l=lo, o=oo, lam=la, ops=ops)

@@ -1,0 +1,182 @@
+"""Pins of the oracle's exact parts: the merge (closed form, split
+invariance), eps=0 reducing to exact attention, eps>=1 to the all-FP4 pass,
+exact attention vs a textbook softmax, GQA, tail alignment, key statistics and
+scores ('The merge that makes it exact'; FFPA docs note on GQA and causal
+tail alignment; 'Mean-centred K')."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from brute_apa import brute_apa, prepare
+from mixed_precision_long_amd.inputs import make_inputs, small_workload
+from oracle import oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def textbook(Q, K, V, scale, causal):
+    """softmax(scale Q K^T) V with numpy, FP64, K/V repeated per GQA group."""
+    B, Hq, Nq, D = Q.shape
+    G = Hq // K.shape[1]
+    Kr = np.repeat(K, G, axis=1).astype(np.float64)
+    Vr = np.repeat(V, G, axis=1).astype(np.float64)
+    S = scale * np.einsum("bhqd,bhkd->bhqk", Q.astype(np.float64), Kr)
+    Nkv = K.shape[2]
+    if causal:
+        r = np.arange(Nq)[:, None]
+        k = np.arange(Nkv)[None, :]
+        S = np.where(k <= r + Nkv - Nq, S, -np.inf)
+    M = S.max(-1, keepdims=True)
+    P = np.exp(S - M)
+    lse = (M[..., 0] + np.log(P.sum(-1)))
+    return (P / P.sum(-1, keepdims=True)) @ Vr, lse
+
+
+def test_merge_golden_examples():
+    cases = json.load(open(os.path.join(HERE, "golden", "merge_example.json")))["cases"]
+    for c in cases:
+        Om, lse = O.merge_row(len(c["o1"]), c["m1"], c["l1"], c["o1"], c["m2"], c["l2"], c["o2"],
+                              c["c"])
+        assert np.allclose(Om, c["O"], rtol=1e-15, atol=0)
+        want = -np.inf if c["lse"] == "-inf" else c["lse"]
+        assert lse == pytest.approx(want, rel=1e-15) if np.isfinite(want) else lse == want
+
+
+def test_merge_equals_softmax_over_union_for_random_splits():
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        n, D = rng.integers(2, 200), 8
+        s = rng.normal(0, 5, n)
+        v = rng.normal(0, 1, (n, D))
+        w = np.exp2(s - s.max())
+        want = (w[:, None] * v).sum(0) / w.sum()
+        want_lse = np.log(2) * (s.max() + np.log2(w.sum()))
+        # random disjoint split into parts, merged in random order
+        parts = rng.integers(0, rng.integers(2, 9), n)
+        state = (-np.inf, 0.0, np.zeros(D))
+        for pi in rng.permutation(np.unique(parts)):
+            idx = parts == pi
+            m2 = s[idx].max()
+            l2 = np.exp2(s[idx] - m2).sum()
+            o2 = (np.exp2(s[idx] - m2)[:, None] * v[idx]).sum(0)
+            Om, lse = O.merge_row(D, state[0], state[1], state[2], m2, l2, o2, 0.0)
+            # carry the merged state forward as a normalised partial
+            M = lse / np.log(2)
+            state = (M, 1.0, Om)
+        assert np.allclose(state[2], want, rtol=1e-12, atol=1e-12)
+        assert abs(state[0] * np.log(2) - want_lse) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_exact_reference_matches_textbook_softmax(causal):
+    w = small_workload(2, 4, 2, 50, 130, 32, seed=21)
+    Q, K, V = make_inputs(w)
+    p = O.Params(2, 4, 2, 50, 130, 32, causal=causal, scale=0.3)
+    Oe, lse = O.exact(p, Q, K, V)
+    Ot, lt = textbook(Q, K, V, float(np.float32(0.3)), causal)
+    assert np.allclose(Oe.reshape(Ot.shape), Ot, rtol=1e-12, atol=1e-12)
+    assert np.allclose(lse.reshape(lt.shape), lt, rtol=1e-12, atol=1e-12)
+
+
+def test_tail_alignment_reduces_to_standard_causal_and_single_row():
+    w = small_workload(1, 2, 1, 96, 96, 32, seed=22)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, 2, 1, 96, 96, 32, scale=0.5)
+    Oe, _ = O.exact(p, Q, K, V)
+    S = 0.5 * np.einsum("qd,kd->qk", Q[0, 0].astype(np.float64), K[0, 0].astype(np.float64))
+    S[np.triu_indices(96, 1)] = -np.inf
+    P = np.exp(S - S.max(1, keepdims=True))
+    assert np.allclose(Oe[:96], (P / P.sum(1, keepdims=True)) @ V[0, 0], atol=1e-12)
+    # a single query row at the tail sees every key
+    p1 = O.Params(1, 2, 1, 1, 96, 32, scale=0.5)
+    O1, _ = O.exact(p1, Q[:, :, -1:], K, V)
+    s = 0.5 * K[0, 0].astype(np.float64) @ Q[0, 0, -1].astype(np.float64)
+    pw = np.exp(s - s.max())
+    assert np.allclose(O1[0], pw @ V[0, 0] / pw.sum(), atol=1e-12)
+
+
+@pytest.mark.parametrize("shape", [(2, 1, 256, 1024, 64), (4, 2, 70, 333, 32), (2, 1, 16, 64, 64)])
+def test_eps_zero_is_exact_attention(shape):
+    Hq, Hkv, Nq, Nkv, D = shape
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=23)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale, eps=0.0)
+    r = O.run(p, Q, K, V)
+    visited = ~np.isnan(r["margin"])
+    assert r["hot"][visited].all()
+    assert np.all(r["l1"] == 0)          # the cold state stays empty
+    # the method scores in log2 units with the FP32 constant sl = fl32(scale
+    # log2 e); the matching natural-log scale is sl / log2 e
+    Ot, lt = textbook(Q, K, V, O.sl(p) / np.log2(np.e), True)
+    assert np.allclose(r["O"], Ot, rtol=1e-10, atol=1e-10)
+    assert np.allclose(r["lse"], lt, rtol=1e-10, atol=1e-10)
+
+
+def test_eps_one_is_the_all_fp4_pass():
+    w = small_workload(1, 2, 1, 64, 1024, 64, seed=24)
+    Q, K, V = make_inputs(w)
+    for eps in (1.0, float("inf")):
+        p = O.Params(1, 2, 1, 64, 1024, 64, scale=w.scale, eps=eps)
+        r = O.run(p, Q, K, V)
+        assert not r["hot"].any()
+        assert np.all(r["l2"] == 0)
+        b = brute_apa(Q, K, V, eps, w.scale)
+        want = b["o"] / b["l"][..., None].astype(np.float64)
+        assert np.allclose(r["O"][0], want, rtol=1e-6, atol=1e-7)
+
+
+def test_key_mean_and_scores():
+    w = small_workload(1, 2, 1, 40, 333, 64, seed=25)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, 2, 1, 40, 333, 64, scale=w.scale)
+    prep = O.quantize(p, Q, K, V)
+    kb = K[0, 0].astype(np.float64).mean(axis=0).astype(np.float32)
+    assert np.array_equal(prep["kbar"][0, 0], kb)
+    am = np.abs((K[0, 0] - kb).astype(np.float32)).max()
+    assert prep["amax_k"][0, 0] == am
+    # the FP4 score of the oracle equals alpha * (dequantised Q).(dequantised K)
+    ops = prepare(Q[0], K[0], V[0], w.scale)[0]
+    b = brute_apa(Q, K, V, 0.02, w.scale)
+    r = O.run(O.Params(1, 2, 1, 40, 333, 64, scale=w.scale, eps=0.02), Q, K, V, prep, pass2=False)
+    for h in range(2):
+        hd = ops["heads"][h]
+        assert hd["alpha"] == 2.0 ** prep["jq"][0, h]
+    # dequantised operands agree with the oracle's codes and scale bytes
+    L = O.lib()
+    for kidx in (0, 5, 332):
+        for d in range(64):
+            byte = prep["kc"][0, 0, kidx, d // 2]
+            c = (byte >> 4) if d & 1 else (byte & 15)
+            val = O.e2m1_value(int(c)) * 2.0 ** (int(prep["ks"][0, 0, kidx, d // 32]) - 127)
+            assert val == ops["kd"][kidx, d]
+
+
+def test_gqa_equals_repeated_kv_heads():
+    w = small_workload(1, 4, 2, 64, 512, 64, seed=26)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, 4, 2, 64, 512, 64, scale=w.scale, eps=0.02)
+    r = O.run(p, Q, K, V)
+    Kr, Vr = np.repeat(K, 2, axis=1), np.repeat(V, 2, axis=1)
+    pr = O.Params(1, 4, 4, 64, 512, 64, scale=w.scale, eps=0.02)
+    rr = O.run(pr, Q, Kr, Vr)
+    assert np.array_equal(r["hot"], rr["hot"])
+    assert np.array_equal(r["O"], rr["O"])
+
+
+def test_centring_keys_keeps_exact_path_and_apa_nearly_invariant():
+    w = small_workload(1, 2, 1, 64, 1024, 64, seed=27)
+    Q, K, V = make_inputs(w)
+    shift = np.float32(0.75) * np.sign(np.random.default_rng(0).standard_normal(64)).astype(
+        np.float32)
+    K2 = (K + shift).astype(np.float16).astype(np.float32)
+    p = O.Params(1, 2, 1, 64, 1024, 64, scale=w.scale, eps=0.02)
+    Oe, _ = O.exact(p, Q, K, V)
+    Oe2, _ = O.exact(p, Q, K2, V)
+    # a per-channel key shift moves every score of a row by the same constant
+    # (up to fp16 rounding of the shifted keys)
+    assert np.abs(Oe - Oe2).max() < 5e-3
+    r1 = O.run(p, Q, K, V)
+    r2 = O.run(p, Q, K2, V)
+    assert np.abs(r1["O"] - r2["O"]).max() < 0.05
