@@ -1,0 +1,179 @@
+/*
+ * apa.h -- C ABI of the MI355X (gfx950) adaptive-precision attention prefill
+ * library (libapa.so).
+ *
+ * The method is APA as described in "APA: sloppy attention, exact where it
+ * counts" (rfriedmann.de/blog/apa-adaptive-precision-attention): pass 1 runs
+ * every key tile of a causal GQA prefill in block-scaled FP4 and marks a tile
+ * "hot" for a 16-row group when any row's tile mass exceeds eps of its running
+ * sum; pass 2 recomputes only the hot tiles in exact FP16; one log-sum-exp
+ * merge combines the two online-softmax states ("The merge that makes it
+ * exact").  Tensor layout and masking follow the FFPA documentation
+ * (ffpa-attn.readthedocs.io, note on cross-attention, GQA and causal):
+ * Q [B, Hq, Nq, D], K and V [B, Hkv, Nkv, D], contiguous, row-major; query
+ * head h uses KV head h / (Hq / Hkv); with is_causal, query row r sees keys
+ * k <= r + (Nkv - Nq) (queries aligned to the KV tail; needs Nkv >= Nq).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are caller-owned DEVICE pointers.  The library never
+ *     allocates, frees or synchronises; calls are enqueued on `stream` (a
+ *     hipStream_t passed as void*, NULL = the null stream) and run in stream
+ *     order.
+ *   - The return value is synchronous validation plus launch status.  On any
+ *     non-APA_OK return nothing was enqueued, except APA_ERR_HIP, which reports
+ *     a failed launch (earlier kernels of the same call may have run).
+ *   - Optional pointers are marked "may be NULL".
+ *   - Empty problems (B, Hq or Nq equal to 0) return APA_OK and do nothing.
+ */
+#ifndef APA_H
+#define APA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum apa_status {
+  APA_OK = 0,
+  APA_ERR_INVALID_ARG = 1, /* NULL required pointer, bad shape or parameter */
+  APA_ERR_UNSUPPORTED = 2, /* valid, but not implemented on this device     */
+  APA_ERR_WORKSPACE = 3,   /* workspace too small (see apa_workspace_bytes)  */
+  APA_ERR_HIP = 4          /* a kernel launch failed                         */
+} apa_status;
+
+enum { APA_F16 = 0, APA_BF16 = 1 };        /* input / output element type */
+enum { APA_MXFP4 = 0, APA_NVFP4 = 1 };     /* FP4 block format             */
+
+/* Problem descriptor.  Fill it with apa_problem_init() and override fields. */
+typedef struct apa_problem {
+  int32_t B, Hq, Hkv, Nq, Nkv, D; /* D in {64, 128, 256}; Hq % Hkv == 0          */
+  int32_t dtype;                  /* APA_F16 or APA_BF16 (Q, K, V and the output) */
+  int32_t is_causal;              /* 1: tail-aligned causal mask; 0: none        */
+  float scale;                    /* softmax scale; <= 0 selects 1/sqrt(D)       */
+  int32_t tile;                   /* keys per tile; must be 64 ("tiles of 64")  */
+  int32_t row_group;              /* rows per hot verdict; must be 16            */
+  int32_t fmt;                    /* APA_MXFP4 (NVFP4 exists only in the oracle) */
+  float tau;                      /* lazy-max threshold in log2 units (4), >= 0  */
+  float hot_frame_offset;         /* H: a hot tile lifts the frame to at most
+                                     max(m, c - H); an integer in [0, 126] (32) */
+} apa_problem;
+
+/* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
+ * fp16, causal. */
+void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
+                      int32_t Nkv, int32_t D);
+
+/* Byte offsets of the sections of the FP4 buffer written by apa_quantize.
+ * NqP = Nq rounded up to 32, NkvP = Nkv rounded up to 64; padding rows and
+ * keys hold zero codes.  Codes pack two 4-bit E2M1 values per byte, element
+ * 2i in the low nibble; a scale byte is an E8M0 exponent (value 2^(byte-127))
+ * of one 32-element block.
+ *   q_codes  [B][Hq][NqP][D/2]       Q along D
+ *   q_scales [B][Hq][NqP][D/32]
+ *   k_codes  [B][Hkv][NkvP][D/2]     K - kbar along D
+ *   k_scales [B][Hkv][NkvP][D/32]
+ *   v_codes  [B][Hkv][D][NkvP/2]     V along keys; inside every 32-key block
+ *                                    the eight 4-key runs are stored in the
+ *                                    order 0,2,4,6,1,3,5,7 (the lane order of
+ *                                    the P operand of the P.V product)
+ *   v_scales [B][Hkv][D][NkvP/32]
+ *   kbar     [B][Hkv][D] float       per-channel key mean
+ *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V, 0, 0
+ *   q_head   [B][Hq][4]  float       amax_Q, inv_Q, j (as float: alpha = 2^j), 0
+ *   q_frame  [B][Hq][NqP] float      c_r = sl * q.kbar, sl = fl32(scale*log2 e)
+ *   status   uint32                  bit 0: a non-finite input was seen      */
+typedef struct apa_fp4_layout {
+  size_t q_codes, q_scales, k_codes, k_scales, v_codes, v_scales;
+  size_t kbar, kv_head, q_head, q_frame, status, total;
+} apa_fp4_layout;
+
+apa_status apa_fp4_layout_of(const apa_problem* p, apa_fp4_layout* out);
+size_t apa_fp4_bytes(const apa_problem* p);
+
+/* Hot mask: uint32 words [B][Hq][ceil(Nq/16)][ceil(ceil(Nkv/64)/32)];
+ * bit (t % 32) of word (t / 32) is tile t of that 16-row group. */
+size_t apa_hotmask_bytes(const apa_problem* p);
+
+enum { APA_CALL_QUANTIZE = 0, APA_CALL_PASS1 = 1, APA_CALL_PASS2 = 2, APA_CALL_MERGE = 3,
+       APA_CALL_EXACT = 4 };
+/* Scratch bytes the given call needs in its `ws` argument (0: pass NULL). */
+size_t apa_workspace_bytes(const apa_problem* p, int32_t which_call);
+
+const char* apa_status_string(apa_status s);
+
+/* Text of the HIP error behind the calling thread's last APA_ERR_HIP. */
+const char* apa_last_hip_error(void);
+
+/* a1 + a2: statistics and block-scaled FP4 quantisation ("Mean-centred K" and
+ * the format paragraph of "Pass 1: FP4 everywhere, with a hot test").
+ * Reads q, k, v (dtype of p), writes the whole FP4 buffer `fp4`
+ * (apa_fp4_bytes(p) bytes, 256-byte aligned).  Per (b, kv-head): kbar = the
+ * per-channel mean of K (FP64 sum in a fixed order), K is centred, and
+ * K - kbar and V are normalised by one FP32 scale per head that maps the
+ * head's largest magnitude to 6; Q's per-head scale is tied to K's so the
+ * score factor is a power of two 2^j.  Blocks of 32 (Q, K along D; V along
+ * keys) get an E8M0 exponent, the smallest that fits the block maximum under
+ * 6, and E2M1 codes rounded to nearest even.  ws: apa_workspace_bytes(p,
+ * APA_CALL_QUANTIZE) bytes. */
+apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
+                        void* fp4, void* ws, size_t ws_bytes, void* stream);
+
+/* a3..a7: pass 1 ("Pass 1: FP4 everywhere, with a hot test", steps 1-5;
+ * "Tile order"; the lazy maximum; the decoupled cold frame of "The bug").
+ * Every row group of 16 rows visits its tiles in the order 0, d, d-1, ..., 1
+ * (d = its causal diagonal tile), scores them from the FP4 buffer, quantises
+ * P per 32-key group, takes the tile row sums with a ones-operand MFMA, and
+ * marks the tile hot when any row's sum exceeds eps times its running sum
+ * (eps == 0: every visited tile hot).  Cold tiles accumulate P.V in FP4.
+ * Outputs (all [B][Hq][Nq], FP32 unless noted):
+ *   cold_m  int32 log2 frame of the cold state (INT32_MIN: empty row)
+ *   cold_l  cold row sum in that frame
+ *   cold_o  [B][Hq][Nq][D] cold unnormalised output times g_V
+ *   hot_bits  apa_hotmask_bytes(p) bytes (every word written)
+ *   lambda_out  may be NULL: final running sum in the frame cold_m
+ * eps must be >= 0 and not NaN (+inf allowed).  Requires the FP4 buffer of
+ * apa_quantize for the same problem. */
+apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
+                     float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
+                     void* stream);
+
+/* a8..a10: pass 2 ("Pass 2: exact FP16 on the hot tiles").  Compacts the hot
+ * mask into per-work-group lists of tiles hot for any of its row groups, then
+ * runs FP16 MFMA flash attention (FP32 online softmax) over those tiles only,
+ * scoring s = sl*q.k - c_r so both passes share the centred logit frame.
+ * fuse_merge = 1: merges with the pass-1 state (see apa_merge) and writes
+ * out [B][Hq][Nq][D] (dtype of p) and lse [B][Hq][Nq] (natural log, may be
+ * NULL).  fuse_merge = 0: writes the hot state hot_m (log2 units, -inf for an
+ * empty row), hot_l, hot_o [..][D] (unnormalised) instead.
+ * ws: apa_workspace_bytes(p, APA_CALL_PASS2) bytes. */
+apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const void* v,
+                     const void* fp4, const uint32_t* hot_bits, const int32_t* cold_m,
+                     const float* cold_l, const float* cold_o, int32_t fuse_merge, void* out,
+                     float* lse, float* hot_m, float* hot_l, float* hot_o, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* a10: exact merge of the cold and hot states ("The merge that makes it
+ * exact"): M = max(m1, m2) over non-empty states, w_i = 2^(m_i - M),
+ * O = (w1 o1 + w2 o2) / (w1 l1 + w2 l2); a state with l = 0 is empty and
+ * skipped; both empty gives O = 0 and lse = -inf ("Half the bytes, exactly
+ * merged", section "The merge").  lse = ln2 (c_r + M + log2 L) with c_r from
+ * the FP4 buffer; lse may be NULL. */
+apa_status apa_merge(const apa_problem* p, const void* fp4, const int32_t* cold_m,
+                     const float* cold_l, const float* cold_o, const float* hot_m,
+                     const float* hot_l, const float* hot_o, void* out, float* lse,
+                     void* stream);
+
+/* a11: all-exact FP16 flash attention over every visible tile (the baseline
+ * APA is compared against: "13.023 ms ... with every tile computed exactly"
+ * in the post's introduction).  Same masking and GQA rules; out in dtype of
+ * p, lse natural log (may be NULL).  ws: apa_workspace_bytes(p,
+ * APA_CALL_EXACT) bytes. */
+apa_status apa_exact(const apa_problem* p, const void* q, const void* k, const void* v,
+                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* APA_H */

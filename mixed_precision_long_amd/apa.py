@@ -1,0 +1,209 @@
+"""Thin ctypes binding of libapa.so (declared in include/apa.h).
+
+Argument marshalling only: every step of the method runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current HIP stream.  Loading
+fails loudly if the library has not been built; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libapa.so")
+
+APA_OK, APA_ERR_INVALID_ARG, APA_ERR_UNSUPPORTED, APA_ERR_WORKSPACE, APA_ERR_HIP = range(5)
+APA_F16, APA_BF16 = 0, 1
+APA_MXFP4, APA_NVFP4 = 0, 1
+CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
+
+EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
+           "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize", "apa_pass1", "apa_pass2",
+           "apa_merge", "apa_exact"]
+
+
+class ApaError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        msg = "%s failed: %s" % (what, status_string(code))
+        if code == APA_ERR_HIP:
+            msg += " (%s)" % lib().apa_last_hip_error().decode()
+        super().__init__(msg)
+        self.code = code
+
+
+class Problem(C.Structure):
+    _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("Nq", C.c_int32),
+                ("Nkv", C.c_int32), ("D", C.c_int32), ("dtype", C.c_int32),
+                ("is_causal", C.c_int32), ("scale", C.c_float), ("tile", C.c_int32),
+                ("row_group", C.c_int32), ("fmt", C.c_int32), ("tau", C.c_float),
+                ("hot_frame_offset", C.c_float)]
+
+
+class Fp4Layout(C.Structure):
+    _fields_ = [(k, C.c_size_t) for k in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes",
+                                          "v_scales", "kbar", "kv_head", "q_head", "q_frame",
+                                          "status", "total")]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libapa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        # PyTorch ships its own HIP runtime (same soname).  Load it first so the
+        # library binds to that one runtime instead of pulling in a second.
+        import torch  # noqa: F401
+        L = C.CDLL(LIB_PATH)
+        P, VP, S = C.POINTER(Problem), C.c_void_p, C.c_size_t
+        L.apa_problem_init.argtypes = [P] + [C.c_int32] * 6
+        L.apa_problem_init.restype = None
+        L.apa_fp4_layout_of.argtypes = [P, C.POINTER(Fp4Layout)]
+        L.apa_fp4_bytes.argtypes = [P]
+        L.apa_fp4_bytes.restype = S
+        L.apa_hotmask_bytes.argtypes = [P]
+        L.apa_hotmask_bytes.restype = S
+        L.apa_workspace_bytes.argtypes = [P, C.c_int32]
+        L.apa_workspace_bytes.restype = S
+        L.apa_status_string.argtypes = [C.c_int]
+        L.apa_status_string.restype = C.c_char_p
+        L.apa_last_hip_error.argtypes = []
+        L.apa_last_hip_error.restype = C.c_char_p
+        L.apa_quantize.argtypes = [P, VP, VP, VP, VP, VP, S, VP]
+        L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP]
+        L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
+                                VP, S, VP]
+        L.apa_merge.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
+        L.apa_exact.argtypes = [P, VP, VP, VP, VP, VP, VP, S, VP]
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().apa_status_string(int(code)).decode()
+
+
+def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
+            fmt=APA_MXFP4) -> Problem:
+    p = Problem()
+    lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
+    p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt = (
+        dtype, causal, scale, tau, hoff, fmt)
+    return p
+
+
+def fp4_layout(p: Problem) -> Fp4Layout:
+    L = Fp4Layout()
+    _check(lib().apa_fp4_layout_of(C.byref(p), C.byref(L)), "apa_fp4_layout_of")
+    return L
+
+
+def fp4_bytes(p: Problem) -> int:
+    return lib().apa_fp4_bytes(C.byref(p))
+
+
+def hotmask_bytes(p: Problem) -> int:
+    return lib().apa_hotmask_bytes(C.byref(p))
+
+
+def workspace_bytes(p: Problem, call: int) -> int:
+    return lib().apa_workspace_bytes(C.byref(p), call)
+
+
+def _check(code: int, what: str):
+    if code != APA_OK:
+        raise ApaError(code, what)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# calls on torch tensors (device memory); all asynchronous on the stream
+# ---------------------------------------------------------------------------
+
+def quantize(p: Problem, q, k, v, fp4, ws, stream=None):
+    _check(lib().apa_quantize(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(),
+                              _stream(stream)), "apa_quantize")
+
+
+def pass1(p: Problem, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=None, stream=None):
+    _check(lib().apa_pass1(C.byref(p), _ptr(fp4), float(eps), _ptr(cold_m), _ptr(cold_l),
+                           _ptr(cold_o), _ptr(hot_bits), _ptr(lam), _stream(stream)), "apa_pass1")
+
+
+def pass2(p: Problem, q, k, v, fp4, hot_bits, cold_m, cold_l, cold_o, fuse_merge: bool, out=None,
+          lse=None, hot_m=None, hot_l=None, hot_o=None, ws=None, stream=None):
+    _check(lib().apa_pass2(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), _ptr(hot_bits),
+                           _ptr(cold_m), _ptr(cold_l), _ptr(cold_o), 1 if fuse_merge else 0,
+                           _ptr(out), _ptr(lse), _ptr(hot_m), _ptr(hot_l), _ptr(hot_o), _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "apa_pass2")
+
+
+def merge(p: Problem, fp4, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, out, lse=None,
+          stream=None):
+    _check(lib().apa_merge(C.byref(p), _ptr(fp4), _ptr(cold_m), _ptr(cold_l), _ptr(cold_o),
+                           _ptr(hot_m), _ptr(hot_l), _ptr(hot_o), _ptr(out), _ptr(lse),
+                           _stream(stream)), "apa_merge")
+
+
+def exact(p: Problem, q, k, v, out, lse=None, ws=None, stream=None):
+    _check(lib().apa_exact(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "apa_exact")
+
+
+@dataclass
+class Buffers:
+    """Device buffers of one APA problem (allocated once, reused per call)."""
+    fp4: object
+    ws_q: object
+    ws_p2: object
+    cold_m: object
+    cold_l: object
+    cold_o: object
+    bits: object
+    lam: object
+    out: object
+    lse: object
+
+
+def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
+    import torch
+    B, Hq, Nq, D = p.B, p.Hq, p.Nq, p.D
+
+    def u8(n):
+        return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
+
+    odt = torch.float16 if p.dtype == APA_F16 else torch.bfloat16
+    return Buffers(
+        fp4=u8(fp4_bytes(p)), ws_q=u8(workspace_bytes(p, CALL_QUANTIZE)),
+        ws_p2=u8(workspace_bytes(p, CALL_PASS2)),
+        cold_m=torch.empty((B, Hq, Nq), dtype=torch.int32, device=device),
+        cold_l=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device),
+        cold_o=torch.empty((B, Hq, Nq, D), dtype=torch.float32, device=device),
+        bits=torch.empty(max(hotmask_bytes(p) // 4, 1), dtype=torch.int32, device=device),
+        lam=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device) if with_lambda else None,
+        out=torch.empty((B, Hq, Nq, D), dtype=odt, device=device),
+        lse=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device))
+
+
+def apa_forward(p: Problem, q, k, v, eps: float, bufs: Buffers, stream=None):
+    """The whole hot path: quantize -> pass 1 -> pass 2 with the fused merge."""
+    quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
+    pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, bufs.lam, stream)
+    pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
+          out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
+    return bufs.out, bufs.lse

@@ -1,0 +1,282 @@
+// C ABI of the APA library: validation, buffer layout, workspace sizing and
+// stream-ordered launches.  No allocation, no synchronisation, no exceptions
+// across the ABI.  Declarations and argument documentation: include/apa.h.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/apa.h"
+#include "apa_kernels.h"
+
+using namespace apa;
+
+namespace {
+
+constexpr float kLog2e32 = 1.44269502162933349609375f;  // fl32(log2 e)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t rup(size_t x, size_t m) { return (x + m - 1) / m * m; }
+
+bool valid_problem(const apa_problem* p) {
+  if (!p) return false;
+  if (p->B < 0 || p->Hq < 0 || p->Hkv < 1 || p->Nq < 0 || p->Nkv < 0) return false;
+  if (p->Hq % p->Hkv != 0) return false;
+  if (p->D != 64 && p->D != 128 && p->D != 256 && p->D != 512) return false;
+  if (p->dtype != APA_F16 && p->dtype != APA_BF16) return false;
+  if (p->is_causal != 0 && p->is_causal != 1) return false;
+  if (p->is_causal && p->Nkv < p->Nq) return false;
+  if (p->tile != 64 || p->row_group != 16) return false;
+  if (p->fmt != APA_MXFP4 && p->fmt != APA_NVFP4) return false;
+  if (!(p->tau >= 0.0f) || !isfinite(p->tau)) return false;
+  const float H = p->hot_frame_offset;
+  if (!(H >= 0.0f && H <= 126.0f) || floorf(H) != H) return false;
+  if (isnan(p->scale)) return false;
+  if (p->Nq > 0 && p->Nkv == 0) return false;
+  return true;
+}
+
+bool empty(const apa_problem* p) { return p->B == 0 || p->Hq == 0 || p->Nq == 0; }
+
+Geom geom(const apa_problem* p) {
+  Geom g;
+  g.B = p->B; g.Hq = p->Hq; g.Hkv = p->Hkv; g.G = p->Hq / p->Hkv;
+  g.Nq = p->Nq; g.Nkv = p->Nkv; g.D = p->D;
+  g.NqP = (int)rup(p->Nq, 32);
+  g.NT = (p->Nkv + 63) / 64;
+  g.NkvP = g.NT * 64;
+  g.NG = (p->Nq + 15) / 16;
+  g.W = (g.NT + 31) / 32;
+  g.causal = p->is_causal;
+  g.off = p->Nkv - p->Nq;
+  g.bf16 = p->dtype == APA_BF16;
+  const float scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->D));
+  g.sl = scale * kLog2e32;
+  return g;
+}
+
+void layout(const apa_problem* p, apa_fp4_layout* L) {
+  const Geom g = geom(p);
+  const size_t B = p->B, Hq = p->Hq, Hkv = p->Hkv, D = p->D;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  L->q_codes = take(B * Hq * g.NqP * D / 2);
+  L->q_scales = take(B * Hq * g.NqP * D / 32);
+  L->k_codes = take(B * Hkv * g.NkvP * D / 2);
+  L->k_scales = take(B * Hkv * g.NkvP * D / 32);
+  L->v_codes = take(B * Hkv * D * g.NkvP / 2);
+  L->v_scales = take(B * Hkv * D * g.NkvP / 32);
+  L->kbar = take(B * Hkv * D * 4);
+  L->kv_head = take(B * Hkv * 8 * 4);
+  L->q_head = take(B * Hq * 4 * 4);
+  L->q_frame = take(B * Hq * g.NqP * 4);
+  L->status = take(4);
+  L->total = o;
+}
+
+Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
+  apa_fp4_layout L;
+  layout(p, &L);
+  uint8_t* b = (uint8_t*)base;
+  Fp4Ptrs f;
+  f.q_codes = b + L.q_codes; f.q_scales = b + L.q_scales;
+  f.k_codes = b + L.k_codes; f.k_scales = b + L.k_scales;
+  f.v_codes = b + L.v_codes; f.v_scales = b + L.v_scales;
+  f.kbar = (float*)(b + L.kbar); f.kv_head = (float*)(b + L.kv_head);
+  f.q_head = (float*)(b + L.q_head); f.q_frame = (float*)(b + L.q_frame);
+  f.status = (unsigned*)(b + L.status);
+  return f;
+}
+
+size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
+  const Geom g = geom(p);
+  const size_t nkv = (size_t)p->B * p->Hkv * g.NT;
+  const int nqt = (p->Nq + 63) / 64;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t a = take(nkv * p->D * 8), b = take(nkv * p->D * 4), c = take(nkv * p->D * 4),
+               d = take(nkv * 4), e = take((size_t)p->B * p->Hq * (nqt > 0 ? nqt : 1) * 4);
+  if (ws && base) {
+    uint8_t* bb = (uint8_t*)base;
+    ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
+    ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e); ws->nqt = nqt;
+  }
+  return o;
+}
+
+size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
+  const Geom g = geom(p);
+  const size_t units = (size_t)p->B * p->Hkv * ((p->Nq + 63) / 64);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t t = take(units * g.NT * 4), m = take(units * g.NT * 4), c = take(units * 4);
+  if (a && base) {
+    uint8_t* bb = (uint8_t*)base;
+    a->list_tiles = (int32_t*)(bb + t); a->list_masks = (uint32_t*)(bb + m);
+    a->list_count = (int32_t*)(bb + c);
+  }
+  return o;
+}
+
+// D and dtype the device kernels implement for each call
+bool kernels_cover(const apa_problem* p, int call) {
+  if (p->fmt != APA_MXFP4) return false;
+  if (call == APA_CALL_QUANTIZE) return true;
+  if (p->D == 512) return false;
+  if (call == APA_CALL_PASS1) return true;
+  if (p->dtype != APA_F16) return false;
+  const int G = p->Hq / p->Hkv;
+  if (call == APA_CALL_PASS2 || call == APA_CALL_EXACT)
+    return G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8;
+  return true;
+}
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+apa_status hip_status(hipError_t e) {
+  g_last_hip = e;
+  return e == hipSuccess ? APA_OK : APA_ERR_HIP;
+}
+
+// Drop any error a previous, unrelated HIP call left behind, so a launch check
+// reports only this call's kernels.
+void clear_hip_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
+                      int32_t Nkv, int32_t D) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->Nq = Nq; p->Nkv = Nkv; p->D = D;
+  p->dtype = APA_F16;
+  p->is_causal = 1;
+  p->scale = 0.0f;
+  p->tile = 64;
+  p->row_group = 16;
+  p->fmt = APA_MXFP4;
+  p->tau = 4.0f;
+  p->hot_frame_offset = 32.0f;
+}
+
+const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
+
+const char* apa_status_string(apa_status s) {
+  switch (s) {
+    case APA_OK: return "APA_OK";
+    case APA_ERR_INVALID_ARG: return "APA_ERR_INVALID_ARG: invalid argument";
+    case APA_ERR_UNSUPPORTED: return "APA_ERR_UNSUPPORTED: not implemented for this problem";
+    case APA_ERR_WORKSPACE: return "APA_ERR_WORKSPACE: workspace too small";
+    case APA_ERR_HIP: return "APA_ERR_HIP: kernel launch failed";
+  }
+  return "APA: unknown status";
+}
+
+apa_status apa_fp4_layout_of(const apa_problem* p, apa_fp4_layout* out) {
+  if (!valid_problem(p) || !out) return APA_ERR_INVALID_ARG;
+  layout(p, out);
+  return APA_OK;
+}
+
+size_t apa_fp4_bytes(const apa_problem* p) {
+  if (!valid_problem(p)) return 0;
+  apa_fp4_layout L;
+  layout(p, &L);
+  return L.total;
+}
+
+size_t apa_hotmask_bytes(const apa_problem* p) {
+  if (!valid_problem(p)) return 0;
+  const Geom g = geom(p);
+  return (size_t)p->B * p->Hq * g.NG * g.W * 4;
+}
+
+size_t apa_workspace_bytes(const apa_problem* p, int32_t which) {
+  if (!valid_problem(p)) return 0;
+  switch (which) {
+    case APA_CALL_QUANTIZE: return quant_ws(p, nullptr, nullptr);
+    case APA_CALL_PASS2: return pass2_ws(p, nullptr, nullptr);
+    default: return 0;
+  }
+}
+
+apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
+                        void* fp4, void* ws, size_t ws_bytes, void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_QUANTIZE)) return APA_ERR_UNSUPPORTED;
+  if (p->B == 0 || p->Hkv == 0) return APA_OK;
+  const size_t need = quant_ws(p, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return APA_ERR_WORKSPACE;
+  QuantWs w;
+  quant_ws(p, &w, ws);
+  clear_hip_error();
+  return hip_status(launch_quantize(geom(p), q, k, v, fp4_ptrs(p, fp4), w, (hipStream_t)stream));
+}
+
+apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
+                     float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
+                     void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!fp4 || !cold_m || !cold_l || !cold_o || !hot_bits) return APA_ERR_INVALID_ARG;
+  if (isnan(eps) || eps < 0.0f) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_PASS1)) return APA_ERR_UNSUPPORTED;
+  if (empty(p)) return APA_OK;
+  Pass1Out o = {cold_m, cold_l, cold_o, hot_bits, lambda_out};
+  clear_hip_error();
+  return hip_status(launch_pass1(geom(p), fp4_ptrs(p, fp4), eps, p->tau,
+                                 (int)p->hot_frame_offset, o, (hipStream_t)stream));
+}
+
+apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const void* v,
+                     const void* fp4, const uint32_t* hot_bits, const int32_t* cold_m,
+                     const float* cold_l, const float* cold_o, int32_t fuse_merge, void* out,
+                     float* lse, float* hot_m, float* hot_l, float* hot_o, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4 || !hot_bits) return APA_ERR_INVALID_ARG;
+  if (fuse_merge != 0 && fuse_merge != 1) return APA_ERR_INVALID_ARG;
+  if (fuse_merge && (!cold_m || !cold_l || !cold_o || !out)) return APA_ERR_INVALID_ARG;
+  if (!fuse_merge && (!hot_m || !hot_l || !hot_o)) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_PASS2)) return APA_ERR_UNSUPPORTED;
+  if (empty(p)) return APA_OK;
+  const size_t need = pass2_ws(p, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return APA_ERR_WORKSPACE;
+  Pass2Args a = {};
+  a.q = q; a.k = k; a.v = v; a.bits = hot_bits;
+  a.cold_m = cold_m; a.cold_l = cold_l; a.cold_o = cold_o;
+  a.fuse = fuse_merge; a.out = out; a.lse = lse;
+  a.hot_m = hot_m; a.hot_l = hot_l; a.hot_o = hot_o;
+  pass2_ws(p, &a, ws);
+  clear_hip_error();
+  return hip_status(launch_pass2(geom(p), fp4_ptrs(p, fp4), a, (hipStream_t)stream));
+}
+
+apa_status apa_merge(const apa_problem* p, const void* fp4, const int32_t* cold_m,
+                     const float* cold_l, const float* cold_o, const float* hot_m,
+                     const float* hot_l, const float* hot_o, void* out, float* lse,
+                     void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!fp4 || !cold_m || !cold_l || !cold_o || !hot_m || !hot_l || !hot_o || !out)
+    return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_MERGE)) return APA_ERR_UNSUPPORTED;
+  if (p->dtype != APA_F16) return APA_ERR_UNSUPPORTED;
+  if (empty(p)) return APA_OK;
+  clear_hip_error();
+  return hip_status(launch_merge(geom(p), fp4_ptrs(p, fp4), cold_m, cold_l, cold_o, hot_m, hot_l,
+                                 hot_o, out, lse, (hipStream_t)stream));
+}
+
+apa_status apa_exact(const apa_problem* p, const void* q, const void* k, const void* v,
+                     void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_EXACT)) return APA_ERR_UNSUPPORTED;
+  if (empty(p)) return APA_OK;
+  clear_hip_error();
+  return hip_status(launch_exact(geom(p), q, k, v, out, lse, (hipStream_t)stream));
+}
+
+}  // extern "C"

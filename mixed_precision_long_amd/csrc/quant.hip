@@ -1,0 +1,299 @@
+// a1 statistics and a2 block-scaled FP4 quantisation.
+//
+// "APA: sloppy attention, exact where it counts" (rfriedmann.de), section
+// "Pass 1: FP4 everywhere, with a hot test": a prep stage writes K and V^T in
+// E2M1 plus their scales, after subtracting the per-channel key mean
+// ("Mean-centred K"), with one FP32 scale per head.  Here the block format is
+// MXFP4: one E8M0 exponent per 32 elements (Q and K along channels, V along
+// keys), the smallest that fits the block maximum under 6, and E2M1 codes
+// rounded to nearest even by the hardware's scaled conversion.
+//
+// HBM-bound work: K and V are read twice (statistics, then quantisation) and
+// Q once; all reductions run in a fixed order, so results are deterministic.
+#include "apa_device.h"
+#include "apa_kernels.h"
+
+namespace apa {
+
+namespace {
+
+__global__ void k_clear_status(unsigned* status) { *status = 0u; }
+
+// Block-wide max over blockDim.x threads (<= 512) through LDS.
+__device__ float block_max(float v, float* red) {
+  const int t = threadIdx.x;
+  // wave-level reduction first
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  __syncthreads();
+  if ((t & 63) == 0) red[t >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)((blockDim.x + 63) >> 6); ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+
+// Per (b, kv-head, 64-key tile): per-channel FP64 sum (ascending keys), min
+// and max of K; max |V| over the tile.  grid (NT, B*Hkv), block D.
+template <typename T>
+__global__ void k_kv_stats(const T* __restrict__ K, const T* __restrict__ V, Geom g, QuantWs ws,
+                           unsigned* status) {
+  __shared__ float red[8];
+  const int d = threadIdx.x, t = blockIdx.x, bh = blockIdx.y;
+  const size_t base = ((size_t)bh * g.Nkv) * g.D;
+  const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
+  double s = 0.0;
+  float mn = __builtin_inff(), mx = -__builtin_inff(), va = 0.0f;
+  bool bad = false;
+  for (int k = k0; k < k1; ++k) {
+    float x = to_f32<T>(K[base + (size_t)k * g.D + d]);
+    float y = to_f32<T>(V[base + (size_t)k * g.D + d]);
+    bad |= !__builtin_isfinite(x) || !__builtin_isfinite(y);
+    s += (double)x;
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+    va = fmaxf(va, fabsf(y));
+  }
+  const size_t o = ((size_t)bh * g.NT + t) * g.D + d;
+  ws.ksum[o] = s;
+  ws.kmin[o] = mn;
+  ws.kmax[o] = mx;
+  if (bad) atomicOr(status, 1u);
+  float m = block_max(va, red);
+  if (d == 0) ws.vamax[(size_t)bh * g.NT + t] = m;
+}
+
+// max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq), block D.
+template <typename T>
+__global__ void k_q_stats(const T* __restrict__ Q, Geom g, QuantWs ws, unsigned* status) {
+  __shared__ float red[8];
+  const int d = threadIdx.x, t = blockIdx.x, bh = blockIdx.y;
+  const size_t base = ((size_t)bh * g.Nq) * g.D;
+  const int r0 = t * 64, r1 = min(g.Nq, r0 + 64);
+  float a = 0.0f;
+  bool bad = false;
+  for (int r = r0; r < r1; ++r) {
+    float x = to_f32<T>(Q[base + (size_t)r * g.D + d]);
+    bad |= !__builtin_isfinite(x);
+    a = fmaxf(a, fabsf(x));
+  }
+  if (bad) atomicOr(status, 1u);
+  float m = block_max(a, red);
+  if (d == 0) ws.qamax[(size_t)bh * ws.nqt + t] = m;
+}
+
+// Head scale mapping amax to 6: g = fl32(amax/6), inv = fl32(6/amax); the FP64
+// quotient rounded once is the correctly rounded binary32 quotient.
+__device__ void head_scale(float amax, float* gs, float* inv) {
+  if (!(amax > 0.0f)) { *gs = 1.0f; *inv = 1.0f; return; }
+  *gs = (float)((double)amax / 6.0);
+  *inv = (float)(6.0 / (double)amax);
+}
+
+// Per (b, kv-head): key mean, |K - kbar| max, V max, their head scales, and
+// the tied Q scales of the group's query heads.  grid (B*Hkv), block D.
+__global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
+  __shared__ float red[8];
+  const int d = threadIdx.x, bh = blockIdx.x;
+  double s = 0.0;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int t = 0; t < g.NT; ++t) {  // tile sums in ascending tile order
+    const size_t o = ((size_t)bh * g.NT + t) * g.D + d;
+    s += ws.ksum[o];
+    mn = fminf(mn, ws.kmin[o]);
+    mx = fmaxf(mx, ws.kmax[o]);
+  }
+  const float kb = g.Nkv > 0 ? (float)(s / (double)g.Nkv) : 0.0f;
+  f.kbar[(size_t)bh * g.D + d] = kb;
+  float dev = 0.0f;
+  if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
+  const float amax_k = block_max(dev, red);
+  float va = 0.0f;
+  for (int t = d; t < g.NT; t += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * g.NT + t]);
+  const float amax_v = block_max(va, red);
+  float gk, ik, gv, iv;
+  head_scale(amax_k, &gk, &ik);
+  head_scale(amax_v, &gv, &iv);
+  if (d == 0) {
+    float* kh = f.kv_head + (size_t)bh * 8;
+    kh[0] = amax_k; kh[1] = gk; kh[2] = ik; kh[3] = amax_v; kh[4] = gv; kh[5] = iv;
+    kh[6] = 0.0f; kh[7] = 0.0f;
+  }
+  // Q heads of this group: inv_q = w * 2^-j, w = fl32(sl * g_k), j the
+  // smallest integer with amax_q * w <= 6 * 2^j.
+  const int b = bh / g.Hkv, hk = bh % g.Hkv;
+  const float w = g.sl * gk;
+  for (int i = 0; i < g.G; ++i) {
+    const int hq = hk * g.G + i;
+    const size_t bq = (size_t)b * g.Hq + hq;
+    float qa = 0.0f;
+    for (int t = d; t < ws.nqt; t += blockDim.x) qa = fmaxf(qa, ws.qamax[bq * ws.nqt + t]);
+    const float amax_q = block_max(qa, red);
+    if (d == 0) {
+      int j = 0;
+      if (amax_q > 0.0f && w > 0.0f) {
+        const double prod = (double)amax_q * (double)w;  // exact
+        int x;
+        frexp(prod / 6.0, &x);
+        j = x - 2;
+        while (6.0 * ldexp(1.0, j) < prod) ++j;
+        while (6.0 * ldexp(1.0, j - 1) >= prod) --j;
+      }
+      float* qh = f.q_head + bq * 4;
+      qh[0] = amax_q;
+      qh[1] = (float)ldexp((double)w, -j);
+      qh[2] = (float)j;
+      qh[3] = 0.0f;
+    }
+  }
+}
+
+// Quantise rows along channels (Q, or K - kbar).  Each thread owns 8
+// consecutive channels; 4 threads form one 32-channel block.  Rows in
+// [Nrows, NP) are padding and get zero codes.  For Q it also writes the frame
+// constant c_r = sl * q.kbar (FP32).  grid (ceil(NP*D/8 / 256), B*H).
+template <typename T, bool IS_Q>
+__global__ void k_quant_rows(const T* __restrict__ X, Geom g, Fp4Ptrs f) {
+  const int H = IS_Q ? g.Hq : g.Hkv;
+  const int Nrows = IS_Q ? g.Nq : g.Nkv;
+  const int NP = IS_Q ? g.NqP : g.NkvP;
+  const int bh = blockIdx.y;
+  const int tpr = g.D / 8;                     // threads per row
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = gid / tpr, c8 = (gid % tpr) * 8;
+  if (row >= NP) return;                       // whole 4-thread blocks exit together
+  const int b = bh / H, h = bh % H;
+  const int hk = IS_Q ? h / g.G : h;
+  const size_t bk = (size_t)b * g.Hkv + hk;
+  float inv;
+  const float* kb = f.kbar + bk * g.D;
+  if (IS_Q) inv = f.q_head[(size_t)bh * 4 + 1];
+  else inv = f.kv_head[bk * 8 + 2];
+  float x[8];
+  float cdot = 0.0f;
+  if (row < Nrows) {
+    const T* src = X + ((size_t)bh * Nrows + row) * g.D + c8;
+    const uint4 raw = *reinterpret_cast<const uint4*>(src);
+    const T* e = reinterpret_cast<const T*>(&raw);
+    for (int i = 0; i < 8; ++i) {
+      float v = to_f32<T>(e[i]);
+      if (IS_Q) {
+        cdot = fmaf(v, kb[c8 + i], cdot);
+      } else {
+        v = v - kb[c8 + i];
+      }
+      float n = v * inv;
+      x[i] = fminf(fmaxf(n, -6.0f), 6.0f);
+    }
+  } else {
+    for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+  }
+  float a = 0.0f;
+  for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  const int e = e8m0_exponent(a);
+  const float s = pow2_scale(e);
+  unsigned w = 0;
+  w = cvt_fp4x2(w, x[0], x[1], s, 0);
+  w = cvt_fp4x2(w, x[2], x[3], s, 1);
+  w = cvt_fp4x2(w, x[4], x[5], s, 2);
+  w = cvt_fp4x2(w, x[6], x[7], s, 3);
+  uint8_t* codes = IS_Q ? f.q_codes : f.k_codes;
+  uint8_t* scales = IS_Q ? f.q_scales : f.k_scales;
+  const size_t r = (size_t)bh * NP + row;
+  *reinterpret_cast<unsigned*>(codes + r * (g.D / 2) + c8 / 2) = w;
+  if ((c8 & 31) == 0) scales[r * (g.D / 32) + c8 / 32] = (uint8_t)(e + 127);
+  if (IS_Q) {
+    // row reduction of the frame constant over the D/8 threads of the row
+    for (int o = 1; o < tpr; o <<= 1) cdot += __shfl_xor(cdot, o);
+    if (c8 == 0) f.q_frame[r] = row < Nrows ? g.sl * cdot : 0.0f;
+  }
+}
+
+// Quantise V along keys into the transposed layout.  One block per (64-key
+// tile, b*kv-head, 128-channel chunk): the tile is staged in LDS, then thread
+// (channel, half) quantises one 32-key block.  Codes of a block are stored
+// with its eight 4-key runs in the order 0,2,4,6,1,3,5,7.
+template <typename T>
+__global__ void k_quant_vt(const T* __restrict__ V, Geom g, Fp4Ptrs f) {
+  constexpr int CH = 128, PAD = 2;
+  __shared__ float tile[kTile][CH + PAD];
+  const int t = blockIdx.x, bh = blockIdx.y, c0 = blockIdx.z * CH;
+  const int nch = min(CH, g.D - c0);
+  const int hk = bh % g.Hkv;
+  (void)hk;
+  const float inv = f.kv_head[(size_t)bh * 8 + 5];
+  const int k0 = t * kTile;
+  // stage: element (key, ch) as float, zero for padding keys
+  for (int i = threadIdx.x; i < kTile * nch; i += blockDim.x) {
+    const int kk = i / nch, c = i % nch;
+    const int key = k0 + kk;
+    float v = 0.0f;
+    if (key < g.Nkv) v = to_f32<T>(V[((size_t)bh * g.Nkv + key) * g.D + c0 + c]);
+    float n = v * inv;
+    tile[kk][c] = fminf(fmaxf(n, -6.0f), 6.0f);
+  }
+  __syncthreads();
+  const int c = threadIdx.x % CH, half = threadIdx.x / CH;
+  if (c >= nch || half >= 2) return;
+  float a = 0.0f;
+  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(tile[half * 32 + i][c]));
+  const int e = e8m0_exponent(a);
+  const float s = pow2_scale(e);
+  // dword j holds runs perm[2j], perm[2j+1]; run q covers keys 4q..4q+3
+  const int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  unsigned out[4];
+  for (int j = 0; j < 4; ++j) {
+    unsigned w = 0;
+    const int ra = perm[2 * j] * 4 + half * 32, rb = perm[2 * j + 1] * 4 + half * 32;
+    w = cvt_fp4x2(w, tile[ra + 0][c], tile[ra + 1][c], s, 0);
+    w = cvt_fp4x2(w, tile[ra + 2][c], tile[ra + 3][c], s, 1);
+    w = cvt_fp4x2(w, tile[rb + 0][c], tile[rb + 1][c], s, 2);
+    w = cvt_fp4x2(w, tile[rb + 2][c], tile[rb + 3][c], s, 3);
+    out[j] = w;
+  }
+  const size_t row = (size_t)bh * g.D + c0 + c;
+  uint4 o4 = {out[0], out[1], out[2], out[3]};
+  *reinterpret_cast<uint4*>(f.v_codes + row * (g.NkvP / 2) + t * 32 + half * 16) = o4;
+  f.v_scales[row * (g.NkvP / 32) + t * 2 + half] = (uint8_t)(e + 127);
+}
+
+template <typename T>
+hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const Fp4Ptrs& f,
+                        const QuantWs& ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, f.status);
+  if (g.Nkv > 0)
+    hipLaunchKernelGGL(k_kv_stats<T>, dim3(g.NT, g.B * g.Hkv), dim3(g.D), 0, s, k, v, g, ws,
+                       f.status);
+  if (g.Nq > 0)
+    hipLaunchKernelGGL(k_q_stats<T>, dim3(ws.nqt, g.B * g.Hq), dim3(g.D), 0, s, q, g, ws,
+                       f.status);
+  hipLaunchKernelGGL(k_finalize, dim3(g.B * g.Hkv), dim3(g.D), 0, s, g, ws, f);
+  if (g.NkvP > 0) {
+    const long thr = (long)g.NkvP * (g.D / 8);
+    hipLaunchKernelGGL((k_quant_rows<T, false>), dim3((unsigned)((thr + 255) / 256), g.B * g.Hkv),
+                       dim3(256), 0, s, k, g, f);
+    hipLaunchKernelGGL(k_quant_vt<T>, dim3(g.NT, g.B * g.Hkv, (g.D + 127) / 128), dim3(256), 0, s,
+                       v, g, f);
+  }
+  if (g.NqP > 0 && g.Hq > 0) {
+    const long thr = (long)g.NqP * (g.D / 8);
+    hipLaunchKernelGGL((k_quant_rows<T, true>), dim3((unsigned)((thr + 255) / 256), g.B * g.Hq),
+                       dim3(256), 0, s, q, g, f);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const Geom& g, const void* q, const void* k, const void* v,
+                           const Fp4Ptrs& f, const QuantWs& ws, hipStream_t s) {
+  if (g.bf16)
+    return run_quantize<uint16_t>(g, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                  f, ws, s);
+  return run_quantize<_Float16>(g, (const _Float16*)q, (const _Float16*)k, (const _Float16*)v, f,
+                                ws, s);
+}
+
+}  // namespace apa

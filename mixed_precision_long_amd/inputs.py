@@ -92,7 +92,8 @@ WORKLOADS = {
 
 
 def _path(rng, n_pos: int, pos0: int, D: int, amp, per, ph) -> np.ndarray:
-    """Unit path vectors c(t) for t = pos0 .. pos0 + n_pos - 1, shape [n_pos, D]."""
+    """Unit path vectors c(t) for t = pos0 .. pos0 + n_pos - 1, shape [n_pos, D].
+    (rng is unused; the path is a deterministic function of its parameters.)"""
     out = np.empty((n_pos, D), np.float64)
     step = 4096
     w = 2.0 * np.pi / per  # [8, D]
@@ -105,45 +106,59 @@ def _path(rng, n_pos: int, pos0: int, D: int, amp, per, ph) -> np.ndarray:
     return out
 
 
-def make_inputs(w: Workload, delta: float | None = None):
+def _kv_group(w: Workload, b: int, j: int, delta: float):
+    """Q rows of the group's query heads, K and V of kv-head j (float32 values
+    of w.dtype).  Own random stream per (seed, b, j): draw order path
+    parameters, K noise, V, then the Q noise of each query head ascending."""
+    rng = np.random.default_rng([w.seed, b, j])
+    Nq, Nkv, D, G = w.Nq, w.Nkv, w.D, w.Hq // w.Hkv
+    off = Nkv - Nq
+    Qg = np.empty((G, Nq, D), np.float32)
+    if w.mode == "path":
+        amp = rng.standard_normal((N_SINES, D))
+        per = np.exp(rng.uniform(np.log(PERIOD_MIN), np.log(PERIOD_MAX), (N_SINES, D)))
+        ph = rng.uniform(0.0, 2.0 * np.pi, (N_SINES, D))
+        kk = rng.standard_normal((Nkv, D)) / np.sqrt(D)
+        kk += w.a * _path(rng, Nkv, 0, D, amp, per, ph)
+        Vj = round_to(rng.standard_normal((Nkv, D)), w.dtype)
+        cq = w.a * _path(rng, Nq, off, D, amp, per, ph)
+        for i in range(G):
+            Qg[i] = round_to(rng.standard_normal((Nq, D)) / np.sqrt(D) + cq, w.dtype)
+    else:
+        kk = rng.standard_normal((Nkv, D))
+        Vj = round_to(rng.standard_normal((Nkv, D)), w.dtype)
+        for i in range(G):
+            Qg[i] = round_to(rng.standard_normal((Nq, D)), w.dtype)
+    if delta != 0.0 and Nkv > 0 and Nq > 0:
+        u = Qg.astype(np.float64).reshape(-1, D).mean(axis=0)
+        nu = float(u @ u)
+        if nu > 0:
+            kk[:SINK_KEYS] += delta * u / (w.scale * nu)
+    return Qg, round_to(kk, w.dtype), Vj
+
+
+def make_inputs(w: Workload, delta: float | None = None, kv_heads=None, threads: int = 8):
     """Returns (Q, K, V) as float32 arrays holding values of w.dtype.
 
-    Q [B, Hq, Nq, D], K and V [B, Hkv, Nkv, D].  Deterministic in w.seed.
-    Draw order per (b, kv-head): path parameters, K noise, V, then the Q noise
-    of each q-head of the group in ascending order.
+    Q [B, Hq, Nq, D], K and V [B, Hkv, Nkv, D].  Deterministic in w.seed; each
+    (batch, kv-head) has its own random stream, so kv_heads (a list of
+    (b, j)) may restrict generation to some groups (the rest stay zero).
     """
+    from concurrent.futures import ThreadPoolExecutor
     delta = w.delta if delta is None else delta
-    rng = np.random.default_rng(w.seed)
     B, Hq, Hkv, Nq, Nkv, D = w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D
     G = Hq // Hkv
-    off = Nkv - Nq
-    Q = np.empty((B, Hq, Nq, D), np.float32)
-    K = np.empty((B, Hkv, Nkv, D), np.float32)
-    V = np.empty((B, Hkv, Nkv, D), np.float32)
-    for b in range(B):
-        for j in range(Hkv):
-            if w.mode == "path":
-                amp = rng.standard_normal((N_SINES, D))
-                per = np.exp(rng.uniform(np.log(PERIOD_MIN), np.log(PERIOD_MAX), (N_SINES, D)))
-                ph = rng.uniform(0.0, 2.0 * np.pi, (N_SINES, D))
-                kk = rng.standard_normal((Nkv, D)) / np.sqrt(D)
-                kk += w.a * _path(rng, Nkv, 0, D, amp, per, ph)
-                V[b, j] = round_to(rng.standard_normal((Nkv, D)), w.dtype)
-                cq = w.a * _path(rng, Nq, off, D, amp, per, ph)
-                for i in range(G):
-                    Q[b, j * G + i] = round_to(rng.standard_normal((Nq, D)) / np.sqrt(D) + cq,
-                                               w.dtype)
-            else:
-                kk = rng.standard_normal((Nkv, D))
-                V[b, j] = round_to(rng.standard_normal((Nkv, D)), w.dtype)
-                for i in range(G):
-                    Q[b, j * G + i] = round_to(rng.standard_normal((Nq, D)), w.dtype)
-            if delta != 0.0 and Nkv > 0 and Nq > 0:
-                u = Q[b, j * G:(j + 1) * G].astype(np.float64).reshape(-1, D).mean(axis=0)
-                nu = float(u @ u)
-                if nu > 0:
-                    kk[:SINK_KEYS] += delta * u / (w.scale * nu)
-            K[b, j] = round_to(kk, w.dtype)
+    Q = np.zeros((B, Hq, Nq, D), np.float32)
+    K = np.zeros((B, Hkv, Nkv, D), np.float32)
+    V = np.zeros((B, Hkv, Nkv, D), np.float32)
+    todo = [(b, j) for b in range(B) for j in range(Hkv)] if kv_heads is None else list(kv_heads)
+
+    def one(bj):
+        b, j = bj
+        Q[b, j * G:(j + 1) * G], K[b, j], V[b, j] = _kv_group(w, b, j, delta)
+
+    with ThreadPoolExecutor(max_workers=max(1, min(threads, len(todo)))) as ex:
+        list(ex.map(one, todo))
     return Q, K, V
 
 
