@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark of the adaptive-precision attention prefill hot path on one GPU.
+
+One step = the whole path on one batch of resident synthetic inputs:
+apa_quantize -> apa_pass1 -> apa_pass2 (fused merge).  The default workload
+is the long-context 3B-shaped prefill: B=1, 24 query heads over 8 KV heads,
+head dim 128, 2048 query rows aligned to the tail of 122880 keys, causal, fp16,
+eps = 0.005.  Prints one JSON line (see --help for the flags).
+
+Throughput is effective TFLOP/s: 4*D*(visible (row, key) pairs) per step over
+the step time, the same numerator for APA and the all-exact path.  The
+roofline object is for pass 1 (the dominant kernel): its algorithmic FP4 MFMA
+work per launch over its average launch time, against the dense FP4 peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP4_TFLOPS = 10100.0      # MI355X dense MXFP4
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense FP16
+METRIC = "ms & effective TFLOP/s, causal GQA prefill 2048q×122880k; % of MFMA peak"
+
+
+def visible_pairs(Nq, Nkv, causal=True):
+    if not causal:
+        return Nq * Nkv
+    off = Nkv - Nq
+    r = np.arange(Nq, dtype=np.int64)
+    return int(np.minimum(r + off + 1, Nkv).sum())
+
+
+def cell_counts(hot, Nq, Nkv, causal=True):
+    """Visited (group, tile) cells and their (row, key) pairs at tile
+    granularity, split into hot and cold, from the hot mask [B,Hq,NG,NT]."""
+    NG, NT = hot.shape[-2], hot.shape[-1]
+    off = Nkv - Nq
+    vis = np.zeros((NG, NT), bool)
+    rows = np.zeros(NG, np.int64)
+    for g in range(NG):
+        last = min(16 * g + 15, Nq - 1)
+        d = min(Nkv - 1, last + off) // 64 if causal else NT - 1
+        vis[g, :d + 1] = True
+        rows[g] = last - 16 * g + 1
+    visb = np.broadcast_to(vis, hot.shape)
+    pairs = np.broadcast_to((rows[:, None] * 64) * np.ones(NT, np.int64), hot.shape)
+    cells = int(visb.sum())
+    hot_cells = int((hot & visb).sum())
+    vp = int(pairs[visb].sum())
+    hp = int(pairs[hot & visb].sum())
+    return cells, hot_cells, vp, hp
+
+
+def src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixed_precision_long_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_src, units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(units)
+    if not e or e.get("src_hash") != src_hash(kernel_src):
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, ngroups, threads):
+    """The oracle as it stands, on a bounded sample of row groups of the same
+    workload (pass 1, exact pass 2 and merge; the K/V quantisation it needs is
+    shared by every row of a KV head and is excluded)."""
+    from oracle import oracle as O
+    from mixed_precision_long_amd.inputs import make_inputs
+    rng = np.random.default_rng(123)
+    p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
+    allg = O.all_groups(p)
+    sel = allg[rng.choice(len(allg), ngroups, replace=False)]
+    kvh = sorted({(int(b), int(h) // (w.Hq // w.Hkv)) for b, h, _ in sel})
+    Q, K, V = make_inputs(w, kv_heads=kvh)
+    prep = O.quantize(p, Q, K, V)
+    t0 = time.perf_counter()
+    O.run(p, Q, K, V, prep, groups=sel, nthreads=threads)
+    dt = time.perf_counter() - t0
+    off = w.Nkv - w.Nq
+    flops = 0
+    for _, _, g in sel:
+        for r in range(16 * g, min(16 * g + 16, w.Nq)):
+            flops += 4 * w.D * min(r + off + 1, w.Nkv)
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s (effective)", cores=threads,
+                kind="oracle", seconds=round(dt, 2),
+                sample="%d random 16-row groups of %s (pass 1 + exact pass 2 + merge; "
+                       "K/V quantisation excluded), %d threads" % (ngroups, w.name, threads))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long3b")
+    ap.add_argument("--eps", type=float, default=None)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-exact", action="store_true", help="skip timing the all-exact path")
+    ap.add_argument("--cpu-groups", type=int, default=32)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path is single-GPU by design (it would shard by "
+              "(batch, kv-head) with no exchange); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mixed_precision_long_amd import apa
+    from mixed_precision_long_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    eps = w.eps if args.eps is None else args.eps
+    torch.cuda.set_device(0)
+    print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    Q, K, V = make_inputs(w)
+    dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
+    q = torch.from_numpy(Q).to(dt).cuda()
+    k = torch.from_numpy(K).to(dt).cuda()
+    v = torch.from_numpy(V).to(dt).cuda()
+    del Q, K, V
+    p = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                    dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16, scale=w.scale)
+    bufs = apa.alloc(p)
+    stream = torch.cuda.current_stream()
+
+    ev = {n: [] for n in ("quantize", "pass1", "pass2")}
+
+    def step(record):
+        if record:
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            e[0].record(stream)
+        apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
+        if record:
+            e[1].record(stream)
+        apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
+                  stream)
+        if record:
+            e[2].record(stream)
+        apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
+                  out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
+        if record:
+            e[3].record(stream)
+            ev["quantize"].append((e[0], e[1]))
+            ev["pass1"].append((e[1], e[2]))
+            ev["pass2"].append((e[2], e[3]))
+
+    print("[bench] warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in ev}
+    print("[bench] APA %.3f ms/step %s" % (ms, kern_ms), file=sys.stderr, flush=True)
+
+    flop = 4.0 * w.D * visible_pairs(w.Nq, w.Nkv) * w.Hq * w.B
+    hot = apa_hot_mask(p, bufs.bits)
+    cells, hot_cells, vpairs, hpairs = cell_counts(hot, w.Nq, w.Nkv)
+    cold_pairs = (vpairs - hpairs) * 1.0
+    # pass-1 algorithmic FP4 work per launch: QK on every visited pair, the
+    # one-column row sum, PV on the cold pairs (tile granularity)
+    w4 = 2.0 * w.D * vpairs + 2.0 * vpairs + 2.0 * w.D * cold_pairs
+    w16 = 4.0 * w.D * hpairs
+    p1_tflops = w4 / (kern_ms["pass1"] * 1e-3) / 1e12
+    t_roof_ms = (w4 / (PEAK_FP4_TFLOPS * 1e12) + w16 / (PEAK_FP16_TFLOPS * 1e12)) * 1e3
+    out = bufs.out.float()
+
+    res = {
+        "metric": METRIC,
+        "value": round(flop / (ms * 1e-3) / 1e12, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp4+fp16", "data": "synthetic",
+        "config": {"workload": "%s: B%d Hq%d Hkv%d D%d Nq%d Nkv%d causal %s eps %g" % (
+            w.name, w.B, w.Hq, w.Hkv, w.D, w.Nq, w.Nkv, w.dtype, eps),
+            "global_batch": w.B, "seq_len": w.Nkv, "parallelism": "single-gpu"},
+        "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern_ms.items()},
+        "roofline": {"bound": "mfma", "kernel": "k_pass1",
+                     "achieved": round(p1_tflops, 3), "peak": PEAK_FP4_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(p1_tflops / PEAK_FP4_TFLOPS, 5),
+                     "traffic": traffic_for(["pass1.hip", "apa_device.h"], "k_pass1"),
+                     "algorithmic_fp4_flop_per_launch": w4},
+        "weighted_roofline": {"t_roof_ms": round(t_roof_ms, 4),
+                              "frac": round(t_roof_ms / ms, 4),
+                              "fp4_flop": w4, "fp16_flop": w16},
+        "hot_fraction": {"cells": round(hot_cells / max(cells, 1), 5),
+                         "pairs": round(hpairs / max(vpairs, 1), 5)},
+    }
+
+    if not args.no_exact:
+        eo = torch.empty_like(q)
+        el = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+        for _ in range(args.warmup):
+            apa.exact(p, q, k, v, eo, el, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_ex = max(3, args.steps // 2)
+        for _ in range(n_ex):
+            apa.exact(p, q, k, v, eo, el, stream=stream)
+        torch.cuda.synchronize()
+        ems = (time.perf_counter() - t0) * 1e3 / n_ex
+        ef = eo.float()
+        cos = torch.nn.functional.cosine_similarity(out.reshape(-1, w.D), ef.reshape(-1, w.D), dim=1)
+        res["exact"] = {"ms": round(ems, 4), "tflops": round(flop / (ems * 1e-3) / 1e12, 3),
+                        "fp16_roofline_frac": round(flop / (ems * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+                        "apa_speedup": round(ems / ms, 3)}
+        res["apa_vs_exact"] = {"cos_min": round(float(cos.min()), 6),
+                               "cos_median": round(float(cos.median()), 6),
+                               "max_abs": round(float((out - ef).abs().max()), 5)}
+        print("[bench] exact %.3f ms" % ems, file=sys.stderr, flush=True)
+
+    if w.eps_sweep:
+        sweep = {}
+        for e2 in w.eps_sweep:
+            for _ in range(2):
+                apa.pass1(p, bufs.fp4, e2, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
+                          stream)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(5):
+                step_eps(apa, p, q, k, v, bufs, e2, stream)
+            torch.cuda.synchronize()
+            hot2 = apa_hot_mask(p, bufs.bits)
+            c2, h2, vp2, hp2 = cell_counts(hot2, w.Nq, w.Nkv)
+            sweep[str(e2)] = {"ms": round((time.perf_counter() - t0) * 1e3 / 5, 4),
+                              "hot_cells": round(h2 / max(c2, 1), 5)}
+        res["eps_sweep"] = sweep
+
+    if not args.no_cpu:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        print("[bench] cpu baseline (%d groups, %d threads)" % (args.cpu_groups, threads),
+              file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_groups, threads)
+
+    print(json.dumps(res), flush=True)
+
+
+def step_eps(apa, p, q, k, v, bufs, eps, stream):
+    apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
+    apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None, stream)
+    apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
+              out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
+
+
+def apa_hot_mask(p, bits):
+    import torch
+    torch.cuda.synchronize()
+    NT = -(-p.Nkv // 64)
+    NG = -(-p.Nq // 16)
+    W = -(-NT // 32)
+    wv = bits.cpu().numpy().view(np.uint32)[:p.B * p.Hq * NG * W].reshape(p.B, p.Hq, NG, W)
+    b = (wv[..., None] >> np.arange(32, dtype=np.uint32)) & 1
+    return b.reshape(p.B, p.Hq, NG, W * 32)[..., :NT].astype(bool)
+
+
+if __name__ == "__main__":
+    main()

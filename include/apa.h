@@ -72,20 +72,23 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  * of one 32-element block.
  *   q_codes  [B][Hq][NqP][D/2]       Q along D
  *   q_scales [B][Hq][NqP][D/32]
- *   k_codes  [B][Hkv][NkvP][D/2]     K - kbar along D
- *   k_scales [B][Hkv][NkvP][D/32]
- *   v_codes  [B][Hkv][D][NkvP/2]     V along keys; inside every 32-key block
- *                                    the eight 4-key runs are stored in the
- *                                    order 0,2,4,6,1,3,5,7 (the lane order of
- *                                    the P operand of the P.V product)
- *   v_scales [B][Hkv][D][NkvP/32]
+ *   kv_blobs [B][Hkv][NkvP/64][68*D]  one blob per 64-key tile, in the
+ *            operand order of the pass-1 MFMAs:
+ *              [0, 32D)    K - kbar codes, [64 keys][D/2], along D
+ *              [32D, 34D)  K scales, [64 keys][D/32]
+ *              [34D, 66D)  V codes along keys, [D channels][32]: 16 bytes
+ *                          per 32-key half whose eight 4-key runs are
+ *                          stored in the order 0,2,4,6,1,3,5,7 (the lane
+ *                          order of the P operand of the P.V product)
+ *              [66D, 68D)  V scales, channel 32*db + n and key half hh at
+ *                          byte (2n + hh) * D/32 + db
  *   kbar     [B][Hkv][D] float       per-channel key mean
  *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V, 0, 0
  *   q_head   [B][Hq][4]  float       amax_Q, inv_Q, j (as float: alpha = 2^j), 0
  *   q_frame  [B][Hq][NqP] float      c_r = sl * q.kbar, sl = fl32(scale*log2 e)
  *   status   uint32                  bit 0: a non-finite input was seen      */
 typedef struct apa_fp4_layout {
-  size_t q_codes, q_scales, k_codes, k_scales, v_codes, v_scales;
+  size_t q_codes, q_scales, kv_blobs;
   size_t kbar, kv_head, q_head, q_frame, status, total;
 } apa_fp4_layout;
 

@@ -41,9 +41,8 @@ class Problem(C.Structure):
 
 
 class Fp4Layout(C.Structure):
-    _fields_ = [(k, C.c_size_t) for k in ("q_codes", "q_scales", "k_codes", "k_scales", "v_codes",
-                                          "v_scales", "kbar", "kv_head", "q_head", "q_frame",
-                                          "status", "total")]
+    _fields_ = [(k, C.c_size_t) for k in ("q_codes", "q_scales", "kv_blobs", "kbar", "kv_head",
+                                          "q_head", "q_frame", "status", "total")]
 
 
 _lib = None

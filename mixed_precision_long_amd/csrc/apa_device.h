@@ -84,6 +84,12 @@ __device__ __forceinline__ unsigned cvt_fp4x2(unsigned old, float a, float b, fl
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// IEEE maximum (NaN-propagating).  Unlike fmaxf it needs no canonicalising
+// of MFMA results and lowers to V_MAXIMUM3_F32, two new operands per
+// instruction.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
 // Smallest integer e with a <= 6 * 2^e (a >= 0), clamped to [-127, 127]:
 // with a = f * 2^x, f in [0.5, 1), 6 * 2^(x-3) = 0.75 * 2^x covers a iff f <= 0.75.
 __device__ __forceinline__ int e8m0_exponent(float a) {

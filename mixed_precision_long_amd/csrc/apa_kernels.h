@@ -11,19 +11,30 @@ struct Geom {
   float sl;  // fl32(scale * fl32(log2 e))
 };
 
+// Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the
+// MFMA operands of pass 1:
+//   [0, 32D)     K codes  [64 keys][D/2]
+//   [32D, 34D)   K scales [64 keys][D/32]
+//   [34D, 66D)   V codes  [D channels][32]: 16 bytes per 32-key half, whose
+//                eight 4-key runs are stored in the order 0,2,4,6,1,3,5,7
+//   [66D, 68D)   V scales [32][2][D/32]: channel 32*db + n, key half hh at
+//                byte (2n + hh) * D/32 + db
 struct Fp4Ptrs {
-  uint8_t *q_codes, *q_scales, *k_codes, *k_scales, *v_codes, *v_scales;
+  uint8_t *q_codes, *q_scales, *kv_blob;
   float *kbar, *kv_head, *q_head, *q_frame;
   unsigned* status;
 };
 
+__host__ __device__ inline size_t blob_bytes(int D) { return (size_t)68 * D; }
+
 struct QuantWs {
-  double* ksum;   // [B*Hkv][NT][D]
-  float* kmin;    // [B*Hkv][NT][D]
-  float* kmax;    // [B*Hkv][NT][D]
-  float* vamax;   // [B*Hkv][NT]
+  double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
+  float* kmin;    // [B*Hkv][NCH][D]
+  float* kmax;    // [B*Hkv][NCH][D]
+  float* vamax;   // [B*Hkv][NCH]
   float* qamax;   // [B*Hq][NQT]
   int nqt;        // ceil(Nq / 64)
+  int nch;        // ceil(NT / 16)
 };
 
 struct Pass1Out {

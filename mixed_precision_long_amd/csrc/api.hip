@@ -60,10 +60,7 @@ void layout(const apa_problem* p, apa_fp4_layout* L) {
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   L->q_codes = take(B * Hq * g.NqP * D / 2);
   L->q_scales = take(B * Hq * g.NqP * D / 32);
-  L->k_codes = take(B * Hkv * g.NkvP * D / 2);
-  L->k_scales = take(B * Hkv * g.NkvP * D / 32);
-  L->v_codes = take(B * Hkv * D * g.NkvP / 2);
-  L->v_scales = take(B * Hkv * D * g.NkvP / 32);
+  L->kv_blobs = take(B * Hkv * g.NT * blob_bytes(p->D));
   L->kbar = take(B * Hkv * D * 4);
   L->kv_head = take(B * Hkv * 8 * 4);
   L->q_head = take(B * Hq * 4 * 4);
@@ -78,8 +75,7 @@ Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
   uint8_t* b = (uint8_t*)base;
   Fp4Ptrs f;
   f.q_codes = b + L.q_codes; f.q_scales = b + L.q_scales;
-  f.k_codes = b + L.k_codes; f.k_scales = b + L.k_scales;
-  f.v_codes = b + L.v_codes; f.v_scales = b + L.v_scales;
+  f.kv_blob = b + L.kv_blobs;
   f.kbar = (float*)(b + L.kbar); f.kv_head = (float*)(b + L.kv_head);
   f.q_head = (float*)(b + L.q_head); f.q_frame = (float*)(b + L.q_frame);
   f.status = (unsigned*)(b + L.status);
@@ -88,7 +84,8 @@ Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
 
 size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
   const Geom g = geom(p);
-  const size_t nkv = (size_t)p->B * p->Hkv * g.NT;
+  const int nch = (g.NT + 15) / 16;
+  const size_t nkv = (size_t)p->B * p->Hkv * nch;
   const int nqt = (p->Nq + 63) / 64;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
@@ -98,6 +95,7 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
     uint8_t* bb = (uint8_t*)base;
     ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
     ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e); ws->nqt = nqt;
+    ws->nch = nch;
   }
   return o;
 }

@@ -186,10 +186,10 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
             if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) s = -__builtin_inff();
           }
           acc[kb][j] = s;
-          tmax = fmaxf(tmax, s);
+          tmax = vmax(tmax, s);
         }
-      tmax = fmaxf(tmax, xor32(tmax));
-      const float mnew = fmaxf(m, tmax);
+      tmax = vmax(tmax, xor32(tmax));
+      const float mnew = vmax(m, tmax);
       if (__ballot(mnew > m) != 0ull) {
         const float alpha = (mnew > m) ? fast_exp2(m - mnew) : 1.0f;  // m=-inf -> 0
 #pragma unroll

@@ -33,34 +33,77 @@ __device__ float block_max(float v, float* red) {
   return r;
 }
 
-// Per (b, kv-head, 64-key tile): per-channel FP64 sum (ascending keys), min
-// and max of K; max |V| over the tile.  grid (NT, B*Hkv), block D.
+// Per (b, kv-head, chunk of 16 tiles of 64 keys): per-channel FP64 sums in a
+// fixed order (keys ascending inside a tile, the chunk's tile sums
+// ascending), min and max of K, and max |V|.  Thread (tile tt, channel group
+// cg) owns 8 consecutive channels of one tile (16-byte loads).
+// grid (NCH, B*Hkv), block 2*D.
 template <typename T>
 __global__ void k_kv_stats(const T* __restrict__ K, const T* __restrict__ V, Geom g, QuantWs ws,
                            unsigned* status) {
-  __shared__ float red[8];
-  const int d = threadIdx.x, t = blockIdx.x, bh = blockIdx.y;
-  const size_t base = ((size_t)bh * g.Nkv) * g.D;
-  const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
-  double s = 0.0;
-  float mn = __builtin_inff(), mx = -__builtin_inff(), va = 0.0f;
+  extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
+  __shared__ float red[16];
+  const int D = g.D, ncg = D / 8;
+  const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
+  const int ch = blockIdx.x, bh = blockIdx.y;
+  const int t = ch * 16 + tt;
+  const size_t base = (size_t)bh * g.Nkv * D + cg * 8;
+  double s[8];
+  float mn[8], mx[8];
+  float va = 0.0f;
   bool bad = false;
-  for (int k = k0; k < k1; ++k) {
-    float x = to_f32<T>(K[base + (size_t)k * g.D + d]);
-    float y = to_f32<T>(V[base + (size_t)k * g.D + d]);
-    bad |= !__builtin_isfinite(x) || !__builtin_isfinite(y);
-    s += (double)x;
-    mn = fminf(mn, x);
-    mx = fmaxf(mx, x);
-    va = fmaxf(va, fabsf(y));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+  if (t < g.NT) {
+    const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
+    for (int k = k0; k < k1; ++k) {
+      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)k * D);
+      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)k * D);
+      const T* ek = reinterpret_cast<const T*>(&rk);
+      const T* evv = reinterpret_cast<const T*>(&rv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float x = to_f32<T>(ek[i]), y = to_f32<T>(evv[i]);
+        bad |= !__builtin_isfinite(x) || !__builtin_isfinite(y);
+        s[i] += (double)x;
+        mn[i] = fminf(mn[i], x);
+        mx[i] = fmaxf(mx[i], x);
+        va = fmaxf(va, fabsf(y));
+      }
+    }
   }
-  const size_t o = ((size_t)bh * g.NT + t) * g.D + d;
-  ws.ksum[o] = s;
-  ws.kmin[o] = mn;
-  ws.kmax[o] = mx;
   if (bad) atomicOr(status, 1u);
-  float m = block_max(va, red);
-  if (d == 0) ws.vamax[(size_t)bh * g.NT + t] = m;
+  double* ssum = sh;
+  float* smn = reinterpret_cast<float*>(sh + 16 * D);
+  float* smx = smn + 16 * D;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ssum[tt * D + cg * 8 + i] = s[i];
+    smn[tt * D + cg * 8 + i] = mn[i];
+    smx[tt * D + cg * 8 + i] = mx[i];
+  }
+  // block max of |V|
+  for (int o = 32; o >= 1; o >>= 1) va = fmaxf(va, __shfl_xor(va, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = va;
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    double c = 0.0;
+    float a = __builtin_inff(), b = -__builtin_inff();
+    for (int i = 0; i < 16; ++i) {  // the chunk's tile sums, ascending
+      c += ssum[i * D + d];
+      a = fminf(a, smn[i * D + d]);
+      b = fmaxf(b, smx[i * D + d]);
+    }
+    const size_t o = ((size_t)bh * ws.nch + ch) * D + d;
+    ws.ksum[o] = c;
+    ws.kmin[o] = a;
+    ws.kmax[o] = b;
+  }
+  if (threadIdx.x == 0) {
+    float m = red[0];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
+    ws.vamax[(size_t)bh * ws.nch + ch] = m;
+  }
 }
 
 // max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq), block D.
@@ -97,8 +140,8 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
   const int d = threadIdx.x, bh = blockIdx.x;
   double s = 0.0;
   float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int t = 0; t < g.NT; ++t) {  // tile sums in ascending tile order
-    const size_t o = ((size_t)bh * g.NT + t) * g.D + d;
+  for (int c = 0; c < ws.nch; ++c) {  // chunk sums in ascending order
+    const size_t o = ((size_t)bh * ws.nch + c) * g.D + d;
     s += ws.ksum[o];
     mn = fminf(mn, ws.kmin[o]);
     mx = fmaxf(mx, ws.kmax[o]);
@@ -109,7 +152,7 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
   if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
   const float amax_k = block_max(dev, red);
   float va = 0.0f;
-  for (int t = d; t < g.NT; t += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * g.NT + t]);
+  for (int c = d; c < ws.nch; c += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
   const float amax_v = block_max(va, red);
   float gk, ik, gv, iv;
   head_scale(amax_k, &gk, &ik);
@@ -199,11 +242,18 @@ __global__ void k_quant_rows(const T* __restrict__ X, Geom g, Fp4Ptrs f) {
   w = cvt_fp4x2(w, x[2], x[3], s, 1);
   w = cvt_fp4x2(w, x[4], x[5], s, 2);
   w = cvt_fp4x2(w, x[6], x[7], s, 3);
-  uint8_t* codes = IS_Q ? f.q_codes : f.k_codes;
-  uint8_t* scales = IS_Q ? f.q_scales : f.k_scales;
   const size_t r = (size_t)bh * NP + row;
-  *reinterpret_cast<unsigned*>(codes + r * (g.D / 2) + c8 / 2) = w;
-  if ((c8 & 31) == 0) scales[r * (g.D / 32) + c8 / 32] = (uint8_t)(e + 127);
+  uint8_t *crow, *srow;
+  if (IS_Q) {
+    crow = f.q_codes + r * (g.D / 2);
+    srow = f.q_scales + r * (g.D / 32);
+  } else {
+    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NT + row / kTile) * blob_bytes(g.D);
+    crow = blob + (row % kTile) * (g.D / 2);
+    srow = blob + 32 * g.D + (row % kTile) * (g.D / 32);
+  }
+  *reinterpret_cast<unsigned*>(crow + c8 / 2) = w;
+  if ((c8 & 31) == 0) srow[c8 / 32] = (uint8_t)(e + 127);
   if (IS_Q) {
     // row reduction of the frame constant over the D/8 threads of the row
     for (int o = 1; o < tpr; o <<= 1) cdot += __shfl_xor(cdot, o);
@@ -217,46 +267,52 @@ __global__ void k_quant_rows(const T* __restrict__ X, Geom g, Fp4Ptrs f) {
 // with its eight 4-key runs in the order 0,2,4,6,1,3,5,7.
 template <typename T>
 __global__ void k_quant_vt(const T* __restrict__ V, Geom g, Fp4Ptrs f) {
-  constexpr int CH = 128, PAD = 2;
-  __shared__ float tile[kTile][CH + PAD];
+  constexpr int CH = 128, PADH = 8;
+  __shared__ T tile[kTile][CH + PADH];
   const int t = blockIdx.x, bh = blockIdx.y, c0 = blockIdx.z * CH;
   const int nch = min(CH, g.D - c0);
-  const int hk = bh % g.Hkv;
-  (void)hk;
   const float inv = f.kv_head[(size_t)bh * 8 + 5];
   const int k0 = t * kTile;
-  // stage: element (key, ch) as float, zero for padding keys
-  for (int i = threadIdx.x; i < kTile * nch; i += blockDim.x) {
-    const int kk = i / nch, c = i % nch;
+  // stage the raw tile, 8 values per 16-byte load; zeros for padding keys
+  const int per_row = nch / 8;
+  for (int i = threadIdx.x; i < kTile * per_row; i += blockDim.x) {
+    const int kk = i / per_row, c = (i % per_row) * 8;
     const int key = k0 + kk;
-    float v = 0.0f;
-    if (key < g.Nkv) v = to_f32<T>(V[((size_t)bh * g.Nkv + key) * g.D + c0 + c]);
-    float n = v * inv;
-    tile[kk][c] = fminf(fmaxf(n, -6.0f), 6.0f);
+    uint4 r = {0u, 0u, 0u, 0u};
+    if (key < g.Nkv) r = *reinterpret_cast<const uint4*>(V + ((size_t)bh * g.Nkv + key) * g.D + c0 + c);
+    *reinterpret_cast<uint4*>(&tile[kk][c]) = r;
   }
   __syncthreads();
   const int c = threadIdx.x % CH, half = threadIdx.x / CH;
   if (c >= nch || half >= 2) return;
+  float x[32];
   float a = 0.0f;
-  for (int i = 0; i < 32; ++i) a = fmaxf(a, fabsf(tile[half * 32 + i][c]));
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float n = to_f32<T>(tile[half * 32 + i][c]) * inv;
+    x[i] = fminf(fmaxf(n, -6.0f), 6.0f);
+    a = fmaxf(a, fabsf(x[i]));
+  }
   const int e = e8m0_exponent(a);
   const float s = pow2_scale(e);
   // dword j holds runs perm[2j], perm[2j+1]; run q covers keys 4q..4q+3
-  const int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
   unsigned out[4];
+#pragma unroll
   for (int j = 0; j < 4; ++j) {
     unsigned w = 0;
-    const int ra = perm[2 * j] * 4 + half * 32, rb = perm[2 * j + 1] * 4 + half * 32;
-    w = cvt_fp4x2(w, tile[ra + 0][c], tile[ra + 1][c], s, 0);
-    w = cvt_fp4x2(w, tile[ra + 2][c], tile[ra + 3][c], s, 1);
-    w = cvt_fp4x2(w, tile[rb + 0][c], tile[rb + 1][c], s, 2);
-    w = cvt_fp4x2(w, tile[rb + 2][c], tile[rb + 3][c], s, 3);
+    const int ra = perm[2 * j] * 4, rb = perm[2 * j + 1] * 4;
+    w = cvt_fp4x2(w, x[ra + 0], x[ra + 1], s, 0);
+    w = cvt_fp4x2(w, x[ra + 2], x[ra + 3], s, 1);
+    w = cvt_fp4x2(w, x[rb + 0], x[rb + 1], s, 2);
+    w = cvt_fp4x2(w, x[rb + 2], x[rb + 3], s, 3);
     out[j] = w;
   }
-  const size_t row = (size_t)bh * g.D + c0 + c;
+  const int ch = c0 + c;
+  uint8_t* blob = f.kv_blob + ((size_t)bh * g.NT + t) * blob_bytes(g.D);
   uint4 o4 = {out[0], out[1], out[2], out[3]};
-  *reinterpret_cast<uint4*>(f.v_codes + row * (g.NkvP / 2) + t * 32 + half * 16) = o4;
-  f.v_scales[row * (g.NkvP / 32) + t * 2 + half] = (uint8_t)(e + 127);
+  *reinterpret_cast<uint4*>(blob + 34 * g.D + ch * 32 + half * 16) = o4;
+  blob[66 * g.D + ((ch % 32) * 2 + half) * (g.D / 32) + ch / 32] = (uint8_t)(e + 127);
 }
 
 template <typename T>
@@ -264,8 +320,8 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
                         const QuantWs& ws, hipStream_t s) {
   hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, f.status);
   if (g.Nkv > 0)
-    hipLaunchKernelGGL(k_kv_stats<T>, dim3(g.NT, g.B * g.Hkv), dim3(g.D), 0, s, k, v, g, ws,
-                       f.status);
+    hipLaunchKernelGGL(k_kv_stats<T>, dim3(ws.nch, g.B * g.Hkv), dim3(2 * g.D),
+                       16 * g.D * (sizeof(double) + 2 * sizeof(float)), s, k, v, g, ws, f.status);
   if (g.Nq > 0)
     hipLaunchKernelGGL(k_q_stats<T>, dim3(ws.nqt, g.B * g.Hq), dim3(g.D), 0, s, q, g, ws,
                        f.status);

@@ -151,9 +151,12 @@ static int p_group_exp(double ymax) {
 /* a1: statistics                                                            */
 /* ------------------------------------------------------------------------ */
 
-/* Per-channel key mean of one (b, kv-head): the FP64 sum runs ascending over
- * the keys of each 64-key tile, then over the tile sums in ascending tile
- * order; k̄ = fl32(sum / Nkv) with the division in FP64.  Also the per-channel
+/* Per-channel key mean of one (b, kv-head): the FP64 sum runs in a fixed
+ * three-level order -- keys ascending inside each 64-key tile, tile sums
+ * ascending inside each chunk of 16 tiles, chunk sums ascending ("All
+ * reductions run in a fixed order", 'What else is in the box'); for fp16 keys
+ * of ordinary magnitude every partial sum is exact, so the order only matters
+ * for extreme inputs.  k̄ = fl32(sum / Nkv) with the division in FP64.  Also the per-channel
  * min and max, and amax_K = max over channels of
  * max(fl32(max_k K - k̄), fl32(k̄ - min_k K)) -- the largest |K - k̄| over the
  * head, exact because rounding is monotone. (Pass 1, "Mean-centred K".) */
@@ -162,15 +165,19 @@ void orc_key_stats(const float* K, int Nkv, int D, int tile, float* kbar, float*
   for (int d = 0; d < D; ++d) {
     double total = 0.0;
     float mn = INFINITY, mx = -INFINITY;
-    for (int t0 = 0; t0 < Nkv; t0 += tile) {
-      double part = 0.0;
-      for (int k = t0; k < Nkv && k < t0 + tile; ++k) {
-        float x = K[(size_t)k * D + d];
-        part += (double)x;
-        if (x < mn) mn = x;
-        if (x > mx) mx = x;
+    for (int c0 = 0; c0 < Nkv; c0 += 16 * tile) {
+      double chunk = 0.0;
+      for (int t0 = c0; t0 < Nkv && t0 < c0 + 16 * tile; t0 += tile) {
+        double part = 0.0;
+        for (int k = t0; k < Nkv && k < t0 + tile; ++k) {
+          float x = K[(size_t)k * D + d];
+          part += (double)x;
+          if (x < mn) mn = x;
+          if (x > mx) mx = x;
+        }
+        chunk += part;
       }
-      total += part;
+      total += chunk;
     }
     float kb = Nkv > 0 ? (float)(total / (double)Nkv) : 0.0f;
     kbar[d] = kb;

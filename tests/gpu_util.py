@@ -45,6 +45,19 @@ def unpermute_v(vcodes_gpu: np.ndarray) -> np.ndarray:
     return pack(canon.reshape(sh))
 
 
+def unblob(blobs: np.ndarray, D: int, Nkv: int) -> dict:
+    """Per-tile blobs [B, Hkv, NT, 68 D] -> canonical K codes/scales [B, Hkv, Nkv, .]
+    and V^T codes/scales [B, Hkv, D, NkvP/.]."""
+    B, Hkv, NT, _ = blobs.shape
+    kc = blobs[..., :32 * D].reshape(B, Hkv, NT * 64, D // 2)[:, :, :Nkv]
+    ks = blobs[..., 32 * D:34 * D].reshape(B, Hkv, NT * 64, D // 32)[:, :, :Nkv]
+    vcb = blobs[..., 34 * D:66 * D].reshape(B, Hkv, NT, D, 32)          # [.., t, ch, 32 B]
+    vc = unpermute_v(np.ascontiguousarray(vcb.transpose(0, 1, 3, 2, 4)).reshape(B, Hkv, D, NT * 32))
+    vsb = blobs[..., 66 * D:68 * D].reshape(B, Hkv, NT, 32, 2, D // 32)  # [.., t, n, hh, db]
+    vs = np.ascontiguousarray(vsb.transpose(0, 1, 5, 3, 2, 4)).reshape(B, Hkv, D, NT * 2)
+    return dict(kc=kc, ks=ks, vc=vc, vs=vs)
+
+
 def fp4_sections(p, fp4_host: np.ndarray) -> dict:
     L = apa.fp4_layout(p)
     B, Hq, Hkv, Nq, Nkv, D = p.B, p.Hq, p.Hkv, p.Nq, p.Nkv, p.D
@@ -58,10 +71,8 @@ def fp4_sections(p, fp4_host: np.ndarray) -> dict:
     return dict(
         qc=sec(L.q_codes, B * Hq * NqP * D // 2, np.uint8, (B, Hq, NqP, D // 2))[:, :, :Nq],
         qs=sec(L.q_scales, B * Hq * NqP * D // 32, np.uint8, (B, Hq, NqP, D // 32))[:, :, :Nq],
-        kc=sec(L.k_codes, B * Hkv * NkvP * D // 2, np.uint8, (B, Hkv, NkvP, D // 2))[:, :, :Nkv],
-        ks=sec(L.k_scales, B * Hkv * NkvP * D // 32, np.uint8, (B, Hkv, NkvP, D // 32))[:, :, :Nkv],
-        vc=unpermute_v(sec(L.v_codes, B * Hkv * D * NkvP // 2, np.uint8, (B, Hkv, D, NkvP // 2))),
-        vs=sec(L.v_scales, B * Hkv * D * NkvP // 32, np.uint8, (B, Hkv, D, NkvP // 32)),
+        **unblob(sec(L.kv_blobs, B * Hkv * (NkvP // 64) * 68 * D, np.uint8,
+                     (B, Hkv, NkvP // 64, 68 * D)), D, Nkv),
         kbar=sec(L.kbar, B * Hkv * D, np.float32, (B, Hkv, D)),
         kv_head=sec(L.kv_head, B * Hkv * 8, np.float32, (B, Hkv, 8)),
         q_head=sec(L.q_head, B * Hq * 4, np.float32, (B, Hq, 4)),
