@@ -1,0 +1,141 @@
+"""The C ABI without a GPU: the library loads, exports every function
+include/apa.h declares, and validates its arguments (status codes, size
+queries) before anything would be enqueued."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+from mixed_precision_long_amd import apa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "apa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(apa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 11
+    L = apa.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(apa.EXPORTS)
+
+
+def test_status_strings():
+    for code in range(5):
+        s = apa.status_string(code)
+        assert s.startswith("APA_")
+    assert "unknown" in apa.status_string(99)
+
+
+def prob(**kw):
+    p = apa.problem(1, 24, 8, 2048, 122880, 128)
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_sizes_and_layout():
+    p = prob()
+    L = apa.fp4_layout(p)
+    offs = [L.q_codes, L.q_scales, L.kv_blobs, L.kbar, L.kv_head, L.q_head, L.q_frame, L.status,
+            L.total]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert L.kv_blobs - L.q_scales >= 24 * 2048 * 4
+    # one 68*D-byte blob per 64-key tile and kv-head: 8704 B at D = 128
+    assert L.kbar - L.kv_blobs == 8 * 1920 * 8704
+    assert apa.fp4_bytes(p) == L.total
+    assert apa.hotmask_bytes(p) == 24 * 128 * 60 * 4
+    assert apa.workspace_bytes(p, apa.CALL_PASS1) == 0
+    assert apa.workspace_bytes(p, apa.CALL_QUANTIZE) > 0
+    assert apa.workspace_bytes(p, apa.CALL_PASS2) > 0
+    # ragged shapes round up
+    q = prob(Nq=100, Nkv=700)
+    assert apa.hotmask_bytes(q) == 24 * 7 * 1 * 4
+
+
+@pytest.mark.parametrize("field,value", [
+    ("Hkv", 5), ("D", 96), ("tile", 32), ("row_group", 8), ("Nkv", 1000), ("dtype", 7),
+    ("is_causal", 2), ("tau", -1.0), ("hot_frame_offset", 2.5), ("hot_frame_offset", 200.0),
+    ("scale", float("nan")), ("fmt", 9)])
+def test_invalid_problems_are_rejected(field, value):
+    p = prob(**{field: value})
+    assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_INVALID_ARG
+    assert apa.fp4_bytes(p) == 0
+
+
+def test_null_pointers_and_bad_arguments():
+    L = apa.lib()
+    p = prob()
+    assert L.apa_quantize(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == apa.APA_ERR_INVALID_ARG
+    assert L.apa_quantize(C.byref(p), None, FAKE, FAKE, FAKE, FAKE, 1, None) == apa.APA_ERR_INVALID_ARG
+    assert L.apa_pass1(C.byref(p), FAKE, 0.01, None, FAKE, FAKE, FAKE, None, None) == \
+        apa.APA_ERR_INVALID_ARG
+    for eps in (float("nan"), -0.1):
+        assert L.apa_pass1(C.byref(p), FAKE, eps, FAKE, FAKE, FAKE, FAKE, None, None) == \
+            apa.APA_ERR_INVALID_ARG
+    # pass 2: fuse flag, and the pointers each mode needs
+    args = [FAKE] * 8
+    assert L.apa_pass2(C.byref(p), *args, 2, FAKE, None, None, None, None, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_INVALID_ARG
+    assert L.apa_pass2(C.byref(p), *args, 1, None, None, None, None, None, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_INVALID_ARG
+    assert L.apa_pass2(C.byref(p), *args, 0, None, None, None, None, None, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_INVALID_ARG
+    assert L.apa_merge(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None) == \
+        apa.APA_ERR_INVALID_ARG
+    assert L.apa_exact(C.byref(p), FAKE, FAKE, None, FAKE, None, None, 0, None) == \
+        apa.APA_ERR_INVALID_ARG
+
+
+def test_workspace_too_small():
+    L = apa.lib()
+    p = prob()
+    need = apa.workspace_bytes(p, apa.CALL_QUANTIZE)
+    assert L.apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        apa.APA_ERR_WORKSPACE
+    assert L.apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, need, None) == \
+        apa.APA_ERR_WORKSPACE
+    need2 = apa.workspace_bytes(p, apa.CALL_PASS2)
+    assert L.apa_pass2(C.byref(p), *([FAKE] * 8), 1, FAKE, None, None, None, None, FAKE, need2 - 1,
+                       None) == apa.APA_ERR_WORKSPACE
+
+
+def test_unsupported_variants_say_so():
+    L = apa.lib()
+    nv = prob(fmt=apa.APA_NVFP4)
+    assert L.apa_quantize(C.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_UNSUPPORTED
+    d512 = prob(D=512)
+    assert L.apa_pass1(C.byref(d512), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        apa.APA_ERR_UNSUPPORTED
+    g5 = prob(Hq=40)  # group of 5 query heads
+    assert L.apa_exact(C.byref(g5), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == \
+        apa.APA_ERR_UNSUPPORTED
+
+
+def test_empty_problems_do_nothing():
+    L = apa.lib()
+    for kw in ({"Nq": 0}, {"B": 0}):
+        p = prob(**kw)
+        assert L.apa_pass1(C.byref(p), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None) == apa.APA_OK
+        assert L.apa_exact(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == apa.APA_OK
+        assert L.apa_merge(C.byref(p), *([FAKE] * 8), None, None) == apa.APA_OK
+        assert L.apa_pass2(C.byref(p), *([FAKE] * 8), 1, FAKE, None, None, None, None, FAKE, 1 << 40,
+                           None) == apa.APA_OK
+
+
+def test_problem_defaults():
+    p = apa.problem(2, 8, 2, 16, 64, 64)
+    assert (p.tile, p.row_group, p.tau, p.hot_frame_offset, p.is_causal) == (64, 16, 4.0, 32.0, 1)
+    assert p.scale == 0.0 and p.fmt == apa.APA_MXFP4 and p.dtype == apa.APA_F16
+    assert math.isfinite(p.tau)
