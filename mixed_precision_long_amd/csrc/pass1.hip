@@ -109,7 +109,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const int lane = threadIdx.x & 63;
   const int n = lane & 31;       // the wave's row handled by this lane
   const int hh = lane >> 5;      // which half of the K dimension this lane feeds
-  const int unit = xcd_remap(blockIdx.x, gridDim.x) * kWaves + (threadIdx.x >> 6);
+  // the wave index is wave-uniform: keep everything derived from it in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int unit = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (unit >= nunits) return;
 
   // unit -> (b, kv-head, 32-row block, head in group), heads innermost
@@ -172,9 +174,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
   // and K of tile it+2 is fetched into kn
   KOps<D> kn;
   v16f acc[2];
+  // (prefetches past the last tile re-read the last tile: in bounds, unused)
+  auto next_blob = [&](int it) { return blobs + (size_t)tile_of(min(it, ntiles - 1)) * BLOB; };
   load_k<D>(kn, blobs, n, hh);
   qk<D>(acc, kn, qa, qs, hh);
-  if (ntiles > 1) load_k<D>(kn, blobs + (size_t)tile_of(1) * BLOB, n, hh);
+  load_k<D>(kn, next_blob(1), n, hh);
 
   for (int it = 0; it < ntiles; ++it) {
     const int t = tile_of(it);
@@ -275,11 +279,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 
     const v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
     const v16f ones_acc = mfma_fp4(ones, pb, v16f{}, kE8M0One, pscale);
     // this tile's scores are consumed: the next tile's go to the matrix cores
-    // now and run during the vote and the P V product
-    if (it + 1 < ntiles) {
-      qk<D>(acc, kn, qa, qs, hh);
-      if (it + 2 < ntiles) load_k<D>(kn, blobs + (size_t)tile_of(it + 2) * BLOB, n, hh);
-    }
+    // behind the row sum and run during the vote and the P V product
+    __builtin_amdgcn_sched_barrier(0);
+    qk<D>(acc, kn, qa, qs, hh);
+    load_k<D>(kn, next_blob(it + 2), n, hh);
     const float ell = ones_acc[0];
 
     // ---- step 4: the hot test (lambda includes this tile)
