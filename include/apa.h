@@ -55,9 +55,10 @@ typedef struct apa_problem {
   int32_t tile;                   /* keys per tile; must be 64 ("tiles of 64")  */
   int32_t row_group;              /* rows per hot verdict; must be 16            */
   int32_t fmt;                    /* APA_MXFP4 (NVFP4 exists only in the oracle) */
-  float tau;                      /* lazy-max threshold in log2 units (4), >= 0  */
+  float tau;                      /* lazy-max threshold in log2 units, in [0, 32]
+                                     (4)                                         */
   float hot_frame_offset;         /* H: a hot tile lifts the frame to at most
-                                     max(m, c - H); an integer in [0, 126] (32) */
+                                     max(m, c - H); an integer in [0, 64] (32)  */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,

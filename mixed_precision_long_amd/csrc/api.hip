@@ -26,9 +26,9 @@ bool valid_problem(const apa_problem* p) {
   if (p->is_causal && p->Nkv < p->Nq) return false;
   if (p->tile != 64 || p->row_group != 16) return false;
   if (p->fmt != APA_MXFP4 && p->fmt != APA_NVFP4) return false;
-  if (!(p->tau >= 0.0f) || !isfinite(p->tau)) return false;
+  if (!(p->tau >= 0.0f && p->tau <= 32.0f)) return false;
   const float H = p->hot_frame_offset;
-  if (!(H >= 0.0f && H <= 126.0f) || floorf(H) != H) return false;
+  if (!(H >= 0.0f && H <= 64.0f) || floorf(H) != H) return false;
   if (isnan(p->scale)) return false;
   if (p->Nq > 0 && p->Nkv == 0) return false;
   return true;

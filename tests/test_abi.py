@@ -64,7 +64,8 @@ def test_sizes_and_layout():
 
 @pytest.mark.parametrize("field,value", [
     ("Hkv", 5), ("D", 96), ("tile", 32), ("row_group", 8), ("Nkv", 1000), ("dtype", 7),
-    ("is_causal", 2), ("tau", -1.0), ("hot_frame_offset", 2.5), ("hot_frame_offset", 200.0),
+    ("is_causal", 2), ("tau", -1.0), ("tau", 40.0), ("hot_frame_offset", 2.5),
+    ("hot_frame_offset", 65.0),
     ("scale", float("nan")), ("fmt", 9)])
 def test_invalid_problems_are_rejected(field, value):
     p = prob(**{field: value})
