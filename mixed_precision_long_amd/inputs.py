@@ -119,9 +119,12 @@ def _kv_group(w: Workload, b: int, j: int, delta: float):
         per = np.exp(rng.uniform(np.log(PERIOD_MIN), np.log(PERIOD_MAX), (N_SINES, D)))
         ph = rng.uniform(0.0, 2.0 * np.pi, (N_SINES, D))
         kk = rng.standard_normal((Nkv, D)) / np.sqrt(D)
-        kk += w.a * _path(rng, Nkv, 0, D, amp, per, ph)
+        ck = _path(rng, Nkv, 0, D, amp, per, ph)
+        kk += w.a * ck
         Vj = round_to(rng.standard_normal((Nkv, D)), w.dtype)
-        cq = w.a * _path(rng, Nq, off, D, amp, per, ph)
+        # query positions off .. Nkv-1 are key positions: same path values
+        cq = w.a * ck[off:off + Nq]
+        del ck
         for i in range(G):
             Qg[i] = round_to(rng.standard_normal((Nq, D)) / np.sqrt(D) + cq, w.dtype)
     else:

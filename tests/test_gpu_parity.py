@@ -150,9 +150,10 @@ def test_deterministic_reruns():
             assert np.array_equal(np.nan_to_num(r[k]), np.nan_to_num(runs[0][k])), k
 
 
-def _sampled(name, ngroups, seed=0):
+def _sampled(name, ngroups, seed=0, delta=None):
     w = WORKLOADS[name]
-    Q, K, V = make_inputs(w)
+    print("[%s] generating inputs (delta %s)" % (name, delta), flush=True)
+    Q, K, V = make_inputs(w, delta=delta, threads=16)
     po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
     g = run_gpu(problem_for(w), Q, K, V, w.eps, lam=False)
     rng = np.random.default_rng(seed)
@@ -174,3 +175,24 @@ def test_short3b_sampled_groups():
 
 def test_long3b_sampled_groups():
     _sampled("long3b", 6)
+
+
+def test_full32k_sampled_groups():
+    """Full causal prefill 32768 x 32768 (32 query heads over 8), the
+    strongest sink of its sweep, at full size on sampled row groups."""
+    _sampled("full32k", 8, delta=12.0)
+
+
+@pytest.mark.parametrize("delta", [0.0, 4.0, 8.0, 12.0])
+def test_full_causal_sink_sweep(delta):
+    """The sink-strength sweep of the full causal workload, at 1024 x 1024
+    with the same head layout, every row group checked."""
+    w = small_workload(1, 32, 8, 1024, 1024, 128, delta=delta, seed=4)
+    Q, K, V = make_inputs(w)
+    po = oracle_for(w, w.eps, 1)
+    prep = O.quantize(po, Q, K, V)
+    r = O.run(po, Q, K, V, prep)
+    g = run_gpu(problem_for(w), Q, K, V, w.eps)
+    check_quant(g, prep)
+    check_mask(g["hot"], r)
+    check_output(g["out"], r["O"])
