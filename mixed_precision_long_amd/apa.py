@@ -159,6 +159,13 @@ def merge(p: Problem, fp4, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, out, lse
 
 
 def exact(p: Problem, q, k, v, out, lse=None, ws=None, stream=None):
+    """All-exact 16-bit attention.  ws: workspace of workspace_bytes(p,
+    CALL_EXACT) bytes (allocated here as a torch tensor when not given)."""
+    if ws is None:
+        need = workspace_bytes(p, CALL_EXACT)
+        if need > 0:
+            import torch
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check(lib().apa_exact(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(ws),
                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
            "apa_exact")
@@ -170,6 +177,7 @@ class Buffers:
     fp4: object
     ws_q: object
     ws_p2: object
+    ws_ex: object
     cold_m: object
     cold_l: object
     cold_o: object
@@ -189,7 +197,7 @@ def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
     odt = torch.float16 if p.dtype == APA_F16 else torch.bfloat16
     return Buffers(
         fp4=u8(fp4_bytes(p)), ws_q=u8(workspace_bytes(p, CALL_QUANTIZE)),
-        ws_p2=u8(workspace_bytes(p, CALL_PASS2)),
+        ws_p2=u8(workspace_bytes(p, CALL_PASS2)), ws_ex=u8(workspace_bytes(p, CALL_EXACT)),
         cold_m=torch.empty((B, Hq, Nq), dtype=torch.int32, device=device),
         cold_l=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device),
         cold_o=torch.empty((B, Hq, Nq, D), dtype=torch.float32, device=device),

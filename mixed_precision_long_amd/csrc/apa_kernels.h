@@ -62,13 +62,20 @@ struct Pass2Args {
   int32_t* list_tiles;   // [units][NT]
   uint32_t* list_masks;  // [units][NT]
   int32_t* list_count;   // [units]
+  // split states when a unit's keys run as S work groups: [S][rows] and
+  // [S][rows][D] (rows = B*Hq*Nq)
+  float *part_m, *part_l, *part_o;
 };
+// Query positions per work group of the 16-bit attention kernels, and the
+// number of key splits they use for a problem.
+int attn_positions(int D);
+int attn_splits(const Geom& g);
 hipError_t launch_pass2(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a, hipStream_t s);
 hipError_t launch_merge(const Geom& g, const Fp4Ptrs& f, const int32_t* cold_m,
                         const float* cold_l, const float* cold_o, const float* hot_m,
                         const float* hot_l, const float* hot_o, void* out, float* lse,
                         hipStream_t s);
 hipError_t launch_exact(const Geom& g, const void* q, const void* k, const void* v, void* out,
-                        float* lse, hipStream_t s);
+                        float* lse, const Pass2Args& parts, hipStream_t s);
 
 }  // namespace apa

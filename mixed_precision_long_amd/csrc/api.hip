@@ -94,15 +94,32 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
   if (ws && base) {
     uint8_t* bb = (uint8_t*)base;
     ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
-    ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e); ws->nqt = nqt;
+    ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e);
+    ws->nqt = nqt;
     ws->nch = nch;
+  }
+  return o;
+}
+
+// Split states of the 16-bit attention kernels (none when one split suffices).
+size_t split_ws(const apa_problem* p, size_t o, Pass2Args* a, void* base) {
+  const Geom g = geom(p);
+  const int S = attn_splits(g);
+  if (S <= 1) return o;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t rows = (size_t)p->B * p->Hq * p->Nq;
+  const size_t m = take(S * rows * 4), l = take(S * rows * 4), po = take(S * rows * p->D * 4);
+  if (a && base) {
+    uint8_t* bb = (uint8_t*)base;
+    a->part_m = (float*)(bb + m); a->part_l = (float*)(bb + l); a->part_o = (float*)(bb + po);
   }
   return o;
 }
 
 size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
   const Geom g = geom(p);
-  const size_t units = (size_t)p->B * p->Hkv * ((p->Nq + 63) / 64);
+  const int pos = attn_positions(p->D);
+  const size_t units = (size_t)p->B * p->Hkv * ((p->Nq + pos - 1) / pos);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   const size_t t = take(units * g.NT * 4), m = take(units * g.NT * 4), c = take(units * 4);
@@ -111,16 +128,17 @@ size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
     a->list_tiles = (int32_t*)(bb + t); a->list_masks = (uint32_t*)(bb + m);
     a->list_count = (int32_t*)(bb + c);
   }
-  return o;
+  return split_ws(p, o, a, base);
+}
+
+size_t exact_ws(const apa_problem* p, Pass2Args* a, void* base) {
+  return split_ws(p, 0, a, base);
 }
 
 // D and dtype the device kernels implement for each call
 bool kernels_cover(const apa_problem* p, int call) {
   if (p->fmt != APA_MXFP4) return false;
-  if (call == APA_CALL_QUANTIZE) return true;
-  if (p->D == 512) return false;
-  if (call == APA_CALL_PASS1) return true;
-  if (p->dtype != APA_F16) return false;
+  if (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1 || call == APA_CALL_MERGE) return true;
   const int G = p->Hq / p->Hkv;
   if (call == APA_CALL_PASS2 || call == APA_CALL_EXACT)
     return G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8;
@@ -194,6 +212,7 @@ size_t apa_workspace_bytes(const apa_problem* p, int32_t which) {
   switch (which) {
     case APA_CALL_QUANTIZE: return quant_ws(p, nullptr, nullptr);
     case APA_CALL_PASS2: return pass2_ws(p, nullptr, nullptr);
+    case APA_CALL_EXACT: return exact_ws(p, nullptr, nullptr);
     default: return 0;
   }
 }
@@ -258,7 +277,6 @@ apa_status apa_merge(const apa_problem* p, const void* fp4, const int32_t* cold_
   if (!fp4 || !cold_m || !cold_l || !cold_o || !hot_m || !hot_l || !hot_o || !out)
     return APA_ERR_INVALID_ARG;
   if (!kernels_cover(p, APA_CALL_MERGE)) return APA_ERR_UNSUPPORTED;
-  if (p->dtype != APA_F16) return APA_ERR_UNSUPPORTED;
   if (empty(p)) return APA_OK;
   clear_hip_error();
   return hip_status(launch_merge(geom(p), fp4_ptrs(p, fp4), cold_m, cold_l, cold_o, hot_m, hot_l,
@@ -267,14 +285,16 @@ apa_status apa_merge(const apa_problem* p, const void* fp4, const int32_t* cold_
 
 apa_status apa_exact(const apa_problem* p, const void* q, const void* k, const void* v,
                      void* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
   if (!q || !k || !v || !out) return APA_ERR_INVALID_ARG;
   if (!kernels_cover(p, APA_CALL_EXACT)) return APA_ERR_UNSUPPORTED;
   if (empty(p)) return APA_OK;
+  const size_t need = exact_ws(p, nullptr, nullptr);
+  if (need > 0 && (!ws || ws_bytes < need)) return APA_ERR_WORKSPACE;
+  Pass2Args parts = {};
+  exact_ws(p, &parts, ws);
   clear_hip_error();
-  return hip_status(launch_exact(geom(p), q, k, v, out, lse, (hipStream_t)stream));
+  return hip_status(launch_exact(geom(p), q, k, v, out, lse, parts, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,23 +1,34 @@
-// a8..a11: FP16 MFMA flash attention -- the exact pass 2 over compacted hot
+// a8..a11: 16-bit MFMA flash attention -- the exact pass 2 over compacted hot
 // tiles with the fused log-sum-exp merge, the standalone merge, and the
-// all-exact baseline.
+// all-exact baseline; fp16 or bf16 inputs.
 //
 // "APA: sloppy attention, exact where it counts" (rfriedmann.de): section
 // "Pass 2: exact FP16 on the hot tiles" (a work group takes the rows of one
 // pass-1 block, collects the union of their hot tiles, streams them from the
-// original FP16 K and V, each wavefront computes only its own hot tiles with
+// original 16-bit K and V, each wavefront computes only its own hot tiles with
 // an FP32 online softmax and merges with its pass-1 state) and "The merge that
 // makes it exact".  The introduction's all-exact baseline is the same core over
-// every visible tile.
+// every visible tile.  Large head dimensions follow the FFPA documentation's
+// interface (same layout and semantics at D = 512).
 //
-// Work group = (batch, kv-head, 64 query positions) x all G query heads of the
-// group: 2G wavefronts of 32 rows each, so every K/V tile staged in LDS feeds
-// all heads that share it.  Per wave and tile (D = 128):
-//   S^T = K Q^T   16 MFMA 32x32x16 f16, K from LDS (row pad 16 B), Q resident;
+// Work group = (batch, kv-head, POS query positions) x all G query heads of the
+// group: G*POS/32 wavefronts of 32 rows each, so every K/V tile staged in LDS
+// feeds all heads that share it.  POS is 64 for D <= 256 (LDS double
+// buffered, the next tile prefetched into registers) and 32 for D = 512 (one
+// LDS stage; the output accumulators live in the accumulation registers).
+// A unit's key range is cut into S splits that run as separate work groups
+// when there are too few units to fill the chip; each split writes a partial
+// online-softmax state and a combine kernel merges them in split order
+// (deterministic).  Per wave and tile (D = 128):
+//   S^T = K Q^T   16 MFMA 32x32x16, K from LDS (row pad 16 B), Q resident;
 //   softmax       scores sl*q.k - c_r in log2 units, FP32 running max/sum;
 //   O^T += V^T P^T 16 MFMA 32x32x16 f16; P stays in the accumulator's lanes
 //                 (its key order is matched by the V^T operand), V^T comes
-//                 from LDS by DS_READ_B64_TR_B16 (row pad 64 B).
+//                 from LDS by DS_READ_B64_TR_B16 (row pad 64 B).  With bf16
+//                 inputs the scores use the bf16 MFMA and V is staged as fp16,
+//                 so P keeps 11 significant bits.
+#include <type_traits>
+
 #include "apa_device.h"
 #include "apa_kernels.h"
 
@@ -27,66 +38,133 @@ namespace {
 
 enum Mode { kExact = 0, kPass2 = 1 };
 
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+
+// 16-bit element types: the MFMA and the conversions.
+template <typename T>
+struct E16;
+template <>
+struct E16<_Float16> {
+  typedef v8h V8;
+  typedef v4h V4;
+  static __device__ __forceinline__ v16f mma(V8 a, V8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ _Float16 from(float x) { return (_Float16)x; }
+};
+template <>
+struct E16<__bf16> {
+  typedef v8bf V8;
+  typedef v4bf V4;
+  static __device__ __forceinline__ v16f mma(V8 a, V8 b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ __bf16 from(float x) { return (__bf16)x; }
+};
+
 template <int D>
-struct Lds {
-  static constexpr int KS = D + 8;   // halves per K row (16-byte pad)
-  static constexpr int VS = D + 32;  // halves per V row (64-byte pad)
+struct Cfg {
+  static constexpr int POS = D >= 512 ? 32 : 64;  // query positions per work group
+  static constexpr int STAGES = D >= 512 ? 1 : 2;
+  static constexpr int KS = D + 8;    // halves per K row (16-byte pad)
+  static constexpr int VS = D + 32;   // halves per V row (64-byte pad)
   static constexpr int K_HALVES = kTile * KS;
   static constexpr int V_HALVES = kTile * VS;
   static constexpr int STAGE = K_HALVES + V_HALVES;
-  static constexpr size_t BYTES = 2 * STAGE * sizeof(_Float16);
+  static constexpr size_t BYTES = (size_t)STAGES * STAGE * 2;
+  static constexpr int CHUNKS = 2 * kTile * D / 8;  // 16-byte chunks per K+V tile
 };
 
-template <int D, int NW, int MODE>
-__global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __restrict__ Q,
-                                                  const _Float16* __restrict__ K,
-                                                  const _Float16* __restrict__ V, Fp4Ptrs f,
-                                                  Pass2Args a, int nunits) {
-  extern __shared__ _Float16 smem[];
-  using L = Lds<D>;
+__device__ __forceinline__ float merge_weight(bool live, float m, float M) {
+  return live ? fast_exp2(m - M) : 0.0f;
+}
+
+// bf16 values of V as fp16 for the P V product: exact inside the fp16 range
+// (8 significant bits fit in 11); magnitudes beyond it are clamped to 65504.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 z) {
+  const uint32_t w[4] = {z.x, z.y, z.z, z.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = fminf(fmaxf(__uint_as_float(w[i] << 16), -65504.0f), 65504.0f);
+    const float hi = fminf(fmaxf(__uint_as_float(w[i] & 0xFFFF0000u), -65504.0f), 65504.0f);
+    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+    r[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  }
+  return uint4{r[0], r[1], r[2], r[3]};
+}
+
+// Split s of n items out of `total` (balanced, contiguous).
+__device__ __forceinline__ int split_lo(int total, int s, int S) {
+  return (int)(((long long)total * s) / S);
+}
+
+template <int D, typename T, int MODE, int NW>
+__device__ __forceinline__ void attn_body(const Geom& g, const T* __restrict__ Q,
+                                          const T* __restrict__ K, const T* __restrict__ V,
+                                          const Fp4Ptrs& f, const Pass2Args& a, int nunits,
+                                          int S) {
+  using C = Cfg<D>;
+  using E = E16<T>;
+  typedef typename E::V8 V8;
+  typedef typename E::V4 V4;
+  extern __shared__ uint16_t smem[];
+  constexpr int POS = C::POS;
+  constexpr int WPH = POS / 32;       // waves per head
+  constexpr int GPU = POS / 16;       // 16-row groups per head and work group
   constexpr int NC = D / 16;          // 16-channel chunks of the QK contraction
   constexpr int ND = D / 32;          // 32-channel blocks of the output
-  constexpr int CHUNKS = 2 * kTile * D / 8;           // 16-byte chunks per K+V tile
-  constexpr int PER = (CHUNKS + NW * 64 - 1) / (NW * 64);
+  constexpr int PER = (C::CHUNKS + NW * 64 - 1) / (NW * 64);
+  constexpr int RND = C::STAGES == 2 ? PER : (PER < 8 ? PER : 8);  // chunks per staging round
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int unit = xcd_remap(blockIdx.x, gridDim.x);
   if (unit >= nunits) return;  // uniform over the block
-  const int nqb = (g.Nq + 63) / 64;
+  const int nqb = (g.Nq + POS - 1) / POS;
   const int qblk = unit % nqb;
-  const int hk = (unit / nqb) % g.Hkv;
-  const int b = unit / (nqb * g.Hkv);
-  const int gi = wave >> 1, half = wave & 1;
+  int u = unit / nqb;
+  const int sp = u % S; u /= S;
+  const int hk = u % g.Hkv;
+  const int b = u / g.Hkv;
+  const int base_unit = (b * g.Hkv + hk) * nqb + qblk;
+  const int gi = wave / WPH, half = wave % WPH;
   const int hq = hk * g.G + gi;
   const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
-  const int r0 = qblk * 64 + half * 32;
+  const int r0 = qblk * POS + half * 32;
   const int row = r0 + n;
   const bool row_ok = row < g.Nq;
   const bool wave_live = r0 < g.Nq;
   auto diag = [&](int lr) { return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile : g.NT - 1; };
   const int d_wave = wave_live ? diag(min(r0 + 31, g.Nq - 1)) : -1;
 
-  // tile list
-  int ntiles;
+  // this split's part of the unit's tile list
+  int lo, hi;
   const int32_t* tiles = nullptr;
   const uint32_t* masks = nullptr;
   if (MODE == kExact) {
-    ntiles = diag(min(qblk * 64 + 63, g.Nq - 1)) + 1;
+    const int ntot = diag(min(qblk * POS + POS - 1, g.Nq - 1)) + 1;
+    lo = split_lo(ntot, sp, S);
+    hi = split_lo(ntot, sp + 1, S);
   } else {
-    ntiles = a.list_count[unit];
-    tiles = a.list_tiles + (size_t)unit * g.NT;
-    masks = a.list_masks + (size_t)unit * g.NT;
+    const int ntot = a.list_count[base_unit];
+    lo = split_lo(ntot, sp, S);
+    hi = split_lo(ntot, sp + 1, S);
+    tiles = a.list_tiles + (size_t)base_unit * g.NT;
+    masks = a.list_masks + (size_t)base_unit * g.NT;
   }
+  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
 
-  // resident Q^T operand: 8 halves per 16-channel chunk
-  v8h qf[NC];
+  // resident Q^T operand: 8 elements per 16-channel chunk
+  V8 qf[NC];
   {
     const int rl = row_ok ? row : (g.Nq > 0 ? g.Nq - 1 : 0);
-    const _Float16* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
+    const T* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const v8h*>(qp + 16 * c);
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const V8*>(qp + 16 * c);
   }
   const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
   const float sl = g.sl;
@@ -94,54 +172,69 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
   float m = -__builtin_inff(), l = 0.0f;
   v16f o[ND];
 #pragma unroll
-  for (int i = 0; i < ND; ++i)
-    for (int j = 0; j < 16; ++j) o[i][j] = 0.0f;
+  for (int i = 0; i < ND; ++i) o[i] = v16f{};
 
-  const _Float16* Kh = K + bhk * (size_t)g.Nkv * D;
-  const _Float16* Vh = V + bhk * (size_t)g.Nkv * D;
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(K) + bhk * (size_t)g.Nkv * D;
+  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(V) + bhk * (size_t)g.Nkv * D;
 
   // cooperative staging: chunk c < CHUNKS/2 is K (row c / (D/8)), else V
-  uint4 pre[PER];
+  auto fetch1 = [&](int t, int c) {
+    uint4 z = {0u, 0u, 0u, 0u};
+    if (c < C::CHUNKS) {
+      const int isv = c >= C::CHUNKS / 2;
+      const int cc = isv ? c - C::CHUNKS / 2 : c;
+      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
+      const int key = t * kTile + r;
+      if (key < g.Nkv) z = *reinterpret_cast<const uint4*>((isv ? Vh : Kh) + (size_t)key * D + col);
+    }
+    return z;
+  };
+  auto stash1 = [&](int buf, int c, uint4 z) {
+    if (c < C::CHUNKS) {
+      uint16_t* st = smem + buf * C::STAGE;
+      const int isv = c >= C::CHUNKS / 2;
+      if (std::is_same<T, __bf16>::value && isv) z = bf16x8_to_f16x8(z);
+      const int cc = isv ? c - C::CHUNKS / 2 : c;
+      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
+      uint16_t* dst = isv ? st + C::K_HALVES + r * C::VS + col : st + r * C::KS + col;
+      *reinterpret_cast<uint4*>(dst) = z;
+    }
+  };
+  uint4 pre[RND];
   auto fetch = [&](int t) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NW * 64;
-      uint4 z = {0u, 0u, 0u, 0u};
-      if (c < CHUNKS) {
-        const int isv = c >= CHUNKS / 2;
-        const int cc = isv ? c - CHUNKS / 2 : c;
-        const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-        const int key = t * kTile + r;
-        if (key < g.Nkv) z = *reinterpret_cast<const uint4*>((isv ? Vh : Kh) + (size_t)key * D + col);
-      }
-      pre[i] = z;
-    }
+    for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + i * NW * 64);
   };
   auto stash = [&](int buf) {
-    _Float16* st = smem + buf * L::STAGE;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int c = tid + i * NW * 64;
-      if (c < CHUNKS) {
-        const int isv = c >= CHUNKS / 2;
-        const int cc = isv ? c - CHUNKS / 2 : c;
-        const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-        _Float16* dst = isv ? st + L::K_HALVES + r * L::VS + col : st + r * L::KS + col;
-        *reinterpret_cast<uint4*>(dst) = pre[i];
-      }
+    for (int i = 0; i < RND; ++i) stash1(buf, tid + i * NW * 64, pre[i]);
+  };
+  // single-stage staging of a whole tile in rounds (large D)
+  auto stage_all = [&](int t) {
+    for (int r0c = 0; r0c < PER; r0c += RND) {
+#pragma unroll
+      for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + (r0c + i) * NW * 64);
+#pragma unroll
+      for (int i = 0; i < RND; ++i) stash1(0, tid + (r0c + i) * NW * 64, pre[i]);
     }
   };
 
-  if (ntiles > 0) {
-    fetch(MODE == kExact ? 0 : tiles[0]);
+  if (C::STAGES == 2 && lo < hi) {
+    fetch(tile_at(lo));
     stash(0);
   }
-  __syncthreads();
+  if (C::STAGES == 2) __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int t = MODE == kExact ? it : tiles[it];
-    const int buf = it & 1;
-    if (it + 1 < ntiles) fetch(MODE == kExact ? it + 1 : tiles[it + 1]);
+  for (int it = lo; it < hi; ++it) {
+    const int t = tile_at(it);
+    const int buf = C::STAGES == 2 ? ((it - lo) & 1) : 0;
+    if (C::STAGES == 2) {
+      if (it + 1 < hi) fetch(tile_at(it + 1));
+    } else {
+      __syncthreads();
+      stage_all(t);
+      __syncthreads();
+    }
 
     // does this wave compute tile t, and for which of its two groups?
     bool on0, on1;
@@ -149,25 +242,24 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
       on0 = on1 = t <= d_wave;
     } else {
       const uint32_t mk = masks[it];
-      const int bit = gi * 4 + half * 2;
+      const int bit = gi * GPU + half * 2;
       on0 = (mk >> bit) & 1u;
       on1 = (mk >> (bit + 1)) & 1u;
     }
     if (wave_live && (on0 || on1)) {
-      const _Float16* Ks = smem + buf * L::STAGE;
-      const _Float16* Vs = Ks + L::K_HALVES;
+      const uint16_t* Ks = smem + buf * C::STAGE;
+      const uint16_t* Vs = Ks + C::K_HALVES;
       const int k0 = t * kTile;
       // ---- S^T = K Q^T
       v16f acc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[kb][j] = 0.0f;
-        const _Float16* kr = Ks + (kb * 32 + n) * L::KS + 8 * hh;
+        acc[kb] = v16f{};
+        const uint16_t* kr = Ks + (kb * 32 + n) * C::KS + 8 * hh;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const v8h kf = *reinterpret_cast<const v8h*>(kr + 16 * c);
-          acc[kb] = mfma_f16(kf, qf[c], acc[kb]);
+          const V8 kf = *reinterpret_cast<const V8*>(kr + 16 * c);
+          acc[kb] = E::mma(kf, qf[c], acc[kb]);
         }
       }
       // ---- scores in log2 units, masking
@@ -175,19 +267,24 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
       const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
                              (r0 + 31 >= g.Nq) || (on0 != on1);
       const int lim = g.causal ? row + g.off : 0x7fffffff;
-      float tmax = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          float s = fmaf(acc[kb][j], sl, -c_r);
-          if (need_mask) {
+        for (int j = 0; j < 16; ++j) acc[kb][j] = fmaf(acc[kb][j], sl, -c_r);
+      if (need_mask) {  // wave-uniform: diagonal, padding and half-masked tiles only
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
             const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) s = -__builtin_inff();
+            if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
           }
-          acc[kb][j] = s;
-          tmax = vmax(tmax, s);
-        }
+      }
+      float tmax = vmax(acc[0][0], acc[0][1]);
+#pragma unroll
+      for (int j = 2; j < 16; j += 2) tmax = vmax3(tmax, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
       tmax = vmax(tmax, xor32(tmax));
       const float mnew = vmax(m, tmax);
       if (__ballot(mnew > m) != 0ull) {
@@ -200,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
         m = mnew;
       }
       const float ms = m == -__builtin_inff() ? 0.0f : m;
-      // ---- P (fp16) and its row sum
+      // ---- P (fp16, also for bf16 inputs: 11 significant bits) and its row sum
       v8h pf[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -222,32 +319,39 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int keyb = kb * 32 + 16 * c + 4 * (G16 >> 1) + (i16 >> 2);
-            const _Float16* p0 = Vs + keyb * L::VS + ch0;
-            const _Float16* p1 = p0 + 8 * L::VS;
-            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            const uint16_t* p0 = Vs + keyb * C::VS + ch0;
+            const uint16_t* p1 = p0 + 8 * C::VS;
+            const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4s*)(p0));
-            const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) v4s*)(p1));
-            const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
             o[db] = mfma_f16(vf, pf[kb][c], o[db]);
           }
       }
     }
-    if (it + 1 < ntiles) stash(buf ^ 1);
-    __syncthreads();
+    if (C::STAGES == 2) {
+      if (it + 1 < hi) stash(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   if (!wave_live) return;
   l += xor32(l);
   if (!row_ok) return;
   const size_t r = bhq * g.Nq + row;
-  // ---- epilogue
-  if (MODE == kPass2 && !a.fuse) {
+  const size_t rows = (size_t)g.B * g.Hq * g.Nq;
+
+  // ---- partial state of one split (merged by k_combine)
+  if (S > 1 || (MODE == kPass2 && !a.fuse)) {
+    float* pm = S > 1 ? a.part_m + (size_t)sp * rows : a.hot_m;
+    float* pl = S > 1 ? a.part_l + (size_t)sp * rows : a.hot_l;
+    float* po = S > 1 ? a.part_o + (size_t)sp * rows * D : a.hot_o;
     if (hh == 0) {
-      a.hot_m[r] = l > 0.0f ? m : -__builtin_inff();
-      a.hot_l[r] = l;
+      pm[r] = l > 0.0f ? m : -__builtin_inff();
+      pl[r] = l;
     }
-    float* orow = a.hot_o + r * D;
+    float* orow = po + r * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -257,6 +361,7 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
       }
     return;
   }
+  // ---- one split: output directly (pass 2: merged with the cold state)
   float w1 = 0.0f, w2 = 0.0f, M = 0.0f, Lsum = 0.0f;
   const float* o1 = nullptr;
   if (MODE == kPass2) {
@@ -267,8 +372,8 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
     M = -__builtin_inff();
     if (e1) M = m1;
     if (e2) M = fmaxf(M, m);
-    w1 = e1 ? fast_exp2(m1 - M) : 0.0f;
-    w2 = e2 ? fast_exp2(m - M) : 0.0f;
+    w1 = merge_weight(e1, m1, M);
+    w2 = merge_weight(e2, m, M);
     Lsum = w1 * l1 + w2 * l;
     o1 = a.cold_o + r * D;
   } else {
@@ -277,7 +382,7 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
     Lsum = l;
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  _Float16* orow = reinterpret_cast<_Float16*>(a.out) + r * D;
+  T* orow = reinterpret_cast<T*>(a.out) + r * D;
 #pragma unroll
   for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -285,10 +390,10 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
       const int ch = db * 32 + 8 * q + 4 * hh;
       v4f c1 = {0.0f, 0.0f, 0.0f, 0.0f};
       if (MODE == kPass2 && w1 != 0.0f) c1 = *reinterpret_cast<const v4f*>(o1 + ch);
-      v4h y;
+      V4 y;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = (_Float16)((w1 * c1[e] + w2 * o[db][4 * q + e]) * inv);
-      *reinterpret_cast<v4h*>(orow + ch) = y;
+      for (int e = 0; e < 4; ++e) y[e] = E::from((w1 * c1[e] + w2 * o[db][4 * q + e]) * inv);
+      *reinterpret_cast<V4*>(orow + ch) = y;
     }
   if (a.lse && hh == 0) {
     const float c0 = MODE == kPass2 ? c_r : 0.0f;
@@ -296,16 +401,34 @@ __global__ __launch_bounds__(NW * 64) void k_fa16(Geom g, const _Float16* __rest
   }
 }
 
-// Hot mask -> per work group list of the tiles hot for any of its 4G row
-// groups, ascending, with a bit mask of the groups each tile is hot for
-// (bit gi*4 + local group).  One wavefront per work group.
-__global__ __launch_bounds__(64) void k_compact(Geom g, const uint32_t* __restrict__ bits,
+template <int D, typename T, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn(Geom g, const T* __restrict__ Q,
+                                                  const T* __restrict__ K,
+                                                  const T* __restrict__ V, Fp4Ptrs f, Pass2Args a,
+                                                  int nunits, int S) {
+  attn_body<D, T, MODE, NW>(g, Q, K, V, f, a, nunits, S);
+}
+
+// D = 512: one wave per SIMD, so the 256 output accumulators per lane can sit
+// in the accumulation registers beside the resident Q operand.
+template <int D, typename T, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_big(
+    Geom g, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, Fp4Ptrs f,
+    Pass2Args a, int nunits, int S) {
+  attn_body<D, T, MODE, NW>(g, Q, K, V, f, a, nunits, S);
+}
+
+// Hot mask -> per unit (batch, kv-head, POS positions) list of the tiles hot
+// for any of its G*POS/16 row groups, ascending, with a bit mask of the groups
+// each tile is hot for (bit gi*POS/16 + local group).  One wavefront per unit.
+__global__ __launch_bounds__(64) void k_compact(Geom g, int pos, const uint32_t* __restrict__ bits,
                                                 int32_t* tiles, uint32_t* masks, int32_t* count,
                                                 int nunits) {
   const int unit = blockIdx.x;
   if (unit >= nunits) return;
   const int lane = threadIdx.x;
-  const int nqb = (g.Nq + 63) / 64;
+  const int gpu = pos / 16;
+  const int nqb = (g.Nq + pos - 1) / pos;
   const int qblk = unit % nqb;
   const int hk = (unit / nqb) % g.Hkv;
   const int b = unit / (nqb * g.Hkv);
@@ -316,8 +439,8 @@ __global__ __launch_bounds__(64) void k_compact(Geom g, const uint32_t* __restri
     if (w < g.W) {
       for (int gi = 0; gi < g.G; ++gi) {
         const size_t bhq = (size_t)b * g.Hq + hk * g.G + gi;
-        for (int lg = 0; lg < 4; ++lg) {
-          const int grp = qblk * 4 + lg;
+        for (int lg = 0; lg < gpu; ++lg) {
+          const int grp = qblk * gpu + lg;
           if (grp < g.NG) u |= bits[(bhq * g.NG + grp) * g.W + w];
         }
       }
@@ -328,7 +451,7 @@ __global__ __launch_bounds__(64) void k_compact(Geom g, const uint32_t* __restri
       const int v = __shfl_up(incl, o);
       if (lane >= o) incl += v;
     }
-    int pos = base + incl - cnt;
+    int pos_out = base + incl - cnt;
     uint32_t rem = u;
     while (rem) {
       const int bit = __ffs(rem) - 1;
@@ -337,106 +460,197 @@ __global__ __launch_bounds__(64) void k_compact(Geom g, const uint32_t* __restri
       uint32_t mk = 0u;
       for (int gi = 0; gi < g.G; ++gi) {
         const size_t bhq = (size_t)b * g.Hq + hk * g.G + gi;
-        for (int lg = 0; lg < 4; ++lg) {
-          const int grp = qblk * 4 + lg;
+        for (int lg = 0; lg < gpu; ++lg) {
+          const int grp = qblk * gpu + lg;
           if (grp < g.NG && ((bits[(bhq * g.NG + grp) * g.W + w] >> bit) & 1u))
-            mk |= 1u << (gi * 4 + lg);
+            mk |= 1u << (gi * gpu + lg);
         }
       }
-      tiles[(size_t)unit * g.NT + pos] = t;
-      masks[(size_t)unit * g.NT + pos] = mk;
-      ++pos;
+      tiles[(size_t)unit * g.NT + pos_out] = t;
+      masks[(size_t)unit * g.NT + pos_out] = mk;
+      ++pos_out;
     }
     base += __shfl(incl, 63);
   }
   if (lane == 0) count[unit] = base;
 }
 
-// Standalone merge of the cold (pass-1) and hot (pass-2) states; one thread
-// per (row, 4 channels).
-template <int D>
-__global__ void k_merge(Geom g, Fp4Ptrs f, const int32_t* __restrict__ cm,
-                        const float* __restrict__ cl, const float* __restrict__ co,
-                        const float* __restrict__ hm, const float* __restrict__ hl,
-                        const float* __restrict__ ho, _Float16* out, float* lse, long nrows) {
-  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long r = gid / (D / 4);
-  const int ch = (int)(gid % (D / 4)) * 4;
-  if (r >= nrows) return;
-  const int m1i = cm[r];
-  const float l1 = cl[r], l2 = hl[r], m2 = hm[r];
+// The merge of a cold (pass-1) state (m1 integer frame, l1, o1) and a hot
+// state (m2, l2, o2) for 4 channels: shared by the standalone merge and the
+// split combine so both round identically.
+template <typename T>
+__device__ __forceinline__ void merge4(int m1i, float l1, v4f a1, float m2, float l2, v4f a2,
+                                       float c0, T* out, float* lse_out) {
+  typedef typename E16<T>::V4 V4;
   const bool e1 = l1 > 0.0f && m1i != (int32_t)0x80000000, e2 = l2 > 0.0f;
   float M = -__builtin_inff();
   if (e1) M = (float)m1i;
   if (e2) M = fmaxf(M, m2);
-  const float w1 = e1 ? fast_exp2((float)m1i - M) : 0.0f;
-  const float w2 = e2 ? fast_exp2(m2 - M) : 0.0f;
+  const float w1 = merge_weight(e1, (float)m1i, M);
+  const float w2 = merge_weight(e2, m2, M);
   const float Ls = w1 * l1 + w2 * l2;
   const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
-  v4f a = e1 ? *reinterpret_cast<const v4f*>(co + r * D + ch) : v4f{0, 0, 0, 0};
-  v4f c = e2 ? *reinterpret_cast<const v4f*>(ho + r * D + ch) : v4f{0, 0, 0, 0};
-  v4h y;
-  for (int e = 0; e < 4; ++e) y[e] = (_Float16)((w1 * a[e] + w2 * c[e]) * inv);
-  *reinterpret_cast<v4h*>(out + r * D + ch) = y;
-  if (lse && ch == 0) {
-    const long bh = r / g.Nq, rr = r % g.Nq;
-    const float c0 = f.q_frame[bh * g.NqP + rr];
-    lse[r] = Ls > 0.0f ? 0.69314718055994531f * (c0 + M + __log2f(Ls)) : -__builtin_inff();
-  }
+  if (!e1) a1 = v4f{0, 0, 0, 0};
+  if (!e2) a2 = v4f{0, 0, 0, 0};
+  V4 y;
+  for (int e = 0; e < 4; ++e) y[e] = E16<T>::from((w1 * a1[e] + w2 * a2[e]) * inv);
+  *reinterpret_cast<V4*>(out) = y;
+  if (lse_out)
+    *lse_out = Ls > 0.0f ? 0.69314718055994531f * (c0 + M + __log2f(Ls)) : -__builtin_inff();
 }
 
-template <int D, int NW, int MODE>
-hipError_t run_fa(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
-                  const Pass2Args& a, hipStream_t s) {
-  const int nunits = g.B * g.Hkv * ((g.Nq + 63) / 64);
+// Standalone merge of the cold and hot states; one thread per (row, 4 channels).
+template <int D, typename T>
+__global__ void k_merge(Geom g, Fp4Ptrs f, const int32_t* __restrict__ cm,
+                        const float* __restrict__ cl, const float* __restrict__ co,
+                        const float* __restrict__ hm, const float* __restrict__ hl,
+                        const float* __restrict__ ho, T* out, float* lse, long nrows) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long r = gid / (D / 4);
+  const int ch = (int)(gid % (D / 4)) * 4;
+  if (r >= nrows) return;
+  const float l1 = cl[r], l2 = hl[r];
+  const v4f a1 = l1 > 0.0f ? *reinterpret_cast<const v4f*>(co + r * D + ch) : v4f{0, 0, 0, 0};
+  const v4f a2 = l2 > 0.0f ? *reinterpret_cast<const v4f*>(ho + r * D + ch) : v4f{0, 0, 0, 0};
+  const long bh = r / g.Nq, rr = r % g.Nq;
+  const float c0 = (lse && ch == 0) ? f.q_frame[bh * g.NqP + rr] : 0.0f;
+  merge4<T>(cm[r], l1, a1, hm[r], l2, a2, c0, out + r * D + ch,
+            (lse && ch == 0) ? lse + r : nullptr);
+}
+
+// Combine the S split states of each row (in split order), then: exact ->
+// output; pass 2 fused -> merge with the cold state; pass 2 unfused -> the hot
+// state.  One thread per (row, 4 channels).
+template <int D, typename T, int MODE>
+__global__ void k_combine(Geom g, Fp4Ptrs f, Pass2Args a, int S, long nrows) {
+  const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long r = gid / (D / 4);
+  const int ch = (int)(gid % (D / 4)) * 4;
+  if (r >= nrows) return;
+  float Mh = -__builtin_inff();
+  for (int s = 0; s < S; ++s)
+    if (a.part_l[s * nrows + r] > 0.0f) Mh = fmaxf(Mh, a.part_m[s * nrows + r]);
+  float Lh = 0.0f;
+  v4f oh = {0, 0, 0, 0};
+  for (int s = 0; s < S; ++s) {
+    const float ls = a.part_l[s * nrows + r];
+    if (ls > 0.0f) {
+      const float w = fast_exp2(a.part_m[s * nrows + r] - Mh);
+      Lh += w * ls;
+      const v4f x = *reinterpret_cast<const v4f*>(a.part_o + (s * nrows + r) * D + ch);
+      for (int e = 0; e < 4; ++e) oh[e] += w * x[e];
+    }
+  }
+  const bool want_lse = a.lse && ch == 0;
+  if (MODE == kExact) {
+    // the state alone: same arithmetic as a merge with an empty cold state
+    merge4<T>((int32_t)0x80000000, 0.0f, v4f{0, 0, 0, 0}, Mh, Lh, oh, 0.0f,
+              reinterpret_cast<T*>(a.out) + r * D + ch, want_lse ? a.lse + r : nullptr);
+    return;
+  }
+  if (!a.fuse) {
+    if (ch == 0) {
+      a.hot_m[r] = Lh > 0.0f ? Mh : -__builtin_inff();
+      a.hot_l[r] = Lh;
+    }
+    *reinterpret_cast<v4f*>(a.hot_o + r * D + ch) = oh;
+    return;
+  }
+  const float l1 = a.cold_l[r];
+  const v4f a1 = l1 > 0.0f ? *reinterpret_cast<const v4f*>(a.cold_o + r * D + ch) : v4f{0, 0, 0, 0};
+  const long bh = r / g.Nq, rr = r % g.Nq;
+  const float c0 = want_lse ? f.q_frame[bh * g.NqP + rr] : 0.0f;
+  merge4<T>(a.cold_m[r], l1, a1, Lh > 0.0f ? Mh : -__builtin_inff(), Lh, oh, c0,
+            reinterpret_cast<T*>(a.out) + r * D + ch, want_lse ? a.lse + r : nullptr);
+}
+
+template <int D, typename T, int MODE, int NW>
+hipError_t run_attn(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
+                    const Pass2Args& a, int S, hipStream_t s) {
+  const int nunits = g.B * g.Hkv * ((g.Nq + Cfg<D>::POS - 1) / Cfg<D>::POS) * S;
   if (nunits == 0) return hipSuccess;
-  auto kern = k_fa16<D, NW, MODE>;
+  void (*kern)(Geom, const T*, const T*, const T*, Fp4Ptrs, Pass2Args, int, int);
+  if constexpr (D >= 512) kern = k_attn_big<D, T, MODE, NW>;
+  else kern = k_attn<D, T, MODE, NW>;
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Lds<D>::BYTES);
+                                       (int)Cfg<D>::BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3(nunits), dim3(NW * 64), Lds<D>::BYTES, s, g, (const _Float16*)q,
-                     (const _Float16*)k, (const _Float16*)v, f, a, nunits);
+  hipLaunchKernelGGL(kern, dim3(nunits), dim3(NW * 64), Cfg<D>::BYTES, s, g, (const T*)q,
+                     (const T*)k, (const T*)v, f, a, nunits, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const long nrows = (long)g.B * g.Hq * g.Nq;
+  const long thr = nrows * (D / 4);
+  hipLaunchKernelGGL((k_combine<D, T, MODE>), dim3((unsigned)((thr + 255) / 256)), dim3(256), 0, s,
+                     g, f, a, S, nrows);
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t dispatch(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
-                    const Pass2Args& a, hipStream_t s) {
-#define APA_FA_CASE(DD, GG)                                                   \
-  if (g.D == DD && g.G == GG) return run_fa<DD, 2 * GG, MODE>(g, q, k, v, f, a, s);
+template <int MODE, typename T>
+hipError_t dispatch_t(const Geom& g, const void* q, const void* k, const void* v,
+                      const Fp4Ptrs& f, const Pass2Args& a, int S, hipStream_t s) {
+#define APA_FA_CASE(DD, GG)                                                              \
+  if (g.D == DD && g.G == GG)                                                            \
+    return run_attn<DD, T, MODE, GG * Cfg<DD>::POS / 32>(g, q, k, v, f, a, S, s);
 #define APA_FA_D(DD) APA_FA_CASE(DD, 1) APA_FA_CASE(DD, 2) APA_FA_CASE(DD, 3) \
   APA_FA_CASE(DD, 4) APA_FA_CASE(DD, 6) APA_FA_CASE(DD, 8)
   APA_FA_D(64)
   APA_FA_D(128)
   APA_FA_D(256)
+  APA_FA_D(512)
 #undef APA_FA_D
 #undef APA_FA_CASE
   return hipErrorInvalidValue;
 }
 
+template <int MODE>
+hipError_t dispatch(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
+                    const Pass2Args& a, int S, hipStream_t s) {
+  return g.bf16 ? dispatch_t<MODE, __bf16>(g, q, k, v, f, a, S, s)
+                : dispatch_t<MODE, _Float16>(g, q, k, v, f, a, S, s);
+}
+
 }  // namespace
 
+int attn_positions(int D) { return D >= 512 ? 32 : 64; }
+
+int attn_splits(const Geom& g) {
+  const int pos = attn_positions(g.D);
+  const long units = (long)g.B * g.Hkv * ((g.Nq + pos - 1) / pos);
+  if (units <= 0) return 1;
+  // one work group per compute unit of the 256-CU part (the register use of
+  // the D <= 256 kernels allows one resident group of G*POS/32 waves per CU)
+  long S = (256 + units - 1) / units;
+  if (S > 8) S = 8;
+  // at least 4 tiles per split of the longest key range
+  long maxs = g.NT / 4;
+  if (maxs < 1) maxs = 1;
+  if (S > maxs) S = maxs;
+  return (int)(S < 1 ? 1 : S);
+}
+
 hipError_t launch_pass2(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a, hipStream_t s) {
-  const int nunits = g.B * g.Hkv * ((g.Nq + 63) / 64);
+  const int pos = attn_positions(g.D);
+  const int nunits = g.B * g.Hkv * ((g.Nq + pos - 1) / pos);
   if (nunits == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_compact, dim3(nunits), dim3(64), 0, s, g, a.bits, a.list_tiles,
+  hipLaunchKernelGGL(k_compact, dim3(nunits), dim3(64), 0, s, g, pos, a.bits, a.list_tiles,
                      a.list_masks, a.list_count, nunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return dispatch<kPass2>(g, a.q, a.k, a.v, f, a, s);
+  return dispatch<kPass2>(g, a.q, a.k, a.v, f, a, attn_splits(g), s);
 }
 
 hipError_t launch_exact(const Geom& g, const void* q, const void* k, const void* v, void* out,
-                        float* lse, hipStream_t s) {
-  Pass2Args a = {};
+                        float* lse, const Pass2Args& parts, hipStream_t s) {
+  Pass2Args a = parts;
   a.out = out;
   a.lse = lse;
   Fp4Ptrs f = {};
-  return dispatch<kExact>(g, q, k, v, f, a, s);
+  return dispatch<kExact>(g, q, k, v, f, a, attn_splits(g), s);
 }
 
 hipError_t launch_merge(const Geom& g, const Fp4Ptrs& f, const int32_t* cold_m,
@@ -447,12 +661,28 @@ hipError_t launch_merge(const Geom& g, const Fp4Ptrs& f, const int32_t* cold_m,
   if (nrows == 0) return hipSuccess;
   const long thr = nrows * (g.D / 4);
   const unsigned nb = (unsigned)((thr + 255) / 256);
-  switch (g.D) {
-    case 64: hipLaunchKernelGGL(k_merge<64>, dim3(nb), dim3(256), 0, s, g, f, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, (_Float16*)out, lse, nrows); break;
-    case 128: hipLaunchKernelGGL(k_merge<128>, dim3(nb), dim3(256), 0, s, g, f, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, (_Float16*)out, lse, nrows); break;
-    case 256: hipLaunchKernelGGL(k_merge<256>, dim3(nb), dim3(256), 0, s, g, f, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, (_Float16*)out, lse, nrows); break;
-    default: return hipErrorInvalidValue;
+#define APA_MERGE(DD, TT)                                                                      \
+  hipLaunchKernelGGL((k_merge<DD, TT>), dim3(nb), dim3(256), 0, s, g, f, cold_m, cold_l, cold_o, \
+                     hot_m, hot_l, hot_o, (TT*)out, lse, nrows);                               \
+  break;
+  if (g.bf16) {
+    switch (g.D) {
+      case 64: APA_MERGE(64, __bf16)
+      case 128: APA_MERGE(128, __bf16)
+      case 256: APA_MERGE(256, __bf16)
+      case 512: APA_MERGE(512, __bf16)
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (g.D) {
+      case 64: APA_MERGE(64, _Float16)
+      case 128: APA_MERGE(128, _Float16)
+      case 256: APA_MERGE(256, _Float16)
+      case 512: APA_MERGE(512, _Float16)
+      default: return hipErrorInvalidValue;
+    }
   }
+#undef APA_MERGE
   return hipGetLastError();
 }
 

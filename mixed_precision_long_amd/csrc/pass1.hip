@@ -53,6 +53,11 @@ namespace {
 constexpr int kWaves = 4;            // wavefronts per work group
 constexpr float kFrameGuard = 80.0f; // largest lead of m over m_o before re-basing
 
+// Two waves per SIMD up to D = 128; one above, where the output accumulators
+// (D/2 per lane) need the accumulation registers.
+template <int D>
+constexpr int kWavesPerSimd = D >= 256 ? 1 : 2;
+
 template <int D>
 struct Tile {
   static constexpr int NH = D / 64;       // 64-channel halves of the QK contraction
@@ -86,10 +91,16 @@ __device__ __forceinline__ void load_scales(uint32_t (&w)[Tile<D>::NW], const ui
     w[0] = *reinterpret_cast<const uint16_t*>(p);
   } else if constexpr (D == 128) {
     w[0] = *reinterpret_cast<const uint32_t*>(p);
-  } else {
+  } else if constexpr (D == 256) {
     const uint2 x = *reinterpret_cast<const uint2*>(p);
     w[0] = x.x;
     w[1] = x.y;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    w[0] = x.x;
+    w[1] = x.y;
+    w[2] = x.z;
+    w[3] = x.w;
   }
 }
 
@@ -128,7 +139,7 @@ __device__ __forceinline__ void qk(v16f (&acc)[2], const KOps<D>& k, const v4i* 
 }
 
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_pass1(
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, int nunits) {
   constexpr int NH = Tile<D>::NH;
   constexpr int ND = Tile<D>::ND;
@@ -432,6 +443,7 @@ hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, i
     case 64: return run<64>(g, f, eps, tau, hoff, o, s);
     case 128: return run<128>(g, f, eps, tau, hoff, o, s);
     case 256: return run<256>(g, f, eps, tau, hoff, o, s);
+    case 512: return run<512>(g, f, eps, tau, hoff, o, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,6 +17,8 @@ namespace apa {
 
 namespace {
 
+// Zero the status word (a kernel, so the sequence holds no memset node if
+// the caller captures it in a graph).
 __global__ void k_clear_status(unsigned* status) { *status = 0u; }
 
 // Block-wide max over blockDim.x threads (<= 512) through LDS.
@@ -39,13 +41,11 @@ __device__ float block_max(float v, float* red) {
 // cg) owns 8 consecutive channels of one tile (16-byte loads).
 // grid (NCH, B*Hkv), block 2*D.
 template <typename T>
-__global__ void k_kv_stats(const T* __restrict__ K, const T* __restrict__ V, Geom g, QuantWs ws,
-                           unsigned* status) {
-  extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
-  __shared__ float red[16];
+__device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const Geom& g,
+                         const QuantWs& ws, unsigned* status, int ch, int bh, double* sh,
+                         float* red) {
   const int D = g.D, ncg = D / 8;
   const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
-  const int ch = blockIdx.x, bh = blockIdx.y;
   const int t = ch * 16 + tt;
   const size_t base = (size_t)bh * g.Nkv * D + cg * 8;
   double s[8];
@@ -107,22 +107,23 @@ __global__ void k_kv_stats(const T* __restrict__ K, const T* __restrict__ V, Geo
 }
 
 // max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq), block D.
+// (block of 2*D threads: thread (half, d) takes rows r0 + half, r0 + half + 2, ...)
 template <typename T>
-__global__ void k_q_stats(const T* __restrict__ Q, Geom g, QuantWs ws, unsigned* status) {
-  __shared__ float red[8];
-  const int d = threadIdx.x, t = blockIdx.x, bh = blockIdx.y;
+__device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws,
+                        unsigned* status, int t, int bh, float* red) {
+  const int d = threadIdx.x % g.D, half = threadIdx.x / g.D;
   const size_t base = ((size_t)bh * g.Nq) * g.D;
   const int r0 = t * 64, r1 = min(g.Nq, r0 + 64);
   float a = 0.0f;
   bool bad = false;
-  for (int r = r0; r < r1; ++r) {
+  for (int r = r0 + half; r < r1; r += 2) {
     float x = to_f32<T>(Q[base + (size_t)r * g.D + d]);
     bad |= !__builtin_isfinite(x);
     a = fmaxf(a, fabsf(x));
   }
   if (bad) atomicOr(status, 1u);
   float m = block_max(a, red);
-  if (d == 0) ws.qamax[(size_t)bh * ws.nqt + t] = m;
+  if (threadIdx.x == 0) ws.qamax[(size_t)bh * ws.nqt + t] = m;
 }
 
 // Head scale mapping amax to 6: g = fl32(amax/6), inv = fl32(6/amax); the FP64
@@ -135,21 +136,39 @@ __device__ void head_scale(float amax, float* gs, float* inv) {
 
 // Per (b, kv-head): key mean, |K - kbar| max, V max, their head scales, and
 // the tied Q scales of the group's query heads.  grid (B*Hkv), block D.
-__global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
-  __shared__ float red[8];
-  const int d = threadIdx.x, bh = blockIdx.x;
-  double s = 0.0;
-  float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int c = 0; c < ws.nch; ++c) {  // chunk sums in ascending order
-    const size_t o = ((size_t)bh * ws.nch + c) * g.D + d;
-    s += ws.ksum[o];
-    mn = fminf(mn, ws.kmin[o]);
-    mx = fmaxf(mx, ws.kmax[o]);
-  }
-  const float kb = g.Nkv > 0 ? (float)(s / (double)g.Nkv) : 0.0f;
-  f.kbar[(size_t)bh * g.D + d] = kb;
+__device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* red) {
+  const int d = threadIdx.x;
+  const bool own = d < g.D;  // threads D .. 2D-1 only join the block reductions
   float dev = 0.0f;
-  if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
+  if (own) {
+    double s = 0.0;
+    float mn = __builtin_inff(), mx = -__builtin_inff();
+    // chunk sums in ascending order; loads issued 8 chunks ahead of the adds
+    constexpr int BATCH = 8;
+    for (int c0 = 0; c0 < ws.nch; c0 += BATCH) {
+      double bs[BATCH];
+      float bmn[BATCH], bmx[BATCH];
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        const int c = min(c0 + i, ws.nch - 1);
+        const size_t o = ((size_t)bh * ws.nch + c) * g.D + d;
+        bs[i] = ws.ksum[o];
+        bmn[i] = ws.kmin[o];
+        bmx[i] = ws.kmax[o];
+      }
+#pragma unroll
+      for (int i = 0; i < BATCH; ++i) {
+        if (c0 + i < ws.nch) {
+          s += bs[i];
+          mn = fminf(mn, bmn[i]);
+          mx = fmaxf(mx, bmx[i]);
+        }
+      }
+    }
+    const float kb = g.Nkv > 0 ? (float)(s / (double)g.Nkv) : 0.0f;
+    f.kbar[(size_t)bh * g.D + d] = kb;
+    if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
+  }
   const float amax_k = block_max(dev, red);
   float va = 0.0f;
   for (int c = d; c < ws.nch; c += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
@@ -196,13 +215,13 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
 // [Nrows, NP) are padding and get zero codes.  For Q it also writes the frame
 // constant c_r = sl * q.kbar (FP32).  grid (ceil(NP*D/8 / 256), B*H).
 template <typename T, bool IS_Q>
-__global__ void k_quant_rows(const T* __restrict__ X, Geom g, Fp4Ptrs f) {
+__device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs& f, int bx,
+                           int bh) {
   const int H = IS_Q ? g.Hq : g.Hkv;
   const int Nrows = IS_Q ? g.Nq : g.Nkv;
   const int NP = IS_Q ? g.NqP : g.NkvP;
-  const int bh = blockIdx.y;
   const int tpr = g.D / 8;                     // threads per row
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int gid = bx * blockDim.x + threadIdx.x;
   const int row = gid / tpr, c8 = (gid % tpr) * 8;
   if (row >= NP) return;                       // whole 4-thread blocks exit together
   const int b = bh / H, h = bh % H;
@@ -266,10 +285,11 @@ __global__ void k_quant_rows(const T* __restrict__ X, Geom g, Fp4Ptrs f) {
 // (channel, half) quantises one 32-key block.  Codes of a block are stored
 // with its eight 4-key runs in the order 0,2,4,6,1,3,5,7.
 template <typename T>
-__global__ void k_quant_vt(const T* __restrict__ V, Geom g, Fp4Ptrs f) {
+__device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& f, int t, int bh,
+                         int cz) {
   constexpr int CH = 128, PADH = 8;
   __shared__ T tile[kTile][CH + PADH];
-  const int t = blockIdx.x, bh = blockIdx.y, c0 = blockIdx.z * CH;
+  const int c0 = cz * CH;
   const int nch = min(CH, g.D - c0);
   const float inv = f.kv_head[(size_t)bh * 8 + 5];
   const int k0 = t * kTile;
@@ -315,29 +335,75 @@ __global__ void k_quant_vt(const T* __restrict__ V, Geom g, Fp4Ptrs f) {
   blob[66 * g.D + ((ch % 32) * 2 + half) * (g.D / 32) + ch / 32] = (uint8_t)(e + 127);
 }
 
+// Statistics in one launch: blocks [0, NKB) take (kv-head, 16-tile chunk),
+// the rest (q-head, 64-row tile).  block 2*D threads, dynamic LDS
+// 16*D*(8+4+4) bytes.
+template <typename T>
+__global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+                        Geom g, QuantWs ws, unsigned* status, int nkb) {
+  extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
+  __shared__ float red[16];
+  if ((int)blockIdx.x < nkb) {
+    kv_stats<T>(K, V, g, ws, status, blockIdx.x % ws.nch, blockIdx.x / ws.nch, sh, red);
+  } else {
+    const int qb = blockIdx.x - nkb;
+    q_stats<T>(Q, g, ws, status, qb % ws.nqt, qb / ws.nqt, red);
+  }
+}
+
+// One block of 2*D threads per (b, kv-head).
+__global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
+  __shared__ float red[16];
+  finalize(g, ws, f, blockIdx.x, red);
+}
+
+// Quantisation in one launch: blocks for K rows, then V tiles, then Q rows.
+template <typename T>
+__global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T* __restrict__ K,
+                                               const T* __restrict__ V, Geom g, Fp4Ptrs f,
+                                               int kpb, int nvb_x, int nvb_z, int qpb) {
+  int b = blockIdx.x;
+  const int nk = kpb * g.B * g.Hkv, nv = g.NT * g.B * g.Hkv * nvb_z;
+  if (b < nk) {
+    quant_rows<T, false>(K, g, f, b % kpb, b / kpb);
+    return;
+  }
+  b -= nk;
+  if (b < nv) {
+    const int t = b % nvb_x, rest = b / nvb_x;
+    quant_vt<T>(V, g, f, t, rest % (g.B * g.Hkv), rest / (g.B * g.Hkv));
+    return;
+  }
+  b -= nv;
+  quant_rows<T, true>(Q, g, f, b % qpb, b / qpb);
+}
+
 template <typename T>
 hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const Fp4Ptrs& f,
                         const QuantWs& ws, hipStream_t s) {
+  const int nkvh = g.B * g.Hkv;
   hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, f.status);
-  if (g.Nkv > 0)
-    hipLaunchKernelGGL(k_kv_stats<T>, dim3(ws.nch, g.B * g.Hkv), dim3(2 * g.D),
-                       16 * g.D * (sizeof(double) + 2 * sizeof(float)), s, k, v, g, ws, f.status);
-  if (g.Nq > 0)
-    hipLaunchKernelGGL(k_q_stats<T>, dim3(ws.nqt, g.B * g.Hq), dim3(g.D), 0, s, q, g, ws,
-                       f.status);
-  hipLaunchKernelGGL(k_finalize, dim3(g.B * g.Hkv), dim3(g.D), 0, s, g, ws, f);
-  if (g.NkvP > 0) {
-    const long thr = (long)g.NkvP * (g.D / 8);
-    hipLaunchKernelGGL((k_quant_rows<T, false>), dim3((unsigned)((thr + 255) / 256), g.B * g.Hkv),
-                       dim3(256), 0, s, k, g, f);
-    hipLaunchKernelGGL(k_quant_vt<T>, dim3(g.NT, g.B * g.Hkv, (g.D + 127) / 128), dim3(256), 0, s,
-                       v, g, f);
+  const size_t stats_lds = 16 * (size_t)g.D * (sizeof(double) + 2 * sizeof(float));
+  static bool stats_attr = false;  // above 64 KB (D = 512) the launch must opt in
+  if (!stats_attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_stats<T>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 512 * 256);
+    if (e != hipSuccess) return e;
+    stats_attr = true;
   }
-  if (g.NqP > 0 && g.Hq > 0) {
-    const long thr = (long)g.NqP * (g.D / 8);
-    hipLaunchKernelGGL((k_quant_rows<T, true>), dim3((unsigned)((thr + 255) / 256), g.B * g.Hq),
-                       dim3(256), 0, s, q, g, f);
-  }
+  const int nkb = g.Nkv > 0 ? ws.nch * nkvh : 0;
+  const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
+  if (nkb + nqb > 0)
+    hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(2 * g.D), stats_lds, s, q, k, v, g, ws,
+                       f.status, nkb);
+  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 0, s, g, ws, f);
+  const int kpb = (int)(((long)g.NkvP * (g.D / 8) + 255) / 256);
+  const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
+  const int nvb_z = (g.D + 127) / 128;
+  const long nblk = (long)kpb * nkvh + (long)g.NT * nkvh * nvb_z + (long)qpb * g.B * g.Hq;
+  if (nblk > 0)
+    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpb, g.NT,
+                       nvb_z, qpb);
   return hipGetLastError();
 }
 

@@ -106,6 +106,11 @@ def test_workspace_too_small():
         apa.APA_ERR_WORKSPACE
     assert L.apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, need, None) == \
         apa.APA_ERR_WORKSPACE
+    few = prob(Nq=256)  # few row blocks: the key range runs as several splits
+    need_ex = apa.workspace_bytes(few, apa.CALL_EXACT)
+    assert need_ex > 0
+    assert L.apa_exact(C.byref(few), FAKE, FAKE, FAKE, FAKE, None, FAKE, need_ex - 1, None) == \
+        apa.APA_ERR_WORKSPACE
     need2 = apa.workspace_bytes(p, apa.CALL_PASS2)
     assert L.apa_pass2(C.byref(p), *([FAKE] * 8), 1, FAKE, None, None, None, None, FAKE, need2 - 1,
                        None) == apa.APA_ERR_WORKSPACE
@@ -115,9 +120,6 @@ def test_unsupported_variants_say_so():
     L = apa.lib()
     nv = prob(fmt=apa.APA_NVFP4)
     assert L.apa_quantize(C.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
-        apa.APA_ERR_UNSUPPORTED
-    d512 = prob(D=512)
-    assert L.apa_pass1(C.byref(d512), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None) == \
         apa.APA_ERR_UNSUPPORTED
     g5 = prob(Hq=40)  # group of 5 query heads
     assert L.apa_exact(C.byref(g5), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == \
