@@ -4,9 +4,10 @@
 //
 // "APA: sloppy attention, exact where it counts" (rfriedmann.de): section
 // "Pass 2: exact FP16 on the hot tiles" (a work group takes the rows of one
-// pass-1 block, collects the union of their hot tiles, streams them from the
-// original 16-bit K and V, each wavefront computes only its own hot tiles with
-// an FP32 online softmax and merges with its pass-1 state) and "The merge that
+// pass-1 block, gathers the tiles hot for any of them, streams those from the
+// original 16-bit K and V; a wavefront works only on tiles hot for its rows,
+// with an FP32 online softmax, and combines the result with the cold state of
+// pass 1) and "The merge that
 // makes it exact".  The introduction's all-exact baseline is the same core over
 // every visible tile.  Large head dimensions follow the FFPA documentation's
 // interface (same layout and semantics at D = 512).

@@ -339,7 +339,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     // E8M0 byte of this lane's 32-key group in the state's frame
     const int pscale = xo - mo + 127;
 
-    // ---- step 3: row sums from the same quantised P (in the state's frame)
+    // ---- step 3: l_t as an MFMA of the quantised P itself (state's frame)
     const v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
     const v16f ones_acc = mfma4(ones, pb, v16f{}, kE8M0One, 0, pscale);
     // this tile's scores are consumed: the next tile's go to the matrix cores

@@ -1,15 +1,15 @@
 // a1 statistics and a2 block-scaled FP4 quantisation.
 //
 // "APA: sloppy attention, exact where it counts" (rfriedmann.de), section
-// "Pass 1: FP4 everywhere, with a hot test": a prep stage writes K and V^T in
-// E2M1 plus their scales, after subtracting the per-channel key mean
+// "Pass 1: FP4 everywhere, with a hot test": before pass 1, K and V^T are
+// stored as E2M1 codes with their scales, K centred on its per-channel mean
 // ("Mean-centred K"), with one FP32 scale per head.  Here the block format is
 // MXFP4: one E8M0 exponent per 32 elements (Q and K along channels, V along
 // keys), the smallest that fits the block maximum under 6, and E2M1 codes
 // rounded to nearest even by the hardware's scaled conversion.
 //
 // HBM-bound work: K and V are read twice (statistics, then quantisation) and
-// Q once; all reductions run in a fixed order, so results are deterministic.
+// Q once; every reduction has a fixed order, so results are deterministic.
 #include "apa_device.h"
 #include "apa_kernels.h"
 

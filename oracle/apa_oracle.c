@@ -153,8 +153,8 @@ static int p_group_exp(double ymax) {
 
 /* Per-channel key mean of one (b, kv-head): the FP64 sum runs in a fixed
  * three-level order -- keys ascending inside each 64-key tile, tile sums
- * ascending inside each chunk of 16 tiles, chunk sums ascending ("All
- * reductions run in a fixed order", 'What else is in the box'); for fp16 keys
+ * ascending inside each chunk of 16 tiles, chunk sums ascending (the page
+ * fixes the order of its reductions, 'What else is in the box'); for fp16 keys
  * of ordinary magnitude every partial sum is exact, so the order only matters
  * for extreme inputs.  k̄ = fl32(sum / Nkv) with the division in FP64.  Also the per-channel
  * min and max, and amax_K = max over channels of

@@ -174,7 +174,7 @@ def test_centring_keys_keeps_exact_path_and_apa_nearly_invariant():
     p = O.Params(1, 2, 1, 64, 1024, 64, scale=w.scale, eps=0.02)
     Oe, _ = O.exact(p, Q, K, V)
     Oe2, _ = O.exact(p, Q, K2, V)
-    # a per-channel key shift moves every score of a row by the same constant
+    # shifting every key by one vector adds one constant to all scores of a row
     # (up to fp16 rounding of the shifted keys)
     assert np.abs(Oe - Oe2).max() < 5e-3
     r1 = O.run(p, Q, K, V)
