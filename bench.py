@@ -160,7 +160,7 @@ def main():
         if record:
             e[1].record(stream)
         apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
-                  stream)
+                  ws=bufs.ws_p1, stream=stream)
         if record:
             e[2].record(stream)
         apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
@@ -257,7 +257,7 @@ def main():
         for e2 in w.eps_sweep:
             for _ in range(2):
                 apa.pass1(p, bufs.fp4, e2, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
-                          stream)
+                          ws=bufs.ws_p1, stream=stream)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(5):
@@ -280,7 +280,8 @@ def main():
 
 def step_eps(apa, p, q, k, v, bufs, eps, stream):
     apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
-    apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None, stream)
+    apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
+              ws=bufs.ws_p1, stream=stream)
     apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
               out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
 

@@ -138,10 +138,20 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
  *   hot_bits  apa_hotmask_bytes(p) bytes (every word written)
  *   lambda_out  may be NULL: final running sum in the frame cold_m
  * eps must be >= 0 and not NaN (+inf allowed).  Requires the FP4 buffer of
- * apa_quantize for the same problem. */
+ * apa_quantize for the same problem.
+ * ws: NULL, or apa_workspace_bytes(p, APA_CALL_PASS1) bytes (0 for problems
+ * whose 32-row blocks already fill the GPU).  With a workspace, each long
+ * visit order is cut in two and run by two wavefronts of one work group at
+ * once; the workspace holds the tiles the second one cannot decide until the
+ * first is done (at most 1024 per 32-row block, 292 bytes each).  Without
+ * one, every block runs as one wavefront (slower when the blocks do not fill
+ * the GPU).  The verdicts and the state are those of a single walk up to FP32
+ * summation order; the returned frame cold_m is then the larger of the two
+ * halves' frames (the state is scaled to match, so cold_l * 2^cold_m and
+ * cold_o / cold_l do not depend on it). */
 apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
                      float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
-                     void* stream);
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* a8..a10: pass 2 ("Pass 2: exact FP16 on the hot tiles").  Compacts the hot
  * mask into per-work-group lists of tiles hot for any of its row groups, then

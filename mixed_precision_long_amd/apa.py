@@ -72,7 +72,7 @@ def lib() -> C.CDLL:
         L.apa_last_hip_error.argtypes = []
         L.apa_last_hip_error.restype = C.c_char_p
         L.apa_quantize.argtypes = [P, VP, VP, VP, VP, VP, S, VP]
-        L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP]
+        L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
                                 VP, S, VP]
         L.apa_merge.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
@@ -137,9 +137,14 @@ def quantize(p: Problem, q, k, v, fp4, ws, stream=None):
                               _stream(stream)), "apa_quantize")
 
 
-def pass1(p: Problem, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=None, stream=None):
+def pass1(p: Problem, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=None, ws=None,
+          stream=None):
+    """Pass 1.  ws: workspace of workspace_bytes(p, CALL_PASS1) bytes (may be
+    None when that is 0)."""
     _check(lib().apa_pass1(C.byref(p), _ptr(fp4), float(eps), _ptr(cold_m), _ptr(cold_l),
-                           _ptr(cold_o), _ptr(hot_bits), _ptr(lam), _stream(stream)), "apa_pass1")
+                           _ptr(cold_o), _ptr(hot_bits), _ptr(lam), _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "apa_pass1")
 
 
 def pass2(p: Problem, q, k, v, fp4, hot_bits, cold_m, cold_l, cold_o, fuse_merge: bool, out=None,
@@ -176,6 +181,7 @@ class Buffers:
     """Device buffers of one APA problem (allocated once, reused per call)."""
     fp4: object
     ws_q: object
+    ws_p1: object
     ws_p2: object
     ws_ex: object
     cold_m: object
@@ -197,6 +203,7 @@ def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
     odt = torch.float16 if p.dtype == APA_F16 else torch.bfloat16
     return Buffers(
         fp4=u8(fp4_bytes(p)), ws_q=u8(workspace_bytes(p, CALL_QUANTIZE)),
+        ws_p1=u8(workspace_bytes(p, CALL_PASS1)) if workspace_bytes(p, CALL_PASS1) > 0 else None,
         ws_p2=u8(workspace_bytes(p, CALL_PASS2)), ws_ex=u8(workspace_bytes(p, CALL_EXACT)),
         cold_m=torch.empty((B, Hq, Nq), dtype=torch.int32, device=device),
         cold_l=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device),
@@ -210,7 +217,8 @@ def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
 def apa_forward(p: Problem, q, k, v, eps: float, bufs: Buffers, stream=None):
     """The whole hot path: quantize -> pass 1 -> pass 2 with the fused merge."""
     quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
-    pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, bufs.lam, stream)
+    pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, bufs.lam,
+          ws=bufs.ws_p1, stream=stream)
     pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
           out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
     return bufs.out, bufs.lse

@@ -47,8 +47,11 @@ struct Pass1Out {
 
 hipError_t launch_quantize(const Geom& g, const void* q, const void* k, const void* v,
                            const Fp4Ptrs& f, const QuantWs& ws, hipStream_t s);
+// Pass-1 workspace bytes (0: the problem runs one wave per unit); with ws the
+// long visit orders run as two waves each plus a join kernel.
+size_t pass1_ws_bytes(const Geom& g);
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
-                        const Pass1Out& o, hipStream_t s);
+                        const Pass1Out& o, void* ws, hipStream_t s);
 
 struct Pass2Args {
   const void *q, *k, *v;

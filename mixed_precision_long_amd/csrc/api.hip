@@ -211,6 +211,7 @@ size_t apa_workspace_bytes(const apa_problem* p, int32_t which) {
   if (!valid_problem(p)) return 0;
   switch (which) {
     case APA_CALL_QUANTIZE: return quant_ws(p, nullptr, nullptr);
+    case APA_CALL_PASS1: return pass1_ws_bytes(geom(p));
     case APA_CALL_PASS2: return pass2_ws(p, nullptr, nullptr);
     case APA_CALL_EXACT: return exact_ws(p, nullptr, nullptr);
     default: return 0;
@@ -233,16 +234,20 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
 
 apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
                      float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
-                     void* stream) {
+                     void* ws, size_t ws_bytes, void* stream) {
   if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
   if (!fp4 || !cold_m || !cold_l || !cold_o || !hot_bits) return APA_ERR_INVALID_ARG;
   if (isnan(eps) || eps < 0.0f) return APA_ERR_INVALID_ARG;
   if (!kernels_cover(p, APA_CALL_PASS1)) return APA_ERR_UNSUPPORTED;
   if (empty(p)) return APA_OK;
+  // the workspace is optional: without it every unit runs as one wave
+  const size_t need = pass1_ws_bytes(geom(p));
+  if (need > 0 && ws && ws_bytes < need) return APA_ERR_WORKSPACE;
   Pass1Out o = {cold_m, cold_l, cold_o, hot_bits, lambda_out};
   clear_hip_error();
   return hip_status(launch_pass1(geom(p), fp4_ptrs(p, fp4), eps, p->tau,
-                                 (int)p->hot_frame_offset, o, (hipStream_t)stream));
+                                 (int)p->hot_frame_offset, o, need > 0 ? ws : nullptr,
+                                 (hipStream_t)stream));
 }
 
 apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const void* v,

@@ -43,6 +43,28 @@
 // values 2^-100 below the row maximum).
 // Hot bits are written as whole 32-tile words, so every word of the mask is
 // defined without a clearing pass.
+//
+// Balance.  With fewer units than about three quarters of the chip's wave
+// slots, a wave per unit leaves SIMDs idle while others run two waves, so each
+// long visit order is cut in two and run by two waves of one work group at
+// once: the head wave takes positions [0, h) (tile 0, the diagonal and the
+// recent half), the tail wave positions [h, n).  The tail wave does not know
+// lambda at position h.  It first replays positions [0, 32) without P V (a
+// prefix of the head's walk, so its lambda is a lower bound of the head's),
+// then walks its own tiles with the vote taken against a lower bound plus its
+// own running lambda: the larger of the replayed lambda and the head's
+// current lambda, which the head keeps publishing in LDS (lambda only grows,
+// so any value read is a bound).  A group that fails the bounded test fails
+// the true one, so it is cold for sure; a group that passes it is undecided:
+// it is treated as cold for now (its P V is accumulated) and its per-row l_t,
+// running tail lambda and frame are recorded in the workspace.  At its end the
+// head leaves its state in LDS; the tail waits for it, decides every recorded
+// group against the head's final lambda, takes the P V of the ones that turn
+// out hot back out of its state (the same FP4 codes with the sign bit set, so
+// the subtraction is of exactly what was added), sets their bits, and merges
+// the two states (their frames only scale them).  If the record fills up, or
+// the tail's frame would need a re-base, the tail walks positions [h, n) again
+// from the head's state instead.
 #include "apa_device.h"
 #include "apa_kernels.h"
 
@@ -52,6 +74,15 @@ namespace {
 
 constexpr int kWaves = 4;            // wavefronts per work group
 constexpr float kFrameGuard = 80.0f; // largest lead of m over m_o before re-basing
+constexpr int kMinSplit = 64;        // shortest visit order that runs as two waves
+constexpr int kReplay = 32;          // leading positions the tail wave replays
+constexpr int kCandCap = 1024;       // most undecided tail tiles recorded per unit
+
+enum Role { kWhole = 0, kHead = 1, kTail = 2 };
+
+// a float in LDS (an address-space-3 pointer keeps the accesses DS
+// instructions, which wait on their own counter, not on vector memory)
+typedef __attribute__((address_space(3))) float lds_float;
 
 // Two waves per SIMD up to D = 128; one above, where the output accumulators
 // (D/2 per lane) need the accumulation registers.
@@ -138,151 +169,323 @@ __device__ __forceinline__ void qk(v16f (&acc)[2], const KOps<D>& k, const v4i* 
   }
 }
 
+
+// One unit: 32 query rows of one query head.
+struct UnitId {
+  int b, hk, qb, gi;
+};
+
+// Units are numbered (batch, kv-head, 32-row block, head in group), heads
+// innermost.
+__device__ __forceinline__ UnitId unit_id(const Geom& g, int u) {
+  const int nq32 = g.NqP / 32;
+  UnitId id;
+  id.gi = u % g.G; u /= g.G;
+  id.qb = u % nq32; u /= nq32;
+  id.hk = u % g.Hkv;
+  id.b = u / g.Hkv;
+  return id;
+}
+
+__device__ __forceinline__ int unit_index(const Geom& g, const UnitId& id) {
+  return ((id.b * g.Hkv + id.hk) * (g.NqP / 32) + id.qb) * g.G + id.gi;
+}
+
+// What a wave needs to walk one unit's tiles.
 template <int D>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
-    Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, int nunits) {
+struct Ctx {
+  size_t bhq, bhk;
+  int r0, row, d0, d1, dW;
+  bool row_ok, has_g1;
+  v4i qa[Tile<D>::NH];  // Q^T operand, 16 bytes per 64-channel half
+  int qs[Tile<D>::NH];  // its E8M0 bytes (block scale + head exponent)
+  const uint8_t* blobs;
+  uint32_t koff, ksoff, voff, vsoff;  // this lane's byte offsets inside a blob
+  float g_v;
+  uint32_t *bits0, *bits1;  // hot words of the two verdict groups
+};
+
+template <int D>
+__device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs& f,
+                                         const Pass1Out& out, const UnitId& id, int lane) {
   constexpr int NH = Tile<D>::NH;
+  constexpr int ND = Tile<D>::ND;
+  const int n = lane & 31, hh = lane >> 5;
+  const int hq = id.hk * g.G + id.gi;
+  c.bhq = (size_t)id.b * g.Hq + hq;
+  c.bhk = (size_t)id.b * g.Hkv + id.hk;
+  c.r0 = id.qb * 32;
+  c.row = c.r0 + n;
+  c.row_ok = c.row < g.Nq;
+  auto diag = [&](int lr) { return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile : g.NT - 1; };
+  c.has_g1 = c.r0 + 16 < g.Nq;
+  c.d0 = diag(min(c.r0 + 15, g.Nq - 1));
+  c.d1 = c.has_g1 ? diag(min(c.r0 + 31, g.Nq - 1)) : -1;
+  c.dW = max(c.d0, c.d1);
+  const int jq = (int)f.q_head[c.bhq * 4 + 2];
+  const uint8_t* qc = f.q_codes + (c.bhq * g.NqP + c.row) * (D / 2);
+  const uint8_t* qsc = f.q_scales + (c.bhq * g.NqP + c.row) * (D / 32);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    c.qa[h] = *reinterpret_cast<const v4i*>(qc + 32 * h + 16 * hh);
+    const int sb = (int)qsc[2 * h + hh] + jq;
+    c.qs[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
+  }
+  c.g_v = f.kv_head[c.bhk * 8 + 4];
+  c.blobs = f.kv_blob + c.bhk * (size_t)g.NT * Tile<D>::BLOB;
+  c.koff = n * (D / 2) + 16 * hh;
+  c.ksoff = 32 * D + n * (D / 32);
+  c.voff = 34 * D + n * 32 + 16 * hh;
+  c.vsoff = 66 * D + (2 * n + hh) * ND;
+  c.bits0 = out.bits + (c.bhq * g.NG + (c.r0 >> 4)) * g.W;
+  c.bits1 = c.bits0 + g.W;
+}
+
+// The accumulated cold state of one row (both lane halves hold the row's
+// scalars; o is in the MFMA result layout).
+template <int D>
+struct St {
+  float mf;  // the method's frame: an integer, -inf before the first key
+  int mo;    // the state's frame
+  float lam, lsum;
+  v16f o[Tile<D>::ND];
+};
+
+// Rows past Nq never see a key and sit at frame 127 so every derived quantity
+// stays finite; mo starts far below any frame so that the first tile re-bases.
+template <int D>
+__device__ __forceinline__ void init_state(St<D>& st, bool row_ok) {
+  st.mf = row_ok ? -__builtin_inff() : 127.0f;
+  st.mo = -(1 << 20);
+  st.lam = 0.0f;
+  st.lsum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < Tile<D>::ND; ++i) st.o[i] = v16f{};
+}
+
+// Hot words a walk could not complete by itself: word 0 (tile 0 belongs to the
+// head segment of a split unit) and the word holding both sides of the split
+// point (wb; -1 when the split point is a word boundary or the unit is whole).
+struct Words {
+  int wb;
+  uint32_t p00, p01, p10, p11;  // word 0 / word wb, verdict group 0 / 1
+};
+
+__device__ __forceinline__ int shared_word(int tb) { return ((tb + 1) & 31) ? (tb >> 5) : -1; }
+
+template <int D>
+__device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint32_t b0,
+                                         uint32_t b1, int lane) {
+  if (w == 0) {
+    wd.p00 |= b0;
+    wd.p01 |= b1;
+  } else if (w == wd.wb) {
+    wd.p10 |= b0;
+    wd.p11 |= b1;
+  } else if (lane == 0) {
+    c.bits0[w] = b0;
+    if (c.has_g1) c.bits1[w] = b1;
+  }
+}
+
+// Undecided tail tiles of one unit, in the workspace: the tail's outcome
+// (records kept, or -1 when it gave up and walked again from the head's
+// state), then `cap` records of the tile (with a flag per verdict group) and,
+// per row, l_t, the tail's running lambda and the lazy frame as an offset from
+// the state frame (0 .. 80).
+struct Cand {
+  int* outcome;
+  uint32_t* tile;  // [cap]: tile | group-0 flag << 30 | group-1 flag << 31
+  float* ell;      // [cap][32]
+  float* lamb;     // [cap][32]
+  uint8_t* dm;     // [cap][32]
+};
+
+__host__ __device__ inline size_t cand_stride(int cap) {
+  return ((size_t)cap * 292 + 16 + 255) & ~(size_t)255;
+}
+
+__device__ __forceinline__ Cand cand_of(uint8_t* ws, int unit, int cap) {
+  uint8_t* b = ws + (size_t)unit * cand_stride(cap);
+  return Cand{reinterpret_cast<int*>(b), reinterpret_cast<uint32_t*>(b + 16),
+              reinterpret_cast<float*>(b + 16 + 4 * (size_t)cap),
+              reinterpret_cast<float*>(b + 16 + 132 * (size_t)cap), b + 16 + 260 * (size_t)cap};
+}
+
+// The head wave's final state, handed to the tail wave in LDS.
+template <int D>
+struct HeadState {
+  v4f o[Tile<D>::ND * 4][64];  // o in lane order: float4 chunk q of block db at [4 db + q]
+  float sc[4][64];             // mf, mo (its bits), lambda, l per lane
+  uint32_t words[4];           // partial words: word 0 and word wb, groups 0 and 1
+  int done;
+};
+
+// masking: causal diagonal, padding keys, rows past Nq (wave-uniform test)
+template <int D>
+__device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const Ctx<D>& c, int t,
+                                            int hh) {
+  const int k0 = t * kTile;
+  if ((k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > c.r0 + g.off) || (c.r0 + 31 >= g.Nq)) {
+    const int lim = g.causal ? c.row + g.off : 0x7fffffff;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+        if (!(c.row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+      }
+  }
+}
+
+// group maxima: gown of this lane's 32-key block hh, goth of the other block
+__device__ __forceinline__ void tile_maxima(const v16f (&acc)[2], float& gown, float& goth) {
+  float gl0 = vmax(acc[0][0], acc[0][1]), gl1 = vmax(acc[1][0], acc[1][1]);
+#pragma unroll
+  for (int j = 2; j < 16; j += 2) {
+    gl0 = vmax3(gl0, acc[0][j], acc[0][j + 1]);
+    gl1 = vmax3(gl1, acc[1][j], acc[1][j + 1]);
+  }
+  int x0, x1;
+  swap_halves(__float_as_int(gl0), __float_as_int(gl1), x0, x1);
+  gown = vmax(__int_as_float(x0), __int_as_float(x1));
+  goth = xor32(gown);
+}
+
+// Step 2: the FP4 codes of P for divisors 2^xof (this lane's block) and 2^xtf
+// (the other), rearranged into the MFMA operand layout (lanes < 32 carry keys
+// 0-31, lanes >= 32 keys 32-63).
+__device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float xof, float xtf, int hh) {
+  const int xo = (int)xof, xt = (int)xtf;
+  // fast path: both divisors normal with room below for the codes that matter
+  const bool odd = (unsigned)(xo + 124) > 244u || (unsigned)(xt + 124) > 244u;
+  unsigned pk[2][2];
+  if (__ballot(odd) == 0ull) {
+    const float so = __int_as_float((xo + 127) << 23), st = __int_as_float((xt + 127) << 23);
+    const float sc0 = hh ? st : so, sc1 = hh ? so : st;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float sc = kb ? sc1 : sc0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        unsigned w = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int i = 8 * j + 2 * p;
+          w = cvt_fp4x2(w, fast_exp2(acc[kb][i]), fast_exp2(acc[kb][i + 1]), sc, p);
+        }
+        pk[kb][j] = w;
+      }
+    }
+  } else {
+    // frame-relative form 2^(s - X) with a unit divisor
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const float sub = (kb == hh) ? xof : xtf;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        unsigned w = 0;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int i = 8 * j + 2 * p;
+          w = cvt_fp4x2(w, fast_exp2(acc[kb][i] - sub), fast_exp2(acc[kb][i + 1] - sub), 1.0f, p);
+        }
+        pk[kb][j] = w;
+      }
+    }
+  }
+  int a0, b0, a1, b1;
+  swap_halves((int)pk[0][0], (int)pk[1][0], a0, b0);
+  swap_halves((int)pk[0][1], (int)pk[1][1], a1, b1);
+  return v4i{a0, a1, b0, b1};
+}
+
+// Walks cnt positions of a unit's visit order 0, d, d-1, ..., 1: first the
+// positions 0 .. nrep-1 as a replay (state and vote only: no P V, no hot
+// bits), then positions p0, p0+1, ...  A walk with a replay is a tail walk:
+// after the replay its vote is taken against a lower bound of the head's
+// lambda (the replayed lambda, or what the head has published in `pub_in`,
+// whichever is larger) plus its own lambda; groups that pass are recorded in
+// cr and treated as cold, and it returns the number of records, or -1 when it
+// has to give up (record full, or a re-base of the state frame).  Other walks
+// return 0.  A head walk publishes its lambda from position nrep_tail on in
+// `pub_out`, in the state frame it had there (the frame the tail's replay ends
+// in).
+template <int D>
+__device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, Words& wd, int nrep,
+                                    int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
+                                    int cap, const volatile lds_float* pub_in,
+                                    volatile lds_float* pub_out, int lane) {
   constexpr int ND = Tile<D>::ND;
   constexpr int NW = Tile<D>::NW;
   constexpr int BLOB = Tile<D>::BLOB;
-  const int lane = threadIdx.x & 63;
-  const int n = lane & 31;       // the wave's row handled by this lane
-  const int hh = lane >> 5;      // which half of the K dimension this lane feeds
-  // the wave index is wave-uniform: keep everything derived from it in SGPRs
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int unit = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
-  if (unit >= nunits) return;
-
-  // unit -> (b, kv-head, 32-row block, head in group), heads innermost
-  const int nq32 = g.NqP / 32;
-  int u = unit;
-  const int gi = u % g.G; u /= g.G;
-  const int qb = u % nq32; u /= nq32;
-  const int hk = u % g.Hkv; u /= g.Hkv;
-  const int b = u;
-  const int hq = hk * g.G + gi;
-  const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
-  const int r0 = qb * 32;
-  const int row = r0 + n;
-  const bool row_ok = row < g.Nq;
-  auto diag = [&](int lr) { return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile : g.NT - 1; };
-  const bool has_g1 = r0 + 16 < g.Nq;
-  const int d0 = diag(min(r0 + 15, g.Nq - 1));
-  const int d1 = has_g1 ? diag(min(r0 + 31, g.Nq - 1)) : -1;
-  const int dW = max(d0, d1);
+  const int n = lane & 31;  // the wave's row handled by this lane
+  const int hh = lane >> 5; // which half of the K dimension this lane feeds
   // lanes of verdict group 0 (rows r0 .. r0+15) in both lane halves
   constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
-
-  // Q^T operand (resident): 16 bytes per 64-channel half, E8M0 byte + j
-  v4i qa[NH];
-  int qs[NH];
-  {
-    const int jq = (int)f.q_head[bhq * 4 + 2];
-    const uint8_t* qc = f.q_codes + (bhq * g.NqP + row) * (D / 2);
-    const uint8_t* qsc = f.q_scales + (bhq * g.NqP + row) * (D / 32);
-#pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      qa[h] = *reinterpret_cast<const v4i*>(qc + 32 * h + 16 * hh);
-      const int sb = (int)qsc[2 * h + hh] + jq;
-      qs[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
-    }
-  }
-  const float g_v = f.kv_head[bhk * 8 + 4];
-  const uint8_t* blobs = f.kv_blob + bhk * (size_t)g.NT * BLOB;
-  // this lane's byte offsets inside a blob
-  const uint32_t koff = n * (D / 2) + 16 * hh;
-  const uint32_t ksoff = 32 * D + n * (D / 32);
-  const uint32_t voff = 34 * D + n * 32 + 16 * hh;
-  const uint32_t vsoff = 66 * D + (2 * n + hh) * ND;
-
-  // frames: mf is the method's (an integer; -inf before the first key), mo the
-  // state's.  Rows past Nq never see a key and sit at frame 127 so every
-  // derived quantity stays finite; mo starts far below any frame so that the
-  // first tile re-bases.
-  float mf = row_ok ? -__builtin_inff() : 127.0f;
-  int mo = -(1 << 20);
-  float lam = 0.0f, lsum = 0.0f;
-  v16f o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) o[i] = v16f{};
-  const float Hf = (float)hoff;
-
-  // hot-bit words: zero the words above each group's diagonal word first
-  uint32_t* bits0 = out.bits + (bhq * g.NG + (r0 >> 4)) * g.W;
-  uint32_t* bits1 = bits0 + g.W;
-  for (int w = d0 / 32 + 1 + lane; w < g.W; w += 64) bits0[w] = 0u;
-  if (has_g1)
-    for (int w = d1 / 32 + 1 + lane; w < g.W; w += 64) bits1[w] = 0u;
-  uint32_t tile0_b0 = 0, tile0_b1 = 0, cur_b0 = 0, cur_b1 = 0;
+  const bool tail = nrep > 0;
+  auto tile_at = [&](int i) {
+    const int p = i < nrep ? i : p0 + (i - nrep);
+    return p == 0 ? 0 : c.dW - p + 1;
+  };
+  float lam_lo = 0.0f;
+  int mo_ref = 0;
+  int ncand = 0;
+  bool gave_up = false;  // leaves the loop at its latch (one exit keeps the state in place)
   int cur_w = -1;
+  uint32_t cur_b0 = 0, cur_b1 = 0;
 
-  const int ntiles = dW + 1;
-  auto tile_of = [&](int it) { return it == 0 ? 0 : dW - it + 1; };
-
-  // pipeline: when tile it starts, its scores are in acc and the K operand of
-  // tile it+1 in kn; once this tile's P is formed, QK(it+1) is issued into acc
-  // and K of tile it+2 is fetched into kn (prefetches past the last tile
-  // re-read the last tile: in bounds, unused)
-  auto next_blob = [&](int it) { return blobs + (size_t)tile_of(min(it, ntiles - 1)) * BLOB; };
+  // pipeline: when position i starts, its scores are in acc and the K operand
+  // of position i+1 in kn; once this tile's P is formed, QK(i+1) is issued into
+  // acc and K of position i+2 is fetched into kn (prefetches past the last
+  // position re-read the last tile: in bounds, unused)
+  auto next_blob = [&](int i) { return c.blobs + (size_t)tile_at(min(i, cnt - 1)) * BLOB; };
   KOps<D> kn;
   v16f acc[2];
-  load_k<D>(kn, blobs, koff, ksoff, hh);
-  qk<D>(acc, kn, qa, qs);
-  load_k<D>(kn, next_blob(1), koff, ksoff, hh);
+  load_k<D>(kn, next_blob(0), c.koff, c.ksoff, hh);
+  qk<D>(acc, kn, c.qa, c.qs);
+  load_k<D>(kn, next_blob(1), c.koff, c.ksoff, hh);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int t = tile_of(it);
-    const uint8_t* blob = blobs + (size_t)t * BLOB;
+  for (int i = 0; i < cnt && !gave_up; ++i) {
+    const int t = tile_at(i);
+    const bool replay = i < nrep;
+    if (tail && i == nrep) {
+      lam_lo = st.lam;
+      st.lam = 0.0f;
+    }
+    if (i == kReplay) mo_ref = st.mo;
+    const uint8_t* blob = c.blobs + (size_t)t * BLOB;
     // V^T operand and scales of this tile (used at its end)
     v4i va[ND];
     uint32_t vsw[NW];
 #pragma unroll
     for (int db = 0; db < ND; ++db)
-      va[db] = *reinterpret_cast<const v4i*>(blob + voff + db * 32 * 32);
-    load_scales<D>(vsw, blob + vsoff);
+      va[db] = *reinterpret_cast<const v4i*>(blob + c.voff + db * 32 * 32);
+    load_scales<D>(vsw, blob + c.vsoff);
 
-    const int k0 = t * kTile;
-    const bool vis0 = t <= d0, vis1 = t <= d1;
-    // masking: causal diagonal, padding keys, rows past Nq (wave-uniform test)
-    if ((k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) || (r0 + 31 >= g.Nq)) {
-      const int lim = g.causal ? row + g.off : 0x7fffffff;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (!(row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
-        }
-    }
-    // group maxima: gown of this lane's block hh, goth of the other block
-    float gl0 = vmax(acc[0][0], acc[0][1]), gl1 = vmax(acc[1][0], acc[1][1]);
-#pragma unroll
-    for (int j = 2; j < 16; j += 2) {
-      gl0 = vmax3(gl0, acc[0][j], acc[0][j + 1]);
-      gl1 = vmax3(gl1, acc[1][j], acc[1][j + 1]);
-    }
-    int x0, x1;
-    swap_halves(__float_as_int(gl0), __float_as_int(gl1), x0, x1);
-    const float gown = vmax(__int_as_float(x0), __int_as_float(x1));
-    const float goth = xor32(gown);
-    const float c = vmax(gown, goth);
+    const bool vis0 = t <= c.d0, vis1 = t <= c.d1;
+    mask_scores<D>(acc, g, c, t, hh);
+    float gown, goth;
+    tile_maxima(acc, gown, goth);
+    const float cmax = vmax(gown, goth);
 
     // ---- lazy maximum (integer frame)
-    const bool fire = c > mf + tau;     // never for a row without a visible key here
-    const float mcf = fire ? ceilf(c) : mf;
+    const bool fire = cmax > st.mf + tau;  // never for a row without a visible key here
+    const float mcf = fire ? ceilf(cmax) : st.mf;
 
     // re-base the state to m_o = max(m, mc - H), a lower bound of every later
     // frame, when the frame has run too far ahead (all lanes; exact powers of two)
-    if (__ballot(mcf - (float)mo > kFrameGuard) != 0ull) {
-      const int mo_new = (int)vmax(mf, mcf - Hf);
-      const int sh = mo - mo_new;
+    if (__ballot(mcf - (float)st.mo > kFrameGuard) != 0ull) {
+      if (tail && !replay) gave_up = true;
+      const int mo_new = (int)vmax(st.mf, mcf - Hf);
+      const int sh = st.mo - mo_new;
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] = ldexpf(o[db][j], sh);
-      lsum = ldexpf(lsum, sh);
-      lam = ldexpf(lam, sh);
-      mo = mo_new;
+        for (int j = 0; j < 16; ++j) st.o[db][j] = ldexpf(st.o[db][j], sh);
+      st.lsum = ldexpf(st.lsum, sh);
+      st.lam = ldexpf(st.lam, sh);
+      st.mo = mo_new;
     }
 
     // ---- step 2: the conversion divisor 2^X of each 32-key group,
@@ -290,54 +493,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     const float lo = mcf - 127.0f;
     const float xof = vmax(ceilf(gown - kLog2_6), lo);
     const float xtf = vmax(ceilf(goth - kLog2_6), lo);
-    const int xo = (int)xof, xt = (int)xtf;
-    // fast path: both divisors normal with room below for the codes that matter
-    const bool odd = (unsigned)(xo + 124) > 244u || (unsigned)(xt + 124) > 244u;
-    unsigned pk[2][2];
-    if (__ballot(odd) == 0ull) {
-      const float so = __int_as_float((xo + 127) << 23), st = __int_as_float((xt + 127) << 23);
-      const float sc0 = hh ? st : so, sc1 = hh ? so : st;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float sc = kb ? sc1 : sc0;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          unsigned w = 0;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int i = 8 * j + 2 * p;
-            w = cvt_fp4x2(w, fast_exp2(acc[kb][i]), fast_exp2(acc[kb][i + 1]), sc, p);
-          }
-          pk[kb][j] = w;
-        }
-      }
-    } else {
-      // frame-relative form 2^(s - X) with a unit divisor
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const float sub = (kb == hh) ? xof : xtf;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          unsigned w = 0;
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const int i = 8 * j + 2 * p;
-            w = cvt_fp4x2(w, fast_exp2(acc[kb][i] - sub), fast_exp2(acc[kb][i + 1] - sub), 1.0f, p);
-          }
-          pk[kb][j] = w;
-        }
-      }
-    }
-    // operand layout: lanes < 32 carry keys 0-31, lanes >= 32 keys 32-63
-    v4i pb;
-    {
-      int a0, b0, a1, b1;
-      swap_halves((int)pk[0][0], (int)pk[1][0], a0, b0);
-      swap_halves((int)pk[0][1], (int)pk[1][1], a1, b1);
-      pb = v4i{a0, a1, b0, b1};
-    }
+    const v4i pb = p_operand(acc, xof, xtf, hh);
     // E8M0 byte of this lane's 32-key group in the state's frame
-    const int pscale = xo - mo + 127;
+    const int pscale = (int)xof - st.mo + 127;
 
     // ---- step 3: l_t as an MFMA of the quantised P itself (state's frame)
     const v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
@@ -345,44 +503,59 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     // this tile's scores are consumed: the next tile's go to the matrix cores
     // behind the row sum and run during the vote and the P V product
     __builtin_amdgcn_sched_barrier(0);
-    qk<D>(acc, kn, qa, qs);
-    load_k<D>(kn, next_blob(it + 2), koff, ksoff, hh);
+    qk<D>(acc, kn, c.qa, c.qs);
+    load_k<D>(kn, next_blob(i + 2), c.koff, c.ksoff, hh);
     const float ell = ones_acc[0];
 
     // ---- step 4: the hot test (lambda includes this tile)
-    lam += ell;
-    const unsigned long long hb = __ballot(ell > eps * lam && hh == 0);
-    const bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
-    const bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
+    st.lam += ell;
+    if (pub_out && i >= kReplay && hh == 0) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
+    float lam_b = lam_lo;
+    if (pub_in && !replay) lam_b = vmax(lam_b, pub_in[n]);
+    const unsigned long long hb = __ballot(ell > eps * (lam_b + st.lam) && hh == 0);
+    bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
+    bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
+    if (tail && !replay && eps != 0.0f && (hot0 || hot1)) {
+      // undecided under the lower bound: record it and treat it as cold for
+      // now
+      if (ncand == cap) {
+        gave_up = true;
+      } else {
+        if (lane == 0)
+          cr.tile[ncand] = (uint32_t)t | (hot0 ? 1u << 30 : 0u) | (hot1 ? 1u << 31 : 0u);
+        if (hh == 0) {
+          cr.ell[ncand * 32 + n] = ell;
+          cr.lamb[ncand * 32 + n] = st.lam;
+          cr.dm[ncand * 32 + n] = (uint8_t)((int)mcf - st.mo);
+        }
+        ++ncand;
+      }
+      hot0 = hot1 = false;
+    }
     const unsigned long long hot_lanes = (hot0 ? kGroup0 : 0ull) | (hot1 ? ~kGroup0 : 0ull);
     const bool my_hot = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
 
     // ---- frame update: cold -> mc; hot -> max(m, mc - H), which is m unless
     // the lazy test fired
-    mf = my_hot ? vmax(mf, mcf - Hf) : mcf;
+    st.mf = my_hot ? vmax(st.mf, mcf - Hf) : mcf;
 
-    // ---- step 5: cold tiles accumulate P V in FP4
-    const bool cold0 = vis0 && !hot0, cold1 = vis1 && !hot1;
+    // ---- step 5: cold tiles accumulate P V in FP4 (not while replaying)
+    const bool cold0 = !replay && vis0 && !hot0, cold1 = !replay && vis1 && !hot1;
     if (cold0 || cold1) {
       const unsigned long long cold_lanes = (cold0 ? kGroup0 : 0ull) | (cold1 ? ~kGroup0 : 0ull);
       const bool keep = __builtin_amdgcn_inverse_ballot_w64(cold_lanes);
       const v4i pz = keep ? pb : v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] = mfma4(va[db], pz, o[db], (int)vsw[db >> 2], db & 3, pscale);
-      lsum = keep ? lsum + ell : lsum;
+      for (int db = 0; db < ND; ++db)
+        st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
+      st.lsum = keep ? st.lsum + ell : st.lsum;
     }
 
-    // ---- hot bits, whole words
-    if (it == 0) {
-      tile0_b0 = hot0 ? 1u : 0u;
-      tile0_b1 = hot1 ? 1u : 0u;
-    } else {
+    // ---- hot bits, whole words (visited in descending order after tile 0)
+    if (!replay) {
       const int w = t >> 5;
       if (w != cur_w) {
-        if (cur_w > 0 && lane == 0) {
-          bits0[cur_w] = cur_b0;
-          if (has_g1) bits1[cur_w] = cur_b1;
-        }
+        if (cur_w >= 0) put_word(c, wd, cur_w, cur_b0, cur_b1, lane);
         cur_w = w;
         cur_b0 = cur_b1 = 0u;
       }
@@ -390,60 +563,350 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       if (hot1) cur_b1 |= 1u << (t & 31);
     }
   }
-  // flush the last word (word 0, which also holds tile 0)
-  if (lane == 0) {
-    if (cur_w > 0) {
-      bits0[cur_w] = cur_b0;
-      if (has_g1) bits1[cur_w] = cur_b1;
+  if (cur_w >= 0) put_word(c, wd, cur_w, cur_b0, cur_b1, lane);
+  return gave_up ? -1 : ncand;
+}
+
+// The cold state's outputs in the method's frame m = mf (o * 2^(mo - m) * g_v,
+// with the power of two folded into g_v: exact).
+template <int D>
+__device__ __forceinline__ void store_state(const Geom& g, const Ctx<D>& c, const Pass1Out& out,
+                                            const St<D>& st, int lane) {
+  if (!c.row_ok) return;
+  const int hh = lane >> 5;
+  const size_t r = c.bhq * g.Nq + c.row;
+  const int m = (int)st.mf;
+  const int sh = st.mo - m;
+  if (hh == 0) {
+    out.m[r] = m;
+    out.l[r] = ldexpf(st.lsum, sh);
+    if (out.lam) out.lam[r] = ldexpf(st.lam, sh);
+  }
+  const float gs = ldexpf(c.g_v, sh);
+  float* orow = out.o + r * D;
+#pragma unroll
+  for (int db = 0; db < Tile<D>::ND; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v4f x = {st.o[db][4 * q] * gs, st.o[db][4 * q + 1] * gs, st.o[db][4 * q + 2] * gs,
+               st.o[db][4 * q + 3] * gs};
+      *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
     }
-    bits0[0] = tile0_b0 | (cur_w == 0 ? cur_b0 : 0u);
-    if (has_g1) bits1[0] = tile0_b1 | (cur_w == 0 ? cur_b1 : 0u);
+}
+
+// zero the hot words above each group's diagonal word
+template <int D>
+__device__ __forceinline__ void zero_above(const Geom& g, const Ctx<D>& c, int lane) {
+  for (int w = c.d0 / 32 + 1 + lane; w < g.W; w += 64) c.bits0[w] = 0u;
+  if (c.has_g1)
+    for (int w = c.d1 / 32 + 1 + lane; w < g.W; w += 64) c.bits1[w] = 0u;
+}
+
+// The tail's end of a split unit, once the head's final state is in LDS:
+// decide the recorded groups against the head's lambda, take the P V of those
+// that are hot after all back out of the tail's state (the same FP4 codes with
+// their sign bits set, so exactly what was added), and set their bits.
+template <int D>
+__device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st, Words& tw,
+                                       const Cand& cr, int ncand, float lam_a, float eps,
+                                       int lane) {
+  constexpr int ND = Tile<D>::ND;
+  constexpr int NW = Tile<D>::NW;
+  constexpr int BLOB = Tile<D>::BLOB;
+  constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
+  const int n = lane & 31, hh = lane >> 5;
+  constexpr int kBatch = 8;  // records decided per round of loads
+  for (int j0 = 0; j0 < ncand; j0 += kBatch) {
+    float e[kBatch], lbv[kBatch];
+    uint32_t hd[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int j = min(j0 + k, ncand - 1);
+      hd[k] = cr.tile[j];
+      e[k] = cr.ell[j * 32 + n];
+      lbv[k] = cr.lamb[j * 32 + n];
+    }
+    uint32_t found = 0;  // 2 bits per record: groups hot after all
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const unsigned long long hb = __ballot(e[k] > eps * (lam_a + lbv[k]) && hh == 0);
+      const uint32_t hdr = (uint32_t)__builtin_amdgcn_readfirstlane((int)hd[k]);
+      const uint32_t gr = ((hdr >> 30 & 1u) && (hb & 0xFFFFull) != 0ull ? 1u : 0u) |
+                          ((hdr >> 31) && (hb & 0xFFFF0000ull) != 0ull ? 2u : 0u);
+      if (j0 + k < ncand) found |= gr << (2 * k);
+    }
+    found = (uint32_t)__builtin_amdgcn_readfirstlane((int)found);
+    while (found) {
+      const int kr = __builtin_ctz(found) >> 1;
+      const uint32_t gr = (found >> (2 * kr)) & 3u;
+      found &= ~(3u << (2 * kr));
+      const int j = j0 + kr;
+      const uint32_t hdr = (uint32_t)__builtin_amdgcn_readfirstlane((int)cr.tile[j]);
+      const int t = (int)(hdr & 0x3FFFFFFFu);
+      const float ell = cr.ell[j * 32 + n];
+      const float mcf = (float)(st.mo + (int)cr.dm[j * 32 + n]);
+      const bool f0 = gr & 1u, f1 = gr & 2u;
+      KOps<D> k;
+      v16f acc[2];
+      const uint8_t* blob = c.blobs + (size_t)t * BLOB;
+      load_k<D>(k, blob, c.koff, c.ksoff, hh);
+      qk<D>(acc, k, c.qa, c.qs);
+      mask_scores<D>(acc, g, c, t, hh);
+      float gown, goth;
+      tile_maxima(acc, gown, goth);
+      const float lo = mcf - 127.0f;
+      const float xof = vmax(ceilf(gown - kLog2_6), lo);
+      const float xtf = vmax(ceilf(goth - kLog2_6), lo);
+      const v4i pb = p_operand(acc, xof, xtf, hh);
+      const int pscale = (int)xof - st.mo + 127;
+      const unsigned long long hot_lanes = (f0 ? kGroup0 : 0ull) | (f1 ? ~kGroup0 : 0ull);
+      const bool keep = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
+      const int neg = (int)0x88888888u;
+      const v4i pz = keep ? (pb ^ v4i{neg, neg, neg, neg}) : v4i{0, 0, 0, 0};
+      v4i va[ND];
+      uint32_t vsw[NW];
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        va[db] = *reinterpret_cast<const v4i*>(blob + c.voff + db * 32 * 32);
+      load_scales<D>(vsw, blob + c.vsoff);
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+        st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
+      st.lsum = keep ? st.lsum - ell : st.lsum;
+      const int w = t >> 5;
+      const uint32_t bit = 1u << (t & 31);
+      if (w == 0) {
+        if (f0) tw.p00 |= bit;
+        if (f1) tw.p01 |= bit;
+      } else if (w == tw.wb) {
+        if (f0) tw.p10 |= bit;
+        if (f1) tw.p11 |= bit;
+      } else if (lane == 0) {
+        if (f0) c.bits0[w] |= bit;
+        if (f1) c.bits1[w] |= bit;
+      }
+    }
+  }
+}
+
+// One wave per unit, or, with a split workspace, two: a unit's head and tail
+// waves sit in one work group (waves numbered (unit, role)).  The head hands
+// its running lambda to the tail through LDS while both walk, and its final
+// state at its end; the tail finishes the unit.  Units are numbered (batch,
+// kv-head, 32-row block, head), so the waves of a work group, and the groups
+// of an XCD, stream the same tiles.
+template <int D>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
+    Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
+    int nwaves) {
+  constexpr int ND = Tile<D>::ND;
+  // per head/tail pair of the group: the head's running lambda and final state
+  __shared__ float pub[kWaves / 2][32];
+  __shared__ HeadState<D> hs[kWaves / 2];
+  const int lane = threadIdx.x & 63;
+  const int hh = lane >> 5;
+  // the wave index is wave-uniform: keep everything derived from it in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int slot = wave >> 1;
+  if (lane < 32) pub[slot][lane] = 0.0f;
+  if (lane == 0) hs[slot].done = 0;
+  __syncthreads();
+  int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
+  if (w >= nwaves) return;
+
+  const int nq32 = g.NqP / 32;
+  int role = kWhole;
+  if (split) {
+    role = (w & 1) ? kTail : kHead;
+    w >>= 1;
+  }
+  UnitId id;
+  id.gi = w % g.G; w /= g.G;
+  id.qb = w % nq32; w /= nq32;
+  id.hk = w % g.Hkv;
+  id.b = w / g.Hkv;
+
+  Ctx<D> c;
+  make_ctx<D>(c, g, f, out, id, lane);
+  const int npos = c.dW + 1;
+  if (role != kWhole && npos < kMinSplit) {
+    if (role == kTail) return;
+    role = kWhole;
+  }
+  const int h = (npos + kReplay) / 2;  // head positions [0, h), tail [h, npos)
+  const int wb = role == kWhole ? -1 : shared_word(c.dW - h + 1);
+
+  St<D> st;
+  init_state<D>(st, c.row_ok);
+  Words wd = {wb, 0u, 0u, 0u, 0u};
+  if (role != kTail) zero_above<D>(g, c, lane);
+  int nrep = 0, p0 = 0, cnt = npos;
+  if (role == kHead) cnt = h;
+  if (role == kTail) {
+    nrep = kReplay;
+    p0 = h;
+    cnt = kReplay + npos - h;
+  }
+  const Cand cr = role == kTail ? cand_of(split, unit_index(g, id), cap)
+                                : Cand{nullptr, nullptr, nullptr, nullptr, nullptr};
+  volatile lds_float* pin = role == kTail ? (volatile lds_float*)pub[slot] : nullptr;
+  volatile lds_float* pout = role == kHead ? (volatile lds_float*)pub[slot] : nullptr;
+  const float Hf = (float)hoff;
+  auto wait_head = [&]() {
+    while (__hip_atomic_load(&hs[slot].done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(2);
+  };
+  int outcome = 0;
+  bool redone = false;
+  // one call site of the walk: a tail that gave up walks again, from the
+  // head's final state, over its own positions
+  for (;;) {
+    outcome = walk<D>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout, lane);
+    if (role != kTail) break;
+    if (!redone && lane == 0) *cr.outcome = outcome;
+    wait_head();
+    if (redone || outcome >= 0) break;
+    redone = true;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const v4f x = hs[slot].o[4 * db + q][lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.o[db][4 * q + e] = x[e];
+      }
+    st.mf = hs[slot].sc[0][lane];
+    st.mo = __float_as_int(hs[slot].sc[1][lane]);
+    st.lam = hs[slot].sc[2][lane];
+    st.lsum = hs[slot].sc[3][lane];
+    wd = Words{wb, 0u, 0u, 0u, 0u};
+    nrep = 0;
+    p0 = h;
+    cnt = npos - h;
+    pin = nullptr;
   }
 
-  // ---- outputs of the cold state, in the method's frame m
-  if (row_ok) {
-    const size_t r = bhq * g.Nq + row;
-    const int m = (int)mf;
-    const int sh = mo - m;
+  if (role == kHead) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        hs[slot].o[4 * db + q][lane] = v4f{st.o[db][4 * q], st.o[db][4 * q + 1],
+                                           st.o[db][4 * q + 2], st.o[db][4 * q + 3]};
+    hs[slot].sc[0][lane] = st.mf;
+    hs[slot].sc[1][lane] = __int_as_float(st.mo);
+    hs[slot].sc[2][lane] = st.lam;
+    hs[slot].sc[3][lane] = st.lsum;
+    if (lane == 0) {
+      hs[slot].words[0] = wd.p00;
+      hs[slot].words[1] = wd.p01;
+      hs[slot].words[2] = wd.p10;
+      hs[slot].words[3] = wd.p11;
+      __hip_atomic_store(&hs[slot].done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    return;
+  }
+  if (role == kTail) {
+    // the shared words: the head's part and the tail's (or the re-walk's)
+    const uint32_t hw0 = hs[slot].words[0], hw1 = hs[slot].words[1];
+    const uint32_t hw2 = hs[slot].words[2], hw3 = hs[slot].words[3];
+    float a_mf = 0.0f, a_lam = 0.0f, a_lsum = 0.0f;
+    int a_mo = 0;
+    if (!redone) {
+      a_mf = hs[slot].sc[0][lane];
+      a_mo = __float_as_int(hs[slot].sc[1][lane]);
+      a_lam = hs[slot].sc[2][lane];
+      a_lsum = hs[slot].sc[3][lane];
+      // the head's lambda in the tail's state frame (the tail never re-based)
+      settle<D>(g, c, st, wd, cr, outcome, ldexpf(a_lam, a_mo - st.mo), eps, lane);
+    }
+    if (lane == 0) {
+      c.bits0[0] = hw0 | wd.p00;
+      if (c.has_g1) c.bits1[0] = hw1 | wd.p01;
+      if (wb > 0) {
+        c.bits0[wb] = hw2 | wd.p10;
+        if (c.has_g1) c.bits1[wb] = hw3 | wd.p11;
+      }
+    }
+    if (redone) {
+      store_state<D>(g, c, out, st, lane);
+      return;
+    }
+    // merge: the larger frame, each state scaled into it by an exact power of two
+    if (!c.row_ok) return;
+    const size_t r = c.bhq * g.Nq + c.row;
+    const int m = (int)vmax(a_mf, st.mf);
+    const int sa = a_mo - m, sb = st.mo - m;
     if (hh == 0) {
       out.m[r] = m;
-      out.l[r] = ldexpf(lsum, sh);
-      if (out.lam) out.lam[r] = ldexpf(lam, sh);
+      out.l[r] = ldexpf(a_lsum, sa) + ldexpf(st.lsum, sb);
+      if (out.lam) out.lam[r] = ldexpf(a_lam, sa) + ldexpf(st.lam, sb);
     }
-    // o * 2^sh * g_v, with 2^sh folded into g_v (exact)
-    const float gs = ldexpf(g_v, sh);
     float* orow = out.o + r * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v4f x = {o[db][4 * q] * gs, o[db][4 * q + 1] * gs, o[db][4 * q + 2] * gs,
-                 o[db][4 * q + 3] * gs};
+        const v4f xa = hs[slot].o[4 * db + q][lane];
+        v4f x;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[e] = (ldexpf(xa[e], sa) + ldexpf(st.o[db][4 * q + e], sb)) * c.g_v;
         *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
       }
+    return;
   }
+  // a whole unit: word 0 (which also holds tile 0) and the state
+  if (lane == 0) {
+    c.bits0[0] = wd.p00;
+    if (c.has_g1) c.bits1[0] = wd.p01;
+  }
+  store_state<D>(g, c, out, st, lane);
 }
+
+// Two waves per unit pay off while there are at most about three quarters as
+// many units as wave slots, and only for visit orders long enough to cut.
+bool split_pays(const Geom& g) {
+  const long units = (long)g.B * g.Hkv * (g.NqP / 32) * g.G;
+  const long slots = 1024L * (g.D >= 256 ? 1 : 2);
+  return units > 0 && 4 * units <= 3 * slots && g.NT >= kMinSplit;
+}
+
+// Records per unit: every tail position of the longest visit order, at most
+// kCandCap.
+int cand_cap(const Geom& g) { return min(kCandCap, g.NT - (g.NT + kReplay) / 2); }
+
+}  // namespace
+
+size_t pass1_ws_bytes(const Geom& g) {
+  if (!split_pays(g)) return 0;
+  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g));
+}
+
+namespace {
 
 template <int D>
 hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
-               const Pass1Out& o, hipStream_t s) {
+               const Pass1Out& o, void* ws, hipStream_t s) {
   const int nunits = g.B * g.Hkv * (g.NqP / 32) * g.G;
   if (nunits == 0) return hipSuccess;
-  const int nblocks = (nunits + kWaves - 1) / kWaves;
+  uint8_t* split = (ws && split_pays(g)) ? static_cast<uint8_t*>(ws) : nullptr;
+  const int nwaves = split ? 2 * nunits : nunits;
+  const int nblocks = (nwaves + kWaves - 1) / kWaves;
   hipLaunchKernelGGL(k_pass1<D>, dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau, hoff, o,
-                     nunits);
+                     split, split ? cand_cap(g) : 0, nwaves);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
-                        const Pass1Out& o, hipStream_t s) {
+                        const Pass1Out& o, void* ws, hipStream_t s) {
   switch (g.D) {
-    case 64: return run<64>(g, f, eps, tau, hoff, o, s);
-    case 128: return run<128>(g, f, eps, tau, hoff, o, s);
-    case 256: return run<256>(g, f, eps, tau, hoff, o, s);
-    case 512: return run<512>(g, f, eps, tau, hoff, o, s);
+    case 64: return run<64>(g, f, eps, tau, hoff, o, ws, s);
+    case 128: return run<128>(g, f, eps, tau, hoff, o, ws, s);
+    case 256: return run<256>(g, f, eps, tau, hoff, o, ws, s);
+    case 512: return run<512>(g, f, eps, tau, hoff, o, ws, s);
     default: return hipErrorInvalidValue;
   }
 }

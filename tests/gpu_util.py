@@ -90,14 +90,42 @@ def unpack_bits(p, words: np.ndarray) -> np.ndarray:
     return bits.reshape(p.B, p.Hq, NG, W * 32)[..., :NT].astype(bool)
 
 
-def run_gpu(p, Q, K, V, eps, dtype="fp16", fused=True, lam=True):
-    """Whole APA forward on the GPU; returns numpy copies of every output."""
+# Pass-1 workspace of a split problem (the layout of pass1.hip's Cand): per
+# 32-row block the tail's outcome (records kept, or -1: it gave up and walked
+# again from the head's state) in the first 4 bytes, then `cap` records of 292
+# bytes, cap = min(1024, the longest tail), the block's stride rounded to 256.
+def tail_outcomes(p, ws) -> np.ndarray:
+    """Outcome of every block whose visit order was cut: number of undecided
+    tail tiles decided at the end, or -1 where the tail walked again."""
+    G, NT, nq32 = p.Hq // p.Hkv, -(-p.Nkv // 64), -(-p.Nq // 32)
+    cap = min(1024, NT - (NT + 32) // 2)
+    stride = (cap * 292 + 16 + 255) // 256 * 256
+    raw = ws.cpu().numpy()
+    out = []
+    for b in range(p.B):
+        for hk in range(p.Hkv):
+            for qb in range(nq32):
+                last = min(qb * 32 + 31, p.Nq - 1)
+                dW = min(p.Nkv - 1, last + p.Nkv - p.Nq) // 64 if p.is_causal else NT - 1
+                if dW + 1 < 64:
+                    continue
+                for gi in range(G):
+                    u = ((b * p.Hkv + hk) * nq32 + qb) * G + gi
+                    out.append(int(raw[u * stride:u * stride + 4].view(np.int32)[0]))
+    return np.array(out, np.int64)
+
+
+def run_gpu(p, Q, K, V, eps, dtype="fp16", fused=True, lam=True, split=True):
+    """Whole APA forward on the GPU; returns numpy copies of every output.
+    split=False runs pass 1 without its workspace (one wave per 32-row block)."""
     import torch
     q, k, v = torch_inputs(Q, K, V, dtype)
     bufs = apa.alloc(p, with_lambda=lam)
     apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q)
-    apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, bufs.lam)
-    res = {}
+    ws1 = bufs.ws_p1 if split else None
+    apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, bufs.lam,
+              ws=ws1)
+    res = {"tail": tail_outcomes(p, ws1) if ws1 is not None else None}
     if fused:
         apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
                   out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2)

@@ -54,7 +54,11 @@ def test_sizes_and_layout():
     assert L.kbar - L.kv_blobs == 8 * 1920 * 8704
     assert apa.fp4_bytes(p) == L.total
     assert apa.hotmask_bytes(p) == 24 * 128 * 60 * 4
-    assert apa.workspace_bytes(p, apa.CALL_PASS1) == 0
+    assert apa.workspace_bytes(p, apa.CALL_PASS1) > 0
+    # enough row blocks to fill the GPU, or visit orders too short to cut:
+    # pass 1 runs one wave per block and needs no workspace
+    assert apa.workspace_bytes(prob(Nq=32768, Nkv=32768, Hq=32), apa.CALL_PASS1) == 0
+    assert apa.workspace_bytes(prob(Nkv=4000), apa.CALL_PASS1) == 0
     assert apa.workspace_bytes(p, apa.CALL_QUANTIZE) > 0
     assert apa.workspace_bytes(p, apa.CALL_PASS2) > 0
     # ragged shapes round up
@@ -79,11 +83,11 @@ def test_null_pointers_and_bad_arguments():
     p = prob()
     assert L.apa_quantize(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1, None) == apa.APA_ERR_INVALID_ARG
     assert L.apa_quantize(C.byref(p), None, FAKE, FAKE, FAKE, FAKE, 1, None) == apa.APA_ERR_INVALID_ARG
-    assert L.apa_pass1(C.byref(p), FAKE, 0.01, None, FAKE, FAKE, FAKE, None, None) == \
-        apa.APA_ERR_INVALID_ARG
+    assert L.apa_pass1(C.byref(p), FAKE, 0.01, None, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                       None) == apa.APA_ERR_INVALID_ARG
     for eps in (float("nan"), -0.1):
-        assert L.apa_pass1(C.byref(p), FAKE, eps, FAKE, FAKE, FAKE, FAKE, None, None) == \
-            apa.APA_ERR_INVALID_ARG
+        assert L.apa_pass1(C.byref(p), FAKE, eps, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 40,
+                           None) == apa.APA_ERR_INVALID_ARG
     # pass 2: fuse flag, and the pointers each mode needs
     args = [FAKE] * 8
     assert L.apa_pass2(C.byref(p), *args, 2, FAKE, None, None, None, None, FAKE, 1 << 40, None) == \
@@ -111,6 +115,12 @@ def test_workspace_too_small():
     assert need_ex > 0
     assert L.apa_exact(C.byref(few), FAKE, FAKE, FAKE, FAKE, None, FAKE, need_ex - 1, None) == \
         apa.APA_ERR_WORKSPACE
+    # pass 1 runs split (two waves per 32-row block) while the blocks do not
+    # fill the GPU: 1536 of them at 2048 x 122880 with 24 over 8 heads
+    need1 = apa.workspace_bytes(p, apa.CALL_PASS1)
+    assert need1 > 0
+    assert L.apa_pass1(C.byref(p), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, FAKE, need1 - 1,
+                       None) == apa.APA_ERR_WORKSPACE
     need2 = apa.workspace_bytes(p, apa.CALL_PASS2)
     assert L.apa_pass2(C.byref(p), *([FAKE] * 8), 1, FAKE, None, None, None, None, FAKE, need2 - 1,
                        None) == apa.APA_ERR_WORKSPACE
@@ -130,7 +140,8 @@ def test_empty_problems_do_nothing():
     L = apa.lib()
     for kw in ({"Nq": 0}, {"B": 0}):
         p = prob(**kw)
-        assert L.apa_pass1(C.byref(p), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None) == apa.APA_OK
+        assert L.apa_pass1(C.byref(p), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                           None) == apa.APA_OK
         assert L.apa_exact(C.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == apa.APA_OK
         assert L.apa_merge(C.byref(p), *([FAKE] * 8), None, None) == apa.APA_OK
         assert L.apa_pass2(C.byref(p), *([FAKE] * 8), 1, FAKE, None, None, None, None, FAKE, 1 << 40,

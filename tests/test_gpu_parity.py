@@ -72,6 +72,28 @@ def check_mask(ghot, r, groups=None):
     return mism
 
 
+def check_cold_state(g, r, mism):
+    """Pass 1's cold state in frame-free units (l 2^m, o / l) on the row groups
+    whose verdicts all agree with the oracle's."""
+    B, Hq, Nq = g["l"].shape
+    NG = -(-Nq // 16)
+    gm = np.where(g["m"] == np.iinfo(np.int32).min, np.nan, g["m"].astype(np.float64))
+    ok_rows = np.zeros((B, Hq, Nq), bool)
+    for b in range(B):
+        for h in range(Hq):
+            for gg in range(NG):
+                if not mism[b, h, gg].any():
+                    ok_rows[b, h, 16 * gg:16 * gg + 16] = True
+    both = ok_rows & (g["l"] > 0) & (r["l1"] > 0)
+    if both.any():
+        gl = g["l"] * np.exp2(np.nan_to_num(gm))
+        ol = r["l1"] * np.exp2(np.nan_to_num(r["m1"]))
+        assert np.allclose(gl[both], ol[both], rtol=1e-3)
+        gco = g["o"] / g["l"][..., None]
+        oco = r["o1"] / r["l1"][..., None]
+        assert np.abs(gco[both] - oco[both]).max() <= 1e-3
+
+
 def out_tol(base, O, dtype):
     """The bar on the method's arithmetic, plus, for bf16 outputs, the output
     format's own rounding, since the oracle's O is not rounded: RNE to 8
@@ -105,22 +127,7 @@ def test_apa_matches_oracle(case):
         assert np.all(g["l"] == 0)
     if eps >= 1.0:
         assert not g["hot"].any()
-    # cold state in frame-free units on groups whose verdicts all agree
-    NG = -(-Nq // 16)
-    gm = np.where(g["m"] == np.iinfo(np.int32).min, np.nan, g["m"].astype(np.float64))
-    ok_rows = np.zeros((1, Hq, Nq), bool)
-    for h in range(Hq):
-        for gg in range(NG):
-            if not mism[0, h, gg].any():
-                ok_rows[0, h, 16 * gg:16 * gg + 16] = True
-    both = ok_rows & (g["l"] > 0) & (r["l1"] > 0)
-    if both.any():
-        gl = g["l"] * np.exp2(np.nan_to_num(gm))
-        ol = r["l1"] * np.exp2(np.nan_to_num(r["m1"]))
-        assert np.allclose(gl[both], ol[both], rtol=1e-3)
-        gco = g["o"] / g["l"][..., None]
-        oco = r["o1"] / r["l1"][..., None]
-        assert np.abs(gco[both] - oco[both]).max() <= 1e-3
+    check_cold_state(g, r, mism)
     check_output(g["out"], r["O"])
     fin = np.isfinite(r["lse"])
     assert np.abs(g["lse"][fin] - r["lse"][fin]).max() <= 2e-3
