@@ -143,7 +143,9 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
  * whose 32-row blocks already fill the GPU).  With a workspace, each long
  * visit order is cut in two and run by two wavefronts of one work group at
  * once; the workspace holds the tiles the second one cannot decide until the
- * first is done (at most 1024 per 32-row block, 292 bytes each).  Without
+ * first is done (at most 512 per 32-row block, 292 bytes each) and room to
+ * hand the first one's state to a re-walk of the second half, for blocks
+ * with more undecided tiles than that.  Without
  * one, every block runs as one wavefront (slower when the blocks do not fill
  * the GPU).  The verdicts and the state are those of a single walk up to FP32
  * summation order; the returned frame cold_m is then the larger of the two

@@ -76,7 +76,7 @@ constexpr int kWaves = 4;            // wavefronts per work group
 constexpr float kFrameGuard = 80.0f; // largest lead of m over m_o before re-basing
 constexpr int kMinSplit = 64;        // shortest visit order that runs as two waves
 constexpr int kReplay = 32;          // leading positions the tail wave replays
-constexpr int kCandCap = 1024;       // most undecided tail tiles recorded per unit
+constexpr int kCandCap = 512;        // most undecided tail tiles recorded per unit
 
 enum Role { kWhole = 0, kHead = 1, kTail = 2 };
 
@@ -115,23 +115,38 @@ __device__ __forceinline__ v16f mfma4(v4i a, v4i b, v16f c, int sa, int opa, int
   }
 }
 
+// A unit's tile blobs are read through a buffer resource: the lane's offset
+// inside a blob is a fixed 32-bit VGPR, the tile's offset a scalar, so no
+// per-tile 64-bit address arithmetic and no address registers per load.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+
+__device__ __forceinline__ Rsrc blob_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ v4i bload128(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // The scale bytes of one key (or one V lane) as little-endian words.
 template <int D>
-__device__ __forceinline__ void load_scales(uint32_t (&w)[Tile<D>::NW], const uint8_t* p) {
+__device__ __forceinline__ void load_scales(uint32_t (&w)[Tile<D>::NW], Rsrc r, uint32_t voff,
+                                            uint32_t soff) {
   if constexpr (D == 64) {
-    w[0] = *reinterpret_cast<const uint16_t*>(p);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
   } else if constexpr (D == 128) {
-    w[0] = *reinterpret_cast<const uint32_t*>(p);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
   } else if constexpr (D == 256) {
-    const uint2 x = *reinterpret_cast<const uint2*>(p);
-    w[0] = x.x;
-    w[1] = x.y;
+    const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = x[0];
+    w[1] = x[1];
   } else {
-    const uint4 x = *reinterpret_cast<const uint4*>(p);
-    w[0] = x.x;
-    w[1] = x.y;
-    w[2] = x.z;
-    w[3] = x.w;
+    const auto x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    w[0] = x[0];
+    w[1] = x[1];
+    w[2] = x[2];
+    w[3] = x[3];
   }
 }
 
@@ -142,15 +157,14 @@ struct KOps {
 };
 
 template <int D>
-__device__ __forceinline__ void load_k(KOps<D>& k, const uint8_t* blob, uint32_t koff,
+__device__ __forceinline__ void load_k(KOps<D>& k, Rsrc r, uint32_t soff, uint32_t koff,
                                        uint32_t ksoff, int hh) {
   constexpr int NH = Tile<D>::NH;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
-      k.a[kb][h] = *reinterpret_cast<const v4i*>(blob + koff + kb * 32 * (D / 2) + 32 * h);
-    load_scales<D>(k.s[kb], blob + ksoff + kb * 32 * (D / 32));
+    for (int h = 0; h < NH; ++h) k.a[kb][h] = bload128(r, koff + kb * 32 * (D / 2) + 32 * h, soff);
+    load_scales<D>(k.s[kb], r, ksoff + kb * 32 * (D / 32), soff);
 #pragma unroll
     for (int w = 0; w < Tile<D>::NW; ++w) k.s[kb][w] >>= 8 * hh;
   }
@@ -199,7 +213,7 @@ struct Ctx {
   bool row_ok, has_g1;
   v4i qa[Tile<D>::NH];  // Q^T operand, 16 bytes per 64-channel half
   int qs[Tile<D>::NH];  // its E8M0 bytes (block scale + head exponent)
-  const uint8_t* blobs;
+  Rsrc blobs;  // the unit's kv-head: NT tile blobs
   uint32_t koff, ksoff, voff, vsoff;  // this lane's byte offsets inside a blob
   float g_v;
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
@@ -232,7 +246,8 @@ __device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs
     c.qs[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
   }
   c.g_v = f.kv_head[c.bhk * 8 + 4];
-  c.blobs = f.kv_blob + c.bhk * (size_t)g.NT * Tile<D>::BLOB;
+  c.blobs = blob_rsrc(f.kv_blob + c.bhk * (size_t)g.NT * Tile<D>::BLOB,
+                      (uint32_t)g.NT * Tile<D>::BLOB);
   c.koff = n * (D / 2) + 16 * hh;
   c.ksoff = 32 * D + n * (D / 32);
   c.voff = 34 * D + n * 32 + 16 * hh;
@@ -292,24 +307,33 @@ __device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint
 // (records kept, or -1 when it gave up and walked again from the head's
 // state), then `cap` records of the tile (with a flag per verdict group) and,
 // per row, l_t, the tail's running lambda and the lazy frame as an offset from
-// the state frame (0 .. 80).
+// the state frame (0 .. 80).  Accessed through a buffer resource over the
+// unit's block (scalar base and offsets, so the rarely taken record branch
+// holds no 64-bit address registers).
 struct Cand {
-  int* outcome;
-  uint32_t* tile;  // [cap]: tile | group-0 flag << 30 | group-1 flag << 31
-  float* ell;      // [cap][32]
-  float* lamb;     // [cap][32]
-  uint8_t* dm;     // [cap][32]
+  Rsrc r;
+  uint32_t tile, ell, lamb, dm;  // byte offsets of the arrays in the block
 };
 
-__host__ __device__ inline size_t cand_stride(int cap) {
+__host__ __device__ inline size_t cand_bytes(int cap) {
   return ((size_t)cap * 292 + 16 + 255) & ~(size_t)255;
 }
 
-__device__ __forceinline__ Cand cand_of(uint8_t* ws, int unit, int cap) {
-  uint8_t* b = ws + (size_t)unit * cand_stride(cap);
-  return Cand{reinterpret_cast<int*>(b), reinterpret_cast<uint32_t*>(b + 16),
-              reinterpret_cast<float*>(b + 16 + 4 * (size_t)cap),
-              reinterpret_cast<float*>(b + 16 + 132 * (size_t)cap), b + 16 + 260 * (size_t)cap};
+// After the records: room for the head's final state, which a tail that gave
+// up leaves there for the re-walk kernel (o in lane order, then the per-lane
+// scalars mf, mo, lambda, l, then the head's partial words).
+__host__ __device__ inline size_t handoff_bytes(int D) {
+  return ((size_t)128 * D + 1024 + 16 + 255) & ~(size_t)255;
+}
+
+__host__ __device__ inline size_t cand_stride(int cap, int D) {
+  return cand_bytes(cap) + handoff_bytes(D);
+}
+
+__device__ __forceinline__ Cand cand_of(uint8_t* ws, int unit, int cap, int D) {
+  const size_t stride = cand_stride(cap, D);
+  return Cand{blob_rsrc(ws + (size_t)unit * stride, (uint32_t)stride), 16u, 16u + 4u * cap,
+              16u + 132u * cap, 16u + 260u * cap};
 }
 
 // The head wave's final state, handed to the tail wave in LDS.
@@ -439,12 +463,12 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   // of position i+1 in kn; once this tile's P is formed, QK(i+1) is issued into
   // acc and K of position i+2 is fetched into kn (prefetches past the last
   // position re-read the last tile: in bounds, unused)
-  auto next_blob = [&](int i) { return c.blobs + (size_t)tile_at(min(i, cnt - 1)) * BLOB; };
+  auto next_blob = [&](int i) { return (uint32_t)(tile_at(min(i, cnt - 1)) * BLOB); };
   KOps<D> kn;
   v16f acc[2];
-  load_k<D>(kn, next_blob(0), c.koff, c.ksoff, hh);
+  load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
   qk<D>(acc, kn, c.qa, c.qs);
-  load_k<D>(kn, next_blob(1), c.koff, c.ksoff, hh);
+  load_k<D>(kn, c.blobs, next_blob(1), c.koff, c.ksoff, hh);
 
   for (int i = 0; i < cnt && !gave_up; ++i) {
     const int t = tile_at(i);
@@ -454,14 +478,13 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       st.lam = 0.0f;
     }
     if (i == kReplay) mo_ref = st.mo;
-    const uint8_t* blob = c.blobs + (size_t)t * BLOB;
+    const uint32_t blob = (uint32_t)(t * BLOB);
     // V^T operand and scales of this tile (used at its end)
     v4i va[ND];
     uint32_t vsw[NW];
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-      va[db] = *reinterpret_cast<const v4i*>(blob + c.voff + db * 32 * 32);
-    load_scales<D>(vsw, blob + c.vsoff);
+    for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
+    load_scales<D>(vsw, c.blobs, c.vsoff, blob);
 
     const bool vis0 = t <= c.d0, vis1 = t <= c.d1;
     mask_scores<D>(acc, g, c, t, hh);
@@ -504,7 +527,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     // behind the row sum and run during the vote and the P V product
     __builtin_amdgcn_sched_barrier(0);
     qk<D>(acc, kn, c.qa, c.qs);
-    load_k<D>(kn, next_blob(i + 2), c.koff, c.ksoff, hh);
+    load_k<D>(kn, c.blobs, next_blob(i + 2), c.koff, c.ksoff, hh);
     const float ell = ones_acc[0];
 
     // ---- step 4: the hot test (lambda includes this tile)
@@ -522,11 +545,16 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
         gave_up = true;
       } else {
         if (lane == 0)
-          cr.tile[ncand] = (uint32_t)t | (hot0 ? 1u << 30 : 0u) | (hot1 ? 1u << 31 : 0u);
+          __builtin_amdgcn_raw_buffer_store_b32(
+              (uint32_t)t | (hot0 ? 1u << 30 : 0u) | (hot1 ? 1u << 31 : 0u), cr.r, 0u,
+              cr.tile + 4u * ncand, 0);
         if (hh == 0) {
-          cr.ell[ncand * 32 + n] = ell;
-          cr.lamb[ncand * 32 + n] = st.lam;
-          cr.dm[ncand * 32 + n] = (uint8_t)((int)mcf - st.mo);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ell), cr.r, 4u * n,
+                                                cr.ell + 128u * ncand, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.lam), cr.r, 4u * n,
+                                                cr.lamb + 128u * ncand, 0);
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)((int)mcf - st.mo), cr.r, (uint32_t)n,
+                                               cr.dm + 32u * ncand, 0);
         }
         ++ncand;
       }
@@ -615,16 +643,16 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
   constexpr int BLOB = Tile<D>::BLOB;
   constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
   const int n = lane & 31, hh = lane >> 5;
-  constexpr int kBatch = 8;  // records decided per round of loads
+  constexpr int kBatch = 4;  // records decided per round of loads
   for (int j0 = 0; j0 < ncand; j0 += kBatch) {
     float e[kBatch], lbv[kBatch];
     uint32_t hd[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int j = min(j0 + k, ncand - 1);
-      hd[k] = cr.tile[j];
-      e[k] = cr.ell[j * 32 + n];
-      lbv[k] = cr.lamb[j * 32 + n];
+      const uint32_t j = (uint32_t)min(j0 + k, ncand - 1);
+      hd[k] = __builtin_amdgcn_raw_buffer_load_b32(cr.r, 0u, cr.tile + 4u * j, 0);
+      e[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(cr.r, 4u * n, cr.ell + 128u * j, 0));
+      lbv[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(cr.r, 4u * n, cr.lamb + 128u * j, 0));
     }
     uint32_t found = 0;  // 2 bits per record: groups hot after all
 #pragma unroll
@@ -640,16 +668,19 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       const int kr = __builtin_ctz(found) >> 1;
       const uint32_t gr = (found >> (2 * kr)) & 3u;
       found &= ~(3u << (2 * kr));
-      const int j = j0 + kr;
-      const uint32_t hdr = (uint32_t)__builtin_amdgcn_readfirstlane((int)cr.tile[j]);
+      const uint32_t j = (uint32_t)(j0 + kr);
+      const uint32_t hdr = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)__builtin_amdgcn_raw_buffer_load_b32(cr.r, 0u, cr.tile + 4u * j, 0));
       const int t = (int)(hdr & 0x3FFFFFFFu);
-      const float ell = cr.ell[j * 32 + n];
-      const float mcf = (float)(st.mo + (int)cr.dm[j * 32 + n]);
+      const float ell =
+          __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(cr.r, 4u * n, cr.ell + 128u * j, 0));
+      const float mcf = (float)(st.mo + (int)__builtin_amdgcn_raw_buffer_load_b8(
+                                            cr.r, (uint32_t)n, cr.dm + 32u * j, 0));
       const bool f0 = gr & 1u, f1 = gr & 2u;
       KOps<D> k;
       v16f acc[2];
-      const uint8_t* blob = c.blobs + (size_t)t * BLOB;
-      load_k<D>(k, blob, c.koff, c.ksoff, hh);
+      const uint32_t blob = (uint32_t)(t * BLOB);
+      load_k<D>(k, c.blobs, blob, c.koff, c.ksoff, hh);
       qk<D>(acc, k, c.qa, c.qs);
       mask_scores<D>(acc, g, c, t, hh);
       float gown, goth;
@@ -666,9 +697,8 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       v4i va[ND];
       uint32_t vsw[NW];
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
-        va[db] = *reinterpret_cast<const v4i*>(blob + c.voff + db * 32 * 32);
-      load_scales<D>(vsw, blob + c.vsoff);
+      for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
+      load_scales<D>(vsw, c.blobs, c.vsoff, blob);
 #pragma unroll
       for (int db = 0; db < ND; ++db)
         st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
@@ -747,8 +777,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     p0 = h;
     cnt = kReplay + npos - h;
   }
-  const Cand cr = role == kTail ? cand_of(split, unit_index(g, id), cap)
-                                : Cand{nullptr, nullptr, nullptr, nullptr, nullptr};
+  const Cand cr = cand_of(role == kTail ? split : f.kv_blob, role == kTail ? unit_index(g, id) : 0,
+                         role == kTail ? cap : 0, D);
   volatile lds_float* pin = role == kTail ? (volatile lds_float*)pub[slot] : nullptr;
   volatile lds_float* pout = role == kHead ? (volatile lds_float*)pub[slot] : nullptr;
   const float Hf = (float)hoff;
@@ -756,35 +786,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     while (__hip_atomic_load(&hs[slot].done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(2);
   };
-  int outcome = 0;
-  bool redone = false;
-  // one call site of the walk: a tail that gave up walks again, from the
-  // head's final state, over its own positions
-  for (;;) {
-    outcome = walk<D>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout, lane);
-    if (role != kTail) break;
-    if (!redone && lane == 0) *cr.outcome = outcome;
-    wait_head();
-    if (redone || outcome >= 0) break;
-    redone = true;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const v4f x = hs[slot].o[4 * db + q][lane];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.o[db][4 * q + e] = x[e];
-      }
-    st.mf = hs[slot].sc[0][lane];
-    st.mo = __float_as_int(hs[slot].sc[1][lane]);
-    st.lam = hs[slot].sc[2][lane];
-    st.lsum = hs[slot].sc[3][lane];
-    wd = Words{wb, 0u, 0u, 0u, 0u};
-    nrep = 0;
-    p0 = h;
-    cnt = npos - h;
-    pin = nullptr;
-  }
+  const int outcome =
+      walk<D>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout, lane);
 
   if (role == kHead) {
 #pragma unroll
@@ -807,30 +810,33 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     return;
   }
   if (role == kTail) {
-    // the shared words: the head's part and the tail's (or the re-walk's)
-    const uint32_t hw0 = hs[slot].words[0], hw1 = hs[slot].words[1];
-    const uint32_t hw2 = hs[slot].words[2], hw3 = hs[slot].words[3];
-    float a_mf = 0.0f, a_lam = 0.0f, a_lsum = 0.0f;
-    int a_mo = 0;
-    if (!redone) {
-      a_mf = hs[slot].sc[0][lane];
-      a_mo = __float_as_int(hs[slot].sc[1][lane]);
-      a_lam = hs[slot].sc[2][lane];
-      a_lsum = hs[slot].sc[3][lane];
-      // the head's lambda in the tail's state frame (the tail never re-based)
-      settle<D>(g, c, st, wd, cr, outcome, ldexpf(a_lam, a_mo - st.mo), eps, lane);
-    }
-    if (lane == 0) {
-      c.bits0[0] = hw0 | wd.p00;
-      if (c.has_g1) c.bits1[0] = hw1 | wd.p01;
-      if (wb > 0) {
-        c.bits0[wb] = hw2 | wd.p10;
-        if (c.has_g1) c.bits1[wb] = hw3 | wd.p11;
-      }
-    }
-    if (redone) {
-      store_state<D>(g, c, out, st, lane);
+    wait_head();
+    if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)outcome, cr.r, 0u, 0u, 0);
+    if (outcome < 0) {
+      // gave up: leave the head's state for the re-walk kernel
+      float* dst = reinterpret_cast<float*>(split + (size_t)unit_index(g, id) * cand_stride(cap, D) +
+                                            cand_bytes(cap));
+#pragma unroll 2
+      for (int k = 0; k < ND * 4; ++k) reinterpret_cast<v4f*>(dst)[k * 64 + lane] = hs[slot].o[k][lane];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[32 * D + 64 * k + lane] = hs[slot].sc[k][lane];
+      if (lane < 4) reinterpret_cast<uint32_t*>(dst)[32 * D + 256 + lane] = hs[slot].words[lane];
       return;
+    }
+    const float a_mf = hs[slot].sc[0][lane];
+    const int a_mo = __float_as_int(hs[slot].sc[1][lane]);
+    const float a_lam = hs[slot].sc[2][lane];
+    const float a_lsum = hs[slot].sc[3][lane];
+    // the head's lambda in the tail's state frame (the tail never re-based)
+    settle<D>(g, c, st, wd, cr, outcome, ldexpf(a_lam, a_mo - st.mo), eps, lane);
+    // the shared words: the head's part and the tail's
+    if (lane == 0) {
+      c.bits0[0] = hs[slot].words[0] | wd.p00;
+      if (c.has_g1) c.bits1[0] = hs[slot].words[1] | wd.p01;
+      if (wb > 0) {
+        c.bits0[wb] = hs[slot].words[2] | wd.p10;
+        if (c.has_g1) c.bits1[wb] = hs[slot].words[3] | wd.p11;
+      }
     }
     // merge: the larger frame, each state scaled into it by an exact power of two
     if (!c.row_ok) return;
@@ -864,6 +870,53 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   store_state<D>(g, c, out, st, lane);
 }
 
+// The re-walk of units whose tail gave up (record full, or a re-base of its
+// frame): the head's state, left in the workspace, walks the tail positions.
+// One wave per unit; the others return at once.
+template <int D>
+__global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float eps, float tau,
+                                                     int hoff, Pass1Out out, uint8_t* split,
+                                                     int cap) {
+  constexpr int ND = Tile<D>::ND;
+  const int lane = threadIdx.x;
+  const UnitId id = unit_id(g, blockIdx.x);
+  const uint8_t* base = split + (size_t)blockIdx.x * cand_stride(cap, D);
+  Ctx<D> c;
+  make_ctx<D>(c, g, f, out, id, lane);
+  const int npos = c.dW + 1;
+  if (npos < kMinSplit) return;
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
+  const int h = (npos + kReplay) / 2;
+  const int wb = shared_word(c.dW - h + 1);
+  const float* src = reinterpret_cast<const float*>(base + cand_bytes(cap));
+  St<D> st;
+#pragma unroll
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f x = reinterpret_cast<const v4f*>(src)[(4 * db + q) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.o[db][4 * q + e] = x[e];
+    }
+  st.mf = src[32 * D + lane];
+  st.mo = __float_as_int(src[32 * D + 64 + lane]);
+  st.lam = src[32 * D + 128 + lane];
+  st.lsum = src[32 * D + 192 + lane];
+  const uint32_t* hw = reinterpret_cast<const uint32_t*>(src + 32 * D + 256);
+  Words wd = {wb, 0u, 0u, 0u, 0u};
+  const Cand none = cand_of(f.kv_blob, 0, 0, D);
+  walk<D>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr, nullptr, lane);
+  if (lane == 0) {
+    c.bits0[0] = hw[0] | wd.p00;
+    if (c.has_g1) c.bits1[0] = hw[1] | wd.p01;
+    if (wb > 0) {
+      c.bits0[wb] = hw[2] | wd.p10;
+      if (c.has_g1) c.bits1[wb] = hw[3] | wd.p11;
+    }
+  }
+  store_state<D>(g, c, out, st, lane);
+}
+
 // Two waves per unit pay off while there are at most about three quarters as
 // many units as wave slots, and only for visit orders long enough to cut.
 bool split_pays(const Geom& g) {
@@ -880,7 +933,7 @@ int cand_cap(const Geom& g) { return min(kCandCap, g.NT - (g.NT + kReplay) / 2);
 
 size_t pass1_ws_bytes(const Geom& g) {
   if (!split_pays(g)) return 0;
-  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g));
+  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g), g.D);
 }
 
 namespace {
@@ -893,8 +946,15 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   uint8_t* split = (ws && split_pays(g)) ? static_cast<uint8_t*>(ws) : nullptr;
   const int nwaves = split ? 2 * nunits : nunits;
   const int nblocks = (nwaves + kWaves - 1) / kWaves;
+  const int cap = split ? cand_cap(g) : 0;
   hipLaunchKernelGGL(k_pass1<D>, dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau, hoff, o,
-                     split, split ? cand_cap(g) : 0, nwaves);
+                     split, cap, nwaves);
+  if (split) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_pass1_rewalk<D>, dim3(nunits), dim3(64), 0, s, g, f, eps, tau, hoff, o,
+                       split, cap);
+  }
   return hipGetLastError();
 }
 

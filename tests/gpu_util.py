@@ -91,15 +91,17 @@ def unpack_bits(p, words: np.ndarray) -> np.ndarray:
 
 
 # Pass-1 workspace of a split problem (the layout of pass1.hip's Cand): per
-# 32-row block the tail's outcome (records kept, or -1: it gave up and walked
-# again from the head's state) in the first 4 bytes, then `cap` records of 292
-# bytes, cap = min(1024, the longest tail), the block's stride rounded to 256.
+# 32-row block the tail's outcome (records kept, or -1: it gave up and the
+# head's state walks the tail again) in the first 4 bytes, then `cap` records
+# of 292 bytes, cap = min(512, the longest tail), rounded up to 256 bytes,
+# then the head's hand-off state (128 D + 1040 bytes, rounded up to 256).
 def tail_outcomes(p, ws) -> np.ndarray:
     """Outcome of every block whose visit order was cut: number of undecided
-    tail tiles decided at the end, or -1 where the tail walked again."""
+    tail tiles decided at the end, or -1 where the tail positions were walked
+    again from the head's state."""
     G, NT, nq32 = p.Hq // p.Hkv, -(-p.Nkv // 64), -(-p.Nq // 32)
-    cap = min(1024, NT - (NT + 32) // 2)
-    stride = (cap * 292 + 16 + 255) // 256 * 256
+    cap = min(512, NT - (NT + 32) // 2)
+    stride = (cap * 292 + 16 + 255) // 256 * 256 + (128 * p.D + 1040 + 255) // 256 * 256
     raw = ws.cpu().numpy()
     out = []
     for b in range(p.B):
