@@ -42,7 +42,9 @@
 // equal those of the method's own frame bookkeeping (up to FP32 underflow of
 // values 2^-100 below the row maximum).
 // Hot bits are written as whole 32-tile words, so every word of the mask is
-// defined without a clearing pass.
+// defined without a clearing pass.  Up to 4096 key tiles the loop only logs
+// each tile's two verdicts as an LDS byte, and the words are built after the
+// walk (lane j builds one word); beyond that they are kept in the loop.
 //
 // Balance.  With fewer units than about three quarters of the chip's wave
 // slots, a wave per unit leaves SIMDs idle while others run two waves, so each
@@ -83,6 +85,12 @@ enum Role { kWhole = 0, kHead = 1, kTail = 2 };
 // a float in LDS (an address-space-3 pointer keeps the accesses DS
 // instructions, which wait on their own counter, not on vector memory)
 typedef __attribute__((address_space(3))) float lds_float;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Problems with at most this many key tiles log each visited tile's verdict
+// as one LDS byte per wave and build the hot words after the walk (no word
+// bookkeeping in the tile loop); longer ones keep the words in the loop.
+constexpr int kLogTiles = 4096;
 
 // Two waves per SIMD up to D = 128; one above, where the output accumulators
 // (D/2 per lane) need the accumulation registers.
@@ -424,6 +432,48 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float xof, float 
   return v4i{a0, a1, b0, b1};
 }
 
+// The hot words of a walk's positions [P0, P0 + np) from its verdict log
+// (tile t at vlog[t]): the tiles dW - P0 - np + 2 .. dW - max(P0, 1) + 1 and,
+// when P0 = 0, tile 0.  Lane j builds word w_lo + j; words 0 and wb go to the
+// partial words, the others are stored.
+template <int D>
+__device__ __forceinline__ void assemble_words(const Ctx<D>& c, Words& wd, const lds_u8* vlog,
+                                               int P0, int np, int lane) {
+  const int t_hi = c.dW - (P0 > 0 ? P0 : 1) + 1;
+  const int t_lo = c.dW - P0 - np + 2;
+  if (P0 == 0 && np > 0) {
+    const uint32_t v = vlog[0];
+    wd.p00 |= v & 1u;
+    wd.p01 |= v >> 1;
+  }
+  if (t_lo > t_hi) return;
+  for (int w0 = t_lo >> 5; w0 <= (t_hi >> 5); w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t b0 = 0u, b1 = 0u;
+    if (w <= (t_hi >> 5)) {
+      const int a = max(32 * w, t_lo), e = min(32 * w + 31, t_hi);
+      for (int tt = a; tt <= e; ++tt) {
+        const uint32_t v = vlog[tt];
+        b0 |= (v & 1u) << (tt & 31);
+        b1 |= (v >> 1) << (tt & 31);
+      }
+      if (w != 0 && w != wd.wb) {
+        c.bits0[w] = b0;
+        if (c.has_g1) c.bits1[w] = b1;
+      }
+    }
+    // the partial words, from the lane that built them
+    if (w0 == 0) {
+      wd.p00 |= (uint32_t)__builtin_amdgcn_readlane((int)b0, 0);
+      wd.p01 |= (uint32_t)__builtin_amdgcn_readlane((int)b1, 0);
+    }
+    if (wd.wb > 0 && wd.wb >= w0 && wd.wb < w0 + 64) {
+      wd.p10 |= (uint32_t)__builtin_amdgcn_readlane((int)b0, wd.wb - w0);
+      wd.p11 |= (uint32_t)__builtin_amdgcn_readlane((int)b1, wd.wb - w0);
+    }
+  }
+}
+
 // Walks cnt positions of a unit's visit order 0, d, d-1, ..., 1: first the
 // positions 0 .. nrep-1 as a replay (state and vote only: no P V, no hot
 // bits), then positions p0, p0+1, ...  A walk with a replay is a tail walk:
@@ -435,11 +485,11 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float xof, float 
 // return 0.  A head walk publishes its lambda from position nrep_tail on in
 // `pub_out`, in the state frame it had there (the frame the tail's replay ends
 // in).
-template <int D>
+template <int D, bool LOG>
 __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
-                                    volatile lds_float* pub_out, int lane) {
+                                    volatile lds_float* pub_out, lds_u8* vlog, int lane) {
   constexpr int ND = Tile<D>::ND;
   constexpr int NW = Tile<D>::NW;
   constexpr int BLOB = Tile<D>::BLOB;
@@ -579,8 +629,11 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       st.lsum = keep ? st.lsum + ell : st.lsum;
     }
 
-    // ---- hot bits, whole words (visited in descending order after tile 0)
-    if (!replay) {
+    // ---- hot bits: one log byte per tile, or whole words (visited in
+    // descending order after tile 0)
+    if (LOG) {
+      if (!replay && lane == 0) vlog[t] = (uint8_t)((hot0 ? 1 : 0) | (hot1 ? 2 : 0));
+    } else if (!replay) {
       const int w = t >> 5;
       if (w != cur_w) {
         if (cur_w >= 0) put_word(c, wd, cur_w, cur_b0, cur_b1, lane);
@@ -591,7 +644,11 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       if (hot1) cur_b1 |= 1u << (t & 31);
     }
   }
-  if (cur_w >= 0) put_word(c, wd, cur_w, cur_b0, cur_b1, lane);
+  if (LOG) {
+    assemble_words<D>(c, wd, vlog, p0, cnt - nrep, lane);
+  } else if (cur_w >= 0) {
+    put_word(c, wd, cur_w, cur_b0, cur_b1, lane);
+  }
   return gave_up ? -1 : ncand;
 }
 
@@ -725,7 +782,7 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
 // state at its end; the tail finishes the unit.  Units are numbered (batch,
 // kv-head, 32-row block, head), so the waves of a work group, and the groups
 // of an XCD, stream the same tiles.
-template <int D>
+template <int D, bool LOG>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
     int nwaves) {
@@ -733,6 +790,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // per head/tail pair of the group: the head's running lambda and final state
   __shared__ float pub[kWaves / 2][32];
   __shared__ HeadState<D> hs[kWaves / 2];
+  __shared__ uint8_t vlog_sh[LOG ? kWaves : 1][LOG ? kLogTiles : 1];  // verdict logs
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   // the wave index is wave-uniform: keep everything derived from it in SGPRs
@@ -787,7 +845,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       __builtin_amdgcn_s_sleep(2);
   };
   const int outcome =
-      walk<D>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout, lane);
+      walk<D, LOG>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout,
+                   (lds_u8*)vlog_sh[LOG ? wave : 0], lane);
 
   if (role == kHead) {
 #pragma unroll
@@ -873,7 +932,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 // The re-walk of units whose tail gave up (record full, or a re-base of its
 // frame): the head's state, left in the workspace, walks the tail positions.
 // One wave per unit; the others return at once.
-template <int D>
+template <int D, bool LOG>
 __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float eps, float tau,
                                                      int hoff, Pass1Out out, uint8_t* split,
                                                      int cap) {
@@ -905,7 +964,9 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   const uint32_t* hw = reinterpret_cast<const uint32_t*>(src + 32 * D + 256);
   Words wd = {wb, 0u, 0u, 0u, 0u};
   const Cand none = cand_of(f.kv_blob, 0, 0, D);
-  walk<D>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr, nullptr, lane);
+  __shared__ uint8_t vlog_sh[LOG ? kLogTiles : 1];
+  walk<D, LOG>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr, nullptr,
+               (lds_u8*)vlog_sh, lane);
   if (lane == 0) {
     c.bits0[0] = hw[0] | wd.p00;
     if (c.has_g1) c.bits1[0] = hw[1] | wd.p01;
@@ -947,13 +1008,22 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   const int nwaves = split ? 2 * nunits : nunits;
   const int nblocks = (nwaves + kWaves - 1) / kWaves;
   const int cap = split ? cand_cap(g) : 0;
-  hipLaunchKernelGGL(k_pass1<D>, dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau, hoff, o,
-                     split, cap, nwaves);
+  const bool log = g.NT <= kLogTiles;
+  if (log)
+    hipLaunchKernelGGL((k_pass1<D, true>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
+                       hoff, o, split, cap, nwaves);
+  else
+    hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
+                       hoff, o, split, cap, nwaves);
   if (split) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_pass1_rewalk<D>, dim3(nunits), dim3(64), 0, s, g, f, eps, tau, hoff, o,
-                       split, cap);
+    if (log)
+      hipLaunchKernelGGL((k_pass1_rewalk<D, true>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+                         hoff, o, split, cap);
+    else
+      hipLaunchKernelGGL((k_pass1_rewalk<D, false>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+                         hoff, o, split, cap);
   }
   return hipGetLastError();
 }
