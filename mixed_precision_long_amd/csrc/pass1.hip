@@ -296,6 +296,11 @@ struct Words {
 
 __device__ __forceinline__ int shared_word(int tb) { return ((tb + 1) & 31) ? (tb >> 5) : -1; }
 
+// Where a visit order of npos >= kMinSplit positions is cut: the tail also
+// replays kReplay positions and its tiles cost a little more (the record
+// keeping), so the head takes half of npos + kReplay plus about 1.5 %.
+__host__ __device__ inline int split_point(int npos) { return (npos + kReplay) / 2 + npos / 64; }
+
 template <int D>
 __device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint32_t b0,
                                          uint32_t b1, int lane) {
@@ -485,7 +490,7 @@ __device__ __forceinline__ void assemble_words(const Ctx<D>& c, Words& wd, const
 // return 0.  A head walk publishes its lambda from position nrep_tail on in
 // `pub_out`, in the state frame it had there (the frame the tail's replay ends
 // in).
-template <int D, bool LOG>
+template <int D, bool LOG, bool TAIL>
 __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
@@ -497,7 +502,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   const int hh = lane >> 5; // which half of the K dimension this lane feeds
   // lanes of verdict group 0 (rows r0 .. r0+15) in both lane halves
   constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
-  const bool tail = nrep > 0;
+  const bool tail = TAIL;  // a tail walk (nrep > 0); its own copy of the loop
   auto tile_at = [&](int i) {
     const int p = i < nrep ? i : p0 + (i - nrep);
     return p == 0 ? 0 : c.dW - p + 1;
@@ -527,7 +532,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       lam_lo = st.lam;
       st.lam = 0.0f;
     }
-    if (i == kReplay) mo_ref = st.mo;
+    if (!TAIL && i == kReplay) mo_ref = st.mo;
     const uint32_t blob = (uint32_t)(t * BLOB);
     // V^T operand and scales of this tile (used at its end)
     v4i va[ND];
@@ -582,9 +587,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
 
     // ---- step 4: the hot test (lambda includes this tile)
     st.lam += ell;
-    if (pub_out && i >= kReplay && hh == 0) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
+    if (!TAIL && pub_out && i >= kReplay && hh == 0) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
     float lam_b = lam_lo;
-    if (pub_in && !replay) lam_b = vmax(lam_b, pub_in[n]);
+    if (TAIL && pub_in && !replay) lam_b = vmax(lam_b, pub_in[n]);
     const unsigned long long hb = __ballot(ell > eps * (lam_b + st.lam) && hh == 0);
     bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
     bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
@@ -821,7 +826,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     if (role == kTail) return;
     role = kWhole;
   }
-  const int h = (npos + kReplay) / 2;  // head positions [0, h), tail [h, npos)
+  const int h = split_point(npos);  // head positions [0, h), tail [h, npos)
   const int wb = role == kWhole ? -1 : shared_word(c.dW - h + 1);
 
   St<D> st;
@@ -844,9 +849,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     while (__hip_atomic_load(&hs[slot].done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
       __builtin_amdgcn_s_sleep(2);
   };
+  // the tail's walk is a copy of its own: the record keeping stays out of the
+  // loop the head and whole units run
   const int outcome =
-      walk<D, LOG>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin, pout,
-                   (lds_u8*)vlog_sh[LOG ? wave : 0], lane);
+      role == kTail ? walk<D, LOG, true>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin,
+                                         pout, (lds_u8*)vlog_sh[LOG ? wave : 0], lane)
+                    : walk<D, LOG, false>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin,
+                                          pout, (lds_u8*)vlog_sh[LOG ? wave : 0], lane);
 
   if (role == kHead) {
 #pragma unroll
@@ -945,7 +954,7 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   const int npos = c.dW + 1;
   if (npos < kMinSplit) return;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
-  const int h = (npos + kReplay) / 2;
+  const int h = split_point(npos);
   const int wb = shared_word(c.dW - h + 1);
   const float* src = reinterpret_cast<const float*>(base + cand_bytes(cap));
   St<D> st;
@@ -965,8 +974,8 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   Words wd = {wb, 0u, 0u, 0u, 0u};
   const Cand none = cand_of(f.kv_blob, 0, 0, D);
   __shared__ uint8_t vlog_sh[LOG ? kLogTiles : 1];
-  walk<D, LOG>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr, nullptr,
-               (lds_u8*)vlog_sh, lane);
+  walk<D, LOG, false>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr,
+                      nullptr, (lds_u8*)vlog_sh, lane);
   if (lane == 0) {
     c.bits0[0] = hw[0] | wd.p00;
     if (c.has_g1) c.bits1[0] = hw[1] | wd.p01;
@@ -988,7 +997,7 @@ bool split_pays(const Geom& g) {
 
 // Records per unit: every tail position of the longest visit order, at most
 // kCandCap.
-int cand_cap(const Geom& g) { return min(kCandCap, g.NT - (g.NT + kReplay) / 2); }
+int cand_cap(const Geom& g) { return min(kCandCap, g.NT - split_point(g.NT)); }
 
 }  // namespace
 

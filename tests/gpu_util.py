@@ -100,7 +100,7 @@ def tail_outcomes(p, ws) -> np.ndarray:
     tail tiles decided at the end, or -1 where the tail positions were walked
     again from the head's state."""
     G, NT, nq32 = p.Hq // p.Hkv, -(-p.Nkv // 64), -(-p.Nq // 32)
-    cap = min(512, NT - (NT + 32) // 2)
+    cap = min(512, NT - ((NT + 32) // 2 + NT // 64))
     stride = (cap * 292 + 16 + 255) // 256 * 256 + (128 * p.D + 1040 + 255) // 256 * 256
     raw = ws.cpu().numpy()
     out = []
