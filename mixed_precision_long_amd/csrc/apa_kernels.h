@@ -62,16 +62,17 @@ struct Pass2Args {
   void* out;
   float* lse;
   float *hot_m, *hot_l, *hot_o;
-  int32_t* list_tiles;   // [units][NT]
+  int32_t* list_tiles;   // [units][NT]  (units: see attn_units)
   uint32_t* list_masks;  // [units][NT]
   int32_t* list_count;   // [units]
   // split states when a unit's keys run as S work groups: [S][rows] and
   // [S][rows][D] (rows = B*Hq*Nq)
   float *part_m, *part_l, *part_o;
 };
-// Query positions per work group of the 16-bit attention kernels, and the
-// number of key splits they use for a problem.
-int attn_positions(int D);
+// Work groups of the 16-bit attention kernels (per batch and kv-head, one per
+// four 32-row blocks of its query heads), and the number of key splits each
+// runs as for a problem.
+int attn_units(const Geom& g);
 int attn_splits(const Geom& g);
 hipError_t launch_pass2(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a, hipStream_t s);
 hipError_t launch_merge(const Geom& g, const Fp4Ptrs& f, const int32_t* cold_m,

@@ -118,8 +118,7 @@ size_t split_ws(const apa_problem* p, size_t o, Pass2Args* a, void* base) {
 
 size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
   const Geom g = geom(p);
-  const int pos = attn_positions(p->D);
-  const size_t units = (size_t)p->B * p->Hkv * ((p->Nq + pos - 1) / pos);
+  const size_t units = (size_t)attn_units(g);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
   const size_t t = take(units * g.NT * 4), m = take(units * g.NT * 4), c = take(units * 4);

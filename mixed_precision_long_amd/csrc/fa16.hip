@@ -3,31 +3,44 @@
 // all-exact baseline; fp16 or bf16 inputs.
 //
 // "APA: sloppy attention, exact where it counts" (rfriedmann.de): section
-// "Pass 2: exact FP16 on the hot tiles" (a work group takes the rows of one
-// pass-1 block, gathers the tiles hot for any of them, streams those from the
+// "Pass 2: exact FP16 on the hot tiles" (a work group takes the rows of a few
+// pass-1 blocks, gathers the tiles hot for any of them, streams those from the
 // original 16-bit K and V; a wavefront works only on tiles hot for its rows,
 // with an FP32 online softmax, and combines the result with the cold state of
-// pass 1) and "The merge that
-// makes it exact".  The introduction's all-exact baseline is the same core over
-// every visible tile.  Large head dimensions follow the FFPA documentation's
-// interface (same layout and semantics at D = 512).
+// pass 1) and "The merge that makes it exact".  The introduction's all-exact
+// baseline is the same core over every visible tile.  Large head dimensions
+// follow the FFPA documentation's interface (same layout and semantics at
+// D = 512).
 //
-// Work group = (batch, kv-head, POS query positions) x all G query heads of the
-// group: G*POS/32 wavefronts of 32 rows each, so every K/V tile staged in LDS
-// feeds all heads that share it.  POS is 64 for D <= 256 (LDS double
-// buffered, the next tile prefetched into registers) and 32 for D = 512 (one
-// LDS stage; the output accumulators live in the accumulation registers).
-// A unit's key range is cut into S splits that run as separate work groups
-// when there are too few units to fill the chip; each split writes a partial
-// online-softmax state and a combine kernel merges them in split order
-// (deterministic).  Per wave and tile (D = 128):
-//   S^T = K Q^T   16 MFMA 32x32x16, K from LDS (row pad 16 B), Q resident;
-//   softmax       scores sl*q.k - c_r in log2 units, FP32 running max/sum;
+// Row blocks.  A row block is 32 consecutive query positions of one query
+// head; the row blocks of one (batch, kv-head) are numbered position-major,
+// head-minor, and a work group takes four consecutive ones, one wavefront
+// each, so the K/V tiles it stages feed every head of the KV group that shares
+// them.  A work group's key range can be cut into S splits that run as
+// separate work groups; each split writes a partial online-softmax state and a
+// combine kernel merges them in split order (deterministic).
+//
+// D <= 256 (k_fa): four wavefronts, one per SIMD, and two work groups per
+// compute unit up to D = 128, so every SIMD runs two independent waves (their
+// matrix and vector phases interleave; the waves of one group meet at one
+// barrier per tile).  K/V tiles go from HBM straight into LDS with buffer
+// loads that write LDS (no staging registers), double buffered.  LDS holds a
+// tile as [D/32][64 keys][32 channels] (64-byte rows): the transposing V reads
+// are conflict-free as laid out, and the K rows have their four 16-byte slots
+// XOR-swizzled by (key / 4) % 4 so that sixteen consecutive keys of one slot
+// hit distinct banks.  Per wave and tile (D = 128):
+//   S^T = K Q^T   16 MFMA 32x32x16, K from LDS, Q^T resident in registers;
+//   softmax       raw maxima, then p = exp2(sl*q.k - (c_r + m)) in one FMA and
+//                 one exp2 per score; the running maximum m moves only when a
+//                 row's maximum exceeds it by more than 8 (log2 units), so the
+//                 rescale of o is rare; row sums by V_DOT2 of the fp16 P;
 //   O^T += V^T P^T 16 MFMA 32x32x16 f16; P stays in the accumulator's lanes
 //                 (its key order is matched by the V^T operand), V^T comes
-//                 from LDS by DS_READ_B64_TR_B16 (row pad 64 B).  With bf16
-//                 inputs the scores use the bf16 MFMA and V is staged as fp16,
-//                 so P keeps 11 significant bits.
+//                 from LDS by DS_READ_B64_TR_B16.  With bf16 inputs the scores
+//                 use the bf16 MFMA and each wave converts the V rows it loaded
+//                 to fp16 in LDS, so P keeps 11 significant bits.
+// D = 512 (k_attn_big): one wave per SIMD, registers staging into a single
+// padded LDS stage, the output accumulators in the accumulation registers.
 #include <type_traits>
 
 #include "apa_device.h"
@@ -41,6 +54,9 @@ enum Mode { kExact = 0, kPass2 = 1 };
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 // 16-bit element types: the MFMA and the conversions.
 template <typename T>
@@ -64,18 +80,23 @@ struct E16<__bf16> {
   static __device__ __forceinline__ __bf16 from(float x) { return (__bf16)x; }
 };
 
-template <int D>
-struct Cfg {
-  static constexpr int POS = D >= 512 ? 32 : 64;  // query positions per work group
-  static constexpr int STAGES = D >= 512 ? 1 : 2;
-  static constexpr int KS = D + 8;    // halves per K row (16-byte pad)
-  static constexpr int VS = D + 32;   // halves per V row (64-byte pad)
-  static constexpr int K_HALVES = kTile * KS;
-  static constexpr int V_HALVES = kTile * VS;
-  static constexpr int STAGE = K_HALVES + V_HALVES;
-  static constexpr size_t BYTES = (size_t)STAGES * STAGE * 2;
-  static constexpr int CHUNKS = 2 * kTile * D / 8;  // 16-byte chunks per K+V tile
+// Row blocks of one (batch, kv-head) and the work groups over them.
+struct RowBlocks {
+  int nqb;  // 32-position blocks
+  int nrb;  // row blocks (G per position block)
+  int nwg;  // work groups of four row blocks
 };
+
+__host__ __device__ inline RowBlocks row_blocks(const Geom& g) {
+  RowBlocks r;
+  r.nqb = (g.Nq + 31) / 32;
+  r.nrb = g.G * r.nqb;
+  r.nwg = (r.nrb + 3) / 4;
+  return r;
+}
+
+constexpr int kWgWaves = 4;      // wavefronts per work group (one row block each)
+constexpr float kLazy = 8.0f;    // lead (log2 units) a row maximum needs to move m
 
 __device__ __forceinline__ float merge_weight(bool live, float m, float M) {
   return live ? fast_exp2(m - M) : 0.0f;
@@ -101,249 +122,43 @@ __device__ __forceinline__ int split_lo(int total, int s, int S) {
   return (int)(((long long)total * s) / S);
 }
 
-template <int D, typename T, int MODE, int NW>
-__device__ __forceinline__ void attn_body(const Geom& g, const T* __restrict__ Q,
-                                          const T* __restrict__ K, const T* __restrict__ V,
-                                          const Fp4Ptrs& f, const Pass2Args& a, int nunits,
-                                          int S) {
-  using C = Cfg<D>;
+// The row block of wave `wave` in work group `wg`: its head in the group and
+// its first query position; live = false past the last row block.
+struct WaveRows {
+  bool live;
+  int gi, r0;
+};
+
+__device__ __forceinline__ WaveRows wave_rows(const Geom& g, const RowBlocks& rb, int wg, int wave) {
+  const int j = wg * kWgWaves + wave;
+  WaveRows w;
+  w.live = j < rb.nrb;
+  w.gi = w.live ? j % g.G : 0;
+  w.r0 = w.live ? (j / g.G) * 32 : 0;
+  return w;
+}
+
+// The key tiles a work group visits in exact mode: up to the diagonal of its
+// last live row.
+__device__ __forceinline__ int exact_tiles(const Geom& g, const RowBlocks& rb, int wg) {
+  const int jl = min(wg * kWgWaves + kWgWaves - 1, rb.nrb - 1);
+  const int lr = min((jl / g.G) * 32 + 31, g.Nq - 1);
+  return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile + 1 : g.NT;
+}
+
+// The epilogue shared by both kernels: a split's partial state (S > 1 or an
+// unfused pass 2), else the output -- merged with the cold state in pass 2.
+// Lane (n, hh) holds row n's output channels 32*db + 8*q + 4*hh + 0..3 in
+// o[db][4q .. 4q+3]; l is already summed over both lane halves.
+template <int D, typename T, int MODE>
+__device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
+                                           int S, int sp, size_t bhq, int row, int hh, float m,
+                                           float l, float c_r, const v16f* o) {
   using E = E16<T>;
-  typedef typename E::V8 V8;
   typedef typename E::V4 V4;
-  extern __shared__ uint16_t smem[];
-  constexpr int POS = C::POS;
-  constexpr int WPH = POS / 32;       // waves per head
-  constexpr int GPU = POS / 16;       // 16-row groups per head and work group
-  constexpr int NC = D / 16;          // 16-channel chunks of the QK contraction
-  constexpr int ND = D / 32;          // 32-channel blocks of the output
-  constexpr int PER = (C::CHUNKS + NW * 64 - 1) / (NW * 64);
-  constexpr int RND = C::STAGES == 2 ? PER : (PER < 8 ? PER : 8);  // chunks per staging round
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, hh = lane >> 5;
-  const int unit = xcd_remap(blockIdx.x, gridDim.x);
-  if (unit >= nunits) return;  // uniform over the block
-  const int nqb = (g.Nq + POS - 1) / POS;
-  const int qblk = unit % nqb;
-  int u = unit / nqb;
-  const int sp = u % S; u /= S;
-  const int hk = u % g.Hkv;
-  const int b = u / g.Hkv;
-  const int base_unit = (b * g.Hkv + hk) * nqb + qblk;
-  const int gi = wave / WPH, half = wave % WPH;
-  const int hq = hk * g.G + gi;
-  const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
-  const int r0 = qblk * POS + half * 32;
-  const int row = r0 + n;
-  const bool row_ok = row < g.Nq;
-  const bool wave_live = r0 < g.Nq;
-  auto diag = [&](int lr) { return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile : g.NT - 1; };
-  const int d_wave = wave_live ? diag(min(r0 + 31, g.Nq - 1)) : -1;
-
-  // this split's part of the unit's tile list
-  int lo, hi;
-  const int32_t* tiles = nullptr;
-  const uint32_t* masks = nullptr;
-  if (MODE == kExact) {
-    const int ntot = diag(min(qblk * POS + POS - 1, g.Nq - 1)) + 1;
-    lo = split_lo(ntot, sp, S);
-    hi = split_lo(ntot, sp + 1, S);
-  } else {
-    const int ntot = a.list_count[base_unit];
-    lo = split_lo(ntot, sp, S);
-    hi = split_lo(ntot, sp + 1, S);
-    tiles = a.list_tiles + (size_t)base_unit * g.NT;
-    masks = a.list_masks + (size_t)base_unit * g.NT;
-  }
-  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
-
-  // resident Q^T operand: 8 elements per 16-channel chunk
-  V8 qf[NC];
-  {
-    const int rl = row_ok ? row : (g.Nq > 0 ? g.Nq - 1 : 0);
-    const T* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const V8*>(qp + 16 * c);
-  }
-  const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
-  const float sl = g.sl;
-
-  float m = -__builtin_inff(), l = 0.0f;
-  v16f o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) o[i] = v16f{};
-
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(K) + bhk * (size_t)g.Nkv * D;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(V) + bhk * (size_t)g.Nkv * D;
-
-  // cooperative staging: chunk c < CHUNKS/2 is K (row c / (D/8)), else V
-  auto fetch1 = [&](int t, int c) {
-    uint4 z = {0u, 0u, 0u, 0u};
-    if (c < C::CHUNKS) {
-      const int isv = c >= C::CHUNKS / 2;
-      const int cc = isv ? c - C::CHUNKS / 2 : c;
-      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-      const int key = t * kTile + r;
-      if (key < g.Nkv) z = *reinterpret_cast<const uint4*>((isv ? Vh : Kh) + (size_t)key * D + col);
-    }
-    return z;
-  };
-  auto stash1 = [&](int buf, int c, uint4 z) {
-    if (c < C::CHUNKS) {
-      uint16_t* st = smem + buf * C::STAGE;
-      const int isv = c >= C::CHUNKS / 2;
-      if (std::is_same<T, __bf16>::value && isv) z = bf16x8_to_f16x8(z);
-      const int cc = isv ? c - C::CHUNKS / 2 : c;
-      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-      uint16_t* dst = isv ? st + C::K_HALVES + r * C::VS + col : st + r * C::KS + col;
-      *reinterpret_cast<uint4*>(dst) = z;
-    }
-  };
-  uint4 pre[RND];
-  auto fetch = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + i * NW * 64);
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < RND; ++i) stash1(buf, tid + i * NW * 64, pre[i]);
-  };
-  // single-stage staging of a whole tile in rounds (large D)
-  auto stage_all = [&](int t) {
-    for (int r0c = 0; r0c < PER; r0c += RND) {
-#pragma unroll
-      for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + (r0c + i) * NW * 64);
-#pragma unroll
-      for (int i = 0; i < RND; ++i) stash1(0, tid + (r0c + i) * NW * 64, pre[i]);
-    }
-  };
-
-  if (C::STAGES == 2 && lo < hi) {
-    fetch(tile_at(lo));
-    stash(0);
-  }
-  if (C::STAGES == 2) __syncthreads();
-
-  for (int it = lo; it < hi; ++it) {
-    const int t = tile_at(it);
-    const int buf = C::STAGES == 2 ? ((it - lo) & 1) : 0;
-    if (C::STAGES == 2) {
-      if (it + 1 < hi) fetch(tile_at(it + 1));
-    } else {
-      __syncthreads();
-      stage_all(t);
-      __syncthreads();
-    }
-
-    // does this wave compute tile t, and for which of its two groups?
-    bool on0, on1;
-    if (MODE == kExact) {
-      on0 = on1 = t <= d_wave;
-    } else {
-      const uint32_t mk = masks[it];
-      const int bit = gi * GPU + half * 2;
-      on0 = (mk >> bit) & 1u;
-      on1 = (mk >> (bit + 1)) & 1u;
-    }
-    if (wave_live && (on0 || on1)) {
-      const uint16_t* Ks = smem + buf * C::STAGE;
-      const uint16_t* Vs = Ks + C::K_HALVES;
-      const int k0 = t * kTile;
-      // ---- S^T = K Q^T
-      v16f acc[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        acc[kb] = v16f{};
-        const uint16_t* kr = Ks + (kb * 32 + n) * C::KS + 8 * hh;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const V8 kf = *reinterpret_cast<const V8*>(kr + 16 * c);
-          acc[kb] = E::mma(kf, qf[c], acc[kb]);
-        }
-      }
-      // ---- scores in log2 units, masking
-      const bool grp_on = (n >> 4) ? on1 : on0;
-      const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
-                             (r0 + 31 >= g.Nq) || (on0 != on1);
-      const int lim = g.causal ? row + g.off : 0x7fffffff;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) acc[kb][j] = fmaf(acc[kb][j], sl, -c_r);
-      if (need_mask) {  // wave-uniform: diagonal, padding and half-masked tiles only
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-            if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
-          }
-      }
-      float tmax = vmax(acc[0][0], acc[0][1]);
-#pragma unroll
-      for (int j = 2; j < 16; j += 2) tmax = vmax3(tmax, acc[0][j], acc[0][j + 1]);
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
-      tmax = vmax(tmax, xor32(tmax));
-      const float mnew = vmax(m, tmax);
-      if (__ballot(mnew > m) != 0ull) {
-        const float alpha = (mnew > m) ? fast_exp2(m - mnew) : 1.0f;  // m=-inf -> 0
-#pragma unroll
-        for (int db = 0; db < ND; ++db)
-#pragma unroll
-          for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-        l *= alpha;
-        m = mnew;
-      }
-      const float ms = m == -__builtin_inff() ? 0.0f : m;
-      // ---- P (fp16, also for bf16 inputs: 11 significant bits) and its row sum
-      v8h pf[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = fast_exp2(acc[kb][8 * c + j] - ms);
-            l += p;
-            pf[kb][c][j] = (_Float16)p;
-          }
-      // ---- O^T += V^T P^T
-      const int G16 = lane >> 4, i16 = lane & 15;
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const int ch0 = db * 32 + 16 * (G16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int keyb = kb * 32 + 16 * c + 4 * (G16 >> 1) + (i16 >> 2);
-            const uint16_t* p0 = Vs + keyb * C::VS + ch0;
-            const uint16_t* p1 = p0 + 8 * C::VS;
-            const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s*)(p0));
-            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s*)(p1));
-            const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[db] = mfma_f16(vf, pf[kb][c], o[db]);
-          }
-      }
-    }
-    if (C::STAGES == 2) {
-      if (it + 1 < hi) stash(buf ^ 1);
-      __syncthreads();
-    }
-  }
-
-  if (!wave_live) return;
-  l += xor32(l);
-  if (!row_ok) return;
+  constexpr int ND = D / 32;
   const size_t r = bhq * g.Nq + row;
   const size_t rows = (size_t)g.B * g.Hq * g.Nq;
-
-  // ---- partial state of one split (merged by k_combine)
   if (S > 1 || (MODE == kPass2 && !a.fuse)) {
     float* pm = S > 1 ? a.part_m + (size_t)sp * rows : a.hot_m;
     float* pl = S > 1 ? a.part_l + (size_t)sp * rows : a.hot_l;
@@ -362,7 +177,6 @@ __device__ __forceinline__ void attn_body(const Geom& g, const T* __restrict__ Q
       }
     return;
   }
-  // ---- one split: output directly (pass 2: merged with the cold state)
   float w1 = 0.0f, w2 = 0.0f, M = 0.0f, Lsum = 0.0f;
   const float* o1 = nullptr;
   if (MODE == kPass2) {
@@ -402,74 +216,519 @@ __device__ __forceinline__ void attn_body(const Geom& g, const T* __restrict__ Q
   }
 }
 
-template <int D, typename T, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn(Geom g, const T* __restrict__ Q,
-                                                  const T* __restrict__ K,
-                                                  const T* __restrict__ V, Fp4Ptrs f, Pass2Args a,
-                                                  int nunits, int S) {
-  attn_body<D, T, MODE, NW>(g, Q, K, V, f, a, nunits, S);
+// ---------------------------------------------------------------------------
+// D <= 256: direct-to-LDS double-buffered tiles, four waves per work group.
+
+template <int D>
+struct FaCfg {
+  static constexpr int TB = kTile * D * 2;  // bytes of one K or V tile
+  static constexpr int STAGE = 2 * TB;      // K then V
+  static constexpr size_t BYTES = 2 * (size_t)STAGE;
+  static constexpr int NLD = D / 32;  // 16-byte LDS loads per lane per tile half
+  static constexpr int GRP = kTile * 64;  // bytes of one 32-channel group of a tile
+};
+
+template <int D, typename T, int MODE>
+__device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
+                                        const T* __restrict__ K, const T* __restrict__ V,
+                                        const Fp4Ptrs& f, const Pass2Args& a, int nitems, int S) {
+  using C = FaCfg<D>;
+  using E = E16<T>;
+  typedef typename E::V8 V8;
+  extern __shared__ __attribute__((aligned(16))) uint8_t fa_smem[];
+  constexpr int NC = D / 16;  // 16-channel chunks of the QK contraction
+  constexpr int ND = D / 32;  // 32-channel blocks of the output
+  constexpr bool BF = std::is_same<T, __bf16>::value;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= nitems) return;  // uniform over the block
+  const RowBlocks rb = row_blocks(g);
+  const int wg = item % rb.nwg;
+  int u = item / rb.nwg;
+  const int sp = u % S;
+  u /= S;
+  const int hk = u % g.Hkv;
+  const int b = u / g.Hkv;
+  const int unit = (b * g.Hkv + hk) * rb.nwg + wg;
+  const WaveRows wr = wave_rows(g, rb, wg, wave);
+  const int hq = hk * g.G + wr.gi;
+  const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
+  const int r0 = wr.r0;
+  const int row = r0 + n;
+  const bool row_ok = wr.live && row < g.Nq;
+  const int d_wave =
+      wr.live ? (g.causal ? min(g.Nkv - 1, min(r0 + 31, g.Nq - 1) + g.off) / kTile : g.NT - 1) : -1;
+
+  // this split's part of the work group's tile list
+  int lo, hi;
+  const int32_t* tiles = nullptr;
+  const uint32_t* masks = nullptr;
+  {
+    const int ntot = MODE == kExact ? exact_tiles(g, rb, wg) : a.list_count[unit];
+    lo = split_lo(ntot, sp, S);
+    hi = split_lo(ntot, sp + 1, S);
+    if (MODE == kPass2) {
+      tiles = a.list_tiles + (size_t)unit * g.NT;
+      masks = a.list_masks + (size_t)unit * g.NT;
+    }
+  }
+  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
+
+  // resident Q^T operand: 8 elements per 16-channel chunk
+  V8 qf[NC];
+  {
+    const int rl = row_ok ? row : 0;
+    const T* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const V8*>(qp + 16 * c);
+  }
+  const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
+  const float sl = g.sl;
+
+  // LDS-writing loads: wave w loads 16-key block w of every 32-channel group;
+  // lane L carries key 16w + L/4 and the row's 16-byte slot L%4 (K: chunk
+  // (L%4) ^ ((key/4)%4), so the slot holds that chunk; V: chunk L%4).
+  const size_t head_bytes = (size_t)g.Nkv * D * 2;
+  const auto rK = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(K) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
+  const auto rV = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T*>(V) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
+  const int ckey = wave * 16 + (lane >> 2);
+  const uint32_t cK = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+  const uint32_t cV = (uint32_t)((lane & 3) * 16);
+  auto issue = [&](int t, int sb) {
+    // rows past the last key re-read the last key (their scores are masked)
+    const uint32_t rowoff = (uint32_t)min(t * kTile + ckey, g.Nkv - 1) * (uint32_t)(D * 2);
+    uint8_t* st = fa_smem + sb * C::STAGE + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < C::NLD; ++i) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void*)(st + i * C::GRP), 16, rowoff + cK,
+                                               i * 64, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void*)(st + C::TB + i * C::GRP), 16,
+                                               rowoff + cV, i * 64, 0, 0);
+    }
+  };
+
+  // per-lane LDS read offsets inside a 32-channel group
+  const int kx = (n >> 2) & 3;
+  const uint32_t kE = (uint32_t)(n * 64 + ((hh ^ kx) * 16));
+  const uint32_t kO = (uint32_t)(n * 64 + (((2 + hh) ^ kx) * 16));
+  const int G16 = lane >> 4, i16 = lane & 15;
+  const uint32_t vl = (uint32_t)((4 * (G16 >> 1) + (i16 >> 2)) * 64 +
+                                 (2 * (G16 & 1) + ((i16 & 3) >> 1)) * 16 + (i16 & 1) * 8);
+
+  float m = -__builtin_inff(), l = 0.0f;
+  v16f o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = v16f{};
+  const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  if (lo < hi) issue(tile_at(lo), 0);
+  for (int it = lo; it < hi; ++it) {
+    const int t = tile_at(it);
+    const int sb = (it - lo) & 1;
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile t are in LDS
+    if (BF) {
+      // the V rows this wave loaded, to fp16 in place
+      uint8_t* st = fa_smem + sb * C::STAGE + C::TB + wave * 1024 + lane * 16;
+#pragma unroll
+      for (int i = 0; i < C::NLD; ++i) {
+        uint4* p = reinterpret_cast<uint4*>(st + i * C::GRP);
+        *p = bf16x8_to_f16x8(*p);
+      }
+    }
+    __syncthreads();
+    if (it + 1 < hi) issue(tile_at(it + 1), sb ^ 1);
+
+    // does this wave compute tile t, and for which of its two groups?
+    bool on0, on1;
+    if (MODE == kExact) {
+      on0 = on1 = t <= d_wave;
+    } else {
+      const uint32_t mk = masks[it];
+      on0 = (mk >> (2 * wave)) & 1u;
+      on1 = (mk >> (2 * wave + 1)) & 1u;
+    }
+    if (!(wr.live && (on0 || on1))) continue;
+    const uint8_t* Ks = fa_smem + sb * C::STAGE;
+    const uint8_t* Vs = Ks + C::TB;
+    const int k0 = t * kTile;
+
+    // ---- S^T = K Q^T (raw dot products)
+    v16f acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      acc[kb] = v16f{};
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const V8 kf = *reinterpret_cast<const V8*>(Ks + (c >> 1) * C::GRP + kb * 2048 +
+                                                   ((c & 1) ? kO : kE));
+        acc[kb] = E::mma(kf, qf[c], acc[kb]);
+      }
+    }
+    // ---- masking: diagonal, padding and half-hot tiles only (wave-uniform)
+    const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
+                           (r0 + 31 >= g.Nq) || (on0 != on1);
+    if (need_mask) {
+      const bool grp_on = (n >> 4) ? on1 : on0;
+      const int lim = g.causal ? row + g.off : 0x7fffffff;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+        }
+    }
+    // ---- row maximum (raw), then in log2 units; lazy move of m
+    float tmax = vmax(acc[0][0], acc[0][1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) tmax = vmax3(tmax, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
+    tmax = vmax(tmax, xor32(tmax));
+    const float smax = fmaf(tmax, sl, -c_r);
+    const bool up = smax > m + kLazy;  // m = -inf: any visible key
+    if (__ballot(up) != 0ull) {
+      const float alpha = up ? fast_exp2(m - smax) : 1.0f;  // m = -inf -> 0
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      l *= alpha;
+      m = up ? smax : m;
+    }
+    const float bias = -(c_r + (m == -__builtin_inff() ? 0.0f : m));
+    // ---- P = 2^(s - m) in fp16 (also for bf16 inputs) and its row sum
+    v8h pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const v2f p2 = {fast_exp2(fmaf(acc[kb][8 * c + j], sl, bias)),
+                          fast_exp2(fmaf(acc[kb][8 * c + j + 1], sl, bias))};
+          const v2h h2 = __builtin_convertvector(p2, v2h);
+          l = __builtin_amdgcn_fdot2(h2, ones, l, false);
+          pf[kb][c][j] = h2[0];
+          pf[kb][c][j + 1] = h2[1];
+        }
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint8_t* p0 = Vs + db * C::GRP + (kb * 32 + 16 * c) * 64 + vl;
+          const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(p0));
+          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(p0 + 8 * 64));
+          const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma_f16(vf, pf[kb][c], o[db]);
+        }
+  }
+
+  if (!wr.live) return;
+  l += xor32(l);
+  if (!row_ok) return;
+  finish_row<D, T, MODE>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o);
 }
 
-// D = 512: one wave per SIMD, so the 256 output accumulators per lane can sit
-// in the accumulation registers beside the resident Q operand.
-template <int D, typename T, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_big(
+// Two work groups per compute unit up to D = 128 (registers <= 256 per
+// lane, LDS 2 x 64 KB), one at D = 256.
+template <int D, typename T, int MODE>
+__global__ __launch_bounds__(kWgWaves * 64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2, D >= 256 ? 1 : 2)))
+void k_fa(Geom g, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+          Fp4Ptrs f, Pass2Args a, int nitems, int S) {
+  fa_body<D, T, MODE>(g, Q, K, V, f, a, nitems, S);
+}
+
+// ---------------------------------------------------------------------------
+// D = 512: one padded LDS stage filled through registers.
+
+template <int D>
+struct BigCfg {
+  static constexpr int KS = D + 8;    // halves per K row (16-byte pad)
+  static constexpr int VS = D + 32;   // halves per V row (64-byte pad)
+  static constexpr int K_HALVES = kTile * KS;
+  static constexpr int V_HALVES = kTile * VS;
+  static constexpr int STAGE = K_HALVES + V_HALVES;
+  static constexpr size_t BYTES = (size_t)STAGE * 2;
+  static constexpr int CHUNKS = 2 * kTile * D / 8;  // 16-byte chunks per K+V tile
+};
+
+template <int D, typename T, int MODE>
+__device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
+                                         const T* __restrict__ K, const T* __restrict__ V,
+                                         const Fp4Ptrs& f, const Pass2Args& a, int nitems,
+                                         int S) {
+  using C = BigCfg<D>;
+  using E = E16<T>;
+  typedef typename E::V8 V8;
+  extern __shared__ uint16_t smem[];
+  constexpr int NW = kWgWaves;
+  constexpr int NC = D / 16;
+  constexpr int ND = D / 32;
+  constexpr int PER = (C::CHUNKS + NW * 64 - 1) / (NW * 64);
+  constexpr int RND = PER < 8 ? PER : 8;  // chunks per staging round
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, hh = lane >> 5;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  if (item >= nitems) return;
+  const RowBlocks rb = row_blocks(g);
+  const int wg = item % rb.nwg;
+  int u = item / rb.nwg;
+  const int sp = u % S;
+  u /= S;
+  const int hk = u % g.Hkv;
+  const int b = u / g.Hkv;
+  const int unit = (b * g.Hkv + hk) * rb.nwg + wg;
+  const WaveRows wr = wave_rows(g, rb, wg, wave);
+  const int hq = hk * g.G + wr.gi;
+  const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
+  const int r0 = wr.r0;
+  const int row = r0 + n;
+  const bool row_ok = wr.live && row < g.Nq;
+  const int d_wave =
+      wr.live ? (g.causal ? min(g.Nkv - 1, min(r0 + 31, g.Nq - 1) + g.off) / kTile : g.NT - 1) : -1;
+
+  int lo, hi;
+  const int32_t* tiles = nullptr;
+  const uint32_t* masks = nullptr;
+  {
+    const int ntot = MODE == kExact ? exact_tiles(g, rb, wg) : a.list_count[unit];
+    lo = split_lo(ntot, sp, S);
+    hi = split_lo(ntot, sp + 1, S);
+    if (MODE == kPass2) {
+      tiles = a.list_tiles + (size_t)unit * g.NT;
+      masks = a.list_masks + (size_t)unit * g.NT;
+    }
+  }
+  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
+
+  V8 qf[NC];
+  {
+    const int rl = row_ok ? row : 0;
+    const T* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const V8*>(qp + 16 * c);
+  }
+  const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
+  const float sl = g.sl;
+
+  float m = -__builtin_inff(), l = 0.0f;
+  v16f o[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) o[i] = v16f{};
+
+  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(K) + bhk * (size_t)g.Nkv * D;
+  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(V) + bhk * (size_t)g.Nkv * D;
+
+  // cooperative staging: chunk c < CHUNKS/2 is K (row c / (D/8)), else V
+  auto fetch1 = [&](int t, int c) {
+    uint4 z = {0u, 0u, 0u, 0u};
+    if (c < C::CHUNKS) {
+      const int isv = c >= C::CHUNKS / 2;
+      const int cc = isv ? c - C::CHUNKS / 2 : c;
+      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
+      const int key = t * kTile + r;
+      if (key < g.Nkv) z = *reinterpret_cast<const uint4*>((isv ? Vh : Kh) + (size_t)key * D + col);
+    }
+    return z;
+  };
+  auto stash1 = [&](int c, uint4 z) {
+    if (c < C::CHUNKS) {
+      const int isv = c >= C::CHUNKS / 2;
+      if (std::is_same<T, __bf16>::value && isv) z = bf16x8_to_f16x8(z);
+      const int cc = isv ? c - C::CHUNKS / 2 : c;
+      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
+      uint16_t* dst = isv ? smem + C::K_HALVES + r * C::VS + col : smem + r * C::KS + col;
+      *reinterpret_cast<uint4*>(dst) = z;
+    }
+  };
+  uint4 pre[RND];
+
+  for (int it = lo; it < hi; ++it) {
+    const int t = tile_at(it);
+    __syncthreads();
+    for (int r0c = 0; r0c < PER; r0c += RND) {
+#pragma unroll
+      for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + (r0c + i) * NW * 64);
+#pragma unroll
+      for (int i = 0; i < RND; ++i) stash1(tid + (r0c + i) * NW * 64, pre[i]);
+    }
+    __syncthreads();
+
+    bool on0, on1;
+    if (MODE == kExact) {
+      on0 = on1 = t <= d_wave;
+    } else {
+      const uint32_t mk = masks[it];
+      on0 = (mk >> (2 * wave)) & 1u;
+      on1 = (mk >> (2 * wave + 1)) & 1u;
+    }
+    if (!(wr.live && (on0 || on1))) continue;
+    const uint16_t* Ks = smem;
+    const uint16_t* Vs = Ks + C::K_HALVES;
+    const int k0 = t * kTile;
+    v16f acc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      acc[kb] = v16f{};
+      const uint16_t* kr = Ks + (kb * 32 + n) * C::KS + 8 * hh;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const V8 kf = *reinterpret_cast<const V8*>(kr + 16 * c);
+        acc[kb] = E::mma(kf, qf[c], acc[kb]);
+      }
+    }
+    const bool grp_on = (n >> 4) ? on1 : on0;
+    const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
+                           (r0 + 31 >= g.Nq) || (on0 != on1);
+    const int lim = g.causal ? row + g.off : 0x7fffffff;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[kb][j] = fmaf(acc[kb][j], sl, -c_r);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
+          if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+        }
+    }
+    float tmax = vmax(acc[0][0], acc[0][1]);
+#pragma unroll
+    for (int j = 2; j < 16; j += 2) tmax = vmax3(tmax, acc[0][j], acc[0][j + 1]);
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
+    tmax = vmax(tmax, xor32(tmax));
+    const float mnew = vmax(m, tmax);
+    if (__ballot(mnew > m) != 0ull) {
+      const float alpha = (mnew > m) ? fast_exp2(m - mnew) : 1.0f;  // m=-inf -> 0
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
+      l *= alpha;
+      m = mnew;
+    }
+    const float ms = m == -__builtin_inff() ? 0.0f : m;
+    v8h pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = fast_exp2(acc[kb][8 * c + j] - ms);
+          l += p;
+          pf[kb][c][j] = (_Float16)p;
+        }
+    const int G16 = lane >> 4, i16 = lane & 15;
+#pragma unroll
+    for (int db = 0; db < ND; ++db) {
+      const int ch0 = db * 32 + 16 * (G16 & 1) + 4 * (i16 & 3);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int keyb = kb * 32 + 16 * c + 4 * (G16 >> 1) + (i16 >> 2);
+          const uint16_t* p0 = Vs + keyb * C::VS + ch0;
+          const uint16_t* p1 = p0 + 8 * C::VS;
+          const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(p0));
+          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(p1));
+          const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[db] = mfma_f16(vf, pf[kb][c], o[db]);
+        }
+    }
+  }
+
+  if (!wr.live) return;
+  l += xor32(l);
+  if (!row_ok) return;
+  finish_row<D, T, MODE>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o);
+}
+
+// One wave per SIMD, so the 256 output accumulators per lane can sit in the
+// accumulation registers beside the resident Q operand.
+template <int D, typename T, int MODE>
+__global__ __launch_bounds__(kWgWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_big(
     Geom g, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, Fp4Ptrs f,
-    Pass2Args a, int nunits, int S) {
-  attn_body<D, T, MODE, NW>(g, Q, K, V, f, a, nunits, S);
+    Pass2Args a, int nitems, int S) {
+  big_body<D, T, MODE>(g, Q, K, V, f, a, nitems, S);
 }
 
-// Hot mask -> per unit (batch, kv-head, POS positions) list of the tiles hot
-// for any of its G*POS/16 row groups, ascending, with a bit mask of the groups
-// each tile is hot for (bit gi*POS/16 + local group).  One wavefront per unit.
-__global__ __launch_bounds__(64) void k_compact(Geom g, int pos, const uint32_t* __restrict__ bits,
+// ---------------------------------------------------------------------------
+
+// Hot mask -> per work group (batch, kv-head, four row blocks) the list of the
+// tiles hot for any of its verdict groups, ascending, with a mask of the
+// groups each tile is hot for (bit 2w + k: wave w's k-th 16-row group).  One
+// wavefront per work group; lane j handles hot word j (+64, ...).
+__global__ __launch_bounds__(64) void k_compact(Geom g, const uint32_t* __restrict__ bits,
                                                 int32_t* tiles, uint32_t* masks, int32_t* count,
                                                 int nunits) {
   const int unit = blockIdx.x;
   if (unit >= nunits) return;
   const int lane = threadIdx.x;
-  const int gpu = pos / 16;
-  const int nqb = (g.Nq + pos - 1) / pos;
-  const int qblk = unit % nqb;
-  const int hk = (unit / nqb) % g.Hkv;
-  const int b = unit / (nqb * g.Hkv);
+  const RowBlocks rb = row_blocks(g);
+  const int wg = unit % rb.nwg;
+  const int bk = unit / rb.nwg;
+  const int b = bk / g.Hkv, hk = bk % g.Hkv;
+  // the hot words of the eight verdict groups (nullptr when absent)
+  const uint32_t* gp[2 * kWgWaves];
+#pragma unroll
+  for (int w = 0; w < kWgWaves; ++w) {
+    const WaveRows wr = wave_rows(g, rb, wg, w);
+    const size_t bhq = (size_t)b * g.Hq + hk * g.G + wr.gi;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int grp = wr.r0 / 16 + k;
+      gp[2 * w + k] = (wr.live && grp < g.NG) ? bits + (bhq * g.NG + grp) * g.W : nullptr;
+    }
+  }
+  int32_t* tl = tiles + (size_t)unit * g.NT;
+  uint32_t* ml = masks + (size_t)unit * g.NT;
   int base = 0;
   for (int w0 = 0; w0 < g.W; w0 += 64) {
     const int w = w0 + lane;
-    uint32_t u = 0u;
-    if (w < g.W) {
-      for (int gi = 0; gi < g.G; ++gi) {
-        const size_t bhq = (size_t)b * g.Hq + hk * g.G + gi;
-        for (int lg = 0; lg < gpu; ++lg) {
-          const int grp = qblk * gpu + lg;
-          if (grp < g.NG) u |= bits[(bhq * g.NG + grp) * g.W + w];
-        }
-      }
+    uint32_t word[2 * kWgWaves];
+    uint32_t un = 0u;
+#pragma unroll
+    for (int k = 0; k < 2 * kWgWaves; ++k) {
+      word[k] = (w < g.W && gp[k]) ? gp[k][w] : 0u;
+      un |= word[k];
     }
-    const int cnt = __popc(u);
+    const int cnt = __popc(un);
     int incl = cnt;
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o);
       if (lane >= o) incl += v;
     }
-    int pos_out = base + incl - cnt;
-    uint32_t rem = u;
+    int pos = base + incl - cnt;
+    uint32_t rem = un;
     while (rem) {
       const int bit = __ffs(rem) - 1;
       rem &= rem - 1u;
-      const int t = w * 32 + bit;
       uint32_t mk = 0u;
-      for (int gi = 0; gi < g.G; ++gi) {
-        const size_t bhq = (size_t)b * g.Hq + hk * g.G + gi;
-        for (int lg = 0; lg < gpu; ++lg) {
-          const int grp = qblk * gpu + lg;
-          if (grp < g.NG && ((bits[(bhq * g.NG + grp) * g.W + w] >> bit) & 1u))
-            mk |= 1u << (gi * gpu + lg);
-        }
-      }
-      tiles[(size_t)unit * g.NT + pos_out] = t;
-      masks[(size_t)unit * g.NT + pos_out] = mk;
-      ++pos_out;
+#pragma unroll
+      for (int k = 0; k < 2 * kWgWaves; ++k) mk |= ((word[k] >> bit) & 1u) << k;
+      tl[pos] = w * 32 + bit;
+      ml[pos] = mk;
+      ++pos;
     }
     base += __shfl(incl, 63);
   }
@@ -565,23 +824,29 @@ __global__ void k_combine(Geom g, Fp4Ptrs f, Pass2Args a, int S, long nrows) {
             reinterpret_cast<T*>(a.out) + r * D + ch, want_lse ? a.lse + r : nullptr);
 }
 
-template <int D, typename T, int MODE, int NW>
+template <int D, typename T, int MODE>
 hipError_t run_attn(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
                     const Pass2Args& a, int S, hipStream_t s) {
-  const int nunits = g.B * g.Hkv * ((g.Nq + Cfg<D>::POS - 1) / Cfg<D>::POS) * S;
-  if (nunits == 0) return hipSuccess;
+  const int nitems = attn_units(g) * S;
+  if (nitems == 0) return hipSuccess;
   void (*kern)(Geom, const T*, const T*, const T*, Fp4Ptrs, Pass2Args, int, int);
-  if constexpr (D >= 512) kern = k_attn_big<D, T, MODE, NW>;
-  else kern = k_attn<D, T, MODE, NW>;
+  size_t bytes;
+  if constexpr (D >= 512) {
+    kern = k_attn_big<D, T, MODE>;
+    bytes = BigCfg<D>::BYTES;
+  } else {
+    kern = k_fa<D, T, MODE>;
+    bytes = FaCfg<D>::BYTES;
+  }
   static bool attr_done = false;
   if (!attr_done) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)Cfg<D>::BYTES);
+                                       (int)bytes);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  hipLaunchKernelGGL(kern, dim3(nunits), dim3(NW * 64), Cfg<D>::BYTES, s, g, (const T*)q,
-                     (const T*)k, (const T*)v, f, a, nunits, S);
+  hipLaunchKernelGGL(kern, dim3(nitems), dim3(kWgWaves * 64), bytes, s, g, (const T*)q,
+                     (const T*)k, (const T*)v, f, a, nitems, S);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const long nrows = (long)g.B * g.Hq * g.Nq;
@@ -594,18 +859,13 @@ hipError_t run_attn(const Geom& g, const void* q, const void* k, const void* v, 
 template <int MODE, typename T>
 hipError_t dispatch_t(const Geom& g, const void* q, const void* k, const void* v,
                       const Fp4Ptrs& f, const Pass2Args& a, int S, hipStream_t s) {
-#define APA_FA_CASE(DD, GG)                                                              \
-  if (g.D == DD && g.G == GG)                                                            \
-    return run_attn<DD, T, MODE, GG * Cfg<DD>::POS / 32>(g, q, k, v, f, a, S, s);
-#define APA_FA_D(DD) APA_FA_CASE(DD, 1) APA_FA_CASE(DD, 2) APA_FA_CASE(DD, 3) \
-  APA_FA_CASE(DD, 4) APA_FA_CASE(DD, 6) APA_FA_CASE(DD, 8)
-  APA_FA_D(64)
-  APA_FA_D(128)
-  APA_FA_D(256)
-  APA_FA_D(512)
-#undef APA_FA_D
-#undef APA_FA_CASE
-  return hipErrorInvalidValue;
+  switch (g.D) {
+    case 64: return run_attn<64, T, MODE>(g, q, k, v, f, a, S, s);
+    case 128: return run_attn<128, T, MODE>(g, q, k, v, f, a, S, s);
+    case 256: return run_attn<256, T, MODE>(g, q, k, v, f, a, S, s);
+    case 512: return run_attn<512, T, MODE>(g, q, k, v, f, a, S, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MODE>
@@ -617,28 +877,27 @@ hipError_t dispatch(const Geom& g, const void* q, const void* k, const void* v, 
 
 }  // namespace
 
-int attn_positions(int D) { return D >= 512 ? 32 : 64; }
+int attn_units(const Geom& g) { return g.B * g.Hkv * row_blocks(g).nwg; }
 
 int attn_splits(const Geom& g) {
-  const int pos = attn_positions(g.D);
-  const long units = (long)g.B * g.Hkv * ((g.Nq + pos - 1) / pos);
+  const long units = attn_units(g);
   if (units <= 0) return 1;
-  // one work group per compute unit of the 256-CU part (the register use of
-  // the D <= 256 kernels allows one resident group of G*POS/32 waves per CU)
-  long S = (256 + units - 1) / units;
+  // about three work groups per resident slot of the 256-CU part (two per CU
+  // up to D = 128, one above), so the dispatcher can even out their lengths
+  const long slots = 256L * (g.D <= 128 ? 2 : 1);
+  long S = (3 * slots + units - 1) / units;
   if (S > 8) S = 8;
-  // at least 4 tiles per split of the longest key range
-  long maxs = g.NT / 4;
+  // at least 16 tiles per split of the longest key range
+  long maxs = g.NT / 16;
   if (maxs < 1) maxs = 1;
   if (S > maxs) S = maxs;
   return (int)(S < 1 ? 1 : S);
 }
 
 hipError_t launch_pass2(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a, hipStream_t s) {
-  const int pos = attn_positions(g.D);
-  const int nunits = g.B * g.Hkv * ((g.Nq + pos - 1) / pos);
+  const int nunits = attn_units(g);
   if (nunits == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_compact, dim3(nunits), dim3(64), 0, s, g, pos, a.bits, a.list_tiles,
+  hipLaunchKernelGGL(k_compact, dim3(nunits), dim3(64), 0, s, g, a.bits, a.list_tiles,
                      a.list_masks, a.list_count, nunits);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
