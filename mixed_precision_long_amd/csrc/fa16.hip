@@ -369,18 +369,37 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
         acc[kb] = E::mma(kf, qf[c], acc[kb]);
       }
     }
-    // ---- masking: diagonal, padding and half-hot tiles only (wave-uniform)
+    // ---- V^T operands (DS_READ_B64_TR_B16 in P's key order); up to D = 128
+    // the whole tile's are read here, so the reads overlap the softmax
+    auto vread = [&](int db, int kb, int c) {
+      const uint8_t* p0 = Vs + db * C::GRP + (kb * 32 + 16 * c) * 64 + vl;
+      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p0));
+      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(p0 + 8 * 64));
+      return __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int NV = D <= 128 ? ND : 1;
+    v8h vf[NV][2][2];
+    if (D <= 128) {
+#pragma unroll
+      for (int db = 0; db < NV; ++db)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int c = 0; c < 2; ++c) vf[db][kb][c] = vread(db, kb, c);
+    }
+    // ---- key masking: diagonal and padding tiles, rows past Nq (wave-uniform)
     const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
-                           (r0 + 31 >= g.Nq) || (on0 != on1);
+                           (r0 + 31 >= g.Nq);
     if (need_mask) {
-      const bool grp_on = (n >> 4) ? on1 : on0;
       const int lim = g.causal ? row + g.off : 0x7fffffff;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+          if (!(row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
         }
     }
     // ---- row maximum (raw), then in log2 units; lazy move of m
@@ -390,7 +409,9 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
 #pragma unroll
     for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
     tmax = vmax(tmax, xor32(tmax));
-    const float smax = fmaf(tmax, sl, -c_r);
+    // pass 2: a 16-row group the tile is not hot for sees no key of it
+    const bool grp_on = MODE == kExact || ((n >> 4) ? on1 : on0);
+    const float smax = grp_on ? fmaf(tmax, sl, -c_r) : -__builtin_inff();
     const bool up = smax > m + kLazy;  // m = -inf: any visible key
     if (__ballot(up) != 0ull) {
       const float alpha = up ? fast_exp2(m - smax) : 1.0f;  // m = -inf -> 0
@@ -401,7 +422,8 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
       l *= alpha;
       m = up ? smax : m;
     }
-    const float bias = -(c_r + (m == -__builtin_inff() ? 0.0f : m));
+    const float bias =
+        grp_on ? -(c_r + (m == -__builtin_inff() ? 0.0f : m)) : -__builtin_inff();
     // ---- P = 2^(s - m) in fp16 (also for bf16 inputs) and its row sum
     v8h pf[2][2];
 #pragma unroll
@@ -423,15 +445,8 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const uint8_t* p0 = Vs + db * C::GRP + (kb * 32 + 16 * c) * 64 + vl;
-          const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(p0));
-          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(p0 + 8 * 64));
-          const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = mfma_f16(vf, pf[kb][c], o[db]);
-        }
+        for (int c = 0; c < 2; ++c)
+          o[db] = mfma_f16(D <= 128 ? vf[db % NV][kb][c] : vread(db, kb, c), pf[kb][c], o[db]);
   }
 
   if (!wr.live) return;
