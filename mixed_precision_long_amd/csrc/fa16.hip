@@ -246,7 +246,9 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= nitems) return;  // uniform over the block
   const RowBlocks rb = row_blocks(g);
-  const int wg = item % rb.nwg;
+  // exact: each (batch, kv-head, split) from its last query positions (the
+  // longest causal key ranges) down
+  const int wg = MODE == kExact ? rb.nwg - 1 - item % rb.nwg : item % rb.nwg;
   int u = item / rb.nwg;
   const int sp = u % S;
   u /= S;
@@ -500,7 +502,7 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= nitems) return;
   const RowBlocks rb = row_blocks(g);
-  const int wg = item % rb.nwg;
+  const int wg = MODE == kExact ? rb.nwg - 1 - item % rb.nwg : item % rb.nwg;
   int u = item / rb.nwg;
   const int sp = u % S;
   u /= S;
