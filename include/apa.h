@@ -45,6 +45,9 @@ typedef enum apa_status {
 
 enum { APA_F16 = 0, APA_BF16 = 1 };        /* input / output element type */
 enum { APA_MXFP4 = 0, APA_NVFP4 = 1 };     /* FP4 block format             */
+/* How apa_pass1 maps 32-row blocks of one query head to wavefronts when it
+ * is given a workspace (see apa_pass1).  AUTO picks from the shape. */
+enum { APA_SCHED_AUTO = 0, APA_SCHED_WHOLE = 1, APA_SCHED_PAIRS = 2, APA_SCHED_TRIPLES = 3 };
 
 /* Problem descriptor.  Fill it with apa_problem_init() and override fields. */
 typedef struct apa_problem {
@@ -59,10 +62,12 @@ typedef struct apa_problem {
                                      (4)                                         */
   float hot_frame_offset;         /* H: a hot tile lifts the frame to at most
                                      max(m, c - H); an integer in [0, 64] (32)  */
+  int32_t pass1_schedule;         /* APA_SCHED_*: scheduling only, the results
+                                     agree up to FP32 summation order (AUTO)   */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
- * fp16, causal. */
+ * fp16, causal, APA_SCHED_AUTO. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 
@@ -141,16 +146,22 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
  * apa_quantize for the same problem.
  * ws: NULL, or apa_workspace_bytes(p, APA_CALL_PASS1) bytes (0 for problems
  * whose 32-row blocks already fill the GPU).  With a workspace, each long
- * visit order is cut in two and run by two wavefronts of one work group at
- * once; the workspace holds the tiles the second one cannot decide until the
- * first is done (at most 512 per 32-row block, 292 bytes each) and room to
- * hand the first one's state to a re-walk of the second half, for blocks
- * with more undecided tiles than that.  Without
- * one, every block runs as one wavefront (slower when the blocks do not fill
- * the GPU).  The verdicts and the state are those of a single walk up to FP32
- * summation order; the returned frame cold_m is then the larger of the two
- * halves' frames (the state is scaled to match, so cold_l * 2^cold_m and
- * cold_o / cold_l do not depend on it). */
+ * visit order (64 tiles or more) is cut in two: a head wavefront walks its
+ * first part while a tail wavefront of the same work group walks the rest.
+ * APA_SCHED_PAIRS gives every block its own tail wavefront (two per block);
+ * APA_SCHED_TRIPLES runs three blocks on four wavefronts, one tail
+ * wavefront walking the three shorter tails one after the other (D <= 256;
+ * at D = 512 it runs as PAIRS); APA_SCHED_WHOLE keeps one wavefront per
+ * block.  AUTO takes PAIRS while two waves per block fit the GPU's wave
+ * slots at once, TRIPLES while four per three blocks do, else WHOLE.  The
+ * workspace holds the tiles a tail cannot decide until its head is done
+ * (at most 512 per 32-row block, 292 bytes each) and room to hand the
+ * head's state to a re-walk of the tail, for blocks with more undecided
+ * tiles than that.  Without one, every block runs as one wavefront (slower
+ * when the blocks do not fill the GPU).  The verdicts and the state are
+ * those of a single walk up to FP32 summation order; the returned frame
+ * cold_m is then the larger of the two parts' frames (the state is scaled
+ * to match, so cold_l * 2^cold_m and cold_o / cold_l do not depend on it). */
 apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
                      float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
                      void* ws, size_t ws_bytes, void* stream);

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libapa.so")
 APA_OK, APA_ERR_INVALID_ARG, APA_ERR_UNSUPPORTED, APA_ERR_WORKSPACE, APA_ERR_HIP = range(5)
 APA_F16, APA_BF16 = 0, 1
 APA_MXFP4, APA_NVFP4 = 0, 1
+SCHED_AUTO, SCHED_WHOLE, SCHED_PAIRS, SCHED_TRIPLES = range(4)
 CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
@@ -37,7 +38,7 @@ class Problem(C.Structure):
                 ("Nkv", C.c_int32), ("D", C.c_int32), ("dtype", C.c_int32),
                 ("is_causal", C.c_int32), ("scale", C.c_float), ("tile", C.c_int32),
                 ("row_group", C.c_int32), ("fmt", C.c_int32), ("tau", C.c_float),
-                ("hot_frame_offset", C.c_float)]
+                ("hot_frame_offset", C.c_float), ("pass1_schedule", C.c_int32)]
 
 
 class Fp4Layout(C.Structure):
@@ -86,11 +87,11 @@ def status_string(code: int) -> str:
 
 
 def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
-            fmt=APA_MXFP4) -> Problem:
+            fmt=APA_MXFP4, sched=SCHED_AUTO) -> Problem:
     p = Problem()
     lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
-    p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt = (
-        dtype, causal, scale, tau, hoff, fmt)
+    p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt, p.pass1_schedule = (
+        dtype, causal, scale, tau, hoff, fmt, sched)
     return p
 
 

@@ -8,7 +8,8 @@ namespace apa {
 
 struct Geom {
   int B, Hq, Hkv, G, Nq, Nkv, D, NqP, NkvP, NT, NG, W, causal, off, bf16;
-  float sl;  // fl32(scale * fl32(log2 e))
+  float sl;   // fl32(scale * fl32(log2 e))
+  int sched;  // requested pass-1 schedule (APA_SCHED_*)
 };
 
 // Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the
@@ -48,7 +49,8 @@ struct Pass1Out {
 hipError_t launch_quantize(const Geom& g, const void* q, const void* k, const void* v,
                            const Fp4Ptrs& f, const QuantWs& ws, hipStream_t s);
 // Pass-1 workspace bytes (0: the problem runs one wave per unit); with ws the
-// long visit orders run as two waves each plus a join kernel.
+// long visit orders are cut into a head and a tail walk (two waves per unit,
+// or three heads and one tail wave per three units) plus a re-walk kernel.
 size_t pass1_ws_bytes(const Geom& g);
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                         const Pass1Out& o, void* ws, hipStream_t s);

@@ -31,6 +31,7 @@ bool valid_problem(const apa_problem* p) {
   if (!(H >= 0.0f && H <= 64.0f) || floorf(H) != H) return false;
   if (isnan(p->scale)) return false;
   if (p->Nq > 0 && p->Nkv == 0) return false;
+  if (p->pass1_schedule < APA_SCHED_AUTO || p->pass1_schedule > APA_SCHED_TRIPLES) return false;
   return true;
 }
 
@@ -50,6 +51,7 @@ Geom geom(const apa_problem* p) {
   g.bf16 = p->dtype == APA_BF16;
   const float scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->D));
   g.sl = scale * kLog2e32;
+  g.sched = p->pass1_schedule;
   return g;
 }
 
@@ -172,6 +174,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->fmt = APA_MXFP4;
   p->tau = 4.0f;
   p->hot_frame_offset = 32.0f;
+  p->pass1_schedule = APA_SCHED_AUTO;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }

@@ -46,11 +46,16 @@
 // each tile's two verdicts as an LDS byte, and the words are built after the
 // walk (lane j builds one word); beyond that they are kept in the loop.
 //
-// Balance.  With fewer units than about three quarters of the chip's wave
-// slots, a wave per unit leaves SIMDs idle while others run two waves, so each
-// long visit order is cut in two and run by two waves of one work group at
-// once: the head wave takes positions [0, h) (tile 0, the diagonal and the
-// recent half), the tail wave positions [h, n).  The tail wave does not know
+// Balance.  With fewer units than the chip's wave slots, a wave per unit
+// leaves SIMDs idle while others run two waves, so each long visit order is
+// cut in two and walked by two waves of one work group at once: the head wave
+// takes positions [0, h) (tile 0, the diagonal and the recent part), a tail
+// wave positions [h, n).  While two waves per unit fit the slots, every unit
+// has its own tail wave (cut near the middle); while four waves per three
+// units fit, a work group holds three units, their three head waves and one
+// wave that walks the three tails (cut near three quarters) one after the
+// other, parking each tail's state in the workspace until the heads are done,
+// so that every SIMD keeps two waves to the end.  A tail walk does not know
 // lambda at position h.  It first replays positions [0, 32) without P V (a
 // prefix of the head's walk, so its lambda is a lower bound of the head's),
 // then walks its own tiles with the vote taken against a lower bound plus its
@@ -96,6 +101,11 @@ constexpr int kLogTiles = 4096;
 // (D/2 per lane) need the accumulation registers.
 template <int D>
 constexpr int kWavesPerSimd = D >= 256 ? 1 : 2;
+
+// Head states a work group holds in LDS: three (triple schedule) up to
+// D = 256; at D = 512 a head state is 65 KB, so two (pair schedule only).
+template <int D>
+constexpr int kSlots = D >= 512 ? 2 : 3;
 
 template <int D>
 struct Tile {
@@ -218,6 +228,7 @@ template <int D>
 struct Ctx {
   size_t bhq, bhk;
   int r0, row, d0, d1, dW;
+  int tmask;  // tiles t >= tmask need the mask (diagonal, padding keys, rows past Nq)
   bool row_ok, has_g1;
   v4i qa[Tile<D>::NH];  // Q^T operand, 16 bytes per 64-channel half
   int qs[Tile<D>::NH];  // its E8M0 bytes (block scale + head exponent)
@@ -244,6 +255,9 @@ __device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs
   c.d0 = diag(min(c.r0 + 15, g.Nq - 1));
   c.d1 = c.has_g1 ? diag(min(c.r0 + 31, g.Nq - 1)) : -1;
   c.dW = max(c.d0, c.d1);
+  // a tile needs the mask when it holds keys past Nkv (t >= Nkv / 64), keys
+  // past a row's diagonal (64 t + 63 > r0 + off) or rows past Nq
+  c.tmask = c.r0 + 31 >= g.Nq ? 0 : min(g.Nkv / kTile, g.causal ? (c.r0 + g.off + 1) / kTile : g.NT);
   const int jq = (int)f.q_head[c.bhq * 4 + 2];
   const uint8_t* qc = f.q_codes + (c.bhq * g.NqP + c.row) * (D / 2);
   const uint8_t* qsc = f.q_scales + (c.bhq * g.NqP + c.row) * (D / 32);
@@ -296,10 +310,22 @@ struct Words {
 
 __device__ __forceinline__ int shared_word(int tb) { return ((tb + 1) & 31) ? (tb >> 5) : -1; }
 
-// Where a visit order of npos >= kMinSplit positions is cut: the tail also
-// replays kReplay positions and its tiles cost a little more (the record
-// keeping), so the head takes half of npos + kReplay plus about 1.5 %.
-__host__ __device__ inline int split_point(int npos) { return (npos + kReplay) / 2 + npos / 64; }
+// Schedules of the 32-row units over wavefronts (the values of the problem's
+// pass-1 schedule): one wave per unit; a head and a tail wave per unit; three
+// head waves and one wave that walks the three tails, per three units.
+enum Sched { kSchedWhole = 1, kSchedPairs = 2, kSchedTriples = 3 };
+
+// Where a visit order of npos >= kMinSplit positions is cut: the head walks
+// [0, cut), the tail replays kReplay positions and walks [cut, npos), and its
+// tiles cost a little more (the record keeping).  With a tail per unit the
+// head takes half of npos + kReplay plus about 1.5 %; with one tail wave for
+// three units, three quarters of it (the tail wave then walks three quarter
+// tails and settles three units) plus about 3 %, the share that measured
+// fastest at 2048 x 122880.
+__host__ __device__ inline int cut_point(int npos, int sched) {
+  if (sched == kSchedTriples) return 3 * (npos + kReplay) / 4 + npos / 32;
+  return (npos + kReplay) / 2 + npos / 64;
+}
 
 template <int D>
 __device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint32_t b0,
@@ -363,7 +389,7 @@ template <int D>
 __device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const Ctx<D>& c, int t,
                                             int hh) {
   const int k0 = t * kTile;
-  if ((k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > c.r0 + g.off) || (c.r0 + 31 >= g.Nq)) {
+  if (t >= c.tmask) {
     const int lim = g.causal ? c.row + g.off : 0x7fffffff;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -375,8 +401,11 @@ __device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const
   }
 }
 
-// group maxima: gown of this lane's 32-key block hh, goth of the other block
-__device__ __forceinline__ void tile_maxima(const v16f (&acc)[2], float& gown, float& goth) {
+// Maxima of the tile's two 32-key groups (keys 0-31: b0, 32-63: b1) of this
+// lane's row, in every lane: each lane's partial maxima, one exchange that
+// gives lanes < 32 both halves of group 0 and lanes >= 32 both halves of
+// group 1, and one that hands each lane the other group's maximum.
+__device__ __forceinline__ void group_maxima(const v16f (&acc)[2], float& b0, float& b1) {
   float gl0 = vmax(acc[0][0], acc[0][1]), gl1 = vmax(acc[1][0], acc[1][1]);
 #pragma unroll
   for (int j = 2; j < 16; j += 2) {
@@ -385,21 +414,22 @@ __device__ __forceinline__ void tile_maxima(const v16f (&acc)[2], float& gown, f
   }
   int x0, x1;
   swap_halves(__float_as_int(gl0), __float_as_int(gl1), x0, x1);
-  gown = vmax(__int_as_float(x0), __int_as_float(x1));
-  goth = xor32(gown);
+  const int own = __float_as_int(vmax(__int_as_float(x0), __int_as_float(x1)));
+  swap_halves(own, own, x0, x1);
+  b0 = __int_as_float(x0);
+  b1 = __int_as_float(x1);
 }
 
-// Step 2: the FP4 codes of P for divisors 2^xof (this lane's block) and 2^xtf
-// (the other), rearranged into the MFMA operand layout (lanes < 32 carry keys
-// 0-31, lanes >= 32 keys 32-63).
-__device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float xof, float xtf, int hh) {
-  const int xo = (int)xof, xt = (int)xtf;
+// Step 2: the FP4 codes of P for divisors 2^x0 (keys 0-31) and 2^x1 (keys
+// 32-63), rearranged into the MFMA operand layout (lanes < 32 carry keys 0-31,
+// lanes >= 32 keys 32-63).
+__device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float x0f, float x1f) {
+  const int x0 = (int)x0f, x1 = (int)x1f;
   // fast path: both divisors normal with room below for the codes that matter
-  const bool odd = (unsigned)(xo + 124) > 244u || (unsigned)(xt + 124) > 244u;
+  const bool odd = (unsigned)(x0 + 124) > 244u || (unsigned)(x1 + 124) > 244u;
   unsigned pk[2][2];
   if (__ballot(odd) == 0ull) {
-    const float so = __int_as_float((xo + 127) << 23), st = __int_as_float((xt + 127) << 23);
-    const float sc0 = hh ? st : so, sc1 = hh ? so : st;
+    const float sc0 = __int_as_float((x0 + 127) << 23), sc1 = __int_as_float((x1 + 127) << 23);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const float sc = kb ? sc1 : sc0;
@@ -418,7 +448,7 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float xof, float 
     // frame-relative form 2^(s - X) with a unit divisor
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const float sub = (kb == hh) ? xof : xtf;
+      const float sub = kb ? x1f : x0f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         unsigned w = 0;
@@ -514,16 +544,28 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   int cur_w = -1;
   uint32_t cur_b0 = 0, cur_b1 = 0;
 
-  // pipeline: when position i starts, its scores are in acc and the K operand
-  // of position i+1 in kn; once this tile's P is formed, QK(i+1) is issued into
-  // acc and K of position i+2 is fetched into kn (prefetches past the last
-  // position re-read the last tile: in bounds, unused)
+  // pipeline: when position i starts, its scores are in acc, the K operand
+  // of position i+1 in kn and its own V^T operand in va; once this tile's P
+  // is formed, QK(i+1) is issued into acc and K of position i+2 is fetched
+  // into kn; once its P V product is issued, V^T of position i+1 is fetched
+  // into va (prefetches past the last position re-read the last tile: in
+  // bounds, unused)
   auto next_blob = [&](int i) { return (uint32_t)(tile_at(min(i, cnt - 1)) * BLOB); };
   KOps<D> kn;
   v16f acc[2];
+  v4i va[ND];
+  uint32_t vsw[NW];
+  auto load_v = [&](uint32_t blob) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
+    load_scales<D>(vsw, c.blobs, c.vsoff, blob);
+  };
+  // (issued in the loop's own order, K(i+1) before V(i), so the waits the
+  // compiler places at the loop head count only the loads they need)
   load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
   qk<D>(acc, kn, c.qa, c.qs);
   load_k<D>(kn, c.blobs, next_blob(1), c.koff, c.ksoff, hh);
+  load_v(next_blob(0));
 
   for (int i = 0; i < cnt && !gave_up; ++i) {
     const int t = tile_at(i);
@@ -533,47 +575,46 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       st.lam = 0.0f;
     }
     if (!TAIL && i == kReplay) mo_ref = st.mo;
-    const uint32_t blob = (uint32_t)(t * BLOB);
-    // V^T operand and scales of this tile (used at its end)
-    v4i va[ND];
-    uint32_t vsw[NW];
-#pragma unroll
-    for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
-    load_scales<D>(vsw, c.blobs, c.vsoff, blob);
 
     const bool vis0 = t <= c.d0, vis1 = t <= c.d1;
     mask_scores<D>(acc, g, c, t, hh);
-    float gown, goth;
-    tile_maxima(acc, gown, goth);
-    const float cmax = vmax(gown, goth);
+    float b0, b1;
+    group_maxima(acc, b0, b1);
+    const float cmax = vmax(b0, b1);
 
-    // ---- lazy maximum (integer frame)
-    const bool fire = cmax > st.mf + tau;  // never for a row without a visible key here
-    const float mcf = fire ? ceilf(cmax) : st.mf;
-
-    // re-base the state to m_o = max(m, mc - H), a lower bound of every later
-    // frame, when the frame has run too far ahead (all lanes; exact powers of two)
-    if (__ballot(mcf - (float)st.mo > kFrameGuard) != 0ull) {
-      if (tail && !replay) gave_up = true;
-      const int mo_new = (int)vmax(st.mf, mcf - Hf);
-      const int sh = st.mo - mo_new;
+    // ---- lazy maximum (integer frame): the frame moves only where the tile
+    // maximum exceeds it by more than tau (never for a row without a visible
+    // key here), which after the first tiles is rare
+    float mcf = st.mf;
+    if (__ballot(cmax > st.mf + tau) != 0ull) {
+      if (cmax > st.mf + tau) mcf = ceilf(cmax);
+      // re-base the state to m_o = max(m, mc - H), a lower bound of every
+      // later frame, when the frame has run too far ahead (all lanes; exact
+      // powers of two).  Only a moving frame can need it: after every tile
+      // m <= mc <= m_o + kFrameGuard.
+      if (__ballot(mcf - (float)st.mo > kFrameGuard) != 0ull) {
+        if (tail && !replay) gave_up = true;
+        const int mo_new = (int)vmax(st.mf, mcf - Hf);
+        const int sh = st.mo - mo_new;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+        for (int db = 0; db < ND; ++db)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) st.o[db][j] = ldexpf(st.o[db][j], sh);
-      st.lsum = ldexpf(st.lsum, sh);
-      st.lam = ldexpf(st.lam, sh);
-      st.mo = mo_new;
+          for (int j = 0; j < 16; ++j) st.o[db][j] = ldexpf(st.o[db][j], sh);
+        st.lsum = ldexpf(st.lsum, sh);
+        st.lam = ldexpf(st.lam, sh);
+        st.mo = mo_new;
+      }
     }
 
     // ---- step 2: the conversion divisor 2^X of each 32-key group,
     // X = E + m = max(ceil(c_g - log2 6), m - 127)
     const float lo = mcf - 127.0f;
-    const float xof = vmax(ceilf(gown - kLog2_6), lo);
-    const float xtf = vmax(ceilf(goth - kLog2_6), lo);
-    const v4i pb = p_operand(acc, xof, xtf, hh);
-    // E8M0 byte of this lane's 32-key group in the state's frame
-    const int pscale = (int)xof - st.mo + 127;
+    const float x0 = vmax(ceilf(b0 - kLog2_6), lo);
+    const float x1 = vmax(ceilf(b1 - kLog2_6), lo);
+    const v4i pb = p_operand(acc, x0, x1);
+    // E8M0 byte of this lane's 32-key group (the B operand's K block) in the
+    // state's frame
+    const int pscale = (int)(hh ? x1 : x0) - st.mo + 127;
 
     // ---- step 3: l_t as an MFMA of the quantised P itself (state's frame)
     const v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
@@ -585,12 +626,13 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     load_k<D>(kn, c.blobs, next_blob(i + 2), c.koff, c.ksoff, hh);
     const float ell = ones_acc[0];
 
-    // ---- step 4: the hot test (lambda includes this tile)
+    // ---- step 4: the hot test (lambda includes this tile); a row's scalars
+    // are the same in both lane halves, so the low 32 ballot bits are the rows
     st.lam += ell;
-    if (!TAIL && pub_out && i >= kReplay && hh == 0) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
+    if (!TAIL && pub_out && i >= kReplay) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
     float lam_b = lam_lo;
     if (TAIL && pub_in && !replay) lam_b = vmax(lam_b, pub_in[n]);
-    const unsigned long long hb = __ballot(ell > eps * (lam_b + st.lam) && hh == 0);
+    const unsigned long long hb = __ballot(ell > eps * (lam_b + st.lam));
     bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
     bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
     if (tail && !replay && eps != 0.0f && (hot0 || hot1)) {
@@ -615,24 +657,33 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
       }
       hot0 = hot1 = false;
     }
-    const unsigned long long hot_lanes = (hot0 ? kGroup0 : 0ull) | (hot1 ? ~kGroup0 : 0ull);
-    const bool my_hot = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
-
     // ---- frame update: cold -> mc; hot -> max(m, mc - H), which is m unless
     // the lazy test fired
-    st.mf = my_hot ? vmax(st.mf, mcf - Hf) : mcf;
+    if (hot0 || hot1) {
+      const unsigned long long hot_lanes = (hot0 ? kGroup0 : 0ull) | (hot1 ? ~kGroup0 : 0ull);
+      const bool my_hot = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
+      st.mf = my_hot ? vmax(st.mf, mcf - Hf) : mcf;
+    } else {
+      st.mf = mcf;
+    }
 
-    // ---- step 5: cold tiles accumulate P V in FP4 (not while replaying)
-    const bool cold0 = !replay && vis0 && !hot0, cold1 = !replay && vis1 && !hot1;
-    if (cold0 || cold1) {
-      const unsigned long long cold_lanes = (cold0 ? kGroup0 : 0ull) | (cold1 ? ~kGroup0 : 0ull);
-      const bool keep = __builtin_amdgcn_inverse_ballot_w64(cold_lanes);
-      const v4i pz = keep ? pb : v4i{0, 0, 0, 0};
+    // ---- step 5: cold tiles accumulate P V in FP4 (not while replaying).  A
+    // group that does not see this tile has all scores masked, so its P and
+    // l_t are exact zeros: only a hot group's rows need taking out.
+    if (!replay && !(hot0 && hot1)) {
+      v4i pz = pb;
+      float ez = ell;
+      if (hot0 || hot1) {
+        const bool keep = __builtin_amdgcn_inverse_ballot_w64(hot0 ? ~kGroup0 : kGroup0);
+        pz = keep ? pb : v4i{0, 0, 0, 0};
+        ez = keep ? ell : 0.0f;
+      }
 #pragma unroll
       for (int db = 0; db < ND; ++db)
         st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
-      st.lsum = keep ? st.lsum + ell : st.lsum;
+      st.lsum += ez;
     }
+    load_v(next_blob(i + 1));
 
     // ---- hot bits: one log byte per tile, or whole words (visited in
     // descending order after tile 0)
@@ -745,13 +796,13 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       load_k<D>(k, c.blobs, blob, c.koff, c.ksoff, hh);
       qk<D>(acc, k, c.qa, c.qs);
       mask_scores<D>(acc, g, c, t, hh);
-      float gown, goth;
-      tile_maxima(acc, gown, goth);
+      float b0, b1;
+      group_maxima(acc, b0, b1);
       const float lo = mcf - 127.0f;
-      const float xof = vmax(ceilf(gown - kLog2_6), lo);
-      const float xtf = vmax(ceilf(goth - kLog2_6), lo);
-      const v4i pb = p_operand(acc, xof, xtf, hh);
-      const int pscale = (int)xof - st.mo + 127;
+      const float x0 = vmax(ceilf(b0 - kLog2_6), lo);
+      const float x1 = vmax(ceilf(b1 - kLog2_6), lo);
+      const v4i pb = p_operand(acc, x0, x1);
+      const int pscale = (int)(hh ? x1 : x0) - st.mo + 127;
       const unsigned long long hot_lanes = (f0 ? kGroup0 : 0ull) | (f1 ? ~kGroup0 : 0ull);
       const bool keep = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
       const int neg = (int)0x88888888u;
@@ -781,133 +832,220 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
   }
 }
 
-// One wave per unit, or, with a split workspace, two: a unit's head and tail
-// waves sit in one work group (waves numbered (unit, role)).  The head hands
-// its running lambda to the tail through LDS while both walk, and its final
-// state at its end; the tail finishes the unit.  Units are numbered (batch,
-// kv-head, 32-row block, head), so the waves of a work group, and the groups
-// of an XCD, stream the same tiles.
+// A wave's state in the hand-off area of a unit's workspace block (after its
+// records): o in lane order (float4 chunk q of block db at [4 db + q]), then
+// mf, mo (its bits), lambda and l per lane, then the four partial hot words
+// (word k from lane k).  The tail of the triple schedule parks its state
+// there while it walks the next unit's tail; a tail that gave up leaves its
+// head's state there for the re-walk kernel.  Each lane reads back only
+// what it wrote.
+template <int D>
+__device__ __forceinline__ float* handoff_of(uint8_t* split, int unit, int cap) {
+  return reinterpret_cast<float*>(split + (size_t)unit * cand_stride(cap, D) + cand_bytes(cap));
+}
+
+template <int D>
+__device__ __forceinline__ void save_state(float* dst, const St<D>& st, const Words& wd, int lane) {
+#pragma unroll
+  for (int db = 0; db < Tile<D>::ND; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<v4f*>(dst)[(4 * db + q) * 64 + lane] =
+          v4f{st.o[db][4 * q], st.o[db][4 * q + 1], st.o[db][4 * q + 2], st.o[db][4 * q + 3]};
+  dst[32 * D + lane] = st.mf;
+  dst[32 * D + 64 + lane] = __int_as_float(st.mo);
+  dst[32 * D + 128 + lane] = st.lam;
+  dst[32 * D + 192 + lane] = st.lsum;
+  const uint32_t w = lane == 0 ? wd.p00 : lane == 1 ? wd.p01 : lane == 2 ? wd.p10 : wd.p11;
+  if (lane < 4) reinterpret_cast<uint32_t*>(dst)[32 * D + 256 + lane] = w;
+}
+
+template <int D>
+__device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& wd, int lane) {
+#pragma unroll
+  for (int db = 0; db < Tile<D>::ND; ++db)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v4f x = reinterpret_cast<const v4f*>(src)[(4 * db + q) * 64 + lane];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.o[db][4 * q + e] = x[e];
+    }
+  st.mf = src[32 * D + lane];
+  st.mo = __float_as_int(src[32 * D + 64 + lane]);
+  st.lam = src[32 * D + 128 + lane];
+  st.lsum = src[32 * D + 192 + lane];
+  const int w = lane < 4 ? (int)reinterpret_cast<const uint32_t*>(src)[32 * D + 256 + lane] : 0;
+  wd.p00 = (uint32_t)__builtin_amdgcn_readlane(w, 0);
+  wd.p01 = (uint32_t)__builtin_amdgcn_readlane(w, 1);
+  wd.p10 = (uint32_t)__builtin_amdgcn_readlane(w, 2);
+  wd.p11 = (uint32_t)__builtin_amdgcn_readlane(w, 3);
+}
+
+// Units run one wave each, or, with a split workspace, as a head and a tail
+// walk (see cut_point).  With the pair schedule a work group holds two units,
+// its waves numbered (unit, role); with the triple schedule it holds three,
+// waves 0-2 their heads and wave 3 the tail of each, one after the other.  A
+// head hands its running lambda to its tail through LDS while both walk, and
+// its final state at its end; the tail finishes the unit.  Units are numbered
+// (batch, kv-head, 32-row block, head), so the waves of a work group, and the
+// groups of an XCD, stream the same tiles.
 template <int D, bool LOG>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
-    int nwaves) {
+    int sched, int nunits) {
   constexpr int ND = Tile<D>::ND;
-  // per head/tail pair of the group: the head's running lambda and final state
-  __shared__ float pub[kWaves / 2][32];
-  __shared__ HeadState<D> hs[kWaves / 2];
+  constexpr int NS = kSlots<D>;
+  // per head of the group: its running lambda and final state
+  __shared__ float pub[NS][32];
+  __shared__ HeadState<D> hs[NS];
   __shared__ uint8_t vlog_sh[LOG ? kWaves : 1][LOG ? kLogTiles : 1];  // verdict logs
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   // the wave index is wave-uniform: keep everything derived from it in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int slot = wave >> 1;
-  if (lane < 32) pub[slot][lane] = 0.0f;
-  if (lane == 0) hs[slot].done = 0;
-  __syncthreads();
-  int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
-  if (w >= nwaves) return;
-
-  const int nq32 = g.NqP / 32;
-  int role = kWhole;
-  if (split) {
-    role = (w & 1) ? kTail : kHead;
-    w >>= 1;
-  }
-  UnitId id;
-  id.gi = w % g.G; w /= g.G;
-  id.qb = w % nq32; w /= nq32;
-  id.hk = w % g.Hkv;
-  id.b = w / g.Hkv;
-
-  Ctx<D> c;
-  make_ctx<D>(c, g, f, out, id, lane);
-  const int npos = c.dW + 1;
-  if (role != kWhole && npos < kMinSplit) {
-    if (role == kTail) return;
-    role = kWhole;
-  }
-  const int h = split_point(npos);  // head positions [0, h), tail [h, npos)
-  const int wb = role == kWhole ? -1 : shared_word(c.dW - h + 1);
-
-  St<D> st;
-  init_state<D>(st, c.row_ok);
-  Words wd = {wb, 0u, 0u, 0u, 0u};
-  if (role != kTail) zero_above<D>(g, c, lane);
-  int nrep = 0, p0 = 0, cnt = npos;
-  if (role == kHead) cnt = h;
-  if (role == kTail) {
-    nrep = kReplay;
-    p0 = h;
-    cnt = kReplay + npos - h;
-  }
-  const Cand cr = cand_of(role == kTail ? split : f.kv_blob, role == kTail ? unit_index(g, id) : 0,
-                         role == kTail ? cap : 0, D);
-  volatile lds_float* pin = role == kTail ? (volatile lds_float*)pub[slot] : nullptr;
-  volatile lds_float* pout = role == kHead ? (volatile lds_float*)pub[slot] : nullptr;
-  const float Hf = (float)hoff;
-  auto wait_head = [&]() {
-    while (__hip_atomic_load(&hs[slot].done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
-      __builtin_amdgcn_s_sleep(2);
-  };
-  // the tail's walk is a copy of its own: the record keeping stays out of the
-  // loop the head and whole units run
-  const int outcome =
-      role == kTail ? walk<D, LOG, true>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin,
-                                         pout, (lds_u8*)vlog_sh[LOG ? wave : 0], lane)
-                    : walk<D, LOG, false>(g, c, st, wd, nrep, p0, cnt, eps, tau, Hf, cr, cap, pin,
-                                          pout, (lds_u8*)vlog_sh[LOG ? wave : 0], lane);
-
-  if (role == kHead) {
+  if (wave == 0) {
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        hs[slot].o[4 * db + q][lane] = v4f{st.o[db][4 * q], st.o[db][4 * q + 1],
-                                           st.o[db][4 * q + 2], st.o[db][4 * q + 3]};
-    hs[slot].sc[0][lane] = st.mf;
-    hs[slot].sc[1][lane] = __int_as_float(st.mo);
-    hs[slot].sc[2][lane] = st.lam;
-    hs[slot].sc[3][lane] = st.lsum;
-    if (lane == 0) {
-      hs[slot].words[0] = wd.p00;
-      hs[slot].words[1] = wd.p01;
-      hs[slot].words[2] = wd.p10;
-      hs[slot].words[3] = wd.p11;
-      __hip_atomic_store(&hs[slot].done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    for (int s = 0; s < NS; ++s) {
+      if (lane < 32) pub[s][lane] = 0.0f;
+      if (lane == 0) hs[s].done = 0;
     }
-    return;
   }
-  if (role == kTail) {
-    wait_head();
-    if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)outcome, cr.r, 0u, 0u, 0);
-    if (outcome < 0) {
-      // gave up: leave the head's state for the re-walk kernel
-      float* dst = reinterpret_cast<float*>(split + (size_t)unit_index(g, id) * cand_stride(cap, D) +
-                                            cand_bytes(cap));
-#pragma unroll 2
-      for (int k = 0; k < ND * 4; ++k) reinterpret_cast<v4f*>(dst)[k * 64 + lane] = hs[slot].o[k][lane];
+  __syncthreads();
+  if (sched == kSchedTriples && NS < 3) return;  // never launched so (too little LDS)
+  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  // the wave's role, its (first) unit, the number of units it walks and the
+  // LDS slot of the first
+  int role, u0, nu = 1, slot;
+  if (sched == kSchedTriples) {
+    role = wave < 3 ? kHead : kTail;
+    slot = wave < 3 ? wave : 0;
+    u0 = blk * 3 + slot;
+    if (wave == 3) nu = min(3, nunits - u0);
+  } else if (sched == kSchedPairs) {
+    role = (wave & 1) ? kTail : kHead;
+    slot = wave >> 1;
+    u0 = blk * 2 + slot;
+  } else {
+    role = kWhole;
+    slot = 0;
+    u0 = blk * kWaves + wave;
+  }
+  if (u0 >= nunits) return;
+  lds_u8* vlog = (lds_u8*)vlog_sh[LOG ? wave : 0];
+  const float Hf = (float)hoff;
+
+  if (role != kTail) {
+    Ctx<D> c;
+    make_ctx<D>(c, g, f, out, unit_id(g, u0), lane);
+    const int npos = c.dW + 1;
+    if (npos < kMinSplit) role = kWhole;  // nothing to cut: its tail wave skips it
+    const int h = cut_point(npos, sched);  // head positions [0, h), tail [h, npos)
+    St<D> st;
+    init_state<D>(st, c.row_ok);
+    Words wd = {role == kWhole ? -1 : shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
+    zero_above<D>(g, c, lane);
+    walk<D, LOG, false>(g, c, st, wd, 0, 0, role == kWhole ? npos : h, eps, tau, Hf,
+                        cand_of(f.kv_blob, 0, 0, D), 0, nullptr,
+                        role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane);
+    if (role == kHead) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) dst[32 * D + 64 * k + lane] = hs[slot].sc[k][lane];
-      if (lane < 4) reinterpret_cast<uint32_t*>(dst)[32 * D + 256 + lane] = hs[slot].words[lane];
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hs[slot].o[4 * db + q][lane] = v4f{st.o[db][4 * q], st.o[db][4 * q + 1],
+                                             st.o[db][4 * q + 2], st.o[db][4 * q + 3]};
+      hs[slot].sc[0][lane] = st.mf;
+      hs[slot].sc[1][lane] = __int_as_float(st.mo);
+      hs[slot].sc[2][lane] = st.lam;
+      hs[slot].sc[3][lane] = st.lsum;
+      if (lane == 0) {
+        hs[slot].words[0] = wd.p00;
+        hs[slot].words[1] = wd.p01;
+        hs[slot].words[2] = wd.p10;
+        hs[slot].words[3] = wd.p11;
+        __hip_atomic_store(&hs[slot].done, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
       return;
     }
-    const float a_mf = hs[slot].sc[0][lane];
-    const int a_mo = __float_as_int(hs[slot].sc[1][lane]);
-    const float a_lam = hs[slot].sc[2][lane];
-    const float a_lsum = hs[slot].sc[3][lane];
+    // a whole unit: word 0 (which also holds tile 0) and the state
+    if (lane == 0) {
+      c.bits0[0] = wd.p00;
+      if (c.has_g1) c.bits1[0] = wd.p01;
+    }
+    store_state<D>(g, c, out, st, lane);
+    return;
+  }
+
+  // A tail wave: walk the tails of units u0 .. u0 + nu - 1 (one loop, so one
+  // inlined copy of the walk), keeping each outcome (records kept; -1 gave
+  // up; -2 no tail: a short visit order its head wave walked whole).  Each
+  // walked state waits in its unit's hand-off area until the heads are done,
+  // so no state lives across the loops.
+  uint32_t outcomes = 0u;  // outcome + 2 in 10 bits per unit
+#pragma nounroll
+  for (int k = 0; k < nu; ++k) {
+    const int u = u0 + k;
+    Ctx<D> c;
+    make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
+    const int npos = c.dW + 1;
+    int oc = -2;
+    if (npos >= kMinSplit) {
+      const int h = cut_point(npos, sched);
+      St<D> st;
+      init_state<D>(st, c.row_ok);
+      Words wd = {shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
+      oc = walk<D, LOG, true>(g, c, st, wd, kReplay, h, kReplay + npos - h, eps, tau, Hf,
+                              cand_of(split, u, cap, D), cap,
+                              (volatile lds_float*)pub[slot + k], nullptr, vlog, lane);
+      if (oc >= 0) save_state<D>(handoff_of<D>(split, u, cap), st, wd, lane);
+    }
+    outcomes |= (uint32_t)(oc + 2) << (10 * k);
+  }
+  // Finish each unit once its head is done, the last walked first.
+#pragma nounroll
+  for (int k = nu - 1; k >= 0; --k) {
+    const int oc = (int)((outcomes >> (10 * k)) & 1023u) - 2;
+    if (oc == -2) continue;
+    const int u = u0 + k;
+    Ctx<D> c;
+    make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
+    const int wb = shared_word(c.dW - cut_point(c.dW + 1, sched) + 1);
+    float* ho = handoff_of<D>(split, u, cap);
+    HeadState<D>& H = hs[slot + k];
+    while (__hip_atomic_load(&H.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+      __builtin_amdgcn_s_sleep(2);
+    const Cand cr = cand_of(split, u, cap, D);
+    if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)oc, cr.r, 0u, 0u, 0);
+    if (oc < 0) {
+      // gave up: leave the head's state for the re-walk kernel
+#pragma unroll 2
+      for (int q = 0; q < ND * 4; ++q) reinterpret_cast<v4f*>(ho)[q * 64 + lane] = H.o[q][lane];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ho[32 * D + 64 * q + lane] = H.sc[q][lane];
+      if (lane < 4) reinterpret_cast<uint32_t*>(ho)[32 * D + 256 + lane] = H.words[lane];
+      continue;
+    }
+    St<D> st;
+    Words wd;
+    load_state<D>(ho, st, wd, lane);
+    wd.wb = wb;
+    const float a_mf = H.sc[0][lane];
+    const int a_mo = __float_as_int(H.sc[1][lane]);
+    const float a_lam = H.sc[2][lane];
+    const float a_lsum = H.sc[3][lane];
     // the head's lambda in the tail's state frame (the tail never re-based)
-    settle<D>(g, c, st, wd, cr, outcome, ldexpf(a_lam, a_mo - st.mo), eps, lane);
+    settle<D>(g, c, st, wd, cr, oc, ldexpf(a_lam, a_mo - st.mo), eps, lane);
     // the shared words: the head's part and the tail's
     if (lane == 0) {
-      c.bits0[0] = hs[slot].words[0] | wd.p00;
-      if (c.has_g1) c.bits1[0] = hs[slot].words[1] | wd.p01;
+      c.bits0[0] = H.words[0] | wd.p00;
+      if (c.has_g1) c.bits1[0] = H.words[1] | wd.p01;
       if (wb > 0) {
-        c.bits0[wb] = hs[slot].words[2] | wd.p10;
-        if (c.has_g1) c.bits1[wb] = hs[slot].words[3] | wd.p11;
+        c.bits0[wb] = H.words[2] | wd.p10;
+        if (c.has_g1) c.bits1[wb] = H.words[3] | wd.p11;
       }
     }
     // merge: the larger frame, each state scaled into it by an exact power of two
-    if (!c.row_ok) return;
+    if (!c.row_ok) continue;
     const size_t r = c.bhq * g.Nq + c.row;
     const int m = (int)vmax(a_mf, st.mf);
     const int sa = a_mo - m, sb = st.mo - m;
@@ -921,21 +1059,14 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const v4f xa = hs[slot].o[4 * db + q][lane];
+        const v4f xa = H.o[4 * db + q][lane];
         v4f x;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           x[e] = (ldexpf(xa[e], sa) + ldexpf(st.o[db][4 * q + e], sb)) * c.g_v;
         *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
       }
-    return;
   }
-  // a whole unit: word 0 (which also holds tile 0) and the state
-  if (lane == 0) {
-    c.bits0[0] = wd.p00;
-    if (c.has_g1) c.bits1[0] = wd.p01;
-  }
-  store_state<D>(g, c, out, st, lane);
 }
 
 // The re-walk of units whose tail gave up (record full, or a re-base of its
@@ -944,7 +1075,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
 template <int D, bool LOG>
 __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float eps, float tau,
                                                      int hoff, Pass1Out out, uint8_t* split,
-                                                     int cap) {
+                                                     int cap, int sched) {
   constexpr int ND = Tile<D>::ND;
   const int lane = threadIdx.x;
   const UnitId id = unit_id(g, blockIdx.x);
@@ -954,7 +1085,7 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   const int npos = c.dW + 1;
   if (npos < kMinSplit) return;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
-  const int h = split_point(npos);
+  const int h = cut_point(npos, sched);
   const int wb = shared_word(c.dW - h + 1);
   const float* src = reinterpret_cast<const float*>(base + cand_bytes(cap));
   St<D> st;
@@ -987,23 +1118,32 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   store_state<D>(g, c, out, st, lane);
 }
 
-// Two waves per unit pay off while there are at most about three quarters as
-// many units as wave slots, and only for visit orders long enough to cut.
-bool split_pays(const Geom& g) {
+// The schedule a launch with a workspace runs: the caller's, else two waves
+// per unit while those fit the GPU's wave slots at once, four waves per three
+// units while those do, else one wave per unit (then there is no workspace).
+// Visit orders shorter than kMinSplit positions leave nothing to cut, and the
+// triple schedule needs three head states in LDS (D <= 256).
+int pass1_sched(const Geom& g) {
   const long units = (long)g.B * g.Hkv * (g.NqP / 32) * g.G;
   const long slots = 1024L * (g.D >= 256 ? 1 : 2);
-  return units > 0 && 4 * units <= 3 * slots && g.NT >= kMinSplit;
+  if (units == 0 || g.NT < kMinSplit) return kSchedWhole;
+  int s = g.sched;
+  if (s != kSchedWhole && s != kSchedPairs && s != kSchedTriples)
+    s = 2 * units <= slots ? kSchedPairs : (4 * units <= 3 * slots ? kSchedTriples : kSchedWhole);
+  if (s == kSchedTriples && g.D > 256) s = kSchedPairs;
+  return s;
 }
 
 // Records per unit: every tail position of the longest visit order, at most
 // kCandCap.
-int cand_cap(const Geom& g) { return min(kCandCap, g.NT - split_point(g.NT)); }
+int cand_cap(const Geom& g, int sched) { return min(kCandCap, g.NT - cut_point(g.NT, sched)); }
 
 }  // namespace
 
 size_t pass1_ws_bytes(const Geom& g) {
-  if (!split_pays(g)) return 0;
-  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g), g.D);
+  const int s = pass1_sched(g);
+  if (s == kSchedWhole) return 0;
+  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g, s), g.D);
 }
 
 namespace {
@@ -1013,26 +1153,27 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                const Pass1Out& o, void* ws, hipStream_t s) {
   const int nunits = g.B * g.Hkv * (g.NqP / 32) * g.G;
   if (nunits == 0) return hipSuccess;
-  uint8_t* split = (ws && split_pays(g)) ? static_cast<uint8_t*>(ws) : nullptr;
-  const int nwaves = split ? 2 * nunits : nunits;
-  const int nblocks = (nwaves + kWaves - 1) / kWaves;
-  const int cap = split ? cand_cap(g) : 0;
+  const int sched = ws ? pass1_sched(g) : kSchedWhole;
+  uint8_t* split = sched != kSchedWhole ? static_cast<uint8_t*>(ws) : nullptr;
+  const int per = sched == kSchedTriples ? 3 : (sched == kSchedPairs ? 2 : kWaves);
+  const int nblocks = (nunits + per - 1) / per;
+  const int cap = split ? cand_cap(g, sched) : 0;
   const bool log = g.NT <= kLogTiles;
   if (log)
     hipLaunchKernelGGL((k_pass1<D, true>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
-                       hoff, o, split, cap, nwaves);
+                       hoff, o, split, cap, sched, nunits);
   else
     hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
-                       hoff, o, split, cap, nwaves);
+                       hoff, o, split, cap, sched, nunits);
   if (split) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (log)
       hipLaunchKernelGGL((k_pass1_rewalk<D, true>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
-                         hoff, o, split, cap);
+                         hoff, o, split, cap, sched);
     else
       hipLaunchKernelGGL((k_pass1_rewalk<D, false>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
-                         hoff, o, split, cap);
+                         hoff, o, split, cap, sched);
   }
   return hipGetLastError();
 }

@@ -90,17 +90,40 @@ def unpack_bits(p, words: np.ndarray) -> np.ndarray:
     return bits.reshape(p.B, p.Hq, NG, W * 32)[..., :NT].astype(bool)
 
 
+def pass1_schedule(p) -> int:
+    """The pass-1 schedule a launch with a workspace runs (the library's
+    choice for SCHED_AUTO, restated for the tests)."""
+    units = p.B * p.Hq * (-(-p.Nq // 32))
+    slots = 1024 * (1 if p.D >= 256 else 2)
+    if units == 0 or -(-p.Nkv // 64) < 64:
+        return apa.SCHED_WHOLE
+    s = p.pass1_schedule
+    if s not in (apa.SCHED_WHOLE, apa.SCHED_PAIRS, apa.SCHED_TRIPLES):
+        s = (apa.SCHED_PAIRS if 2 * units <= slots else
+             apa.SCHED_TRIPLES if 4 * units <= 3 * slots else apa.SCHED_WHOLE)
+    if s == apa.SCHED_TRIPLES and p.D > 256:
+        s = apa.SCHED_PAIRS
+    return s
+
+
+def cut_point(npos: int, sched: int) -> int:
+    """First tail position of a visit order of npos positions."""
+    if sched == apa.SCHED_TRIPLES:
+        return 3 * (npos + 32) // 4 + npos // 32
+    return (npos + 32) // 2 + npos // 64
+
+
 # Pass-1 workspace of a split problem (the layout of pass1.hip's Cand): per
 # 32-row block the tail's outcome (records kept, or -1: it gave up and the
 # head's state walks the tail again) in the first 4 bytes, then `cap` records
 # of 292 bytes, cap = min(512, the longest tail), rounded up to 256 bytes,
-# then the head's hand-off state (128 D + 1040 bytes, rounded up to 256).
+# then the hand-off state (128 D + 1040 bytes, rounded up to 256).
 def tail_outcomes(p, ws) -> np.ndarray:
     """Outcome of every block whose visit order was cut: number of undecided
     tail tiles decided at the end, or -1 where the tail positions were walked
     again from the head's state."""
     G, NT, nq32 = p.Hq // p.Hkv, -(-p.Nkv // 64), -(-p.Nq // 32)
-    cap = min(512, NT - ((NT + 32) // 2 + NT // 64))
+    cap = min(512, NT - cut_point(NT, pass1_schedule(p)))
     stride = (cap * 292 + 16 + 255) // 256 * 256 + (128 * p.D + 1040 + 255) // 256 * 256
     raw = ws.cpu().numpy()
     out = []

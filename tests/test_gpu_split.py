@@ -1,5 +1,7 @@
 """Pass 1 with its workspace: each long visit order runs as a head and a tail
-wave of one work group, the tail finishing the unit.  Checked against the oracle (same bars as the other
+walk in one work group, the tail finishing the unit; with the pair schedule
+every 32-row block has its own tail wave, with the triple schedule one wave
+walks the tails of three blocks one after the other.  Checked against the oracle (same bars as the other
 parity tests) and against the one-wave walk of the same inputs, with the
 tail's outcome per 32-row block read back from the workspace to show which
 way the tail finished: records decided (the lower bound of lambda left some
@@ -9,7 +11,7 @@ frame)."""
 import numpy as np
 import pytest
 
-from gpu_util import problem_for, run_gpu
+from gpu_util import pass1_schedule, problem_for, run_gpu
 from mixed_precision_long_amd import apa
 from mixed_precision_long_amd.inputs import make_inputs, small_workload
 from oracle import oracle as O
@@ -29,9 +31,13 @@ def lift_key(w, Q, K, key, nats):
     return K
 
 
-def run_case(w, eps, Q, K, V):
-    p = problem_for(w)
+SCHEDS = [apa.SCHED_PAIRS, apa.SCHED_TRIPLES]
+
+
+def run_case(w, eps, Q, K, V, sched):
+    p = problem_for(w, sched=sched)
     assert apa.workspace_bytes(p, apa.CALL_PASS1) > 0, "this shape should run split"
+    assert pass1_schedule(p) == sched
     po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, causal=w.causal, scale=w.scale, eps=eps)
     prep = O.quantize(po, Q, K, V)
     r = O.run(po, Q, K, V, prep)
@@ -55,51 +61,56 @@ def run_case(w, eps, Q, K, V):
 
 # gauss inputs: every tile carries about the same mass, so lambda grows
 # linearly and the tail's bounded test passes for its first tiles
-def test_split_decides_undecided_tail_tiles():
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_split_decides_undecided_tail_tiles(sched):
     w = small_workload(1, 2, 1, 64, 16384, 64, mode="gauss", seed=31)
     Q, K, V = make_inputs(w)
-    g = run_case(w, 0.02, Q, K, V)
+    g = run_case(w, 0.02, Q, K, V, sched)
     assert (g["tail"] > 0).any(), g["tail"]
     assert (g["tail"] >= 0).all(), g["tail"]
 
 
-def test_split_full_record_walks_the_tail():
-    # about 541 tail positions per block, nearly all undecided: more than the 512
-    # records
-    w = small_workload(1, 2, 1, 64, 73728, 64, mode="gauss", seed=32)
+@pytest.mark.parametrize("sched,nkv", [(apa.SCHED_PAIRS, 73728), (apa.SCHED_TRIPLES, 163840)])
+def test_split_full_record_walks_the_tail(sched, nkv):
+    # about 541 (pairs) or 536 (triples) tail positions per block, nearly all
+    # undecided: more than the 512 records
+    w = small_workload(1, 2, 1, 64, nkv, 64, mode="gauss", seed=32)
     Q, K, V = make_inputs(w)
-    g = run_case(w, 1e-4, Q, K, V)
+    g = run_case(w, 1e-4, Q, K, V, sched)
     assert (g["tail"] == -1).all(), g["tail"]
 
 
-def test_split_rebase_in_tail_walks_the_tail():
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_split_rebase_in_tail_walks_the_tail(sched):
     w = small_workload(1, 2, 1, 64, 16384, 64, seed=33)
     Q, K, V = make_inputs(w)
-    K = lift_key(w, Q, K, 50 * 64 + 7, 70.0)  # tile 50: in every block's tail segment
-    g = run_case(w, 0.005, Q, K, V)
+    K = lift_key(w, Q, K, 20 * 64 + 7, 70.0)  # tile 20: in every block's tail segment
+    g = run_case(w, 0.005, Q, K, V, sched)
     assert (g["tail"] == -1).all(), g["tail"]
 
 
-def test_split_hot_tail_tile_leaves_the_state():
-    """A key lifted by 8 nats in the middle of the tail segment makes its tile
-    hot for every row group: the tail records it undecided, accumulates it as
-    cold, and at its end finds it hot and takes its P V back out."""
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_split_hot_tail_tile_leaves_the_state(sched):
+    """A key lifted by 8 nats in the tail segment makes its tile hot for every
+    row group: the tail records it undecided, accumulates it as cold, and at
+    its end finds it hot and takes its P V back out."""
     w = small_workload(1, 2, 1, 64, 16384, 64, seed=37)
     Q, K, V = make_inputs(w)
-    K = lift_key(w, Q, K, 50 * 64 + 7, 8.0)
-    g = run_case(w, 0.005, Q, K, V)
+    K = lift_key(w, Q, K, 20 * 64 + 7, 8.0)
+    g = run_case(w, 0.005, Q, K, V, sched)
     assert (g["tail"] > 0).all(), g["tail"]
-    assert g["hot"][..., 50].all()
+    assert g["hot"][..., 20].all()
 
 
+@pytest.mark.parametrize("sched", SCHEDS)
 @pytest.mark.parametrize("case", [
     (2, 1, 32, 266240, 64, 0.005, 38, 1),   # 4160 key tiles: hot words kept in the tile loop
     (6, 2, 200, 9000, 128, 0.005, 34, 1),   # GQA 3, ragged rows and keys
     (4, 1, 96, 12000, 64, 0.01, 35, 0),     # non-causal
     (2, 1, 64, 8192, 256, 0.005, 36, 1),    # D = 256
 ])
-def test_split_path_inputs(case):
+def test_split_path_inputs(case, sched):
     Hq, Hkv, Nq, Nkv, D, eps, seed, causal = case
     w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed, causal=causal)
     Q, K, V = make_inputs(w)
-    run_case(w, eps, Q, K, V)
+    run_case(w, eps, Q, K, V, sched)
