@@ -288,11 +288,12 @@ struct St {
   v16f o[Tile<D>::ND];
 };
 
-// Rows past Nq never see a key and sit at frame 127 so every derived quantity
-// stays finite; mo starts far below any frame so that the first tile re-bases.
+// Rows past Nq never see a key and sit at frame 64 so every derived quantity
+// stays finite (and their P divisors inside the conversion's fast range); mo
+// starts far below any frame so that the first tile re-bases.
 template <int D>
 __device__ __forceinline__ void init_state(St<D>& st, bool row_ok) {
-  st.mf = row_ok ? -__builtin_inff() : 127.0f;
+  st.mf = row_ok ? -__builtin_inff() : 64.0f;
   st.mo = -(1 << 20);
   st.lam = 0.0f;
   st.lsum = 0.0f;
@@ -420,22 +421,29 @@ __device__ __forceinline__ void group_maxima(const v16f (&acc)[2], float& b0, fl
   b1 = __int_as_float(x1);
 }
 
+// Whether both P divisors 2^x0, 2^x1 of every lane are normal with room below
+// for the codes that matter: the fast form of the conversion.
+__device__ __forceinline__ bool divisors_fast(int x0, int x1) {
+  return __ballot((unsigned)(x0 + 124) > 244u || (unsigned)(x1 + 124) > 244u) == 0ull;
+}
+
 // Step 2: the FP4 codes of P for divisors 2^x0 (keys 0-31) and 2^x1 (keys
 // 32-63), rearranged into the MFMA operand layout (lanes < 32 carry keys 0-31,
-// lanes >= 32 keys 32-63).
-__device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float x0f, float x1f) {
-  const int x0 = (int)x0f, x1 = (int)x1f;
-  // fast path: both divisors normal with room below for the codes that matter
-  const bool odd = (unsigned)(x0 + 124) > 244u || (unsigned)(x1 + 124) > 244u;
+// lanes >= 32 keys 32-63).  fast: see divisors_fast.
+__device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], int x0, int x1, float x0f,
+                                         float x1f, bool fast) {
   unsigned pk[2][2];
-  if (__ballot(odd) == 0ull) {
+  if (fast) {
     const float sc0 = __int_as_float((x0 + 127) << 23), sc1 = __int_as_float((x1 + 127) << 23);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const float sc = kb ? sc1 : sc0;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        unsigned w = 0;
+        // every byte is written below: the starting value does not matter (a
+        // distinct non-volatile placeholder per word: no move, no barrier)
+        unsigned w;
+        asm("" : "=v"(w) : "n"(2 * kb + j));
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int i = 8 * j + 2 * p;
@@ -451,7 +459,8 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float x0f, float 
       const float sub = kb ? x1f : x0f;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        unsigned w = 0;
+        unsigned w;
+        asm("" : "=v"(w) : "n"(4 + 2 * kb + j));
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const int i = 8 * j + 2 * p;
@@ -461,10 +470,15 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], float x0f, float 
       }
     }
   }
-  int a0, b0, a1, b1;
-  swap_halves((int)pk[0][0], (int)pk[1][0], a0, b0);
-  swap_halves((int)pk[0][1], (int)pk[1][1], a1, b1);
-  return v4i{a0, a1, b0, b1};
+  v4i r = {(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1]};
+  int a, b;
+  swap_halves(r[0], r[2], a, b);
+  r[0] = a;
+  r[2] = b;
+  swap_halves(r[1], r[3], a, b);
+  r[1] = a;
+  r[3] = b;
+  return r;
 }
 
 // The hot words of a walk's positions [P0, P0 + np) from its verdict log
@@ -562,6 +576,10 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   };
   // (issued in the loop's own order, K(i+1) before V(i), so the waits the
   // compiler places at the loop head count only the loads they need)
+  // the all-ones operand of the row-sum MFMA, kept in registers (made opaque
+  // before any load is in flight)
+  v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
+  asm volatile("" : "+v"(ones));
   load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
   qk<D>(acc, kn, c.qa, c.qs);
   load_k<D>(kn, c.blobs, next_blob(1), c.koff, c.ksoff, hh);
@@ -611,13 +629,13 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     const float lo = mcf - 127.0f;
     const float x0 = vmax(ceilf(b0 - kLog2_6), lo);
     const float x1 = vmax(ceilf(b1 - kLog2_6), lo);
-    const v4i pb = p_operand(acc, x0, x1);
+    const int x0i = (int)x0, x1i = (int)x1;
+    const v4i pb = p_operand(acc, x0i, x1i, x0, x1, divisors_fast(x0i, x1i));
     // E8M0 byte of this lane's 32-key group (the B operand's K block) in the
     // state's frame
-    const int pscale = (int)(hh ? x1 : x0) - st.mo + 127;
+    const int pscale = (hh ? x1i : x0i) - st.mo + 127;
 
     // ---- step 3: l_t as an MFMA of the quantised P itself (state's frame)
-    const v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
     const v16f ones_acc = mfma4(ones, pb, v16f{}, kE8M0One, 0, pscale);
     // this tile's scores are consumed: the next tile's go to the matrix cores
     // behind the row sum and run during the vote and the P V product
@@ -630,9 +648,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     // are the same in both lane halves, so the low 32 ballot bits are the rows
     st.lam += ell;
     if (!TAIL && pub_out && i >= kReplay) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
-    float lam_b = lam_lo;
-    if (TAIL && pub_in && !replay) lam_b = vmax(lam_b, pub_in[n]);
-    const unsigned long long hb = __ballot(ell > eps * (lam_b + st.lam));
+    float lam_t = st.lam;  // the running mass the vote compares against
+    if (TAIL) lam_t = (pub_in && !replay ? vmax(lam_lo, pub_in[n]) : lam_lo) + st.lam;
+    const unsigned long long hb = __ballot(ell > eps * lam_t);
     bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
     bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
     if (tail && !replay && eps != 0.0f && (hot0 || hot1)) {
@@ -801,8 +819,9 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       const float lo = mcf - 127.0f;
       const float x0 = vmax(ceilf(b0 - kLog2_6), lo);
       const float x1 = vmax(ceilf(b1 - kLog2_6), lo);
-      const v4i pb = p_operand(acc, x0, x1);
-      const int pscale = (int)(hh ? x1 : x0) - st.mo + 127;
+      const int x0i = (int)x0, x1i = (int)x1;
+      const v4i pb = p_operand(acc, x0i, x1i, x0, x1, divisors_fast(x0i, x1i));
+      const int pscale = (hh ? x1i : x0i) - st.mo + 127;
       const unsigned long long hot_lanes = (f0 ? kGroup0 : 0ull) | (f1 ? ~kGroup0 : 0ull);
       const bool keep = __builtin_amdgcn_inverse_ballot_w64(hot_lanes);
       const int neg = (int)0x88888888u;
