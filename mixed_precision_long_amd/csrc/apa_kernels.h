@@ -34,8 +34,10 @@ struct QuantWs {
   float* kmax;    // [B*Hkv][NCH][D]
   float* vamax;   // [B*Hkv][NCH]
   float* qamax;   // [B*Hq][NQT]
+  unsigned* flags;  // [NKB + NQB] per statistics block: a non-finite input seen
   int nqt;        // ceil(Nq / 64)
   int nch;        // ceil(NT / 16)
+  int nflags;     // NKB + NQB
 };
 
 struct Pass1Out {

@@ -91,14 +91,18 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
   const int nqt = (p->Nq + 63) / 64;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t nflags = (p->Nkv > 0 ? nkv : 0) + (p->Nq > 0 ? (size_t)p->B * p->Hq * nqt : 0);
   const size_t a = take(nkv * p->D * 8), b = take(nkv * p->D * 4), c = take(nkv * p->D * 4),
-               d = take(nkv * 4), e = take((size_t)p->B * p->Hq * (nqt > 0 ? nqt : 1) * 4);
+               d = take(nkv * 4), e = take((size_t)p->B * p->Hq * (nqt > 0 ? nqt : 1) * 4),
+               fl = take((nflags > 0 ? nflags : 1) * 4);
   if (ws && base) {
     uint8_t* bb = (uint8_t*)base;
     ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
     ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e);
+    ws->flags = (unsigned*)(bb + fl);
     ws->nqt = nqt;
     ws->nch = nch;
+    ws->nflags = (int)nflags;
   }
   return o;
 }

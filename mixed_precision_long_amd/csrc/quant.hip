@@ -10,16 +10,15 @@
 //
 // HBM-bound work: K and V are read twice (statistics, then quantisation) and
 // Q once; every reduction has a fixed order, so results are deterministic.
+// The quantisation pass takes Q and the KV heads in the reverse of the order
+// the statistics pass read them, so the data read last, still in the
+// last-level (Infinity) cache, is read again first.
 #include "apa_device.h"
 #include "apa_kernels.h"
 
 namespace apa {
 
 namespace {
-
-// Zero the status word (a kernel, so the sequence holds no memset node if
-// the caller captures it in a graph).
-__global__ void k_clear_status(unsigned* status) { *status = 0u; }
 
 // Block-wide max over blockDim.x threads (<= 512) through LDS.
 __device__ float block_max(float v, float* red) {
@@ -42,8 +41,7 @@ __device__ float block_max(float v, float* red) {
 // grid (NCH, B*Hkv), block 2*D.
 template <typename T>
 __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const Geom& g,
-                         const QuantWs& ws, unsigned* status, int ch, int bh, double* sh,
-                         float* red) {
+                         const QuantWs& ws, int ch, int bh, double* sh, float* red) {
   const int D = g.D, ncg = D / 8;
   const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
   const int t = ch * 16 + tt;
@@ -56,6 +54,7 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
   for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
   if (t < g.NT) {
     const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
+#pragma unroll 4
     for (int k = k0; k < k1; ++k) {
       const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)k * D);
       const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)k * D);
@@ -72,7 +71,6 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
       }
     }
   }
-  if (bad) atomicOr(status, 1u);
   double* ssum = sh;
   float* smn = reinterpret_cast<float*>(sh + 16 * D);
   float* smx = smn + 16 * D;
@@ -82,10 +80,11 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
     smn[tt * D + cg * 8 + i] = mn[i];
     smx[tt * D + cg * 8 + i] = mx[i];
   }
-  // block max of |V|
+  // block max of |V|, and whether the block saw a non-finite input
   for (int o = 32; o >= 1; o >>= 1) va = fmaxf(va, __shfl_xor(va, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = va;
-  __syncthreads();
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) ws.flags[(size_t)bh * ws.nch + ch] = bad ? 1u : 0u;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     double c = 0.0;
     float a = __builtin_inff(), b = -__builtin_inff();
@@ -109,8 +108,8 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
 // max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq), block D.
 // (block of 2*D threads: thread (half, d) takes rows r0 + half, r0 + half + 2, ...)
 template <typename T>
-__device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws,
-                        unsigned* status, int t, int bh, float* red) {
+__device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws, int flag, int t,
+                        int bh, float* red) {
   const int d = threadIdx.x % g.D, half = threadIdx.x / g.D;
   const size_t base = ((size_t)bh * g.Nq) * g.D;
   const int r0 = t * 64, r1 = min(g.Nq, r0 + 64);
@@ -121,9 +120,12 @@ __device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& w
     bad |= !__builtin_isfinite(x);
     a = fmaxf(a, fabsf(x));
   }
-  if (bad) atomicOr(status, 1u);
+  bad = __syncthreads_or(bad);
   float m = block_max(a, red);
-  if (threadIdx.x == 0) ws.qamax[(size_t)bh * ws.nqt + t] = m;
+  if (threadIdx.x == 0) {
+    ws.qamax[(size_t)bh * ws.nqt + t] = m;
+    ws.flags[flag] = bad ? 1u : 0u;
+  }
 }
 
 // Head scale mapping amax to 6: g = fl32(amax/6), inv = fl32(6/amax); the FP64
@@ -134,41 +136,65 @@ __device__ void head_scale(float amax, float* gs, float* inv) {
   *inv = (float)(6.0 / (double)amax);
 }
 
+// Chunk statistics are read in batches of kFinBatch chunks with every load of
+// a batch in flight (the block is latency-bound: few blocks, short chains).
+constexpr int kFinBatch = 32;
+
 // Per (b, kv-head): key mean, |K - kbar| max, V max, their head scales, and
-// the tied Q scales of the group's query heads.  grid (B*Hkv), block D.
-__device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* red) {
-  const int d = threadIdx.x;
-  const bool own = d < g.D;  // threads D .. 2D-1 only join the block reductions
-  float dev = 0.0f;
-  if (own) {
-    double s = 0.0;
-    float mn = __builtin_inff(), mx = -__builtin_inff();
-    // chunk sums in ascending order; loads issued 8 chunks ahead of the adds
-    constexpr int BATCH = 8;
-    for (int c0 = 0; c0 < ws.nch; c0 += BATCH) {
-      double bs[BATCH];
-      float bmn[BATCH], bmx[BATCH];
+// the tied Q scales of the group's query heads; every block also folds the
+// statistics blocks' non-finite flags and block 0 writes the status word.
+// grid (B*Hkv), block 2D.
+__device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* xch,
+                         float* red) {
+  const int d = threadIdx.x, nthr = blockDim.x, D = g.D;
+  const bool own = d < D;  // threads D .. 2D-1 fold min and max, and join the block reductions
+  const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
+  double s = 0.0;
+  float mn = __builtin_inff(), mx = -__builtin_inff();
+  for (int c0 = 0; c0 < ws.nch; c0 += kFinBatch) {
+    if (own) {
+      // channel d's chunk sums, added in ascending order
+      double v[kFinBatch];
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        const int c = min(c0 + i, ws.nch - 1);
-        const size_t o = ((size_t)bh * ws.nch + c) * g.D + d;
-        bs[i] = ws.ksum[o];
-        bmn[i] = ws.kmin[o];
-        bmx[i] = ws.kmax[o];
+      for (int i = 0; i < kFinBatch; ++i)
+        v[i] = c0 + i < ws.nch ? ws.ksum[base + (size_t)(c0 + i) * D] : 0.0;
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+        if (c0 + i < ws.nch) s += v[i];
+    } else {
+      float a[kFinBatch], b[kFinBatch];
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i) {
+        const bool in = c0 + i < ws.nch;
+        a[i] = in ? ws.kmin[base + (size_t)(c0 + i) * D] : __builtin_inff();
+        b[i] = in ? ws.kmax[base + (size_t)(c0 + i) * D] : -__builtin_inff();
       }
 #pragma unroll
-      for (int i = 0; i < BATCH; ++i) {
-        if (c0 + i < ws.nch) {
-          s += bs[i];
-          mn = fminf(mn, bmn[i]);
-          mx = fmaxf(mx, bmx[i]);
-        }
+      for (int i = 0; i < kFinBatch; ++i) {
+        mn = fminf(mn, a[i]);
+        mx = fmaxf(mx, b[i]);
       }
     }
+  }
+  if (!own) {
+    xch[d - D] = mn;
+    xch[d] = mx;  // = xch[D + (d - D)]
+  }
+  __syncthreads();
+  float dev = 0.0f;
+  if (own) {
+    mn = xch[d];
+    mx = xch[D + d];
     const float kb = g.Nkv > 0 ? (float)(s / (double)g.Nkv) : 0.0f;
-    f.kbar[(size_t)bh * g.D + d] = kb;
+    f.kbar[(size_t)bh * D + d] = kb;
     if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
   }
+  // non-finite inputs anywhere (every block reads all flags; block 0 writes)
+  unsigned badf = 0u;
+#pragma unroll 8
+  for (int i = d; i < ws.nflags; i += nthr) badf |= ws.flags[i];
+  badf = __syncthreads_or(badf != 0u);
+  if (bh == 0 && d == 0) *f.status = badf ? 1u : 0u;
   const float amax_k = block_max(dev, red);
   float va = 0.0f;
   for (int c = d; c < ws.nch; c += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
@@ -295,6 +321,7 @@ __device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& 
   const int k0 = t * kTile;
   // stage the raw tile, 8 values per 16-byte load; zeros for padding keys
   const int per_row = nch / 8;
+#pragma unroll 4
   for (int i = threadIdx.x; i < kTile * per_row; i += blockDim.x) {
     const int kk = i / per_row, c = (i % per_row) * 8;
     const int key = k0 + kk;
@@ -340,49 +367,51 @@ __device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& 
 // 16*D*(8+4+4) bytes.
 template <typename T>
 __global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                        Geom g, QuantWs ws, unsigned* status, int nkb) {
+                        Geom g, QuantWs ws, int nkb) {
   extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
   __shared__ float red[16];
   if ((int)blockIdx.x < nkb) {
-    kv_stats<T>(K, V, g, ws, status, blockIdx.x % ws.nch, blockIdx.x / ws.nch, sh, red);
+    kv_stats<T>(K, V, g, ws, blockIdx.x % ws.nch, blockIdx.x / ws.nch, sh, red);
   } else {
     const int qb = blockIdx.x - nkb;
-    q_stats<T>(Q, g, ws, status, qb % ws.nqt, qb / ws.nqt, red);
+    q_stats<T>(Q, g, ws, blockIdx.x, qb % ws.nqt, qb / ws.nqt, red);
   }
 }
 
 // One block of 2*D threads per (b, kv-head).
 __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
+  extern __shared__ float xch[];  // [2][D]: min and max of each channel
   __shared__ float red[16];
-  finalize(g, ws, f, blockIdx.x, red);
+  finalize(g, ws, f, blockIdx.x, xch, red);
 }
 
-// Quantisation in one launch: blocks for K rows, then V tiles, then Q rows.
+// Quantisation in one launch: blocks for Q rows first, then per (b, kv-head),
+// last first, per 64-key tile its kpt K-row blocks (16 rows of 128 channels,
+// or the same 2048 elements at other D) and its nvb_z V^T blocks -- the
+// reverse of the order the statistics pass read them.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T* __restrict__ K,
                                                const T* __restrict__ V, Geom g, Fp4Ptrs f,
-                                               int kpb, int nvb_x, int nvb_z, int qpb) {
+                                               int kpt, int nvb_z, int qpb, int nq) {
   int b = blockIdx.x;
-  const int nk = kpb * g.B * g.Hkv, nv = g.NT * g.B * g.Hkv * nvb_z;
-  if (b < nk) {
-    quant_rows<T, false>(K, g, f, b % kpb, b / kpb);
+  if (b < nq) {
+    quant_rows<T, true>(Q, g, f, b % qpb, b / qpb);
     return;
   }
-  b -= nk;
-  if (b < nv) {
-    const int t = b % nvb_x, rest = b / nvb_x;
-    quant_vt<T>(V, g, f, t, rest % (g.B * g.Hkv), rest / (g.B * g.Hkv));
-    return;
-  }
-  b -= nv;
-  quant_rows<T, true>(Q, g, f, b % qpb, b / qpb);
+  b -= nq;
+  const int per_tile = kpt + nvb_z, per_head = g.NT * per_tile;
+  const int bh = g.B * g.Hkv - 1 - b / per_head;
+  const int r = b % per_head, t = r / per_tile, j = r % per_tile;
+  if (j < kpt)
+    quant_rows<T, false>(K, g, f, t * kpt + j, bh);
+  else
+    quant_vt<T>(V, g, f, t, bh, j - kpt);
 }
 
 template <typename T>
 hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const Fp4Ptrs& f,
                         const QuantWs& ws, hipStream_t s) {
   const int nkvh = g.B * g.Hkv;
-  hipLaunchKernelGGL(k_clear_status, dim3(1), dim3(1), 0, s, f.status);
   const size_t stats_lds = 16 * (size_t)g.D * (sizeof(double) + 2 * sizeof(float));
   static bool stats_attr = false;  // above 64 KB (D = 512) the launch must opt in
   if (!stats_attr) {
@@ -395,15 +424,17 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(2 * g.D), stats_lds, s, q, k, v, g, ws,
-                       f.status, nkb);
-  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 0, s, g, ws, f);
-  const int kpb = (int)(((long)g.NkvP * (g.D / 8) + 255) / 256);
+                       nkb);
+  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 2 * g.D * sizeof(float), s, g, ws, f);
+  // K rows: a 64-key tile of D channels is kTile * D / 8 threads, D / 32 blocks
+  const int kpt = g.D / 32;
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
   const int nvb_z = (g.D + 127) / 128;
-  const long nblk = (long)kpb * nkvh + (long)g.NT * nkvh * nvb_z + (long)qpb * g.B * g.Hq;
+  const long nq = (long)qpb * g.B * g.Hq;
+  const long nblk = nq + (long)g.NT * nkvh * (kpt + nvb_z);
   if (nblk > 0)
-    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpb, g.NT,
-                       nvb_z, qpb);
+    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpt,
+                       nvb_z, qpb, (int)nq);
   return hipGetLastError();
 }
 
