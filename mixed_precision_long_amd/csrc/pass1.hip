@@ -582,8 +582,15 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   asm volatile("" : "+v"(ones));
   load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
   qk<D>(acc, kn, c.qa, c.qs);
-  load_k<D>(kn, c.blobs, next_blob(1), c.koff, c.ksoff, hh);
+  // blob offset of the K operand fetched last (position i + 1 when position
+  // i starts): the V operand of position i + 1 is fetched from it at the end
+  // of position i
+  uint32_t kblob = next_blob(1);
+  load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
   load_v(next_blob(0));
+  // eps = 0 marks every visited tile hot: with -1 as the factor, every row
+  // with mass so far passes (l_t > -lambda), and every visible group has one
+  const float epsv = eps == 0.0f ? -1.0f : eps;
 
   for (int i = 0; i < cnt && !gave_up; ++i) {
     const int t = tile_at(i);
@@ -641,7 +648,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     // behind the row sum and run during the vote and the P V product
     __builtin_amdgcn_sched_barrier(0);
     qk<D>(acc, kn, c.qa, c.qs);
-    load_k<D>(kn, c.blobs, next_blob(i + 2), c.koff, c.ksoff, hh);
+    const uint32_t vblob = kblob;
+    kblob = next_blob(i + 2);
+    load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
     const float ell = ones_acc[0];
 
     // ---- step 4: the hot test (lambda includes this tile); a row's scalars
@@ -650,9 +659,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     if (!TAIL && pub_out && i >= kReplay) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
     float lam_t = st.lam;  // the running mass the vote compares against
     if (TAIL) lam_t = (pub_in && !replay ? vmax(lam_lo, pub_in[n]) : lam_lo) + st.lam;
-    const unsigned long long hb = __ballot(ell > eps * lam_t);
-    bool hot0 = vis0 && (eps == 0.0f || (hb & 0xFFFFull) != 0ull);
-    bool hot1 = vis1 && (eps == 0.0f || (hb & 0xFFFF0000ull) != 0ull);
+    const unsigned long long hb = __ballot(ell > epsv * lam_t);
+    bool hot0 = vis0 && (hb & 0xFFFFull) != 0ull;
+    bool hot1 = vis1 && (hb & 0xFFFF0000ull) != 0ull;
     if (tail && !replay && eps != 0.0f && (hot0 || hot1)) {
       // undecided under the lower bound: record it and treat it as cold for
       // now
@@ -701,7 +710,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
         st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
       st.lsum += ez;
     }
-    load_v(next_blob(i + 1));
+    load_v(vblob);
 
     // ---- hot bits: one log byte per tile, or whole words (visited in
     // descending order after tile 0)
