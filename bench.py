@@ -113,8 +113,9 @@ def cpu_baseline(w, ngroups, threads):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first; the GPU clocks settle over the first ~20 steps")
     ap.add_argument("--workload", default="long3b")
     ap.add_argument("--eps", type=float, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
