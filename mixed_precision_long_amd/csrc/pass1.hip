@@ -940,7 +940,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   }
   __syncthreads();
   if (sched == kSchedTriples && NS < 3) return;  // never launched so (too little LDS)
-  const int blk = xcd_remap(blockIdx.x, gridDim.x);
+  // work groups in descending unit order: with causal masking the last row
+  // blocks of a kv-head have the longest visit orders, and they start first
+  // (the dispatcher then fills in with shorter ones); XCD ranges stay contiguous
+  const int blk = (int)gridDim.x - 1 - xcd_remap(blockIdx.x, gridDim.x);
   // the wave's role, its (first) unit, the number of units it walks and the
   // LDS slot of the first
   int role, u0, nu = 1, slot;
