@@ -79,7 +79,6 @@ namespace apa {
 
 namespace {
 
-constexpr int kWaves = 4;            // wavefronts per work group
 constexpr float kFrameGuard = 80.0f; // largest lead of m over m_o before re-basing
 constexpr int kMinSplit = 64;        // shortest visit order that runs as two waves
 constexpr int kReplay = 32;          // leading positions the tail wave replays
@@ -102,10 +101,21 @@ constexpr int kLogTiles = 4096;
 template <int D>
 constexpr int kWavesPerSimd = D >= 256 ? 1 : 2;
 
-// Head states a work group holds in LDS: three (triple schedule) up to
-// D = 256; at D = 512 a head state is 65 KB, so two (pair schedule only).
+// Wavefronts per work group: with two waves per SIMD (D <= 128) a group of
+// eight, so the two waves that share a SIMD (w and w + 4) belong to one
+// group and pace each other through LDS (a wave behind its partner takes the
+// higher issue priority; by default the older wave wins every tie and the
+// younger one finishes alone, at the lower one-wave rate); four above.
 template <int D>
-constexpr int kSlots = D >= 512 ? 2 : 3;
+constexpr int kWgWaves = D >= 256 ? 4 : 8;
+
+// Head states a work group holds in LDS: three per four waves (triple
+// schedule) up to D = 256; at D = 512 a head state is 65 KB, so two (pair
+// schedule only).
+template <int D>
+constexpr int kSlots = D >= 512 ? 2 : 3 * kWgWaves<D> / 4;
+
+typedef __attribute__((address_space(3))) int lds_int;
 
 template <int D>
 struct Tile {
@@ -538,7 +548,10 @@ template <int D, bool LOG, bool TAIL>
 __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
-                                    volatile lds_float* pub_out, lds_u8* vlog, int lane) {
+                                    volatile lds_float* pub_out, lds_u8* vlog, int lane,
+                                    volatile lds_int* pace_me = nullptr,
+                                    const volatile lds_int* pace_mate = nullptr,
+                                    int pace_base = 0) {
   constexpr int ND = Tile<D>::ND;
   constexpr int NW = Tile<D>::NW;
   constexpr int BLOB = Tile<D>::BLOB;
@@ -595,6 +608,13 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   for (int i = 0; i < cnt && !gave_up; ++i) {
     const int t = tile_at(i);
     const bool replay = i < nrep;
+    // pacing: publish this wave's position count; the SIMD partner's is read
+    // now and compared once the tile's maxima are done
+    int mate = 0;
+    if (pace_me) {
+      *pace_me = pace_base + i;
+      mate = *pace_mate;
+    }
     if (tail && i == nrep) {
       lam_lo = st.lam;
       st.lam = 0.0f;
@@ -606,6 +626,12 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     float b0, b1;
     group_maxima(acc, b0, b1);
     const float cmax = vmax(b0, b1);
+    if (pace_me) {
+      if (pace_base + i > __builtin_amdgcn_readfirstlane(mate))
+        __builtin_amdgcn_s_setprio(0);
+      else
+        __builtin_amdgcn_s_setprio(1);
+    }
 
     // ---- lazy maximum (integer frame): the frame moves only where the tile
     // maximum exceeds it by more than tau (never for a row without a visible
@@ -918,15 +944,17 @@ __device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& w
 // (batch, kv-head, 32-row block, head), so the waves of a work group, and the
 // groups of an XCD, stream the same tiles.
 template <int D, bool LOG>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
+__global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
     int sched, int nunits) {
   constexpr int ND = Tile<D>::ND;
   constexpr int NS = kSlots<D>;
+  constexpr int W = kWgWaves<D>;
   // per head of the group: its running lambda and final state
   __shared__ float pub[NS][32];
   __shared__ HeadState<D> hs[NS];
-  __shared__ uint8_t vlog_sh[LOG ? kWaves : 1][LOG ? kLogTiles : 1];  // verdict logs
+  __shared__ uint8_t vlog_sh[LOG ? W : 1][LOG ? kLogTiles : 1];  // verdict logs
+  __shared__ int pace[W];  // position counts of the waves (for the SIMD partner)
   const int lane = threadIdx.x & 63;
   const int hh = lane >> 5;
   // the wave index is wave-uniform: keep everything derived from it in SGPRs
@@ -937,6 +965,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       if (lane < 32) pub[s][lane] = 0.0f;
       if (lane == 0) hs[s].done = 0;
     }
+    if (lane < W) pace[lane] = 0;
   }
   __syncthreads();
   if (sched == kSchedTriples && NS < 3) return;  // never launched so (too little LDS)
@@ -948,22 +977,27 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // LDS slot of the first
   int role, u0, nu = 1, slot;
   if (sched == kSchedTriples) {
-    role = wave < 3 ? kHead : kTail;
-    slot = wave < 3 ? wave : 0;
-    u0 = blk * 3 + slot;
-    if (wave == 3) nu = min(3, nunits - u0);
+    // per four waves: three heads and the wave that walks their tails
+    const int grp = wave >> 2, wq = wave & 3;
+    role = wq < 3 ? kHead : kTail;
+    slot = grp * 3 + (wq < 3 ? wq : 0);
+    u0 = blk * (3 * W / 4) + slot;
+    if (wq == 3) nu = min(3, nunits - u0);
   } else if (sched == kSchedPairs) {
     role = (wave & 1) ? kTail : kHead;
     slot = wave >> 1;
-    u0 = blk * 2 + slot;
+    u0 = blk * (W / 2) + slot;
   } else {
     role = kWhole;
     slot = 0;
-    u0 = blk * kWaves + wave;
+    u0 = blk * W + wave;
   }
   if (u0 >= nunits) return;
   lds_u8* vlog = (lds_u8*)vlog_sh[LOG ? wave : 0];
   const float Hf = (float)hoff;
+  // the partner on this wave's SIMD (waves w and w + 4 of a group of eight)
+  volatile lds_int* pace_me = W == 8 ? (volatile lds_int*)&pace[wave] : nullptr;
+  const volatile lds_int* pace_mate = W == 8 ? (const volatile lds_int*)&pace[wave ^ 4] : nullptr;
 
   if (role != kTail) {
     Ctx<D> c;
@@ -977,7 +1011,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
     zero_above<D>(g, c, lane);
     walk<D, LOG, false>(g, c, st, wd, 0, 0, role == kWhole ? npos : h, eps, tau, Hf,
                         cand_of(f.kv_blob, 0, 0, D), 0, nullptr,
-                        role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane);
+                        role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane,
+                        pace_me, pace_mate, 0);
     if (role == kHead) {
 #pragma unroll
       for (int db = 0; db < ND; ++db)
@@ -1013,6 +1048,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
   // walked state waits in its unit's hand-off area until the heads are done,
   // so no state lives across the loops.
   uint32_t outcomes = 0u;  // outcome + 2 in 10 bits per unit
+  int walked = 0;          // positions walked so far (pacing)
 #pragma nounroll
   for (int k = 0; k < nu; ++k) {
     const int u = u0 + k;
@@ -1027,12 +1063,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(kWa
       Words wd = {shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
       oc = walk<D, LOG, true>(g, c, st, wd, kReplay, h, kReplay + npos - h, eps, tau, Hf,
                               cand_of(split, u, cap, D), cap,
-                              (volatile lds_float*)pub[slot + k], nullptr, vlog, lane);
+                              (volatile lds_float*)pub[slot + k], nullptr, vlog, lane, pace_me,
+                              pace_mate, walked);
+      walked += kReplay + npos - h;
       if (oc >= 0) save_state<D>(handoff_of<D>(split, u, cap), st, wd, lane);
     }
     outcomes |= (uint32_t)(oc + 2) << (10 * k);
   }
   // Finish each unit once its head is done, the last walked first.
+  __builtin_amdgcn_s_setprio(0);
 #pragma nounroll
   for (int k = nu - 1; k >= 0; --k) {
     const int oc = (int)((outcomes >> (10 * k)) & 1023u) - 2;
@@ -1186,15 +1225,16 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   if (nunits == 0) return hipSuccess;
   const int sched = ws ? pass1_sched(g) : kSchedWhole;
   uint8_t* split = sched != kSchedWhole ? static_cast<uint8_t*>(ws) : nullptr;
-  const int per = sched == kSchedTriples ? 3 : (sched == kSchedPairs ? 2 : kWaves);
+  constexpr int W = kWgWaves<D>;
+  const int per = sched == kSchedTriples ? 3 * W / 4 : (sched == kSchedPairs ? W / 2 : W);
   const int nblocks = (nunits + per - 1) / per;
   const int cap = split ? cand_cap(g, sched) : 0;
   const bool log = g.NT <= kLogTiles;
   if (log)
-    hipLaunchKernelGGL((k_pass1<D, true>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
+    hipLaunchKernelGGL((k_pass1<D, true>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
                        hoff, o, split, cap, sched, nunits);
   else
-    hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(kWaves * 64), 0, s, g, f, eps, tau,
+    hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
                        hoff, o, split, cap, sched, nunits);
   if (split) {
     const hipError_t e = hipGetLastError();
