@@ -70,7 +70,7 @@ def test_sizes_and_layout():
     ("Hkv", 5), ("D", 96), ("tile", 32), ("row_group", 8), ("Nkv", 1000), ("dtype", 7),
     ("is_causal", 2), ("tau", -1.0), ("tau", 40.0), ("hot_frame_offset", 2.5),
     ("hot_frame_offset", 65.0),
-    ("scale", float("nan")), ("fmt", 9)])
+    ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4)])
 def test_invalid_problems_are_rejected(field, value):
     p = prob(**{field: value})
     assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
@@ -152,4 +152,27 @@ def test_problem_defaults():
     p = apa.problem(2, 8, 2, 16, 64, 64)
     assert (p.tile, p.row_group, p.tau, p.hot_frame_offset, p.is_causal) == (64, 16, 4.0, 32.0, 1)
     assert p.scale == 0.0 and p.fmt == apa.APA_MXFP4 and p.dtype == apa.APA_F16
+    assert p.pass1_schedule == apa.SCHED_AUTO
     assert math.isfinite(p.tau)
+
+
+def test_pass1_schedule_sizes_the_workspace():
+    """The pass-1 workspace follows the schedule a launch would run: none for
+    one wave per block; per block the outcome word, the records of a tail (at
+    most 512, up to the longest tail of the schedule's cut) and the hand-off
+    area.  The 2048 x 122880 shape (1536 blocks) runs the triple schedule by
+    default, with shorter tails than the pair schedule."""
+    def ws(sched, **kw):
+        return apa.workspace_bytes(prob(pass1_schedule=sched, **kw), apa.CALL_PASS1)
+    units = 24 * 2048 // 32
+    auto, pairs, triples = ws(apa.SCHED_AUTO), ws(apa.SCHED_PAIRS), ws(apa.SCHED_TRIPLES)
+    assert ws(apa.SCHED_WHOLE) == 0
+    assert auto == triples and 0 < triples < pairs
+    hand = (128 * 128 + 1040 + 255) // 256 * 256
+    for total, cut in ((pairs, (1920 + 32) // 2 + 1920 // 64),
+                       (triples, 3 * (1920 + 32) // 4 + 1920 // 32)):
+        cap = min(512, 1920 - cut)
+        assert total == units * ((cap * 292 + 16 + 255) // 256 * 256 + hand)
+    # few blocks: pairs by default; D = 512 has no triple schedule
+    assert ws(apa.SCHED_AUTO, Nq=64) == ws(apa.SCHED_PAIRS, Nq=64)
+    assert ws(apa.SCHED_TRIPLES, D=512, Nq=64) == ws(apa.SCHED_PAIRS, D=512, Nq=64)
