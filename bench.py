@@ -219,6 +219,9 @@ def main():
             w.name, w.B, w.Hq, w.Hkv, w.D, w.Nq, w.Nkv, w.dtype, eps),
             "global_batch": w.B, "seq_len": w.Nkv, "parallelism": "single-gpu"},
         "kernels_ms": {k2: round(v2, 4) for k2, v2 in kern_ms.items()},
+        # the attention alone, with K/V already in the FP4 format (a persistent FP4
+        # K/V cache): pass 1 + pass 2 of the same steps
+        "apa_attn_ms": round(kern_ms["pass1"] + kern_ms["pass2"], 4),
         "roofline": {"bound": "mfma", "kernel": "k_pass1",
                      "achieved": round(p1_tflops, 3), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p1_tflops / PEAK_FP4_TFLOPS, 5),
