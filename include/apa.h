@@ -145,15 +145,17 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
  * eps must be >= 0 and not NaN (+inf allowed).  Requires the FP4 buffer of
  * apa_quantize for the same problem.
  * ws: NULL, or apa_workspace_bytes(p, APA_CALL_PASS1) bytes (0 for problems
- * whose 32-row blocks already fill the GPU).  With a workspace, each long
- * visit order (64 tiles or more) is cut in two: a head wavefront walks its
- * first part while a tail wavefront of the same work group walks the rest.
- * APA_SCHED_PAIRS gives every block its own tail wavefront (two per block);
- * APA_SCHED_TRIPLES runs three blocks on four wavefronts, one tail
- * wavefront walking the three shorter tails one after the other (D <= 256;
- * at D = 512 it runs as PAIRS); APA_SCHED_WHOLE keeps one wavefront per
- * block.  AUTO takes PAIRS while two waves per block fit the GPU's wave
- * slots at once, TRIPLES while four per three blocks do, else WHOLE.  The
+ * whose 32-row blocks already fill the GPU, and at D = 512, where every
+ * block runs as two wavefronts, each holding half of the output channels).
+ * With a workspace, each long visit order (64 tiles or more) is cut in two:
+ * a head wavefront walks its first part while a tail wavefront of the same
+ * work group walks the rest.  APA_SCHED_PAIRS gives every block its own tail
+ * wavefront (two per block); APA_SCHED_TRIPLES runs three blocks on four
+ * wavefronts, one tail wavefront walking the three shorter tails one after
+ * the other; APA_SCHED_WHOLE keeps one wavefront per block.  AUTO takes
+ * PAIRS while two waves per block fit the GPU's wave slots at once, TRIPLES
+ * while four per three blocks do, else WHOLE; at D = 512 every request runs
+ * as WHOLE.  The
  * workspace holds the tiles a tail cannot decide until its head is done
  * (at most 512 per 32-row block, 292 bytes each) and room to hand the
  * head's state to a re-walk of the tail, for blocks with more undecided

@@ -24,9 +24,17 @@ FLAGS = [
 # Per-source extras.  Pass 1 issues the next tile's score MFMAs in the middle
 # of the current tile so they overlap the vote and the P V product; machine
 # sinking would move them to the loop latch (and force the K prefetch into
-# temporaries plus copies that wait on the loads just issued).
+# temporaries plus copies that wait on the loads just issued).  Kernels whose
+# registers exceed the 256 vector registers (one wave per SIMD, D >= 256) keep
+# their MFMA accumulators in vector registers with the VGPR form of the MFMA
+# instructions; otherwise the compiler takes the accumulation-register form
+# for every MFMA and copies the accumulators to vector registers and back in
+# every tile (hundreds of copies per tile; code up to D = 128 is unchanged).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {
-    "pass1.hip": ["-mllvm", "-disable-machine-sink"],
+    "pass1.hip": ["-mllvm", "-disable-machine-sink", *VGPR_FORM],
+    "fa16.hip": VGPR_FORM,
+    "big16.hip": VGPR_FORM,
 }
 
 

@@ -39,182 +39,13 @@
 //                 from LDS by DS_READ_B64_TR_B16.  With bf16 inputs the scores
 //                 use the bf16 MFMA and each wave converts the V rows it loaded
 //                 to fp16 in LDS, so P keeps 11 significant bits.
-// D = 512 (k_attn_big): one wave per SIMD, registers staging into a single
-// padded LDS stage, the output accumulators in the accumulation registers.
-#include <type_traits>
-
-#include "apa_device.h"
-#include "apa_kernels.h"
+// D = 512 runs in big16.hip (two work groups per unit, one per half of the
+// output channels).
+#include "attn16.h"
 
 namespace apa {
 
 namespace {
-
-enum Mode { kExact = 0, kPass2 = 1 };
-
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef float v2f __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16-bit element types: the MFMA and the conversions.
-template <typename T>
-struct E16;
-template <>
-struct E16<_Float16> {
-  typedef v8h V8;
-  typedef v4h V4;
-  static __device__ __forceinline__ v16f mma(V8 a, V8 b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ _Float16 from(float x) { return (_Float16)x; }
-};
-template <>
-struct E16<__bf16> {
-  typedef v8bf V8;
-  typedef v4bf V4;
-  static __device__ __forceinline__ v16f mma(V8 a, V8 b, v16f c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-  static __device__ __forceinline__ __bf16 from(float x) { return (__bf16)x; }
-};
-
-// Row blocks of one (batch, kv-head) and the work groups over them.
-struct RowBlocks {
-  int nqb;  // 32-position blocks
-  int nrb;  // row blocks (G per position block)
-  int nwg;  // work groups of four row blocks
-};
-
-__host__ __device__ inline RowBlocks row_blocks(const Geom& g) {
-  RowBlocks r;
-  r.nqb = (g.Nq + 31) / 32;
-  r.nrb = g.G * r.nqb;
-  r.nwg = (r.nrb + 3) / 4;
-  return r;
-}
-
-constexpr int kWgWaves = 4;      // wavefronts per work group (one row block each)
-constexpr float kLazy = 8.0f;    // lead (log2 units) a row maximum needs to move m
-
-__device__ __forceinline__ float merge_weight(bool live, float m, float M) {
-  return live ? fast_exp2(m - M) : 0.0f;
-}
-
-// bf16 values of V as fp16 for the P V product: exact inside the fp16 range
-// (8 significant bits fit in 11); magnitudes beyond it are clamped to 65504.
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 z) {
-  const uint32_t w[4] = {z.x, z.y, z.z, z.w};
-  uint32_t r[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float lo = fminf(fmaxf(__uint_as_float(w[i] << 16), -65504.0f), 65504.0f);
-    const float hi = fminf(fmaxf(__uint_as_float(w[i] & 0xFFFF0000u), -65504.0f), 65504.0f);
-    const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-    r[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-  }
-  return uint4{r[0], r[1], r[2], r[3]};
-}
-
-// Split s of n items out of `total` (balanced, contiguous).
-__device__ __forceinline__ int split_lo(int total, int s, int S) {
-  return (int)(((long long)total * s) / S);
-}
-
-// The row block of wave `wave` in work group `wg`: its head in the group and
-// its first query position; live = false past the last row block.
-struct WaveRows {
-  bool live;
-  int gi, r0;
-};
-
-__device__ __forceinline__ WaveRows wave_rows(const Geom& g, const RowBlocks& rb, int wg, int wave) {
-  const int j = wg * kWgWaves + wave;
-  WaveRows w;
-  w.live = j < rb.nrb;
-  w.gi = w.live ? j % g.G : 0;
-  w.r0 = w.live ? (j / g.G) * 32 : 0;
-  return w;
-}
-
-// The key tiles a work group visits in exact mode: up to the diagonal of its
-// last live row.
-__device__ __forceinline__ int exact_tiles(const Geom& g, const RowBlocks& rb, int wg) {
-  const int jl = min(wg * kWgWaves + kWgWaves - 1, rb.nrb - 1);
-  const int lr = min((jl / g.G) * 32 + 31, g.Nq - 1);
-  return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile + 1 : g.NT;
-}
-
-// The epilogue shared by both kernels: a split's partial state (S > 1 or an
-// unfused pass 2), else the output -- merged with the cold state in pass 2.
-// Lane (n, hh) holds row n's output channels 32*db + 8*q + 4*hh + 0..3 in
-// o[db][4q .. 4q+3]; l is already summed over both lane halves.
-template <int D, typename T, int MODE>
-__device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
-                                           int S, int sp, size_t bhq, int row, int hh, float m,
-                                           float l, float c_r, const v16f* o) {
-  using E = E16<T>;
-  typedef typename E::V4 V4;
-  constexpr int ND = D / 32;
-  const size_t r = bhq * g.Nq + row;
-  const size_t rows = (size_t)g.B * g.Hq * g.Nq;
-  if (S > 1 || (MODE == kPass2 && !a.fuse)) {
-    float* pm = S > 1 ? a.part_m + (size_t)sp * rows : a.hot_m;
-    float* pl = S > 1 ? a.part_l + (size_t)sp * rows : a.hot_l;
-    float* po = S > 1 ? a.part_o + (size_t)sp * rows * D : a.hot_o;
-    if (hh == 0) {
-      pm[r] = l > 0.0f ? m : -__builtin_inff();
-      pl[r] = l;
-    }
-    float* orow = po + r * D;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v4f x = {o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]};
-        *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
-      }
-    return;
-  }
-  float w1 = 0.0f, w2 = 0.0f, M = 0.0f, Lsum = 0.0f;
-  const float* o1 = nullptr;
-  if (MODE == kPass2) {
-    const int m1i = a.cold_m[r];
-    const float l1 = a.cold_l[r];
-    const bool e1 = l1 > 0.0f && m1i != (int32_t)0x80000000, e2 = l > 0.0f;
-    const float m1 = (float)m1i;
-    M = -__builtin_inff();
-    if (e1) M = m1;
-    if (e2) M = fmaxf(M, m);
-    w1 = merge_weight(e1, m1, M);
-    w2 = merge_weight(e2, m, M);
-    Lsum = w1 * l1 + w2 * l;
-    o1 = a.cold_o + r * D;
-  } else {
-    M = m;
-    w2 = 1.0f;
-    Lsum = l;
-  }
-  const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
-  T* orow = reinterpret_cast<T*>(a.out) + r * D;
-#pragma unroll
-  for (int db = 0; db < ND; ++db)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int ch = db * 32 + 8 * q + 4 * hh;
-      v4f c1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (MODE == kPass2 && w1 != 0.0f) c1 = *reinterpret_cast<const v4f*>(o1 + ch);
-      V4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = E::from((w1 * c1[e] + w2 * o[db][4 * q + e]) * inv);
-      *reinterpret_cast<V4*>(orow + ch) = y;
-    }
-  if (a.lse && hh == 0) {
-    const float c0 = MODE == kPass2 ? c_r : 0.0f;
-    a.lse[r] = Lsum > 0.0f ? 0.69314718055994531f * (c0 + M + __log2f(Lsum)) : -__builtin_inff();
-  }
-}
 
 // ---------------------------------------------------------------------------
 // D <= 256: direct-to-LDS double-buffered tiles, four waves per work group.
@@ -467,229 +298,6 @@ void k_fa(Geom g, const T* __restrict__ Q, const T* __restrict__ K, const T* __r
 }
 
 // ---------------------------------------------------------------------------
-// D = 512: one padded LDS stage filled through registers.
-
-template <int D>
-struct BigCfg {
-  static constexpr int KS = D + 8;    // halves per K row (16-byte pad)
-  static constexpr int VS = D + 32;   // halves per V row (64-byte pad)
-  static constexpr int K_HALVES = kTile * KS;
-  static constexpr int V_HALVES = kTile * VS;
-  static constexpr int STAGE = K_HALVES + V_HALVES;
-  static constexpr size_t BYTES = (size_t)STAGE * 2;
-  static constexpr int CHUNKS = 2 * kTile * D / 8;  // 16-byte chunks per K+V tile
-};
-
-template <int D, typename T, int MODE>
-__device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
-                                         const T* __restrict__ K, const T* __restrict__ V,
-                                         const Fp4Ptrs& f, const Pass2Args& a, int nitems,
-                                         int S) {
-  using C = BigCfg<D>;
-  using E = E16<T>;
-  typedef typename E::V8 V8;
-  extern __shared__ uint16_t smem[];
-  constexpr int NW = kWgWaves;
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int PER = (C::CHUNKS + NW * 64 - 1) / (NW * 64);
-  constexpr int RND = PER < 8 ? PER : 8;  // chunks per staging round
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 31, hh = lane >> 5;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  if (item >= nitems) return;
-  const RowBlocks rb = row_blocks(g);
-  const int wg = MODE == kExact ? rb.nwg - 1 - item % rb.nwg : item % rb.nwg;
-  int u = item / rb.nwg;
-  const int sp = u % S;
-  u /= S;
-  const int hk = u % g.Hkv;
-  const int b = u / g.Hkv;
-  const int unit = (b * g.Hkv + hk) * rb.nwg + wg;
-  const WaveRows wr = wave_rows(g, rb, wg, wave);
-  const int hq = hk * g.G + wr.gi;
-  const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
-  const int r0 = wr.r0;
-  const int row = r0 + n;
-  const bool row_ok = wr.live && row < g.Nq;
-  const int d_wave =
-      wr.live ? (g.causal ? min(g.Nkv - 1, min(r0 + 31, g.Nq - 1) + g.off) / kTile : g.NT - 1) : -1;
-
-  int lo, hi;
-  const int32_t* tiles = nullptr;
-  const uint32_t* masks = nullptr;
-  {
-    const int ntot = MODE == kExact ? exact_tiles(g, rb, wg) : a.list_count[unit];
-    lo = split_lo(ntot, sp, S);
-    hi = split_lo(ntot, sp + 1, S);
-    if (MODE == kPass2) {
-      tiles = a.list_tiles + (size_t)unit * g.NT;
-      masks = a.list_masks + (size_t)unit * g.NT;
-    }
-  }
-  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
-
-  V8 qf[NC];
-  {
-    const int rl = row_ok ? row : 0;
-    const T* qp = Q + ((bhq * g.Nq) + rl) * D + 8 * hh;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) qf[c] = *reinterpret_cast<const V8*>(qp + 16 * c);
-  }
-  const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
-  const float sl = g.sl;
-
-  float m = -__builtin_inff(), l = 0.0f;
-  v16f o[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) o[i] = v16f{};
-
-  const uint16_t* Kh = reinterpret_cast<const uint16_t*>(K) + bhk * (size_t)g.Nkv * D;
-  const uint16_t* Vh = reinterpret_cast<const uint16_t*>(V) + bhk * (size_t)g.Nkv * D;
-
-  // cooperative staging: chunk c < CHUNKS/2 is K (row c / (D/8)), else V
-  auto fetch1 = [&](int t, int c) {
-    uint4 z = {0u, 0u, 0u, 0u};
-    if (c < C::CHUNKS) {
-      const int isv = c >= C::CHUNKS / 2;
-      const int cc = isv ? c - C::CHUNKS / 2 : c;
-      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-      const int key = t * kTile + r;
-      if (key < g.Nkv) z = *reinterpret_cast<const uint4*>((isv ? Vh : Kh) + (size_t)key * D + col);
-    }
-    return z;
-  };
-  auto stash1 = [&](int c, uint4 z) {
-    if (c < C::CHUNKS) {
-      const int isv = c >= C::CHUNKS / 2;
-      if (std::is_same<T, __bf16>::value && isv) z = bf16x8_to_f16x8(z);
-      const int cc = isv ? c - C::CHUNKS / 2 : c;
-      const int r = cc / (D / 8), col = (cc % (D / 8)) * 8;
-      uint16_t* dst = isv ? smem + C::K_HALVES + r * C::VS + col : smem + r * C::KS + col;
-      *reinterpret_cast<uint4*>(dst) = z;
-    }
-  };
-  uint4 pre[RND];
-
-  for (int it = lo; it < hi; ++it) {
-    const int t = tile_at(it);
-    __syncthreads();
-    for (int r0c = 0; r0c < PER; r0c += RND) {
-#pragma unroll
-      for (int i = 0; i < RND; ++i) pre[i] = fetch1(t, tid + (r0c + i) * NW * 64);
-#pragma unroll
-      for (int i = 0; i < RND; ++i) stash1(tid + (r0c + i) * NW * 64, pre[i]);
-    }
-    __syncthreads();
-
-    bool on0, on1;
-    if (MODE == kExact) {
-      on0 = on1 = t <= d_wave;
-    } else {
-      const uint32_t mk = masks[it];
-      on0 = (mk >> (2 * wave)) & 1u;
-      on1 = (mk >> (2 * wave + 1)) & 1u;
-    }
-    if (!(wr.live && (on0 || on1))) continue;
-    const uint16_t* Ks = smem;
-    const uint16_t* Vs = Ks + C::K_HALVES;
-    const int k0 = t * kTile;
-    v16f acc[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      acc[kb] = v16f{};
-      const uint16_t* kr = Ks + (kb * 32 + n) * C::KS + 8 * hh;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const V8 kf = *reinterpret_cast<const V8*>(kr + 16 * c);
-        acc[kb] = E::mma(kf, qf[c], acc[kb]);
-      }
-    }
-    const bool grp_on = (n >> 4) ? on1 : on0;
-    const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
-                           (r0 + 31 >= g.Nq) || (on0 != on1);
-    const int lim = g.causal ? row + g.off : 0x7fffffff;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc[kb][j] = fmaf(acc[kb][j], sl, -c_r);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (!(grp_on && row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
-        }
-    }
-    float tmax = vmax(acc[0][0], acc[0][1]);
-#pragma unroll
-    for (int j = 2; j < 16; j += 2) tmax = vmax3(tmax, acc[0][j], acc[0][j + 1]);
-#pragma unroll
-    for (int j = 0; j < 16; j += 2) tmax = vmax3(tmax, acc[1][j], acc[1][j + 1]);
-    tmax = vmax(tmax, xor32(tmax));
-    const float mnew = vmax(m, tmax);
-    if (__ballot(mnew > m) != 0ull) {
-      const float alpha = (mnew > m) ? fast_exp2(m - mnew) : 1.0f;  // m=-inf -> 0
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o[db][j] *= alpha;
-      l *= alpha;
-      m = mnew;
-    }
-    const float ms = m == -__builtin_inff() ? 0.0f : m;
-    v8h pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = fast_exp2(acc[kb][8 * c + j] - ms);
-          l += p;
-          pf[kb][c][j] = (_Float16)p;
-        }
-    const int G16 = lane >> 4, i16 = lane & 15;
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int ch0 = db * 32 + 16 * (G16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int keyb = kb * 32 + 16 * c + 4 * (G16 >> 1) + (i16 >> 2);
-          const uint16_t* p0 = Vs + keyb * C::VS + ch0;
-          const uint16_t* p1 = p0 + 8 * C::VS;
-          const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(p0));
-          const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(p1));
-          const v8h vf = __builtin_bit_cast(v8h, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[db] = mfma_f16(vf, pf[kb][c], o[db]);
-        }
-    }
-  }
-
-  if (!wr.live) return;
-  l += xor32(l);
-  if (!row_ok) return;
-  finish_row<D, T, MODE>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o);
-}
-
-// One wave per SIMD, so the 256 output accumulators per lane can sit in the
-// accumulation registers beside the resident Q operand.
-template <int D, typename T, int MODE>
-__global__ __launch_bounds__(kWgWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_attn_big(
-    Geom g, const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, Fp4Ptrs f,
-    Pass2Args a, int nitems, int S) {
-  big_body<D, T, MODE>(g, Q, K, V, f, a, nitems, S);
-}
-
-// ---------------------------------------------------------------------------
 
 // Hot mask -> per work group (batch, kv-head, four row blocks) the list of the
 // tiles hot for any of its verdict groups, ascending, with a mask of the
@@ -846,25 +454,23 @@ hipError_t run_attn(const Geom& g, const void* q, const void* k, const void* v, 
                     const Pass2Args& a, int S, hipStream_t s) {
   const int nitems = attn_units(g) * S;
   if (nitems == 0) return hipSuccess;
-  void (*kern)(Geom, const T*, const T*, const T*, Fp4Ptrs, Pass2Args, int, int);
-  size_t bytes;
+  hipError_t e;
   if constexpr (D >= 512) {
-    kern = k_attn_big<D, T, MODE>;
-    bytes = BigCfg<D>::BYTES;
+    e = launch_attn_big(g, q, k, v, f, a, S, MODE, s);
   } else {
-    kern = k_fa<D, T, MODE>;
-    bytes = FaCfg<D>::BYTES;
+    auto kern = k_fa<D, T, MODE>;
+    constexpr size_t bytes = FaCfg<D>::BYTES;
+    static bool attr_done = false;
+    if (!attr_done) {
+      e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)bytes);
+      if (e != hipSuccess) return e;
+      attr_done = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(nitems), dim3(kWgWaves * 64), bytes, s, g, (const T*)q,
+                       (const T*)k, (const T*)v, f, a, nitems, S);
+    e = hipGetLastError();
   }
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)bytes);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(nitems), dim3(kWgWaves * 64), bytes, s, g, (const T*)q,
-                     (const T*)k, (const T*)v, f, a, nitems, S);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const long nrows = (long)g.B * g.Hq * g.Nq;
   const long thr = nrows * (D / 4);
@@ -900,9 +506,11 @@ int attn_splits(const Geom& g) {
   const long units = attn_units(g);
   if (units <= 0) return 1;
   // about three work groups per resident slot of the 256-CU part (two per CU
-  // up to D = 128, one above), so the dispatcher can even out their lengths
+  // up to D = 128, one above), so the dispatcher can even out their lengths;
+  // at D = 512 each unit and split runs as two work groups (output halves)
   const long slots = 256L * (g.D <= 128 ? 2 : 1);
-  long S = (3 * slots + units - 1) / units;
+  const long wgs = units * (g.D >= 512 ? 2 : 1);
+  long S = (3 * slots + wgs - 1) / wgs;
   if (S > 8) S = 8;
   // at least 16 tiles per split of the longest key range
   long maxs = g.NT / 16;

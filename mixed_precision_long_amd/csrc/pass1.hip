@@ -110,18 +110,29 @@ template <int D>
 constexpr int kWgWaves = D >= 256 ? 4 : 8;
 
 // Head states a work group holds in LDS: three per four waves (triple
-// schedule) up to D = 256; at D = 512 a head state is 65 KB, so two (pair
-// schedule only).
+// schedule) up to D = 256; none used at D = 512 (one wave pair per unit, no
+// head/tail split).
 template <int D>
-constexpr int kSlots = D >= 512 ? 2 : 3 * kWgWaves<D> / 4;
+constexpr int kSlots = D >= 512 ? 1 : 3 * kWgWaves<D> / 4;
 
 typedef __attribute__((address_space(3))) int lds_int;
+
+// Output channels per wave.  At D = 512 a unit runs as two waves, each with
+// the accumulators of half of the output channels (32 x 256 FP32: 128
+// registers per lane instead of 256, which with the operands of a tile would
+// not fit): both walk the same tiles with the same scores, frames and
+// verdicts (the same arithmetic on the same operands), each adds the P V of
+// its own channels, and only the first writes the row scalars and hot words.
+template <int D>
+constexpr int kOutSplit = D >= 512 ? 2 : 1;
 
 template <int D>
 struct Tile {
   static constexpr int NH = D / 64;       // 64-channel halves of the QK contraction
   static constexpr int ND = D / 32;       // 32-channel blocks of the output
+  static constexpr int NDO = ND / kOutSplit<D>;  // of them, held by one wave
   static constexpr int NW = (D / 32 + 3) / 4;  // 32-bit words of one key's scale bytes
+  static constexpr int NWO = (NDO + 3) / 4;    // of one V lane's scale bytes (a wave's)
   static constexpr int BLOB = 68 * D;
 };
 
@@ -157,15 +168,15 @@ __device__ __forceinline__ v4i bload128(Rsrc r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// The scale bytes of one key (or one V lane) as little-endian words.
-template <int D>
-__device__ __forceinline__ void load_scales(uint32_t (&w)[Tile<D>::NW], Rsrc r, uint32_t voff,
+// NB scale bytes (of one key, or one V lane's blocks) as little-endian words.
+template <int NB>
+__device__ __forceinline__ void load_scales(uint32_t (&w)[(NB + 3) / 4], Rsrc r, uint32_t voff,
                                             uint32_t soff) {
-  if constexpr (D == 64) {
+  if constexpr (NB == 2) {
     w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-  } else if constexpr (D == 128) {
+  } else if constexpr (NB == 4) {
     w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-  } else if constexpr (D == 256) {
+  } else if constexpr (NB == 8) {
     const auto x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
     w[0] = x[0];
     w[1] = x[1];
@@ -192,7 +203,7 @@ __device__ __forceinline__ void load_k(KOps<D>& k, Rsrc r, uint32_t soff, uint32
   for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) k.a[kb][h] = bload128(r, koff + kb * 32 * (D / 2) + 32 * h, soff);
-    load_scales<D>(k.s[kb], r, ksoff + kb * 32 * (D / 32), soff);
+    load_scales<D / 32>(k.s[kb], r, ksoff + kb * 32 * (D / 32), soff);
 #pragma unroll
     for (int w = 0; w < Tile<D>::NW; ++w) k.s[kb][w] >>= 8 * hh;
   }
@@ -244,13 +255,16 @@ struct Ctx {
   int qs[Tile<D>::NH];  // its E8M0 bytes (block scale + head exponent)
   Rsrc blobs;  // the unit's kv-head: NT tile blobs
   uint32_t koff, ksoff, voff, vsoff;  // this lane's byte offsets inside a blob
+  int dh;     // which share of the output channels the wave holds
+  bool lead;  // the wave that writes the row scalars and hot words (dh = 0)
   float g_v;
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
 };
 
 template <int D>
 __device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs& f,
-                                         const Pass1Out& out, const UnitId& id, int lane) {
+                                         const Pass1Out& out, const UnitId& id, int lane,
+                                         int dh = 0) {
   constexpr int NH = Tile<D>::NH;
   constexpr int ND = Tile<D>::ND;
   const int n = lane & 31, hh = lane >> 5;
@@ -282,8 +296,11 @@ __device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs
                       (uint32_t)g.NT * Tile<D>::BLOB);
   c.koff = n * (D / 2) + 16 * hh;
   c.ksoff = 32 * D + n * (D / 32);
-  c.voff = 34 * D + n * 32 + 16 * hh;
-  c.vsoff = 66 * D + (2 * n + hh) * ND;
+  constexpr int NDO = Tile<D>::NDO;
+  c.dh = dh;
+  c.lead = dh == 0;
+  c.voff = 34 * D + n * 32 + 16 * hh + dh * NDO * 32 * 32;
+  c.vsoff = 66 * D + (2 * n + hh) * ND + dh * NDO;
   c.bits0 = out.bits + (c.bhq * g.NG + (c.r0 >> 4)) * g.W;
   c.bits1 = c.bits0 + g.W;
 }
@@ -295,7 +312,7 @@ struct St {
   float mf;  // the method's frame: an integer, -inf before the first key
   int mo;    // the state's frame
   float lam, lsum;
-  v16f o[Tile<D>::ND];
+  v16f o[Tile<D>::NDO];
 };
 
 // Rows past Nq never see a key and sit at frame 64 so every derived quantity
@@ -308,7 +325,7 @@ __device__ __forceinline__ void init_state(St<D>& st, bool row_ok) {
   st.lam = 0.0f;
   st.lsum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < Tile<D>::ND; ++i) st.o[i] = v16f{};
+  for (int i = 0; i < Tile<D>::NDO; ++i) st.o[i] = v16f{};
 }
 
 // Hot words a walk could not complete by itself: word 0 (tile 0 belongs to the
@@ -347,7 +364,7 @@ __device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint
   } else if (w == wd.wb) {
     wd.p10 |= b0;
     wd.p11 |= b1;
-  } else if (lane == 0) {
+  } else if (lane == 0 && c.lead) {
     c.bits0[w] = b0;
     if (c.has_g1) c.bits1[w] = b1;
   }
@@ -389,7 +406,7 @@ __device__ __forceinline__ Cand cand_of(uint8_t* ws, int unit, int cap, int D) {
 // The head wave's final state, handed to the tail wave in LDS.
 template <int D>
 struct HeadState {
-  v4f o[Tile<D>::ND * 4][64];  // o in lane order: float4 chunk q of block db at [4 db + q]
+  v4f o[Tile<D>::NDO * 4][64];  // o in lane order: float4 chunk q of block db at [4 db + q]
   float sc[4][64];             // mf, mo (its bits), lambda, l per lane
   uint32_t words[4];           // partial words: word 0 and word wb, groups 0 and 1
   int done;
@@ -516,7 +533,7 @@ __device__ __forceinline__ void assemble_words(const Ctx<D>& c, Words& wd, const
         b0 |= (v & 1u) << (tt & 31);
         b1 |= (v >> 1) << (tt & 31);
       }
-      if (w != 0 && w != wd.wb) {
+      if (w != 0 && w != wd.wb && c.lead) {
         c.bits0[w] = b0;
         if (c.has_g1) c.bits1[w] = b1;
       }
@@ -552,8 +569,8 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
                                     volatile lds_int* pace_me = nullptr,
                                     const volatile lds_int* pace_mate = nullptr,
                                     int pace_base = 0) {
-  constexpr int ND = Tile<D>::ND;
-  constexpr int NW = Tile<D>::NW;
+  constexpr int ND = Tile<D>::NDO;  // output blocks of this wave
+  constexpr int NW = Tile<D>::NWO;
   constexpr int BLOB = Tile<D>::BLOB;
   const int n = lane & 31;  // the wave's row handled by this lane
   const int hh = lane >> 5; // which half of the K dimension this lane feeds
@@ -585,7 +602,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   auto load_v = [&](uint32_t blob) {
 #pragma unroll
     for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
-    load_scales<D>(vsw, c.blobs, c.vsoff, blob);
+    load_scales<ND>(vsw, c.blobs, c.vsoff, blob);
   };
   // (issued in the loop's own order, K(i+1) before V(i), so the waits the
   // compiler places at the loop head count only the loads they need)
@@ -594,10 +611,10 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
   asm volatile("" : "+v"(ones));
   load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
-  qk<D>(acc, kn, c.qa, c.qs);
   // blob offset of the K operand fetched last (position i + 1 when position
   // i starts): the V operand of position i + 1 is fetched from it at the end
   // of position i
+  qk<D>(acc, kn, c.qa, c.qs);
   uint32_t kblob = next_blob(1);
   load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
   load_v(next_blob(0));
@@ -771,15 +788,15 @@ __device__ __forceinline__ void store_state(const Geom& g, const Ctx<D>& c, cons
   const size_t r = c.bhq * g.Nq + c.row;
   const int m = (int)st.mf;
   const int sh = st.mo - m;
-  if (hh == 0) {
+  if (hh == 0 && c.lead) {
     out.m[r] = m;
     out.l[r] = ldexpf(st.lsum, sh);
     if (out.lam) out.lam[r] = ldexpf(st.lam, sh);
   }
   const float gs = ldexpf(c.g_v, sh);
-  float* orow = out.o + r * D;
+  float* orow = out.o + r * D + c.dh * Tile<D>::NDO * 32;
 #pragma unroll
-  for (int db = 0; db < Tile<D>::ND; ++db)
+  for (int db = 0; db < Tile<D>::NDO; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       v4f x = {st.o[db][4 * q] * gs, st.o[db][4 * q + 1] * gs, st.o[db][4 * q + 2] * gs,
@@ -791,6 +808,7 @@ __device__ __forceinline__ void store_state(const Geom& g, const Ctx<D>& c, cons
 // zero the hot words above each group's diagonal word
 template <int D>
 __device__ __forceinline__ void zero_above(const Geom& g, const Ctx<D>& c, int lane) {
+  if (!c.lead) return;
   for (int w = c.d0 / 32 + 1 + lane; w < g.W; w += 64) c.bits0[w] = 0u;
   if (c.has_g1)
     for (int w = c.d1 / 32 + 1 + lane; w < g.W; w += 64) c.bits1[w] = 0u;
@@ -804,8 +822,8 @@ template <int D>
 __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st, Words& tw,
                                        const Cand& cr, int ncand, float lam_a, float eps,
                                        int lane) {
-  constexpr int ND = Tile<D>::ND;
-  constexpr int NW = Tile<D>::NW;
+  constexpr int ND = Tile<D>::NDO;
+  constexpr int NW = Tile<D>::NWO;
   constexpr int BLOB = Tile<D>::BLOB;
   constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
   const int n = lane & 31, hh = lane >> 5;
@@ -865,7 +883,7 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       uint32_t vsw[NW];
 #pragma unroll
       for (int db = 0; db < ND; ++db) va[db] = bload128(c.blobs, c.voff + db * 32 * 32, blob);
-      load_scales<D>(vsw, c.blobs, c.vsoff, blob);
+      load_scales<ND>(vsw, c.blobs, c.vsoff, blob);
 #pragma unroll
       for (int db = 0; db < ND; ++db)
         st.o[db] = mfma4(va[db], pz, st.o[db], (int)vsw[db >> 2], db & 3, pscale);
@@ -901,7 +919,7 @@ __device__ __forceinline__ float* handoff_of(uint8_t* split, int unit, int cap) 
 template <int D>
 __device__ __forceinline__ void save_state(float* dst, const St<D>& st, const Words& wd, int lane) {
 #pragma unroll
-  for (int db = 0; db < Tile<D>::ND; ++db)
+  for (int db = 0; db < Tile<D>::NDO; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       reinterpret_cast<v4f*>(dst)[(4 * db + q) * 64 + lane] =
@@ -917,7 +935,7 @@ __device__ __forceinline__ void save_state(float* dst, const St<D>& st, const Wo
 template <int D>
 __device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& wd, int lane) {
 #pragma unroll
-  for (int db = 0; db < Tile<D>::ND; ++db)
+  for (int db = 0; db < Tile<D>::NDO; ++db)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const v4f x = reinterpret_cast<const v4f*>(src)[(4 * db + q) * 64 + lane];
@@ -947,7 +965,7 @@ template <int D, bool LOG>
 __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
     int sched, int nunits) {
-  constexpr int ND = Tile<D>::ND;
+  constexpr int ND = Tile<D>::NDO;
   constexpr int NS = kSlots<D>;
   constexpr int W = kWgWaves<D>;
   // per head of the group: its running lambda and final state
@@ -969,13 +987,14 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
   }
   __syncthreads();
   if (sched == kSchedTriples && NS < 3) return;  // never launched so (too little LDS)
+  if (kOutSplit<D> > 1 && sched != kSchedWhole) return;  // never launched so
   // work groups in descending unit order: with causal masking the last row
   // blocks of a kv-head have the longest visit orders, and they start first
   // (the dispatcher then fills in with shorter ones); XCD ranges stay contiguous
   const int blk = (int)gridDim.x - 1 - xcd_remap(blockIdx.x, gridDim.x);
   // the wave's role, its (first) unit, the number of units it walks and the
   // LDS slot of the first
-  int role, u0, nu = 1, slot;
+  int role, u0, nu = 1, slot, dh = 0;
   if (sched == kSchedTriples) {
     // per four waves: three heads and the wave that walks their tails
     const int grp = wave >> 2, wq = wave & 3;
@@ -988,9 +1007,11 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     slot = wave >> 1;
     u0 = blk * (W / 2) + slot;
   } else {
+    // (at D = 512 two consecutive waves per unit, one per half of the output)
     role = kWhole;
     slot = 0;
-    u0 = blk * W + wave;
+    u0 = (blk * W + wave) / kOutSplit<D>;
+    dh = (blk * W + wave) % kOutSplit<D>;
   }
   if (u0 >= nunits) return;
   lds_u8* vlog = (lds_u8*)vlog_sh[LOG ? wave : 0];
@@ -1001,7 +1022,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
 
   if (role != kTail) {
     Ctx<D> c;
-    make_ctx<D>(c, g, f, out, unit_id(g, u0), lane);
+    make_ctx<D>(c, g, f, out, unit_id(g, u0), lane, dh);
     const int npos = c.dW + 1;
     if (npos < kMinSplit) role = kWhole;  // nothing to cut: its tail wave skips it
     const int h = cut_point(npos, sched);  // head positions [0, h), tail [h, npos)
@@ -1013,7 +1034,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
                         cand_of(f.kv_blob, 0, 0, D), 0, nullptr,
                         role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane,
                         pace_me, pace_mate, 0);
-    if (role == kHead) {
+    if (kOutSplit<D> == 1 && role == kHead) {
 #pragma unroll
       for (int db = 0; db < ND; ++db)
 #pragma unroll
@@ -1034,7 +1055,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
       return;
     }
     // a whole unit: word 0 (which also holds tile 0) and the state
-    if (lane == 0) {
+    if (lane == 0 && c.lead) {
       c.bits0[0] = wd.p00;
       if (c.has_g1) c.bits1[0] = wd.p01;
     }
@@ -1047,6 +1068,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
   // up; -2 no tail: a short visit order its head wave walked whole).  Each
   // walked state waits in its unit's hand-off area until the heads are done,
   // so no state lives across the loops.
+  if constexpr (kOutSplit<D> == 1) {
   uint32_t outcomes = 0u;  // outcome + 2 in 10 bits per unit
   int walked = 0;          // positions walked so far (pacing)
 #pragma nounroll
@@ -1137,6 +1159,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
         *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
       }
   }
+  }
 }
 
 // The re-walk of units whose tail gave up (record full, or a re-base of its
@@ -1191,16 +1214,16 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
 // The schedule a launch with a workspace runs: the caller's, else two waves
 // per unit while those fit the GPU's wave slots at once, four waves per three
 // units while those do, else one wave per unit (then there is no workspace).
-// Visit orders shorter than kMinSplit positions leave nothing to cut, and the
-// triple schedule needs three head states in LDS (D <= 256).
+// Visit orders shorter than kMinSplit positions leave nothing to cut, the
+// triple schedule needs three head states in LDS (D <= 256), and at D = 512
+// every unit already runs as two waves (one per half of the output channels).
 int pass1_sched(const Geom& g) {
   const long units = (long)g.B * g.Hkv * (g.NqP / 32) * g.G;
   const long slots = 1024L * (g.D >= 256 ? 1 : 2);
-  if (units == 0 || g.NT < kMinSplit) return kSchedWhole;
+  if (units == 0 || g.NT < kMinSplit || g.D >= 512) return kSchedWhole;
   int s = g.sched;
   if (s != kSchedWhole && s != kSchedPairs && s != kSchedTriples)
     s = 2 * units <= slots ? kSchedPairs : (4 * units <= 3 * slots ? kSchedTriples : kSchedWhole);
-  if (s == kSchedTriples && g.D > 256) s = kSchedPairs;
   return s;
 }
 
@@ -1226,7 +1249,8 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   const int sched = ws ? pass1_sched(g) : kSchedWhole;
   uint8_t* split = sched != kSchedWhole ? static_cast<uint8_t*>(ws) : nullptr;
   constexpr int W = kWgWaves<D>;
-  const int per = sched == kSchedTriples ? 3 * W / 4 : (sched == kSchedPairs ? W / 2 : W);
+  const int per = sched == kSchedTriples ? 3 * W / 4
+                  : (sched == kSchedPairs ? W / 2 : W / kOutSplit<D>);
   const int nblocks = (nunits + per - 1) / per;
   const int cap = split ? cand_cap(g, sched) : 0;
   const bool log = g.NT <= kLogTiles;
@@ -1236,7 +1260,8 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   else
     hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
                        hoff, o, split, cap, sched, nunits);
-  if (split) {
+  if constexpr (kOutSplit<D> == 1) {
+    if (!split) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (log)

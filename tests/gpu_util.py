@@ -95,7 +95,7 @@ def pass1_schedule(p) -> int:
     choice for SCHED_AUTO, restated for the tests)."""
     units = p.B * p.Hq * (-(-p.Nq // 32))
     slots = 1024 * (1 if p.D >= 256 else 2)
-    if units == 0 or -(-p.Nkv // 64) < 64:
+    if units == 0 or -(-p.Nkv // 64) < 64 or p.D >= 512:
         return apa.SCHED_WHOLE
     s = p.pass1_schedule
     if s not in (apa.SCHED_WHOLE, apa.SCHED_PAIRS, apa.SCHED_TRIPLES):

@@ -173,6 +173,8 @@ def test_pass1_schedule_sizes_the_workspace():
                        (triples, 3 * (1920 + 32) // 4 + 1920 // 32)):
         cap = min(512, 1920 - cut)
         assert total == units * ((cap * 292 + 16 + 255) // 256 * 256 + hand)
-    # few blocks: pairs by default; D = 512 has no triple schedule
+    # few blocks: pairs by default; at D = 512 every unit runs as two waves
+    # (one per half of the output channels) and is never cut
     assert ws(apa.SCHED_AUTO, Nq=64) == ws(apa.SCHED_PAIRS, Nq=64)
-    assert ws(apa.SCHED_TRIPLES, D=512, Nq=64) == ws(apa.SCHED_PAIRS, D=512, Nq=64)
+    for sched in (apa.SCHED_AUTO, apa.SCHED_PAIRS, apa.SCHED_TRIPLES):
+        assert ws(sched, D=512, Nq=64) == 0
