@@ -120,7 +120,7 @@ def main():
     ap.add_argument("--eps", type=float, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip timing the all-exact path")
-    ap.add_argument("--cpu-groups", type=int, default=32)
+    ap.add_argument("--cpu-groups", type=int, default=64)
     ap.add_argument("--no-sweep", action="store_true", help="skip the eps sweep")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
