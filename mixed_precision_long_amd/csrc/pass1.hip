@@ -26,7 +26,7 @@
 //             E + m = max(ceil(c_g - log2 6), m - 127); one V_PERMLANE32_SWAP
 //             per dword turns the accumulator layout into the MFMA operand
 //             layout (V^T is stored in the matching key order);
-//   l_t     : one FP4 MFMA of P against an all-ones operand (numerator and
+//   l_t     : one FP4 MFMA of P against a ones selector (numerator and
 //             denominator carry the same quantisation);
 //   vote    : row hot iff l_t > eps * lambda (lambda includes this tile),
 //             ballot over 16 rows;
@@ -152,6 +152,29 @@ __device__ __forceinline__ v16f mfma4(v4i a, v4i b, v16f c, int sa, int opa, int
     case 2: return mfma4_sel<2, 0>(a, b, c, sa, sb);
     default: return mfma4_sel<3, 0>(a, b, c, sa, sb);
   }
+}
+
+// Row sums of the quantised P by one scaled FP4 MFMA 16x16x128 (half the
+// matrix cycles of a 32x32x64 product against ones).  It reads the P operand,
+// laid out for the 32x32x64 products (lane l: row l%32, keys 32*(l/32)..+31),
+// as column l%16 with K block l/16, so column c holds row c in blocks 0 and 2
+// and row c+16 in blocks 1 and 3.  The selector operand holds E2M1 ones in
+// blocks 0 and 2 of rows 0 and 8 and in blocks 1 and 3 of rows 4 and 12 (zeros
+// elsewhere); row c's sum then lands in C[0][c] and C[8][c], row c+16's in
+// C[4][c] and C[12][c], and the result register 0 of lane l (element
+// C[4*(l/16)][l%16]) is the sum of the lane's own row.
+__device__ __forceinline__ v4i rowsum_selector(int lane) {
+  const int r = lane & 7;          // row l%16 of A, modulo 8
+  const int odd = (lane >> 4) & 1;  // K block l/16 is 1 or 3
+  const int w = (r == 0 && !odd) || (r == 4 && odd) ? kE2M1Ones : 0;
+  return v4i{w, w, w, w};
+}
+
+__device__ __forceinline__ float rowsum4(v4i sel, v4i p, int sp) {
+  v8i A = {sel[0], sel[1], sel[2], sel[3], 0, 0, 0, 0};
+  v8i B = {p[0], p[1], p[2], p[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, v4f{}, 4, 4, 0, kE8M0One, 0,
+                                                          sp)[0];
 }
 
 // A unit's tile blobs are read through a buffer resource: the lane's offset
@@ -606,9 +629,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   };
   // (issued in the loop's own order, K(i+1) before V(i), so the waits the
   // compiler places at the loop head count only the loads they need)
-  // the all-ones operand of the row-sum MFMA, kept in registers (made opaque
+  // the selector operand of the row-sum MFMA, kept in registers (made opaque
   // before any load is in flight)
-  v4i ones = {kE2M1Ones, kE2M1Ones, kE2M1Ones, kE2M1Ones};
+  v4i ones = rowsum_selector(lane);
   asm volatile("" : "+v"(ones));
   load_k<D>(kn, c.blobs, next_blob(0), c.koff, c.ksoff, hh);
   // blob offset of the K operand fetched last (position i + 1 when position
@@ -686,7 +709,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     const int pscale = (hh ? x1i : x0i) - st.mo + 127;
 
     // ---- step 3: l_t as an MFMA of the quantised P itself (state's frame)
-    const v16f ones_acc = mfma4(ones, pb, v16f{}, kE8M0One, 0, pscale);
+    const float ell = rowsum4(ones, pb, pscale);
     // this tile's scores are consumed: the next tile's go to the matrix cores
     // behind the row sum and run during the vote and the P V product
     __builtin_amdgcn_sched_barrier(0);
@@ -694,7 +717,6 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     const uint32_t vblob = kblob;
     kblob = next_blob(i + 2);
     load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
-    const float ell = ones_acc[0];
 
     // ---- step 4: the hot test (lambda includes this tile); a row's scalars
     // are the same in both lane halves, so the low 32 ballot bits are the rows
