@@ -33,7 +33,9 @@
  * eps=0 against FP64 exact attention; eps>=1 against the frame-free all-FP4
  * result; the merge against softmax over the union of arbitrary key splits;
  * the cold-verdict safety bound; frame invariance over (tau, H); the NV-mode
- * sink bug; the tile order against hand-derived orders.  Parity unpinned: the
+ * sink bug; the tile order against hand-derived orders; the two-term Q
+ * quantisation against a nearest-value search of the residual, and its scores
+ * against the brute force.  Parity unpinned: the
  * pages' measured numbers (they come from activation dumps that are not
  * available), listed as such in the design notes.
  */
@@ -57,6 +59,7 @@ typedef struct {
   float eps;        /* hot threshold */
   int32_t tile;     /* keys per tile (64) */
   int32_t rg;       /* rows per verdict (16) */
+  int32_t q_terms;  /* 1: Q quantised once; 2: plus the FP4 residual term */
 } orc_params;
 
 /* ------------------------------------------------------------------------ */
@@ -301,6 +304,37 @@ void orc_quant_rows(const float* X, int n, int D, const float* centre, float inv
   }
 }
 
+/* Two-term quantisation of rows along channels ("Second hunt: which operand
+ * is to blame": Q is quantised twice, the first term as before and the second
+ * the FP4 residual of the first, in the same per-head scale).  Per block: the
+ * first term's codes and scale as orc_quant_rows; the residual of each
+ * normalised value, fl32(x' - dequantised first term), is then quantised as a
+ * block of its own (own exponent or UE4M3 scale).  codes2/scales2 have the
+ * layout of codes/scales. */
+void orc_quant_rows2(const float* X, int n, int D, float inv, int fmt, uint8_t* codes,
+                     uint8_t* scales, uint8_t* codes2, uint8_t* scales2) {
+  int Bs = fmt == ORC_NV ? 16 : 32;
+  float buf[32], res[32];
+  uint8_t cb[32], cb2[32];
+  for (int r = 0; r < n; ++r) {
+    for (int b0 = 0; b0 < D; b0 += Bs) {
+      size_t sidx = (size_t)r * (D / Bs) + b0 / Bs;
+      for (int i = 0; i < Bs; ++i) buf[i] = normalise(X[(size_t)r * D + b0 + i], inv, fmt);
+      quant_block(buf, Bs, fmt, cb, &scales[sidx]);
+      double sv = orc_scale_value(scales[sidx], fmt);
+      for (int i = 0; i < Bs; ++i) {
+        float deq = (float)(sv * orc_e2m1_value(cb[i])); /* exact: a few bits */
+        res[i] = buf[i] - deq;
+      }
+      quant_block(res, Bs, fmt, cb2, &scales2[sidx]);
+      for (int i = 0; i < Bs; i += 2) {
+        codes[(size_t)r * (D / 2) + (b0 + i) / 2] = (uint8_t)(cb[i] | (cb[i + 1] << 4));
+        codes2[(size_t)r * (D / 2) + (b0 + i) / 2] = (uint8_t)(cb2[i] | (cb2[i + 1] << 4));
+      }
+    }
+  }
+}
+
 /* Quantise V along the key axis (the transposed layout the P.V product
  * contracts over).  V: [Nkv][D].  Keys are padded with zeros up to NkvP, a
  * multiple of the tile.  codes: [D][NkvP/2]; scales: [D][NkvP/Bs]. */
@@ -372,6 +406,7 @@ typedef struct {
   const orc_params* p;
   /* quantised operands for this (b, q-head) and its kv-head */
   const uint8_t *qc, *qs;   /* [Nq][D/2], [Nq][D/Bs] */
+  const uint8_t *qc2, *qs2; /* the residual term of Q, or NULL */
   const uint8_t *kc, *ks;   /* [Nkv][D/2], [Nkv][D/Bs] */
   const uint8_t *vc, *vs;   /* [D][NkvP/2], [D][NkvP/Bs] */
   int NkvP;
@@ -386,7 +421,9 @@ static double code_at(const uint8_t* codes, size_t idx) {
 }
 
 /* FP4 score of (row r, key k): s = fl32(alpha * fl32(dot)), where dot is the
- * exact block-scaled dot product of the codes ("Scores in FP4"). */
+ * exact block-scaled dot product of the codes ("Scores in FP4"); with two Q
+ * terms, dot adds the residual term's block products against the same K
+ * codes before the one rounding. */
 static float fp4_score(const orc_head_ops* h, int r, int k) {
   const orc_params* p = h->p;
   int D = p->D, Bs = p->fmt == ORC_NV ? 16 : 32, nb = D / Bs;
@@ -400,6 +437,15 @@ static float fp4_score(const orc_head_ops* h, int r, int k) {
     double sc = orc_scale_value(h->qs[(size_t)r * nb + b], p->fmt) *
                 orc_scale_value(h->ks[(size_t)k * nb + b], p->fmt);
     dot += sc * part;
+    if (h->qc2) {
+      double part2 = 0.0;
+      for (int i = 0; i < Bs; ++i) {
+        int d = b * Bs + i;
+        part2 += code_at(h->qc2, (size_t)r * D + d) * code_at(h->kc, (size_t)k * D + d);
+      }
+      dot += orc_scale_value(h->qs2[(size_t)r * nb + b], p->fmt) *
+             orc_scale_value(h->ks[(size_t)k * nb + b], p->fmt) * part2;
+    }
   }
   float d32 = (float)dot;
   return (float)(h->alpha * (double)d32);
@@ -697,6 +743,7 @@ typedef struct {
   const float *Q, *K, *V;
   /* quantised operands and per-head scales (from the quantise step) */
   const uint8_t *qc, *qs, *kc, *ks, *vc, *vs;
+  const uint8_t *qc2, *qs2;  /* the residual term of Q, or NULL */
   const float *kbar, *g_v;
   const int32_t* jq;
   /* work list: triplets (b, h, g) */
@@ -733,6 +780,8 @@ static void run_group(orc_job* J, int w) {
   ops.p = p;
   ops.qc = J->qc + bh * p->Nq * (D / 2);
   ops.qs = J->qs + bh * p->Nq * (D / Bs);
+  ops.qc2 = J->qc2 ? J->qc2 + bh * p->Nq * (D / 2) : NULL;
+  ops.qs2 = J->qs2 ? J->qs2 + bh * p->Nq * (D / Bs) : NULL;
   ops.kc = J->kc + bk * p->Nkv * (D / 2);
   ops.ks = J->ks + bk * p->Nkv * (D / Bs);
   ops.vc = J->vc + bk * D * (NkvP / 2);

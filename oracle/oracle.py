@@ -44,7 +44,8 @@ class _Params(C.Structure):
     _fields_ = [("B", C.c_int32), ("Hq", C.c_int32), ("Hkv", C.c_int32), ("Nq", C.c_int32),
                 ("Nkv", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32), ("scale", C.c_float),
                 ("fmt", C.c_int32), ("int_frame", C.c_int32), ("tau", C.c_float),
-                ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32)]
+                ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32),
+                ("q_terms", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -53,7 +54,7 @@ _P = C.c_void_p
 class _Job(C.Structure):
     _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P),
                 ("qc", _P), ("qs", _P), ("kc", _P), ("ks", _P), ("vc", _P), ("vs", _P),
-                ("kbar", _P), ("g_v", _P), ("jq", _P),
+                ("qc2", _P), ("qs2", _P), ("kbar", _P), ("g_v", _P), ("jq", _P),
                 ("groups", _P), ("ngroups", C.c_int),
                 ("hot", _P), ("margin", _P), ("m1", _P), ("l1", _P), ("lam", _P), ("o1", _P),
                 ("shift", _P), ("m2", _P), ("l2", _P), ("o2", _P), ("cr", _P), ("O", _P),
@@ -84,6 +85,7 @@ def lib():
         L.orc_head_scale.argtypes = [C.c_float, C.c_int, _P, _P]
         L.orc_q_scale.argtypes = [C.c_float, C.c_float, C.c_float, C.c_int, _P, _P]
         L.orc_quant_rows.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, C.c_int, _P, _P]
+        L.orc_quant_rows2.argtypes = [_P, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P, _P, _P]
         L.orc_quant_vt.argtypes = [_P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P]
         L.orc_sl.argtypes = [_P]
         L.orc_sl.restype = C.c_float
@@ -120,15 +122,17 @@ class Params:
     eps: float = 0.005
     tile: int = 64
     rg: int = 16
+    q_terms: int = 1        # 2: Q plus its FP4 residual term
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
         assert self.Hq % self.Hkv == 0
+        assert self.q_terms in (1, 2)
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
                        self.scale, self.fmt, self.int_frame, self.tau, self.hoff, self.eps,
-                       self.tile, self.rg)
+                       self.tile, self.rg, self.q_terms)
 
     @property
     def n_tiles(self) -> int:
@@ -262,7 +266,16 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             out["inv_q"][b, h], out["jq"][b, h] = f[0], ji[0]
             qc = np.zeros((Nq, D // 2), np.uint8)
             qs = np.zeros((Nq, D // bs), np.uint8)
-            L.orc_quant_rows(_ptr(Qh), Nq, D, None, C.c_float(f[0]), p.fmt, _ptr(qc), _ptr(qs))
+            if p.q_terms == 2:
+                qc2 = np.zeros((Nq, D // 2), np.uint8)
+                qs2 = np.zeros((Nq, D // bs), np.uint8)
+                L.orc_quant_rows2(_ptr(Qh), Nq, D, C.c_float(f[0]), p.fmt, _ptr(qc), _ptr(qs),
+                                  _ptr(qc2), _ptr(qs2))
+                out.setdefault("qc2", np.zeros((B, Hq, Nq, D // 2), np.uint8))[b, h] = qc2
+                out.setdefault("qs2", np.zeros((B, Hq, Nq, D // bs), np.uint8))[b, h] = qs2
+            else:
+                L.orc_quant_rows(_ptr(Qh), Nq, D, None, C.c_float(f[0]), p.fmt, _ptr(qc),
+                                 _ptr(qs))
             out["qc"][b, h], out["qs"][b, h] = qc, qs
     return out
 
@@ -314,6 +327,8 @@ def run(p: Params, Q, K, V, prep: dict | None = None, groups=None, nthreads: int
     for k in ("qc", "qs", "kc", "ks", "vc", "vs", "kbar", "g_v"):
         setattr(job, k, _ptr(prep[k]))
     job.jq = _ptr(prep["jq"])
+    job.qc2 = _ptr(prep.get("qc2")) if p.q_terms == 2 else None
+    job.qs2 = _ptr(prep.get("qs2")) if p.q_terms == 2 else None
     job.groups, job.ngroups = _ptr(groups), len(groups)
     for k in ("hot", "margin", "m1", "l1", "lam", "o1", "shift", "m2", "l2", "o2", "cr", "O",
               "lse"):

@@ -65,9 +65,11 @@ def quantise_blocks(x: np.ndarray, bs: int = 32):
     return val.reshape(sh)
 
 
-def prepare(Q, K, V, scale: float):
+def prepare(Q, K, V, scale: float, q_terms: int = 1):
     """Per-head scales and dequantised operands (without the per-head factors
-    that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry."""
+    that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry.
+    q_terms=2 adds the quantised residual of Q ("Second hunt": Q2 is the FP4
+    residual Q - Q1 in the same scale) to the dequantised Q."""
     Hq, Nq, D = Q.shape
     Hkv = K.shape[0]
     G = Hq // Hkv
@@ -105,7 +107,12 @@ def prepare(Q, K, V, scale: float):
                     j += 1
             inv_q = np.float32(np.ldexp(np.float64(w), -j))
             qn = np.clip((Qh * inv_q).astype(np.float32), -6, 6)
-            heads.append(dict(qd=quantise_blocks(qn), alpha=2.0 ** j, Qh=Qh))
+            qd = quantise_blocks(qn)
+            if q_terms == 2:
+                # the residual in FP32, quantised as blocks of its own; the sum
+                # of the two dequantised terms is exact in FP64
+                qd = qd + quantise_blocks((qn.astype(np.float64) - qd).astype(np.float32))
+            heads.append(dict(qd=qd, alpha=2.0 ** j, Qh=Qh))
         out.append(dict(kd=kd, vd=vd, g_v=g_v, heads=heads, kbar=kbar, sl=sl))
     return out
 
@@ -163,7 +170,7 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
     return hot, lsum, o, lam
 
 
-def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True):
+def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: int = 1):
     """Frame-free pass 1 for every row group of a batch-1 problem.
 
     Returns dict with hot [Hq, NG, NT], l [Hq, Nq], o [Hq, Nq, D] (o already
@@ -175,7 +182,7 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True):
     off = Nkv - Nq
     nt = -(-Nkv // 64)
     ng = -(-Nq // 16)
-    ops = prepare(Q, K, V, scale)
+    ops = prepare(Q, K, V, scale, q_terms)
     hot = np.zeros((Hq, ng, nt), bool)
     lo = np.zeros((Hq, Nq), np.float32)
     oo = np.zeros((Hq, Nq, D), np.float32)

@@ -1,11 +1,13 @@
 """Pins of the oracle's number formats (E2M1, E8M0 block exponents, UE4M3)
 against brute-force nearest-value searches and the values the APA post prints
 ('Pass 1: FP4 everywhere, with a hot test', format paragraph)."""
+import ctypes as C
 import json
 import os
 
 import numpy as np
 
+from brute_apa import quantise_blocks
 from oracle import oracle as O
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -125,3 +127,42 @@ def test_quant_rows_roundtrip_and_bound():
     assert s2[0, 0] == 127
     vals = [O.e2m1_value((c2[0, i // 2] >> (4 * (i & 1))) & 15) for i in range(32)]
     assert np.array_equal(vals, Y[0])
+
+
+def test_quant_rows2_first_term_and_residual_by_nearest_search():
+    # two-term quantisation ("Second hunt"): the first term is the one-term
+    # quantisation; the second is the nearest-value quantisation of the FP32
+    # residual x' - Q1 with its own block exponent; the residual error never
+    # grows and stays within half the coarsest E2M1 step of the second scale
+    rng = np.random.default_rng(7)
+    X = (rng.standard_normal((40, 128)) * np.exp(rng.standard_normal((40, 1)))).astype(np.float32)
+    X[3, :32] = 0.0                       # an all-zero block
+    inv = np.float32(6.0 / np.abs(X).max())
+    L = O.lib()
+    c1 = np.zeros((40, 64), np.uint8)
+    s1 = np.zeros((40, 4), np.uint8)
+    c2, s2 = np.zeros_like(c1), np.zeros_like(s1)
+    L.orc_quant_rows2(O._ptr(X), 40, 128, C.c_float(inv), O.MX, O._ptr(c1), O._ptr(s1),
+                      O._ptr(c2), O._ptr(s2))
+    r1c, r1s = O.quant_rows(X, inv)
+    assert np.array_equal(c1, r1c) and np.array_equal(s1, r1s)
+
+    def deq(c, sb):
+        lo, hi = c & 15, c >> 4
+        codes = np.stack([lo, hi], -1).reshape(c.shape[0], -1)
+        sign = np.where(codes & 8, -1.0, 1.0)
+        scale = np.ldexp(1.0, sb.astype(np.int64) - 127).repeat(32, axis=1)
+        return sign * MAGS[codes & 7] * scale
+
+    xn = np.clip((X * inv).astype(np.float32), -6, 6)
+    d1 = deq(c1, s1)
+    res = (xn.astype(np.float64) - d1).astype(np.float32)
+    assert np.array_equal(deq(c2, s2), quantise_blocks(res))
+    err1 = np.abs(xn - d1)
+    err2 = np.abs(xn - d1 - deq(c2, s2))
+    assert np.all(err2 <= err1)
+    step2 = np.ldexp(1.0, s2.astype(np.int64) - 127).repeat(32, axis=1)
+    assert np.all(err2 <= step2 + 0.0)
+    assert np.all(c2[3, :16] == 0) and np.all(s2[3, 0] == 0)   # E8M0 floor 2^-127
+    assert np.all(deq(c2, s2)[res == 0] == 0)
+    assert err2.mean() < 0.2 * err1.mean()

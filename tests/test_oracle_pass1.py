@@ -8,7 +8,7 @@ import os
 import numpy as np
 import pytest
 
-from brute_apa import MAGS, brute_apa, nearest_mag_code
+from brute_apa import MAGS, brute_apa, nearest_mag_code, prepare
 from mixed_precision_long_amd.inputs import make_inputs, small_workload
 from oracle import oracle as O
 
@@ -43,6 +43,47 @@ def test_pass1_bitwise_vs_framefree_brute_force(case):
     assert np.array_equal((r["l1"][0] * sc).astype(np.float32), b["l"])
     assert np.array_equal((r["lam"][0] * sc).astype(np.float32), b["lam"])
     assert np.array_equal((r["o1"][0] * sc[..., None]).astype(np.float32), b["o"])
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[4]])
+def test_two_term_q_pass1_bitwise_vs_framefree_brute_force(case):
+    # "Second hunt: which operand is to blame": Q quantised twice (Q1, then the
+    # FP4 residual Q - Q1 in the same scale), both terms against the same K
+    Hq, Hkv, Nq, Nkv, D, eps, causal, seed = case
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, Hq, Hkv, Nq, Nkv, D, causal=causal, scale=w.scale, eps=eps, q_terms=2)
+    r = O.run(p, Q, K, V, pass2=False)
+    b = brute_apa(Q, K, V, eps, w.scale, bool(causal), q_terms=2)
+    sc = _frame_scale(r["m1"][0])
+    assert np.array_equal(r["hot"][0].astype(bool), b["hot"])
+    assert np.array_equal((r["l1"][0] * sc).astype(np.float32), b["l"])
+    assert np.array_equal((r["lam"][0] * sc).astype(np.float32), b["lam"])
+    assert np.array_equal((r["o1"][0] * sc[..., None]).astype(np.float32), b["o"])
+    # the second term changes the scores: a one-term brute force disagrees
+    b1 = brute_apa(Q, K, V, eps, w.scale, bool(causal), q_terms=1)
+    assert not np.array_equal(b1["lam"], b["lam"])
+
+
+def test_two_term_q_brings_scores_closer_to_exact():
+    # the residual term removes most of Q's quantisation error: FP4 scores
+    # against the exact scores of the centred keys (same K codes)
+    w = small_workload(1, 2, 1, 64, 512, 64, seed=21)
+    Q, K, V = make_inputs(w)
+    err = {}
+    for qt in (1, 2):
+        ops = prepare(Q[0], K[0], V[0], w.scale, qt)
+        kv = ops[0]
+        kd = kv["kd"].astype(np.float64)
+        for hd in kv["heads"]:
+            Qh = hd["Qh"].astype(np.float64)
+            # exact Q against the quantised K, in the same normalised units
+            qn = Qh / np.abs(Qh).max()
+            qdn = hd["qd"] / np.abs(hd["qd"]).max()
+            e = np.abs(qdn @ kd.T - qn @ kd.T).mean() / np.abs(qn @ kd.T).mean()
+            err.setdefault(qt, []).append(e)
+    e1, e2 = np.mean(err[1]), np.mean(err[2])
+    assert e2 < 0.25 * e1, (e1, e2)
 
 
 def test_frame_invariance_over_tau_and_H():
