@@ -64,10 +64,15 @@ typedef struct apa_problem {
                                      max(m, c - H); an integer in [0, 64] (32)  */
   int32_t pass1_schedule;         /* APA_SCHED_*: scheduling only, the results
                                      agree up to FP32 summation order (AUTO)   */
+  int32_t q_terms;                /* FP4 terms of Q in pass 1: 1, or 2 (the
+                                     APA page's "Second hunt" fix: Q1, then the
+                                     FP4 residual Q - Q1 in the same per-head
+                                     scale, both against the same K codes;
+                                     D <= 256, else APA_ERR_UNSUPPORTED) (1)  */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
- * fp16, causal, APA_SCHED_AUTO. */
+ * fp16, causal, APA_SCHED_AUTO, one Q term. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 
@@ -92,10 +97,15 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V, 0, 0
  *   q_head   [B][Hq][4]  float       amax_Q, inv_Q, j (as float: alpha = 2^j), 0
  *   q_frame  [B][Hq][NqP] float      c_r = sl * q.kbar, sl = fl32(scale*log2 e)
- *   status   uint32                  bit 0: a non-finite input was seen      */
+ *   status   uint32                  bit 0: a non-finite input was seen
+ *   q2_codes, q2_scales               with q_terms = 2: the residual term of Q,
+ *            laid out as q_codes and q_scales: per 32-channel block, the
+ *            FP32 residual of the normalised values after the first term's
+ *            dequantised values, with its own E8M0 exponent (empty sections
+ *            with one term)                                                  */
 typedef struct apa_fp4_layout {
   size_t q_codes, q_scales, kv_blobs;
-  size_t kbar, kv_head, q_head, q_frame, status, total;
+  size_t kbar, kv_head, q_head, q_frame, status, q2_codes, q2_scales, total;
 } apa_fp4_layout;
 
 apa_status apa_fp4_layout_of(const apa_problem* p, apa_fp4_layout* out);

@@ -10,6 +10,7 @@ struct Geom {
   int B, Hq, Hkv, G, Nq, Nkv, D, NqP, NkvP, NT, NG, W, causal, off, bf16;
   float sl;   // fl32(scale * fl32(log2 e))
   int sched;  // requested pass-1 schedule (APA_SCHED_*)
+  int qterms; // FP4 terms of Q: 1, or 2 with the residual term
 };
 
 // Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the
@@ -22,6 +23,7 @@ struct Geom {
 //                byte (2n + hh) * D/32 + db
 struct Fp4Ptrs {
   uint8_t *q_codes, *q_scales, *kv_blob;
+  uint8_t *q2_codes, *q2_scales;  // the residual term of Q (nullptr with one term)
   float *kbar, *kv_head, *q_head, *q_frame;
   unsigned* status;
 };

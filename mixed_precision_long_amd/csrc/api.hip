@@ -32,6 +32,7 @@ bool valid_problem(const apa_problem* p) {
   if (isnan(p->scale)) return false;
   if (p->Nq > 0 && p->Nkv == 0) return false;
   if (p->pass1_schedule < APA_SCHED_AUTO || p->pass1_schedule > APA_SCHED_TRIPLES) return false;
+  if (p->q_terms != 1 && p->q_terms != 2) return false;
   return true;
 }
 
@@ -52,6 +53,7 @@ Geom geom(const apa_problem* p) {
   const float scale = p->scale > 0.0f ? p->scale : (float)(1.0 / sqrt((double)p->D));
   g.sl = scale * kLog2e32;
   g.sched = p->pass1_schedule;
+  g.qterms = p->q_terms;
   return g;
 }
 
@@ -68,6 +70,9 @@ void layout(const apa_problem* p, apa_fp4_layout* L) {
   L->q_head = take(B * Hq * 4 * 4);
   L->q_frame = take(B * Hq * g.NqP * 4);
   L->status = take(4);
+  const size_t q2 = p->q_terms == 2 ? 1 : 0;
+  L->q2_codes = take(q2 * B * Hq * g.NqP * D / 2);
+  L->q2_scales = take(q2 * B * Hq * g.NqP * D / 32);
   L->total = o;
 }
 
@@ -81,6 +86,8 @@ Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
   f.kbar = (float*)(b + L.kbar); f.kv_head = (float*)(b + L.kv_head);
   f.q_head = (float*)(b + L.q_head); f.q_frame = (float*)(b + L.q_frame);
   f.status = (unsigned*)(b + L.status);
+  f.q2_codes = p->q_terms == 2 ? b + L.q2_codes : nullptr;
+  f.q2_scales = p->q_terms == 2 ? b + L.q2_scales : nullptr;
   return f;
 }
 
@@ -143,6 +150,8 @@ size_t exact_ws(const apa_problem* p, Pass2Args* a, void* base) {
 // D and dtype the device kernels implement for each call
 bool kernels_cover(const apa_problem* p, int call) {
   if (p->fmt != APA_MXFP4) return false;
+  if (p->q_terms == 2 && p->D > 256 && (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1))
+    return false;
   if (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1 || call == APA_CALL_MERGE) return true;
   const int G = p->Hq / p->Hkv;
   if (call == APA_CALL_PASS2 || call == APA_CALL_EXACT)
@@ -179,6 +188,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->tau = 4.0f;
   p->hot_frame_offset = 32.0f;
   p->pass1_schedule = APA_SCHED_AUTO;
+  p->q_terms = 1;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }

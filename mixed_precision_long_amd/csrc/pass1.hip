@@ -269,7 +269,7 @@ __device__ __forceinline__ int unit_index(const Geom& g, const UnitId& id) {
 
 // What a wave needs to walk one unit's tiles.
 template <int D>
-struct Ctx {
+struct CtxBase {
   size_t bhq, bhk;
   int r0, row, d0, d1, dW;
   int tmask;  // tiles t >= tmask need the mask (diagonal, padding keys, rows past Nq)
@@ -284,8 +284,19 @@ struct Ctx {
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
 };
 
+// The context with one Q term, and with two (the FP4 residual of Q as a
+// second B operand of the score MFMAs against the same K operands: "Second
+// hunt: which operand is to blame").
+template <int D, int QT>
+struct Ctx : CtxBase<D> {};
 template <int D>
-__device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs& f,
+struct Ctx<D, 2> : CtxBase<D> {
+  v4i qa2[Tile<D>::NH];
+  int qs2[Tile<D>::NH];
+};
+
+template <int D>
+__device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4Ptrs& f,
                                          const Pass1Out& out, const UnitId& id, int lane,
                                          int dh = 0) {
   constexpr int NH = Tile<D>::NH;
@@ -326,6 +337,41 @@ __device__ __forceinline__ void make_ctx(Ctx<D>& c, const Geom& g, const Fp4Ptrs
   c.vsoff = 66 * D + (2 * n + hh) * ND + dh * NDO;
   c.bits0 = out.bits + (c.bhq * g.NG + (c.r0 >> 4)) * g.W;
   c.bits1 = c.bits0 + g.W;
+}
+
+// S^T with every Q term of the context: the residual term accumulates into
+// the same scores against the same K operands.
+template <int D>
+__device__ __forceinline__ void qk_all(v16f (&acc)[2], const KOps<D>& k, const Ctx<D, 1>& c) {
+  qk<D>(acc, k, c.qa, c.qs);
+}
+template <int D>
+__device__ __forceinline__ void qk_all(v16f (&acc)[2], const KOps<D>& k, const Ctx<D, 2>& c) {
+  constexpr int NH = Tile<D>::NH;
+  qk<D>(acc, k, c.qa, c.qs);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      acc[kb] = mfma4(k.a[kb][h], c.qa2[h], acc[kb], (int)k.s[kb][h >> 1], 2 * (h & 1), c.qs2[h]);
+}
+
+// The residual Q term's operand and E8M0 bytes (with the same head exponent
+// as the first term); nothing with one term.
+template <int D>
+__device__ __forceinline__ void load_q2(Ctx<D, 1>&, const Geom&, const Fp4Ptrs&, int) {}
+template <int D>
+__device__ __forceinline__ void load_q2(Ctx<D, 2>& c, const Geom& g, const Fp4Ptrs& f, int lane) {
+  const int hh = lane >> 5;
+  const int jq = (int)f.q_head[c.bhq * 4 + 2];
+  const uint8_t* qc = f.q2_codes + (c.bhq * g.NqP + c.row) * (D / 2);
+  const uint8_t* qsc = f.q2_scales + (c.bhq * g.NqP + c.row) * (D / 32);
+#pragma unroll
+  for (int h = 0; h < Tile<D>::NH; ++h) {
+    c.qa2[h] = *reinterpret_cast<const v4i*>(qc + 32 * h + 16 * hh);
+    const int sb = (int)qsc[2 * h + hh] + jq;
+    c.qs2[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
+  }
 }
 
 // The accumulated cold state of one row (both lane halves hold the row's
@@ -379,7 +425,7 @@ __host__ __device__ inline int cut_point(int npos, int sched) {
 }
 
 template <int D>
-__device__ __forceinline__ void put_word(const Ctx<D>& c, Words& wd, int w, uint32_t b0,
+__device__ __forceinline__ void put_word(const CtxBase<D>& c, Words& wd, int w, uint32_t b0,
                                          uint32_t b1, int lane) {
   if (w == 0) {
     wd.p00 |= b0;
@@ -437,7 +483,7 @@ struct HeadState {
 
 // masking: causal diagonal, padding keys, rows past Nq (wave-uniform test)
 template <int D>
-__device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const Ctx<D>& c, int t,
+__device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const CtxBase<D>& c, int t,
                                             int hh) {
   const int k0 = t * kTile;
   if (t >= c.tmask) {
@@ -536,7 +582,7 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], int x0, int x1, f
 // when P0 = 0, tile 0.  Lane j builds word w_lo + j; words 0 and wb go to the
 // partial words, the others are stored.
 template <int D>
-__device__ __forceinline__ void assemble_words(const Ctx<D>& c, Words& wd, const lds_u8* vlog,
+__device__ __forceinline__ void assemble_words(const CtxBase<D>& c, Words& wd, const lds_u8* vlog,
                                                int P0, int np, int lane) {
   const int t_hi = c.dW - (P0 > 0 ? P0 : 1) + 1;
   const int t_lo = c.dW - P0 - np + 2;
@@ -584,8 +630,8 @@ __device__ __forceinline__ void assemble_words(const Ctx<D>& c, Words& wd, const
 // return 0.  A head walk publishes its lambda from position nrep_tail on in
 // `pub_out`, in the state frame it had there (the frame the tail's replay ends
 // in).
-template <int D, bool LOG, bool TAIL>
-__device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, Words& wd, int nrep,
+template <int D, bool LOG, bool TAIL, int QT>
+__device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
                                     volatile lds_float* pub_out, lds_u8* vlog, int lane,
@@ -637,7 +683,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
   // blob offset of the K operand fetched last (position i + 1 when position
   // i starts): the V operand of position i + 1 is fetched from it at the end
   // of position i
-  qk<D>(acc, kn, c.qa, c.qs);
+  qk_all<D>(acc, kn, c);
   uint32_t kblob = next_blob(1);
   load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
   load_v(next_blob(0));
@@ -713,7 +759,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
     // this tile's scores are consumed: the next tile's go to the matrix cores
     // behind the row sum and run during the vote and the P V product
     __builtin_amdgcn_sched_barrier(0);
-    qk<D>(acc, kn, c.qa, c.qs);
+    qk_all<D>(acc, kn, c);
     const uint32_t vblob = kblob;
     kblob = next_blob(i + 2);
     load_k<D>(kn, c.blobs, kblob, c.koff, c.ksoff, hh);
@@ -803,7 +849,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D>& c, St<D>& st, W
 // The cold state's outputs in the method's frame m = mf (o * 2^(mo - m) * g_v,
 // with the power of two folded into g_v: exact).
 template <int D>
-__device__ __forceinline__ void store_state(const Geom& g, const Ctx<D>& c, const Pass1Out& out,
+__device__ __forceinline__ void store_state(const Geom& g, const CtxBase<D>& c, const Pass1Out& out,
                                             const St<D>& st, int lane) {
   if (!c.row_ok) return;
   const int hh = lane >> 5;
@@ -829,7 +875,7 @@ __device__ __forceinline__ void store_state(const Geom& g, const Ctx<D>& c, cons
 
 // zero the hot words above each group's diagonal word
 template <int D>
-__device__ __forceinline__ void zero_above(const Geom& g, const Ctx<D>& c, int lane) {
+__device__ __forceinline__ void zero_above(const Geom& g, const CtxBase<D>& c, int lane) {
   if (!c.lead) return;
   for (int w = c.d0 / 32 + 1 + lane; w < g.W; w += 64) c.bits0[w] = 0u;
   if (c.has_g1)
@@ -840,8 +886,8 @@ __device__ __forceinline__ void zero_above(const Geom& g, const Ctx<D>& c, int l
 // decide the recorded groups against the head's lambda, take the P V of those
 // that are hot after all back out of the tail's state (the same FP4 codes with
 // their sign bits set, so exactly what was added), and set their bits.
-template <int D>
-__device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st, Words& tw,
+template <int D, int QT>
+__device__ __forceinline__ void settle(const Geom& g, const Ctx<D, QT>& c, St<D>& st, Words& tw,
                                        const Cand& cr, int ncand, float lam_a, float eps,
                                        int lane) {
   constexpr int ND = Tile<D>::NDO;
@@ -887,7 +933,7 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D>& c, St<D>& st
       v16f acc[2];
       const uint32_t blob = (uint32_t)(t * BLOB);
       load_k<D>(k, c.blobs, blob, c.koff, c.ksoff, hh);
-      qk<D>(acc, k, c.qa, c.qs);
+      qk_all<D>(acc, k, c);
       mask_scores<D>(acc, g, c, t, hh);
       float b0, b1;
       group_maxima(acc, b0, b1);
@@ -983,7 +1029,7 @@ __device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& w
 // its final state at its end; the tail finishes the unit.  Units are numbered
 // (batch, kv-head, 32-row block, head), so the waves of a work group, and the
 // groups of an XCD, stream the same tiles.
-template <int D, bool LOG>
+template <int D, bool LOG, int QT>
 __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
     int sched, int nunits) {
@@ -1043,8 +1089,9 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
   const volatile lds_int* pace_mate = W == 8 ? (const volatile lds_int*)&pace[wave ^ 4] : nullptr;
 
   if (role != kTail) {
-    Ctx<D> c;
+    Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u0), lane, dh);
+    load_q2<D>(c, g, f, lane);
     const int npos = c.dW + 1;
     if (npos < kMinSplit) role = kWhole;  // nothing to cut: its tail wave skips it
     const int h = cut_point(npos, sched);  // head positions [0, h), tail [h, npos)
@@ -1096,8 +1143,9 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
 #pragma nounroll
   for (int k = 0; k < nu; ++k) {
     const int u = u0 + k;
-    Ctx<D> c;
+    Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
+    load_q2<D>(c, g, f, lane);
     const int npos = c.dW + 1;
     int oc = -2;
     if (npos >= kMinSplit) {
@@ -1121,8 +1169,9 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     const int oc = (int)((outcomes >> (10 * k)) & 1023u) - 2;
     if (oc == -2) continue;
     const int u = u0 + k;
-    Ctx<D> c;
+    Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
+    load_q2<D>(c, g, f, lane);
     const int wb = shared_word(c.dW - cut_point(c.dW + 1, sched) + 1);
     float* ho = handoff_of<D>(split, u, cap);
     HeadState<D>& H = hs[slot + k];
@@ -1187,7 +1236,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
 // The re-walk of units whose tail gave up (record full, or a re-base of its
 // frame): the head's state, left in the workspace, walks the tail positions.
 // One wave per unit; the others return at once.
-template <int D, bool LOG>
+template <int D, bool LOG, int QT>
 __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float eps, float tau,
                                                      int hoff, Pass1Out out, uint8_t* split,
                                                      int cap, int sched) {
@@ -1195,8 +1244,9 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   const int lane = threadIdx.x;
   const UnitId id = unit_id(g, blockIdx.x);
   const uint8_t* base = split + (size_t)blockIdx.x * cand_stride(cap, D);
-  Ctx<D> c;
+  Ctx<D, QT> c;
   make_ctx<D>(c, g, f, out, id, lane);
+  load_q2<D>(c, g, f, lane);
   const int npos = c.dW + 1;
   if (npos < kMinSplit) return;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
@@ -1263,9 +1313,9 @@ size_t pass1_ws_bytes(const Geom& g) {
 
 namespace {
 
-template <int D>
-hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
-               const Pass1Out& o, void* ws, hipStream_t s) {
+template <int D, int QT>
+hipError_t run_qt(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                  const Pass1Out& o, void* ws, hipStream_t s) {
   const int nunits = g.B * g.Hkv * (g.NqP / 32) * g.G;
   if (nunits == 0) return hipSuccess;
   const int sched = ws ? pass1_sched(g) : kSchedWhole;
@@ -1277,23 +1327,35 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   const int cap = split ? cand_cap(g, sched) : 0;
   const bool log = g.NT <= kLogTiles;
   if (log)
-    hipLaunchKernelGGL((k_pass1<D, true>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
+    hipLaunchKernelGGL((k_pass1<D, true, QT>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
                        hoff, o, split, cap, sched, nunits);
   else
-    hipLaunchKernelGGL((k_pass1<D, false>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
+    hipLaunchKernelGGL((k_pass1<D, false, QT>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
                        hoff, o, split, cap, sched, nunits);
   if constexpr (kOutSplit<D> == 1) {
     if (!split) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (log)
-      hipLaunchKernelGGL((k_pass1_rewalk<D, true>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+      hipLaunchKernelGGL((k_pass1_rewalk<D, true, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
                          hoff, o, split, cap, sched);
     else
-      hipLaunchKernelGGL((k_pass1_rewalk<D, false>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+      hipLaunchKernelGGL((k_pass1_rewalk<D, false, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
                          hoff, o, split, cap, sched);
   }
   return hipGetLastError();
+}
+
+// One Q term, or two (up to D = 256: at D = 512 the second term's operands
+// do not fit beside the others).
+template <int D>
+hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+               const Pass1Out& o, void* ws, hipStream_t s) {
+  if (g.qterms == 2) {
+    if constexpr (D <= 256) return run_qt<D, 2>(g, f, eps, tau, hoff, o, ws, s);
+    return hipErrorInvalidValue;
+  }
+  return run_qt<D, 1>(g, f, eps, tau, hoff, o, ws, s);
 }
 
 }  // namespace

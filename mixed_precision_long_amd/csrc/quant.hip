@@ -299,6 +299,29 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
   }
   *reinterpret_cast<unsigned*>(crow + c8 / 2) = w;
   if ((c8 & 31) == 0) srow[c8 / 32] = (uint8_t)(e + 127);
+  if (IS_Q && g.qterms == 2) {
+    // the second term: the FP32 residual of each normalised value after the
+    // first term's dequantised value, quantised as a block of its own
+    constexpr float kMag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    float a2 = 0.0f;
+    for (int i = 0; i < 8; ++i) {
+      const unsigned c = (w >> (4 * i)) & 15u;
+      const float d = kMag[c & 7u] * s;  // exact: a power of two times a short value
+      x[i] = x[i] - ((c & 8u) ? -d : d);
+      a2 = fmaxf(a2, fabsf(x[i]));
+    }
+    a2 = fmaxf(a2, __shfl_xor(a2, 1));
+    a2 = fmaxf(a2, __shfl_xor(a2, 2));
+    const int e2 = e8m0_exponent(a2);
+    const float s2 = pow2_scale(e2);
+    unsigned w2 = 0;
+    w2 = cvt_fp4x2(w2, x[0], x[1], s2, 0);
+    w2 = cvt_fp4x2(w2, x[2], x[3], s2, 1);
+    w2 = cvt_fp4x2(w2, x[4], x[5], s2, 2);
+    w2 = cvt_fp4x2(w2, x[6], x[7], s2, 3);
+    *reinterpret_cast<unsigned*>(f.q2_codes + r * (g.D / 2) + c8 / 2) = w2;
+    if ((c8 & 31) == 0) f.q2_scales[r * (g.D / 32) + c8 / 32] = (uint8_t)(e2 + 127);
+  }
   if (IS_Q) {
     // row reduction of the frame constant over the D/8 threads of the row
     for (int o = 1; o < tpr; o <<= 1) cdot += __shfl_xor(cdot, o);

@@ -68,7 +68,14 @@ def fp4_sections(p, fp4_host: np.ndarray) -> dict:
         return np.frombuffer(fp4_host[off:off + count * np.dtype(dtype).itemsize].tobytes(),
                              dtype).reshape(shape)
 
+    extra = {}
+    if p.q_terms == 2:
+        extra = dict(
+            qc2=sec(L.q2_codes, B * Hq * NqP * D // 2, np.uint8, (B, Hq, NqP, D // 2))[:, :, :Nq],
+            qs2=sec(L.q2_scales, B * Hq * NqP * D // 32, np.uint8,
+                    (B, Hq, NqP, D // 32))[:, :, :Nq])
     return dict(
+        **extra,
         qc=sec(L.q_codes, B * Hq * NqP * D // 2, np.uint8, (B, Hq, NqP, D // 2))[:, :, :Nq],
         qs=sec(L.q_scales, B * Hq * NqP * D // 32, np.uint8, (B, Hq, NqP, D // 32))[:, :, :Nq],
         **unblob(sec(L.kv_blobs, B * Hkv * (NkvP // 64) * 68 * D, np.uint8,

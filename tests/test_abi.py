@@ -47,8 +47,14 @@ def test_sizes_and_layout():
     p = prob()
     L = apa.fp4_layout(p)
     offs = [L.q_codes, L.q_scales, L.kv_blobs, L.kbar, L.kv_head, L.q_head, L.q_frame, L.status,
-            L.total]
+            L.q2_codes, L.q2_scales, L.total]
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    # one Q term: the residual sections are empty; two: each as large as Q's
+    assert L.q2_scales == L.q2_codes == L.total
+    L2 = apa.fp4_layout(prob(q_terms=2))
+    assert L2.q2_scales - L2.q2_codes == L.q_scales - L.q_codes
+    assert L2.total - L2.q2_scales >= 24 * 2048 * 4
+    assert [L2.q_codes, L2.kv_blobs, L2.status] == [L.q_codes, L.kv_blobs, L.status]
     assert L.kv_blobs - L.q_scales >= 24 * 2048 * 4
     # one 68*D-byte blob per 64-key tile and kv-head: 8704 B at D = 128
     assert L.kbar - L.kv_blobs == 8 * 1920 * 8704
@@ -70,7 +76,8 @@ def test_sizes_and_layout():
     ("Hkv", 5), ("D", 96), ("tile", 32), ("row_group", 8), ("Nkv", 1000), ("dtype", 7),
     ("is_causal", 2), ("tau", -1.0), ("tau", 40.0), ("hot_frame_offset", 2.5),
     ("hot_frame_offset", 65.0),
-    ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4)])
+    ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4),
+    ("q_terms", 0), ("q_terms", 3)])
 def test_invalid_problems_are_rejected(field, value):
     p = prob(**{field: value})
     assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
@@ -131,6 +138,11 @@ def test_unsupported_variants_say_so():
     nv = prob(fmt=apa.APA_NVFP4)
     assert L.apa_quantize(C.byref(nv), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
         apa.APA_ERR_UNSUPPORTED
+    big2 = prob(D=512, q_terms=2)  # the second Q term stops at D = 256
+    assert L.apa_quantize(C.byref(big2), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
+        apa.APA_ERR_UNSUPPORTED
+    assert L.apa_pass1(C.byref(big2), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                       None) == apa.APA_ERR_UNSUPPORTED
     g5 = prob(Hq=40)  # group of 5 query heads
     assert L.apa_exact(C.byref(g5), FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == \
         apa.APA_ERR_UNSUPPORTED
@@ -152,7 +164,7 @@ def test_problem_defaults():
     p = apa.problem(2, 8, 2, 16, 64, 64)
     assert (p.tile, p.row_group, p.tau, p.hot_frame_offset, p.is_causal) == (64, 16, 4.0, 32.0, 1)
     assert p.scale == 0.0 and p.fmt == apa.APA_MXFP4 and p.dtype == apa.APA_F16
-    assert p.pass1_schedule == apa.SCHED_AUTO
+    assert p.pass1_schedule == apa.SCHED_AUTO and p.q_terms == 1
     assert math.isfinite(p.tau)
 
 

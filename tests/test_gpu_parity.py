@@ -35,16 +35,19 @@ CASES = [
 ]
 
 
-def oracle_for(w, eps, causal, groups=None):
-    p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, causal=causal, scale=w.scale, eps=eps)
+def oracle_for(w, eps, causal, groups=None, q_terms=1):
+    p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, causal=causal, scale=w.scale, eps=eps,
+                 q_terms=q_terms)
     return p
 
 
 def check_quant(g, prep):
     f = g["fp4"]
     assert f["status"] == 0
-    for k in ("qc", "qs", "kc", "ks", "vc", "vs"):
-        assert np.array_equal(f[k], prep[k]), k
+    for k in ("qc", "qs", "kc", "ks", "vc", "vs", "qc2", "qs2"):
+        assert (k in f) == (k in prep), k
+        if k in f:
+            assert np.array_equal(f[k], prep[k]), k
     assert np.array_equal(f["kbar"], prep["kbar"])
     kv = f["kv_head"]
     assert np.array_equal(kv[..., 0], prep["amax_k"])
@@ -131,6 +134,40 @@ def test_apa_matches_oracle(case):
     check_output(g["out"], r["O"])
     fin = np.isfinite(r["lse"])
     assert np.abs(g["lse"][fin] - r["lse"][fin]).max() <= 2e-3
+
+
+# the pages' second-hunt fix: Q quantised twice (the residual term in the same
+# scale), both terms against the same K codes; with and without the split
+# pass-1 schedules
+@pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[3], CASES[4], CASES[7], CASES[8]],
+                         ids=["mixed", "gqa3", "gqa4", "noncausal", "d256", "eps0"])
+@pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])
+def test_two_term_q_matches_oracle(case, split):
+    Hq, Hkv, Nq, Nkv, D, eps, causal, seed = case
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed, causal=causal)
+    Q, K, V = make_inputs(w)
+    po = oracle_for(w, eps, causal, q_terms=2)
+    prep = O.quantize(po, Q, K, V)
+    r = O.run(po, Q, K, V, prep)
+    g = run_gpu(problem_for(w, q_terms=2), Q, K, V, eps, split=split)
+    check_quant(g, prep)
+    mism = check_mask(g["hot"], r)
+    check_cold_state(g, r, mism)
+    check_output(g["out"], r["O"])
+
+
+def test_two_term_q_long3b_sampled_groups():
+    w = WORKLOADS["long3b"]
+    Q, K, V = make_inputs(w, threads=16)
+    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps, q_terms=2)
+    g = run_gpu(problem_for(w, q_terms=2), Q, K, V, w.eps, lam=False)
+    sel = O.all_groups(po)[np.random.default_rng(5).choice(3072, 6, replace=False)]
+    prep = O.quantize(po, Q, K, V)
+    check_quant(g, prep)
+    r = O.run(po, Q, K, V, prep, groups=sel)
+    check_mask(g["hot"], r, groups=sel)
+    rows = np.array([(b, h, gg * 16 + i) for b, h, gg in sel for i in range(16)], np.int32)
+    check_output(g["out"], r["O"], rows)
 
 
 @pytest.mark.parametrize("case", [CASES[2], CASES[4], CASES[6]], ids=["gqa3", "noncausal", "self"])
