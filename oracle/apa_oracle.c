@@ -60,6 +60,7 @@ typedef struct {
   int32_t tile;     /* keys per tile (64) */
   int32_t rg;       /* rows per verdict (16) */
   int32_t q_terms;  /* 1: Q quantised once; 2: plus the FP4 residual term */
+  int32_t k_lsq;    /* 1: K block exponents by least squared error (MX) */
 } orc_params;
 
 /* ------------------------------------------------------------------------ */
@@ -300,6 +301,66 @@ void orc_quant_rows(const float* X, int n, int D, const float* centre, float inv
       quant_block(buf, Bs, fmt, cb, &scales[(size_t)r * (D / Bs) + b0 / Bs]);
       for (int i = 0; i < Bs; i += 2)
         codes[(size_t)r * (D / 2) + (b0 + i) / 2] = (uint8_t)(cb[i] | (cb[i + 1] << 4));
+    }
+  }
+}
+
+/* Least-squares block exponent ("Second hunt": at short context K decided the
+ * worst rows, fixed by picking every block scale from a small set of
+ * candidates by least squared error instead of the nearest one).  MX only.
+ * Candidates: the no-clipping exponent e of orc_e8m0_exp, then e-1 (finer
+ * steps, the largest values clipped at 6) and e+1, each clamped to [-127,
+ * 127]; a later candidate wins only with a strictly smaller error, so ties
+ * keep e.  The error is a float decision taken in FP32 in a fixed order: per
+ * run of 8 consecutive elements d = fl32(x - q), acc = fl32(acc + fl32(d*d))
+ * in element order, then the four run sums as (r0 + r1) + (r2 + r3). */
+static int lsq_block_exp(const float* xs) {
+  double a = 0.0;
+  for (int i = 0; i < 32; ++i) if (fabs((double)xs[i]) > a) a = fabs((double)xs[i]);
+  int e0 = orc_e8m0_exp(a);
+  int cand[3] = {e0, e0 - 1, e0 + 1};
+  int best = e0;
+  float best_err = 0.0f;
+  for (int c = 0; c < 3; ++c) {
+    int e = cand[c] < -127 ? -127 : (cand[c] > 127 ? 127 : cand[c]);
+    float run[4];
+    for (int r = 0; r < 4; ++r) {
+      float acc = 0.0f;
+      for (int i = 8 * r; i < 8 * r + 8; ++i) {
+        float q = (float)(ldexp(1.0, e) * orc_e2m1_value(orc_e2m1_code(ldexp((double)xs[i], -e))));
+        float d = xs[i] - q;
+        float sq = d * d;
+        acc = acc + sq;
+      }
+      run[r] = acc;
+    }
+    float err = (run[0] + run[1]) + (run[2] + run[3]);
+    if (c == 0 || err < best_err) {
+      best_err = err;
+      best = e;
+    }
+  }
+  return best;
+}
+
+/* orc_quant_rows with least-squares block exponents (MX, 32-element blocks). */
+void orc_quant_rows_lsq(const float* X, int n, int D, const float* centre, float inv,
+                        uint8_t* codes, uint8_t* scales) {
+  float buf[32];
+  for (int r = 0; r < n; ++r) {
+    for (int b0 = 0; b0 < D; b0 += 32) {
+      for (int i = 0; i < 32; ++i) {
+        float x = X[(size_t)r * D + b0 + i];
+        float xc = centre ? x - centre[b0 + i] : x;
+        buf[i] = normalise(xc, inv, ORC_MX);
+      }
+      int e = lsq_block_exp(buf);
+      scales[(size_t)r * (D / 32) + b0 / 32] = (uint8_t)(e + 127);
+      for (int i = 0; i < 32; i += 2) {
+        int c0 = orc_e2m1_code(ldexp((double)buf[i], -e));
+        int c1 = orc_e2m1_code(ldexp((double)buf[i + 1], -e));
+        codes[(size_t)r * (D / 2) + (b0 + i) / 2] = (uint8_t)(c0 | (c1 << 4));
+      }
     }
   }
 }

@@ -45,7 +45,7 @@ class _Params(C.Structure):
                 ("Nkv", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32), ("scale", C.c_float),
                 ("fmt", C.c_int32), ("int_frame", C.c_int32), ("tau", C.c_float),
                 ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32),
-                ("q_terms", C.c_int32)]
+                ("q_terms", C.c_int32), ("k_lsq", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -85,6 +85,7 @@ def lib():
         L.orc_head_scale.argtypes = [C.c_float, C.c_int, _P, _P]
         L.orc_q_scale.argtypes = [C.c_float, C.c_float, C.c_float, C.c_int, _P, _P]
         L.orc_quant_rows.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, C.c_int, _P, _P]
+        L.orc_quant_rows_lsq.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, _P, _P]
         L.orc_quant_rows2.argtypes = [_P, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P, _P, _P]
         L.orc_quant_vt.argtypes = [_P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P]
         L.orc_sl.argtypes = [_P]
@@ -123,16 +124,18 @@ class Params:
     tile: int = 64
     rg: int = 16
     q_terms: int = 1        # 2: Q plus its FP4 residual term
+    k_lsq: int = 0          # 1: K block exponents by least squared error (MX)
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
         assert self.Hq % self.Hkv == 0
         assert self.q_terms in (1, 2)
+        assert self.k_lsq in (0, 1) and not (self.k_lsq and self.fmt != MX)
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
                        self.scale, self.fmt, self.int_frame, self.tau, self.hoff, self.eps,
-                       self.tile, self.rg, self.q_terms)
+                       self.tile, self.rg, self.q_terms, self.k_lsq)
 
     @property
     def n_tiles(self) -> int:
@@ -249,8 +252,12 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]
             kc = np.zeros((Nkv, D // 2), np.uint8)
             ks = np.zeros((Nkv, D // bs), np.uint8)
-            L.orc_quant_rows(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]), p.fmt,
-                             _ptr(kc), _ptr(ks))
+            if p.k_lsq:
+                L.orc_quant_rows_lsq(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
+                                     _ptr(kc), _ptr(ks))
+            else:
+                L.orc_quant_rows(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
+                                 p.fmt, _ptr(kc), _ptr(ks))
             out["kc"][b, hk], out["ks"][b, hk] = kc, ks
             vc = np.zeros((D, NkvP // 2), np.uint8)
             vs = np.zeros((D, NkvP // bs), np.uint8)

@@ -166,3 +166,41 @@ def test_quant_rows2_first_term_and_residual_by_nearest_search():
     assert np.all(c2[3, :16] == 0) and np.all(s2[3, 0] == 0)   # E8M0 floor 2^-127
     assert np.all(deq(c2, s2)[res == 0] == 0)
     assert err2.mean() < 0.2 * err1.mean()
+
+
+def test_k_least_squares_block_exponents():
+    # "Second hunt": every K block scale picked from a small set of candidates
+    # by least squared error.  Candidates e (no clipping), e-1, e+1; the
+    # oracle's pick has the smallest FP64 error up to FP32 rounding of the
+    # error sums, its codes are the nearest-value codes at that exponent, and
+    # the search lowers the total error against the nearest rule
+    rng = np.random.default_rng(3)
+    X = (rng.standard_normal((64, 128)) ** 3).astype(np.float32)  # heavy tails
+    inv = np.float32(6.0 / np.abs(X).max())
+    L = O.lib()
+    c = np.zeros((64, 64), np.uint8)
+    s = np.zeros((64, 4), np.uint8)
+    L.orc_quant_rows_lsq(O._ptr(X), 64, 128, None, C.c_float(inv), O._ptr(c), O._ptr(s))
+    cn, sn = O.quant_rows(X, inv)
+    xn = np.clip((X * inv).astype(np.float32), -6, 6).astype(np.float64).reshape(64, 4, 32)
+
+    def sse(e):
+        sc = np.ldexp(1.0, e)[..., None]
+        codes = np.array([[[nearest_even(v) for v in blk] for blk in row] for row in xn / sc])
+        q = np.sign(xn) * MAGS[codes] * sc
+        return ((xn - q) ** 2).sum(-1), q
+
+    e0 = sn.astype(np.int64) - 127
+    errs = {d: sse(e0 + d)[0] for d in (-1, 0, 1)}
+    best = np.minimum(np.minimum(errs[-1], errs[0]), errs[1])
+    el = s.astype(np.int64) - 127
+    assert set(np.unique(el - e0)) <= {-1, 0, 1}
+    got = np.choose(el - e0 + 1, [errs[-1], errs[0], errs[1]])
+    assert np.all(got <= best * (1 + 1e-5) + 1e-30)
+    assert (el != e0).any() and (el == e0).any()
+    _, q = sse(el)
+    lo, hi = c & 15, c >> 4
+    codes = np.stack([lo, hi], -1).reshape(64, 4, 32)
+    dq = np.where(codes & 8, -1.0, 1.0) * MAGS[codes & 7] * np.ldexp(1.0, el)[..., None]
+    assert np.array_equal(dq, q)
+    assert got.sum() < errs[0].sum()
