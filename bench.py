@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--cpu-groups", type=int, default=64)
     ap.add_argument("--no-sweep", action="store_true", help="skip the eps sweep")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip timing the two-term Q variant")
+                    help="skip timing the accuracy variants (two-term Q, least-squares K scales)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "known-size kernel that scales the HBM byte counters)")
@@ -259,40 +259,45 @@ def main():
         print("[bench] exact %.3f ms" % ems, file=sys.stderr, flush=True)
 
     if not args.no_variants and w.D <= 256:
-        # the pages' second-hunt accuracy fix: Q plus its FP4 residual term
-        p2 = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
-                         dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
-                         scale=w.scale, q_terms=2)
-        b2 = apa.alloc(p2)
-        ev2 = []
-        for i in range(2 + 10):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            e[0].record(stream)
-            apa.quantize(p2, q, k, v, b2.fp4, b2.ws_q, stream)
-            apa.pass1(p2, b2.fp4, eps, b2.cold_m, b2.cold_l, b2.cold_o, b2.bits, None,
-                      ws=b2.ws_p1, stream=stream)
-            e[1].record(stream)
-            apa.pass2(p2, q, k, v, b2.fp4, b2.bits, b2.cold_m, b2.cold_l, b2.cold_o, True,
-                      out=b2.out, lse=b2.lse, ws=b2.ws_p2, stream=stream)
-            e[2].record(stream)
-            if i >= 2:
-                ev2.append(e)
-        torch.cuda.synchronize()
-        hot2 = apa_hot_mask(p2, b2.bits)
-        c2, h2, _, _ = cell_counts(hot2, w.Nq, w.Nkv)
-        tt = {"ms": round(float(np.mean([a.elapsed_time(c) for a, _, c in ev2])), 4),
-              "quantize_pass1_ms": round(float(np.mean([a.elapsed_time(b) for a, b, _ in ev2])), 4),
-              "hot_cells": round(h2 / max(c2, 1), 5)}
-        if "apa_vs_exact" in res:
-            o2 = b2.out.float()
-            cos2 = torch.nn.functional.cosine_similarity(o2.reshape(-1, w.D), ef.reshape(-1, w.D),
-                                                         dim=1)
-            tt["vs_exact"] = {"cos_min": round(float(cos2.min()), 6),
-                              "cos_median": round(float(cos2.median()), 6),
-                              "max_abs": round(float((o2 - ef).abs().max()), 5)}
-        res["two_term_q"] = tt
-        del b2
-        print("[bench] two-term Q %.3f ms" % tt["ms"], file=sys.stderr, flush=True)
+        # the pages' second-hunt accuracy fixes: Q plus its FP4 residual term,
+        # K block exponents by least squared error, and both
+        for name, qt, kl in (("two_term_q", 2, 0), ("k_lsq", 1, 1), ("two_term_q_k_lsq", 2, 1)):
+            p2 = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                             dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
+                             scale=w.scale, q_terms=qt, k_lsq=kl)
+            b2 = apa.alloc(p2)
+            ev2 = []
+            for i in range(2 + 10):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+                e[0].record(stream)
+                apa.quantize(p2, q, k, v, b2.fp4, b2.ws_q, stream)
+                e[1].record(stream)
+                apa.pass1(p2, b2.fp4, eps, b2.cold_m, b2.cold_l, b2.cold_o, b2.bits, None,
+                          ws=b2.ws_p1, stream=stream)
+                e[2].record(stream)
+                apa.pass2(p2, q, k, v, b2.fp4, b2.bits, b2.cold_m, b2.cold_l, b2.cold_o, True,
+                          out=b2.out, lse=b2.lse, ws=b2.ws_p2, stream=stream)
+                e[3].record(stream)
+                if i >= 2:
+                    ev2.append(e)
+            torch.cuda.synchronize()
+            hot2 = apa_hot_mask(p2, b2.bits)
+            c2, h2, _, _ = cell_counts(hot2, w.Nq, w.Nkv)
+            kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in ev2])) for a in range(3)]
+            tt = {"ms": round(float(np.mean([x[0].elapsed_time(x[3]) for x in ev2])), 4),
+                  "kernels_ms": {"quantize": round(kms[0], 4), "pass1": round(kms[1], 4),
+                                 "pass2": round(kms[2], 4)},
+                  "hot_cells": round(h2 / max(c2, 1), 5)}
+            if "apa_vs_exact" in res:
+                o2 = b2.out.float()
+                cos2 = torch.nn.functional.cosine_similarity(o2.reshape(-1, w.D),
+                                                             ef.reshape(-1, w.D), dim=1)
+                tt["vs_exact"] = {"cos_min": round(float(cos2.min()), 6),
+                                  "cos_median": round(float(cos2.median()), 6),
+                                  "max_abs": round(float((o2 - ef).abs().max()), 5)}
+            res[name] = tt
+            del b2
+            print("[bench] %s %.3f ms" % (name, tt["ms"]), file=sys.stderr, flush=True)
 
     if w.eps_sweep and not args.no_sweep:
         sweep = {}

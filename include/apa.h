@@ -69,10 +69,16 @@ typedef struct apa_problem {
                                      FP4 residual Q - Q1 in the same per-head
                                      scale, both against the same K codes;
                                      D <= 256, else APA_ERR_UNSUPPORTED) (1)  */
+  int32_t k_scale_lsq;            /* 1: each 32-channel block exponent of K is
+                                     picked from {e, e-1, e+1} (e: the smallest
+                                     that does not clip) by least squared error,
+                                     the APA page's other "Second hunt" fix;
+                                     the error is summed in FP32 in a fixed
+                                     order; 0: the nearest rule (0)           */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
- * fp16, causal, APA_SCHED_AUTO, one Q term. */
+ * fp16, causal, APA_SCHED_AUTO, one Q term, nearest K block exponents. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 

@@ -11,6 +11,7 @@ struct Geom {
   float sl;   // fl32(scale * fl32(log2 e))
   int sched;  // requested pass-1 schedule (APA_SCHED_*)
   int qterms; // FP4 terms of Q: 1, or 2 with the residual term
+  int klsq;   // 1: K block exponents by least squared error
 };
 
 // Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the

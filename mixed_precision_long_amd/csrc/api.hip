@@ -33,6 +33,7 @@ bool valid_problem(const apa_problem* p) {
   if (p->Nq > 0 && p->Nkv == 0) return false;
   if (p->pass1_schedule < APA_SCHED_AUTO || p->pass1_schedule > APA_SCHED_TRIPLES) return false;
   if (p->q_terms != 1 && p->q_terms != 2) return false;
+  if (p->k_scale_lsq != 0 && p->k_scale_lsq != 1) return false;
   return true;
 }
 
@@ -54,6 +55,7 @@ Geom geom(const apa_problem* p) {
   g.sl = scale * kLog2e32;
   g.sched = p->pass1_schedule;
   g.qterms = p->q_terms;
+  g.klsq = p->k_scale_lsq;
   return g;
 }
 
@@ -189,6 +191,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->hot_frame_offset = 32.0f;
   p->pass1_schedule = APA_SCHED_AUTO;
   p->q_terms = 1;
+  p->k_scale_lsq = 0;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }

@@ -236,6 +236,44 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   }
 }
 
+// Least-squares block exponent of a 32-element block held 8 per thread by 4
+// consecutive lanes ("Second hunt": K's block scales picked from a small set
+// of candidates by least squared error).  Candidates: e0 (no clipping), then
+// e0 - 1 and e0 + 1, clamped to [-127, 127]; a later one wins only with a
+// strictly smaller error.  The error is summed in FP32: d*d added in element
+// order inside a lane, then the lanes' sums as (r0 + r1) + (r2 + r3).
+__device__ __forceinline__ int lsq_exponent(const float (&x)[8], int e0) {
+  constexpr float kMag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  int best = e0;
+  float best_err = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int e = e0 + (c == 0 ? 0 : (c == 1 ? -1 : 1));
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    const float s = pow2_scale(e);
+    unsigned w = 0;
+    w = cvt_fp4x2(w, x[0], x[1], s, 0);
+    w = cvt_fp4x2(w, x[2], x[3], s, 1);
+    w = cvt_fp4x2(w, x[4], x[5], s, 2);
+    w = cvt_fp4x2(w, x[6], x[7], s, 3);
+    float acc = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const unsigned code = (w >> (4 * i)) & 15u;
+      const float q = kMag[code & 7u] * s;
+      const float d = x[i] - ((code & 8u) ? -q : q);
+      acc = acc + d * d;
+    }
+    acc = acc + __shfl_xor(acc, 1);
+    acc = acc + __shfl_xor(acc, 2);
+    if (c == 0 || acc < best_err) {
+      best_err = acc;
+      best = e;
+    }
+  }
+  return best;
+}
+
 // Quantise rows along channels (Q, or K - kbar).  Each thread owns 8
 // consecutive channels; 4 threads form one 32-channel block.  Rows in
 // [Nrows, NP) are padding and get zero codes.  For Q it also writes the frame
@@ -280,7 +318,8 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
   a = fmaxf(a, __shfl_xor(a, 1));
   a = fmaxf(a, __shfl_xor(a, 2));
-  const int e = e8m0_exponent(a);
+  int e = e8m0_exponent(a);
+  if (!IS_Q && g.klsq) e = lsq_exponent(x, e);
   const float s = pow2_scale(e);
   unsigned w = 0;
   w = cvt_fp4x2(w, x[0], x[1], s, 0);

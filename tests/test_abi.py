@@ -77,7 +77,7 @@ def test_sizes_and_layout():
     ("is_causal", 2), ("tau", -1.0), ("tau", 40.0), ("hot_frame_offset", 2.5),
     ("hot_frame_offset", 65.0),
     ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4),
-    ("q_terms", 0), ("q_terms", 3)])
+    ("q_terms", 0), ("q_terms", 3), ("k_scale_lsq", 2)])
 def test_invalid_problems_are_rejected(field, value):
     p = prob(**{field: value})
     assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
@@ -164,7 +164,7 @@ def test_problem_defaults():
     p = apa.problem(2, 8, 2, 16, 64, 64)
     assert (p.tile, p.row_group, p.tau, p.hot_frame_offset, p.is_causal) == (64, 16, 4.0, 32.0, 1)
     assert p.scale == 0.0 and p.fmt == apa.APA_MXFP4 and p.dtype == apa.APA_F16
-    assert p.pass1_schedule == apa.SCHED_AUTO and p.q_terms == 1
+    assert p.pass1_schedule == apa.SCHED_AUTO and p.q_terms == 1 and p.k_scale_lsq == 0
     assert math.isfinite(p.tau)
 
 

@@ -35,9 +35,9 @@ CASES = [
 ]
 
 
-def oracle_for(w, eps, causal, groups=None, q_terms=1):
+def oracle_for(w, eps, causal, groups=None, q_terms=1, k_lsq=0):
     p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, causal=causal, scale=w.scale, eps=eps,
-                 q_terms=q_terms)
+                 q_terms=q_terms, k_lsq=k_lsq)
     return p
 
 
@@ -150,6 +150,25 @@ def test_two_term_q_matches_oracle(case, split):
     prep = O.quantize(po, Q, K, V)
     r = O.run(po, Q, K, V, prep)
     g = run_gpu(problem_for(w, q_terms=2), Q, K, V, eps, split=split)
+    check_quant(g, prep)
+    mism = check_mask(g["hot"], r)
+    check_cold_state(g, r, mism)
+    check_output(g["out"], r["O"])
+
+
+# the pages' other second-hunt fix: K block exponents by least squared error,
+# alone and with two Q terms (the pages' full accuracy configuration)
+@pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[4], CASES[7]],
+                         ids=["mixed", "gqa3", "noncausal", "d256"])
+@pytest.mark.parametrize("q_terms", [1, 2])
+def test_k_lsq_matches_oracle(case, q_terms):
+    Hq, Hkv, Nq, Nkv, D, eps, causal, seed = case
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed, causal=causal)
+    Q, K, V = make_inputs(w)
+    po = oracle_for(w, eps, causal, q_terms=q_terms, k_lsq=1)
+    prep = O.quantize(po, Q, K, V)
+    r = O.run(po, Q, K, V, prep)
+    g = run_gpu(problem_for(w, q_terms=q_terms, k_lsq=1), Q, K, V, eps)
     check_quant(g, prep)
     mism = check_mask(g["hot"], r)
     check_cold_state(g, r, mism)
