@@ -285,7 +285,8 @@ struct CtxBase {
 };
 
 // The context with one Q term, and with two (the FP4 residual of Q as a
-// second B operand of the score MFMAs against the same K operands: "Second
+// second B operand of the score MFMAs, beside the first, on the K operands
+// already loaded: "Second
 // hunt: which operand is to blame").
 template <int D, int QT>
 struct Ctx : CtxBase<D> {};
@@ -340,7 +341,7 @@ __device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4
 }
 
 // S^T with every Q term of the context: the residual term accumulates into
-// the same scores against the same K operands.
+// the same scores, on the K operands already loaded.
 template <int D>
 __device__ __forceinline__ void qk_all(v16f (&acc)[2], const KOps<D>& k, const Ctx<D, 1>& c) {
   qk<D>(acc, k, c.qa, c.qs);

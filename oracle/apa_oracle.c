@@ -305,9 +305,9 @@ void orc_quant_rows(const float* X, int n, int D, const float* centre, float inv
   }
 }
 
-/* Least-squares block exponent ("Second hunt": at short context K decided the
- * worst rows, fixed by picking every block scale from a small set of
- * candidates by least squared error instead of the nearest one).  MX only.
+/* Least-squares block exponent (section "Second hunt: which operand is to
+ * blame": for K, a block's scale is the candidate with the smallest squared
+ * quantisation error rather than the nearest-rule one).  MX only.
  * Candidates: the no-clipping exponent e of orc_e8m0_exp, then e-1 (finer
  * steps, the largest values clipped at 6) and e+1, each clamped to [-127,
  * 127]; a later candidate wins only with a strictly smaller error, so ties
@@ -365,13 +365,13 @@ void orc_quant_rows_lsq(const float* X, int n, int D, const float* centre, float
   }
 }
 
-/* Two-term quantisation of rows along channels ("Second hunt: which operand
- * is to blame": Q is quantised twice, the first term as before and the second
- * the FP4 residual of the first, in the same per-head scale).  Per block: the
- * first term's codes and scale as orc_quant_rows; the residual of each
- * normalised value, fl32(x' - dequantised first term), is then quantised as a
- * block of its own (own exponent or UE4M3 scale).  codes2/scales2 have the
- * layout of codes/scales. */
+/* Two-term quantisation of rows along channels (section "Second hunt: which
+ * operand is to blame": a second FP4 term holds what the first one leaves
+ * over, sharing its per-head scale).  Per block: the first term's codes and
+ * scale as orc_quant_rows; the residual of each normalised value, fl32(x' -
+ * dequantised first term), is then quantised as a block of its own (own
+ * exponent or UE4M3 scale).  codes2/scales2 have the layout of
+ * codes/scales. */
 void orc_quant_rows2(const float* X, int n, int D, float inv, int fmt, uint8_t* codes,
                      uint8_t* scales, uint8_t* codes2, uint8_t* scales2) {
   int Bs = fmt == ORC_NV ? 16 : 32;

@@ -68,8 +68,9 @@ def quantise_blocks(x: np.ndarray, bs: int = 32):
 def prepare(Q, K, V, scale: float, q_terms: int = 1):
     """Per-head scales and dequantised operands (without the per-head factors
     that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry.
-    q_terms=2 adds the quantised residual of Q ("Second hunt": Q2 is the FP4
-    residual Q - Q1 in the same scale) to the dequantised Q."""
+    q_terms=2 adds the quantised residual of Q (section "Second hunt": a second
+    FP4 term for what the first leaves over, sharing its scale) to the
+    dequantised Q."""
     Hq, Nq, D = Q.shape
     Hkv = K.shape[0]
     G = Hq // Hkv

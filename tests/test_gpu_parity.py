@@ -136,9 +136,8 @@ def test_apa_matches_oracle(case):
     assert np.abs(g["lse"][fin] - r["lse"][fin]).max() <= 2e-3
 
 
-# the pages' second-hunt fix: Q quantised twice (the residual term in the same
-# scale), both terms against the same K codes; with and without the split
-# pass-1 schedules
+# the pages' second-hunt fix for Q: a second FP4 term for what the first leaves
+# over, sharing its scale; with and without the split pass-1 schedules
 @pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[3], CASES[4], CASES[7], CASES[8]],
                          ids=["mixed", "gqa3", "gqa4", "noncausal", "d256", "eps0"])
 @pytest.mark.parametrize("split", [True, False], ids=["split", "whole"])

@@ -169,11 +169,11 @@ def test_quant_rows2_first_term_and_residual_by_nearest_search():
 
 
 def test_k_least_squares_block_exponents():
-    # "Second hunt": every K block scale picked from a small set of candidates
-    # by least squared error.  Candidates e (no clipping), e-1, e+1; the
-    # oracle's pick has the smallest FP64 error up to FP32 rounding of the
-    # error sums, its codes are the nearest-value codes at that exponent, and
-    # the search lowers the total error against the nearest rule
+    # "Second hunt": each K block scale is the candidate with the smallest
+    # squared error.  Candidates e (no clipping), e-1, e+1; the oracle's pick
+    # has the smallest FP64 error up to FP32 rounding of the error sums, its
+    # codes are the nearest-value codes at that exponent, and the search
+    # lowers the total error against the nearest rule
     rng = np.random.default_rng(3)
     X = (rng.standard_normal((64, 128)) ** 3).astype(np.float32)  # heavy tails
     inv = np.float32(6.0 / np.abs(X).max())

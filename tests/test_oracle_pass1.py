@@ -47,8 +47,8 @@ def test_pass1_bitwise_vs_framefree_brute_force(case):
 
 @pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[4]])
 def test_two_term_q_pass1_bitwise_vs_framefree_brute_force(case):
-    # "Second hunt: which operand is to blame": Q quantised twice (Q1, then the
-    # FP4 residual Q - Q1 in the same scale), both terms against the same K
+    # "Second hunt: which operand is to blame": a second FP4 term of Q for what
+    # the first leaves over, sharing its scale, on the same K codes
     Hq, Hkv, Nq, Nkv, D, eps, causal, seed = case
     w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed)
     Q, K, V = make_inputs(w)
