@@ -51,7 +51,10 @@ enum { APA_SCHED_AUTO = 0, APA_SCHED_WHOLE = 1, APA_SCHED_PAIRS = 2, APA_SCHED_T
 
 /* Problem descriptor.  Fill it with apa_problem_init() and override fields. */
 typedef struct apa_problem {
-  int32_t B, Hq, Hkv, Nq, Nkv, D; /* D in {64, 128, 256}; Hq % Hkv == 0          */
+  int32_t B, Hq, Hkv, Nq, Nkv, D; /* D in {64, 128, 256, 512}; Hq % Hkv == 0;
+                                     apa_pass2 and apa_exact also need the group
+                                     size Hq / Hkv in {1, 2, 3, 4, 6, 8}
+                                     (else APA_ERR_UNSUPPORTED)                  */
   int32_t dtype;                  /* APA_F16 or APA_BF16 (Q, K, V and the output) */
   int32_t is_causal;              /* 1: tail-aligned causal mask; 0: none        */
   float scale;                    /* softmax scale; <= 0 selects 1/sqrt(D)       */
@@ -183,6 +186,16 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
 apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* cold_m,
                      float* cold_l, float* cold_o, uint32_t* hot_bits, float* lambda_out,
                      void* ws, size_t ws_bytes, void* stream);
+
+/* Host-only query of how apa_pass1 with a workspace cuts visit orders (no
+ * device work).  Returns the schedule such a launch runs for p
+ * (APA_SCHED_WHOLE, _PAIRS or _TRIPLES; -1 for an invalid p).  For a visit
+ * order of npos >= 0 positions, *cut (may be NULL) receives the first
+ * position the tail wavefront walks: npos when the order runs whole, else a
+ * value with 32 <= cut <= npos - 8 (the tail first replays positions
+ * [0, 32)).  *records (may be NULL) receives the undecided tail tiles kept
+ * per 32-row block (0 under APA_SCHED_WHOLE). */
+int32_t apa_pass1_split(const apa_problem* p, int32_t npos, int32_t* cut, int32_t* records);
 
 /* a8..a10: pass 2 ("Pass 2: exact FP16 on the hot tiles").  Compacts the hot
  * mask into per-work-group lists of tiles hot for any of its row groups, then

@@ -20,8 +20,8 @@ SCHED_AUTO, SCHED_WHOLE, SCHED_PAIRS, SCHED_TRIPLES = range(4)
 CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
-           "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize", "apa_pass1", "apa_pass2",
-           "apa_merge", "apa_exact"]
+           "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize",
+           "apa_pass1", "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact"]
 
 
 class ApaError(RuntimeError):
@@ -74,6 +74,8 @@ def lib() -> C.CDLL:
         L.apa_status_string.restype = C.c_char_p
         L.apa_last_hip_error.argtypes = []
         L.apa_last_hip_error.restype = C.c_char_p
+        L.apa_pass1_split.argtypes = [P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+        L.apa_pass1_split.restype = C.c_int32
         L.apa_quantize.argtypes = [P, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
@@ -115,6 +117,16 @@ def hotmask_bytes(p: Problem) -> int:
 
 def workspace_bytes(p: Problem, call: int) -> int:
     return lib().apa_workspace_bytes(C.byref(p), call)
+
+
+def pass1_split(p: Problem, npos: int):
+    """(schedule, first tail position, records per block) of apa_pass1 with a
+    workspace for a visit order of npos positions (host-only query)."""
+    cut, rec = C.c_int32(0), C.c_int32(0)
+    s = lib().apa_pass1_split(C.byref(p), int(npos), C.byref(cut), C.byref(rec))
+    if s < 0:
+        raise ApaError(APA_ERR_INVALID_ARG, "apa_pass1_split")
+    return int(s), int(cut.value), int(rec.value)
 
 
 def _check(code: int, what: str):

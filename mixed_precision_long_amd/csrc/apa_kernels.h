@@ -57,6 +57,10 @@ hipError_t launch_quantize(const Geom& g, const void* q, const void* k, const vo
 // long visit orders are cut into a head and a tail walk (two waves per unit,
 // or three heads and one tail wave per three units) plus a re-walk kernel.
 size_t pass1_ws_bytes(const Geom& g);
+// The schedule a pass-1 launch with a workspace runs (APA_SCHED_*), the first
+// tail position of a visit order of npos positions under it (npos: walked
+// whole) and the undecided-tile records kept per unit.
+int pass1_split_info(const Geom& g, int npos, int* cut, int* cap);
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                         const Pass1Out& o, void* ws, hipStream_t s);
 

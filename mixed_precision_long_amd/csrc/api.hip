@@ -269,6 +269,15 @@ apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* 
                                  (hipStream_t)stream));
 }
 
+int32_t apa_pass1_split(const apa_problem* p, int32_t npos, int32_t* cut, int32_t* records) {
+  if (!valid_problem(p) || npos < 0) return -1;
+  int c = npos, r = 0;
+  const int s = pass1_split_info(geom(p), npos, &c, &r);
+  if (cut) *cut = c;
+  if (records) *records = r;
+  return s;
+}
+
 apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const void* v,
                      const void* fp4, const uint32_t* hot_bits, const int32_t* cold_m,
                      const float* cold_l, const float* cold_o, int32_t fuse_merge, void* out,

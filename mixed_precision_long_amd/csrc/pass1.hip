@@ -81,6 +81,7 @@ namespace {
 
 constexpr float kFrameGuard = 80.0f; // largest lead of m over m_o before re-basing
 constexpr int kMinSplit = 64;        // shortest visit order that runs as two waves
+constexpr int kMinTail = 8;          // fewest positions a tail wave walks past its replay
 constexpr int kReplay = 32;          // leading positions the tail wave replays
 constexpr int kCandCap = 512;        // most undecided tail tiles recorded per unit
 
@@ -413,16 +414,21 @@ __device__ __forceinline__ int shared_word(int tb) { return ((tb + 1) & 31) ? (t
 // head waves and one wave that walks the three tails, per three units.
 enum Sched { kSchedWhole = 1, kSchedPairs = 2, kSchedTriples = 3 };
 
-// Where a visit order of npos >= kMinSplit positions is cut: the head walks
-// [0, cut), the tail replays kReplay positions and walks [cut, npos), and its
-// tiles cost a little more (the record keeping).  With a tail per unit the
-// head takes half of npos + kReplay plus about 1.5 %; with one tail wave for
-// three units, three quarters of it (the tail wave then walks three quarter
-// tails and settles three units) plus about 3 %, the share that measured
-// fastest at 2048 x 122880.
-__host__ __device__ inline int cut_point(int npos, int sched) {
-  if (sched == kSchedTriples) return 3 * (npos + kReplay) / 4 + npos / 32;
-  return (npos + kReplay) / 2 + npos / 64;
+// Where a visit order of npos positions is cut: the head walks [0, cut), the
+// tail replays kReplay positions and walks [cut, npos), and its tiles cost a
+// little more (the record keeping).  With a tail per unit the head takes half
+// of npos + kReplay plus about 1.5 %; with one tail wave for three units,
+// three quarters of it (the tail wave then walks three quarter tails and
+// settles three units) plus about 3 %, the share that measured fastest at
+// 2048 x 122880.  A unit is cut only when that leaves the tail at least
+// kMinTail positions (under the triple rule from about 150 positions on);
+// otherwise the result is npos and its head wave walks it whole.  Either way
+// kReplay <= cut <= npos, and cut < npos means a tail of >= kMinTail positions.
+__host__ __device__ inline int split_cut(int npos, int sched) {
+  if (npos < kMinSplit) return npos;
+  const int cut = sched == kSchedTriples ? 3 * (npos + kReplay) / 4 + npos / 32
+                                         : (npos + kReplay) / 2 + npos / 64;
+  return npos - cut >= kMinTail ? cut : npos;
 }
 
 template <int D>
@@ -1023,7 +1029,7 @@ __device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& w
 }
 
 // Units run one wave each, or, with a split workspace, as a head and a tail
-// walk (see cut_point).  With the pair schedule a work group holds two units,
+// walk (see split_cut).  With the pair schedule a work group holds two units,
 // its waves numbered (unit, role); with the triple schedule it holds three,
 // waves 0-2 their heads and wave 3 the tail of each, one after the other.  A
 // head hands its running lambda to its tail through LDS while both walk, and
@@ -1094,8 +1100,8 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     make_ctx<D>(c, g, f, out, unit_id(g, u0), lane, dh);
     load_q2<D>(c, g, f, lane);
     const int npos = c.dW + 1;
-    if (npos < kMinSplit) role = kWhole;  // nothing to cut: its tail wave skips it
-    const int h = cut_point(npos, sched);  // head positions [0, h), tail [h, npos)
+    const int h = split_cut(npos, sched);  // head positions [0, h), tail [h, npos)
+    if (h >= npos) role = kWhole;  // nothing to cut: its tail wave skips it
     St<D> st;
     init_state<D>(st, c.row_ok);
     Words wd = {role == kWhole ? -1 : shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
@@ -1148,9 +1154,9 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
     load_q2<D>(c, g, f, lane);
     const int npos = c.dW + 1;
+    const int h = split_cut(npos, sched);
     int oc = -2;
-    if (npos >= kMinSplit) {
-      const int h = cut_point(npos, sched);
+    if (h < npos) {
       St<D> st;
       init_state<D>(st, c.row_ok);
       Words wd = {shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
@@ -1173,7 +1179,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
     load_q2<D>(c, g, f, lane);
-    const int wb = shared_word(c.dW - cut_point(c.dW + 1, sched) + 1);
+    const int wb = shared_word(c.dW - split_cut(c.dW + 1, sched) + 1);
     float* ho = handoff_of<D>(split, u, cap);
     HeadState<D>& H = hs[slot + k];
     while (__hip_atomic_load(&H.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
@@ -1249,9 +1255,9 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   make_ctx<D>(c, g, f, out, id, lane);
   load_q2<D>(c, g, f, lane);
   const int npos = c.dW + 1;
-  if (npos < kMinSplit) return;
+  const int h = split_cut(npos, sched);
+  if (h >= npos) return;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
-  const int h = cut_point(npos, sched);
   const int wb = shared_word(c.dW - h + 1);
   const float* src = reinterpret_cast<const float*>(base + cand_bytes(cap));
   St<D> st;
@@ -1290,6 +1296,14 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
 // Visit orders shorter than kMinSplit positions leave nothing to cut, the
 // triple schedule needs three head states in LDS (D <= 256), and at D = 512
 // every unit already runs as two waves (one per half of the output channels).
+// Longest tail any visit order of at most NT positions gets under a schedule
+// (0: no order is cut).
+int longest_tail(int NT, int sched) {
+  int m = 0;
+  for (int n = kMinSplit; n <= NT; ++n) m = max(m, n - split_cut(n, sched));
+  return m;
+}
+
 int pass1_sched(const Geom& g) {
   const long units = (long)g.B * g.Hkv * (g.NqP / 32) * g.G;
   const long slots = 1024L * (g.D >= 256 ? 1 : 2);
@@ -1297,12 +1311,14 @@ int pass1_sched(const Geom& g) {
   int s = g.sched;
   if (s != kSchedWhole && s != kSchedPairs && s != kSchedTriples)
     s = 2 * units <= slots ? kSchedPairs : (4 * units <= 3 * slots ? kSchedTriples : kSchedWhole);
+  // a schedule under which no visit order of this problem is cut is the whole one
+  if (s != kSchedWhole && longest_tail(g.NT, s) == 0) s = kSchedWhole;
   return s;
 }
 
-// Records per unit: every tail position of the longest visit order, at most
-// kCandCap.
-int cand_cap(const Geom& g, int sched) { return min(kCandCap, g.NT - cut_point(g.NT, sched)); }
+// Records per unit: every position of the longest tail, at most kCandCap (a
+// tail with more undecided tiles gives up and is walked again).
+int cand_cap(const Geom& g, int sched) { return min(kCandCap, longest_tail(g.NT, sched)); }
 
 }  // namespace
 
@@ -1310,6 +1326,13 @@ size_t pass1_ws_bytes(const Geom& g) {
   const int s = pass1_sched(g);
   if (s == kSchedWhole) return 0;
   return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * cand_stride(cand_cap(g, s), g.D);
+}
+
+int pass1_split_info(const Geom& g, int npos, int* cut, int* cap) {
+  const int s = pass1_sched(g);
+  if (cut) *cut = s == kSchedWhole ? npos : split_cut(npos, s);
+  if (cap) *cap = s == kSchedWhole ? 0 : cand_cap(g, s);
+  return s;
 }
 
 namespace {

@@ -98,39 +98,23 @@ def unpack_bits(p, words: np.ndarray) -> np.ndarray:
 
 
 def pass1_schedule(p) -> int:
-    """The pass-1 schedule a launch with a workspace runs (the library's
-    choice for SCHED_AUTO, restated for the tests)."""
-    units = p.B * p.Hq * (-(-p.Nq // 32))
-    slots = 1024 * (1 if p.D >= 256 else 2)
-    if units == 0 or -(-p.Nkv // 64) < 64 or p.D >= 512:
-        return apa.SCHED_WHOLE
-    s = p.pass1_schedule
-    if s not in (apa.SCHED_WHOLE, apa.SCHED_PAIRS, apa.SCHED_TRIPLES):
-        s = (apa.SCHED_PAIRS if 2 * units <= slots else
-             apa.SCHED_TRIPLES if 4 * units <= 3 * slots else apa.SCHED_WHOLE)
-    if s == apa.SCHED_TRIPLES and p.D > 256:
-        s = apa.SCHED_PAIRS
-    return s
-
-
-def cut_point(npos: int, sched: int) -> int:
-    """First tail position of a visit order of npos positions."""
-    if sched == apa.SCHED_TRIPLES:
-        return 3 * (npos + 32) // 4 + npos // 32
-    return (npos + 32) // 2 + npos // 64
+    """The pass-1 schedule a launch with a workspace runs (the library's own
+    host-side query)."""
+    return apa.pass1_split(p, 0)[0]
 
 
 # Pass-1 workspace of a split problem (the layout of pass1.hip's Cand): per
 # 32-row block the tail's outcome (records kept, or -1: it gave up and the
 # head's state walks the tail again) in the first 4 bytes, then `cap` records
-# of 292 bytes, cap = min(512, the longest tail), rounded up to 256 bytes,
-# then the hand-off state (128 D + 1040 bytes, rounded up to 256).
+# of 292 bytes, rounded up to 256 bytes, then the hand-off state (128 D + 1040
+# bytes, rounded up to 256).  The cut of each visit order and cap come from
+# the library's query.
 def tail_outcomes(p, ws) -> np.ndarray:
     """Outcome of every block whose visit order was cut: number of undecided
     tail tiles decided at the end, or -1 where the tail positions were walked
     again from the head's state."""
     G, NT, nq32 = p.Hq // p.Hkv, -(-p.Nkv // 64), -(-p.Nq // 32)
-    cap = min(512, NT - cut_point(NT, pass1_schedule(p)))
+    cap = apa.pass1_split(p, NT)[2]
     stride = (cap * 292 + 16 + 255) // 256 * 256 + (128 * p.D + 1040 + 255) // 256 * 256
     raw = ws.cpu().numpy()
     out = []
@@ -139,8 +123,8 @@ def tail_outcomes(p, ws) -> np.ndarray:
             for qb in range(nq32):
                 last = min(qb * 32 + 31, p.Nq - 1)
                 dW = min(p.Nkv - 1, last + p.Nkv - p.Nq) // 64 if p.is_causal else NT - 1
-                if dW + 1 < 64:
-                    continue
+                if apa.pass1_split(p, dW + 1)[1] >= dW + 1:
+                    continue  # walked whole by its head wave
                 for gi in range(G):
                     u = ((b * p.Hkv + hk) * nq32 + qb) * G + gi
                     out.append(int(raw[u * stride:u * stride + 4].view(np.int32)[0]))
@@ -192,10 +176,12 @@ def run_exact_gpu(p, Q, K, V, dtype="fp16"):
 
 
 def cosine_rows(a, b):
+    """Per-row cosine; 1 where both rows are zero, -1 (a failure) where exactly
+    one of them is."""
     a = a.reshape(-1, a.shape[-1]).astype(np.float64)
     b = b.reshape(-1, b.shape[-1]).astype(np.float64)
     na, nb = np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
     ok = (na > 0) & (nb > 0)
-    c = np.ones(len(a))
+    c = np.where((na > 0) != (nb > 0), -1.0, 1.0)
     c[ok] = (a[ok] * b[ok]).sum(1) / (na[ok] * nb[ok])
     return c

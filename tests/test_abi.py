@@ -181,12 +181,50 @@ def test_pass1_schedule_sizes_the_workspace():
     assert ws(apa.SCHED_WHOLE) == 0
     assert auto == triples and 0 < triples < pairs
     hand = (128 * 128 + 1040 + 255) // 256 * 256
-    for total, cut in ((pairs, (1920 + 32) // 2 + 1920 // 64),
-                       (triples, 3 * (1920 + 32) // 4 + 1920 // 32)):
-        cap = min(512, 1920 - cut)
+    for total, sched in ((pairs, apa.SCHED_PAIRS), (triples, apa.SCHED_TRIPLES)):
+        p = prob(pass1_schedule=sched)
+        # records: the longest tail of any visit order up to 1920 positions
+        cap = min(512, max(n - apa.pass1_split(p, n)[1] for n in range(1921)))
+        assert cap == apa.pass1_split(p, 1920)[2] and cap > 300
         assert total == units * ((cap * 292 + 16 + 255) // 256 * 256 + hand)
     # few blocks: pairs by default; at D = 512 every unit runs as two waves
     # (one per half of the output channels) and is never cut
     assert ws(apa.SCHED_AUTO, Nq=64) == ws(apa.SCHED_PAIRS, Nq=64)
     for sched in (apa.SCHED_AUTO, apa.SCHED_PAIRS, apa.SCHED_TRIPLES):
         assert ws(sched, D=512, Nq=64) == 0
+
+
+@pytest.mark.parametrize("sched", [apa.SCHED_PAIRS, apa.SCHED_TRIPLES])
+def test_pass1_split_points(sched):
+    """Every visit order is either walked whole or cut so that the head walks
+    at least the 32 positions the tail replays and the tail walks at least 8
+    of its own: never past the end of the order (a cut at or beyond it would
+    visit tiles that do not exist)."""
+    p = prob(pass1_schedule=sched)
+    NT = -(-p.Nkv // 64)
+    s, _, rec = apa.pass1_split(p, 0)
+    assert s == sched and 0 < rec <= 512
+    longest = 0
+    cut_any = False
+    for npos in range(0, NT + 1):
+        s2, cut, rec2 = apa.pass1_split(p, npos)
+        assert (s2, rec2) == (s, rec)
+        if cut == npos:
+            assert npos < 64 or sched == apa.SCHED_TRIPLES, npos
+            continue
+        cut_any = True
+        assert 32 <= cut <= npos - 8, (npos, cut)
+        longest = max(longest, npos - cut)
+    assert cut_any and rec == min(512, longest)
+    # under the triple rule short orders (64 .. 108 positions among them) run whole
+    if sched == apa.SCHED_TRIPLES:
+        assert all(apa.pass1_split(p, n)[1] == n for n in range(64, 109))
+
+
+def test_pass1_split_whole_without_tails():
+    # a problem whose every order is too short to cut runs one wave per block
+    p = prob(Nkv=4000)
+    assert apa.pass1_split(p, 60) == (apa.SCHED_WHOLE, 60, 0)
+    assert apa.pass1_split(prob(D=512), 1000) == (apa.SCHED_WHOLE, 1000, 0)
+    with pytest.raises(apa.ApaError):
+        apa.pass1_split(prob(D=96), 10)

@@ -75,23 +75,30 @@ def check_mask(ghot, r, groups=None):
     return mism
 
 
-def check_cold_state(g, r, mism):
+def check_cold_state(g, r, mism, groups=None):
     """Pass 1's cold state in frame-free units (l 2^m, o / l) on the row groups
-    whose verdicts all agree with the oracle's."""
+    whose verdicts all agree with the oracle's (only the listed groups when
+    `groups` is given).  A row that is empty on one side and not on the other
+    fails, and so does a wrong total mass (l 2^m is scale-sensitive where the
+    per-row cosine of the output is not)."""
     B, Hq, Nq = g["l"].shape
     NG = -(-Nq // 16)
     gm = np.where(g["m"] == np.iinfo(np.int32).min, np.nan, g["m"].astype(np.float64))
     ok_rows = np.zeros((B, Hq, Nq), bool)
-    for b in range(B):
-        for h in range(Hq):
-            for gg in range(NG):
-                if not mism[b, h, gg].any():
-                    ok_rows[b, h, 16 * gg:16 * gg + 16] = True
-    both = ok_rows & (g["l"] > 0) & (r["l1"] > 0)
+    todo = ([(b, h, gg) for b in range(B) for h in range(Hq) for gg in range(NG)]
+            if groups is None else [tuple(x) for x in groups])
+    for b, h, gg in todo:
+        if not mism[b, h, gg].any():
+            ok_rows[b, h, 16 * gg:16 * gg + 16] = True
+    assert ok_rows.any()
+    gl_pos = g["l"] > 0
+    ol_pos = np.nan_to_num(r["l1"], nan=0.0) > 0
+    assert np.array_equal(gl_pos[ok_rows], ol_pos[ok_rows]), "a cold state is missing or extra"
+    both = ok_rows & gl_pos & ol_pos
     if both.any():
         gl = g["l"] * np.exp2(np.nan_to_num(gm))
         ol = r["l1"] * np.exp2(np.nan_to_num(r["m1"]))
-        assert np.allclose(gl[both], ol[both], rtol=1e-3)
+        assert np.allclose(gl[both], ol[both], rtol=1e-3), np.abs(gl[both] / ol[both] - 1).max()
         gco = g["o"] / g["l"][..., None]
         oco = r["o1"] / r["l1"][..., None]
         assert np.abs(gco[both] - oco[both]).max() <= 1e-3
@@ -200,8 +207,14 @@ def test_exact_matches_fp64(case):
     assert np.abs(gl.reshape(-1) - lse).max() <= 1e-3
 
 
-def test_standalone_merge_equals_fused():
-    w = small_workload(1, 6, 2, 200, 1500, 128, seed=2)
+@pytest.mark.parametrize("shape", [(6, 2, 200, 1500, 128), (4, 1, 128, 4096, 128),
+                                   (4, 1, 96, 4096, 256)],
+                         ids=["one_split", "four_splits", "d256_splits"])
+def test_standalone_merge_equals_fused(shape):
+    """The fused merge in the pass-2 epilogue (one key split) or in the split
+    combine (several) equals pass 2's hot state merged by apa_merge, bit for
+    bit."""
+    w = small_workload(1, *shape, seed=2)
     Q, K, V = make_inputs(w)
     p = problem_for(w)
     a = run_gpu(p, Q, K, V, 0.02, fused=True)
@@ -233,10 +246,14 @@ def _sampled(name, ngroups, seed=0, delta=None):
     prep = O.quantize(po, Q, K, V)
     check_quant(g, prep)
     r = O.run(po, Q, K, V, prep, groups=sel)
-    check_mask(g["hot"], r, groups=sel)
+    mism = check_mask(g["hot"], r, groups=sel)
+    check_cold_state(g, r, mism, groups=sel)
     rows = np.array([(b, h, gg * 16 + i) for b, h, gg in sel for i in range(16)
                      if gg * 16 + i < w.Nq], np.int32)
     check_output(g["out"], r["O"], rows, dtype=w.dtype)
+    lg = g["lse"][rows[:, 0], rows[:, 1], rows[:, 2]]
+    lo = r["lse"][rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.abs(lg - lo).max() <= 2e-3
 
 
 def test_short3b_sampled_groups():

@@ -115,3 +115,21 @@ def test_split_path_inputs(case, sched):
     w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed, causal=causal)
     Q, K, V = make_inputs(w)
     run_case(w, eps, Q, K, V, sched)
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_split_orders_near_the_cut(sched):
+    """Visit orders of 61 to 180 positions, diffuse gauss rows without a sink:
+    orders the cut rule leaves without a tail of 8 positions run whole, the
+    rest are cut inside the order.  Regression: an earlier rule cut orders of
+    64 to 108 positions at or past their end under the triple schedule; the
+    tail then visited tile 0 a second time and tiles before it, which the
+    strict cold-state check (no missing or extra mass) sees."""
+    w = small_workload(1, 2, 1, 7680, 11520, 64, mode="gauss", delta=0.0, seed=40)
+    p = problem_for(w, sched=sched)
+    cuts = [apa.pass1_split(p, n)[1] for n in range(61, 181)]
+    assert all(c == n or 32 <= c <= n - 8 for c, n in zip(cuts, range(61, 181)))
+    assert any(c < n for c, n in zip(cuts, range(61, 181)))
+    Q, K, V = make_inputs(w)
+    g = run_case(w, 0.02, Q, K, V, sched)
+    assert len(g["tail"]) > 0
