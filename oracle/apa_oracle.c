@@ -35,7 +35,13 @@
  * the cold-verdict safety bound; frame invariance over (tau, H); the NV-mode
  * sink bug; the tile order against hand-derived orders; the two-term Q
  * quantisation against a nearest-value search of the residual, and its scores
- * against the brute force.  Parity unpinned: the
+ * against the brute force; the per-cell margin bitwise against the brute
+ * force's own l and lambda; the key mean against an exactly rounded sum in
+ * a shuffled order; the reports (true share of each cold tile, hot and cold
+ * parts of the reference output) against a numpy softmax and their closed
+ * forms; the per-operand emulation against the brute force with the same
+ * operands quantised and, with none, against FP64 attention; the sliding
+ * window against the brute force and a masked softmax.  Parity unpinned: the
  * pages' measured numbers (they come from activation dumps that are not
  * available), listed as such in the design notes.
  */
@@ -61,7 +67,24 @@ typedef struct {
   int32_t rg;       /* rows per verdict (16) */
   int32_t q_terms;  /* 1: Q quantised once; 2: plus the FP4 residual term */
   int32_t k_lsq;    /* 1: K block exponents by least squared error (MX) */
+  int32_t qmask;    /* which of pass 1's FP4 roundings apply: ORC_QUANT_Q | _K | _V | _P
+                       (all: the method; fewer: the per-operand emulation) */
+  int32_t window;   /* > 0: causal sliding window of this many keys; 0: full causal */
 } orc_params;
+
+/* Per-operand switches of pass 1's FP4 roundings ("Second hunt: which operand
+ * is to blame": the page finds the guilty operand by emulating pass 1 with one
+ * quantisation at a time).  An operand whose bit is clear enters pass 1 at its
+ * exact value, in the same normalised units (Q: q * inv_q, K: (k - kbar) *
+ * inv_k, V: v * inv_v, each product exact in FP64, no clamp), and P at its
+ * exact value 2^(s - m) (FP64 exp2).  Everything else -- the FP32 scores,
+ * frames, sums and state updates -- is the method's arithmetic unchanged, so
+ * with every bit set this is the oracle itself. */
+#define ORC_QUANT_Q 1
+#define ORC_QUANT_K 2
+#define ORC_QUANT_V 4
+#define ORC_QUANT_P 8
+#define ORC_QUANT_ALL 15
 
 /* ------------------------------------------------------------------------ */
 /* Formats                                                                   */
@@ -430,32 +453,48 @@ float orc_sl(const orc_params* p) { return softmax_sl(p); }
 
 static int n_tiles(const orc_params* p) { return (p->Nkv + p->tile - 1) / p->tile; }
 
-/* Key k is visible from query row r (tail-aligned causal mask). */
+/* Key k is visible from query row r: tail-aligned causal mask (row r sees
+ * k <= r + Nkv - Nq), and with a sliding window of W keys only the W most
+ * recent of those, k > r + Nkv - Nq - W ("What else is in the box": sliding
+ * window). */
 static int visible(const orc_params* p, int r, int k) {
   if (k >= p->Nkv) return 0;
   if (!p->causal) return 1;
-  return k <= r + (p->Nkv - p->Nq);
+  int last = r + (p->Nkv - p->Nq);
+  if (k > last) return 0;
+  return p->window <= 0 || k > last - p->window;
 }
 
 /* Visit order of one row group: tile 0 (the sink) first, then from the causal
  * diagonal backwards, "0, d, d-1, ..., 1", where d is the tile holding the
- * last key visible to the group's last row ("Tile order").  Returns the
- * count. */
+ * last key visible to the group's last row ("Tile order").  With a sliding
+ * window whose keys start past tile 0 for the group's first row (first
+ * visible tile lo > 0), the sink is not visible and the order is the
+ * diagonal backwards alone, "d, d-1, ..., lo".  Returns the count. */
 int orc_visit_order(const orc_params* p, int g, int* order) {
   int NT = n_tiles(p);
+  int first = g * p->rg;
   int last = (g + 1) * p->rg - 1;
   if (last > p->Nq - 1) last = p->Nq - 1;
-  int d;
+  int d, lo = 0;
   if (p->causal) {
     int kmax = last + (p->Nkv - p->Nq);
     if (kmax > p->Nkv - 1) kmax = p->Nkv - 1;
     d = kmax / p->tile;
+    if (p->window > 0) {
+      int kmin = first + (p->Nkv - p->Nq) - p->window + 1;
+      lo = kmin > 0 ? kmin / p->tile : 0;
+    }
   } else {
     d = NT - 1;
   }
   int n = 0;
-  order[n++] = 0;
-  for (int t = d; t >= 1; --t) order[n++] = t;
+  if (lo == 0) {
+    order[n++] = 0;
+    for (int t = d; t >= 1; --t) order[n++] = t;
+  } else {
+    for (int t = d; t >= lo; --t) order[n++] = t;
+  }
   return n;
 }
 
@@ -473,6 +512,9 @@ typedef struct {
   int NkvP;
   double alpha;             /* 2^j */
   float g_v;
+  /* the unquantised operands (per-operand emulation, see ORC_QUANT_*) */
+  const float *Qh, *Kh, *Vh, *kbar; /* [Nq][D], [Nkv][D], [Nkv][D], [D] */
+  float inv_q, inv_k, inv_v;
 } orc_head_ops;
 
 static double code_at(const uint8_t* codes, size_t idx) {
@@ -481,13 +523,42 @@ static double code_at(const uint8_t* codes, size_t idx) {
   return orc_e2m1_value(c);
 }
 
+/* Q and K in normalised units at (row or key, channel d): the dequantised
+ * FP4 value, or, with its quantisation switched off, the exact value. */
+static double q_value(const orc_head_ops* h, int r, int d) {
+  const orc_params* p = h->p;
+  int D = p->D, Bs = p->fmt == ORC_NV ? 16 : 32, nb = D / Bs;
+  if (!(p->qmask & ORC_QUANT_Q)) return (double)h->Qh[(size_t)r * D + d] * (double)h->inv_q;
+  double v = orc_scale_value(h->qs[(size_t)r * nb + d / Bs], p->fmt) *
+             code_at(h->qc, (size_t)r * D + d);
+  if (h->qc2)
+    v += orc_scale_value(h->qs2[(size_t)r * nb + d / Bs], p->fmt) *
+         code_at(h->qc2, (size_t)r * D + d);
+  return v;
+}
+static double k_value(const orc_head_ops* h, int k, int d) {
+  const orc_params* p = h->p;
+  int D = p->D, Bs = p->fmt == ORC_NV ? 16 : 32, nb = D / Bs;
+  if (!(p->qmask & ORC_QUANT_K))
+    return ((double)h->Kh[(size_t)k * D + d] - (double)h->kbar[d]) * (double)h->inv_k;
+  return orc_scale_value(h->ks[(size_t)k * nb + d / Bs], p->fmt) *
+         code_at(h->kc, (size_t)k * D + d);
+}
+
 /* FP4 score of (row r, key k): s = fl32(alpha * fl32(dot)), where dot is the
  * exact block-scaled dot product of the codes ("Scores in FP4"); with two Q
  * terms, dot adds the residual term's block products against the same K
- * codes before the one rounding. */
+ * codes before the one rounding.  With Q or K unquantised (emulation), dot
+ * is the FP64 sum over channels of the two operands' values. */
 static float fp4_score(const orc_head_ops* h, int r, int k) {
   const orc_params* p = h->p;
   int D = p->D, Bs = p->fmt == ORC_NV ? 16 : 32, nb = D / Bs;
+  if ((p->qmask & (ORC_QUANT_Q | ORC_QUANT_K)) != (ORC_QUANT_Q | ORC_QUANT_K)) {
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += q_value(h, r, d) * k_value(h, k, d);
+    float d32 = (float)dot;
+    return (float)(h->alpha * (double)d32);
+  }
   double dot = 0.0;
   for (int b = 0; b < nb; ++b) {
     double part = 0.0;
@@ -512,9 +583,12 @@ static float fp4_score(const orc_head_ops* h, int r, int k) {
   return (float)(h->alpha * (double)d32);
 }
 
-/* Dequantised V' (without the per-head g_v) at (key k, channel d). */
+/* Dequantised V' (without the per-head g_v) at (key k, channel d); with V's
+ * quantisation switched off, the exact v * inv_v (padding keys: 0). */
 static double vprime(const orc_head_ops* h, int k, int d) {
   int Bs = h->p->fmt == ORC_NV ? 16 : 32;
+  if (!(h->p->qmask & ORC_QUANT_V))
+    return k < h->p->Nkv ? (double)h->Vh[(size_t)k * h->p->D + d] * (double)h->inv_v : 0.0;
   double sc = orc_scale_value(h->vs[(size_t)d * (h->NkvP / Bs) + k / Bs], h->p->fmt);
   return sc * code_at(h->vc, (size_t)d * h->NkvP + k);
 }
@@ -595,7 +669,13 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
           double y = (double)s[i * T + kk] - mc[i];
           if (y > ymax) ymax = y;
         }
-        if (p->fmt == ORC_MX) {
+        if (!(p->qmask & ORC_QUANT_P)) {
+          /* emulation: P at its exact value */
+          for (int kk = q0; kk < q0 + Bp; ++kk) {
+            double y = (double)s[i * T + kk] - mc[i];
+            ph[i * T + kk] = (y == -INFINITY || mc[i] == -INFINITY) ? 0.0 : exp2(y);
+          }
+        } else if (p->fmt == ORC_MX) {
           int E = p_group_exp(ymax);
           for (int kk = q0; kk < q0 + Bp; ++kk) {
             double y = (double)s[i * T + kk] - mc[i];
@@ -807,6 +887,7 @@ typedef struct {
   const uint8_t *qc2, *qs2;  /* the residual term of Q, or NULL */
   const float *kbar, *g_v;
   const int32_t* jq;
+  const float *inv_q, *inv_k, *inv_v; /* per-head scales (unquantised operands) */
   /* work list: triplets (b, h, g) */
   const int32_t* groups;
   int ngroups;
@@ -850,6 +931,13 @@ static void run_group(orc_job* J, int w) {
   ops.NkvP = NkvP;
   ops.alpha = ldexp(1.0, J->jq[bh]);
   ops.g_v = J->g_v[bk];
+  ops.Qh = J->Q + bh * p->Nq * D;
+  ops.Kh = J->K + bk * p->Nkv * D;
+  ops.Vh = J->V + bk * p->Nkv * D;
+  ops.kbar = J->kbar + bk * D;
+  ops.inv_q = J->inv_q[bh];
+  ops.inv_k = J->inv_k[bk];
+  ops.inv_v = J->inv_v[bk];
   int r0 = g * R;
   orc_p1_out out;
   out.hot = J->hot + (bh * NG + g) * NT;
@@ -956,3 +1044,115 @@ int orc_exact_rows(const orc_params* p, const float* Q, const float* K, const fl
   pthread_mutex_destroy(&J.mu);
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Reports against exact attention (FP64)                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Where one row's exact softmax mass and output sit relative to a hot mask:
+ * the exact FP64 weights w_k = exp(scale q.k - max) / L over the visible keys,
+ * summed per key tile; hot_share and cold_share are the mass on the tiles the
+ * mask marks hot and not hot; cold_tile_max is the largest mass of a single
+ * tile not marked hot, at tile *cold_tile_arg (-1 if none) -- the "true share
+ * of a cold tile" the page compares with eps ("Pass 1", on safe cold
+ * verdicts); O_hot and O_cold are the reference output's parts over the hot
+ * and the other keys (the diagnostic split of "The bug"), O_ref their sum
+ * computed directly, lse the natural log-sum-exp.  hot: [NT] bytes of the
+ * row's 16-row group. */
+void orc_report_row(const orc_params* p, const float* Qh, const float* Kh, const float* Vh,
+                    const uint8_t* hot, int r, double* O_ref, double* O_hot, double* O_cold,
+                    double* lse, double* hot_share, double* cold_share, double* cold_tile_max,
+                    int* cold_tile_arg) {
+  int D = p->D, T = p->tile, NT = n_tiles(p);
+  double scale = p->scale > 0.0f ? (double)p->scale : 1.0 / sqrt((double)D);
+  const float* q = Qh + (size_t)r * D;
+  double* sc = (double*)malloc((size_t)(p->Nkv > 0 ? p->Nkv : 1) * sizeof(double));
+  double mx = -INFINITY;
+  for (int k = 0; k < p->Nkv; ++k) {
+    double v = -INFINITY;
+    if (visible(p, r, k)) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d) dot += (double)q[d] * (double)Kh[(size_t)k * D + d];
+      v = scale * dot;
+    }
+    sc[k] = v;
+    if (v > mx) mx = v;
+  }
+  for (int d = 0; d < D; ++d) O_ref[d] = O_hot[d] = O_cold[d] = 0.0;
+  *hot_share = *cold_share = *cold_tile_max = 0.0;
+  *cold_tile_arg = -1;
+  if (mx == -INFINITY) { *lse = -INFINITY; free(sc); return; }
+  double L = 0.0;
+  for (int k = 0; k < p->Nkv; ++k)
+    if (sc[k] != -INFINITY) L += exp(sc[k] - mx);
+  for (int t = 0; t < NT; ++t) {
+    double tile_mass = 0.0;
+    for (int k = t * T; k < p->Nkv && k < (t + 1) * T; ++k) {
+      if (sc[k] == -INFINITY) continue;
+      double w = exp(sc[k] - mx) / L;
+      tile_mass += w;
+      for (int d = 0; d < D; ++d) {
+        double wv = w * (double)Vh[(size_t)k * D + d];
+        O_ref[d] += wv;
+        if (hot[t]) O_hot[d] += wv; else O_cold[d] += wv;
+      }
+    }
+    if (hot[t]) {
+      *hot_share += tile_mass;
+    } else {
+      *cold_share += tile_mass;
+      if (tile_mass > *cold_tile_max) { *cold_tile_max = tile_mass; *cold_tile_arg = t; }
+    }
+  }
+  *lse = mx + log(L);
+  free(sc);
+}
+
+typedef struct {
+  const orc_params* p;
+  const float *Q, *K, *V;
+  const uint8_t* hot;   /* [B][Hq][NG][NT] */
+  const int32_t* rows;  /* [nrows][3] (b, q-head, r) */
+  int nrows;
+  double *O_ref, *O_hot, *O_cold; /* [nrows][D] */
+  double *lse, *hot_share, *cold_share, *cold_tile_max; /* [nrows] */
+  int32_t* cold_tile_arg;
+  int next;
+  pthread_mutex_t mu;
+} orc_report_job;
+
+static void* report_worker(void* arg) {
+  orc_report_job* J = (orc_report_job*)arg;
+  const orc_params* p = J->p;
+  int D = p->D, G = p->Hq / p->Hkv, NT = n_tiles(p), NG = (p->Nq + p->rg - 1) / p->rg;
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int w = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (w >= J->nrows) break;
+    int b = J->rows[3 * w], h = J->rows[3 * w + 1], r = J->rows[3 * w + 2];
+    size_t bh = (size_t)b * p->Hq + h, bk = (size_t)b * p->Hkv + h / G;
+    orc_report_row(p, J->Q + bh * p->Nq * D, J->K + bk * p->Nkv * D, J->V + bk * p->Nkv * D,
+                   J->hot + (bh * NG + r / p->rg) * NT, r, J->O_ref + (size_t)w * D,
+                   J->O_hot + (size_t)w * D, J->O_cold + (size_t)w * D, J->lse + w,
+                   J->hot_share + w, J->cold_share + w, J->cold_tile_max + w,
+                   J->cold_tile_arg + w);
+  }
+  return NULL;
+}
+
+/* orc_report_row for a list of rows on nthreads threads (each row computed
+ * by one thread: results do not depend on the thread count). */
+int orc_report_rows(orc_report_job* J, int nthreads) {
+  J->next = 0;
+  pthread_mutex_init(&J->mu, NULL);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  pthread_t th[256];
+  for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, report_worker, J);
+  for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+  pthread_mutex_destroy(&J->mu);
+  return 0;
+}
+
+size_t orc_report_job_size(void) { return sizeof(orc_report_job); }

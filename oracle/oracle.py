@@ -27,6 +27,9 @@ _SRC = os.path.join(_HERE, "apa_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 MX, NV = 0, 1
+# per-operand switches of pass 1's FP4 roundings (see apa_oracle.c, ORC_QUANT_*)
+QUANT_Q, QUANT_K, QUANT_V, QUANT_P = 1, 2, 4, 8
+QUANT_ALL = 15
 
 
 def build(force: bool = False) -> str:
@@ -45,7 +48,8 @@ class _Params(C.Structure):
                 ("Nkv", C.c_int32), ("D", C.c_int32), ("causal", C.c_int32), ("scale", C.c_float),
                 ("fmt", C.c_int32), ("int_frame", C.c_int32), ("tau", C.c_float),
                 ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32),
-                ("q_terms", C.c_int32), ("k_lsq", C.c_int32)]
+                ("q_terms", C.c_int32), ("k_lsq", C.c_int32), ("qmask", C.c_int32),
+                ("window", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -55,11 +59,19 @@ class _Job(C.Structure):
     _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P),
                 ("qc", _P), ("qs", _P), ("kc", _P), ("ks", _P), ("vc", _P), ("vs", _P),
                 ("qc2", _P), ("qs2", _P), ("kbar", _P), ("g_v", _P), ("jq", _P),
+                ("inv_q", _P), ("inv_k", _P), ("inv_v", _P),
                 ("groups", _P), ("ngroups", C.c_int),
                 ("hot", _P), ("margin", _P), ("m1", _P), ("l1", _P), ("lam", _P), ("o1", _P),
                 ("shift", _P), ("m2", _P), ("l2", _P), ("o2", _P), ("cr", _P), ("O", _P),
                 ("lse", _P), ("do_pass2", C.c_int), ("next", C.c_int),
                 ("mu", C.c_int64 * 8)]
+
+
+class _ReportJob(C.Structure):
+    _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P), ("hot", _P), ("rows", _P),
+                ("nrows", C.c_int), ("O_ref", _P), ("O_hot", _P), ("O_cold", _P), ("lse", _P),
+                ("hot_share", _P), ("cold_share", _P), ("cold_tile_max", _P),
+                ("cold_tile_arg", _P), ("next", C.c_int), ("mu", C.c_int64 * 8)]
 
 
 _lib = None
@@ -95,6 +107,9 @@ def lib():
         L.orc_exact_rows.argtypes = [_P, _P, _P, _P, _P, C.c_int, _P, _P, C.c_int]
         L.orc_merge_row.argtypes = [C.c_int, C.c_double, C.c_double, _P, C.c_double, C.c_double,
                                     _P, C.c_double, _P, _P]
+        L.orc_report_rows.argtypes = [_P, C.c_int]
+        L.orc_report_job_size.restype = C.c_size_t
+        assert L.orc_report_job_size() <= C.sizeof(_ReportJob)
         L.orc_job_size.restype = C.c_size_t
         L.orc_params_size.restype = C.c_size_t
         assert L.orc_params_size() == C.sizeof(_Params)
@@ -125,17 +140,21 @@ class Params:
     rg: int = 16
     q_terms: int = 1        # 2: Q plus its FP4 residual term
     k_lsq: int = 0          # 1: K block exponents by least squared error (MX)
+    qmask: int = QUANT_ALL  # pass 1's FP4 roundings that apply (per-operand emulation)
+    window: int = 0         # > 0: causal sliding window of this many keys
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
         assert self.Hq % self.Hkv == 0
         assert self.q_terms in (1, 2)
         assert self.k_lsq in (0, 1) and not (self.k_lsq and self.fmt != MX)
+        assert 0 <= self.qmask <= QUANT_ALL
+        assert self.window >= 0 and (self.window == 0 or self.causal)
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
                        self.scale, self.fmt, self.int_frame, self.tau, self.hoff, self.eps,
-                       self.tile, self.rg, self.q_terms, self.k_lsq)
+                       self.tile, self.rg, self.q_terms, self.k_lsq, self.qmask, self.window)
 
     @property
     def n_tiles(self) -> int:
@@ -334,6 +353,7 @@ def run(p: Params, Q, K, V, prep: dict | None = None, groups=None, nthreads: int
     for k in ("qc", "qs", "kc", "ks", "vc", "vs", "kbar", "g_v"):
         setattr(job, k, _ptr(prep[k]))
     job.jq = _ptr(prep["jq"])
+    job.inv_q, job.inv_k, job.inv_v = (_ptr(prep[k]) for k in ("inv_q", "inv_k", "inv_v"))
     job.qc2 = _ptr(prep.get("qc2")) if p.q_terms == 2 else None
     job.qs2 = _ptr(prep.get("qs2")) if p.q_terms == 2 else None
     job.groups, job.ngroups = _ptr(groups), len(groups)
@@ -382,3 +402,57 @@ def merge_row(D, m1, l1, o1, m2, l2, o2, c):
     lib().orc_merge_row(int(D), float(m1), float(l1), _ptr(o1), float(m2), float(l2), _ptr(o2),
                         float(c), _ptr(O), _ptr(lse))
     return O, float(lse[0])
+
+
+# --------------------------------------------------------------------------
+# reports against exact FP64 attention
+# --------------------------------------------------------------------------
+
+def reports(p: Params, Q, K, V, hot, rows=None, nthreads: int | None = None) -> dict:
+    """Where the exact FP64 softmax mass and output of each listed row sit
+    relative to a hot mask hot [B, Hq, NG, NT] (the method's, or a GPU's):
+    O_ref (exact attention), its parts O_hot and O_cold over the keys of hot
+    and of other tiles, lse, the mass on hot and on other tiles, and the
+    largest mass of one tile not marked hot (its index in cold_tile_arg, -1 if
+    none).  rows [n, 3] of (b, q-head, r); all rows if None."""
+    L = lib()
+    cp = p.c()
+    Q = np.ascontiguousarray(Q, np.float32)
+    K = np.ascontiguousarray(K, np.float32)
+    V = np.ascontiguousarray(V, np.float32)
+    hot = np.ascontiguousarray(hot, np.uint8)
+    assert hot.shape == (p.B, p.Hq, p.n_groups, p.n_tiles), hot.shape
+    if rows is None:
+        rows = np.array([(b, h, r) for b in range(p.B) for h in range(p.Hq) for r in range(p.Nq)],
+                        np.int32).reshape(-1, 3)
+    rows = np.ascontiguousarray(rows, np.int32).reshape(-1, 3)
+    n = len(rows)
+    out = dict(O_ref=np.zeros((n, p.D)), O_hot=np.zeros((n, p.D)), O_cold=np.zeros((n, p.D)),
+               lse=np.zeros(n), hot_share=np.zeros(n), cold_share=np.zeros(n),
+               cold_tile_max=np.zeros(n), cold_tile_arg=np.zeros(n, np.int32))
+    job = _ReportJob()
+    job.p = C.cast(C.pointer(cp), C.c_void_p)
+    job.Q, job.K, job.V, job.hot, job.rows, job.nrows = (_ptr(Q), _ptr(K), _ptr(V), _ptr(hot),
+                                                         _ptr(rows), n)
+    for k in out:
+        setattr(job, k, _ptr(out[k]))
+    if nthreads is None:
+        nthreads = os.cpu_count() or 1
+    L.orc_report_rows(C.byref(job), int(nthreads))
+    out["rows"] = rows
+    return out
+
+
+def compare_rows(O_test, O_ref) -> dict:
+    """Per-row agreement of an output with the reference: cosine (a row that
+    is zero on exactly one side scores -1, zero on both 1), mean squared
+    error and largest absolute difference, over every element."""
+    a = np.asarray(O_test, np.float64).reshape(-1, np.shape(O_ref)[-1])
+    b = np.asarray(O_ref, np.float64).reshape(a.shape)
+    na, nb = np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
+    cos = np.where((na > 0) != (nb > 0), -1.0, 1.0)
+    ok = (na > 0) & (nb > 0)
+    cos[ok] = (a[ok] * b[ok]).sum(1) / (na[ok] * nb[ok])
+    d = a - b
+    return dict(cos=cos, mse=float((d * d).mean()), max_abs=float(np.abs(d).max()),
+                row_mse=(d * d).mean(axis=1))

@@ -14,6 +14,13 @@ hot test ("APA: sloppy attention, exact where it counts", "Pass 1" steps 1-5,
 
 Valid while no block exponent reaches the E8M0 floor (2^-127) and nothing
 underflows FP32; the tiny workloads used by the tests stay far from both.
+
+Options mirror the oracle's: `quant` switches each operand's FP4 rounding
+(Q, K, V, P; an operand switched off enters at its exact value in the same
+normalised units, "Second hunt: which operand is to blame"), and `window`
+restricts every row to its `window` most recent keys ("What else is in the
+box": sliding window).  The per-cell margin max_r (l_r - eps lambda_r) /
+lambda_r is recomputed from this brute force's own l and lambda.
 """
 from __future__ import annotations
 
@@ -65,12 +72,16 @@ def quantise_blocks(x: np.ndarray, bs: int = 32):
     return val.reshape(sh)
 
 
-def prepare(Q, K, V, scale: float, q_terms: int = 1):
+QUANT_ALL = "QKVP"
+
+
+def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL):
     """Per-head scales and dequantised operands (without the per-head factors
     that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry.
     q_terms=2 adds the quantised residual of Q (section "Second hunt": a second
     FP4 term for what the first leaves over, sharing its scale) to the
-    dequantised Q."""
+    dequantised Q.  An operand missing from `quant` is kept at its exact value
+    in normalised units (FP64, no clamp)."""
     Hq, Nq, D = Q.shape
     Hkv = K.shape[0]
     G = Hq // Hkv
@@ -84,7 +95,8 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1):
         g_k = f32(amax_k / 6.0) if amax_k > 0 else np.float32(1)
         inv_k = f32(6.0 / amax_k) if amax_k > 0 else np.float32(1)
         kn = np.clip((kc * inv_k).astype(np.float32), -6, 6)
-        kd = quantise_blocks(kn)
+        kd = (quantise_blocks(kn) if "K" in quant else
+              (Kh.astype(np.float64) - kbar.astype(np.float64)) * np.float64(inv_k))
         Vh = V[hk].astype(np.float32)
         amax_v = np.abs(Vh).max()
         g_v = f32(amax_v / 6.0) if amax_v > 0 else np.float32(1)
@@ -95,6 +107,8 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1):
         vpad = np.zeros((NkvP, D), np.float32)
         vpad[:Nkv] = vn
         vd = quantise_blocks(vpad.T).T[:Nkv]              # blocks of 32 keys per channel
+        if "V" not in quant:
+            vd = Vh.astype(np.float64) * np.float64(inv_v)
         w = np.float32(sl * g_k)
         heads = []
         for i in range(G):
@@ -109,7 +123,9 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1):
             inv_q = np.float32(np.ldexp(np.float64(w), -j))
             qn = np.clip((Qh * inv_q).astype(np.float32), -6, 6)
             qd = quantise_blocks(qn)
-            if q_terms == 2:
+            if "Q" not in quant:
+                qd = Qh.astype(np.float64) * np.float64(inv_q)
+            elif q_terms == 2:
                 # the residual in FP32, quantised as blocks of its own; the sum
                 # of the two dequantised terms is exact in FP64
                 qd = qd + quantise_blocks((qn.astype(np.float64) - qd).astype(np.float32))
@@ -118,36 +134,51 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1):
     return out
 
 
-def visit_order(last_row: int, off: int, Nkv: int, causal: bool, tile: int = 64):
+def visit_order(last_row: int, off: int, Nkv: int, causal: bool, tile: int = 64,
+                first_row: int = 0, window: int = 0):
     nt = -(-Nkv // tile)
     d = min(Nkv - 1, last_row + off) // tile if causal else nt - 1
+    lo = max(0, first_row + off - window + 1) // tile if (causal and window > 0) else 0
+    if lo > 0:
+        return list(range(d, lo - 1, -1))
     return [0] + list(range(d, 0, -1))
 
 
 def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray, off: int,
-                Nkv: int, causal: bool):
+                Nkv: int, causal: bool, quant_p: bool = True, window: int = 0):
     """Frame-free pass 1 of one row group.
 
     scores: [R, Nkv] FP4 scores in log2 units (fl32), vd: [Nkv, D] dequantised
-    V'.  Returns (hot [NT] bool, l [R], o [R, D], lam [R]) in frame-free units.
+    V'.  Returns (hot [NT] bool, l [R], o [R, D], lam [R], margin [NT]) in
+    frame-free units; margin is NaN for tiles not visited.
     """
     R = scores.shape[0]
     D = vd.shape[1]
     nt = -(-Nkv // 64)
     hot = np.zeros(nt, bool)
+    margin = np.full(nt, np.nan)
     lam = np.zeros(R, np.float32)
     lsum = np.zeros(R, np.float32)
     o = np.zeros((R, D), np.float32)
     keys = np.arange(Nkv)
     vis = (keys[None, :] <= rows[:, None] + off) if causal else np.ones((R, Nkv), bool)
+    if causal and window > 0:
+        vis &= keys[None, :] > rows[:, None] + off - window
     s = np.where(vis, scores.astype(np.float64), -np.inf)
     eps32 = np.float32(eps)
-    for t in visit_order(int(rows[-1]), off, Nkv, causal):
+    for t in visit_order(int(rows[-1]), off, Nkv, causal, first_row=int(rows[0]), window=window):
         k0, k1 = 64 * t, min(Nkv, 64 * t + 64)
         st = np.full((R, 64), -np.inf)
         st[:, :k1 - k0] = s[:, k0:k1]
+        if not np.isfinite(st).any():
+            continue  # no row of the group sees a key of this tile: not visited
         ph = np.zeros((R, 64))
         for q0 in (0, 32):
+            if not quant_p:
+                g = st[:, q0:q0 + 32]
+                with np.errstate(invalid="ignore", over="ignore"):
+                    ph[:, q0:q0 + 32] = np.where(np.isfinite(g), np.exp2(g), 0.0)
+                continue
             g = st[:, q0:q0 + 32]
             cg = g.max(axis=1)
             E = np.where(np.isfinite(cg), np.ceil(cg - np.log2(6.0)), 0).astype(np.int64)
@@ -162,20 +193,25 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
         thr = (eps32 * lam).astype(np.float32)
         h = (eps == 0.0) or bool(np.any(ell > thr))
         hot[t] = h
+        pos = lam > 0
+        lam64 = lam.astype(np.float64)
+        mg = (ell.astype(np.float64) - np.float64(eps32) * lam64) / np.where(pos, lam64, 1.0)
+        margin[t] = mg[pos].max() if pos.any() else -np.inf
         if not h:
             vt = np.zeros((64, D))
             vt[:k1 - k0] = vd[k0:k1]
             pv = f32(ph @ vt)
             o = (o + pv).astype(np.float32)
             lsum = (lsum + ell).astype(np.float32)
-    return hot, lsum, o, lam
+    return hot, lsum, o, lam, margin
 
 
-def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: int = 1):
+def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: int = 1,
+              quant: str = QUANT_ALL, window: int = 0):
     """Frame-free pass 1 for every row group of a batch-1 problem.
 
     Returns dict with hot [Hq, NG, NT], l [Hq, Nq], o [Hq, Nq, D] (o already
-    times g_v), lam [Hq, Nq], all frame-free."""
+    times g_v), lam [Hq, Nq], all frame-free, and margin [Hq, NG, NT]."""
     Q, K, V = Q[0], K[0], V[0]
     Hq, Nq, D = Q.shape
     Nkv = K.shape[1]
@@ -183,8 +219,9 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
     off = Nkv - Nq
     nt = -(-Nkv // 64)
     ng = -(-Nq // 16)
-    ops = prepare(Q, K, V, scale, q_terms)
+    ops = prepare(Q, K, V, scale, q_terms, quant)
     hot = np.zeros((Hq, ng, nt), bool)
+    margin = np.full((Hq, ng, nt), np.nan)
     lo = np.zeros((Hq, Nq), np.float32)
     oo = np.zeros((Hq, Nq, D), np.float32)
     la = np.zeros((Hq, Nq), np.float32)
@@ -195,9 +232,11 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
         scores = f32(hd["alpha"] * dot.astype(np.float64))
         for g in range(ng):
             rows = np.arange(16 * g, min(Nq, 16 * g + 16))
-            hh, l, o, lam = pass1_group(scores[rows], kv["vd"], eps, rows, off, Nkv, causal)
+            hh, l, o, lam, mg = pass1_group(scores[rows], kv["vd"], eps, rows, off, Nkv, causal,
+                                            quant_p="P" in quant, window=window)
             hot[h, g] = hh
+            margin[h, g] = mg
             lo[h, rows] = l
             oo[h, rows] = (o * kv["g_v"]).astype(np.float32)
             la[h, rows] = lam
-    return dict(hot=hot, l=lo, o=oo, lam=la, ops=ops)
+    return dict(hot=hot, l=lo, o=oo, lam=la, margin=margin, ops=ops)

@@ -107,8 +107,8 @@ def test_split_hot_tail_tile_leaves_the_state(sched):
     (2, 1, 32, 266240, 64, 0.005, 38, 1),   # 4160 key tiles: hot words kept in the tile loop
     (6, 2, 200, 9000, 128, 0.005, 34, 1),   # GQA 3, ragged rows and keys
     (4, 1, 96, 12000, 64, 0.01, 35, 0),     # non-causal
-    (2, 1, 64, 8192, 256, 0.005, 36, 1),    # D = 256
-    (2, 1, 64, 8192, 64, 0.0, 39, 1),       # eps = 0: every visited tile hot, no records
+    (2, 1, 64, 12288, 256, 0.005, 36, 1),   # D = 256
+    (2, 1, 64, 12288, 64, 0.0, 39, 1),      # eps = 0: every visited tile hot, no records
 ])
 def test_split_path_inputs(case, sched):
     Hq, Hkv, Nq, Nkv, D, eps, seed, causal = case

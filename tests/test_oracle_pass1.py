@@ -142,7 +142,7 @@ def test_cold_verdicts_are_safe():
 def test_visit_orders_match_hand_derivation():
     cases = json.load(open(os.path.join(HERE, "golden", "visit_orders.json")))["cases"]
     for c in cases:
-        p = O.Params(1, 1, 1, c["Nq"], c["Nkv"], 64, causal=c["causal"])
+        p = O.Params(1, 1, 1, c["Nq"], c["Nkv"], 64, causal=c["causal"], window=c.get("window", 0))
         assert O.visit_order(p, c["group"]) == c["order"], c
 
 
@@ -158,7 +158,7 @@ def test_ascending_order_makes_more_tiles_hot():
     import brute_apa as BA
     saved = BA.visit_order
     try:
-        BA.visit_order = lambda last, off, Nkv, causal, tile=64: list(
+        BA.visit_order = lambda last, off, Nkv, causal, tile=64, **kw: list(
             range(0, (min(Nkv - 1, last + off) // tile) + 1))
         asc = BA.brute_apa(Q, K, V, 0.01, w.scale)
     finally:
