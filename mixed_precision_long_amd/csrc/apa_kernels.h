@@ -79,7 +79,12 @@ struct Pass2Args {
   // split states when a unit's keys run as S work groups: [S][rows] and
   // [S][rows][D] (rows = B*Hq*Nq)
   float *part_m, *part_l, *part_o;
+  // exact path with bf16 inputs: max |V| per (b, kv-head) and chunk of
+  // kVmaxChunk keys, [B*Hkv][vmax_nch] (written by a pre-pass)
+  float* vmax;
+  int vmax_nch;
 };
+constexpr int kVmaxChunk = 1024;
 // Work groups of the 16-bit attention kernels (per batch and kv-head, one per
 // four 32-row blocks of its query heads), and the number of key splits each
 // runs as for a problem.

@@ -145,8 +145,19 @@ size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
   return split_ws(p, o, a, base);
 }
 
+// The exact path's workspace: with bf16 inputs the per-(b, kv-head, key
+// chunk) maxima of |V|, then the split states.
 size_t exact_ws(const apa_problem* p, Pass2Args* a, void* base) {
-  return split_ws(p, 0, a, base);
+  size_t o = 0;
+  if (p->dtype == APA_BF16 && p->Nkv > 0) {
+    const int nch = (p->Nkv + kVmaxChunk - 1) / kVmaxChunk;
+    if (a && base) {
+      a->vmax = (float*)base;
+      a->vmax_nch = nch;
+    }
+    o = align256((size_t)p->B * p->Hkv * nch * 4);
+  }
+  return split_ws(p, o, a, base);
 }
 
 // D and dtype the device kernels implement for each call

@@ -67,15 +67,29 @@ __device__ __forceinline__ float merge_weight(bool live, float m, float M) {
   return live ? fast_exp2(m - M) : 0.0f;
 }
 
-// bf16 values of V as fp16 for the P V product: exact inside the fp16 range
-// (8 significant bits fit in 11); magnitudes beyond it are clamped to 65504.
-__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 z) {
+// The power of two 2^s by which a kv-head's bf16 V is divided so that its
+// largest magnitude amax fits the fp16 range: s = 0 up to 65504, else with
+// amax = f 2^x (f in [0.5, 1); a bf16 value has f <= 1 - 2^-8), s = x - 16
+// brings it to f 2^16 <= 65280.  Non-finite amax (flagged by the status
+// word) gives 0.
+__device__ __forceinline__ int v_shift(float amax) {
+  if (!(amax > 65504.0f) || !(amax < __builtin_inff())) return 0;
+  int x;
+  (void)frexpf(amax, &x);
+  return x - 16;
+}
+
+// bf16 values of V times 2^-s (down = 2^-s, s from v_shift) as fp16 for the
+// P V product: exact in the fp16 normal range (8 significant bits fit in 11);
+// below 2^-14 the fp16 subnormal spacing 2^-24 bounds the rounding.  The
+// product is scaled back by 2^s in the epilogue.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 z, float down) {
   const uint32_t w[4] = {z.x, z.y, z.z, z.w};
   uint32_t r[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float lo = fminf(fmaxf(__uint_as_float(w[i] << 16), -65504.0f), 65504.0f);
-    const float hi = fminf(fmaxf(__uint_as_float(w[i] & 0xFFFF0000u), -65504.0f), 65504.0f);
+    const float lo = __uint_as_float(w[i] << 16) * down;
+    const float hi = __uint_as_float(w[i] & 0xFFFF0000u) * down;
     const _Float16 a = (_Float16)lo, b = (_Float16)hi;
     r[i] = (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
   }
@@ -111,17 +125,30 @@ __device__ __forceinline__ int exact_tiles(const Geom& g, const RowBlocks& rb, i
   return g.causal ? min(g.Nkv - 1, lr + g.off) / kTile + 1 : g.NT;
 }
 
+// The largest |V| of a kv-head for the bf16 conversion: from the FP4
+// buffer's per-head statistics in pass 2, from the exact path's chunk
+// maxima otherwise (nullptr for fp16 inputs, where it is not needed).
+__device__ __forceinline__ float head_vamax(const Fp4Ptrs& f, const Pass2Args& a, size_t bhk,
+                                            int mode_pass2) {
+  if (mode_pass2) return f.kv_head[bhk * 8 + 3];
+  float m = 0.0f;
+  for (int c = 0; c < a.vmax_nch; ++c) m = fmaxf(m, a.vmax[bhk * a.vmax_nch + c]);
+  return m;
+}
+
 // The epilogue shared by both kernels: a split's partial state (S > 1 or an
 // unfused pass 2), else the output -- merged with the cold state in pass 2.
 // Lane (n, hh) holds row n's output channels ch0 + 32*db + 8*q + 4*hh + 0..3
 // in o[db][4q .. 4q+3] for db < ND (all D channels, or the share of a wave
 // that holds part of them); l is already summed over both lane halves.  The
-// row scalars (partial m and l, LSE) are written when `scalars` is set.
+// row scalars (partial m and l, LSE) are written when `scalars` is set.  o is
+// in units of 2^-vsh (bf16 V scaled into the fp16 range), scaled back here.
 template <int D, typename T, int MODE, int ND = D / 32>
 __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
                                            int S, int sp, size_t bhq, int row, int hh, float m,
-                                           float l, float c_r, const v16f* o, int ch0 = 0,
-                                           bool scalars = true) {
+                                           float l, float c_r, const v16f* o, int vsh,
+                                           int ch0 = 0, bool scalars = true) {
+  const float up = __int_as_float((vsh + 127) << 23);  // 2^vsh, vsh in [0, 112]
   using E = E16<T>;
   typedef typename E::V4 V4;
   const size_t r = bhq * g.Nq + row;
@@ -139,7 +166,8 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v4f x = {o[db][4 * q], o[db][4 * q + 1], o[db][4 * q + 2], o[db][4 * q + 3]};
+        v4f x = {o[db][4 * q] * up, o[db][4 * q + 1] * up, o[db][4 * q + 2] * up,
+                 o[db][4 * q + 3] * up};
         *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
       }
     return;
@@ -164,6 +192,7 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
     Lsum = l;
   }
   const float inv = Lsum > 0.0f ? 1.0f / Lsum : 0.0f;
+  w2 *= up;  // exact: a power of two
   T* orow = reinterpret_cast<T*>(a.out) + r * D + ch0;
 #pragma unroll
   for (int db = 0; db < ND; ++db)

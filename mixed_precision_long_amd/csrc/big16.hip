@@ -105,6 +105,9 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
   }
   const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
   const float sl = g.sl;
+  // bf16 V: the head's power-of-two shift into the fp16 range
+  const int vsh = BF ? v_shift(head_vamax(f, a, bhk, MODE == kPass2)) : 0;
+  const float vdown = __int_as_float((127 - vsh) << 23);
 
   // LDS-writing loads of a stage: wave w fills keys 16 (w % 2) .. +15 of the
   // groups w / 2, w / 2 + 2, ... (eight K groups, four V groups of the half);
@@ -166,7 +169,7 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
 #pragma unroll
       for (int i = 0; i < D / 128; ++i) {
         uint4* p = reinterpret_cast<uint4*>(st + (g0 + 2 * i) * C::GRP);
-        *p = bf16x8_to_f16x8(*p);
+        *p = bf16x8_to_f16x8(*p, vdown);
       }
     }
     __syncthreads();
@@ -256,7 +259,7 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
   if (!wr.live) return;
   l += xor32(l);
   if (!row_ok) return;
-  finish_row<D, T, MODE, NDO>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o, dh * NDO * 32,
+  finish_row<D, T, MODE, NDO>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o, vsh, dh * NDO * 32,
                               dh == 0);
 }
 

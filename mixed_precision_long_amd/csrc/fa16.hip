@@ -38,7 +38,10 @@
 //                 (its key order is matched by the V^T operand), V^T comes
 //                 from LDS by DS_READ_B64_TR_B16.  With bf16 inputs the scores
 //                 use the bf16 MFMA and each wave converts the V rows it loaded
-//                 to fp16 in LDS, so P keeps 11 significant bits.
+//                 to fp16 in LDS, so P keeps 11 significant bits; V is first
+//                 divided by a per-head power of two that brings its largest
+//                 magnitude into the fp16 range (exact), undone in the
+//                 epilogue.
 // D = 512 runs in big16.hip (two work groups per unit, one per half of the
 // output channels).
 #include "attn16.h"
@@ -120,6 +123,9 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   }
   const float c_r = (MODE == kPass2) ? f.q_frame[bhq * g.NqP + (row_ok ? row : 0)] : 0.0f;
   const float sl = g.sl;
+  // bf16 V: the head's power-of-two shift into the fp16 range
+  const int vsh = BF ? v_shift(head_vamax(f, a, bhk, MODE == kPass2)) : 0;
+  const float vdown = __int_as_float((127 - vsh) << 23);
 
   // LDS-writing loads: wave w loads 16-key block w of every 32-channel group;
   // lane L carries key 16w + L/4 and the row's 16-byte slot L%4 (K: chunk
@@ -170,7 +176,7 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
 #pragma unroll
       for (int i = 0; i < C::NLD; ++i) {
         uint4* p = reinterpret_cast<uint4*>(st + i * C::GRP);
-        *p = bf16x8_to_f16x8(*p);
+        *p = bf16x8_to_f16x8(*p, vdown);
       }
     }
     __syncthreads();
@@ -285,7 +291,7 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   if (!wr.live) return;
   l += xor32(l);
   if (!row_ok) return;
-  finish_row<D, T, MODE>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o);
+  finish_row<D, T, MODE>(g, f, a, S, sp, bhq, row, hh, m, l, c_r, o, vsh);
 }
 
 // Two work groups per compute unit up to D = 128 (registers <= 256 per
@@ -449,6 +455,31 @@ __global__ void k_combine(Geom g, Fp4Ptrs f, Pass2Args a, int S, long nrows) {
             reinterpret_cast<T*>(a.out) + r * D + ch, want_lse ? a.lse + r : nullptr);
 }
 
+// max |V| per (b, kv-head) and chunk of kVmaxChunk keys, for bf16 inputs of
+// the exact path (the NaN-ignoring maximum: non-finite inputs give undefined
+// outputs either way).  grid (nch, B*Hkv), 256 threads, 16-byte loads.
+__global__ __launch_bounds__(256) void k_vmax(Geom g, const uint16_t* __restrict__ V, float* out,
+                                              int nch) {
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int k0 = c * kVmaxChunk, k1 = min(g.Nkv, k0 + kVmaxChunk);
+  const long n8 = (long)(k1 - k0) * g.D / 8;
+  const uint4* src = reinterpret_cast<const uint4*>(V + ((size_t)bh * g.Nkv + k0) * g.D);
+  float m = 0.0f;
+  for (long i = threadIdx.x; i < n8; i += 256) {
+    const uint4 z = src[i];
+    const uint32_t w[4] = {z.x, z.y, z.z, z.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[j] << 16)),
+                         fabsf(__uint_as_float(w[j] & 0xFFFF0000u))));
+  }
+  __shared__ float red[4];
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) out[(size_t)bh * nch + c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 template <int D, typename T, int MODE>
 hipError_t run_attn(const Geom& g, const void* q, const void* k, const void* v, const Fp4Ptrs& f,
                     const Pass2Args& a, int S, hipStream_t s) {
@@ -535,6 +566,13 @@ hipError_t launch_exact(const Geom& g, const void* q, const void* k, const void*
   a.out = out;
   a.lse = lse;
   Fp4Ptrs f = {};
+  if (g.bf16 && g.Nkv > 0) {
+    // the largest |V| of each kv-head, for the shift of bf16 V into the fp16 range
+    hipLaunchKernelGGL(k_vmax, dim3(a.vmax_nch, g.B * g.Hkv), dim3(256), 0, s, g,
+                       (const uint16_t*)v, a.vmax, a.vmax_nch);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   return dispatch<kExact>(g, q, k, v, f, a, attn_splits(g), s);
 }
 

@@ -545,42 +545,19 @@ static double k_value(const orc_head_ops* h, int k, int d) {
          code_at(h->kc, (size_t)k * D + d);
 }
 
-/* FP4 score of (row r, key k): s = fl32(alpha * fl32(dot)), where dot is the
- * exact block-scaled dot product of the codes ("Scores in FP4"); with two Q
- * terms, dot adds the residual term's block products against the same K
- * codes before the one rounding.  With Q or K unquantised (emulation), dot
- * is the FP64 sum over channels of the two operands' values. */
-static float fp4_score(const orc_head_ops* h, int r, int k) {
-  const orc_params* p = h->p;
-  int D = p->D, Bs = p->fmt == ORC_NV ? 16 : 32, nb = D / Bs;
-  if ((p->qmask & (ORC_QUANT_Q | ORC_QUANT_K)) != (ORC_QUANT_Q | ORC_QUANT_K)) {
-    double dot = 0.0;
-    for (int d = 0; d < D; ++d) dot += q_value(h, r, d) * k_value(h, k, d);
-    float d32 = (float)dot;
-    return (float)(h->alpha * (double)d32);
-  }
+/* FP4 score from decoded operands ("Scores in FP4"): s = fl32(alpha *
+ * fl32(dot)), dot = the FP64 sum over channels of q'_d k'_d, where q' and k'
+ * are the dequantised values (code times block scale; with two Q terms the
+ * sum of both terms) or, with an operand's quantisation switched off, its
+ * exact value.  With FP4 operands every product is exact and so is the sum
+ * (within a block a small multiple of one power of two; blocks combine
+ * exactly unless their exponents span more than ~38 octaves), so s is the
+ * exact block-scaled dot product rounded once to FP32, then scaled. */
+static float fp4_score(const double* q, const double* k, int D, double alpha) {
   double dot = 0.0;
-  for (int b = 0; b < nb; ++b) {
-    double part = 0.0;
-    for (int i = 0; i < Bs; ++i) {
-      int d = b * Bs + i;
-      part += code_at(h->qc, (size_t)r * D + d) * code_at(h->kc, (size_t)k * D + d);
-    }
-    double sc = orc_scale_value(h->qs[(size_t)r * nb + b], p->fmt) *
-                orc_scale_value(h->ks[(size_t)k * nb + b], p->fmt);
-    dot += sc * part;
-    if (h->qc2) {
-      double part2 = 0.0;
-      for (int i = 0; i < Bs; ++i) {
-        int d = b * Bs + i;
-        part2 += code_at(h->qc2, (size_t)r * D + d) * code_at(h->kc, (size_t)k * D + d);
-      }
-      dot += orc_scale_value(h->qs2[(size_t)r * nb + b], p->fmt) *
-             orc_scale_value(h->ks[(size_t)k * nb + b], p->fmt) * part2;
-    }
-  }
+  for (int d = 0; d < D; ++d) dot += q[d] * k[d];
   float d32 = (float)dot;
-  return (float)(h->alpha * (double)d32);
+  return (float)(alpha * (double)d32);
 }
 
 /* Dequantised V' (without the per-head g_v) at (key k, channel d); with V's
@@ -631,6 +608,13 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
   double* ph = (double*)malloc((size_t)R * T * sizeof(double));
   float* tpv = (float*)malloc((size_t)D * sizeof(float));
   int* order = (int*)malloc((size_t)(NT + 1) * sizeof(int));
+  /* the operands decoded once: the group's Q rows, and per visited tile its
+   * K rows and (for a cold tile) its V rows, zero past Nkv */
+  double* qd = (double*)malloc((size_t)R * D * sizeof(double));
+  double* kd = (double*)malloc((size_t)T * D * sizeof(double));
+  double* vd = (double*)malloc((size_t)T * D * sizeof(double));
+  for (int i = 0; i < nr; ++i)
+    for (int d = 0; d < D; ++d) qd[(size_t)i * D + d] = q_value(h, r0 + i, d);
   for (int i = 0; i < R; ++i) { m[i] = -INFINITY; lam[i] = 0.0f; l[i] = 0.0f; out->shift_max[i] = 0.0; }
   for (int t = 0; t < NT; ++t) { out->hot[t] = 0; out->margin[t] = NAN; }
 
@@ -642,6 +626,9 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
     for (int i = 0; i < nr && !any; ++i)
       for (int kk = 0; kk < T && !any; ++kk) any = visible(p, r0 + i, k0 + kk);
     if (!any) continue;
+    for (int kk = 0; kk < T; ++kk)
+      for (int d = 0; d < D; ++d)
+        kd[(size_t)kk * D + d] = k0 + kk < p->Nkv ? k_value(h, k0 + kk, d) : 0.0;
 
     double mc[16];
     float lc[16], lamc[16];
@@ -654,7 +641,9 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
       double c = -INFINITY;
       for (int kk = 0; kk < T; ++kk) {
         int k = k0 + kk;
-        s[i * T + kk] = visible(p, r, k) ? fp4_score(h, r, k) : -INFINITY;
+        s[i * T + kk] = visible(p, r, k)
+                            ? fp4_score(qd + (size_t)i * D, kd + (size_t)kk * D, D, h->alpha)
+                            : -INFINITY;
         if ((double)s[i * T + kk] > c) c = s[i * T + kk];
       }
       /* lazy maximum: move the frame only when the tile max exceeds it by
@@ -716,10 +705,13 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
       if (!hot) {
         mn = mc[i];
         double sh = m[i] - mn;
+        if (i == 0)
+          for (int kk = 0; kk < T; ++kk)
+            for (int d = 0; d < D; ++d) vd[(size_t)kk * D + d] = vprime(h, k0 + kk, d);
         for (int d = 0; d < D; ++d) {
           double acc = 0.0;
           for (int kk = 0; kk < T; ++kk)
-            if (ph[i * T + kk] != 0.0) acc += ph[i * T + kk] * vprime(h, k0 + kk, d);
+            if (ph[i * T + kk] != 0.0) acc += ph[i * T + kk] * vd[(size_t)kk * D + d];
           tpv[d] = (float)acc;
         }
         for (int d = 0; d < D; ++d) {
@@ -756,7 +748,7 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
     out->lam[i] = lam[i];
     for (int d = 0; d < D; ++d) out->o[(size_t)i * D + d] = o[i * D + d] * h->g_v;
   }
-  free(o); free(s); free(ph); free(tpv); free(order);
+  free(o); free(s); free(ph); free(tpv); free(order); free(qd); free(kd); free(vd);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -233,19 +233,33 @@ def test_deterministic_reruns():
             assert np.array_equal(np.nan_to_num(r[k]), np.nan_to_num(runs[0][k])), k
 
 
-def _sampled(name, ngroups, seed=0, delta=None):
+_INPUTS = {}
+
+
+def _workload_inputs(name, delta=None):
+    """Full-size inputs of a named workload, generated once per process (the
+    parity tests at one shape share them)."""
+    key = (name, delta)
+    if key not in _INPUTS:
+        _INPUTS.clear()
+        w = WORKLOADS[name]
+        print("[%s] generating inputs (delta %s)" % (name, delta), flush=True)
+        Q, K, V = make_inputs(w, delta=delta, threads=16)
+        po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
+        _INPUTS[key] = (Q, K, V, O.quantize(po, Q, K, V))
+    return _INPUTS[key]
+
+
+def _check_groups(name, sel, eps=None, delta=None):
+    """The whole path on the GPU at the workload's full size; the oracle on the
+    row groups `sel` [n, 3]: codes, masks, cold state, output and LSE."""
     w = WORKLOADS[name]
-    print("[%s] generating inputs (delta %s)" % (name, delta), flush=True)
-    Q, K, V = make_inputs(w, delta=delta, threads=16)
-    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
-    g = run_gpu(problem_for(w), Q, K, V, w.eps, dtype=w.dtype, lam=False)
-    rng = np.random.default_rng(seed)
-    allg = O.all_groups(po)
-    sel = allg[rng.choice(len(allg), ngroups, replace=False)]
-    # the oracle needs only the sampled kv heads
-    prep = O.quantize(po, Q, K, V)
+    eps = w.eps if eps is None else eps
+    Q, K, V, prep = _workload_inputs(name, delta)
+    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=eps)
+    g = run_gpu(problem_for(w), Q, K, V, eps, dtype=w.dtype, lam=False)
     check_quant(g, prep)
-    r = O.run(po, Q, K, V, prep, groups=sel)
+    r = O.run(po, Q, K, V, prep, groups=sel, nthreads=16)
     mism = check_mask(g["hot"], r, groups=sel)
     check_cold_state(g, r, mism, groups=sel)
     rows = np.array([(b, h, gg * 16 + i) for b, h, gg in sel for i in range(16)
@@ -254,20 +268,50 @@ def _sampled(name, ngroups, seed=0, delta=None):
     lg = g["lse"][rows[:, 0], rows[:, 1], rows[:, 2]]
     lo = r["lse"][rows[:, 0], rows[:, 1], rows[:, 2]]
     assert np.abs(lg - lo).max() <= 2e-3
+    cells = sum(1 for b, h, gg in sel for t in range(r["hot"].shape[-1])
+                if not np.isnan(r["margin"][b, h, gg, t]))
+    print("[%s eps %g] %d groups, %d cells, %d mask mismatches, hot %.4f" % (
+        name, eps, len(sel), cells, int(mism.sum()),
+        float(np.mean([r["hot"][b, h, gg].sum() for b, h, gg in sel]))), flush=True)
+    return g, r
+
+
+def _sampled(name, ngroups, seed=0, delta=None):
+    w = WORKLOADS[name]
+    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
+    allg = O.all_groups(po)
+    sel = allg[np.random.default_rng(seed).choice(len(allg), ngroups, replace=False)]
+    _check_groups(name, sel, delta=delta)
 
 
 def test_short3b_sampled_groups():
     _sampled("short3b", 12)
 
 
-def test_long3b_sampled_groups():
-    _sampled("long3b", 6)
+@pytest.mark.parametrize("eps", [0.002, 0.005, 0.02])
+def test_long3b_every_group_of_one_kv_head(eps):
+    """The headline shape (2048 rows at the tail of 122880 keys, 24 query
+    heads over 8) at each of its three eps: every row group of the three
+    query heads that share KV head 0 (384 groups, about 0.74 M visited cells)
+    -- not a sample ("The bug": a 1 % sample overstates the worst case)."""
+    w = WORKLOADS["long3b"]
+    G = w.Hq // w.Hkv
+    sel = np.array([(0, h, gg) for h in range(G) for gg in range(w.Nq // 16)], np.int32)
+    _check_groups("long3b", sel, eps=eps)
 
 
-def test_full32k_sampled_groups():
-    """Full causal prefill 32768 x 32768 (32 query heads over 8), the
-    strongest sink of its sweep, at full size on sampled row groups."""
-    _sampled("full32k", 8, delta=12.0)
+@pytest.mark.parametrize("delta", [0.0, 4.0, 8.0, 12.0])
+def test_full32k_sampled_groups(delta):
+    """Full causal prefill 32768 x 32768 (32 query heads over 8) at each sink
+    strength of its sweep, at full size on sampled row groups (the longest
+    groups included)."""
+    w = WORKLOADS["full32k"]
+    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
+    allg = O.all_groups(po)
+    rng = np.random.default_rng(int(delta))
+    sel = allg[rng.choice(len(allg), 8, replace=False)]
+    last = np.array([(0, int(rng.integers(w.Hq)), w.Nq // 16 - 1)], np.int32)
+    _check_groups("full32k", np.concatenate([sel, last]), delta=delta)
 
 
 @pytest.mark.parametrize("delta", [0.0, 4.0, 8.0, 12.0])
@@ -326,7 +370,7 @@ def test_exact_dtypes_and_large_head_dim(case):
 def test_bigd_sampled_groups():
     """Large head dimension, bf16: 32 query heads over 8, D = 512, 1024 rows
     at the tail of 4096 keys, at full size on sampled row groups."""
-    _sampled("bigd", 16)
+    _sampled("bigd", 32)
 
 
 def test_long3b_exact_sampled_rows():
