@@ -83,31 +83,84 @@ def traffic_for(kernel_src, units):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, ngroups, threads):
-    """The oracle as it stands, on a bounded sample of row groups of the same
-    workload (pass 1, exact pass 2 and merge; the K/V quantisation it needs is
-    shared by every row of a KV head and is excluded)."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def sample_groups(w, ngroups):
+    """The row groups the CPU legs use: a seeded random sample of the
+    workload's (batch, query head, 16-row group) triples."""
     from oracle import oracle as O
-    from mixed_precision_long_amd.inputs import make_inputs
-    rng = np.random.default_rng(123)
     p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps)
     allg = O.all_groups(p)
-    sel = allg[rng.choice(len(allg), ngroups, replace=False)]
+    return allg[np.random.default_rng(123).choice(len(allg), ngroups, replace=False)]
+
+
+def cpu_legs(w, eps, ngroups, threads, gpu_out, gpu_hot, exact_out):
+    """The oracle as it stands, timed on a bounded sample of row groups of the
+    same workload (pass 1, exact pass 2 and merge; the K/V quantisation it
+    needs is shared by every row of a KV head and is excluded), and, untimed,
+    the FP64 reports on the same rows: the GPU's APA output and the all-exact
+    output against FP64 attention, and the true FP64 share of the tiles the
+    GPU left cold."""
+    from oracle import oracle as O
+    from mixed_precision_long_amd.inputs import make_inputs
+    p = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=eps)
+    sel = sample_groups(w, ngroups)
     kvh = sorted({(int(b), int(h) // (w.Hq // w.Hkv)) for b, h, _ in sel})
     Q, K, V = make_inputs(w, kv_heads=kvh)
     prep = O.quantize(p, Q, K, V)
     t0 = time.perf_counter()
-    O.run(p, Q, K, V, prep, groups=sel, nthreads=threads)
+    r = O.run(p, Q, K, V, prep, groups=sel, nthreads=threads)
     dt = time.perf_counter() - t0
     off = w.Nkv - w.Nq
     flops = 0
     for _, _, g in sel:
-        for r in range(16 * g, min(16 * g + 16, w.Nq)):
-            flops += 4 * w.D * min(r + off + 1, w.Nkv)
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s (effective)", cores=threads,
-                kind="oracle", seconds=round(dt, 2),
-                sample="%d random 16-row groups of %s (pass 1 + exact pass 2 + merge; "
-                       "K/V quantisation excluded), %d threads" % (ngroups, w.name, threads))
+        for row in range(16 * g, min(16 * g + 16, w.Nq)):
+            flops += 4 * w.D * min(row + off + 1, w.Nkv)
+    base = dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s (effective)", cores=threads,
+                kind="oracle", seconds=round(dt, 2), cpu_model=cpu_model(),
+                logical_cores_visible=os.cpu_count(),
+                sample="%d random 16-row groups of %s (pass 1 + exact pass 2 + merge; K/V "
+                       "quantisation excluded), one worker thread per core of the %d-core "
+                       "share a GPU gets on this host" % (ngroups, w.name, threads))
+    rows = np.array([(b, h, g * 16 + i) for b, h, g in sel for i in range(16)
+                     if g * 16 + i < w.Nq], np.int32)
+    rep = O.reports(p, Q, K, V, gpu_hot, rows, nthreads=threads)
+    ix = (rows[:, 0], rows[:, 1], rows[:, 2])
+
+    def summ(out):
+        c = O.compare_rows(out[ix], rep["O_ref"])
+        return {"cos_min": round(float(c["cos"].min()), 6),
+                "cos_median": round(float(np.median(c["cos"])), 6),
+                "mse": float("%.4g" % c["mse"]), "max_abs": round(c["max_abs"], 6)}
+
+    apa = O.compare_rows(gpu_out[ix], rep["O_ref"])
+    worst = int(np.argmin(apa["cos"]))
+    nref = np.linalg.norm(rep["O_ref"][worst])
+    vs = {"rows": len(rows), "sample": "the rows of the CPU baseline's row groups",
+          "apa": summ(gpu_out), "oracle_apa": summ(r["O"]),
+          "cold_tile_true_share_max": round(float(rep["cold_tile_max"].max()), 6),
+          "page_cold_tile_true_share_max": 0.0118,
+          "cold_share": {"max": round(float(rep["cold_share"].max()), 6),
+                         "median": round(float(np.median(rep["cold_share"])), 6)},
+          "worst_row": {"row": [int(x) for x in rows[worst]],
+                        "cos": round(float(apa["cos"][worst]), 6),
+                        "cold_share": round(float(rep["cold_share"][worst]), 6),
+                        "cold_part_norm_over_ref": round(float(
+                            np.linalg.norm(rep["O_cold"][worst]) / nref), 6) if nref > 0 else None,
+                        "hot_part_norm_over_ref": round(float(
+                            np.linalg.norm(rep["O_hot"][worst]) / nref), 6) if nref > 0 else None}}
+    if exact_out is not None:
+        vs["exact"] = summ(exact_out)
+    return base, vs
 
 
 def main():
@@ -120,7 +173,8 @@ def main():
     ap.add_argument("--eps", type=float, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip timing the all-exact path")
-    ap.add_argument("--cpu-groups", type=int, default=64)
+    ap.add_argument("--cpu-groups", type=int, default=64,
+                    help="row groups of the CPU oracle's sample (also the rows of vs_fp64)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the eps sweep")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the accuracy variants (two-term Q, least-squares K scales)")
@@ -196,9 +250,11 @@ def main():
     ms = wall * 1e3 / args.steps
     kern_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in ev[n]])) for n in ev}
     print("[bench] APA %.3f ms/step %s" % (ms, kern_ms), file=sys.stderr, flush=True)
+    gpu_out_host = bufs.out.float().cpu().numpy()
 
     flop = 4.0 * w.D * visible_pairs(w.Nq, w.Nkv) * w.Hq * w.B
     hot = apa_hot_mask(p, bufs.bits)
+    gpu_hot_host = hot.astype(np.uint8)
     cells, hot_cells, vpairs, hpairs = cell_counts(hot, w.Nq, w.Nkv)
     cold_pairs = (vpairs - hpairs) * 1.0
     # pass-1 algorithmic FP4 work per launch: QK on every visited pair, the
@@ -236,6 +292,7 @@ def main():
                          "pairs": round(hpairs / max(vpairs, 1), 5)},
     }
 
+    exact_out_host = None
     if not args.no_exact:
         eo = torch.empty_like(q)
         el = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
@@ -249,6 +306,7 @@ def main():
         torch.cuda.synchronize()
         ems = (time.perf_counter() - t0) * 1e3 / n_ex
         ef = eo.float()
+        exact_out_host = ef.cpu().numpy()
         cos = torch.nn.functional.cosine_similarity(out.reshape(-1, w.D), ef.reshape(-1, w.D), dim=1)
         res["exact"] = {"ms": round(ems, 4), "tflops": round(flop / (ems * 1e-3) / 1e12, 3),
                         "fp16_roofline_frac": round(flop / (ems * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
@@ -300,37 +358,59 @@ def main():
             print("[bench] %s %.3f ms" % (name, tt["ms"]), file=sys.stderr, flush=True)
 
     if w.eps_sweep and not args.no_sweep:
+        # each eps: the same step, warmed up, with its kernels timed apart
         sweep = {}
         for e2 in w.eps_sweep:
-            for _ in range(2):
-                apa.pass1(p, bufs.fp4, e2, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
-                          ws=bufs.ws_p1, stream=stream)
+            for _ in range(3):
+                step_eps(apa, p, q, k, v, bufs, e2, stream, None)
             torch.cuda.synchronize()
+            evs = []
             t0 = time.perf_counter()
-            for _ in range(5):
-                step_eps(apa, p, q, k, v, bufs, e2, stream)
+            for _ in range(10):
+                step_eps(apa, p, q, k, v, bufs, e2, stream, evs)
             torch.cuda.synchronize()
-            ms2 = (time.perf_counter() - t0) * 1e3 / 5
+            ms2 = (time.perf_counter() - t0) * 1e3 / 10
+            kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in evs])) for a in range(3)]
             hot2 = apa_hot_mask(p, bufs.bits)
             c2, h2, vp2, hp2 = cell_counts(hot2, w.Nq, w.Nkv)
-            sweep[str(e2)] = {"ms": round(ms2, 4), "hot_cells": round(h2 / max(c2, 1), 5)}
+            sweep[str(e2)] = {"ms": round(ms2, 4), "hot_cells": round(h2 / max(c2, 1), 5),
+                              "kernels_ms": {"quantize": round(kms[0], 4),
+                                             "pass1": round(kms[1], 4),
+                                             "pass2": round(kms[2], 4)}}
+            if "exact" in res:
+                sweep[str(e2)]["apa_speedup_vs_exact"] = round(res["exact"]["ms"] / ms2, 3)
         res["eps_sweep"] = sweep
 
     if not args.no_cpu:
+        # one worker thread per core of the host share a GPU gets (16 here,
+        # whatever the host's visible core count)
         threads = max(1, min(16, os.cpu_count() or 1))
         print("[bench] cpu baseline (%d groups, %d threads)" % (args.cpu_groups, threads),
               file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_groups, threads)
+        res["cpu_baseline"], res["vs_fp64"] = cpu_legs(w, eps, args.cpu_groups, threads,
+                                                        gpu_out_host, gpu_hot_host,
+                                                        exact_out_host)
 
     print(json.dumps(res), flush=True)
 
 
-def step_eps(apa, p, q, k, v, bufs, eps, stream):
+def step_eps(apa, p, q, k, v, bufs, eps, stream, evs):
+    import torch
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if evs is not None else None
+    if e:
+        e[0].record(stream)
     apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q, stream)
+    if e:
+        e[1].record(stream)
     apa.pass1(p, bufs.fp4, eps, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
               ws=bufs.ws_p1, stream=stream)
+    if e:
+        e[2].record(stream)
     apa.pass2(p, q, k, v, bufs.fp4, bufs.bits, bufs.cold_m, bufs.cold_l, bufs.cold_o, True,
               out=bufs.out, lse=bufs.lse, ws=bufs.ws_p2, stream=stream)
+    if e:
+        e[3].record(stream)
+        evs.append(e)
 
 
 def apa_hot_mask(p, bits):
