@@ -148,6 +148,21 @@ const char* apa_last_hip_error(void);
 apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
                         void* fp4, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or call hipMalloc (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid it):
+ * apa_quantize without a workspace argument.  Its scratch is a fixed device
+ * array inside the library, 16 MiB per GPU, held until the process ends;
+ * the call allocates nothing.  Problems
+ * whose apa_workspace_bytes(p, APA_CALL_QUANTIZE) exceeds that get
+ * APA_ERR_WORKSPACE (about B * Hkv * ceil(Nkv / 1024) * D * 16 bytes: one
+ * million keys at 8 KV heads and D = 128 fit).  Every call on one GPU uses
+ * that GPU's one array, and each call writes all of the scratch it reads, so
+ * nothing carries over between calls; calls that overlap on one GPU (on
+ * different streams without ordering) race and must not be issued.  Same
+ * arguments and results as apa_quantize otherwise. */
+apa_status apa_quantize_static(const apa_problem* p, const void* q, const void* k, const void* v,
+                               void* fp4, void* stream);
+
 /* a3..a7: pass 1 ("Pass 1: FP4 everywhere, with a hot test", steps 1-5;
  * "Tile order"; the lazy maximum; the decoupled cold frame of "The bug").
  * Every row group of 16 rows visits its tiles in the order 0, d, d-1, ..., 1

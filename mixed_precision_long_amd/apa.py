@@ -21,7 +21,8 @@ CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
            "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize",
-           "apa_pass1", "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact"]
+           "apa_quantize_static", "apa_pass1",
+           "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact"]
 
 
 class ApaError(RuntimeError):
@@ -77,6 +78,7 @@ def lib() -> C.CDLL:
         L.apa_pass1_split.argtypes = [P, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
         L.apa_pass1_split.restype = C.c_int32
         L.apa_quantize.argtypes = [P, VP, VP, VP, VP, VP, S, VP]
+        L.apa_quantize_static.argtypes = [P, VP, VP, VP, VP, VP]
         L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
                                 VP, S, VP]
@@ -152,6 +154,12 @@ def quantize(p: Problem, q, k, v, fp4, ws, stream=None):
     _check(lib().apa_quantize(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)), "apa_quantize")
+
+
+def quantize_static(p: Problem, q, k, v, fp4, stream=None):
+    """apa_quantize with the library's fixed scratch (allocates nothing)."""
+    _check(lib().apa_quantize_static(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4),
+                                     _stream(stream)), "apa_quantize_static")
 
 
 def pass1(p: Problem, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=None, ws=None,

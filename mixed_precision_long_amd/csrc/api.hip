@@ -4,10 +4,22 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/apa.h"
 #include "apa_kernels.h"
 
 using namespace apa;
+
+// Scratch of apa_quantize_static: a fixed device array of the library, one
+// copy per GPU (held until the process ends).  In host code `scratch` names
+// a host-side stand-in, not device memory: its device address is fetched
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.  The statistics kernels write
+// every word they later read (partial sums, extrema, flags), so nothing in
+// it needs clearing between calls.
+constexpr size_t kStaticScratch = (size_t)16 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratch];
 
 namespace {
 
@@ -174,6 +186,27 @@ bool kernels_cover(const apa_problem* p, int call) {
 
 thread_local hipError_t g_last_hip = hipSuccess;
 
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, fetched on its first use.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 apa_status hip_status(hipError_t e) {
   g_last_hip = e;
   return e == hipSuccess ? APA_OK : APA_ERR_HIP;
@@ -259,6 +292,22 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
   QuantWs w;
   quant_ws(p, &w, ws);
   clear_hip_error();
+  return hip_status(launch_quantize(geom(p), q, k, v, fp4_ptrs(p, fp4), w, (hipStream_t)stream));
+}
+
+apa_status apa_quantize_static(const apa_problem* p, const void* q, const void* k, const void* v,
+                               void* fp4, void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_QUANTIZE)) return APA_ERR_UNSUPPORTED;
+  if (p->B == 0 || p->Hkv == 0) return APA_OK;
+  if (quant_ws(p, nullptr, nullptr) > kStaticScratch) return APA_ERR_WORKSPACE;
+  clear_hip_error();
+  void* base = nullptr;
+  const hipError_t e = scratch_address(&base);
+  if (e != hipSuccess) return hip_status(e);
+  QuantWs w;
+  quant_ws(p, &w, base);
   return hip_status(launch_quantize(geom(p), q, k, v, fp4_ptrs(p, fp4), w, (hipStream_t)stream));
 }
 
