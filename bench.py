@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the eps sweep")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the accuracy variants (two-term Q, least-squares K scales)")
+    ap.add_argument("--no-window", action="store_true",
+                    help="skip timing the sliding-window variant (4096 keys)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "known-size kernel that scales the HBM byte counters)")
@@ -380,6 +382,44 @@ def main():
             if "exact" in res:
                 sweep[str(e2)]["apa_speedup_vs_exact"] = round(res["exact"]["ms"] / ms2, 3)
         res["eps_sweep"] = sweep
+
+    if not args.no_window and w.causal:
+        # the page's sliding-window case: each row sees its 4096 most recent
+        # keys; APA (same eps) and the all-exact path on the same inputs
+        W = 4096
+        pw = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                         dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
+                         scale=w.scale, window=W)
+        bw = apa.alloc(pw)
+        evw = []
+        for i in range(5 + 20):
+            step_eps(apa, pw, q, k, v, bw, eps, stream, evw if i >= 5 else None)
+        torch.cuda.synchronize()
+        kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in evw])) for a in range(3)]
+        tot = float(np.mean([x[0].elapsed_time(x[3]) for x in evw]))
+        eow = torch.empty_like(q)
+        for _ in range(5):
+            apa.exact(pw, q, k, v, eow, None, stream=stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(10):
+            apa.exact(pw, q, k, v, eow, None, stream=stream)
+        torch.cuda.synchronize()
+        ewms = (time.perf_counter() - t0) * 1e3 / 10
+        cosw = torch.nn.functional.cosine_similarity(bw.out.float().reshape(-1, w.D),
+                                                     eow.float().reshape(-1, w.D), dim=1)
+        hotw = apa_hot_mask(pw, bw.bits)
+        res["sliding_window"] = {
+            "window": W, "ms": round(tot, 4),
+            "kernels_ms": {"quantize": round(kms[0], 4), "pass1": round(kms[1], 4),
+                           "pass2": round(kms[2], 4)},
+            "exact_ms": round(ewms, 4), "causal_ms": round(ms, 4),
+            "hot_groups_tiles": int(hotw.sum()),
+            "apa_vs_exact_cos_min": round(float(cosw.min()), 6),
+            "page_ms_window_vs_causal": [0.804, 6.053]}
+        del bw
+        print("[bench] window %d: %.3f ms (exact %.3f)" % (W, tot, ewms), file=sys.stderr,
+              flush=True)
 
     if not args.no_cpu:
         # one worker thread per core of the host share a GPU gets (16 here,

@@ -78,10 +78,18 @@ typedef struct apa_problem {
                                      the APA page's other "Second hunt" fix;
                                      the error is summed in FP32 in a fixed
                                      order; 0: the nearest rule (0)           */
+  int32_t window;                 /* > 0: causal sliding window of this many keys
+                                     (the APA page's "What else is in the box"):
+                                     row r sees keys r + Nkv - Nq - window < k
+                                     <= r + Nkv - Nq; a row group whose first
+                                     row no longer sees tile 0 visits its tiles
+                                     from the diagonal backwards; needs
+                                     is_causal.  0: the full causal mask (0)   */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
- * fp16, causal, APA_SCHED_AUTO, one Q term, nearest K block exponents. */
+ * fp16, causal, APA_SCHED_AUTO, one Q term, nearest K block exponents, no
+ * window. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 

@@ -40,7 +40,7 @@ class Problem(C.Structure):
                 ("is_causal", C.c_int32), ("scale", C.c_float), ("tile", C.c_int32),
                 ("row_group", C.c_int32), ("fmt", C.c_int32), ("tau", C.c_float),
                 ("hot_frame_offset", C.c_float), ("pass1_schedule", C.c_int32),
-                ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32)]
+                ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32), ("window", C.c_int32)]
 
 
 class Fp4Layout(C.Structure):
@@ -93,13 +93,14 @@ def status_string(code: int) -> str:
 
 
 def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
-            fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0) -> Problem:
+            fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0, window=0) -> Problem:
     p = Problem()
     lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
     p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt, p.pass1_schedule = (
         dtype, causal, scale, tau, hoff, fmt, sched)
     p.q_terms = q_terms
     p.k_scale_lsq = k_lsq
+    p.window = window
     return p
 
 

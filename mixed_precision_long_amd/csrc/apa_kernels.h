@@ -12,6 +12,8 @@ struct Geom {
   int sched;  // requested pass-1 schedule (APA_SCHED_*)
   int qterms; // FP4 terms of Q: 1, or 2 with the residual term
   int klsq;   // 1: K block exponents by least squared error
+  int window; // > 0: causal sliding window of this many keys (row r sees
+              // keys r + off - window < k <= r + off); 0: none
 };
 
 // Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the

@@ -46,6 +46,7 @@ bool valid_problem(const apa_problem* p) {
   if (p->pass1_schedule < APA_SCHED_AUTO || p->pass1_schedule > APA_SCHED_TRIPLES) return false;
   if (p->q_terms != 1 && p->q_terms != 2) return false;
   if (p->k_scale_lsq != 0 && p->k_scale_lsq != 1) return false;
+  if (p->window < 0 || (p->window > 0 && !p->is_causal)) return false;
   return true;
 }
 
@@ -68,6 +69,7 @@ Geom geom(const apa_problem* p) {
   g.sched = p->pass1_schedule;
   g.qterms = p->q_terms;
   g.klsq = p->k_scale_lsq;
+  g.window = p->window;
   return g;
 }
 
@@ -236,6 +238,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->pass1_schedule = APA_SCHED_AUTO;
   p->q_terms = 1;
   p->k_scale_lsq = 0;
+  p->window = 0;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }

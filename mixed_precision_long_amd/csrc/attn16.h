@@ -117,8 +117,15 @@ __device__ __forceinline__ WaveRows wave_rows(const Geom& g, const RowBlocks& rb
   return w;
 }
 
+// The first key tile a row from `first_row` on sees with a sliding window
+// (row r sees keys r + off - window < k <= r + off); 0 without one.
+__host__ __device__ inline int window_lo(const Geom& g, int first_row) {
+  const int first_key = first_row + g.off - g.window + 1;
+  return g.causal && g.window > 0 && first_key > 0 ? first_key / kTile : 0;
+}
+
 // The key tiles a work group visits in exact mode: up to the diagonal of its
-// last live row.
+// last live row (from window_lo of its first row).
 __device__ __forceinline__ int exact_tiles(const Geom& g, const RowBlocks& rb, int wg) {
   const int jl = min(wg * kWgWaves + kWgWaves - 1, rb.nrb - 1);
   const int lr = min((jl / g.G) * 32 + 31, g.Nq - 1);

@@ -97,13 +97,16 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   const bool row_ok = wr.live && row < g.Nq;
   const int d_wave =
       wr.live ? (g.causal ? min(g.Nkv - 1, min(r0 + 31, g.Nq - 1) + g.off) / kTile : g.NT - 1) : -1;
+  const int lo_wave = window_lo(g, r0);  // with a sliding window, the first tile it sees
 
   // this split's part of the work group's tile list
-  int lo, hi;
+  int lo, hi, base = 0;
   const int32_t* tiles = nullptr;
   const uint32_t* masks = nullptr;
   {
-    const int ntot = MODE == kExact ? exact_tiles(g, rb, wg) : a.list_count[unit];
+    // exact: the tiles from the first row's window start to the last row's diagonal
+    if (MODE == kExact) base = window_lo(g, wave_rows(g, rb, wg, 0).r0);
+    const int ntot = MODE == kExact ? exact_tiles(g, rb, wg) - base : a.list_count[unit];
     lo = split_lo(ntot, sp, S);
     hi = split_lo(ntot, sp + 1, S);
     if (MODE == kPass2) {
@@ -111,7 +114,7 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
       masks = a.list_masks + (size_t)unit * g.NT;
     }
   }
-  auto tile_at = [&](int it) { return MODE == kExact ? it : tiles[it]; };
+  auto tile_at = [&](int it) { return MODE == kExact ? base + it : tiles[it]; };
 
   // resident Q^T operand: 8 elements per 16-channel chunk
   V8 qf[NC];
@@ -185,7 +188,7 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
     // does this wave compute tile t, and for which of its two groups?
     bool on0, on1;
     if (MODE == kExact) {
-      on0 = on1 = t <= d_wave;
+      on0 = on1 = t <= d_wave && t >= lo_wave;
     } else {
       const uint32_t mk = masks[it];
       on0 = (mk >> (2 * wave)) & 1u;
@@ -229,16 +232,19 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
           for (int c = 0; c < 2; ++c) vf[db][kb][c] = vread(db, kb, c);
     }
     // ---- key masking: diagonal and padding tiles, rows past Nq (wave-uniform)
+    const bool win = g.causal && g.window > 0;
     const bool need_mask = (k0 + kTile > g.Nkv) || (g.causal && k0 + kTile - 1 > r0 + g.off) ||
-                           (r0 + 31 >= g.Nq);
+                           (r0 + 31 >= g.Nq) || (win && k0 <= r0 + 31 + g.off - g.window);
     if (need_mask) {
       const int lim = g.causal ? row + g.off : 0x7fffffff;
+      const int lim_lo = win ? row + g.off - g.window : -1;  // keys <= lim_lo: outside the window
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-          if (!(row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+          if (!(row_ok && key < g.Nkv && key <= lim && key > lim_lo))
+            acc[kb][j] = -__builtin_inff();
         }
     }
     // ---- row maximum (raw), then in log2 units; lazy move of m

@@ -273,7 +273,12 @@ template <int D>
 struct CtxBase {
   size_t bhq, bhk;
   int r0, row, d0, d1, dW;
-  int tmask;  // tiles t >= tmask need the mask (diagonal, padding keys, rows past Nq)
+  // sliding window: the first tile each verdict group sees (0 without one);
+  // sh = 1 when the walk starts with tile 0 (the first row sees it), so
+  // position p is tile 0 for p = 0 and dW + 1 - p after; sh = 0: dW - p
+  int lo0, lo1, sh;
+  int tmask;     // tiles t >= tmask need the mask (diagonal, padding keys, rows past Nq)
+  int tmask_lo;  // tiles t < tmask_lo need the window's lower mask
   bool row_ok, has_g1;
   v4i qa[Tile<D>::NH];  // Q^T operand, 16 bytes per 64-channel half
   int qs[Tile<D>::NH];  // its E8M0 bytes (block scale + head exponent)
@@ -283,6 +288,9 @@ struct CtxBase {
   bool lead;  // the wave that writes the row scalars and hot words (dh = 0)
   float g_v;
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
+  // the visit order: positions [0, npos()), position p at tile tile_of(p)
+  __device__ __forceinline__ int npos() const { return dW + 1 - lo0; }
+  __device__ __forceinline__ int tile_of(int p) const { return sh && p == 0 ? 0 : dW + sh - p; }
 };
 
 // The context with one Q term, and with two (the FP4 residual of Q as a
@@ -315,6 +323,16 @@ __device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4
   c.d0 = diag(min(c.r0 + 15, g.Nq - 1));
   c.d1 = c.has_g1 ? diag(min(c.r0 + 31, g.Nq - 1)) : -1;
   c.dW = max(c.d0, c.d1);
+  // with a window, the first key of row r is r + off - window + 1
+  const bool win = g.causal && g.window > 0;
+  auto first_tile = [&](int fr) { return win ? max(0, fr + g.off - g.window + 1) / kTile : 0; };
+  c.lo0 = first_tile(c.r0);
+  c.lo1 = c.has_g1 ? first_tile(c.r0 + 16) : 0x7fffffff;
+  c.sh = c.lo0 == 0 ? 1 : 0;
+  {
+    const int e = c.r0 + 31 + g.off - g.window;  // keys <= e are outside some row's window
+    c.tmask_lo = win && e >= 0 ? e / kTile + 1 : 0;
+  }
   // a tile needs the mask when it holds keys past Nkv (t >= Nkv / 64), keys
   // past a row's diagonal (64 t + 63 > r0 + off) or rows past Nq
   c.tmask = c.r0 + 31 >= g.Nq ? 0 : min(g.Nkv / kTile, g.causal ? (c.r0 + g.off + 1) / kTile : g.NT);
@@ -493,14 +511,16 @@ template <int D>
 __device__ __forceinline__ void mask_scores(v16f (&acc)[2], const Geom& g, const CtxBase<D>& c, int t,
                                             int hh) {
   const int k0 = t * kTile;
-  if (t >= c.tmask) {
+  if (t >= c.tmask || t < c.tmask_lo) {
     const int lim = g.causal ? c.row + g.off : 0x7fffffff;
+    const int lim_lo = g.causal && g.window > 0 ? c.row + g.off - g.window : -1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int key = k0 + kb * 32 + 8 * (j >> 2) + 4 * hh + (j & 3);
-        if (!(c.row_ok && key < g.Nkv && key <= lim)) acc[kb][j] = -__builtin_inff();
+        if (!(c.row_ok && key < g.Nkv && key <= lim && key > lim_lo))
+          acc[kb][j] = -__builtin_inff();
       }
   }
 }
@@ -585,15 +605,16 @@ __device__ __forceinline__ v4i p_operand(const v16f (&acc)[2], int x0, int x1, f
 }
 
 // The hot words of a walk's positions [P0, P0 + np) from its verdict log
-// (tile t at vlog[t]): the tiles dW - P0 - np + 2 .. dW - max(P0, 1) + 1 and,
-// when P0 = 0, tile 0.  Lane j builds word w_lo + j; words 0 and wb go to the
-// partial words, the others are stored.
+// (tile t at vlog[t]): the tiles of positions max(P0, sh) .. P0 + np - 1 (a
+// descending run) and, when the order starts with tile 0 and P0 = 0, tile 0.
+// Lane j builds word w_lo + j; words 0 and wb go to the partial words, the
+// others are stored.
 template <int D>
 __device__ __forceinline__ void assemble_words(const CtxBase<D>& c, Words& wd, const lds_u8* vlog,
                                                int P0, int np, int lane) {
-  const int t_hi = c.dW - (P0 > 0 ? P0 : 1) + 1;
-  const int t_lo = c.dW - P0 - np + 2;
-  if (P0 == 0 && np > 0) {
+  const int t_hi = c.dW + c.sh - max(P0, c.sh);  // tile of the first position past tile 0
+  const int t_lo = c.dW + c.sh - (P0 + np - 1);  // tile of the last position
+  if (c.sh && P0 == 0 && np > 0) {
     const uint32_t v = vlog[0];
     wd.p00 |= v & 1u;
     wd.p01 |= v >> 1;
@@ -653,10 +674,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& s
   // lanes of verdict group 0 (rows r0 .. r0+15) in both lane halves
   constexpr unsigned long long kGroup0 = 0x0000FFFF0000FFFFull;
   const bool tail = TAIL;  // a tail walk (nrep > 0); its own copy of the loop
-  auto tile_at = [&](int i) {
-    const int p = i < nrep ? i : p0 + (i - nrep);
-    return p == 0 ? 0 : c.dW - p + 1;
-  };
+  auto tile_at = [&](int i) { return c.tile_of(i < nrep ? i : p0 + (i - nrep)); };
   float lam_lo = 0.0f;
   int mo_ref = 0;
   int ncand = 0;
@@ -714,7 +732,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& s
     }
     if (!TAIL && i == kReplay) mo_ref = st.mo;
 
-    const bool vis0 = t <= c.d0, vis1 = t <= c.d1;
+    const bool vis0 = t <= c.d0 && t >= c.lo0, vis1 = t <= c.d1 && t >= c.lo1;
     mask_scores<D>(acc, g, c, t, hh);
     float b0, b1;
     group_maxima(acc, b0, b1);
@@ -880,13 +898,19 @@ __device__ __forceinline__ void store_state(const Geom& g, const CtxBase<D>& c, 
     }
 }
 
-// zero the hot words above each group's diagonal word
+// zero the hot words the walk does not write: those above each group's
+// diagonal word, and, with a window, those between word 0 (always written as
+// a partial word) and the word of the walk's first tile
 template <int D>
-__device__ __forceinline__ void zero_above(const Geom& g, const CtxBase<D>& c, int lane) {
+__device__ __forceinline__ void zero_outside(const Geom& g, const CtxBase<D>& c, int lane) {
   if (!c.lead) return;
   for (int w = c.d0 / 32 + 1 + lane; w < g.W; w += 64) c.bits0[w] = 0u;
   if (c.has_g1)
     for (int w = c.d1 / 32 + 1 + lane; w < g.W; w += 64) c.bits1[w] = 0u;
+  for (int w = 1 + lane; w < c.lo0 / 32; w += 64) {
+    c.bits0[w] = 0u;
+    if (c.has_g1) c.bits1[w] = 0u;
+  }
 }
 
 // The tail's end of a split unit, once the head's final state is in LDS:
@@ -1099,13 +1123,13 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u0), lane, dh);
     load_q2<D>(c, g, f, lane);
-    const int npos = c.dW + 1;
+    const int npos = c.npos();
     const int h = split_cut(npos, sched);  // head positions [0, h), tail [h, npos)
     if (h >= npos) role = kWhole;  // nothing to cut: its tail wave skips it
     St<D> st;
     init_state<D>(st, c.row_ok);
-    Words wd = {role == kWhole ? -1 : shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
-    zero_above<D>(g, c, lane);
+    Words wd = {role == kWhole ? -1 : shared_word(c.tile_of(h)), 0u, 0u, 0u, 0u};
+    zero_outside<D>(g, c, lane);
     walk<D, LOG, false>(g, c, st, wd, 0, 0, role == kWhole ? npos : h, eps, tau, Hf,
                         cand_of(f.kv_blob, 0, 0, D), 0, nullptr,
                         role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane,
@@ -1153,13 +1177,13 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
     load_q2<D>(c, g, f, lane);
-    const int npos = c.dW + 1;
+    const int npos = c.npos();
     const int h = split_cut(npos, sched);
     int oc = -2;
     if (h < npos) {
       St<D> st;
       init_state<D>(st, c.row_ok);
-      Words wd = {shared_word(c.dW - h + 1), 0u, 0u, 0u, 0u};
+      Words wd = {shared_word(c.tile_of(h)), 0u, 0u, 0u, 0u};
       oc = walk<D, LOG, true>(g, c, st, wd, kReplay, h, kReplay + npos - h, eps, tau, Hf,
                               cand_of(split, u, cap, D), cap,
                               (volatile lds_float*)pub[slot + k], nullptr, vlog, lane, pace_me,
@@ -1179,7 +1203,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     Ctx<D, QT> c;
     make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
     load_q2<D>(c, g, f, lane);
-    const int wb = shared_word(c.dW - split_cut(c.dW + 1, sched) + 1);
+    const int wb = shared_word(c.tile_of(split_cut(c.npos(), sched)));
     float* ho = handoff_of<D>(split, u, cap);
     HeadState<D>& H = hs[slot + k];
     while (__hip_atomic_load(&H.done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
@@ -1254,11 +1278,11 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   Ctx<D, QT> c;
   make_ctx<D>(c, g, f, out, id, lane);
   load_q2<D>(c, g, f, lane);
-  const int npos = c.dW + 1;
+  const int npos = c.npos();
   const int h = split_cut(npos, sched);
   if (h >= npos) return;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(base)) >= 0) return;
-  const int wb = shared_word(c.dW - h + 1);
+  const int wb = shared_word(c.tile_of(h));
   const float* src = reinterpret_cast<const float*>(base + cand_bytes(cap));
   St<D> st;
 #pragma unroll

@@ -77,9 +77,13 @@ def test_sizes_and_layout():
     ("is_causal", 2), ("tau", -1.0), ("tau", 40.0), ("hot_frame_offset", 2.5),
     ("hot_frame_offset", 65.0),
     ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4),
-    ("q_terms", 0), ("q_terms", 3), ("k_scale_lsq", 2)])
+    ("q_terms", 0), ("q_terms", 3), ("k_scale_lsq", 2), ("window", -1),
+    ("window+noncausal", 4096)])
 def test_invalid_problems_are_rejected(field, value):
-    p = prob(**{field: value})
+    if field == "window+noncausal":
+        p = prob(window=value, is_causal=0)  # a sliding window needs the causal mask
+    else:
+        p = prob(**{field: value})
     assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
         apa.APA_ERR_INVALID_ARG
     assert apa.fp4_bytes(p) == 0
