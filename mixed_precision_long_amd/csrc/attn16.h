@@ -22,6 +22,13 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+// Memory a kernel only reads and that no wave writes while it runs (the
+// compacted tile lists of pass 2, written by an earlier launch): reads through
+// the constant address space become scalar loads, which wait on their own
+// counter instead of the vector-memory counter that also tracks the
+// LDS-writing tile loads in flight.
+typedef __attribute__((address_space(4))) const int32_t cint32;
+typedef __attribute__((address_space(4))) const uint32_t cuint32;
 
 // 16-bit element types: the MFMA and the conversions.
 template <typename T>

@@ -83,8 +83,8 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
 
   // this split's part of the work group's tile list
   int lo, hi, base = 0;
-  const int32_t* tiles = nullptr;
-  const uint32_t* masks = nullptr;
+  const cint32* tiles = nullptr;
+  const cuint32* masks = nullptr;
   {
     // exact: the tiles from the first row's window start to the last row's diagonal
     if (MODE == kExact) base = window_lo(g, wave_rows(g, rb, wg, 0).r0);
@@ -92,8 +92,8 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
     lo = split_lo(ntot, sp, S);
     hi = split_lo(ntot, sp + 1, S);
     if (MODE == kPass2) {
-      tiles = a.list_tiles + (size_t)unit * g.NT;
-      masks = a.list_masks + (size_t)unit * g.NT;
+      tiles = (const cint32*)(a.list_tiles + (size_t)unit * g.NT);
+      masks = (const cuint32*)(a.list_masks + (size_t)unit * g.NT);
     }
   }
   auto tile_at = [&](int it) { return MODE == kExact ? base + it : tiles[it]; };
@@ -160,11 +160,17 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
 
   // stages: the two 32-key halves of each tile of the range, in order
   const int nst = 2 * (hi - lo);
-  if (nst > 0) issue(tile_at(lo), 0, 0);
+  int t_cur = nst > 0 ? tile_at(lo) : 0;
+  if (nst > 0) issue(t_cur, 0, 0);
   for (int q = 0; q < nst; ++q) {
     const int it = lo + (q >> 1), half = q & 1;
-    const int t = tile_at(it);
     const int sb = q & 1;
+    // the next tile's index and this tile's mask (scalar loads), read before
+    // the wait so their latency hides behind it
+    const int t = t_cur;
+    const int t_next = half && it + 1 < hi ? tile_at(it + 1) : t;
+    t_cur = t_next;
+    const uint32_t mk = MODE == kPass2 ? masks[it] : 0u;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of the stage are in LDS
     if (BF) {
       // the V rows this wave loaded, to fp16 in place
@@ -176,14 +182,13 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
       }
     }
     __syncthreads();
-    if (q + 1 < nst) issue(half ? tile_at(it + 1) : t, half ^ 1, sb ^ 1);
+    if (q + 1 < nst) issue(t_next, half ^ 1, sb ^ 1);
 
     // does this wave compute tile t, and for which of its two groups?
     bool on0, on1;
     if (MODE == kExact) {
       on0 = on1 = t <= d_wave && t >= lo_wave;
     } else {
-      const uint32_t mk = masks[it];
       on0 = (mk >> (2 * wave)) & 1u;
       on1 = (mk >> (2 * wave + 1)) & 1u;
     }

@@ -101,8 +101,8 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
 
   // this split's part of the work group's tile list
   int lo, hi, base = 0;
-  const int32_t* tiles = nullptr;
-  const uint32_t* masks = nullptr;
+  const cint32* tiles = nullptr;
+  const cuint32* masks = nullptr;
   {
     // exact: the tiles from the first row's window start to the last row's diagonal
     if (MODE == kExact) base = window_lo(g, wave_rows(g, rb, wg, 0).r0);
@@ -110,8 +110,8 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
     lo = split_lo(ntot, sp, S);
     hi = split_lo(ntot, sp + 1, S);
     if (MODE == kPass2) {
-      tiles = a.list_tiles + (size_t)unit * g.NT;
-      masks = a.list_masks + (size_t)unit * g.NT;
+      tiles = (const cint32*)(a.list_tiles + (size_t)unit * g.NT);
+      masks = (const cuint32*)(a.list_masks + (size_t)unit * g.NT);
     }
   }
   auto tile_at = [&](int it) { return MODE == kExact ? base + it : tiles[it]; };
@@ -168,10 +168,15 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   for (int i = 0; i < ND; ++i) o[i] = v16f{};
   const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-  if (lo < hi) issue(tile_at(lo), 0);
+  int t_next = lo < hi ? tile_at(lo) : 0;
+  if (lo < hi) issue(t_next, 0);
   for (int it = lo; it < hi; ++it) {
-    const int t = tile_at(it);
+    const int t = t_next;
     const int sb = (it - lo) & 1;
+    // the next tile's index and this tile's mask (scalar loads), read before
+    // the wait so their latency hides behind it
+    t_next = it + 1 < hi ? tile_at(it + 1) : 0;
+    const uint32_t mk = MODE == kPass2 ? masks[it] : 0u;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads of tile t are in LDS
     if (BF) {
       // the V rows this wave loaded, to fp16 in place
@@ -183,14 +188,13 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
       }
     }
     __syncthreads();
-    if (it + 1 < hi) issue(tile_at(it + 1), sb ^ 1);
+    if (it + 1 < hi) issue(t_next, sb ^ 1);
 
     // does this wave compute tile t, and for which of its two groups?
     bool on0, on1;
     if (MODE == kExact) {
       on0 = on1 = t <= d_wave && t >= lo_wave;
     } else {
-      const uint32_t mk = masks[it];
       on0 = (mk >> (2 * wave)) & 1u;
       on1 = (mk >> (2 * wave + 1)) & 1u;
     }
