@@ -33,6 +33,14 @@ struct Fp4Ptrs {
 
 __host__ __device__ inline size_t blob_bytes(int D) { return (size_t)68 * D; }
 
+// The first key tile any query row sees: 0, or with a sliding window the
+// tile of row 0's first key (Nkv - Nq - window + 1).  K/V statistics and
+// codes cover the tiles from there on; earlier blobs are never read.
+__host__ __device__ inline int first_key_tile(const Geom& g) {
+  const int k = g.off - g.window + 1;
+  return g.causal && g.window > 0 && k > 0 ? k / 64 : 0;
+}
+
 struct QuantWs {
   double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
   float* kmin;    // [B*Hkv][NCH][D]
@@ -42,6 +50,7 @@ struct QuantWs {
   unsigned* flags;  // [NKB + NQB] per statistics block: a non-finite input seen
   int nqt;        // ceil(Nq / 64)
   int nch;        // ceil(NT / 16)
+  int ch0;        // first chunk holding a tile some row sees (first_key_tile / 16)
   int nflags;     // NKB + NQB
 };
 

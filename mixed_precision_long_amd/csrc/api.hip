@@ -125,6 +125,7 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
     ws->flags = (unsigned*)(bb + fl);
     ws->nqt = nqt;
     ws->nch = nch;
+    ws->ch0 = first_key_tile(g) / 16;
     ws->nflags = (int)nflags;
   }
   return o;

@@ -52,7 +52,7 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-  if (t < g.NT) {
+  if (t < g.NT && t >= first_key_tile(g)) {
     const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
 #pragma unroll 4
     for (int k = k0; k < k1; ++k) {
@@ -151,7 +151,7 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
   double s = 0.0;
   float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int c0 = 0; c0 < ws.nch; c0 += kFinBatch) {
+  for (int c0 = ws.ch0; c0 < ws.nch; c0 += kFinBatch) {
     if (own) {
       // channel d's chunk sums, added in ascending order
       double v[kFinBatch];
@@ -185,19 +185,24 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   if (own) {
     mn = xch[d];
     mx = xch[D + d];
-    const float kb = g.Nkv > 0 ? (float)(s / (double)g.Nkv) : 0.0f;
+    const int nk = g.Nkv - first_key_tile(g) * kTile;  // the keys the statistics cover
+    const float kb = nk > 0 ? (float)(s / (double)nk) : 0.0f;
     f.kbar[(size_t)bh * D + d] = kb;
     if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
   }
-  // non-finite inputs anywhere (every block reads all flags; block 0 writes)
+  // non-finite inputs anywhere (every block reads all flags; block 0 writes);
+  // the K/V flags of chunks before ch0 were not written
   unsigned badf = 0u;
+  const int nkvf = ws.nflags - (g.Nq > 0 ? g.B * g.Hq * ws.nqt : 0);
 #pragma unroll 8
-  for (int i = d; i < ws.nflags; i += nthr) badf |= ws.flags[i];
+  for (int i = d; i < ws.nflags; i += nthr)
+    if (i >= nkvf || i % ws.nch >= ws.ch0) badf |= ws.flags[i];
   badf = __syncthreads_or(badf != 0u);
   if (bh == 0 && d == 0) *f.status = badf ? 1u : 0u;
   const float amax_k = block_max(dev, red);
   float va = 0.0f;
-  for (int c = d; c < ws.nch; c += blockDim.x) va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
+  for (int c = ws.ch0 + d; c < ws.nch; c += blockDim.x)
+    va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
   const float amax_v = block_max(va, red);
   float gk, ik, gv, iv;
   head_scale(amax_k, &gk, &ik);
@@ -433,10 +438,13 @@ __global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const 
   extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
   __shared__ float red[16];
   if ((int)blockIdx.x < nkb) {
-    kv_stats<T>(K, V, g, ws, blockIdx.x % ws.nch, blockIdx.x / ws.nch, sh, red);
+    const int nc = ws.nch - ws.ch0;  // chunks from the first one some row sees
+    kv_stats<T>(K, V, g, ws, ws.ch0 + blockIdx.x % nc, blockIdx.x / nc, sh, red);
   } else {
     const int qb = blockIdx.x - nkb;
-    q_stats<T>(Q, g, ws, blockIdx.x, qb % ws.nqt, qb / ws.nqt, red);
+    // Q flags follow every (kv-head, chunk) slot, written or not
+    const int qflag0 = ws.nflags - g.B * g.Hq * ws.nqt;
+    q_stats<T>(Q, g, ws, qflag0 + qb, qb % ws.nqt, qb / ws.nqt, red);
   }
 }
 
@@ -461,9 +469,10 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
     return;
   }
   b -= nq;
-  const int per_tile = kpt + nvb_z, per_head = g.NT * per_tile;
+  const int t0 = first_key_tile(g);
+  const int per_tile = kpt + nvb_z, per_head = (g.NT - t0) * per_tile;
   const int bh = g.B * g.Hkv - 1 - b / per_head;
-  const int r = b % per_head, t = r / per_tile, j = r % per_tile;
+  const int r = b % per_head, t = t0 + r / per_tile, j = r % per_tile;
   if (j < kpt)
     quant_rows<T, false>(K, g, f, t * kpt + j, bh);
   else
@@ -482,7 +491,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
     if (e != hipSuccess) return e;
     stats_attr = true;
   }
-  const int nkb = g.Nkv > 0 ? ws.nch * nkvh : 0;
+  const int nkb = g.Nkv > 0 ? (ws.nch - ws.ch0) * nkvh : 0;
   const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(2 * g.D), stats_lds, s, q, k, v, g, ws,
@@ -493,7 +502,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
   const int nvb_z = (g.D + 127) / 128;
   const long nq = (long)qpb * g.B * g.Hq;
-  const long nblk = nq + (long)g.NT * nkvh * (kpt + nvb_z);
+  const long nblk = nq + (long)(g.NT - first_key_tile(g)) * nkvh * (kpt + nvb_z);
   if (nblk > 0)
     hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpt,
                        nvb_z, qpb, (int)nq);

@@ -168,6 +168,14 @@ class Params:
     def block(self) -> int:
         return 16 if self.fmt == NV else 32
 
+    @property
+    def first_tile(self) -> int:
+        """The first key tile any query row sees: 0, or with a sliding window
+        the tile of the first key of row 0 (key Nkv - Nq - window + 1)."""
+        if self.window > 0 and self.causal:
+            return max(0, self.Nkv - self.Nq - self.window + 1) // self.tile
+        return 0
+
 
 # --------------------------------------------------------------------------
 # format helpers (thin wrappers, used by the pins)
@@ -229,7 +237,9 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
     """Stats and block-scaled FP4 quantisation of Q, K (centred), V (along keys).
 
     Q [B,Hq,Nq,D], K/V [B,Hkv,Nkv,D] float32 arrays holding the fp16/bf16
-    input values.  Returns codes, scale bytes and per-head scales.
+    input values.  Returns codes, scale bytes and per-head scales.  With a
+    sliding window the K/V statistics (key mean, per-head scales) and codes
+    cover the key tiles from first_tile on, the ones some row sees.
     """
     L = lib()
     cp = p.c()
@@ -256,11 +266,16 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
     ji = np.zeros(1, np.int32)
     for b in range(B):
         for hk in range(Hkv):
-            Kh = np.ascontiguousarray(K[b, hk])
-            Vh = np.ascontiguousarray(V[b, hk])
+            # statistics and codes over the key tiles some query row sees:
+            # all, or with a sliding window from first_tile on (the others
+            # are never read; their codes stay zero here)
+            k0 = p.first_tile * p.tile
+            nk = Nkv - k0
+            Kh = np.ascontiguousarray(K[b, hk, k0:])
+            Vh = np.ascontiguousarray(V[b, hk, k0:])
             kb = np.zeros(D, np.float32)
             am = np.zeros(1, np.float32)
-            L.orc_key_stats(_ptr(Kh), Nkv, D, p.tile, _ptr(kb), _ptr(am))
+            L.orc_key_stats(_ptr(Kh), nk, D, p.tile, _ptr(kb), _ptr(am))
             out["kbar"][b, hk] = kb
             out["amax_k"][b, hk] = am[0]
             L.orc_head_scale(C.c_float(am[0]), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
@@ -269,20 +284,20 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             out["amax_v"][b, hk] = av
             L.orc_head_scale(C.c_float(av), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
             out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]
-            kc = np.zeros((Nkv, D // 2), np.uint8)
-            ks = np.zeros((Nkv, D // bs), np.uint8)
+            kc = np.zeros((nk, D // 2), np.uint8)
+            ks = np.zeros((nk, D // bs), np.uint8)
             if p.k_lsq:
-                L.orc_quant_rows_lsq(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
+                L.orc_quant_rows_lsq(_ptr(Kh), nk, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
                                      _ptr(kc), _ptr(ks))
             else:
-                L.orc_quant_rows(_ptr(Kh), Nkv, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
+                L.orc_quant_rows(_ptr(Kh), nk, D, _ptr(kb), C.c_float(out["inv_k"][b, hk]),
                                  p.fmt, _ptr(kc), _ptr(ks))
-            out["kc"][b, hk], out["ks"][b, hk] = kc, ks
-            vc = np.zeros((D, NkvP // 2), np.uint8)
-            vs = np.zeros((D, NkvP // bs), np.uint8)
-            L.orc_quant_vt(_ptr(Vh), Nkv, NkvP, D, C.c_float(out["inv_v"][b, hk]), p.fmt,
+            out["kc"][b, hk, k0:], out["ks"][b, hk, k0:] = kc, ks
+            vc = np.zeros((D, (NkvP - k0) // 2), np.uint8)
+            vs = np.zeros((D, (NkvP - k0) // bs), np.uint8)
+            L.orc_quant_vt(_ptr(Vh), nk, NkvP - k0, D, C.c_float(out["inv_v"][b, hk]), p.fmt,
                            _ptr(vc), _ptr(vs))
-            out["vc"][b, hk], out["vs"][b, hk] = vc, vs
+            out["vc"][b, hk, :, k0 // 2:], out["vs"][b, hk, :, k0 // bs:] = vc, vs
         for h in range(Hq):
             Qh = np.ascontiguousarray(Q[b, h])
             aq = L.orc_absmax(_ptr(Qh), Qh.size)

@@ -75,13 +75,15 @@ def quantise_blocks(x: np.ndarray, bs: int = 32):
 QUANT_ALL = "QKVP"
 
 
-def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL):
+def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0: int = 0):
     """Per-head scales and dequantised operands (without the per-head factors
     that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry.
     q_terms=2 adds the quantised residual of Q (section "Second hunt": a second
     FP4 term for what the first leaves over, sharing its scale) to the
     dequantised Q.  An operand missing from `quant` is kept at its exact value
-    in normalised units (FP64, no clamp)."""
+    in normalised units (FP64, no clamp).  The K/V statistics (key mean,
+    per-head scales) are taken over keys k0.. (a sliding window's first visible
+    tile; 0 otherwise)."""
     Hq, Nq, D = Q.shape
     Hkv = K.shape[0]
     G = Hq // Hkv
@@ -89,16 +91,16 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL):
     out = []
     for hk in range(Hkv):
         Kh = K[hk].astype(np.float32)
-        kbar = f32(Kh.astype(np.float64).sum(axis=0) / Kh.shape[0])
+        kbar = f32(Kh[k0:].astype(np.float64).sum(axis=0) / (Kh.shape[0] - k0))
         kc = (Kh - kbar).astype(np.float32)              # fl32 subtraction
-        amax_k = np.abs(kc).max() if kc.size else np.float32(0)
+        amax_k = np.abs(kc[k0:]).max() if kc[k0:].size else np.float32(0)
         g_k = f32(amax_k / 6.0) if amax_k > 0 else np.float32(1)
         inv_k = f32(6.0 / amax_k) if amax_k > 0 else np.float32(1)
         kn = np.clip((kc * inv_k).astype(np.float32), -6, 6)
         kd = (quantise_blocks(kn) if "K" in quant else
               (Kh.astype(np.float64) - kbar.astype(np.float64)) * np.float64(inv_k))
         Vh = V[hk].astype(np.float32)
-        amax_v = np.abs(Vh).max()
+        amax_v = np.abs(Vh[k0:]).max()
         g_v = f32(amax_v / 6.0) if amax_v > 0 else np.float32(1)
         inv_v = f32(6.0 / amax_v) if amax_v > 0 else np.float32(1)
         vn = np.clip((Vh * inv_v).astype(np.float32), -6, 6)
@@ -219,7 +221,8 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
     off = Nkv - Nq
     nt = -(-Nkv // 64)
     ng = -(-Nq // 16)
-    ops = prepare(Q, K, V, scale, q_terms, quant)
+    k0 = max(0, off - window + 1) // 64 * 64 if (causal and window > 0) else 0
+    ops = prepare(Q, K, V, scale, q_terms, quant, k0)
     hot = np.zeros((Hq, ng, nt), bool)
     margin = np.full((Hq, ng, nt), np.nan)
     lo = np.zeros((Hq, Nq), np.float32)

@@ -41,13 +41,23 @@ def oracle_for(w, eps, causal, groups=None, q_terms=1, k_lsq=0):
     return p
 
 
-def check_quant(g, prep):
+def check_quant(g, prep, first_tile=0):
+    """Codes, scale bytes and per-head scales bitwise.  With a sliding window
+    the K/V codes are compared from the first tile some row sees on (the
+    library does not write the others; they are never read)."""
     f = g["fp4"]
     assert f["status"] == 0
+    cut = {"kc": (2, 64), "ks": (2, 64), "vc": (3, 32), "vs": (3, 2)}
     for k in ("qc", "qs", "kc", "ks", "vc", "vs", "qc2", "qs2"):
         assert (k in f) == (k in prep), k
         if k in f:
-            assert np.array_equal(f[k], prep[k]), k
+            a, b = f[k], prep[k]
+            if first_tile and k in cut:
+                ax, per = cut[k]
+                sl = [slice(None)] * a.ndim
+                sl[ax] = slice(first_tile * per, None)
+                a, b = a[tuple(sl)], b[tuple(sl)]
+            assert np.array_equal(a, b), k
     assert np.array_equal(f["kbar"], prep["kbar"])
     kv = f["kv_head"]
     assert np.array_equal(kv[..., 0], prep["amax_k"])

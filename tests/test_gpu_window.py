@@ -38,7 +38,7 @@ def test_window_matches_oracle(case):
     prep = O.quantize(po, Q, K, V)
     r = O.run(po, Q, K, V, prep)
     g = run_gpu(problem_for(w, window=window), Q, K, V, eps, dtype=dtype)
-    check_quant(g, prep)
+    check_quant(g, prep, po.first_tile)
     mism = check_mask(g["hot"], r)
     check_cold_state(g, r, mism)
     check_output(g["out"], r["O"], dtype=dtype)
@@ -70,7 +70,7 @@ def test_window_split_schedules(sched):
     r = O.run(po, Q, K, V, prep)
     g = run_gpu(p, Q, K, V, 0.02)
     assert len(g["tail"]) > 0
-    check_quant(g, prep)
+    check_quant(g, prep, po.first_tile)
     mism = check_mask(g["hot"], r)
     check_cold_state(g, r, mism)
     check_output(g["out"], r["O"])
@@ -86,7 +86,8 @@ def test_long3b_window_4096_every_group_of_one_kv_head():
     po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=w.eps, window=window)
     g = run_gpu(problem_for(w, window=window), Q, K, V, w.eps, lam=False)
     prep = O.quantize(po, Q, K, V)
-    check_quant(g, prep)
+    check_quant(g, prep, po.first_tile)
+    assert po.first_tile == (122880 - 2048 - 4096 + 1) // 64
     G = w.Hq // w.Hkv
     sel = np.array([(0, h, gg) for h in range(G) for gg in range(w.Nq // 16)], np.int32)
     r = O.run(po, Q, K, V, prep, groups=sel, nthreads=16)
