@@ -85,22 +85,44 @@ typedef struct apa_problem {
                                      row no longer sees tile 0 visits its tiles
                                      from the diagonal backwards; needs
                                      is_causal.  0: the full causal mask (0)   */
+  int32_t kv_capacity;            /* keys the FP4 buffer's K/V sections hold (a
+                                     persistent FP4 K/V cache for chunked
+                                     prefill: every chunk's problem names the
+                                     same capacity, so those sections keep their
+                                     size and place); >= Nkv.  0: Nkv (0)       */
+  int32_t stat_keys;              /* > 0: the K/V statistics (key mean, per-head
+                                     scales) cover the keys before this one --
+                                     chunked prefill keeps them from its last
+                                     restat (the APA page restats once the
+                                     context has grown by 1.125x); later keys
+                                     beyond their range clamp at the FP4
+                                     maximum.  0: all keys (0)                */
+  const int32_t* block_table;     /* paged 16-bit K/V (the APA page: pass 2 reads
+                                     through a block table): NULL, or a DEVICE
+                                     array [B][block_table_stride] of page
+                                     indices; then k and v of every call are
+                                     pools [pages][Hkv][64][D] and key k of
+                                     batch b is row k % 64 of page
+                                     block_table[b * stride + k / 64] (NULL) */
+  int32_t block_table_stride;     /* entries per batch row, >= ceil(Nkv / 64) */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
  * fp16, causal, APA_SCHED_AUTO, one Q term, nearest K block exponents, no
- * window. */
+ * window, capacity Nkv, statistics over all keys, flat K/V. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 
-/* Byte offsets of the sections of the FP4 buffer written by apa_quantize.
- * NqP = Nq rounded up to 32, NkvP = Nkv rounded up to 64; padding rows and
- * keys hold zero codes.  Codes pack two 4-bit E2M1 values per byte, element
+/* Byte offsets of the sections of the FP4 buffer written by apa_quantize,
+ * the K/V sections first (kv_blobs, kbar, kv_head, status: sized by the
+ * capacity, so a persistent cache keeps them), then the query sections.
+ * NqP = Nq rounded up to 32, NkvP = Nkv rounded up to 64, NTc = the capacity
+ * in 64-key tiles; padding rows and keys hold zero codes.  Codes pack two 4-bit E2M1 values per byte, element
  * 2i in the low nibble; a scale byte is an E8M0 exponent (value 2^(byte-127))
  * of one 32-element block.
  *   q_codes  [B][Hq][NqP][D/2]       Q along D
  *   q_scales [B][Hq][NqP][D/32]
- *   kv_blobs [B][Hkv][NkvP/64][68*D]  one blob per 64-key tile, in the
+ *   kv_blobs [B][Hkv][NTc][68*D]  one blob per 64-key tile, in the
  *            operand order of the pass-1 MFMAs:
  *              [0, 32D)    K - kbar codes, [64 keys][D/2], along D
  *              [32D, 34D)  K scales, [64 keys][D/32]
@@ -155,6 +177,23 @@ const char* apa_last_hip_error(void);
  * APA_CALL_QUANTIZE) bytes. */
 apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
                         void* fp4, void* ws, size_t ws_bytes, void* stream);
+
+/* Chunked prefill over a persistent FP4 K/V cache (the APA page, "What else
+ * is in the box": chunked prefill keeps the quantised tiles and only
+ * quantises new keys): quantises Q, and the K/V tiles [tile_begin, tile_end)
+ * of p, with the K/V statistics the FP4 buffer already holds (kbar and the
+ * per-head scales of an earlier apa_quantize of the same cache, i.e. the same
+ * kv_capacity and stat_keys), leaving every other blob and the statistics as
+ * they are.  Q's per-head scale ties to the cache's K scale as in
+ * apa_quantize.  A chunk whose keys are [0, Nkv) after a previous chunk
+ * ending at key N0 passes tile_begin = N0 / 64 (re-quantising a partly
+ * filled last tile).  The status word reports non-finite values among Q and
+ * the quantised tiles.  0 <= tile_begin <= tile_end <= ceil(Nkv / 64) (from
+ * the window's first tile with a window).  ws: apa_workspace_bytes(p,
+ * APA_CALL_QUANTIZE) bytes. */
+apa_status apa_quantize_tiles(const apa_problem* p, const void* q, const void* k, const void* v,
+                              void* fp4, int32_t tile_begin, int32_t tile_end, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /* For callers that cannot allocate device memory or call hipMalloc (code
  * under HIP graph capture, tight serving loops, harnesses that forbid it):

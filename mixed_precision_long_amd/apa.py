@@ -21,7 +21,7 @@ CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
            "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize",
-           "apa_quantize_static", "apa_pass1",
+           "apa_quantize_static", "apa_quantize_tiles", "apa_pass1",
            "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact"]
 
 
@@ -40,7 +40,9 @@ class Problem(C.Structure):
                 ("is_causal", C.c_int32), ("scale", C.c_float), ("tile", C.c_int32),
                 ("row_group", C.c_int32), ("fmt", C.c_int32), ("tau", C.c_float),
                 ("hot_frame_offset", C.c_float), ("pass1_schedule", C.c_int32),
-                ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32), ("window", C.c_int32)]
+                ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32), ("window", C.c_int32),
+                ("kv_capacity", C.c_int32), ("stat_keys", C.c_int32),
+                ("block_table", C.c_void_p), ("block_table_stride", C.c_int32)]
 
 
 class Fp4Layout(C.Structure):
@@ -79,6 +81,7 @@ def lib() -> C.CDLL:
         L.apa_pass1_split.restype = C.c_int32
         L.apa_quantize.argtypes = [P, VP, VP, VP, VP, VP, S, VP]
         L.apa_quantize_static.argtypes = [P, VP, VP, VP, VP, VP]
+        L.apa_quantize_tiles.argtypes = [P, VP, VP, VP, VP, C.c_int32, C.c_int32, VP, S, VP]
         L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
                                 VP, S, VP]
@@ -93,7 +96,10 @@ def status_string(code: int) -> str:
 
 
 def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
-            fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0, window=0) -> Problem:
+            fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0, window=0, kv_capacity=0,
+            stat_keys=0, block_table=None) -> Problem:
+    """block_table: a device int32 tensor [B, stride] of page indices (paged
+    K/V), or None."""
     p = Problem()
     lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
     p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt, p.pass1_schedule = (
@@ -101,6 +107,11 @@ def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4
     p.q_terms = q_terms
     p.k_scale_lsq = k_lsq
     p.window = window
+    p.kv_capacity = kv_capacity
+    p.stat_keys = stat_keys
+    if block_table is not None:
+        p.block_table = block_table.data_ptr()
+        p.block_table_stride = block_table.shape[-1]
     return p
 
 
@@ -155,6 +166,15 @@ def quantize(p: Problem, q, k, v, fp4, ws, stream=None):
     _check(lib().apa_quantize(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), _ptr(ws),
                               0 if ws is None else ws.numel() * ws.element_size(),
                               _stream(stream)), "apa_quantize")
+
+
+def quantize_tiles(p: Problem, q, k, v, fp4, tile_begin: int, tile_end: int, ws,
+                   stream=None):
+    """Q and the K/V tiles [tile_begin, tile_end) with the cache's statistics."""
+    _check(lib().apa_quantize_tiles(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4),
+                                    int(tile_begin), int(tile_end), _ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)), "apa_quantize_tiles")
 
 
 def quantize_static(p: Problem, q, k, v, fp4, stream=None):

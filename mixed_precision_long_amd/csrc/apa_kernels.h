@@ -14,7 +14,25 @@ struct Geom {
   int klsq;   // 1: K block exponents by least squared error
   int window; // > 0: causal sliding window of this many keys (row r sees
               // keys r + off - window < k <= r + off); 0: none
+  int NTc;    // key tiles per (b, kv-head) in the FP4 blob section (capacity >= NT)
+  int stat_hi;  // K/V statistics cover keys [first_key_tile * 64, stat_hi)
+  int qt0, qt1; // K/V tiles whose codes a quantise call writes
+  int frozen;   // 1: keep the FP4 buffer's K/V statistics (quantise only tiles)
+  // paged 16-bit K/V: logical tile t of batch b is page bt[b * bts + t] of
+  // pools [pages][Hkv][64][D]; nullptr: [B][Hkv][Nkv][D]
+  const int32_t* bt;
+  int bts;
 };
+
+// Element offset of key k of (b, kv-head hk) in a 16-bit K or V input.  The
+// 64 keys of a tile are contiguous in both layouts.
+__device__ __forceinline__ size_t kv_elem(const Geom& g, int b, int hk, int k) {
+  if (g.bt) {
+    const int pg = g.bt[(size_t)b * g.bts + (k >> 6)];
+    return (((size_t)pg * g.Hkv + hk) * 64 + (k & 63)) * g.D;
+  }
+  return (((size_t)b * g.Hkv + hk) * g.Nkv + k) * g.D;
+}
 
 // Per (b, kv-head, 64-key tile) FP4 blob of 68*D bytes, laid out for the
 // MFMA operands of pass 1:
@@ -41,6 +59,16 @@ __host__ __device__ inline int first_key_tile(const Geom& g) {
   return g.causal && g.window > 0 && k > 0 ? k / 64 : 0;
 }
 
+// The K/V tiles a quantise call reads for statistics, and the keys they
+// stop before: the tiles some row sees up to stat_hi; with frozen statistics
+// (quantising only tiles [qt0, qt1) of a persistent cache) those tiles,
+// read for their non-finite check alone.
+__host__ __device__ inline int stat_t0(const Geom& g) { return g.frozen ? g.qt0 : first_key_tile(g); }
+__host__ __device__ inline int stat_t1(const Geom& g) {
+  return g.frozen ? g.qt1 : (g.stat_hi + 63) / 64;
+}
+__host__ __device__ inline int stat_khi(const Geom& g) { return g.frozen ? g.Nkv : g.stat_hi; }
+
 struct QuantWs {
   double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
   float* kmin;    // [B*Hkv][NCH][D]
@@ -50,7 +78,7 @@ struct QuantWs {
   unsigned* flags;  // [NKB + NQB] per statistics block: a non-finite input seen
   int nqt;        // ceil(Nq / 64)
   int nch;        // ceil(NT / 16)
-  int ch0;        // first chunk holding a tile some row sees (first_key_tile / 16)
+  int ch0, ch1;   // the chunks holding the statistics tiles [stat_t0, stat_t1)
   int nflags;     // NKB + NQB
 };
 

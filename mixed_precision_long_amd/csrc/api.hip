@@ -47,6 +47,9 @@ bool valid_problem(const apa_problem* p) {
   if (p->q_terms != 1 && p->q_terms != 2) return false;
   if (p->k_scale_lsq != 0 && p->k_scale_lsq != 1) return false;
   if (p->window < 0 || (p->window > 0 && !p->is_causal)) return false;
+  if (p->kv_capacity < 0 || (p->kv_capacity > 0 && p->kv_capacity < p->Nkv)) return false;
+  if (p->stat_keys < 0 || p->stat_keys > p->Nkv) return false;
+  if (p->block_table && (p->block_table_stride < (p->Nkv + 63) / 64)) return false;
   return true;
 }
 
@@ -70,6 +73,13 @@ Geom geom(const apa_problem* p) {
   g.qterms = p->q_terms;
   g.klsq = p->k_scale_lsq;
   g.window = p->window;
+  g.NTc = p->kv_capacity > 0 ? (p->kv_capacity + 63) / 64 : g.NT;
+  g.stat_hi = p->stat_keys > 0 ? p->stat_keys : p->Nkv;
+  g.qt0 = first_key_tile(g);
+  g.qt1 = g.NT;
+  g.frozen = 0;
+  g.bt = p->block_table;
+  g.bts = p->block_table_stride;
   return g;
 }
 
@@ -78,14 +88,16 @@ void layout(const apa_problem* p, apa_fp4_layout* L) {
   const size_t B = p->B, Hq = p->Hq, Hkv = p->Hkv, D = p->D;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-  L->q_codes = take(B * Hq * g.NqP * D / 2);
-  L->q_scales = take(B * Hq * g.NqP * D / 32);
-  L->kv_blobs = take(B * Hkv * g.NT * blob_bytes(p->D));
+  // the K/V sections first (sized by the capacity), so that a persistent
+  // cache keeps them in place while the query sections change
+  L->kv_blobs = take(B * Hkv * g.NTc * blob_bytes(p->D));
   L->kbar = take(B * Hkv * D * 4);
   L->kv_head = take(B * Hkv * 8 * 4);
+  L->status = take(4);
+  L->q_codes = take(B * Hq * g.NqP * D / 2);
+  L->q_scales = take(B * Hq * g.NqP * D / 32);
   L->q_head = take(B * Hq * 4 * 4);
   L->q_frame = take(B * Hq * g.NqP * 4);
-  L->status = take(4);
   const size_t q2 = p->q_terms == 2 ? 1 : 0;
   L->q2_codes = take(q2 * B * Hq * g.NqP * D / 2);
   L->q2_scales = take(q2 * B * Hq * g.NqP * D / 32);
@@ -125,7 +137,8 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
     ws->flags = (unsigned*)(bb + fl);
     ws->nqt = nqt;
     ws->nch = nch;
-    ws->ch0 = first_key_tile(g) / 16;
+    ws->ch0 = stat_t0(g) / 16;
+    ws->ch1 = (stat_t1(g) + 15) / 16;
     ws->nflags = (int)nflags;
   }
   return o;
@@ -240,6 +253,10 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->q_terms = 1;
   p->k_scale_lsq = 0;
   p->window = 0;
+  p->kv_capacity = 0;
+  p->stat_keys = 0;
+  p->block_table = nullptr;
+  p->block_table_stride = 0;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
@@ -297,6 +314,29 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
   quant_ws(p, &w, ws);
   clear_hip_error();
   return hip_status(launch_quantize(geom(p), q, k, v, fp4_ptrs(p, fp4), w, (hipStream_t)stream));
+}
+
+apa_status apa_quantize_tiles(const apa_problem* p, const void* q, const void* k, const void* v,
+                              void* fp4, int32_t tile_begin, int32_t tile_end, void* ws,
+                              size_t ws_bytes, void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4) return APA_ERR_INVALID_ARG;
+  Geom g = geom(p);
+  if (tile_begin < first_key_tile(g) || tile_end > g.NT || tile_begin > tile_end)
+    return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_QUANTIZE)) return APA_ERR_UNSUPPORTED;
+  if (p->B == 0 || p->Hkv == 0) return APA_OK;
+  const size_t need = quant_ws(p, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return APA_ERR_WORKSPACE;
+  g.frozen = 1;
+  g.qt0 = tile_begin;
+  g.qt1 = tile_end;
+  QuantWs w;
+  quant_ws(p, &w, ws);
+  w.ch0 = tile_begin / 16;
+  w.ch1 = (tile_end + 15) / 16;
+  clear_hip_error();
+  return hip_status(launch_quantize(g, q, k, v, fp4_ptrs(p, fp4), w, (hipStream_t)stream));
 }
 
 apa_status apa_quantize_static(const apa_problem* p, const void* q, const void* k, const void* v,

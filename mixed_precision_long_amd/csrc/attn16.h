@@ -30,6 +30,23 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(4))) const int32_t cint32;
 typedef __attribute__((address_space(4))) const uint32_t cuint32;
 
+// Buffer resources over one key tile's 64 rows of a 16-bit K or V input
+// (flat, or the tile's page with a block table; the page index is a scalar
+// load) and the byte offset of key `key` (a key of tile t) inside it.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const Geom& g, const T* X, int b,
+                                                            int hk, int t) {
+  size_t e;
+  if (g.bt) {
+    const int pg = ((const cint32*)g.bt)[(size_t)b * g.bts + t];
+    e = ((size_t)pg * g.Hkv + hk) * 64 * g.D;
+  } else {
+    e = (((size_t)b * g.Hkv + hk) * g.Nkv + (size_t)t * 64) * g.D;
+  }
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X) + e, (short)0, 64 * g.D * 2,
+                                           0x00020000);
+}
+
 // 16-bit element types: the MFMA and the conversions.
 template <typename T>
 struct E16;

@@ -117,18 +117,17 @@ __device__ __forceinline__ void big_body(const Geom& g, const T* __restrict__ Q,
   // lane L carries key 16 (w % 2) + L / 4 and the row's 16-byte slot L % 4
   // (K: channel chunk (L % 4) ^ ((key / 4) % 4), so the slot holds that chunk;
   // V: chunk L % 4).
-  const size_t head_bytes = (size_t)g.Nkv * D * 2;
-  const auto rK = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(K) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
-  const auto rV = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(V) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
   const int kblk = wave & 1, g0 = wave >> 1;
+  const int b_ = (int)(bhk / g.Hkv), hk_ = (int)(bhk % g.Hkv);
   const uint32_t cK = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
   const uint32_t cV = (uint32_t)((lane & 3) * 16);
   auto issue = [&](int t, int half, int sb) {
     // rows past the last key re-read the last key (their scores are masked)
+    // one tile's rows (flat or paged)
+    const auto rK = tile_rsrc<T>(g, K, b_, hk_, t);
+    const auto rV = tile_rsrc<T>(g, V, b_, hk_, t);
     const int key = t * kTile + half * C::KEYS + 16 * kblk + (lane >> 2);
-    const uint32_t rowoff = (uint32_t)min(key, g.Nkv - 1) * (uint32_t)(D * 2);
+    const uint32_t rowoff = (uint32_t)(min(key, g.Nkv - 1) - t * kTile) * (uint32_t)(D * 2);
     uint8_t* st = big_smem + sb * C::STAGE + kblk * 1024;
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {

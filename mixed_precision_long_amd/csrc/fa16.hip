@@ -133,17 +133,17 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   // LDS-writing loads: wave w loads 16-key block w of every 32-channel group;
   // lane L carries key 16w + L/4 and the row's 16-byte slot L%4 (K: chunk
   // (L%4) ^ ((key/4)%4), so the slot holds that chunk; V: chunk L%4).
-  const size_t head_bytes = (size_t)g.Nkv * D * 2;
-  const auto rK = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(K) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
-  const auto rV = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<T*>(V) + bhk * (size_t)g.Nkv * D, (short)0, (int)head_bytes, 0x00020000);
   const int ckey = wave * 16 + (lane >> 2);
   const uint32_t cK = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
   const uint32_t cV = (uint32_t)((lane & 3) * 16);
+  const int b_ = (int)(bhk / g.Hkv), hk_ = (int)(bhk % g.Hkv);
   auto issue = [&](int t, int sb) {
-    // rows past the last key re-read the last key (their scores are masked)
-    const uint32_t rowoff = (uint32_t)min(t * kTile + ckey, g.Nkv - 1) * (uint32_t)(D * 2);
+    // one tile's rows (flat or paged); rows past the last key re-read the
+    // last key (their scores are masked)
+    const auto rK = tile_rsrc<T>(g, K, b_, hk_, t);
+    const auto rV = tile_rsrc<T>(g, V, b_, hk_, t);
+    const uint32_t rowoff =
+        (uint32_t)(min(t * kTile + ckey, g.Nkv - 1) - t * kTile) * (uint32_t)(D * 2);
     uint8_t* st = fa_smem + sb * C::STAGE + wave * 1024;
 #pragma unroll
     for (int i = 0; i < C::NLD; ++i) {
@@ -471,17 +471,19 @@ __global__ void k_combine(Geom g, Fp4Ptrs f, Pass2Args a, int S, long nrows) {
 __global__ __launch_bounds__(256) void k_vmax(Geom g, const uint16_t* __restrict__ V, float* out,
                                               int nch) {
   const int c = blockIdx.x, bh = blockIdx.y;
-  const int k0 = c * kVmaxChunk, k1 = min(g.Nkv, k0 + kVmaxChunk);
-  const long n8 = (long)(k1 - k0) * g.D / 8;
-  const uint4* src = reinterpret_cast<const uint4*>(V + ((size_t)bh * g.Nkv + k0) * g.D);
   float m = 0.0f;
-  for (long i = threadIdx.x; i < n8; i += 256) {
-    const uint4 z = src[i];
-    const uint32_t w[4] = {z.x, z.y, z.z, z.w};
+  // the chunk's key tiles (contiguous rows each, flat or paged)
+  for (int t = c * (kVmaxChunk / 64); t < min(g.NT, (c + 1) * (kVmaxChunk / 64)); ++t) {
+    const long n8 = (long)min(64, g.Nkv - t * 64) * g.D / 8;
+    const uint4* src = reinterpret_cast<const uint4*>(V + kv_elem(g, bh / g.Hkv, bh % g.Hkv, t * 64));
+    for (long i = threadIdx.x; i < n8; i += 256) {
+      const uint4 z = src[i];
+      const uint32_t w[4] = {z.x, z.y, z.z, z.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[j] << 16)),
-                         fabsf(__uint_as_float(w[j] & 0xFFFF0000u))));
+      for (int j = 0; j < 4; ++j)
+        m = fmaxf(m, fmaxf(fabsf(__uint_as_float(w[j] << 16)),
+                           fabsf(__uint_as_float(w[j] & 0xFFFF0000u))));
+    }
   }
   __shared__ float red[4];
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));

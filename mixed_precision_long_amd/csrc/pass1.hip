@@ -346,7 +346,7 @@ __device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4
     c.qs[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
   }
   c.g_v = f.kv_head[c.bhk * 8 + 4];
-  c.blobs = blob_rsrc(f.kv_blob + c.bhk * (size_t)g.NT * Tile<D>::BLOB,
+  c.blobs = blob_rsrc(f.kv_blob + c.bhk * (size_t)g.NTc * Tile<D>::BLOB,
                       (uint32_t)g.NT * Tile<D>::BLOB);
   c.koff = n * (D / 2) + 16 * hh;
   c.ksoff = 32 * D + n * (D / 32);

@@ -45,19 +45,20 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
   const int D = g.D, ncg = D / 8;
   const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
   const int t = ch * 16 + tt;
-  const size_t base = (size_t)bh * g.Nkv * D + cg * 8;
   double s[8];
   float mn[8], mx[8];
   float va = 0.0f;
   bool bad = false;
 #pragma unroll
   for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-  if (t < g.NT && t >= first_key_tile(g)) {
-    const int k0 = t * kTile, k1 = min(g.Nkv, k0 + kTile);
+  if (t < g.NT && t >= stat_t0(g) && t < stat_t1(g)) {
+    const int k0 = t * kTile, k1 = min(min(g.Nkv, stat_khi(g)), k0 + kTile);
+    // the tile's keys are contiguous (flat or paged input)
+    const size_t base = kv_elem(g, bh / g.Hkv, bh % g.Hkv, k0) + cg * 8;
 #pragma unroll 4
     for (int k = k0; k < k1; ++k) {
-      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)k * D);
-      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)k * D);
+      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
+      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)(k - k0) * D);
       const T* ek = reinterpret_cast<const T*>(&rk);
       const T* evv = reinterpret_cast<const T*>(&rv);
 #pragma unroll
@@ -151,21 +152,21 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
   double s = 0.0;
   float mn = __builtin_inff(), mx = -__builtin_inff();
-  for (int c0 = ws.ch0; c0 < ws.nch; c0 += kFinBatch) {
+  for (int c0 = ws.ch0; c0 < ws.ch1 && !g.frozen; c0 += kFinBatch) {
     if (own) {
       // channel d's chunk sums, added in ascending order
       double v[kFinBatch];
 #pragma unroll
       for (int i = 0; i < kFinBatch; ++i)
-        v[i] = c0 + i < ws.nch ? ws.ksum[base + (size_t)(c0 + i) * D] : 0.0;
+        v[i] = c0 + i < ws.ch1 ? ws.ksum[base + (size_t)(c0 + i) * D] : 0.0;
 #pragma unroll
       for (int i = 0; i < kFinBatch; ++i)
-        if (c0 + i < ws.nch) s += v[i];
+        if (c0 + i < ws.ch1) s += v[i];
     } else {
       float a[kFinBatch], b[kFinBatch];
 #pragma unroll
       for (int i = 0; i < kFinBatch; ++i) {
-        const bool in = c0 + i < ws.nch;
+        const bool in = c0 + i < ws.ch1;
         a[i] = in ? ws.kmin[base + (size_t)(c0 + i) * D] : __builtin_inff();
         b[i] = in ? ws.kmax[base + (size_t)(c0 + i) * D] : -__builtin_inff();
       }
@@ -185,29 +186,31 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   if (own) {
     mn = xch[d];
     mx = xch[D + d];
-    const int nk = g.Nkv - first_key_tile(g) * kTile;  // the keys the statistics cover
+    const int nk = stat_khi(g) - stat_t0(g) * kTile;  // the keys the statistics cover
     const float kb = nk > 0 ? (float)(s / (double)nk) : 0.0f;
-    f.kbar[(size_t)bh * D + d] = kb;
-    if (g.Nkv > 0) dev = fmaxf(mx - kb, kb - mn);
+    if (!g.frozen) f.kbar[(size_t)bh * D + d] = kb;
+    if (nk > 0) dev = fmaxf(mx - kb, kb - mn);
   }
   // non-finite inputs anywhere (every block reads all flags; block 0 writes);
-  // the K/V flags of chunks before ch0 were not written
+  // only the K/V flags of chunks [ch0, ch1) were written
   unsigned badf = 0u;
   const int nkvf = ws.nflags - (g.Nq > 0 ? g.B * g.Hq * ws.nqt : 0);
 #pragma unroll 8
   for (int i = d; i < ws.nflags; i += nthr)
-    if (i >= nkvf || i % ws.nch >= ws.ch0) badf |= ws.flags[i];
+    if (i >= nkvf || (i % ws.nch >= ws.ch0 && i % ws.nch < ws.ch1)) badf |= ws.flags[i];
   badf = __syncthreads_or(badf != 0u);
   if (bh == 0 && d == 0) *f.status = badf ? 1u : 0u;
   const float amax_k = block_max(dev, red);
   float va = 0.0f;
-  for (int c = ws.ch0 + d; c < ws.nch; c += blockDim.x)
+  for (int c = ws.ch0 + d; c < ws.ch1; c += blockDim.x)
     va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
   const float amax_v = block_max(va, red);
   float gk, ik, gv, iv;
   head_scale(amax_k, &gk, &ik);
   head_scale(amax_v, &gv, &iv);
-  if (d == 0) {
+  // frozen statistics: the K/V scales stay the cache's; Q's tie to its g_K
+  if (g.frozen) gk = f.kv_head[(size_t)bh * 8 + 1];
+  if (d == 0 && !g.frozen) {
     float* kh = f.kv_head + (size_t)bh * 8;
     kh[0] = amax_k; kh[1] = gk; kh[2] = ik; kh[3] = amax_v; kh[4] = gv; kh[5] = iv;
     kh[6] = 0.0f; kh[7] = 0.0f;
@@ -303,7 +306,7 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
   float x[8];
   float cdot = 0.0f;
   if (row < Nrows) {
-    const T* src = X + ((size_t)bh * Nrows + row) * g.D + c8;
+    const T* src = X + (IS_Q ? ((size_t)bh * Nrows + row) * g.D : kv_elem(g, b, hk, row)) + c8;
     const uint4 raw = *reinterpret_cast<const uint4*>(src);
     const T* e = reinterpret_cast<const T*>(&raw);
     for (int i = 0; i < 8; ++i) {
@@ -337,7 +340,7 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
     crow = f.q_codes + r * (g.D / 2);
     srow = f.q_scales + r * (g.D / 32);
   } else {
-    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NT + row / kTile) * blob_bytes(g.D);
+    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + row / kTile) * blob_bytes(g.D);
     crow = blob + (row % kTile) * (g.D / 2);
     srow = blob + 32 * g.D + (row % kTile) * (g.D / 32);
   }
@@ -393,7 +396,8 @@ __device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& 
     const int kk = i / per_row, c = (i % per_row) * 8;
     const int key = k0 + kk;
     uint4 r = {0u, 0u, 0u, 0u};
-    if (key < g.Nkv) r = *reinterpret_cast<const uint4*>(V + ((size_t)bh * g.Nkv + key) * g.D + c0 + c);
+    if (key < g.Nkv)
+      r = *reinterpret_cast<const uint4*>(V + kv_elem(g, bh / g.Hkv, bh % g.Hkv, key) + c0 + c);
     *reinterpret_cast<uint4*>(&tile[kk][c]) = r;
   }
   __syncthreads();
@@ -423,7 +427,7 @@ __device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& 
     out[j] = w;
   }
   const int ch = c0 + c;
-  uint8_t* blob = f.kv_blob + ((size_t)bh * g.NT + t) * blob_bytes(g.D);
+  uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(g.D);
   uint4 o4 = {out[0], out[1], out[2], out[3]};
   *reinterpret_cast<uint4*>(blob + 34 * g.D + ch * 32 + half * 16) = o4;
   blob[66 * g.D + ((ch % 32) * 2 + half) * (g.D / 32) + ch / 32] = (uint8_t)(e + 127);
@@ -438,7 +442,7 @@ __global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const 
   extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
   __shared__ float red[16];
   if ((int)blockIdx.x < nkb) {
-    const int nc = ws.nch - ws.ch0;  // chunks from the first one some row sees
+    const int nc = ws.ch1 - ws.ch0;  // the chunks of the statistics tiles
     kv_stats<T>(K, V, g, ws, ws.ch0 + blockIdx.x % nc, blockIdx.x / nc, sh, red);
   } else {
     const int qb = blockIdx.x - nkb;
@@ -469,10 +473,9 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
     return;
   }
   b -= nq;
-  const int t0 = first_key_tile(g);
-  const int per_tile = kpt + nvb_z, per_head = (g.NT - t0) * per_tile;
+  const int per_tile = kpt + nvb_z, per_head = (g.qt1 - g.qt0) * per_tile;
   const int bh = g.B * g.Hkv - 1 - b / per_head;
-  const int r = b % per_head, t = t0 + r / per_tile, j = r % per_tile;
+  const int r = b % per_head, t = g.qt0 + r / per_tile, j = r % per_tile;
   if (j < kpt)
     quant_rows<T, false>(K, g, f, t * kpt + j, bh);
   else
@@ -491,7 +494,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
     if (e != hipSuccess) return e;
     stats_attr = true;
   }
-  const int nkb = g.Nkv > 0 ? (ws.nch - ws.ch0) * nkvh : 0;
+  const int nkb = g.Nkv > 0 ? (ws.ch1 - ws.ch0) * nkvh : 0;
   const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(2 * g.D), stats_lds, s, q, k, v, g, ws,
@@ -502,7 +505,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
   const int nvb_z = (g.D + 127) / 128;
   const long nq = (long)qpb * g.B * g.Hq;
-  const long nblk = nq + (long)(g.NT - first_key_tile(g)) * nkvh * (kpt + nvb_z);
+  const long nblk = nq + (long)(g.qt1 - g.qt0) * nkvh * (kpt + nvb_z);
   if (nblk > 0)
     hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpt,
                        nvb_z, qpb, (int)nq);

@@ -142,6 +142,8 @@ class Params:
     k_lsq: int = 0          # 1: K block exponents by least squared error (MX)
     qmask: int = QUANT_ALL  # pass 1's FP4 roundings that apply (per-operand emulation)
     window: int = 0         # > 0: causal sliding window of this many keys
+    stat_keys: int = 0      # > 0: K/V statistics over the keys before this one (chunked
+                            # prefill: frozen at the last restat); 0: over all keys
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
@@ -150,6 +152,7 @@ class Params:
         assert self.k_lsq in (0, 1) and not (self.k_lsq and self.fmt != MX)
         assert 0 <= self.qmask <= QUANT_ALL
         assert self.window >= 0 and (self.window == 0 or self.causal)
+        assert self.stat_keys == 0 or self.first_tile * self.tile < self.stat_keys <= self.Nkv
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
@@ -239,7 +242,9 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
     Q [B,Hq,Nq,D], K/V [B,Hkv,Nkv,D] float32 arrays holding the fp16/bf16
     input values.  Returns codes, scale bytes and per-head scales.  With a
     sliding window the K/V statistics (key mean, per-head scales) and codes
-    cover the key tiles from first_tile on, the ones some row sees.
+    cover the key tiles from first_tile on, the ones some row sees.  With
+    stat_keys the statistics cover only the keys before it (values of later
+    keys beyond the frozen range clamp at the format's largest value).
     """
     L = lib()
     cp = p.c()
@@ -268,19 +273,24 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
         for hk in range(Hkv):
             # statistics and codes over the key tiles some query row sees:
             # all, or with a sliding window from first_tile on (the others
-            # are never read; their codes stay zero here)
+            # are never read; their codes stay zero here); with stat_keys the
+            # statistics stop before that key (chunked prefill keeps them
+            # from the last restat) while the codes cover every key
             k0 = p.first_tile * p.tile
             nk = Nkv - k0
+            ks_hi = p.stat_keys if p.stat_keys > 0 else Nkv
             Kh = np.ascontiguousarray(K[b, hk, k0:])
             Vh = np.ascontiguousarray(V[b, hk, k0:])
+            Ks = np.ascontiguousarray(K[b, hk, k0:ks_hi])
             kb = np.zeros(D, np.float32)
             am = np.zeros(1, np.float32)
-            L.orc_key_stats(_ptr(Kh), nk, D, p.tile, _ptr(kb), _ptr(am))
+            L.orc_key_stats(_ptr(Ks), ks_hi - k0, D, p.tile, _ptr(kb), _ptr(am))
             out["kbar"][b, hk] = kb
             out["amax_k"][b, hk] = am[0]
             L.orc_head_scale(C.c_float(am[0]), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
             out["g_k"][b, hk], out["inv_k"][b, hk] = f[0], f[1]
-            av = L.orc_absmax(_ptr(Vh), Vh.size)
+            Vs = np.ascontiguousarray(V[b, hk, k0:ks_hi])
+            av = L.orc_absmax(_ptr(Vs), Vs.size)
             out["amax_v"][b, hk] = av
             L.orc_head_scale(C.c_float(av), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
             out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]

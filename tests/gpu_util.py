@@ -46,8 +46,9 @@ def unpermute_v(vcodes_gpu: np.ndarray) -> np.ndarray:
 
 
 def unblob(blobs: np.ndarray, D: int, Nkv: int) -> dict:
-    """Per-tile blobs [B, Hkv, NT, 68 D] -> canonical K codes/scales [B, Hkv, Nkv, .]
-    and V^T codes/scales [B, Hkv, D, NkvP/.]."""
+    """Per-tile blobs [B, Hkv, NTc, 68 D] (NTc >= NT: a capacity) -> canonical K
+    codes/scales [B, Hkv, Nkv, .] and V^T codes/scales [B, Hkv, D, NkvP/.]."""
+    blobs = blobs[:, :, :-(-Nkv // 64)]
     B, Hkv, NT, _ = blobs.shape
     kc = blobs[..., :32 * D].reshape(B, Hkv, NT * 64, D // 2)[:, :, :Nkv]
     ks = blobs[..., 32 * D:34 * D].reshape(B, Hkv, NT * 64, D // 32)[:, :, :Nkv]
@@ -62,7 +63,7 @@ def fp4_sections(p, fp4_host: np.ndarray) -> dict:
     L = apa.fp4_layout(p)
     B, Hq, Hkv, Nq, Nkv, D = p.B, p.Hq, p.Hkv, p.Nq, p.Nkv, p.D
     NqP = -(-Nq // 32) * 32
-    NkvP = -(-Nkv // 64) * 64
+    NkvP = -(-max(Nkv, p.kv_capacity) // 64) * 64
 
     def sec(off, count, dtype, shape):
         return np.frombuffer(fp4_host[off:off + count * np.dtype(dtype).itemsize].tobytes(),
@@ -131,11 +132,12 @@ def tail_outcomes(p, ws) -> np.ndarray:
     return np.array(out, np.int64)
 
 
-def run_gpu(p, Q, K, V, eps, dtype="fp16", fused=True, lam=True, split=True):
+def run_gpu(p, Q, K, V, eps, dtype="fp16", fused=True, lam=True, split=True, tensors=None):
     """Whole APA forward on the GPU; returns numpy copies of every output.
-    split=False runs pass 1 without its workspace (one wave per 32-row block)."""
+    split=False runs pass 1 without its workspace (one wave per 32-row block).
+    tensors: device (q, k, v) to pass instead of Q, K, V (e.g. paged pools)."""
     import torch
-    q, k, v = torch_inputs(Q, K, V, dtype)
+    q, k, v = torch_inputs(Q, K, V, dtype) if tensors is None else tensors
     bufs = apa.alloc(p, with_lambda=lam)
     apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q)
     ws1 = bufs.ws_p1 if split else None
@@ -165,9 +167,9 @@ def run_gpu(p, Q, K, V, eps, dtype="fp16", fused=True, lam=True, split=True):
     return res
 
 
-def run_exact_gpu(p, Q, K, V, dtype="fp16"):
+def run_exact_gpu(p, Q, K, V, dtype="fp16", tensors=None):
     import torch
-    q, k, v = torch_inputs(Q, K, V, dtype)
+    q, k, v = torch_inputs(Q, K, V, dtype) if tensors is None else tensors
     out = torch.empty(q.shape, dtype=q.dtype, device="cuda")
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
     apa.exact(p, q, k, v, out, lse)

@@ -46,21 +46,30 @@ def prob(**kw):
 def test_sizes_and_layout():
     p = prob()
     L = apa.fp4_layout(p)
-    offs = [L.q_codes, L.q_scales, L.kv_blobs, L.kbar, L.kv_head, L.q_head, L.q_frame, L.status,
+    # the K/V sections first (a persistent cache keeps them), then the queries'
+    offs = [L.kv_blobs, L.kbar, L.kv_head, L.status, L.q_codes, L.q_scales, L.q_head, L.q_frame,
             L.q2_codes, L.q2_scales, L.total]
-    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs) and L.kv_blobs == 0
     # one Q term: the residual sections are empty; two: each as large as Q's
     assert L.q2_scales == L.q2_codes == L.total
     L2 = apa.fp4_layout(prob(q_terms=2))
     assert L2.q2_scales - L2.q2_codes == L.q_scales - L.q_codes
     assert L2.total - L2.q2_scales >= 24 * 2048 * 4
     assert [L2.q_codes, L2.kv_blobs, L2.status] == [L.q_codes, L.kv_blobs, L.status]
-    assert L.kv_blobs - L.q_scales >= 24 * 2048 * 4
+    assert L.q_frame - L.q_head >= 24 * 4 * 4
     # one 68*D-byte blob per 64-key tile and kv-head: 8704 B at D = 128
     assert L.kbar - L.kv_blobs == 8 * 1920 * 8704
     assert apa.fp4_bytes(p) == L.total
     assert apa.hotmask_bytes(p) == 24 * 128 * 60 * 4
     assert apa.workspace_bytes(p, apa.CALL_PASS1) > 0
+    # a capacity sizes the K/V sections and keeps them where they are for any
+    # Nq and any Nkv up to it (a persistent FP4 cache across chunks)
+    cap = [apa.fp4_layout(prob(Nq=nq, Nkv=nkv, kv_capacity=131072))
+           for nq, nkv in ((2048, 122880), (512, 65536), (64, 100000))]
+    for c in cap:
+        assert (c.kv_blobs, c.kbar, c.kv_head, c.status) == (cap[0].kv_blobs, cap[0].kbar,
+                                                             cap[0].kv_head, cap[0].status)
+        assert c.kbar - c.kv_blobs == 8 * 2048 * 8704
     # enough row blocks to fill the GPU, or visit orders too short to cut:
     # pass 1 runs one wave per block and needs no workspace
     assert apa.workspace_bytes(prob(Nq=32768, Nkv=32768, Hq=32), apa.CALL_PASS1) == 0
@@ -78,10 +87,14 @@ def test_sizes_and_layout():
     ("hot_frame_offset", 65.0),
     ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4),
     ("q_terms", 0), ("q_terms", 3), ("k_scale_lsq", 2), ("window", -1),
-    ("window+noncausal", 4096)])
+    ("window+noncausal", 4096), ("kv_capacity", 1000), ("kv_capacity", -1),
+    ("stat_keys", -1), ("stat_keys", 200000), ("block_table_stride", 1000)])
 def test_invalid_problems_are_rejected(field, value):
     if field == "window+noncausal":
         p = prob(window=value, is_causal=0)  # a sliding window needs the causal mask
+    elif field == "block_table_stride":
+        # a block table needs an entry for every tile of a batch row
+        p = prob(block_table=FAKE.value, block_table_stride=value)
     else:
         p = prob(**{field: value})
     assert apa.lib().apa_quantize(C.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == \
@@ -232,3 +245,19 @@ def test_pass1_split_whole_without_tails():
     assert apa.pass1_split(prob(D=512), 1000) == (apa.SCHED_WHOLE, 1000, 0)
     with pytest.raises(apa.ApaError):
         apa.pass1_split(prob(D=96), 10)
+
+
+def test_quantize_tiles_validates_its_range():
+    L = apa.lib()
+    p = prob()
+    need = apa.workspace_bytes(p, apa.CALL_QUANTIZE)
+    for tb, te in ((-1, 10), (5, 4), (0, 1921)):
+        assert L.apa_quantize_tiles(C.byref(p), FAKE, FAKE, FAKE, FAKE, tb, te, FAKE, need,
+                                    None) == apa.APA_ERR_INVALID_ARG
+    assert L.apa_quantize_tiles(C.byref(p), FAKE, FAKE, FAKE, FAKE, 0, 10, FAKE, need - 1,
+                                None) == apa.APA_ERR_WORKSPACE
+    # with a window the range starts at the window's first tile
+    pw = prob(window=4096)
+    first = (122880 - 2048 - 4096 + 1) // 64
+    assert L.apa_quantize_tiles(C.byref(pw), FAKE, FAKE, FAKE, FAKE, first - 1, 1920, FAKE,
+                                need, None) == apa.APA_ERR_INVALID_ARG
