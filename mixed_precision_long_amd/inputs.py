@@ -176,3 +176,27 @@ def digest(*arrays) -> str:
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+def boost_value_tiles(V: np.ndarray, n_tiles: int, factor: float = 4.0, seed: int = 0,
+                      tile: int = 64, first_tile: int = 0) -> tuple:
+    """Values of a few key tiles made `factor` times larger, in place.
+
+    Stands in for the tokens with outsized value vectors behind the hazard
+    of a cold tile whose small mass carries a large output component ("APA:
+    sloppy attention, exact where it counts", section "Honest limits"): per
+    (batch, kv-head), n_tiles distinct tiles
+    drawn from [first_tile, ceil(Nkv / tile)) by a seeded generator, with
+    their V rows scaled by factor (a power of two keeps fp16/bf16 values
+    exact while nothing overflows).  Returns the chosen tiles [B][Hkv][n]."""
+    B, Hkv, Nkv, _ = V.shape
+    nt = -(-Nkv // tile)
+    rng = np.random.default_rng(seed)
+    picks = np.zeros((B, Hkv, n_tiles), np.int64)
+    for b in range(B):
+        for j in range(Hkv):
+            ts = rng.choice(np.arange(first_tile, nt), size=n_tiles, replace=False)
+            picks[b, j] = ts
+            for t in ts:
+                V[b, j, t * tile:min(Nkv, t * tile + tile)] *= np.float32(factor)
+    return picks

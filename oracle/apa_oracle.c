@@ -41,7 +41,10 @@
  * parts of the reference output) against a numpy softmax and their closed
  * forms; the per-operand emulation against the brute force with the same
  * operands quantised and, with none, against FP64 attention; the sliding
- * window against the brute force and a masked softmax.  Parity unpinned: the
+ * window against the brute force and a masked softmax; the value-norm
+ * weighted hot test (weights computed by the Python side of the oracle)
+ * against the brute force, the closed forms of equal value norms and of one
+ * planted tile, and the output-norm bound it gives.  Parity unpinned: the
  * pages' measured numbers (they come from activation dumps that are not
  * available), listed as such in the design notes.
  */
@@ -70,6 +73,8 @@ typedef struct {
   int32_t qmask;    /* which of pass 1's FP4 roundings apply: ORC_QUANT_Q | _K | _V | _P
                        (all: the method; fewer: the per-operand emulation) */
   int32_t window;   /* > 0: causal sliding window of this many keys; 0: full causal */
+  int32_t vweight;  /* 1: the hot test weighs each tile's mass by its value-norm weight
+                       (orc_job.vw); 0: mass only */
 } orc_params;
 
 /* Per-operand switches of pass 1's FP4 roundings ("Second hunt: which operand
@@ -515,6 +520,7 @@ typedef struct {
   /* the unquantised operands (per-operand emulation, see ORC_QUANT_*) */
   const float *Qh, *Kh, *Vh, *kbar; /* [Nq][D], [Nkv][D], [Nkv][D], [D] */
   float inv_q, inv_k, inv_v;
+  const float* tw;          /* [NT] value-norm weights of the hot test, or NULL */
 } orc_head_ops;
 
 static double code_at(const uint8_t* codes, size_t idx) {
@@ -688,11 +694,13 @@ void orc_pass1_group(const orc_head_ops* h, int g, orc_p1_out* out) {
       /* running sum over every tile seen so far, this one included */
       float lam_prev = m[i] == -INFINITY ? 0.0f : rescale(lam[i], m[i] - mc[i]);
       lamc[i] = lam_prev + lc[i];
-      /* step 4: the hot test */
+      /* step 4: the hot test; with value-norm weights the tile's mass
+       * counts w_t times (w_t >= 1, one FP32 product) */
       float thr = p->eps * lamc[i];
-      if (lc[i] > thr) hot = 1;
+      float lw = h->tw ? lc[i] * h->tw[t] : lc[i];
+      if (lw > thr) hot = 1;
       if (lamc[i] > 0.0f) {
-        double mg = ((double)lc[i] - (double)p->eps * (double)lamc[i]) / (double)lamc[i];
+        double mg = ((double)lw - (double)p->eps * (double)lamc[i]) / (double)lamc[i];
         if (mg > margin) margin = mg;
       }
     }
@@ -880,6 +888,7 @@ typedef struct {
   const float *kbar, *g_v;
   const int32_t* jq;
   const float *inv_q, *inv_k, *inv_v; /* per-head scales (unquantised operands) */
+  const float* vw;   /* [B][Hkv][NT] value-norm weights (used with p->vweight) */
   /* work list: triplets (b, h, g) */
   const int32_t* groups;
   int ngroups;
@@ -930,6 +939,7 @@ static void run_group(orc_job* J, int w) {
   ops.inv_q = J->inv_q[bh];
   ops.inv_k = J->inv_k[bk];
   ops.inv_v = J->inv_v[bk];
+  ops.tw = p->vweight && J->vw ? J->vw + bk * NT : NULL;
   int r0 = g * R;
   orc_p1_out out;
   out.hot = J->hot + (bh * NG + g) * NT;

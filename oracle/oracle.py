@@ -49,7 +49,7 @@ class _Params(C.Structure):
                 ("fmt", C.c_int32), ("int_frame", C.c_int32), ("tau", C.c_float),
                 ("hoff", C.c_float), ("eps", C.c_float), ("tile", C.c_int32), ("rg", C.c_int32),
                 ("q_terms", C.c_int32), ("k_lsq", C.c_int32), ("qmask", C.c_int32),
-                ("window", C.c_int32)]
+                ("window", C.c_int32), ("vweight", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -59,7 +59,7 @@ class _Job(C.Structure):
     _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P),
                 ("qc", _P), ("qs", _P), ("kc", _P), ("ks", _P), ("vc", _P), ("vs", _P),
                 ("qc2", _P), ("qs2", _P), ("kbar", _P), ("g_v", _P), ("jq", _P),
-                ("inv_q", _P), ("inv_k", _P), ("inv_v", _P),
+                ("inv_q", _P), ("inv_k", _P), ("inv_v", _P), ("vw", _P),
                 ("groups", _P), ("ngroups", C.c_int),
                 ("hot", _P), ("margin", _P), ("m1", _P), ("l1", _P), ("lam", _P), ("o1", _P),
                 ("shift", _P), ("m2", _P), ("l2", _P), ("o2", _P), ("cr", _P), ("O", _P),
@@ -144,6 +144,8 @@ class Params:
     window: int = 0         # > 0: causal sliding window of this many keys
     stat_keys: int = 0      # > 0: K/V statistics over the keys before this one (chunked
                             # prefill: frozen at the last restat); 0: over all keys
+    hot_weight: int = 0     # 1: the hot test weighs a tile's mass by its value-norm
+                            # weight (see tile_weights); 0: mass only
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
@@ -153,11 +155,13 @@ class Params:
         assert 0 <= self.qmask <= QUANT_ALL
         assert self.window >= 0 and (self.window == 0 or self.causal)
         assert self.stat_keys == 0 or self.first_tile * self.tile < self.stat_keys <= self.Nkv
+        assert self.hot_weight in (0, 1)
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
                        self.scale, self.fmt, self.int_frame, self.tau, self.hoff, self.eps,
-                       self.tile, self.rg, self.q_terms, self.k_lsq, self.qmask, self.window)
+                       self.tile, self.rg, self.q_terms, self.k_lsq, self.qmask, self.window,
+                       self.hot_weight)
 
     @property
     def n_tiles(self) -> int:
@@ -236,11 +240,42 @@ def quant_rows(X: np.ndarray, inv: float, fmt: int = MX, centre=None):
 # a1 + a2: statistics, per-head scales, quantisation
 # --------------------------------------------------------------------------
 
+def tile_weights(p: Params, Vh: np.ndarray):
+    """Value-norm weights of the hot test for one (b, kv-head), V [Nkv, D].
+
+    "APA: sloppy attention, exact where it counts", section "Honest limits",
+    its point on mass versus output: the hot test bounds a cold tile's share
+    of the softmax mass, while what the tile adds to the output also scales
+    with the size of its values; the page proposes weighing the test by value
+    norm.
+    Reading taken here: nu_k = ||v_k||_2 of every key (FP64); nu_bar = their
+    mean over the keys the K/V statistics cover; a tile's weight is
+    w_t = max(1, fl32(max_{k in t} nu_k / nu_bar)) (1 when nu_bar is 0).  The
+    weighted test marks a tile hot when fl32(l_t * w_t) > fl32(eps * lambda).
+    A cold tile t then adds at most l_t * max nu_k <= eps * lambda * nu_bar to
+    the output's norm, and, since w_t >= 1, its share of the mass stays under
+    eps as before.  Returns (w [NT] float32, nu_bar); tiles before first_tile
+    (never visited) get weight 1."""
+    Nkv, NT, T = p.Nkv, p.n_tiles, p.tile
+    k0 = p.first_tile * T
+    ks_hi = p.stat_keys if p.stat_keys > 0 else Nkv
+    v = np.asarray(Vh, np.float64)
+    nu = np.sqrt((v * v).sum(axis=1))          # squares exact, FP64 sum
+    nbar = float(nu[k0:ks_hi].sum() / (ks_hi - k0)) if ks_hi > k0 else 0.0
+    w = np.ones(NT, np.float32)
+    if nbar > 0.0:
+        for t in range(p.first_tile, NT):
+            r = np.float32(nu[t * T:min(Nkv, t * T + T)].max() / nbar)
+            w[t] = max(np.float32(1.0), r)
+    return w, nbar
+
+
 def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
     """Stats and block-scaled FP4 quantisation of Q, K (centred), V (along keys).
 
     Q [B,Hq,Nq,D], K/V [B,Hkv,Nkv,D] float32 arrays holding the fp16/bf16
-    input values.  Returns codes, scale bytes and per-head scales.  With a
+    input values.  Returns codes, scale bytes, per-head scales and the hot
+    test's value-norm weights (vw [B,Hkv,NT], nu_bar [B,Hkv]).  With a
     sliding window the K/V statistics (key mean, per-head scales) and codes
     cover the key tiles from first_tile on, the ones some row sees.  With
     stat_keys the statistics cover only the keys before it (values of later
@@ -266,7 +301,8 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
         kc=np.zeros((B, Hkv, Nkv, D // 2), np.uint8),
         ks=np.zeros((B, Hkv, Nkv, D // bs), np.uint8),
         vc=np.zeros((B, Hkv, D, NkvP // 2), np.uint8),
-        vs=np.zeros((B, Hkv, D, NkvP // bs), np.uint8), sl=np.float32(s_l))
+        vs=np.zeros((B, Hkv, D, NkvP // bs), np.uint8), sl=np.float32(s_l),
+        vw=np.ones((B, Hkv, p.n_tiles), np.float32), nu_bar=np.zeros((B, Hkv)))
     f = np.zeros(2, np.float32)
     ji = np.zeros(1, np.int32)
     for b in range(B):
@@ -308,6 +344,7 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             L.orc_quant_vt(_ptr(Vh), nk, NkvP - k0, D, C.c_float(out["inv_v"][b, hk]), p.fmt,
                            _ptr(vc), _ptr(vs))
             out["vc"][b, hk, :, k0 // 2:], out["vs"][b, hk, :, k0 // bs:] = vc, vs
+            out["vw"][b, hk], out["nu_bar"][b, hk] = tile_weights(p, V[b, hk])
         for h in range(Hq):
             Qh = np.ascontiguousarray(Q[b, h])
             aq = L.orc_absmax(_ptr(Qh), Qh.size)
@@ -379,6 +416,7 @@ def run(p: Params, Q, K, V, prep: dict | None = None, groups=None, nthreads: int
         setattr(job, k, _ptr(prep[k]))
     job.jq = _ptr(prep["jq"])
     job.inv_q, job.inv_k, job.inv_v = (_ptr(prep[k]) for k in ("inv_q", "inv_k", "inv_v"))
+    job.vw = _ptr(prep["vw"]) if p.hot_weight else None
     job.qc2 = _ptr(prep.get("qc2")) if p.q_terms == 2 else None
     job.qs2 = _ptr(prep.get("qs2")) if p.q_terms == 2 else None
     job.groups, job.ngroups = _ptr(groups), len(groups)

@@ -19,7 +19,10 @@ Options mirror the oracle's: `quant` switches each operand's FP4 rounding
 (Q, K, V, P; an operand switched off enters at its exact value in the same
 normalised units, "Second hunt: which operand is to blame"), and `window`
 restricts every row to its `window` most recent keys ("What else is in the
-box": sliding window).  The per-cell margin max_r (l_r - eps lambda_r) /
+box": sliding window).  With `hot_weight` the hot test weighs each tile's
+mass by max(1, max key value norm in the tile / mean key value norm of the
+head) ("Honest limits", mass versus output), the norms taken here with
+numpy's own norm routine.  The per-cell margin max_r (l_r w - eps lambda_r) /
 lambda_r is recomputed from this brute force's own l and lambda.
 """
 from __future__ import annotations
@@ -111,6 +114,13 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
         vd = quantise_blocks(vpad.T).T[:Nkv]              # blocks of 32 keys per channel
         if "V" not in quant:
             vd = Vh.astype(np.float64) * np.float64(inv_v)
+        # value-norm weights of the hot test, per 64-key tile
+        nu = np.linalg.norm(Vh.astype(np.float64), axis=1)
+        nbar = nu[k0:].mean() if Nkv > k0 else 0.0
+        vw = np.ones(NkvP // 64, np.float32)
+        if nbar > 0:
+            for t in range(k0 // 64, NkvP // 64):
+                vw[t] = max(1.0, f32(nu[64 * t:64 * t + 64].max() / nbar))
         w = np.float32(sl * g_k)
         heads = []
         for i in range(G):
@@ -132,7 +142,7 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
                 # of the two dequantised terms is exact in FP64
                 qd = qd + quantise_blocks((qn.astype(np.float64) - qd).astype(np.float32))
             heads.append(dict(qd=qd, alpha=2.0 ** j, Qh=Qh))
-        out.append(dict(kd=kd, vd=vd, g_v=g_v, heads=heads, kbar=kbar, sl=sl))
+        out.append(dict(kd=kd, vd=vd, g_v=g_v, heads=heads, kbar=kbar, sl=sl, vw=vw))
     return out
 
 
@@ -147,11 +157,11 @@ def visit_order(last_row: int, off: int, Nkv: int, causal: bool, tile: int = 64,
 
 
 def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray, off: int,
-                Nkv: int, causal: bool, quant_p: bool = True, window: int = 0):
+                Nkv: int, causal: bool, quant_p: bool = True, window: int = 0, tw=None):
     """Frame-free pass 1 of one row group.
 
     scores: [R, Nkv] FP4 scores in log2 units (fl32), vd: [Nkv, D] dequantised
-    V'.  Returns (hot [NT] bool, l [R], o [R, D], lam [R], margin [NT]) in
+    V', tw: per-tile weights of the hot test or None.  Returns (hot [NT] bool, l [R], o [R, D], lam [R], margin [NT]) in
     frame-free units; margin is NaN for tiles not visited.
     """
     R = scores.shape[0]
@@ -193,11 +203,12 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
         ell = f32(ph.sum(axis=1))
         lam = (lam + ell).astype(np.float32)
         thr = (eps32 * lam).astype(np.float32)
-        h = (eps == 0.0) or bool(np.any(ell > thr))
+        lw = ell if tw is None else (ell * np.float32(tw[t])).astype(np.float32)
+        h = (eps == 0.0) or bool(np.any(lw > thr))
         hot[t] = h
         pos = lam > 0
         lam64 = lam.astype(np.float64)
-        mg = (ell.astype(np.float64) - np.float64(eps32) * lam64) / np.where(pos, lam64, 1.0)
+        mg = (lw.astype(np.float64) - np.float64(eps32) * lam64) / np.where(pos, lam64, 1.0)
         margin[t] = mg[pos].max() if pos.any() else -np.inf
         if not h:
             vt = np.zeros((64, D))
@@ -209,7 +220,7 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
 
 
 def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: int = 1,
-              quant: str = QUANT_ALL, window: int = 0):
+              quant: str = QUANT_ALL, window: int = 0, hot_weight: bool = False):
     """Frame-free pass 1 for every row group of a batch-1 problem.
 
     Returns dict with hot [Hq, NG, NT], l [Hq, Nq], o [Hq, Nq, D] (o already
@@ -236,7 +247,8 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
         for g in range(ng):
             rows = np.arange(16 * g, min(Nq, 16 * g + 16))
             hh, l, o, lam, mg = pass1_group(scores[rows], kv["vd"], eps, rows, off, Nkv, causal,
-                                            quant_p="P" in quant, window=window)
+                                            quant_p="P" in quant, window=window,
+                                            tw=kv["vw"] if hot_weight else None)
             hot[h, g] = hh
             margin[h, g] = mg
             lo[h, rows] = l

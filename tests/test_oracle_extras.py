@@ -15,15 +15,19 @@ oracle itself:
   every switch on is the oracle itself, each single operand against the brute
   force with only that operand quantised, all off against FP64 attention;
 * the sliding window ("What else is in the box") against the brute force and
-  a masked numpy softmax.
+  a masked numpy softmax;
+* the value-norm weighted hot test ("Honest limits", mass versus output)
+  against the brute force (norms by numpy's norm routine), the closed forms
+  of equal norms (every weight 1: the mass test itself) and of one planted
+  tile, the output-norm bound it promises, and its effect on the error.
 """
 import math
 
 import numpy as np
 import pytest
 
-from brute_apa import brute_apa
-from mixed_precision_long_amd.inputs import make_inputs, small_workload
+from brute_apa import MAGS, brute_apa, nearest_mag_code
+from mixed_precision_long_amd.inputs import boost_value_tiles, make_inputs, small_workload
 from oracle import oracle as O
 
 
@@ -331,3 +335,153 @@ def test_window_exact_and_eps0():
     assert np.abs(r["O"].reshape(-1, 64) - Oe).max() <= 1e-7
     # keys outside every row's window are never hot
     assert not r["hot"][..., :(2048 - 96 - 500) // 64].any()
+
+
+# ---------------------------------------------------------------------------
+# value-norm weighted hot test
+# ---------------------------------------------------------------------------
+
+def _same_norm_values(V, seed):
+    """Every key's value a signed permutation of one vector with entries in
+    [0.5, 2): all key norms are equal, and their FP64 squares and sums are
+    exact."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, Nkv, D = V.shape
+    u = np.float16(rng.uniform(0.5, 2.0, D)).astype(np.float32)
+    out = np.empty_like(V)
+    for b in range(B):
+        for j in range(Hkv):
+            for k in range(Nkv):
+                out[b, j, k] = rng.permutation(u) * rng.choice([-1.0, 1.0], D)
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    (2, 1, 128, 2048, 64, 0.02, 0, 3, 4.0, 61),
+    (4, 2, 100, 1300, 64, 0.05, 0, 2, 8.0, 62),
+    (2, 1, 96, 2048, 64, 0.05, 300, 3, 16.0, 71),  # with a sliding window
+])
+def test_hot_weight_pass1_bitwise_vs_brute_force(case):
+    """The weighted hot test against the brute force, which takes its norms
+    with numpy's own norm routine: weights, verdicts, margins and the cold
+    state agree bit for bit."""
+    Hq, Hkv, Nq, Nkv, D, eps, window, nb, factor, seed = case
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed)
+    Q, K, V = make_inputs(w)
+    p = O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale, eps=eps, window=window, hot_weight=1)
+    boost_value_tiles(V, nb, factor, seed=seed, first_tile=p.first_tile)
+    prep = O.quantize(p, Q, K, V)
+    r = O.run(p, Q, K, V, prep, pass2=False)
+    b = brute_apa(Q, K, V, eps, w.scale, window=window, hot_weight=True)
+    for j in range(Hkv):
+        assert np.array_equal(prep["vw"][0, j], b["ops"][j]["vw"])
+    assert (prep["vw"] > 1.0).any()
+    sc = _frame_scale(r["m1"][0])
+    assert np.array_equal(r["hot"][0].astype(bool), b["hot"])
+    om, bm = r["margin"][0], b["margin"]
+    vis = ~np.isnan(om)
+    assert np.array_equal(vis, ~np.isnan(bm)) and np.array_equal(om[vis], bm[vis])
+    assert np.array_equal((r["l1"][0] * sc).astype(np.float32), b["l"])
+    assert np.array_equal((r["o1"][0] * sc[..., None]).astype(np.float32), b["o"])
+    # and the weights change verdicts on these inputs
+    r0 = O.run(O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale, eps=eps, window=window),
+               Q, K, V, pass2=False)
+    assert r["hot"].sum() > r0["hot"].sum()
+
+
+def test_hot_weight_equal_norms_is_the_mass_test():
+    """With every key's value norm equal, every weight is exactly 1 and the
+    weighted run is the unweighted one, bit for bit."""
+    w = small_workload(1, 2, 1, 128, 2048, 64, seed=64)
+    Q, K, V = make_inputs(w)
+    V = _same_norm_values(V, 64)
+    p0 = O.Params(1, 2, 1, 128, 2048, 64, scale=w.scale, eps=0.01)
+    p1 = O.Params(1, 2, 1, 128, 2048, 64, scale=w.scale, eps=0.01, hot_weight=1)
+    prep = O.quantize(p1, Q, K, V)
+    assert np.all(prep["vw"] == 1.0)
+    r0 = O.run(p0, Q, K, V)
+    r1 = O.run(p1, Q, K, V, prep)
+    for k in ("hot", "margin", "l1", "o1", "m1", "O"):
+        assert np.array_equal(r0[k], r1[k], equal_nan=True), k
+
+
+def test_hot_weight_planted_tile_closed_form():
+    """Equal norms nu everywhere except one tile whose values are 2^j times
+    larger: nu_bar = nu (n - 64 + 64 2^j) / n, so that tile's weight is
+    fl32(2^j n / (n - 64 + 64 2^j)) and every other weight is 1."""
+    Nkv, t_big, j = 2048, 9, 3
+    w = small_workload(1, 2, 1, 64, Nkv, 64, seed=65)
+    Q, K, V = make_inputs(w)
+    V = _same_norm_values(V, 65)
+    V[0, 0, 64 * t_big:64 * t_big + 64] *= np.float32(2.0 ** j)
+    p = O.Params(1, 2, 1, 64, Nkv, 64, scale=w.scale, hot_weight=1)
+    prep = O.quantize(p, Q, K, V)
+    want = np.ones(Nkv // 64, np.float32)
+    want[t_big] = np.float32(2.0 ** j * Nkv / (Nkv - 64 + 64 * 2.0 ** j))
+    assert np.array_equal(prep["vw"][0, 0], want)
+
+
+@pytest.mark.parametrize("eps", [0.005, 0.02])
+def test_hot_weight_bounds_cold_output_norm(eps):
+    """The bound the weighted test gives: for every cold cell, the FP4 mass of
+    each row times the tile's largest value norm stays under eps * lambda *
+    nu_bar (lambda final, so at least what the vote saw); the norms here are
+    recomputed independently."""
+    Nq, Nkv = 128, 8192
+    w = small_workload(1, 2, 1, Nq, Nkv, 64, seed=66)
+    Q, K, V = make_inputs(w)
+    boost_value_tiles(V, 4, 8.0, seed=66)
+    b = brute_apa(Q, K, V, eps, w.scale, hot_weight=True)
+    nu = np.linalg.norm(V[0, 0].astype(np.float64), axis=1)
+    nbar = nu.mean()
+    ops = b["ops"][0]
+    off = Nkv - Nq
+    checked = 0
+    for h in range(2):
+        hd = ops["heads"][h]
+        s = (hd["alpha"] * (hd["qd"] @ ops["kd"].T)).astype(np.float32).astype(np.float64)
+        for g in range(Nq // 16):
+            rows = np.arange(16 * g, 16 * g + 16)
+            lam = b["lam"][h, rows].astype(np.float64)
+            for t in np.flatnonzero(~b["hot"][h, g]):
+                if 64 * t > rows[-1] + off:
+                    continue
+                st = s[rows, 64 * t:64 * t + 64].copy()
+                st[np.arange(64 * t, 64 * t + 64)[None, :] > rows[:, None] + off] = -np.inf
+                mass = np.zeros(16)
+                for q0 in (0, 32):
+                    gg = st[:, q0:q0 + 32]
+                    cg = gg.max(1)
+                    live = np.isfinite(cg)
+                    cg = np.where(live, cg, 0.0)
+                    E = np.ceil(cg - np.log2(6.0))
+                    E = np.where(np.exp2(cg - E) > 6, E + 1, E)
+                    E = np.where(np.exp2(cg - E + 1) <= 6, E - 1, E)
+                    with np.errstate(invalid="ignore"):
+                        pq = MAGS[nearest_mag_code(np.exp2(gg - E[:, None]))]
+                    pq = np.where(np.isfinite(gg), pq, 0.0)
+                    mass += np.where(live, (pq * np.exp2(E)[:, None]).sum(1), 0.0)
+                numax = nu[64 * t:64 * t + 64].max()
+                assert np.all(mass * numax <= eps * lam * nbar * (1 + 1e-6)), (h, g, t)
+                assert np.all(mass <= eps * lam * (1 + 1e-6))
+                checked += 1
+    assert checked > 100
+
+
+def test_hot_weight_lowers_the_error_of_large_value_tiles():
+    """On inputs with tiles of outsized values the weighted test makes more
+    tiles exact and brings the output closer to FP64 attention (an inverted
+    weight, or one applied to lambda instead of the tile, would not)."""
+    Nq, Nkv = 128, 4096
+    w = small_workload(1, 4, 1, Nq, Nkv, 64, seed=67)
+    Q, K, V = make_inputs(w)
+    boost_value_tiles(V, 6, 16.0, seed=67)
+    Oe, _ = O.exact(O.Params(1, 4, 1, Nq, Nkv, 64, scale=w.scale), Q, K, V)
+    err, nhot = {}, {}
+    for hw in (0, 1):
+        p = O.Params(1, 4, 1, Nq, Nkv, 64, scale=w.scale, eps=0.02, hot_weight=hw)
+        r = O.run(p, Q, K, V)
+        err[hw] = np.abs(r["O"].reshape(-1, 64) - Oe.reshape(-1, 64)).max()
+        nhot[hw] = int(r["hot"].sum())
+    assert nhot[1] > nhot[0]
+    assert err[1] < 0.7 * err[0], err
