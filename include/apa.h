@@ -105,16 +105,34 @@ typedef struct apa_problem {
                                      batch b is row k % 64 of page
                                      block_table[b * stride + k / 64] (NULL) */
   int32_t block_table_stride;     /* entries per batch row, >= ceil(Nkv / 64) */
+  int32_t hot_weight;             /* 1: the hot test weighs each tile's mass by
+                                     its value-norm weight w_t (the APA page's
+                                     "Honest limits": a cold tile's small mass
+                                     can still carry a large output part; the
+                                     page proposes a test weighted by value
+                                     norm): w_t = max(1, nu_t / nu_bar), nu_t
+                                     the largest L2 norm of a value vector in
+                                     tile t, nu_bar the mean norm over the keys
+                                     the statistics cover (w_t = 1 when nu_bar
+                                     is 0).  A row's tile counts as hot when
+                                     l_t * w_t > eps * lambda, so a cold tile
+                                     adds at most eps * lambda * nu_bar to the
+                                     row's unnormalised output and keeps its
+                                     mass share under eps.  apa_quantize writes
+                                     the weights into the FP4 buffer; every call
+                                     on one FP4 buffer must name the same value.
+                                     0: the mass test (0)                       */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
  * fp16, causal, APA_SCHED_AUTO, one Q term, nearest K block exponents, no
- * window, capacity Nkv, statistics over all keys, flat K/V. */
+ * window, capacity Nkv, statistics over all keys, flat K/V, the mass-only
+ * hot test. */
 void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_t Nq,
                       int32_t Nkv, int32_t D);
 
 /* Byte offsets of the sections of the FP4 buffer written by apa_quantize,
- * the K/V sections first (kv_blobs, kbar, kv_head, status: sized by the
+ * the K/V sections first (kv_blobs, kbar, kv_head, tile_w, status: sized by the
  * capacity, so a persistent cache keeps them), then the query sections.
  * NqP = Nq rounded up to 32, NkvP = Nkv rounded up to 64, NTc = the capacity
  * in 64-key tiles; padding rows and keys hold zero codes.  Codes pack two 4-bit E2M1 values per byte, element
@@ -133,7 +151,11 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *              [66D, 68D)  V scales, channel 32*db + n and key half hh at
  *                          byte (2n + hh) * D/32 + db
  *   kbar     [B][Hkv][D] float       per-channel key mean
- *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V, 0, 0
+ *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V,
+ *                                    nu_bar (with hot_weight, else 0), 0
+ *   tile_w   [B][Hkv][NTc] float     with hot_weight: the value-norm weight
+ *                                    w_t of every tile some row sees (the
+ *                                    rest untouched)
  *   q_head   [B][Hq][4]  float       amax_Q, inv_Q, j (as float: alpha = 2^j), 0
  *   q_frame  [B][Hq][NqP] float      c_r = sl * q.kbar, sl = fl32(scale*log2 e)
  *   status   uint32                  bit 0: a non-finite input was seen
@@ -144,7 +166,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *            with one term)                                                  */
 typedef struct apa_fp4_layout {
   size_t q_codes, q_scales, kv_blobs;
-  size_t kbar, kv_head, q_head, q_frame, status, q2_codes, q2_scales, total;
+  size_t kbar, kv_head, tile_w, q_head, q_frame, status, q2_codes, q2_scales, total;
 } apa_fp4_layout;
 
 apa_status apa_fp4_layout_of(const apa_problem* p, apa_fp4_layout* out);
@@ -173,8 +195,11 @@ const char* apa_last_hip_error(void);
  * head's largest magnitude to 6; Q's per-head scale is tied to K's so the
  * score factor is a power of two 2^j.  Blocks of 32 (Q, K along D; V along
  * keys) get an E8M0 exponent, the smallest that fits the block maximum under
- * 6, and E2M1 codes rounded to nearest even.  ws: apa_workspace_bytes(p,
- * APA_CALL_QUANTIZE) bytes. */
+ * 6, and E2M1 codes rounded to nearest even.  With hot_weight it also
+ * writes nu_bar (FP64 sum of the FP32 key norms, in key order per tile and
+ * tiles ascending) and the weight of every tile some row sees.  The status
+ * word reports non-finite values among Q and every K/V tile it quantises.
+ * ws: apa_workspace_bytes(p, APA_CALL_QUANTIZE) bytes. */
 apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
                         void* fp4, void* ws, size_t ws_bytes, void* stream);
 
@@ -187,7 +212,8 @@ apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, cons
  * they are.  Q's per-head scale ties to the cache's K scale as in
  * apa_quantize.  A chunk whose keys are [0, Nkv) after a previous chunk
  * ending at key N0 passes tile_begin = N0 / 64 (re-quantising a partly
- * filled last tile).  The status word reports non-finite values among Q and
+ * filled last tile).  With hot_weight, the new tiles' weights use the
+ * cache's nu_bar.  The status word reports non-finite values among Q and
  * the quantised tiles.  0 <= tile_begin <= tile_end <= ceil(Nkv / 64) (from
  * the window's first tile with a window).  ws: apa_workspace_bytes(p,
  * APA_CALL_QUANTIZE) bytes. */
@@ -215,8 +241,9 @@ apa_status apa_quantize_static(const apa_problem* p, const void* q, const void* 
  * Every row group of 16 rows visits its tiles in the order 0, d, d-1, ..., 1
  * (d = its causal diagonal tile), scores them from the FP4 buffer, quantises
  * P per 32-key group, takes the tile row sums with a ones-operand MFMA, and
- * marks the tile hot when any row's sum exceeds eps times its running sum
- * (eps == 0: every visited tile hot).  Cold tiles accumulate P.V in FP4.
+ * marks the tile hot when any row's sum (times the tile's value-norm weight
+ * with hot_weight) exceeds eps times its running sum (eps == 0: every
+ * visited tile hot).  Cold tiles accumulate P.V in FP4.
  * Outputs (all [B][Hq][Nq], FP32 unless noted):
  *   cold_m  int32 log2 frame of the cold state (INT32_MIN: empty row)
  *   cold_l  cold row sum in that frame

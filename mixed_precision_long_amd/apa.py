@@ -42,12 +42,13 @@ class Problem(C.Structure):
                 ("hot_frame_offset", C.c_float), ("pass1_schedule", C.c_int32),
                 ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32), ("window", C.c_int32),
                 ("kv_capacity", C.c_int32), ("stat_keys", C.c_int32),
-                ("block_table", C.c_void_p), ("block_table_stride", C.c_int32)]
+                ("block_table", C.c_void_p), ("block_table_stride", C.c_int32),
+                ("hot_weight", C.c_int32)]
 
 
 class Fp4Layout(C.Structure):
     _fields_ = [(k, C.c_size_t) for k in ("q_codes", "q_scales", "kv_blobs", "kbar", "kv_head",
-                                          "q_head", "q_frame", "status", "q2_codes",
+                                          "tile_w", "q_head", "q_frame", "status", "q2_codes",
                                           "q2_scales", "total")]
 
 
@@ -97,9 +98,9 @@ def status_string(code: int) -> str:
 
 def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
             fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0, window=0, kv_capacity=0,
-            stat_keys=0, block_table=None) -> Problem:
+            stat_keys=0, block_table=None, hot_weight=0) -> Problem:
     """block_table: a device int32 tensor [B, stride] of page indices (paged
-    K/V), or None."""
+    K/V), or None; hot_weight: 1 for the value-norm weighted hot test."""
     p = Problem()
     lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
     p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt, p.pass1_schedule = (
@@ -109,6 +110,7 @@ def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4
     p.window = window
     p.kv_capacity = kv_capacity
     p.stat_keys = stat_keys
+    p.hot_weight = hot_weight
     if block_table is not None:
         p.block_table = block_table.data_ptr()
         p.block_table_stride = block_table.shape[-1]

@@ -22,6 +22,7 @@ struct Geom {
   // pools [pages][Hkv][64][D]; nullptr: [B][Hkv][Nkv][D]
   const int32_t* bt;
   int bts;
+  int vweight;  // 1: the hot test weighs each tile's mass by its value-norm weight
 };
 
 // Element offset of key k of (b, kv-head hk) in a 16-bit K or V input.  The
@@ -46,6 +47,7 @@ struct Fp4Ptrs {
   uint8_t *q_codes, *q_scales, *kv_blob;
   uint8_t *q2_codes, *q2_scales;  // the residual term of Q (nullptr with one term)
   float *kbar, *kv_head, *q_head, *q_frame;
+  float* tile_w;  // [B][Hkv][NTc] value-norm weights of the hot test
   unsigned* status;
 };
 
@@ -59,14 +61,12 @@ __host__ __device__ inline int first_key_tile(const Geom& g) {
   return g.causal && g.window > 0 && k > 0 ? k / 64 : 0;
 }
 
-// The K/V tiles a quantise call reads for statistics, and the keys they
-// stop before: the tiles some row sees up to stat_hi; with frozen statistics
-// (quantising only tiles [qt0, qt1) of a persistent cache) those tiles,
-// read for their non-finite check alone.
+// The statistics pass reads the K/V tiles a quantise call codes, [qt0,
+// qt1): for their non-finite check and value norms, and, up to the key
+// stat_khi, for the statistics, which start at tile stat_t0.  With frozen
+// statistics (quantising only tiles [qt0, qt1) of a persistent cache) none
+// are taken.
 __host__ __device__ inline int stat_t0(const Geom& g) { return g.frozen ? g.qt0 : first_key_tile(g); }
-__host__ __device__ inline int stat_t1(const Geom& g) {
-  return g.frozen ? g.qt1 : (g.stat_hi + 63) / 64;
-}
 __host__ __device__ inline int stat_khi(const Geom& g) { return g.frozen ? g.Nkv : g.stat_hi; }
 
 struct QuantWs {
@@ -76,9 +76,11 @@ struct QuantWs {
   float* vamax;   // [B*Hkv][NCH]
   float* qamax;   // [B*Hq][NQT]
   unsigned* flags;  // [NKB + NQB] per statistics block: a non-finite input seen
+  float* vnt;     // [B*Hkv][NT]  largest key value norm of each tile read
+  double* vnsum;  // [B*Hkv][NCH] sum of the statistics keys' value norms per chunk
   int nqt;        // ceil(Nq / 64)
   int nch;        // ceil(NT / 16)
-  int ch0, ch1;   // the chunks holding the statistics tiles [stat_t0, stat_t1)
+  int ch0, ch1;   // the chunks holding the tiles read, [qt0, qt1)
   int nflags;     // NKB + NQB
 };
 

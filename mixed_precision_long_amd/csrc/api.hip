@@ -50,6 +50,7 @@ bool valid_problem(const apa_problem* p) {
   if (p->kv_capacity < 0 || (p->kv_capacity > 0 && p->kv_capacity < p->Nkv)) return false;
   if (p->stat_keys < 0 || p->stat_keys > p->Nkv) return false;
   if (p->block_table && (p->block_table_stride < (p->Nkv + 63) / 64)) return false;
+  if (p->hot_weight != 0 && p->hot_weight != 1) return false;
   return true;
 }
 
@@ -80,6 +81,7 @@ Geom geom(const apa_problem* p) {
   g.frozen = 0;
   g.bt = p->block_table;
   g.bts = p->block_table_stride;
+  g.vweight = p->hot_weight;
   return g;
 }
 
@@ -93,6 +95,7 @@ void layout(const apa_problem* p, apa_fp4_layout* L) {
   L->kv_blobs = take(B * Hkv * g.NTc * blob_bytes(p->D));
   L->kbar = take(B * Hkv * D * 4);
   L->kv_head = take(B * Hkv * 8 * 4);
+  L->tile_w = take(B * Hkv * g.NTc * 4);
   L->status = take(4);
   L->q_codes = take(B * Hq * g.NqP * D / 2);
   L->q_scales = take(B * Hq * g.NqP * D / 32);
@@ -114,6 +117,7 @@ Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
   f.kbar = (float*)(b + L.kbar); f.kv_head = (float*)(b + L.kv_head);
   f.q_head = (float*)(b + L.q_head); f.q_frame = (float*)(b + L.q_frame);
   f.status = (unsigned*)(b + L.status);
+  f.tile_w = (float*)(b + L.tile_w);
   f.q2_codes = p->q_terms == 2 ? b + L.q2_codes : nullptr;
   f.q2_scales = p->q_terms == 2 ? b + L.q2_scales : nullptr;
   return f;
@@ -130,15 +134,20 @@ size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
   const size_t a = take(nkv * p->D * 8), b = take(nkv * p->D * 4), c = take(nkv * p->D * 4),
                d = take(nkv * 4), e = take((size_t)p->B * p->Hq * (nqt > 0 ? nqt : 1) * 4),
                fl = take((nflags > 0 ? nflags : 1) * 4);
+  // value norms, with the weighted hot test only
+  const size_t vn = p->hot_weight ? (size_t)p->B * p->Hkv : 0;
+  const size_t t1 = take(vn * g.NT * 4), s1 = take(vn * nch * 8);
   if (ws && base) {
     uint8_t* bb = (uint8_t*)base;
     ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
     ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e);
     ws->flags = (unsigned*)(bb + fl);
+    ws->vnt = vn ? (float*)(bb + t1) : nullptr;
+    ws->vnsum = vn ? (double*)(bb + s1) : nullptr;
     ws->nqt = nqt;
     ws->nch = nch;
-    ws->ch0 = stat_t0(g) / 16;
-    ws->ch1 = (stat_t1(g) + 15) / 16;
+    ws->ch0 = g.qt0 / 16;
+    ws->ch1 = (g.qt1 + 15) / 16;
     ws->nflags = (int)nflags;
   }
   return o;
@@ -257,6 +266,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->stat_keys = 0;
   p->block_table = nullptr;
   p->block_table_stride = 0;
+  p->hot_weight = 0;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }

@@ -29,7 +29,8 @@
 //   l_t     : one FP4 MFMA of P against a ones selector (numerator and
 //             denominator carry the same quantisation);
 //   vote    : row hot iff l_t > eps * lambda (lambda includes this tile),
-//             ballot over 16 rows;
+//             with value-norm weights l_t * w_t > eps * lambda; ballot over
+//             16 rows;
 //   cold PV : O^T += V^T P^T for the rows of cold groups, FP4 MFMA.
 // The accumulated state (o, l, lambda) is held in a second integer frame m_o
 // per row that trails the method's frame: P's E8M0 byte is E + m - m_o + 127,
@@ -72,6 +73,8 @@
 // the two states (their frames only scale them).  If the record fills up, or
 // the tail's frame would need a re-base, the tail walks positions [h, n) again
 // from the head's state instead.
+#include <type_traits>
+
 #include "apa_device.h"
 #include "apa_kernels.h"
 
@@ -90,6 +93,8 @@ enum Role { kWhole = 0, kHead = 1, kTail = 2 };
 // a float in LDS (an address-space-3 pointer keeps the accesses DS
 // instructions, which wait on their own counter, not on vector memory)
 typedef __attribute__((address_space(3))) float lds_float;
+// a read-only global float read through the scalar cache (uniform index)
+typedef __attribute__((address_space(4))) const float cfloat;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // Problems with at most this many key tiles log each visited tile's verdict
@@ -287,6 +292,7 @@ struct CtxBase {
   int dh;     // which share of the output channels the wave holds
   bool lead;  // the wave that writes the row scalars and hot words (dh = 0)
   float g_v;
+  const cfloat* tw;  // value-norm weights of the kv-head's tiles (nullptr: mass test)
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
   // the visit order: positions [0, npos()), position p at tile tile_of(p)
   __device__ __forceinline__ int npos() const { return dW + 1 - lo0; }
@@ -346,6 +352,7 @@ __device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4
     c.qs[h] = sb < 0 ? 0 : (sb > 254 ? 254 : sb);
   }
   c.g_v = f.kv_head[c.bhk * 8 + 4];
+  c.tw = g.vweight ? (const cfloat*)(f.tile_w + c.bhk * (size_t)g.NTc) : nullptr;
   c.blobs = blob_rsrc(f.kv_blob + c.bhk * (size_t)g.NTc * Tile<D>::BLOB,
                       (uint32_t)g.NT * Tile<D>::BLOB);
   c.koff = n * (D / 2) + 16 * hh;
@@ -658,7 +665,7 @@ __device__ __forceinline__ void assemble_words(const CtxBase<D>& c, Words& wd, c
 // return 0.  A head walk publishes its lambda from position nrep_tail on in
 // `pub_out`, in the state frame it had there (the frame the tail's replay ends
 // in).
-template <int D, bool LOG, bool TAIL, int QT>
+template <int D, bool LOG, bool TAIL, bool VW, int QT>
 __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
@@ -718,6 +725,9 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& s
 
   for (int i = 0; i < cnt && !gave_up; ++i) {
     const int t = tile_at(i);
+    // the tile's weight in the vote (a scalar load, consumed after the MFMAs;
+    // the mass test compiles without it)
+    const float wt = VW ? c.tw[t] : 1.0f;
     const bool replay = i < nrep;
     // pacing: publish this wave's position count; the SIMD partner's is read
     // now and compared once the tile's maxima are done
@@ -795,7 +805,7 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& s
     if (!TAIL && pub_out && i >= kReplay) pub_out[n] = ldexpf(st.lam, st.mo - mo_ref);
     float lam_t = st.lam;  // the running mass the vote compares against
     if (TAIL) lam_t = (pub_in && !replay ? vmax(lam_lo, pub_in[n]) : lam_lo) + st.lam;
-    const unsigned long long hb = __ballot(ell > epsv * lam_t);
+    const unsigned long long hb = __ballot(ell * wt > epsv * lam_t);
     bool hot0 = vis0 && (hb & 0xFFFFull) != 0ull;
     bool hot1 = vis1 && (hb & 0xFFFF0000ull) != 0ull;
     if (tail && !replay && eps != 0.0f && (hot0 || hot1)) {
@@ -917,7 +927,7 @@ __device__ __forceinline__ void zero_outside(const Geom& g, const CtxBase<D>& c,
 // decide the recorded groups against the head's lambda, take the P V of those
 // that are hot after all back out of the tail's state (the same FP4 codes with
 // their sign bits set, so exactly what was added), and set their bits.
-template <int D, int QT>
+template <int D, bool VW, int QT>
 __device__ __forceinline__ void settle(const Geom& g, const Ctx<D, QT>& c, St<D>& st, Words& tw,
                                        const Cand& cr, int ncand, float lam_a, float eps,
                                        int lane) {
@@ -940,8 +950,9 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D, QT>& c, St<D>
     uint32_t found = 0;  // 2 bits per record: groups hot after all
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const unsigned long long hb = __ballot(e[k] > eps * (lam_a + lbv[k]) && hh == 0);
       const uint32_t hdr = (uint32_t)__builtin_amdgcn_readfirstlane((int)hd[k]);
+      const float wk = VW ? c.tw[hdr & 0x3FFFFFFFu] : 1.0f;
+      const unsigned long long hb = __ballot(e[k] * wk > eps * (lam_a + lbv[k]) && hh == 0);
       const uint32_t gr = ((hdr >> 30 & 1u) && (hb & 0xFFFFull) != 0ull ? 1u : 0u) |
                           ((hdr >> 31) && (hb & 0xFFFF0000ull) != 0ull ? 2u : 0u);
       if (j0 + k < ncand) found |= gr << (2 * k);
@@ -1060,7 +1071,7 @@ __device__ __forceinline__ void load_state(const float* src, St<D>& st, Words& w
 // its final state at its end; the tail finishes the unit.  Units are numbered
 // (batch, kv-head, 32-row block, head), so the waves of a work group, and the
 // groups of an XCD, stream the same tiles.
-template <int D, bool LOG, int QT>
+template <int D, bool LOG, int QT, bool VW>
 __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>, kWavesPerSimd<D>))) void k_pass1(
     Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, uint8_t* split, int cap,
     int sched, int nunits) {
@@ -1130,7 +1141,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     init_state<D>(st, c.row_ok);
     Words wd = {role == kWhole ? -1 : shared_word(c.tile_of(h)), 0u, 0u, 0u, 0u};
     zero_outside<D>(g, c, lane);
-    walk<D, LOG, false>(g, c, st, wd, 0, 0, role == kWhole ? npos : h, eps, tau, Hf,
+    walk<D, LOG, false, VW>(g, c, st, wd, 0, 0, role == kWhole ? npos : h, eps, tau, Hf,
                         cand_of(f.kv_blob, 0, 0, D), 0, nullptr,
                         role == kHead ? (volatile lds_float*)pub[slot] : nullptr, vlog, lane,
                         pace_me, pace_mate, 0);
@@ -1184,7 +1195,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
       St<D> st;
       init_state<D>(st, c.row_ok);
       Words wd = {shared_word(c.tile_of(h)), 0u, 0u, 0u, 0u};
-      oc = walk<D, LOG, true>(g, c, st, wd, kReplay, h, kReplay + npos - h, eps, tau, Hf,
+      oc = walk<D, LOG, true, VW>(g, c, st, wd, kReplay, h, kReplay + npos - h, eps, tau, Hf,
                               cand_of(split, u, cap, D), cap,
                               (volatile lds_float*)pub[slot + k], nullptr, vlog, lane, pace_me,
                               pace_mate, walked);
@@ -1228,7 +1239,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
     const float a_lam = H.sc[2][lane];
     const float a_lsum = H.sc[3][lane];
     // the head's lambda in the tail's state frame (the tail never re-based)
-    settle<D>(g, c, st, wd, cr, oc, ldexpf(a_lam, a_mo - st.mo), eps, lane);
+    settle<D, VW>(g, c, st, wd, cr, oc, ldexpf(a_lam, a_mo - st.mo), eps, lane);
     // the shared words: the head's part and the tail's
     if (lane == 0) {
       c.bits0[0] = H.words[0] | wd.p00;
@@ -1267,7 +1278,7 @@ __global__ __launch_bounds__(kWgWaves<D> * 64) __attribute__((amdgpu_waves_per_e
 // The re-walk of units whose tail gave up (record full, or a re-base of its
 // frame): the head's state, left in the workspace, walks the tail positions.
 // One wave per unit; the others return at once.
-template <int D, bool LOG, int QT>
+template <int D, bool LOG, int QT, bool VW>
 __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float eps, float tau,
                                                      int hoff, Pass1Out out, uint8_t* split,
                                                      int cap, int sched) {
@@ -1301,7 +1312,7 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   Words wd = {wb, 0u, 0u, 0u, 0u};
   const Cand none = cand_of(f.kv_blob, 0, 0, D);
   __shared__ uint8_t vlog_sh[LOG ? kLogTiles : 1];
-  walk<D, LOG, false>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr,
+  walk<D, LOG, false, VW>(g, c, st, wd, 0, h, npos - h, eps, tau, (float)hoff, none, 0, nullptr,
                       nullptr, (lds_u8*)vlog_sh, lane);
   if (lane == 0) {
     c.bits0[0] = hw[0] | wd.p00;
@@ -1374,22 +1385,32 @@ hipError_t run_qt(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hof
   const int nblocks = (nunits + per - 1) / per;
   const int cap = split ? cand_cap(g, sched) : 0;
   const bool log = g.NT <= kLogTiles;
-  if (log)
-    hipLaunchKernelGGL((k_pass1<D, true, QT>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
-                       hoff, o, split, cap, sched, nunits);
-  else
-    hipLaunchKernelGGL((k_pass1<D, false, QT>), dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau,
-                       hoff, o, split, cap, sched, nunits);
+  // kernels per (log, weighted): the mass test carries no weight loads
+  auto main = [&](auto lg, auto vw) {
+    hipLaunchKernelGGL((k_pass1<D, decltype(lg)::value, QT, decltype(vw)::value>),
+                       dim3(nblocks), dim3(W * 64), 0, s, g, f, eps, tau, hoff, o, split, cap,
+                       sched, nunits);
+  };
+  auto rewalk = [&](auto lg, auto vw) {
+    hipLaunchKernelGGL((k_pass1_rewalk<D, decltype(lg)::value, QT, decltype(vw)::value>),
+                       dim3(nunits), dim3(64), 0, s, g, f, eps, tau, hoff, o, split, cap, sched);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (log) {
+    if (g.vweight) main(T{}, T{}); else main(T{}, F{});
+  } else {
+    if (g.vweight) main(F{}, T{}); else main(F{}, F{});
+  }
   if constexpr (kOutSplit<D> == 1) {
     if (!split) return hipGetLastError();
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (log)
-      hipLaunchKernelGGL((k_pass1_rewalk<D, true, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
-                         hoff, o, split, cap, sched);
-    else
-      hipLaunchKernelGGL((k_pass1_rewalk<D, false, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
-                         hoff, o, split, cap, sched);
+    if (log) {
+      if (g.vweight) rewalk(T{}, T{}); else rewalk(T{}, F{});
+    } else {
+      if (g.vweight) rewalk(F{}, T{}); else rewalk(F{}, F{});
+    }
   }
   return hipGetLastError();
 }

@@ -34,14 +34,34 @@ __device__ float block_max(float v, float* red) {
   return r;
 }
 
+// L2 norm of one value vector held 8 channels per thread by the ncg
+// consecutive lanes of a tile: squares summed in FP32 in channel order inside
+// a lane, then across the lanes by an xor butterfly (every lane ends with the
+// same sum: each step adds the same two values in either order).
+template <typename T>
+__device__ __forceinline__ float value_norm(const T* y, int ncg) {
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float v = to_f32<T>(y[i]);
+    q = fmaf(v, v, q);
+  }
+  for (int o = 1; o < ncg; o <<= 1) q += __shfl_xor(q, o);
+  return sqrtf(q);
+}
+
 // Per (b, kv-head, chunk of 16 tiles of 64 keys): per-channel FP64 sums in a
 // fixed order (keys ascending inside a tile, the chunk's tile sums
-// ascending), min and max of K, and max |V|.  Thread (tile tt, channel group
-// cg) owns 8 consecutive channels of one tile (16-byte loads).
-// grid (NCH, B*Hkv), block 2*D.
+// ascending), min and max of K, and max |V| over the statistics keys; a
+// non-finite check over every key read; with the weighted hot test, each
+// tile's largest value norm and the chunk's FP64 sum of the statistics keys'
+// value norms (keys ascending inside a tile, tiles ascending).  Thread (tile
+// tt, channel group cg) owns 8 consecutive channels of one tile (16-byte
+// loads).  grid (NCH, B*Hkv), block 2*D.
 template <typename T>
 __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const Geom& g,
-                         const QuantWs& ws, int ch, int bh, double* sh, float* red) {
+                         const QuantWs& ws, int ch, int bh, double* sh, float* red,
+                         double* tvs) {
   const int D = g.D, ncg = D / 8;
   const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
   const int t = ch * 16 + tt;
@@ -49,10 +69,15 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
   float mn[8], mx[8];
   float va = 0.0f;
   bool bad = false;
+  float vnm = 0.0f;  // the tile's largest value norm
+  double vns = 0.0;  // its statistics keys' value norms, summed
 #pragma unroll
   for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-  if (t < g.NT && t >= stat_t0(g) && t < stat_t1(g)) {
-    const int k0 = t * kTile, k1 = min(min(g.Nkv, stat_khi(g)), k0 + kTile);
+  const bool in = t < g.NT && t >= g.qt0 && t < g.qt1;
+  if (in) {
+    // keys [k0, k1) feed the statistics, [k1, kend) only the checks
+    const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
+    const int k1 = max(k0, min(stat_khi(g), kend));
     // the tile's keys are contiguous (flat or paged input)
     const size_t base = kv_elem(g, bh / g.Hkv, bh % g.Hkv, k0) + cg * 8;
 #pragma unroll 4
@@ -70,7 +95,26 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
         mx[i] = fmaxf(mx[i], x);
         va = fmaxf(va, fabsf(y));
       }
+      if (g.vweight) {
+        const float nu = value_norm<T>(evv, ncg);
+        vnm = fmaxf(vnm, nu);
+        vns += (double)nu;
+      }
     }
+    for (int k = k1; k < kend; ++k) {
+      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
+      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)(k - k0) * D);
+      const T* ek = reinterpret_cast<const T*>(&rk);
+      const T* evv = reinterpret_cast<const T*>(&rv);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        bad |= !__builtin_isfinite(to_f32<T>(ek[i])) || !__builtin_isfinite(to_f32<T>(evv[i]));
+      if (g.vweight) vnm = fmaxf(vnm, value_norm<T>(evv, ncg));
+    }
+  }
+  if (g.vweight && cg == 0) {
+    tvs[tt] = vns;
+    if (in) ws.vnt[(size_t)bh * g.NT + t] = vnm;
   }
   double* ssum = sh;
   float* smn = reinterpret_cast<float*>(sh + 16 * D);
@@ -103,6 +147,11 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
     float m = red[0];
     for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
     ws.vamax[(size_t)bh * ws.nch + ch] = m;
+    if (g.vweight) {
+      double c = 0.0;
+      for (int i = 0; i < 16; ++i) c += tvs[i];  // the chunk's tiles, ascending
+      ws.vnsum[(size_t)bh * ws.nch + ch] = c;
+    }
   }
 }
 
@@ -142,11 +191,14 @@ __device__ void head_scale(float amax, float* gs, float* inv) {
 constexpr int kFinBatch = 32;
 
 // Per (b, kv-head): key mean, |K - kbar| max, V max, their head scales, and
-// the tied Q scales of the group's query heads; every block also folds the
-// statistics blocks' non-finite flags and block 0 writes the status word.
-// grid (B*Hkv), block 2D.
+// the tied Q scales of the group's query heads; with the weighted hot test
+// the mean value norm nu_bar (FP64 sum of the chunk sums, ascending, over the
+// statistics keys; a frozen cache keeps its own) and the weight
+// w_t = max(1, nu_t / nu_bar) of every tile read (1 when nu_bar is 0).  Every
+// block also folds the statistics blocks' non-finite flags and block 0 writes
+// the status word.  grid (B*Hkv), block 2D.
 __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* xch,
-                         float* red) {
+                         float* red, float* nbs) {
   const int d = threadIdx.x, nthr = blockDim.x, D = g.D;
   const bool own = d < D;  // threads D .. 2D-1 fold min and max, and join the block reductions
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
@@ -210,10 +262,29 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   head_scale(amax_v, &gv, &iv);
   // frozen statistics: the K/V scales stay the cache's; Q's tie to its g_K
   if (g.frozen) gk = f.kv_head[(size_t)bh * 8 + 1];
+  if (g.vweight) {
+    if (d == 0) {
+      float nb = f.kv_head[(size_t)bh * 8 + 6];
+      if (!g.frozen) {
+        double sv = 0.0;
+        for (int c = ws.ch0; c < ws.ch1; ++c) sv += ws.vnsum[(size_t)bh * ws.nch + c];
+        const int nk = stat_khi(g) - stat_t0(g) * kTile;
+        nb = nk > 0 ? (float)(sv / (double)nk) : 0.0f;
+      }
+      *nbs = nb;
+    }
+    __syncthreads();
+    const float nb = *nbs;
+    for (int t = g.qt0 + d; t < g.qt1; t += nthr) {
+      const float nt = ws.vnt[(size_t)bh * g.NT + t];
+      f.tile_w[(size_t)bh * g.NTc + t] = nb > 0.0f ? fmaxf(1.0f, nt / nb) : 1.0f;
+    }
+  }
   if (d == 0 && !g.frozen) {
     float* kh = f.kv_head + (size_t)bh * 8;
     kh[0] = amax_k; kh[1] = gk; kh[2] = ik; kh[3] = amax_v; kh[4] = gv; kh[5] = iv;
-    kh[6] = 0.0f; kh[7] = 0.0f;
+    kh[6] = g.vweight ? *nbs : 0.0f;
+    kh[7] = 0.0f;
   }
   // Q heads of this group: inv_q = w * 2^-j, w = fl32(sl * g_k), j the
   // smallest integer with amax_q * w <= 6 * 2^j.
@@ -441,9 +512,10 @@ __global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const 
                         Geom g, QuantWs ws, int nkb) {
   extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
   __shared__ float red[16];
+  __shared__ double tvs[16];      // the tiles' value-norm sums
   if ((int)blockIdx.x < nkb) {
-    const int nc = ws.ch1 - ws.ch0;  // the chunks of the statistics tiles
-    kv_stats<T>(K, V, g, ws, ws.ch0 + blockIdx.x % nc, blockIdx.x / nc, sh, red);
+    const int nc = ws.ch1 - ws.ch0;  // the chunks of the tiles read
+    kv_stats<T>(K, V, g, ws, ws.ch0 + blockIdx.x % nc, blockIdx.x / nc, sh, red, tvs);
   } else {
     const int qb = blockIdx.x - nkb;
     // Q flags follow every (kv-head, chunk) slot, written or not
@@ -456,7 +528,8 @@ __global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const 
 __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
   extern __shared__ float xch[];  // [2][D]: min and max of each channel
   __shared__ float red[16];
-  finalize(g, ws, f, blockIdx.x, xch, red);
+  __shared__ float nbs;  // nu_bar
+  finalize(g, ws, f, blockIdx.x, xch, red, &nbs);
 }
 
 // Quantisation in one launch: blocks for Q rows first, then per (b, kv-head),

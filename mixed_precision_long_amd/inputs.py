@@ -178,25 +178,31 @@ def digest(*arrays) -> str:
     return h.hexdigest()
 
 
-def boost_value_tiles(V: np.ndarray, n_tiles: int, factor: float = 4.0, seed: int = 0,
-                      tile: int = 64, first_tile: int = 0) -> tuple:
-    """Values of a few key tiles made `factor` times larger, in place.
+def outlier_value_tiles(V: np.ndarray, n_tiles: int, factor: float = 4.0, seed: int = 0,
+                        tile: int = 64, first_tile: int = 0, dtype: str = "fp16") -> np.ndarray:
+    """A few key tiles whose values are `factor` times larger than the rest's,
+    in place: the chosen tiles keep their values and every other key's value
+    is divided by factor, so the largest values stay at the input's own scale.
 
     Stands in for the tokens with outsized value vectors behind the hazard
     of a cold tile whose small mass carries a large output component ("APA:
     sloppy attention, exact where it counts", section "Honest limits"): per
-    (batch, kv-head), n_tiles distinct tiles
-    drawn from [first_tile, ceil(Nkv / tile)) by a seeded generator, with
-    their V rows scaled by factor (a power of two keeps fp16/bf16 values
-    exact while nothing overflows).  Returns the chosen tiles [B][Hkv][n]."""
+    (batch, kv-head), n_tiles distinct tiles drawn from [first_tile,
+    ceil(Nkv / tile)) by a seeded generator.  The shrunken values are
+    rounded to `dtype` again (a power-of-two factor changes only their
+    exponent, except where fp16 values fall below its normal range).  Returns
+    the chosen tiles [B][Hkv][n]."""
     B, Hkv, Nkv, _ = V.shape
     nt = -(-Nkv // tile)
     rng = np.random.default_rng(seed)
     picks = np.zeros((B, Hkv, n_tiles), np.int64)
+    keep = np.zeros(Nkv, bool)
     for b in range(B):
         for j in range(Hkv):
             ts = rng.choice(np.arange(first_tile, nt), size=n_tiles, replace=False)
             picks[b, j] = ts
+            keep[:] = False
             for t in ts:
-                V[b, j, t * tile:min(Nkv, t * tile + tile)] *= np.float32(factor)
+                keep[t * tile:min(Nkv, t * tile + tile)] = True
+            V[b, j, ~keep] = round_to(V[b, j, ~keep] / np.float64(factor), dtype)
     return picks

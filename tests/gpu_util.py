@@ -83,6 +83,8 @@ def fp4_sections(p, fp4_host: np.ndarray) -> dict:
                      (B, Hkv, NkvP // 64, 68 * D)), D, Nkv),
         kbar=sec(L.kbar, B * Hkv * D, np.float32, (B, Hkv, D)),
         kv_head=sec(L.kv_head, B * Hkv * 8, np.float32, (B, Hkv, 8)),
+        tile_w=sec(L.tile_w, B * Hkv * (NkvP // 64), np.float32,
+                   (B, Hkv, NkvP // 64))[..., :-(-Nkv // 64)],
         q_head=sec(L.q_head, B * Hq * 4, np.float32, (B, Hq, 4)),
         q_frame=sec(L.q_frame, B * Hq * NqP, np.float32, (B, Hq, NqP))[:, :, :Nq],
         status=int(sec(L.status, 1, np.uint32, (1,))[0]))

@@ -20,21 +20,26 @@ import torch
 
 from gpu_util import fp4_sections, problem_for, run_exact_gpu, run_gpu, torch_inputs
 from mixed_precision_long_amd import apa
-from mixed_precision_long_amd.inputs import make_inputs, small_workload
+from mixed_precision_long_amd.inputs import outlier_value_tiles, make_inputs, small_workload
 from oracle import oracle as O
 from test_gpu_parity import check_cold_state, check_mask, check_output, check_quant
+from test_gpu_weight import check_weights
 
 pytestmark = pytest.mark.gpu
 
 RESTAT = 1.125
 
 
-@pytest.mark.parametrize("D,dtype", [(128, "fp16"), (64, "bf16")])
-def test_chunked_prefill_over_a_persistent_fp4_cache(D, dtype):
+@pytest.mark.parametrize("D,dtype,hw", [(128, "fp16", 0), (64, "bf16", 0), (128, "fp16", 1)])
+def test_chunked_prefill_over_a_persistent_fp4_cache(D, dtype, hw):
+    """hw = 1: the value-norm weighted hot test, whose new tiles take their
+    weights against the cache's mean value norm."""
     Hq, Hkv, N = 4, 2, 2400
     chunks = [2048, 2200, 2400]  # 2200 < 1.125 x 2048: tiles only; 2400 > 2304: restat
     w = small_workload(1, Hq, Hkv, N, N, D, dtype=dtype, seed=81)
     Qall, Kall, Vall = make_inputs(w)
+    if hw:
+        outlier_value_tiles(Vall, 4, 8.0, seed=81)
     eps = 0.02
     cap = N
     # one device copy of K/V at full length; each chunk's problem uses its prefix
@@ -59,7 +64,8 @@ def test_chunked_prefill_over_a_persistent_fp4_cache(D, dtype):
         kk = kd[:, :, :n].contiguous()
         vv = vd[:, :, :n].contiguous()
         p = apa.problem(1, Hq, Hkv, nq, n, D, dtype=apa.APA_F16 if dtype == "fp16" else apa.APA_BF16,
-                        scale=w.scale, kv_capacity=cap, stat_keys=0 if stat == n else stat)
+                        scale=w.scale, kv_capacity=cap, stat_keys=0 if stat == n else stat,
+                        hot_weight=hw)
         bufs = apa.alloc(p, with_lambda=True)
         bufs.fp4 = fp4
         if restat:
@@ -77,10 +83,12 @@ def test_chunked_prefill_over_a_persistent_fp4_cache(D, dtype):
                  hot=unpack_bits(p, bufs.bits.cpu().numpy()), out=bufs.out.float().cpu().numpy(),
                  lse=bufs.lse.cpu().numpy())
         po = O.Params(1, Hq, Hkv, nq, n, D, scale=w.scale, eps=eps,
-                      stat_keys=0 if stat == n else stat)
+                      stat_keys=0 if stat == n else stat, hot_weight=hw)
         prep = O.quantize(po, Q, K, V)
         r = O.run(po, Q, K, V, prep)
         check_quant(g, prep)
+        if hw:
+            check_weights(g, prep)
         mism = check_mask(g["hot"], r)
         check_cold_state(g, r, mism)
         check_output(g["out"], r["O"], dtype=dtype)
@@ -89,7 +97,8 @@ def test_chunked_prefill_over_a_persistent_fp4_cache(D, dtype):
         # the same problem quantised in one shot with the same statistics
         one = run_gpu(apa.problem(1, Hq, Hkv, nq, n, D,
                                   dtype=apa.APA_F16 if dtype == "fp16" else apa.APA_BF16,
-                                  scale=w.scale, stat_keys=0 if stat == n else stat),
+                                  scale=w.scale, stat_keys=0 if stat == n else stat,
+                                  hot_weight=hw),
                       Q, K, V, eps, dtype=dtype)
         for key in ("out", "lse", "hot"):
             assert np.array_equal(np.nan_to_num(one[key]), np.nan_to_num(g[key])), key
@@ -108,14 +117,17 @@ def _pages(arr, B, Hkv, Nkv, D, perm, npages, dt):
 
 
 @pytest.mark.parametrize("case", [
-    (2, 6, 2, 200, 3000, 128, "fp16", "path", 0),
-    (2, 4, 1, 96, 2048, 512, "bf16", "gauss", 0),
-    (1, 4, 2, 128, 5000, 64, "fp16", "path", 1500),   # with a sliding window
-], ids=["gqa3_D128", "bf16_D512", "window"])
+    (2, 6, 2, 200, 3000, 128, "fp16", "path", 0, 0),
+    (2, 4, 1, 96, 2048, 512, "bf16", "gauss", 0, 0),
+    (1, 4, 2, 128, 5000, 64, "fp16", "path", 1500, 0),   # with a sliding window
+    (2, 6, 2, 200, 3000, 128, "fp16", "path", 0, 1),     # value-norm weighted test
+], ids=["gqa3_D128", "bf16_D512", "window", "weighted"])
 def test_paged_kv_equals_flat(case):
-    B, Hq, Hkv, Nq, Nkv, D, dtype, mode, window = case
+    B, Hq, Hkv, Nq, Nkv, D, dtype, mode, window, hw = case
     w = small_workload(B, Hq, Hkv, Nq, Nkv, D, dtype=dtype, mode=mode, seed=82)
     Q, K, V = make_inputs(w)
+    if hw:
+        outlier_value_tiles(V, 4, 8.0, seed=82)
     eps = 0.02
     NT = -(-Nkv // 64)
     npages = B * NT + 5
@@ -125,7 +137,7 @@ def test_paged_kv_equals_flat(case):
     kp, vp = (_pages(x, B, Hkv, Nkv, D, perm, npages, dt) for x in (K, V))
     q = torch.from_numpy(Q).to(dt).cuda()
     kw = dict(dtype=apa.APA_F16 if dtype == "fp16" else apa.APA_BF16, scale=w.scale,
-              window=window)
+              window=window, hot_weight=hw)
     flat = run_gpu(apa.problem(B, Hq, Hkv, Nq, Nkv, D, **kw), Q, K, V, eps, dtype=dtype)
     paged = run_gpu(apa.problem(B, Hq, Hkv, Nq, Nkv, D, block_table=bt, **kw), Q, K, V, eps,
                     dtype=dtype, tensors=(q, kp, vp))
@@ -135,7 +147,9 @@ def test_paged_kv_equals_flat(case):
     # the codes the library writes (with a window: from the first visible tile)
     t0 = max(0, Nkv - Nq - window + 1) // 64 if window else 0
     cut = {"kc": (2, 64), "ks": (2, 64), "vc": (3, 32), "vs": (3, 2)}
-    for key in ("kc", "ks", "vc", "vs", "qc", "qs", "kbar", "kv_head", "q_head", "q_frame"):
+    cut["tile_w"] = (2, 1)
+    for key in ("kc", "ks", "vc", "vs", "qc", "qs", "kbar", "kv_head", "q_head", "q_frame") + (
+            ("tile_w",) if hw else ()):
         a, b = flat["fp4"][key], paged["fp4"][key]
         if key in cut:
             ax, per = cut[key]

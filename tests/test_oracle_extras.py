@@ -27,7 +27,7 @@ import numpy as np
 import pytest
 
 from brute_apa import MAGS, brute_apa, nearest_mag_code
-from mixed_precision_long_amd.inputs import boost_value_tiles, make_inputs, small_workload
+from mixed_precision_long_amd.inputs import outlier_value_tiles, make_inputs, small_workload
 from oracle import oracle as O
 
 
@@ -369,7 +369,7 @@ def test_hot_weight_pass1_bitwise_vs_brute_force(case):
     w = small_workload(1, Hq, Hkv, Nq, Nkv, D, seed=seed)
     Q, K, V = make_inputs(w)
     p = O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale, eps=eps, window=window, hot_weight=1)
-    boost_value_tiles(V, nb, factor, seed=seed, first_tile=p.first_tile)
+    outlier_value_tiles(V, nb, factor, seed=seed, first_tile=p.first_tile)
     prep = O.quantize(p, Q, K, V)
     r = O.run(p, Q, K, V, prep, pass2=False)
     b = brute_apa(Q, K, V, eps, w.scale, window=window, hot_weight=True)
@@ -430,7 +430,7 @@ def test_hot_weight_bounds_cold_output_norm(eps):
     Nq, Nkv = 128, 8192
     w = small_workload(1, 2, 1, Nq, Nkv, 64, seed=66)
     Q, K, V = make_inputs(w)
-    boost_value_tiles(V, 4, 8.0, seed=66)
+    outlier_value_tiles(V, 4, 8.0, seed=66)
     b = brute_apa(Q, K, V, eps, w.scale, hot_weight=True)
     nu = np.linalg.norm(V[0, 0].astype(np.float64), axis=1)
     nbar = nu.mean()
@@ -475,7 +475,7 @@ def test_hot_weight_lowers_the_error_of_large_value_tiles():
     Nq, Nkv = 128, 4096
     w = small_workload(1, 4, 1, Nq, Nkv, 64, seed=67)
     Q, K, V = make_inputs(w)
-    boost_value_tiles(V, 6, 16.0, seed=67)
+    outlier_value_tiles(V, 6, 16.0, seed=67)
     Oe, _ = O.exact(O.Params(1, 4, 1, Nq, Nkv, 64, scale=w.scale), Q, K, V)
     err, nhot = {}, {}
     for hw in (0, 1):
