@@ -192,7 +192,7 @@ def main():
 
     import torch
     from mixed_precision_long_amd import apa
-    from mixed_precision_long_amd.inputs import WORKLOADS, make_inputs
+    from mixed_precision_long_amd.inputs import WORKLOADS, make_inputs, outlier_value_tiles
 
     w = WORKLOADS[args.workload]
     eps = w.eps if args.eps is None else args.eps
@@ -203,7 +203,8 @@ def main():
     q = torch.from_numpy(Q).to(dt).cuda()
     k = torch.from_numpy(K).to(dt).cuda()
     v = torch.from_numpy(V).to(dt).cuda()
-    del Q, K, V
+    V_host = V  # kept for the outlier-value inputs of the weighted hot test
+    del Q, K
     p = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
                     dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16, scale=w.scale)
     bufs = apa.alloc(p)
@@ -318,46 +319,68 @@ def main():
                                "max_abs": round(float((out - ef).abs().max()), 5)}
         print("[bench] exact %.3f ms" % ems, file=sys.stderr, flush=True)
 
+    def variant(p2, vv=None, ref=None):
+        """One APA configuration on the same inputs (V replaced by vv if
+        given): 10 timed steps after 2, per-kernel times, hot cells, and its
+        output against `ref` (the exact output of the same inputs)."""
+        vv = v if vv is None else vv
+        b2 = apa.alloc(p2)
+        ev2 = []
+        for i in range(2 + 10):
+            step_eps(apa, p2, q, k, vv, b2, eps, stream, ev2 if i >= 2 else None)
+        torch.cuda.synchronize()
+        hot2 = apa_hot_mask(p2, b2.bits)
+        c2, h2, _, _ = cell_counts(hot2, w.Nq, w.Nkv)
+        kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in ev2])) for a in range(3)]
+        tt = {"ms": round(float(np.mean([x[0].elapsed_time(x[3]) for x in ev2])), 4),
+              "kernels_ms": {"quantize": round(kms[0], 4), "pass1": round(kms[1], 4),
+                             "pass2": round(kms[2], 4)},
+              "hot_cells": round(h2 / max(c2, 1), 5)}
+        if ref is not None:
+            o2 = b2.out.float()
+            cos2 = torch.nn.functional.cosine_similarity(o2.reshape(-1, w.D),
+                                                         ref.reshape(-1, w.D), dim=1)
+            tt["vs_exact"] = {"cos_min": round(float(cos2.min()), 6),
+                              "cos_median": round(float(cos2.median()), 6),
+                              "max_abs": round(float((o2 - ref).abs().max()), 5)}
+        del b2
+        return tt
+
+    def prob(**kw):
+        return apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                           dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
+                           scale=w.scale, **kw)
+
+    ef_or_none = ef if "apa_vs_exact" in res else None
     if not args.no_variants and w.D <= 256:
         # the pages' second-hunt accuracy fixes: Q plus its FP4 residual term,
         # K block exponents by least squared error, and both
         for name, qt, kl in (("two_term_q", 2, 0), ("k_lsq", 1, 1), ("two_term_q_k_lsq", 2, 1)):
-            p2 = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
-                             dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
-                             scale=w.scale, q_terms=qt, k_lsq=kl)
-            b2 = apa.alloc(p2)
-            ev2 = []
-            for i in range(2 + 10):
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                e[0].record(stream)
-                apa.quantize(p2, q, k, v, b2.fp4, b2.ws_q, stream)
-                e[1].record(stream)
-                apa.pass1(p2, b2.fp4, eps, b2.cold_m, b2.cold_l, b2.cold_o, b2.bits, None,
-                          ws=b2.ws_p1, stream=stream)
-                e[2].record(stream)
-                apa.pass2(p2, q, k, v, b2.fp4, b2.bits, b2.cold_m, b2.cold_l, b2.cold_o, True,
-                          out=b2.out, lse=b2.lse, ws=b2.ws_p2, stream=stream)
-                e[3].record(stream)
-                if i >= 2:
-                    ev2.append(e)
-            torch.cuda.synchronize()
-            hot2 = apa_hot_mask(p2, b2.bits)
-            c2, h2, _, _ = cell_counts(hot2, w.Nq, w.Nkv)
-            kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in ev2])) for a in range(3)]
-            tt = {"ms": round(float(np.mean([x[0].elapsed_time(x[3]) for x in ev2])), 4),
-                  "kernels_ms": {"quantize": round(kms[0], 4), "pass1": round(kms[1], 4),
-                                 "pass2": round(kms[2], 4)},
-                  "hot_cells": round(h2 / max(c2, 1), 5)}
-            if "apa_vs_exact" in res:
-                o2 = b2.out.float()
-                cos2 = torch.nn.functional.cosine_similarity(o2.reshape(-1, w.D),
-                                                             ef.reshape(-1, w.D), dim=1)
-                tt["vs_exact"] = {"cos_min": round(float(cos2.min()), 6),
-                                  "cos_median": round(float(cos2.median()), 6),
-                                  "max_abs": round(float((o2 - ef).abs().max()), 5)}
-            res[name] = tt
-            del b2
-            print("[bench] %s %.3f ms" % (name, tt["ms"]), file=sys.stderr, flush=True)
+            res[name] = variant(prob(q_terms=qt, k_lsq=kl), ref=ef_or_none)
+            print("[bench] %s %.3f ms" % (name, res[name]["ms"]), file=sys.stderr, flush=True)
+
+    if not args.no_variants:
+        # the value-norm weighted hot test: on these inputs, and on the same
+        # inputs with outlier values (64 tiles per KV head whose values are 8x
+        # the rest's), the mass test and the weighted test against the exact
+        # output of those inputs
+        vw = {"inputs": variant(prob(hot_weight=1), ref=ef_or_none)}
+        Vo = V_host.copy()
+        outlier_value_tiles(Vo, 64, 8.0, seed=5, dtype=w.dtype)
+        vo = torch.from_numpy(Vo).to(dt).cuda()
+        del Vo
+        eo2 = torch.empty_like(q)
+        apa.exact(p, q, k, vo, eo2, None, stream=stream)
+        ref2 = eo2.float()
+        del eo2
+        vw["outlier_values"] = {
+            "recipe": "64 tiles per KV head keep their values, all other keys' values / 8",
+            "mass_test": variant(prob(), vv=vo, ref=ref2),
+            "weighted_test": variant(prob(hot_weight=1), vv=vo, ref=ref2)}
+        del vo, ref2
+        res["value_norm_weight"] = vw
+        print("[bench] value-norm weight %.3f ms" % vw["inputs"]["ms"], file=sys.stderr,
+              flush=True)
 
     if w.eps_sweep and not args.no_sweep:
         # each eps: the same step, warmed up, with its kernels timed apart
