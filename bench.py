@@ -173,7 +173,7 @@ def main():
     ap.add_argument("--eps", type=float, default=None)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-exact", action="store_true", help="skip timing the all-exact path")
-    ap.add_argument("--cpu-groups", type=int, default=64,
+    ap.add_argument("--cpu-groups", type=int, default=384,
                     help="row groups of the CPU oracle's sample (also the rows of vs_fp64)")
     ap.add_argument("--no-sweep", action="store_true", help="skip the eps sweep")
     ap.add_argument("--no-variants", action="store_true",

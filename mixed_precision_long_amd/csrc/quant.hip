@@ -315,9 +315,10 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   }
 }
 
-// Least-squares block exponent of a 32-element block held 8 per thread by 4
-// consecutive lanes ("Second hunt": K's block scales picked from a small set
-// of candidates by least squared error).  Candidates: e0 (no clipping), then
+// Block exponent of K by squared error ("Second hunt: which operand is to
+// blame"), for a 32-element block held 8 per thread by 4 consecutive lanes:
+// each candidate exponent quantises the block, and the one whose dequantised
+// values lie closest to the inputs wins.  Candidates: e0 (no clipping), then
 // e0 - 1 and e0 + 1, clamped to [-127, 127]; a later one wins only with a
 // strictly smaller error.  The error is summed in FP32: d*d added in element
 // order inside a lane, then the lanes' sums as (r0 + r1) + (r2 + r3).
