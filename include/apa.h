@@ -151,7 +151,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *              [66D, 68D)  V scales, channel 32*db + n and key half hh at
  *                          byte (2n + hh) * D/32 + db
  *   kbar     [B][Hkv][D] float       per-channel key mean
- *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, g_V, inv_V,
+ *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, 1, 1 (V's scale),
  *                                    nu_bar (with hot_weight, else 0), 0
  *   tile_w   [B][Hkv][NTc] float     with hot_weight: the value-norm weight
  *                                    w_t of every tile some row sees (the
@@ -191,13 +191,14 @@ const char* apa_last_hip_error(void);
  * Reads q, k, v (dtype of p), writes the whole FP4 buffer `fp4`
  * (apa_fp4_bytes(p) bytes, 256-byte aligned).  Per (b, kv-head): kbar = the
  * per-channel mean of K (FP64 sum in a fixed order), K is centred, and
- * K - kbar and V are normalised by one FP32 scale per head that maps the
- * head's largest magnitude to 6; Q's per-head scale is tied to K's so the
- * score factor is a power of two 2^j.  Blocks of 32 (Q, K along D; V along
- * keys) get an E8M0 exponent, the smallest that fits the block maximum under
- * 6, and E2M1 codes rounded to nearest even.  With hot_weight it also
- * writes nu_bar (FP64 sum of the FP32 key norms, in key order per tile and
- * tiles ascending) and the weight of every tile some row sees.  The status
+ * K - kbar is normalised by one FP32 scale per head that maps the head's
+ * largest magnitude to 6; Q's per-head scale is tied to K's so the score
+ * factor is a power of two 2^j; V keeps its own scale (per-head scale 1:
+ * the E8M0 block exponents hold its range).  Blocks of 32 (Q, K along D; V
+ * along keys) get an E8M0 exponent, the smallest that fits the block maximum
+ * under 6, and E2M1 codes rounded to nearest even.  With hot_weight it also
+ * writes nu_bar (FP64 sums of the FP32 key norms, keys ascending per tile,
+ * then runs of tiles) and the weight of every tile some row sees.  The status
  * word reports non-finite values among Q and every K/V tile it quantises.
  * ws: apa_workspace_bytes(p, APA_CALL_QUANTIZE) bytes. */
 apa_status apa_quantize(const apa_problem* p, const void* q, const void* k, const void* v,
@@ -227,8 +228,9 @@ apa_status apa_quantize_tiles(const apa_problem* p, const void* q, const void* k
  * array inside the library, 16 MiB per GPU, held until the process ends;
  * the call allocates nothing.  Problems
  * whose apa_workspace_bytes(p, APA_CALL_QUANTIZE) exceeds that get
- * APA_ERR_WORKSPACE (about B * Hkv * ceil(Nkv / 1024) * D * 16 bytes: one
- * million keys at 8 KV heads and D = 128 fit).  Every call on one GPU uses
+ * APA_ERR_WORKSPACE (about B * Hkv * ceil(Nkv / 1024) * D * 16 bytes plus
+ * 8 bytes per 64-key tile and 128-channel slice: 960000 keys at 8 KV heads
+ * and D = 128 fit).  Every call on one GPU uses
  * that GPU's one array, and each call writes all of the scratch it reads, so
  * nothing carries over between calls; calls that overlap on one GPU (on
  * different streams without ordering) race and must not be issued.  Same

@@ -69,20 +69,29 @@ __host__ __device__ inline int first_key_tile(const Geom& g) {
 __host__ __device__ inline int stat_t0(const Geom& g) { return g.frozen ? g.qt0 : first_key_tile(g); }
 __host__ __device__ inline int stat_khi(const Geom& g) { return g.frozen ? g.Nkv : g.stat_hi; }
 
+// Statistics scratch.  V items are (b, kv-head, tile, 128-channel slice): the
+// V^T coding blocks of the statistics pass.  flags: one word per statistics
+// block (a non-finite input seen), K chunks first, then V items, then Q tiles.
 struct QuantWs {
   double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
   float* kmin;    // [B*Hkv][NCH][D]
   float* kmax;    // [B*Hkv][NCH][D]
-  float* vamax;   // [B*Hkv][NCH]
+  float* vamax;   // [B*Hkv][NT][NVZ] max |V| over the statistics keys per V item
   float* qamax;   // [B*Hq][NQT]
-  unsigned* flags;  // [NKB + NQB] per statistics block: a non-finite input seen
-  float* vnt;     // [B*Hkv][NT]  largest key value norm of each tile read
-  double* vnsum;  // [B*Hkv][NCH] sum of the statistics keys' value norms per chunk
+  unsigned* flags;  // [B*Hkv*NCH + B*Hkv*NT*NVZ + B*Hq*NQT]
+  float* vnt;     // [B*Hkv][NT]  largest value norm of each tile read (weighted test)
+  double* vnst;   // [B*Hkv][NT]  the sum of its statistics keys' value norms
   int nqt;        // ceil(Nq / 64)
   int nch;        // ceil(NT / 16)
+  int nvz;        // 128-channel slices of V per tile: ceil(D / 128)
   int ch0, ch1;   // the chunks holding the tiles read, [qt0, qt1)
-  int nflags;     // NKB + NQB
 };
+__host__ __device__ inline size_t vflag0(const Geom& g, const QuantWs& ws) {
+  return (size_t)g.B * g.Hkv * ws.nch;
+}
+__host__ __device__ inline size_t qflag0(const Geom& g, const QuantWs& ws) {
+  return vflag0(g, ws) + (size_t)g.B * g.Hkv * g.NT * ws.nvz;
+}
 
 struct Pass1Out {
   int32_t* m;

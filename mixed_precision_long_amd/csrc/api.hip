@@ -126,29 +126,31 @@ Fp4Ptrs fp4_ptrs(const apa_problem* p, const void* base) {
 size_t quant_ws(const apa_problem* p, QuantWs* ws, void* base) {
   const Geom g = geom(p);
   const int nch = (g.NT + 15) / 16;
+  const int nvz = (p->D + 127) / 128;
   const size_t nkv = (size_t)p->B * p->Hkv * nch;
+  const size_t nvi = (size_t)p->B * p->Hkv * g.NT * nvz;
   const int nqt = (p->Nq + 63) / 64;
+  const size_t nqf = (size_t)p->B * p->Hq * nqt;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-  const size_t nflags = (p->Nkv > 0 ? nkv : 0) + (p->Nq > 0 ? (size_t)p->B * p->Hq * nqt : 0);
   const size_t a = take(nkv * p->D * 8), b = take(nkv * p->D * 4), c = take(nkv * p->D * 4),
-               d = take(nkv * 4), e = take((size_t)p->B * p->Hq * (nqt > 0 ? nqt : 1) * 4),
-               fl = take((nflags > 0 ? nflags : 1) * 4);
+               d = take((nvi > 0 ? nvi : 1) * 4), e = take((nqf > 0 ? nqf : 1) * 4),
+               fl = take((nkv + nvi + nqf > 0 ? nkv + nvi + nqf : 1) * 4);
   // value norms, with the weighted hot test only
-  const size_t vn = p->hot_weight ? (size_t)p->B * p->Hkv : 0;
-  const size_t t1 = take(vn * g.NT * 4), s1 = take(vn * nch * 8);
+  const size_t vn = p->hot_weight ? (size_t)p->B * p->Hkv * g.NT : 0;
+  const size_t t1 = take(vn * 4), s1 = take(vn * 8);
   if (ws && base) {
     uint8_t* bb = (uint8_t*)base;
     ws->ksum = (double*)(bb + a); ws->kmin = (float*)(bb + b); ws->kmax = (float*)(bb + c);
     ws->vamax = (float*)(bb + d); ws->qamax = (float*)(bb + e);
     ws->flags = (unsigned*)(bb + fl);
     ws->vnt = vn ? (float*)(bb + t1) : nullptr;
-    ws->vnsum = vn ? (double*)(bb + s1) : nullptr;
+    ws->vnst = vn ? (double*)(bb + s1) : nullptr;
     ws->nqt = nqt;
     ws->nch = nch;
+    ws->nvz = nvz;
     ws->ch0 = g.qt0 / 16;
     ws->ch1 = (g.qt1 + 15) / 16;
-    ws->nflags = (int)nflags;
   }
   return o;
 }

@@ -6,13 +6,19 @@
 // ("Mean-centred K"), with one FP32 scale per head.  Here the block format is
 // MXFP4: one E8M0 exponent per 32 elements (Q and K along channels, V along
 // keys), the smallest that fits the block maximum under 6, and E2M1 codes
-// rounded to nearest even by the hardware's scaled conversion.
+// rounded to nearest even by the hardware's scaled conversion.  The page's
+// per-head scale serves NVFP4's narrow UE4M3 block scales; with E8M0 block
+// exponents it only moves the mantissas of the normalised values, so V, whose
+// codes need no statistics, enters at its own scale (per-head scale 1) and is
+// coded in the statistics pass.  K needs its mean first and Q its tie to K's
+// scale, so they are coded in a second pass.
 //
-// HBM-bound work: K and V are read twice (statistics, then quantisation) and
-// Q once; every reduction has a fixed order, so results are deterministic.
-// The quantisation pass takes Q and the KV heads in the reverse of the order
-// the statistics pass read them, so the data read last, still in the
-// last-level (Infinity) cache, is read again first.
+// HBM-bound work: K is read twice (statistics, then quantisation), V and Q
+// once each (Q twice: its maximum, then its codes); every reduction has a
+// fixed order, so results are deterministic.  The quantisation pass takes Q
+// and the KV heads in the reverse of the order the statistics pass read
+// them, so the data read last, still in the last-level (Infinity) cache, is
+// read again first.
 #include "apa_device.h"
 #include "apa_kernels.h"
 
@@ -34,100 +40,62 @@ __device__ float block_max(float v, float* red) {
   return r;
 }
 
-// L2 norm of one value vector held 8 channels per thread by the ncg
-// consecutive lanes of a tile: squares summed in FP32 in channel order inside
-// a lane, then across the lanes by an xor butterfly (every lane ends with the
-// same sum: each step adds the same two values in either order).
+// Per (b, kv-head, chunk of 16 tiles of 64 keys): per-channel FP64 sums of K
+// in a fixed order (keys ascending inside a tile, the chunk's tile sums
+// ascending), min and max of K over the statistics keys, and a non-finite
+// check over every key read.  Thread (tile tt, channel group cg) owns 8
+// consecutive channels of one tile (16-byte loads); a block of
+// min(2*D, 512) threads takes the chunk's 16 tiles at once (in two passes of
+// 8 at D = 512).
 template <typename T>
-__device__ __forceinline__ float value_norm(const T* y, int ncg) {
-  float q = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float v = to_f32<T>(y[i]);
-    q = fmaf(v, v, q);
-  }
-  for (int o = 1; o < ncg; o <<= 1) q += __shfl_xor(q, o);
-  return sqrtf(q);
-}
-
-// Per (b, kv-head, chunk of 16 tiles of 64 keys): per-channel FP64 sums in a
-// fixed order (keys ascending inside a tile, the chunk's tile sums
-// ascending), min and max of K, and max |V| over the statistics keys; a
-// non-finite check over every key read; with the weighted hot test, each
-// tile's largest value norm and the chunk's FP64 sum of the statistics keys'
-// value norms (keys ascending inside a tile, tiles ascending).  Thread (tile
-// tt, channel group cg) owns 8 consecutive channels of one tile (16-byte
-// loads).  grid (NCH, B*Hkv), block 2*D.
-template <typename T>
-__device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const Geom& g,
-                         const QuantWs& ws, int ch, int bh, double* sh, float* red,
-                         double* tvs) {
+__device__ void k_chunk_stats(const T* __restrict__ K, const Geom& g, const QuantWs& ws, int ch,
+                              int bh, double* sh) {
   const int D = g.D, ncg = D / 8;
-  const int tt = threadIdx.x / ncg, cg = threadIdx.x % ncg;
-  const int t = ch * 16 + tt;
-  double s[8];
-  float mn[8], mx[8];
-  float va = 0.0f;
-  bool bad = false;
-  float vnm = 0.0f;  // the tile's largest value norm
-  double vns = 0.0;  // its statistics keys' value norms, summed
-#pragma unroll
-  for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-  const bool in = t < g.NT && t >= g.qt0 && t < g.qt1;
-  if (in) {
-    // keys [k0, k1) feed the statistics, [k1, kend) only the checks
-    const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
-    const int k1 = max(k0, min(stat_khi(g), kend));
-    // the tile's keys are contiguous (flat or paged input)
-    const size_t base = kv_elem(g, bh / g.Hkv, bh % g.Hkv, k0) + cg * 8;
-#pragma unroll 4
-    for (int k = k0; k < k1; ++k) {
-      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
-      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)(k - k0) * D);
-      const T* ek = reinterpret_cast<const T*>(&rk);
-      const T* evv = reinterpret_cast<const T*>(&rv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = to_f32<T>(ek[i]), y = to_f32<T>(evv[i]);
-        bad |= !__builtin_isfinite(x) || !__builtin_isfinite(y);
-        s[i] += (double)x;
-        mn[i] = fminf(mn[i], x);
-        mx[i] = fmaxf(mx[i], x);
-        va = fmaxf(va, fabsf(y));
-      }
-      if (g.vweight) {
-        const float nu = value_norm<T>(evv, ncg);
-        vnm = fmaxf(vnm, nu);
-        vns += (double)nu;
-      }
-    }
-    for (int k = k1; k < kend; ++k) {
-      const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
-      const uint4 rv = *reinterpret_cast<const uint4*>(V + base + (size_t)(k - k0) * D);
-      const T* ek = reinterpret_cast<const T*>(&rk);
-      const T* evv = reinterpret_cast<const T*>(&rv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        bad |= !__builtin_isfinite(to_f32<T>(ek[i])) || !__builtin_isfinite(to_f32<T>(evv[i]));
-      if (g.vweight) vnm = fmaxf(vnm, value_norm<T>(evv, ncg));
-    }
-  }
-  if (g.vweight && cg == 0) {
-    tvs[tt] = vns;
-    if (in) ws.vnt[(size_t)bh * g.NT + t] = vnm;
-  }
+  const int tpp = blockDim.x / ncg;  // tiles per pass
+  const int cg = threadIdx.x % ncg;
   double* ssum = sh;
   float* smn = reinterpret_cast<float*>(sh + 16 * D);
   float* smx = smn + 16 * D;
+  bool bad = false;
+  for (int tt = threadIdx.x / ncg; tt < 16; tt += tpp) {
+    const int t = ch * 16 + tt;
+    double s[8];
+    float mn[8], mx[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ssum[tt * D + cg * 8 + i] = s[i];
-    smn[tt * D + cg * 8 + i] = mn[i];
-    smx[tt * D + cg * 8 + i] = mx[i];
+    for (int i = 0; i < 8; ++i) { s[i] = 0.0; mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+    if (t < g.NT && t >= g.qt0 && t < g.qt1) {
+      // keys [k0, k1) feed the statistics, [k1, kend) only the check
+      const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
+      const int k1 = max(k0, min(stat_khi(g), kend));
+      // the tile's keys are contiguous (flat or paged input)
+      const size_t base = kv_elem(g, bh / g.Hkv, bh % g.Hkv, k0) + cg * 8;
+#pragma unroll 8
+      for (int k = k0; k < k1; ++k) {
+        const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
+        const T* ek = reinterpret_cast<const T*>(&rk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float x = to_f32<T>(ek[i]);
+          bad |= !__builtin_isfinite(x);
+          s[i] += (double)x;
+          mn[i] = fminf(mn[i], x);
+          mx[i] = fmaxf(mx[i], x);
+        }
+      }
+      for (int k = k1; k < kend; ++k) {
+        const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
+        const T* ek = reinterpret_cast<const T*>(&rk);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bad |= !__builtin_isfinite(to_f32<T>(ek[i]));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ssum[tt * D + cg * 8 + i] = s[i];
+      smn[tt * D + cg * 8 + i] = mn[i];
+      smx[tt * D + cg * 8 + i] = mx[i];
+    }
   }
-  // block max of |V|, and whether the block saw a non-finite input
-  for (int o = 32; o >= 1; o >>= 1) va = fmaxf(va, __shfl_xor(va, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = va;
   bad = __syncthreads_or(bad);
   if (threadIdx.x == 0) ws.flags[(size_t)bh * ws.nch + ch] = bad ? 1u : 0u;
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
@@ -143,29 +111,121 @@ __device__ void kv_stats(const T* __restrict__ K, const T* __restrict__ V, const
     ws.kmin[o] = a;
     ws.kmax[o] = b;
   }
+}
+
+// V^T codes of one V item (b, kv-head, 64-key tile, 128-channel slice cz).
+// V enters at its own scale: its E8M0 block exponents carry the range, so its
+// codes need no statistics and are written here, in the statistics pass.  The
+// slice is staged in LDS (16-byte loads, zeros for keys past Nkv), then thread
+// (channel c, key half) takes one 32-key block: the smallest exponent that
+// fits its maximum under 6, E2M1 codes stored with the eight 4-key runs in
+// the order 0,2,4,6,1,3,5,7.  Also: the item's max |V| over the statistics
+// keys and its non-finite flag; with the weighted test and cz = 0, every
+// key's value norm (squares in FP32 in channel order inside a thread, over
+// the threads of the key by an xor butterfly), the tile's largest norm and
+// the FP64 sum of its statistics keys' norms, keys ascending.
+template <typename T>
+__device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws, const Fp4Ptrs& f,
+                       int bh, int t, int cz, T* tile, float* red, float* knu) {
+  constexpr int CH = 128, PADH = 8;
+  const int D = g.D, c0 = cz * CH, nch = min(CH, D - c0), ld = nch + PADH;
+  const int b = bh / g.Hkv, hk = bh % g.Hkv;
+  const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
+  const int k1 = max(k0, min(stat_khi(g), kend));
+  const int per_row = nch / 8;
+#pragma unroll 4
+  for (int i = threadIdx.x; i < kTile * per_row; i += blockDim.x) {
+    const int kk = i / per_row, c = (i % per_row) * 8;
+    uint4 r = {0u, 0u, 0u, 0u};
+    if (k0 + kk < kend) r = *reinterpret_cast<const uint4*>(V + kv_elem(g, b, hk, k0 + kk) + c0 + c);
+    *reinterpret_cast<uint4*>(&tile[kk * ld + c]) = r;
+  }
+  __syncthreads();
+  const int c = threadIdx.x % nch, half = threadIdx.x / nch;
+  bool bad = false;
+  float as = 0.0f;
+  if (half < 2) {
+    float x[32];
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = to_f32<T>(tile[(half * 32 + i) * ld + c]);
+      bad |= !__builtin_isfinite(x[i]);
+      a = fmaxf(a, fabsf(x[i]));
+      if (k0 + half * 32 + i < k1) as = fmaxf(as, fabsf(x[i]));
+    }
+    const int e = e8m0_exponent(a);
+    const float sc = pow2_scale(e);
+    constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+    unsigned out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      unsigned w = 0;
+      const int ra = perm[2 * j] * 4, rb = perm[2 * j + 1] * 4;
+      w = cvt_fp4x2(w, x[ra + 0], x[ra + 1], sc, 0);
+      w = cvt_fp4x2(w, x[ra + 2], x[ra + 3], sc, 1);
+      w = cvt_fp4x2(w, x[rb + 0], x[rb + 1], sc, 2);
+      w = cvt_fp4x2(w, x[rb + 2], x[rb + 3], sc, 3);
+      out[j] = w;
+    }
+    const int ch = c0 + c;
+    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(D);
+    *reinterpret_cast<uint4*>(blob + 34 * D + ch * 32 + half * 16) =
+        uint4{out[0], out[1], out[2], out[3]};
+    blob[66 * D + ((ch % 32) * 2 + half) * (D / 32) + ch / 32] = (uint8_t)(e + 127);
+  }
+  bad = __syncthreads_or(bad);
+  const float m = block_max(as, red);
+  const size_t item = ((size_t)bh * g.NT + t) * ws.nvz + cz;
   if (threadIdx.x == 0) {
-    float m = red[0];
-    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) m = fmaxf(m, red[w]);
-    ws.vamax[(size_t)bh * ws.nch + ch] = m;
-    if (g.vweight) {
-      double c = 0.0;
-      for (int i = 0; i < 16; ++i) c += tvs[i];  // the chunk's tiles, ascending
-      ws.vnsum[(size_t)bh * ws.nch + ch] = c;
+    ws.vamax[item] = m;
+    ws.flags[vflag0(g, ws) + item] = bad ? 1u : 0u;
+  }
+  if (g.vweight && cz == 0) {
+    // parts threads per key, each D / parts consecutive channels
+    const int parts = blockDim.x / kTile, cpp = D / parts;
+    const int kk = threadIdx.x / parts, part = threadIdx.x % parts;
+    float q = 0.0f;
+    if (k0 + kk < kend) {
+      const T* row = V + kv_elem(g, b, hk, k0 + kk) + part * cpp;
+      for (int c8 = 0; c8 < cpp; c8 += 8) {
+        const uint4 r = *reinterpret_cast<const uint4*>(row + c8);
+        const T* e = reinterpret_cast<const T*>(&r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float y = to_f32<T>(e[i]);
+          q = fmaf(y, y, q);
+        }
+      }
+    }
+    for (int o = 1; o < parts; o <<= 1) q += __shfl_xor(q, o);
+    if (part == 0) knu[kk] = sqrtf(q);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mx = 0.0f;
+      double sn = 0.0;
+      for (int i = 0; i < kTile; ++i) {
+        mx = fmaxf(mx, knu[i]);
+        if (k0 + i < k1) sn += (double)knu[i];
+      }
+      ws.vnt[(size_t)bh * g.NT + t] = mx;
+      ws.vnst[(size_t)bh * g.NT + t] = sn;
     }
   }
 }
 
-// max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq), block D.
-// (block of 2*D threads: thread (half, d) takes rows r0 + half, r0 + half + 2, ...)
+// max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq); a block of nh*D
+// threads (nh = 2, or 1 at D = 512): thread (half, d) takes rows r0 + half,
+// r0 + half + nh, ...
 template <typename T>
-__device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws, int flag, int t,
-                        int bh, float* red) {
-  const int d = threadIdx.x % g.D, half = threadIdx.x / g.D;
+__device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws, int t, int bh,
+                        float* red) {
+  const int d = threadIdx.x % g.D, half = threadIdx.x / g.D, nh = blockDim.x / g.D;
   const size_t base = ((size_t)bh * g.Nq) * g.D;
   const int r0 = t * 64, r1 = min(g.Nq, r0 + 64);
   float a = 0.0f;
   bool bad = false;
-  for (int r = r0 + half; r < r1; r += 2) {
+  for (int r = r0 + half; r < r1; r += nh) {
     float x = to_f32<T>(Q[base + (size_t)r * g.D + d]);
     bad |= !__builtin_isfinite(x);
     a = fmaxf(a, fabsf(x));
@@ -174,7 +234,7 @@ __device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& w
   float m = block_max(a, red);
   if (threadIdx.x == 0) {
     ws.qamax[(size_t)bh * ws.nqt + t] = m;
-    ws.flags[flag] = bad ? 1u : 0u;
+    ws.flags[qflag0(g, ws) + (size_t)bh * ws.nqt + t] = bad ? 1u : 0u;
   }
 }
 
@@ -190,15 +250,16 @@ __device__ void head_scale(float amax, float* gs, float* inv) {
 // a batch in flight (the block is latency-bound: few blocks, short chains).
 constexpr int kFinBatch = 32;
 
-// Per (b, kv-head): key mean, |K - kbar| max, V max, their head scales, and
-// the tied Q scales of the group's query heads; with the weighted hot test
-// the mean value norm nu_bar (FP64 sum of the chunk sums, ascending, over the
-// statistics keys; a frozen cache keeps its own) and the weight
-// w_t = max(1, nu_t / nu_bar) of every tile read (1 when nu_bar is 0).  Every
-// block also folds the statistics blocks' non-finite flags and block 0 writes
-// the status word.  grid (B*Hkv), block 2D.
+// Per (b, kv-head): key mean, |K - kbar| max, V max, the K head scale (V's
+// is 1), and the tied Q scales of the group's query heads; with the weighted
+// hot test the mean value norm nu_bar (FP64: each thread sums a contiguous
+// run of tiles ascending, then the runs are added in thread order; a frozen
+// cache keeps its own) and the weight w_t = max(1, nu_t / nu_bar) of every
+// tile read (1 when nu_bar is 0).  Each block folds the non-finite flags of
+// its own K chunks, V items and Q tiles and ORs the result into the status
+// word (which the statistics pass cleared).  grid (B*Hkv), block 2D.
 __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* xch,
-                         float* red, float* nbs) {
+                         float* red, float* nbs, double* part) {
   const int d = threadIdx.x, nthr = blockDim.x, D = g.D;
   const bool own = d < D;  // threads D .. 2D-1 fold min and max, and join the block reductions
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
@@ -243,31 +304,50 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
     if (!g.frozen) f.kbar[(size_t)bh * D + d] = kb;
     if (nk > 0) dev = fmaxf(mx - kb, kb - mn);
   }
-  // non-finite inputs anywhere (every block reads all flags; block 0 writes);
-  // only the K/V flags of chunks [ch0, ch1) were written
+  // this head's non-finite flags: its K chunks [ch0, ch1), its V items of
+  // tiles [qt0, qt1) and the Q tiles of its query heads; with them max |V|
   unsigned badf = 0u;
-  const int nkvf = ws.nflags - (g.Nq > 0 ? g.B * g.Hq * ws.nqt : 0);
-#pragma unroll 8
-  for (int i = d; i < ws.nflags; i += nthr)
-    if (i >= nkvf || (i % ws.nch >= ws.ch0 && i % ws.nch < ws.ch1)) badf |= ws.flags[i];
-  badf = __syncthreads_or(badf != 0u);
-  if (bh == 0 && d == 0) *f.status = badf ? 1u : 0u;
-  const float amax_k = block_max(dev, red);
+  for (int c = ws.ch0 + d; c < ws.ch1; c += nthr) badf |= ws.flags[(size_t)bh * ws.nch + c];
   float va = 0.0f;
-  for (int c = ws.ch0 + d; c < ws.ch1; c += blockDim.x)
-    va = fmaxf(va, ws.vamax[(size_t)bh * ws.nch + c]);
+  {
+    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
+    const int n = (g.qt1 - g.qt0) * ws.nvz;
+#pragma unroll 8
+    for (int i = d; i < n; i += nthr) {
+      va = fmaxf(va, ws.vamax[i0 + i]);
+      badf |= ws.flags[vflag0(g, ws) + i0 + i];
+    }
+  }
+  {
+    const int b = bh / g.Hkv, hk = bh % g.Hkv;
+    const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G) * ws.nqt;
+    for (int i = d; i < g.G * ws.nqt; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
+  }
+  badf = __syncthreads_or(badf != 0u);
+  if (d == 0 && badf) atomicOr(f.status, 1u);
+  const float amax_k = block_max(dev, red);
   const float amax_v = block_max(va, red);
-  float gk, ik, gv, iv;
+  float gk, ik;
   head_scale(amax_k, &gk, &ik);
-  head_scale(amax_v, &gv, &iv);
+  // V is coded at its own scale (per-head scale 1)
+  const float gv = 1.0f, iv = 1.0f;
   // frozen statistics: the K/V scales stay the cache's; Q's tie to its g_K
   if (g.frozen) gk = f.kv_head[(size_t)bh * 8 + 1];
   if (g.vweight) {
+    if (!g.frozen) {
+      // thread d sums tiles [qt0 + d * run, qt0 + (d + 1) * run), ascending
+      const int n = g.qt1 - g.qt0, run = (n + nthr - 1) / nthr;
+      double sv = 0.0;
+      for (int i = d * run; i < min(n, (d + 1) * run); ++i)
+        sv += ws.vnst[(size_t)bh * g.NT + g.qt0 + i];
+      part[d] = sv;
+    }
+    __syncthreads();
     if (d == 0) {
       float nb = f.kv_head[(size_t)bh * 8 + 6];
       if (!g.frozen) {
         double sv = 0.0;
-        for (int c = ws.ch0; c < ws.ch1; ++c) sv += ws.vnsum[(size_t)bh * ws.nch + c];
+        for (int i = 0; i < nthr; ++i) sv += part[i];
         const int nk = stat_khi(g) - stat_t0(g) * kTile;
         nb = nk > 0 ? (float)(sv / (double)nk) : 0.0f;
       }
@@ -354,20 +434,37 @@ __device__ __forceinline__ int lsq_exponent(const float (&x)[8], int e0) {
   return best;
 }
 
-// Quantise rows along channels (Q, or K - kbar).  Each thread owns 8
-// consecutive channels; 4 threads form one 32-channel block.  Rows in
-// [Nrows, NP) are padding and get zero codes.  For Q it also writes the frame
-// constant c_r = sl * q.kbar (FP32).  grid (ceil(NP*D/8 / 256), B*H).
+// Rows of one sub-block of 256 threads (thread: 8 consecutive channels of a
+// row): the row of this thread, and its 16 input bytes (zeros for padding
+// rows [Nrows, NP) and past the sub-blocks of the head).
 template <typename T, bool IS_Q>
-__device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs& f, int bx,
-                           int bh) {
+__device__ __forceinline__ uint4 load_row(const T* __restrict__ X, const Geom& g, int sub,
+                                          int bh, int* row_out) {
+  const int H = IS_Q ? g.Hq : g.Hkv;
+  const int Nrows = IS_Q ? g.Nq : g.Nkv;
+  const int tpr = g.D / 8;
+  const int gid = sub * 256 + threadIdx.x;
+  const int row = gid / tpr, c8 = (gid % tpr) * 8;
+  *row_out = row;
+  if (row >= Nrows) return uint4{0u, 0u, 0u, 0u};
+  const int b = bh / H, h = bh % H;
+  const int hk = IS_Q ? h / g.G : h;
+  const T* src = X + (IS_Q ? ((size_t)bh * Nrows + row) * g.D : kv_elem(g, b, hk, row)) + c8;
+  return *reinterpret_cast<const uint4*>(src);
+}
+
+// Quantise rows along channels (Q, or K - kbar).  Each thread owns 8
+// consecutive channels of row `row` (its input in raw); 4 threads form one
+// 32-channel block.  Rows in [Nrows, NP) are padding and get zero codes.  For
+// Q it also writes the frame constant c_r = sl * q.kbar (FP32).
+template <typename T, bool IS_Q>
+__device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int row, int bh) {
   const int H = IS_Q ? g.Hq : g.Hkv;
   const int Nrows = IS_Q ? g.Nq : g.Nkv;
   const int NP = IS_Q ? g.NqP : g.NkvP;
   const int tpr = g.D / 8;                     // threads per row
-  const int gid = bx * blockDim.x + threadIdx.x;
-  const int row = gid / tpr, c8 = (gid % tpr) * 8;
-  if (row >= NP) return;                       // whole 4-thread blocks exit together
+  const int c8 = (threadIdx.x % tpr) * 8;
+  if (row >= NP) return;                       // whole rows exit together
   const int b = bh / H, h = bh % H;
   const int hk = IS_Q ? h / g.G : h;
   const size_t bk = (size_t)b * g.Hkv + hk;
@@ -378,8 +475,6 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
   float x[8];
   float cdot = 0.0f;
   if (row < Nrows) {
-    const T* src = X + (IS_Q ? ((size_t)bh * Nrows + row) * g.D : kv_elem(g, b, hk, row)) + c8;
-    const uint4 raw = *reinterpret_cast<const uint4*>(src);
     const T* e = reinterpret_cast<const T*>(&raw);
     for (int i = 0; i < 8; ++i) {
       float v = to_f32<T>(e[i]);
@@ -448,112 +543,87 @@ __device__ void quant_rows(const T* __restrict__ X, const Geom& g, const Fp4Ptrs
   }
 }
 
-// Quantise V along keys into the transposed layout.  One block per (64-key
-// tile, b*kv-head, 128-channel chunk): the tile is staged in LDS, then thread
-// (channel, half) quantises one 32-key block.  Codes of a block are stored
-// with its eight 4-key runs in the order 0,2,4,6,1,3,5,7.
+// K and Q statistics in one launch: blocks [0, NKB) take (kv-head, 16-tile
+// chunk) of K, the rest (q-head, 64-row tile).  Block 0 clears the status word
+// first (the finalize blocks OR into it).  block min(2*D, 512) threads,
+// dynamic LDS 16*D*(8+4+4) bytes (the K chunk sums).
 template <typename T>
-__device__ void quant_vt(const T* __restrict__ V, const Geom& g, const Fp4Ptrs& f, int t, int bh,
-                         int cz) {
-  constexpr int CH = 128, PADH = 8;
-  __shared__ T tile[kTile][CH + PADH];
-  const int c0 = cz * CH;
-  const int nch = min(CH, g.D - c0);
-  const float inv = f.kv_head[(size_t)bh * 8 + 5];
-  const int k0 = t * kTile;
-  // stage the raw tile, 8 values per 16-byte load; zeros for padding keys
-  const int per_row = nch / 8;
-#pragma unroll 4
-  for (int i = threadIdx.x; i < kTile * per_row; i += blockDim.x) {
-    const int kk = i / per_row, c = (i % per_row) * 8;
-    const int key = k0 + kk;
-    uint4 r = {0u, 0u, 0u, 0u};
-    if (key < g.Nkv)
-      r = *reinterpret_cast<const uint4*>(V + kv_elem(g, bh / g.Hkv, bh % g.Hkv, key) + c0 + c);
-    *reinterpret_cast<uint4*>(&tile[kk][c]) = r;
-  }
-  __syncthreads();
-  const int c = threadIdx.x % CH, half = threadIdx.x / CH;
-  if (c >= nch || half >= 2) return;
-  float x[32];
-  float a = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float n = to_f32<T>(tile[half * 32 + i][c]) * inv;
-    x[i] = fminf(fmaxf(n, -6.0f), 6.0f);
-    a = fmaxf(a, fabsf(x[i]));
-  }
-  const int e = e8m0_exponent(a);
-  const float s = pow2_scale(e);
-  // dword j holds runs perm[2j], perm[2j+1]; run q covers keys 4q..4q+3
-  constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-  unsigned out[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    unsigned w = 0;
-    const int ra = perm[2 * j] * 4, rb = perm[2 * j + 1] * 4;
-    w = cvt_fp4x2(w, x[ra + 0], x[ra + 1], s, 0);
-    w = cvt_fp4x2(w, x[ra + 2], x[ra + 3], s, 1);
-    w = cvt_fp4x2(w, x[rb + 0], x[rb + 1], s, 2);
-    w = cvt_fp4x2(w, x[rb + 2], x[rb + 3], s, 3);
-    out[j] = w;
-  }
-  const int ch = c0 + c;
-  uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(g.D);
-  uint4 o4 = {out[0], out[1], out[2], out[3]};
-  *reinterpret_cast<uint4*>(blob + 34 * g.D + ch * 32 + half * 16) = o4;
-  blob[66 * g.D + ((ch % 32) * 2 + half) * (g.D / 32) + ch / 32] = (uint8_t)(e + 127);
-}
-
-// Statistics in one launch: blocks [0, NKB) take (kv-head, 16-tile chunk),
-// the rest (q-head, 64-row tile).  block 2*D threads, dynamic LDS
-// 16*D*(8+4+4) bytes.
-template <typename T>
-__global__ void k_stats(const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-                        Geom g, QuantWs ws, int nkb) {
-  extern __shared__ double sh[];  // [16][D] tile sums, then [16][D] min and max as float
+__global__ __launch_bounds__(512) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
+                                               Geom g, QuantWs ws, Fp4Ptrs f, int nkb) {
+  extern __shared__ double sh[];
   __shared__ float red[16];
-  __shared__ double tvs[16];      // the tiles' value-norm sums
-  if ((int)blockIdx.x < nkb) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+  const int bx = blockIdx.x;
+  if (bx < nkb) {
     const int nc = ws.ch1 - ws.ch0;  // the chunks of the tiles read
-    kv_stats<T>(K, V, g, ws, ws.ch0 + blockIdx.x % nc, blockIdx.x / nc, sh, red, tvs);
+    k_chunk_stats<T>(K, g, ws, ws.ch0 + bx % nc, bx / nc, sh);
   } else {
-    const int qb = blockIdx.x - nkb;
-    // Q flags follow every (kv-head, chunk) slot, written or not
-    const int qflag0 = ws.nflags - g.B * g.Hq * ws.nqt;
-    q_stats<T>(Q, g, ws, qflag0 + qb, qb % ws.nqt, qb / ws.nqt, red);
+    const int qb = bx - nkb;
+    q_stats<T>(Q, g, ws, qb % ws.nqt, qb / ws.nqt, red);
   }
 }
 
-// One block of 2*D threads per (b, kv-head).
-__global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f) {
+// The V items of the tiles read, one block each (per kv-head, tile,
+// 128-channel slice), 2 * min(D, 128) threads.  Runs after k_stats, whose
+// block 0 cleared the status word.
+template <typename T>
+__global__ __launch_bounds__(256) void k_vcode(const T* __restrict__ V, Geom g, QuantWs ws,
+                                               Fp4Ptrs f) {
+  __shared__ T tile[kTile * (128 + 8)];
+  __shared__ float red[16];
+  __shared__ float knu[kTile];  // a tile's key norms
+  const int per_head = (g.qt1 - g.qt0) * ws.nvz;
+  const int r = blockIdx.x % per_head;
+  v_item<T>(V, g, ws, f, blockIdx.x / per_head, g.qt0 + r / ws.nvz, r % ws.nvz, tile, red, knu);
+}
+
+// One block of 2*D threads per (b, kv-head).  clear: the statistics pass did
+// not run (nothing to check), so block 0 clears the status word itself.
+__global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f, int clear) {
   extern __shared__ float xch[];  // [2][D]: min and max of each channel
   __shared__ float red[16];
-  __shared__ float nbs;  // nu_bar
-  finalize(g, ws, f, blockIdx.x, xch, red, &nbs);
+  __shared__ float nbs;           // nu_bar
+  __shared__ double part[1024];   // the threads' runs of tile norm sums
+  if (clear && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+  finalize(g, ws, f, blockIdx.x, xch, red, &nbs, part);
 }
 
 // Quantisation in one launch: blocks for Q rows first, then per (b, kv-head),
-// last first, per 64-key tile its kpt K-row blocks (16 rows of 128 channels,
-// or the same 2048 elements at other D) and its nvb_z V^T blocks -- the
-// reverse of the order the statistics pass read them.
+// last first, per 64-key tile its K rows -- the reverse of the order the
+// statistics pass read them (V^T was coded there).  A block takes up to 4
+// sub-blocks of 256 threads (2048 elements each: 16 rows of 128 channels, or
+// the same at other D), their loads issued together before any is used.
+constexpr int kSubs = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T* __restrict__ K,
-                                               const T* __restrict__ V, Geom g, Fp4Ptrs f,
-                                               int kpt, int nvb_z, int qpb, int nq) {
+                                               Geom g, Fp4Ptrs f, int kpt, int qpb, int nq) {
   int b = blockIdx.x;
+  uint4 raw[kSubs];
+  int row[kSubs];
   if (b < nq) {
-    quant_rows<T, true>(Q, g, f, b % qpb, b / qpb);
+    const int bpq = (qpb + kSubs - 1) / kSubs;  // blocks per q-head
+    const int bh = b / bpq, s0 = (b % bpq) * kSubs, ns = min(kSubs, qpb - s0);
+#pragma unroll
+    for (int i = 0; i < kSubs; ++i)
+      raw[i] = i < ns ? load_row<T, true>(Q, g, s0 + i, bh, &row[i]) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < kSubs; ++i)
+      if (i < ns) quant_rows<T, true>(raw[i], g, f, row[i], bh);
     return;
   }
   b -= nq;
-  const int per_tile = kpt + nvb_z, per_head = (g.qt1 - g.qt0) * per_tile;
+  const int bpt = (kpt + kSubs - 1) / kSubs;  // blocks per tile
+  const int per_head = (g.qt1 - g.qt0) * bpt;
   const int bh = g.B * g.Hkv - 1 - b / per_head;
-  const int r = b % per_head, t = g.qt0 + r / per_tile, j = r % per_tile;
-  if (j < kpt)
-    quant_rows<T, false>(K, g, f, t * kpt + j, bh);
-  else
-    quant_vt<T>(V, g, f, t, bh, j - kpt);
+  const int r = b % per_head, t = g.qt0 + r / bpt, s0 = (r % bpt) * kSubs;
+  const int ns = min(kSubs, kpt - s0);
+#pragma unroll
+  for (int i = 0; i < kSubs; ++i)
+    raw[i] = i < ns ? load_row<T, false>(K, g, t * kpt + s0 + i, bh, &row[i])
+                    : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < kSubs; ++i)
+    if (i < ns) quant_rows<T, false>(raw[i], g, f, row[i], bh);
 }
 
 template <typename T>
@@ -569,20 +639,24 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
     stats_attr = true;
   }
   const int nkb = g.Nkv > 0 ? (ws.ch1 - ws.ch0) * nkvh : 0;
+  const int nvb = g.Nkv > 0 ? (g.qt1 - g.qt0) * ws.nvz * nkvh : 0;
   const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
-    hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(2 * g.D), stats_lds, s, q, k, v, g, ws,
-                       nkb);
-  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 2 * g.D * sizeof(float), s, g, ws, f);
-  // K rows: a 64-key tile of D channels is kTile * D / 8 threads, D / 32 blocks
+    hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(min(2 * g.D, 512)), stats_lds, s, q, k,
+                       g, ws, f, nkb);
+  if (nvb > 0)
+    hipLaunchKernelGGL(k_vcode<T>, dim3(nvb), dim3(2 * min(g.D, 128)), 0, s, v, g, ws, f);
+  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 2 * g.D * sizeof(float), s, g, ws, f,
+                     nkb + nqb > 0 ? 0 : 1);
+  // K rows: a 64-key tile of D channels is kTile * D / 8 threads, D / 32
+  // sub-blocks of 256; Q: qpb sub-blocks per head
   const int kpt = g.D / 32;
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
-  const int nvb_z = (g.D + 127) / 128;
-  const long nq = (long)qpb * g.B * g.Hq;
-  const long nblk = nq + (long)(g.qt1 - g.qt0) * nkvh * (kpt + nvb_z);
+  const long nq = (long)((qpb + kSubs - 1) / kSubs) * g.B * g.Hq;
+  const long nblk = nq + (long)(g.qt1 - g.qt0) * nkvh * ((kpt + kSubs - 1) / kSubs);
   if (nblk > 0)
-    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, v, g, f, kpt,
-                       nvb_z, qpb, (int)nq);
+    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, g, f, kpt, qpb,
+                       (int)nq);
   return hipGetLastError();
 }
 

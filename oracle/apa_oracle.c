@@ -426,9 +426,13 @@ void orc_quant_rows2(const float* X, int n, int D, float inv, int fmt, uint8_t* 
 
 /* Quantise V along the key axis (the transposed layout the P.V product
  * contracts over).  V: [Nkv][D].  Keys are padded with zeros up to NkvP, a
- * multiple of the tile.  codes: [D][NkvP/2]; scales: [D][NkvP/Bs]. */
-void orc_quant_vt(const float* V, int Nkv, int NkvP, int D, float inv, int fmt, uint8_t* codes,
-                  uint8_t* scales) {
+ * multiple of the tile.  codes: [D][NkvP/2]; scales: [D][NkvP/Bs].  raw: the
+ * values enter at their own scale, neither normalised nor clamped (MX: the
+ * E8M0 block exponents span the whole range of the inputs, so V's per-head
+ * scale is 1; with a scale that is not a power of two it would only move the
+ * mantissas of the normalised values); otherwise normalised by inv. */
+void orc_quant_vt(const float* V, int Nkv, int NkvP, int D, float inv, int fmt, int raw,
+                  uint8_t* codes, uint8_t* scales) {
   int Bs = fmt == ORC_NV ? 16 : 32;
   float buf[32];
   uint8_t cb[32];
@@ -436,7 +440,8 @@ void orc_quant_vt(const float* V, int Nkv, int NkvP, int D, float inv, int fmt, 
     for (int k0 = 0; k0 < NkvP; k0 += Bs) {
       for (int i = 0; i < Bs; ++i) {
         int k = k0 + i;
-        buf[i] = k < Nkv ? normalise(V[(size_t)k * D + d], inv, fmt) : 0.0f;
+        float v = k < Nkv ? V[(size_t)k * D + d] : 0.0f;
+        buf[i] = raw ? v : normalise(v, inv, fmt);
       }
       quant_block(buf, Bs, fmt, cb, &scales[(size_t)d * (NkvP / Bs) + k0 / Bs]);
       for (int i = 0; i < Bs; i += 2)

@@ -99,7 +99,8 @@ def lib():
         L.orc_quant_rows.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, C.c_int, _P, _P]
         L.orc_quant_rows_lsq.argtypes = [_P, C.c_int, C.c_int, _P, C.c_float, _P, _P]
         L.orc_quant_rows2.argtypes = [_P, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P, _P, _P]
-        L.orc_quant_vt.argtypes = [_P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int, _P, _P]
+        L.orc_quant_vt.argtypes = [_P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_int, C.c_int,
+                                   _P, _P]
         L.orc_sl.argtypes = [_P]
         L.orc_sl.restype = C.c_float
         L.orc_visit_order.argtypes = [_P, C.c_int, _P]
@@ -279,7 +280,12 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
     sliding window the K/V statistics (key mean, per-head scales) and codes
     cover the key tiles from first_tile on, the ones some row sees.  With
     stat_keys the statistics cover only the keys before it (values of later
-    keys beyond the frozen range clamp at the format's largest value).
+    keys beyond the frozen range clamp at the format's largest value).  In MX
+    mode V enters at its own scale (g_v = inv_v = 1; amax_v is still
+    recorded): its E8M0 block exponents carry the range that NVFP4's narrow
+    UE4M3 block scales leave to the per-head scale (the section "Pass 1: FP4
+    everywhere, with a hot test" of "APA: sloppy attention, exact where it
+    counts" gives one FP32 scale per head for that format).
     """
     L = lib()
     cp = p.c()
@@ -328,8 +334,12 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             Vs = np.ascontiguousarray(V[b, hk, k0:ks_hi])
             av = L.orc_absmax(_ptr(Vs), Vs.size)
             out["amax_v"][b, hk] = av
-            L.orc_head_scale(C.c_float(av), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
-            out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]
+            if p.fmt == MX:
+                # V at its own scale: per-head scale 1 (see orc_quant_vt)
+                out["g_v"][b, hk], out["inv_v"][b, hk] = 1.0, 1.0
+            else:
+                L.orc_head_scale(C.c_float(av), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
+                out["g_v"][b, hk], out["inv_v"][b, hk] = f[0], f[1]
             kc = np.zeros((nk, D // 2), np.uint8)
             ks = np.zeros((nk, D // bs), np.uint8)
             if p.k_lsq:
@@ -342,6 +352,7 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             vc = np.zeros((D, (NkvP - k0) // 2), np.uint8)
             vs = np.zeros((D, (NkvP - k0) // bs), np.uint8)
             L.orc_quant_vt(_ptr(Vh), nk, NkvP - k0, D, C.c_float(out["inv_v"][b, hk]), p.fmt,
+                           1 if p.fmt == MX else 0,
                            _ptr(vc), _ptr(vs))
             out["vc"][b, hk, :, k0 // 2:], out["vs"][b, hk, :, k0 // bs:] = vc, vs
             out["vw"][b, hk], out["nu_bar"][b, hk] = tile_weights(p, V[b, hk])

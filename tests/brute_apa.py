@@ -103,10 +103,11 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
         kd = (quantise_blocks(kn) if "K" in quant else
               (Kh.astype(np.float64) - kbar.astype(np.float64)) * np.float64(inv_k))
         Vh = V[hk].astype(np.float32)
-        amax_v = np.abs(Vh[k0:]).max()
-        g_v = f32(amax_v / 6.0) if amax_v > 0 else np.float32(1)
-        inv_v = f32(6.0 / amax_v) if amax_v > 0 else np.float32(1)
-        vn = np.clip((Vh * inv_v).astype(np.float32), -6, 6)
+        # MX: V at its own scale (per-head scale 1, no clamp); the block
+        # exponents take the range
+        g_v = np.float32(1)
+        inv_v = np.float32(1)
+        vn = Vh
         Nkv = Vh.shape[0]
         NkvP = -(-Nkv // 64) * 64
         vpad = np.zeros((NkvP, D), np.float32)

@@ -33,10 +33,11 @@ def test_bf16_v_beyond_fp16_range_exact(D):
 
 @pytest.mark.parametrize("D", [128, 512])
 def test_bf16_v_beyond_fp16_range_apa(D):
-    """The whole APA path with the same scaled V: FP4 codes are those of the
-    unscaled V (the per-head scale absorbs the factor), the cold state is
-    2^20 times larger, pass 2 scales its V into the fp16 range, and the output
-    over 2^20 meets the usual bars against the oracle on the unscaled V."""
+    """The whole APA path with the same scaled V: V's FP4 codes are those of
+    the unscaled V and its block exponents 20 larger (V is coded at its own
+    scale), the cold state is 2^20 times larger, pass 2 scales its V into the
+    fp16 range, and the output over 2^20 meets the usual bars against the
+    oracle on the unscaled V."""
     w = small_workload(1, 4, 1, 96, 4096, D, dtype="bf16", mode="gauss", seed=52)
     Q, K, V = make_inputs(w)
     eps = 0.05
@@ -45,7 +46,9 @@ def test_bf16_v_beyond_fp16_range_apa(D):
     r = O.run(po, Q, K, V, prep)
     g = run_gpu(problem_for(w), Q, K, V * BIG, eps, dtype="bf16")
     assert g["fp4"]["status"] == 0
-    assert np.array_equal(g["fp4"]["vc"], prep["vc"]) and np.array_equal(g["fp4"]["vs"], prep["vs"])
+    assert np.array_equal(g["fp4"]["vc"], prep["vc"])
+    vs = prep["vs"].astype(np.int32)
+    assert np.array_equal(g["fp4"]["vs"], np.where(vs == 0, 0, vs + 20))
     check_mask(g["hot"], r)
     check_output(g["out"] / BIG, r["O"], dtype="bf16")
     # the hot part ran in pass 2 (some tiles hot, some cold)
