@@ -122,8 +122,9 @@ __device__ void k_chunk_stats(const T* __restrict__ K, const Geom& g, const Quan
 // the order 0,2,4,6,1,3,5,7.  Also: the item's max |V| over the statistics
 // keys and its non-finite flag; with the weighted test and cz = 0, every
 // key's value norm (squares in FP32 in channel order inside a thread, over
-// the threads of the key by an xor butterfly), the tile's largest norm and
-// the FP64 sum of its statistics keys' norms, keys ascending.
+// the threads of the key by an xor butterfly; from the staged slice when it
+// holds the whole row, D <= 128), the tile's largest norm and the FP64 sum of
+// its statistics keys' norms, keys ascending.
 template <typename T>
 __device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws, const Fp4Ptrs& f,
                        int bh, int t, int cz, T* tile, float* red, float* knu) {
@@ -186,7 +187,19 @@ __device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws
     const int parts = blockDim.x / kTile, cpp = D / parts;
     const int kk = threadIdx.x / parts, part = threadIdx.x % parts;
     float q = 0.0f;
-    if (k0 + kk < kend) {
+    if (nch == D) {
+      // the whole row is in the staged slice (zeros past Nkv)
+      const T* row = tile + kk * ld + part * cpp;
+      for (int c8 = 0; c8 < cpp; c8 += 8) {
+        const uint4 r = *reinterpret_cast<const uint4*>(row + c8);
+        const T* e = reinterpret_cast<const T*>(&r);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float y = to_f32<T>(e[i]);
+          q = fmaf(y, y, q);
+        }
+      }
+    } else if (k0 + kk < kend) {
       const T* row = V + kv_elem(g, b, hk, k0 + kk) + part * cpp;
       for (int c8 = 0; c8 < cpp; c8 += 8) {
         const uint4 r = *reinterpret_cast<const uint4*>(row + c8);
