@@ -44,7 +44,10 @@
  * window against the brute force and a masked softmax; the value-norm
  * weighted hot test (weights computed by the Python side of the oracle)
  * against the brute force, the closed forms of equal value norms and of one
- * planted tile, and the output-norm bound it gives.  Parity unpinned: the
+ * planted tile, and the output-norm bound it gives; NVFP4 mode (blocks of 16
+ * with UE4M3 scales, P in 16-key groups) bitwise against the brute force's own
+ * NV quantisation on inputs whose P scales stay in UE4M3's normal range, and
+ * its 2^-6 scale floor through the sink bug.  Parity unpinned: the
  * pages' measured numbers (they come from activation dumps that are not
  * available), listed as such in the design notes.
  */

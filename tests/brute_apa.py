@@ -78,7 +78,51 @@ def quantise_blocks(x: np.ndarray, bs: int = 32):
 QUANT_ALL = "QKVP"
 
 
-def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0: int = 0):
+def _ue4m3_values() -> np.ndarray:
+    """Every finite unsigned E4M3 value, ascending (encoding order): exponent
+    bias 7, 3 mantissa bits, subnormals below 2^-6, the top encoding NaN."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:
+                continue
+            vals.append(m / 8 * 2.0 ** -6 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+UE4M3 = _ue4m3_values()
+
+
+def ue4m3_nearest(a) -> np.ndarray:
+    """Nearest UE4M3 value (ties to the even encoding), saturating at 448."""
+    a = np.minimum(np.asarray(a, np.float64), UE4M3[-1])
+    dist = np.abs(a[..., None] - UE4M3)
+    cand = dist == dist.min(axis=-1, keepdims=True)
+    idx = np.arange(len(UE4M3))
+    return UE4M3[np.where(cand, (idx % 2) * 1000 + idx, 10 ** 6).argmin(axis=-1)]
+
+
+def rn_4bits(x) -> np.ndarray:
+    """x > 0 rounded to 4 significant bits, ties to even, with no exponent
+    limit: UE4M3 rounding wherever its normal range holds, and scale
+    invariant (rn(x 2^k) = rn(x) 2^k)."""
+    m, e = np.frexp(np.asarray(x, np.float64))
+    return np.ldexp(np.round(m * 16.0) / 16.0, e)
+
+
+def quantise_blocks_nv(x: np.ndarray, bs: int = 16):
+    """NVFP4 blocks of 16: scale = nearest UE4M3 of the block max / 6, codes
+    by nearest-value search of x / scale (a zero scale gives zero values)."""
+    sh = x.shape
+    xb = np.asarray(x, np.float64).reshape(sh[:-1] + (sh[-1] // bs, bs))
+    sc = ue4m3_nearest(np.abs(xb).max(axis=-1) / 6.0)[..., None]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        code = nearest_mag_code(np.where(sc > 0, xb / np.where(sc > 0, sc, 1.0), 0.0))
+    return (np.sign(xb) * MAGS[code] * sc).reshape(sh)
+
+
+def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0: int = 0,
+            fmt: str = "MX"):
     """Per-head scales and dequantised operands (without the per-head factors
     that fold into alpha and g_v).  Q [Hq,Nq,D] etc. for one batch entry.
     q_terms=2 adds the quantised residual of Q (section "Second hunt": a second
@@ -86,8 +130,12 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
     dequantised Q.  An operand missing from `quant` is kept at its exact value
     in normalised units (FP64, no clamp).  The K/V statistics (key mean,
     per-head scales) are taken over keys k0.. (a sliding window's first visible
-    tile; 0 otherwise)."""
+    tile; 0 otherwise).  fmt "NV": blocks of 16 with UE4M3 scales and per-head
+    scales mapping the head maximum to 6 x 448 (V included)."""
     Hq, Nq, D = Q.shape
+    nv = fmt == "NV"
+    X = 2688.0 if nv else 6.0
+    qblocks = quantise_blocks_nv if nv else quantise_blocks
     Hkv = K.shape[0]
     G = Hq // Hkv
     sl = np.float32(np.float32(scale) * LOG2E32)
@@ -97,22 +145,28 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
         kbar = f32(Kh[k0:].astype(np.float64).sum(axis=0) / (Kh.shape[0] - k0))
         kc = (Kh - kbar).astype(np.float32)              # fl32 subtraction
         amax_k = np.abs(kc[k0:]).max() if kc[k0:].size else np.float32(0)
-        g_k = f32(amax_k / 6.0) if amax_k > 0 else np.float32(1)
-        inv_k = f32(6.0 / amax_k) if amax_k > 0 else np.float32(1)
-        kn = np.clip((kc * inv_k).astype(np.float32), -6, 6)
-        kd = (quantise_blocks(kn) if "K" in quant else
+        g_k = f32(amax_k / X) if amax_k > 0 else np.float32(1)
+        inv_k = f32(X / amax_k) if amax_k > 0 else np.float32(1)
+        kn = np.clip((kc * inv_k).astype(np.float32), -X, X)
+        kd = (qblocks(kn) if "K" in quant else
               (Kh.astype(np.float64) - kbar.astype(np.float64)) * np.float64(inv_k))
         Vh = V[hk].astype(np.float32)
-        # MX: V at its own scale (per-head scale 1, no clamp); the block
-        # exponents take the range
-        g_v = np.float32(1)
-        inv_v = np.float32(1)
-        vn = Vh
+        if nv:
+            amax_v = np.abs(Vh[k0:]).max()
+            g_v = f32(amax_v / X) if amax_v > 0 else np.float32(1)
+            inv_v = f32(X / amax_v) if amax_v > 0 else np.float32(1)
+            vn = np.clip((Vh * inv_v).astype(np.float32), -X, X)
+        else:
+            # MX: V at its own scale (per-head scale 1, no clamp); the block
+            # exponents take the range
+            g_v = np.float32(1)
+            inv_v = np.float32(1)
+            vn = Vh
         Nkv = Vh.shape[0]
         NkvP = -(-Nkv // 64) * 64
         vpad = np.zeros((NkvP, D), np.float32)
         vpad[:Nkv] = vn
-        vd = quantise_blocks(vpad.T).T[:Nkv]              # blocks of 32 keys per channel
+        vd = qblocks(vpad.T).T[:Nkv]                      # blocks of keys per channel
         if "V" not in quant:
             vd = Vh.astype(np.float64) * np.float64(inv_v)
         # value-norm weights of the hot test, per 64-key tile
@@ -130,12 +184,12 @@ def prepare(Q, K, V, scale: float, q_terms: int = 1, quant: str = QUANT_ALL, k0:
             j = 0
             if amax_q > 0:
                 prod = float(amax_q) * float(w)
-                j = int(np.ceil(np.log2(prod / 6.0))) - 1
-                while 6.0 * 2.0 ** j < prod:
+                j = int(np.ceil(np.log2(prod / X))) - 1
+                while X * 2.0 ** j < prod:
                     j += 1
             inv_q = np.float32(np.ldexp(np.float64(w), -j))
-            qn = np.clip((Qh * inv_q).astype(np.float32), -6, 6)
-            qd = quantise_blocks(qn)
+            qn = np.clip((Qh * inv_q).astype(np.float32), -X, X)
+            qd = qblocks(qn)
             if "Q" not in quant:
                 qd = Qh.astype(np.float64) * np.float64(inv_q)
             elif q_terms == 2:
@@ -158,7 +212,8 @@ def visit_order(last_row: int, off: int, Nkv: int, causal: bool, tile: int = 64,
 
 
 def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray, off: int,
-                Nkv: int, causal: bool, quant_p: bool = True, window: int = 0, tw=None):
+                Nkv: int, causal: bool, quant_p: bool = True, window: int = 0, tw=None,
+                fmt: str = "MX"):
     """Frame-free pass 1 of one row group.
 
     scores: [R, Nkv] FP4 scores in log2 units (fl32), vd: [Nkv, D] dequantised
@@ -186,7 +241,19 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
         if not np.isfinite(st).any():
             continue  # no row of the group sees a key of this tile: not visited
         ph = np.zeros((R, 64))
-        for q0 in (0, 32):
+        if fmt == "NV":
+            # P in groups of 16 keys, scale = the group maximum / 6 rounded
+            # to 4 significant bits (UE4M3 inside its normal range, which
+            # inputs flat enough for the frame never to leave keep)
+            for q0 in range(0, 64, 16):
+                g = st[:, q0:q0 + 16]
+                cg = g.max(axis=1)
+                live = np.isfinite(cg)
+                sg = rn_4bits(np.exp2(np.where(live, cg, 0.0)) / 6.0)[:, None]
+                with np.errstate(invalid="ignore", over="ignore"):
+                    code = nearest_mag_code(np.exp2(g) / sg)
+                ph[:, q0:q0 + 16] = np.where(np.isfinite(g), MAGS[code] * sg, 0.0)
+        for q0 in ((0, 32) if fmt == "MX" else ()):
             if not quant_p:
                 g = st[:, q0:q0 + 32]
                 with np.errstate(invalid="ignore", over="ignore"):
@@ -221,7 +288,8 @@ def pass1_group(scores: np.ndarray, vd: np.ndarray, eps: float, rows: np.ndarray
 
 
 def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: int = 1,
-              quant: str = QUANT_ALL, window: int = 0, hot_weight: bool = False):
+              quant: str = QUANT_ALL, window: int = 0, hot_weight: bool = False,
+              fmt: str = "MX"):
     """Frame-free pass 1 for every row group of a batch-1 problem.
 
     Returns dict with hot [Hq, NG, NT], l [Hq, Nq], o [Hq, Nq, D] (o already
@@ -234,7 +302,7 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
     nt = -(-Nkv // 64)
     ng = -(-Nq // 16)
     k0 = max(0, off - window + 1) // 64 * 64 if (causal and window > 0) else 0
-    ops = prepare(Q, K, V, scale, q_terms, quant, k0)
+    ops = prepare(Q, K, V, scale, q_terms, quant, k0, fmt)
     hot = np.zeros((Hq, ng, nt), bool)
     margin = np.full((Hq, ng, nt), np.nan)
     lo = np.zeros((Hq, Nq), np.float32)
@@ -249,7 +317,7 @@ def brute_apa(Q, K, V, eps: float, scale: float, causal: bool = True, q_terms: i
             rows = np.arange(16 * g, min(Nq, 16 * g + 16))
             hh, l, o, lam, mg = pass1_group(scores[rows], kv["vd"], eps, rows, off, Nkv, causal,
                                             quant_p="P" in quant, window=window,
-                                            tw=kv["vw"] if hot_weight else None)
+                                            tw=kv["vw"] if hot_weight else None, fmt=fmt)
             hot[h, g] = hh
             margin[h, g] = mg
             lo[h, rows] = l

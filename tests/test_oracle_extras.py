@@ -19,7 +19,8 @@ oracle itself:
 * the value-norm weighted hot test ("Honest limits", mass versus output)
   against the brute force (norms by numpy's norm routine), the closed forms
   of equal norms (every weight 1: the mass test itself) and of one planted
-  tile, the output-norm bound it promises, and its effect on the error.
+  tile, the output-norm bound it promises, and its effect on the error;
+* NVFP4 pass 1 against the brute force's own NV quantisation.
 """
 import math
 
@@ -485,3 +486,46 @@ def test_hot_weight_lowers_the_error_of_large_value_tiles():
         nhot[hw] = int(r["hot"].sum())
     assert nhot[1] > nhot[0]
     assert err[1] < 0.7 * err[0], err
+
+
+# ---------------------------------------------------------------------------
+# NVFP4 pass 1 (the page's own format; an oracle option)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("eps,seed", [(0.03, 81), (0.1, 82)])
+def test_nv_pass1_bitwise_vs_brute_force_on_flat_scores(eps, seed):
+    """NVFP4 mode ("Pass 1: FP4 everywhere, with a hot test": UE4M3 scales per
+    16 elements, per-head scales to 6 x 448, P in 16-key groups) against the
+    brute force's own NV quantisation (UE4M3 values built from the format's
+    bit layout, nearest search; P scales rounded to 4 significant bits with
+    no exponent limit).  Frame-free agreement needs every P group scale
+    inside UE4M3's normal range in the oracle's frame: with scores spanning
+    less than 2.4 log2 units no group maximum falls more than 3.4 below the
+    frame, so the 2^-6 floor never binds (checked below); the floor itself is
+    pinned by the sink-bug test."""
+    Nkv = 3000
+    w = small_workload(1, 2, 1, 96, Nkv, 64, mode="gauss", delta=0.0, seed=seed)
+    Q, K, V = make_inputs(w)
+    scale = 0.03
+    p = O.Params(1, 2, 1, 96, Nkv, 64, scale=scale, eps=eps, fmt=O.NV)
+    r = O.run(p, Q, K, V, pass2=False)
+    b = brute_apa(Q, K, V, eps, scale, fmt="NV")
+    ops = b["ops"][0]
+    off = Nkv - 96
+    for h in range(2):
+        hd = ops["heads"][h]
+        s = (hd["alpha"] * (hd["qd"] @ ops["kd"].T)).astype(np.float32).astype(np.float64)
+        vis = np.arange(Nkv)[None, :] <= np.arange(96)[:, None] + off
+        sv = np.where(vis, s, -np.inf)
+        smax = sv.max()
+        # the smallest maximum of any 16-key group of any row that sees one
+        pad = -(-Nkv // 16) * 16 - Nkv
+        gmax = np.pad(sv, ((0, 0), (0, pad)), constant_values=-np.inf).reshape(96, -1, 16).max(2)
+        gm = gmax[np.isfinite(gmax)].min()
+        assert smax + 1.0 - gm < 3.4, (smax, gm)
+    sc = _frame_scale(r["m1"][0])
+    assert np.array_equal(r["hot"][0].astype(bool), b["hot"])
+    assert 0 < b["hot"].sum() < (~np.isnan(r["margin"][0])).sum()
+    assert np.array_equal((r["l1"][0] * sc).astype(np.float32), b["l"])
+    assert np.array_equal((r["lam"][0] * sc).astype(np.float32), b["lam"])
+    assert np.array_equal((r["o1"][0] * sc[..., None]).astype(np.float32), b["o"])
