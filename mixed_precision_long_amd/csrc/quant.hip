@@ -276,6 +276,32 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   const int d = threadIdx.x, nthr = blockDim.x, D = g.D;
   const bool own = d < D;  // threads D .. 2D-1 fold min and max, and join the block reductions
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
+  const int b = bh / g.Hkv, hk = bh % g.Hkv;
+  // first the loads that do not wait on the key statistics, so that they are
+  // in flight with them: this head's non-finite flags (its K chunks [ch0,
+  // ch1), its V items of tiles [qt0, qt1), the Q tiles of its query heads),
+  // max |V| and each query head's max |Q|
+  unsigned badf = 0u;
+  float va = 0.0f;
+  float qa[8];
+  {
+    for (int c = ws.ch0 + d; c < ws.ch1; c += nthr) badf |= ws.flags[(size_t)bh * ws.nch + c];
+    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
+    const int n = (g.qt1 - g.qt0) * ws.nvz;
+#pragma unroll 8
+    for (int i = d; i < n; i += nthr) {
+      va = fmaxf(va, ws.vamax[i0 + i]);
+      badf |= ws.flags[vflag0(g, ws) + i0 + i];
+    }
+    const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G) * ws.nqt;
+    for (int i = d; i < g.G * ws.nqt; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      qa[i] = 0.0f;
+      if (i < g.G)
+        for (int t = d; t < ws.nqt; t += nthr) qa[i] = fmaxf(qa[i], ws.qamax[q0 + (size_t)i * ws.nqt + t]);
+    }
+  }
   double s = 0.0;
   float mn = __builtin_inff(), mx = -__builtin_inff();
   for (int c0 = ws.ch0; c0 < ws.ch1 && !g.frozen; c0 += kFinBatch) {
@@ -316,25 +342,6 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
     const float kb = nk > 0 ? (float)(s / (double)nk) : 0.0f;
     if (!g.frozen) f.kbar[(size_t)bh * D + d] = kb;
     if (nk > 0) dev = fmaxf(mx - kb, kb - mn);
-  }
-  // this head's non-finite flags: its K chunks [ch0, ch1), its V items of
-  // tiles [qt0, qt1) and the Q tiles of its query heads; with them max |V|
-  unsigned badf = 0u;
-  for (int c = ws.ch0 + d; c < ws.ch1; c += nthr) badf |= ws.flags[(size_t)bh * ws.nch + c];
-  float va = 0.0f;
-  {
-    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
-    const int n = (g.qt1 - g.qt0) * ws.nvz;
-#pragma unroll 8
-    for (int i = d; i < n; i += nthr) {
-      va = fmaxf(va, ws.vamax[i0 + i]);
-      badf |= ws.flags[vflag0(g, ws) + i0 + i];
-    }
-  }
-  {
-    const int b = bh / g.Hkv, hk = bh % g.Hkv;
-    const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G) * ws.nqt;
-    for (int i = d; i < g.G * ws.nqt; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
   }
   badf = __syncthreads_or(badf != 0u);
   if (d == 0 && badf) atomicOr(f.status, 1u);
@@ -380,15 +387,12 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
     kh[7] = 0.0f;
   }
   // Q heads of this group: inv_q = w * 2^-j, w = fl32(sl * g_k), j the
-  // smallest integer with amax_q * w <= 6 * 2^j.
-  const int b = bh / g.Hkv, hk = bh % g.Hkv;
+  // smallest integer with amax_q * w <= 6 * 2^j.  The first eight heads' max
+  // |Q| were loaded above; further heads (groups above 8) load theirs here.
   const float w = g.sl * gk;
-  for (int i = 0; i < g.G; ++i) {
-    const int hq = hk * g.G + i;
-    const size_t bq = (size_t)b * g.Hq + hq;
-    float qa = 0.0f;
-    for (int t = d; t < ws.nqt; t += blockDim.x) qa = fmaxf(qa, ws.qamax[bq * ws.nqt + t]);
-    const float amax_q = block_max(qa, red);
+  auto q_scale = [&](int i, float qv) {
+    const size_t bq = (size_t)b * g.Hq + hk * g.G + i;
+    const float amax_q = block_max(qv, red);
     if (d == 0) {
       int j = 0;
       if (amax_q > 0.0f && w > 0.0f) {
@@ -405,6 +409,15 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
       qh[2] = (float)j;
       qh[3] = 0.0f;
     }
+  };
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < g.G) q_scale(i, qa[i]);
+  for (int i = 8; i < g.G; ++i) {
+    const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G + i) * ws.nqt;
+    float qv = 0.0f;
+    for (int t = d; t < ws.nqt; t += nthr) qv = fmaxf(qv, ws.qamax[q0 + t]);
+    q_scale(i, qv);
   }
 }
 

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 from gpu_util import cosine_rows, problem_for, run_exact_gpu, run_gpu
+from mixed_precision_long_amd import apa
 from mixed_precision_long_amd.inputs import WORKLOADS, make_inputs, small_workload
 from oracle import oracle as O
 
@@ -396,3 +397,25 @@ def test_long3b_exact_sampled_rows():
     Oe, lse = O.exact(po, Q, K, V, rows=rows)
     assert np.abs(go[rows[:, 0], rows[:, 1], rows[:, 2]] - Oe).max() <= EXACT_ABS
     assert np.abs(gl[rows[:, 0], rows[:, 1], rows[:, 2]] - lse).max() <= 1e-3
+
+
+def test_quantize_group_above_eight():
+    """apa_quantize with 12 query heads per KV head (pass 2 does not take such
+    groups; quantise and pass 1 do): codes, scales and the tied Q scales of
+    all twelve heads bitwise, and pass 1's mask against the oracle."""
+    w = small_workload(1, 12, 1, 96, 1024, 64, seed=71)
+    Q, K, V = make_inputs(w)
+    po = O.Params(1, 12, 1, 96, 1024, 64, scale=w.scale, eps=0.02)
+    prep = O.quantize(po, Q, K, V)
+    r = O.run(po, Q, K, V, prep, pass2=False)
+    import torch
+    from gpu_util import fp4_sections, torch_inputs, unpack_bits
+    p = problem_for(w)
+    q, k, v = torch_inputs(Q, K, V)
+    bufs = apa.alloc(p)
+    apa.quantize(p, q, k, v, bufs.fp4, bufs.ws_q)
+    apa.pass1(p, bufs.fp4, 0.02, bufs.cold_m, bufs.cold_l, bufs.cold_o, bufs.bits, None,
+              ws=bufs.ws_p1)
+    torch.cuda.synchronize()
+    check_quant({"fp4": fp4_sections(p, bufs.fp4.cpu().numpy())}, prep)
+    check_mask(unpack_bits(p, bufs.bits.cpu().numpy()), r)
