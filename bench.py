@@ -135,6 +135,33 @@ def cpu_legs(w, eps, ngroups, threads, gpu_out, gpu_hot, exact_out):
                      if g * 16 + i < w.Nq], np.int32)
     rep = O.reports(p, Q, K, V, gpu_hot, rows, nthreads=threads)
     ix = (rows[:, 0], rows[:, 1], rows[:, 2])
+    # the GPU's verdicts against the oracle's on the sampled groups: agreement
+    # over visited cells and the largest |margin| of a disagreeing one
+    vis_c, mism_c, worst_m = 0, 0, 0.0
+    for b, h, g in sel:
+        mg = r["margin"][b, h, g]
+        vis = ~np.isnan(mg)
+        diff = vis & (gpu_hot[b, h, g].astype(bool) != r["hot"][b, h, g].astype(bool))
+        vis_c += int(vis.sum())
+        mism_c += int(diff.sum())
+        if diff.any():
+            worst_m = max(worst_m, float(np.abs(mg[diff]).max()))
+    # the sink as realised: the mass of keys 0..3 (exact softmax) and their
+    # mean logit above the row's mean visible logit (nats; the mean key of the
+    # visible prefix from prefix sums of K)
+    G = w.Hq // w.Hkv
+    lift, mass = [], []
+    for b, hk in kvh:
+        Kh = K[b, hk].astype(np.float64)
+        pre = np.cumsum(Kh, axis=0)
+        ksink = Kh[:4].mean(axis=0)
+        for i in np.flatnonzero((rows[:, 0] == b) & (rows[:, 1] // G == hk)):
+            qr = Q[b, rows[i, 1], rows[i, 2]].astype(np.float64)
+            last = min(w.Nkv - 1, int(rows[i, 2]) + off)
+            s4 = w.scale * (Kh[:4] @ qr)
+            mass.append(float(np.exp(s4 - rep["lse"][i]).sum()))
+            lift.append(float(w.scale * (qr @ ksink - qr @ (pre[last] / (last + 1)))))
+    pct = lambda a, qs: {"p%d" % q: round(float(np.percentile(a, q)), 4) for q in qs}
 
     def summ(out):
         c = O.compare_rows(out[ix], rep["O_ref"])
@@ -160,6 +187,10 @@ def cpu_legs(w, eps, ngroups, threads, gpu_out, gpu_hot, exact_out):
                             np.linalg.norm(rep["O_hot"][worst]) / nref), 6) if nref > 0 else None}}
     if exact_out is not None:
         vs["exact"] = summ(exact_out)
+    vs["mask_vs_oracle"] = {"cells": vis_c, "agree": round(1.0 - mism_c / max(vis_c, 1), 6),
+                            "mismatches": mism_c, "worst_mismatch_margin": worst_m}
+    vs["sink"] = {"keys": 4, "mass": pct(mass, (10, 50, 90)),
+                  "lift_nats": pct(lift, (10, 50, 90)), "generator_lift_nats": w.delta}
     return base, vs
 
 
@@ -199,6 +230,8 @@ def main():
     torch.cuda.set_device(0)
     print("[bench] generating %s inputs" % w.name, file=sys.stderr, flush=True)
     Q, K, V = make_inputs(w)
+    data_sha = {n: hashlib.sha256(np.ascontiguousarray(x).tobytes()).hexdigest()
+                for n, x in (("Q", Q), ("K", K), ("V", V))}
     dt = torch.float16 if w.dtype == "fp16" else torch.bfloat16
     q = torch.from_numpy(Q).to(dt).cuda()
     k = torch.from_numpy(K).to(dt).cuda()
@@ -292,7 +325,9 @@ def main():
                               "frac": round(t_roof_ms / ms, 4),
                               "fp4_flop": w4, "fp16_flop": w16},
         "hot_fraction": {"cells": round(hot_cells / max(cells, 1), 5),
-                         "pairs": round(hpairs / max(vpairs, 1), 5)},
+                         "pairs": round(hpairs / max(vpairs, 1), 5),
+                         "page_real_dumps": "6-10 %"},
+        "data_sha256": data_sha,
     }
 
     exact_out_host = None
