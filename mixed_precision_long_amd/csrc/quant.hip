@@ -21,8 +21,11 @@
 // read again first.
 #include "apa_device.h"
 #include "apa_kernels.h"
+#include <type_traits>
 
 namespace apa {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 namespace {
 
@@ -69,19 +72,69 @@ __device__ void k_chunk_stats(const T* __restrict__ K, const Geom& g, const Quan
       const int k1 = max(k0, min(stat_khi(g), kend));
       // the tile's keys are contiguous (flat or paged input)
       const size_t base = kv_elem(g, bh / g.Hkv, bh % g.Hkv, k0) + cg * 8;
-#pragma unroll 8
-      for (int k = k0; k < k1; ++k) {
-        const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
-        const T* ek = reinterpret_cast<const T*>(&rk);
+      auto row = [&](int k) {
+        return *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
+      };
+      // rows in batches of eight: every load of a batch is issued before the
+      // first is used
+      constexpr int kB = 8;
+      int k = k0;
+      if constexpr (std::is_same<T, _Float16>::value) {
+        // fp16: minima and maxima two channels at a time in fp16 (exact)
+        h2 hmn[4], hmx[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          hmn[j] = h2{(_Float16)__builtin_inff(), (_Float16)__builtin_inff()};
+          hmx[j] = -hmn[j];
+        }
+        auto add = [&](const uint4& rk) {
+          const h2* e2 = reinterpret_cast<const h2*>(&rk);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            hmn[j] = __builtin_elementwise_min(hmn[j], e2[j]);
+            hmx[j] = __builtin_elementwise_max(hmx[j], e2[j]);
+            s[2 * j] += (double)(float)e2[j][0];
+            s[2 * j + 1] += (double)(float)e2[j][1];
+          }
+        };
+        for (; k + kB <= k1; k += kB) {
+          uint4 r[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u) r[u] = row(k + u);
+#pragma unroll
+          for (int u = 0; u < kB; ++u) add(r[u]);
+        }
+        for (; k < k1; ++k) add(row(k));
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float x = to_f32<T>(ek[i]);
-          bad |= !__builtin_isfinite(x);
-          s[i] += (double)x;
-          mn[i] = fminf(mn[i], x);
-          mx[i] = fmaxf(mx[i], x);
+          mn[i] = (float)hmn[i >> 1][i & 1];
+          mx[i] = (float)hmx[i >> 1][i & 1];
         }
+      } else {
+        auto add = [&](const uint4& rk) {
+          const T* ek = reinterpret_cast<const T*>(&rk);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float x = to_f32<T>(ek[i]);
+            s[i] += (double)x;
+            mn[i] = fminf(mn[i], x);
+            mx[i] = fmaxf(mx[i], x);
+          }
+        };
+        for (; k + kB <= k1; k += kB) {
+          uint4 r[kB];
+#pragma unroll
+          for (int u = 0; u < kB; ++u) r[u] = row(k + u);
+#pragma unroll
+          for (int u = 0; u < kB; ++u) add(r[u]);
+        }
+        for (; k < k1; ++k) add(row(k));
       }
+      // a NaN or an infinity among the statistics keys leaves its channel's
+      // FP64 sum non-finite (the sum of finite 16-bit values over one tile is
+      // far inside the FP64 range)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bad |= !__builtin_isfinite(s[i]);
       for (int k = k1; k < kend; ++k) {
         const uint4 rk = *reinterpret_cast<const uint4*>(K + base + (size_t)(k - k0) * D);
         const T* ek = reinterpret_cast<const T*>(&rk);
@@ -134,12 +187,27 @@ __device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws
   const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
   const int k1 = max(k0, min(stat_khi(g), kend));
   const int per_row = nch / 8;
-#pragma unroll 4
-  for (int i = threadIdx.x; i < kTile * per_row; i += blockDim.x) {
-    const int kk = i / per_row, c = (i % per_row) * 8;
-    uint4 r = {0u, 0u, 0u, 0u};
-    if (k0 + kk < kend) r = *reinterpret_cast<const uint4*>(V + kv_elem(g, b, hk, k0 + kk) + c0 + c);
-    *reinterpret_cast<uint4*>(&tile[kk * ld + c]) = r;
+  // 64 rows x nch channels in 16-byte pieces, kStage per thread (the block has
+  // 2 * nch threads); the tile's rows are contiguous (flat or paged), rows
+  // past Nkv re-read the last key and are stored as zeros.  All loads are
+  // issued before the first is used.
+  constexpr int kStage = 4;
+  {
+    const T* src = V + kv_elem(g, b, hk, k0) + c0;
+    const int last = kend - 1 - k0;
+    uint4 r[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      const int kk = i / per_row, c = (i % per_row) * 8;
+      r[j] = *reinterpret_cast<const uint4*>(src + (size_t)min(kk, last) * D + c);
+    }
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      const int kk = i / per_row, c = (i % per_row) * 8;
+      *reinterpret_cast<uint4*>(&tile[kk * ld + c]) = kk <= last ? r[j] : uint4{0u, 0u, 0u, 0u};
+    }
   }
   __syncthreads();
   const int c = threadIdx.x % nch, half = threadIdx.x / nch;
