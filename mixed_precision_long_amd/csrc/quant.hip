@@ -547,25 +547,44 @@ __device__ __forceinline__ uint4 load_row(const T* __restrict__ X, const Geom& g
   return *reinterpret_cast<const uint4*>(src);
 }
 
+// What every row of a block's sub-blocks shares for one thread: its 8
+// channels' kbar, the head's scale and the channel offset (loaded once per
+// block: the code stores go through byte pointers, which the compiler must
+// assume alias any global load after them).
+struct RowConst {
+  float kb[8];
+  float inv;
+  int c8;
+};
+
+template <bool IS_Q>
+__device__ __forceinline__ RowConst row_const(const Geom& g, const Fp4Ptrs& f, int bh) {
+  RowConst rc;
+  rc.c8 = (threadIdx.x % (g.D / 8)) * 8;  // the same in every sub-block (256 % (D/8) == 0)
+  const int H = IS_Q ? g.Hq : g.Hkv;
+  const int b = bh / H, h = bh % H;
+  const int hk = IS_Q ? h / g.G : h;
+  const size_t bk = (size_t)b * g.Hkv + hk;
+  rc.inv = IS_Q ? f.q_head[(size_t)bh * 4 + 1] : f.kv_head[bk * 8 + 2];
+  const float4* kp = reinterpret_cast<const float4*>(f.kbar + bk * g.D + rc.c8);
+  const float4 k0 = kp[0], k1 = kp[1];
+  rc.kb[0] = k0.x; rc.kb[1] = k0.y; rc.kb[2] = k0.z; rc.kb[3] = k0.w;
+  rc.kb[4] = k1.x; rc.kb[5] = k1.y; rc.kb[6] = k1.z; rc.kb[7] = k1.w;
+  return rc;
+}
+
 // Quantise rows along channels (Q, or K - kbar).  Each thread owns 8
 // consecutive channels of row `row` (its input in raw); 4 threads form one
 // 32-channel block.  Rows in [Nrows, NP) are padding and get zero codes.  For
 // Q it also writes the frame constant c_r = sl * q.kbar (FP32).
 template <typename T, bool IS_Q>
-__device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int row, int bh) {
-  const int H = IS_Q ? g.Hq : g.Hkv;
+__device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int row, int bh,
+                           const RowConst& rc) {
   const int Nrows = IS_Q ? g.Nq : g.Nkv;
   const int NP = IS_Q ? g.NqP : g.NkvP;
   const int tpr = g.D / 8;                     // threads per row
-  const int c8 = (threadIdx.x % tpr) * 8;
+  const int c8 = rc.c8;
   if (row >= NP) return;                       // whole rows exit together
-  const int b = bh / H, h = bh % H;
-  const int hk = IS_Q ? h / g.G : h;
-  const size_t bk = (size_t)b * g.Hkv + hk;
-  float inv;
-  const float* kb = f.kbar + bk * g.D;
-  if (IS_Q) inv = f.q_head[(size_t)bh * 4 + 1];
-  else inv = f.kv_head[bk * 8 + 2];
   float x[8];
   float cdot = 0.0f;
   if (row < Nrows) {
@@ -573,11 +592,11 @@ __device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int
     for (int i = 0; i < 8; ++i) {
       float v = to_f32<T>(e[i]);
       if (IS_Q) {
-        cdot = fmaf(v, kb[c8 + i], cdot);
+        cdot = fmaf(v, rc.kb[i], cdot);
       } else {
-        v = v - kb[c8 + i];
+        v = v - rc.kb[i];
       }
-      float n = v * inv;
+      float n = v * rc.inv;
       x[i] = fminf(fmaxf(n, -6.0f), 6.0f);
     }
   } else {
@@ -700,9 +719,10 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
 #pragma unroll
     for (int i = 0; i < kSubs; ++i)
       raw[i] = i < ns ? load_row<T, true>(Q, g, s0 + i, bh, &row[i]) : uint4{0u, 0u, 0u, 0u};
+    const RowConst rc = row_const<true>(g, f, bh);
 #pragma unroll
     for (int i = 0; i < kSubs; ++i)
-      if (i < ns) quant_rows<T, true>(raw[i], g, f, row[i], bh);
+      if (i < ns) quant_rows<T, true>(raw[i], g, f, row[i], bh, rc);
     return;
   }
   b -= nq;
@@ -715,9 +735,10 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
   for (int i = 0; i < kSubs; ++i)
     raw[i] = i < ns ? load_row<T, false>(K, g, t * kpt + s0 + i, bh, &row[i])
                     : uint4{0u, 0u, 0u, 0u};
+  const RowConst rc = row_const<false>(g, f, bh);
 #pragma unroll
   for (int i = 0; i < kSubs; ++i)
-    if (i < ns) quant_rows<T, false>(raw[i], g, f, row[i], bh);
+    if (i < ns) quant_rows<T, false>(raw[i], g, f, row[i], bh, rc);
 }
 
 template <typename T>
