@@ -536,15 +536,22 @@ __device__ __forceinline__ uint4 load_row(const T* __restrict__ X, const Geom& g
                                           int bh, int* row_out) {
   const int H = IS_Q ? g.Hq : g.Hkv;
   const int Nrows = IS_Q ? g.Nq : g.Nkv;
-  const int tpr = g.D / 8;
+  const int lt = __builtin_ctz(g.D / 8);  // threads per row: D / 8, a power of two
   const int gid = sub * 256 + threadIdx.x;
-  const int row = gid / tpr, c8 = (gid % tpr) * 8;
+  const int row = gid >> lt, c8 = (gid & ((1 << lt) - 1)) * 8;
   *row_out = row;
   if (row >= Nrows) return uint4{0u, 0u, 0u, 0u};
   const int b = bh / H, h = bh % H;
   const int hk = IS_Q ? h / g.G : h;
   const T* src = X + (IS_Q ? ((size_t)bh * Nrows + row) * g.D : kv_elem(g, b, hk, row)) + c8;
   return *reinterpret_cast<const uint4*>(src);
+}
+
+// The maximum over the four lanes of a quad (the threads of one 32-channel
+// block), by two DPP quad permutations; every lane of the quad is active.
+__device__ __forceinline__ float quad_max(float a) {
+  a = fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0xB1, 0xF, 0xF, false)));
+  return fmaxf(a, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(a), 0x4E, 0xF, 0xF, false)));
 }
 
 // What every row of a block's sub-blocks shares for one thread: its 8
@@ -560,7 +567,7 @@ struct RowConst {
 template <bool IS_Q>
 __device__ __forceinline__ RowConst row_const(const Geom& g, const Fp4Ptrs& f, int bh) {
   RowConst rc;
-  rc.c8 = (threadIdx.x % (g.D / 8)) * 8;  // the same in every sub-block (256 % (D/8) == 0)
+  rc.c8 = (threadIdx.x & (g.D / 8 - 1)) * 8;  // the same in every sub-block (256 % (D/8) == 0)
   const int H = IS_Q ? g.Hq : g.Hkv;
   const int b = bh / H, h = bh % H;
   const int hk = IS_Q ? h / g.G : h;
@@ -604,8 +611,7 @@ __device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int
   }
   float a = 0.0f;
   for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(x[i]));
-  a = fmaxf(a, __shfl_xor(a, 1));
-  a = fmaxf(a, __shfl_xor(a, 2));
+  a = quad_max(a);
   int e = e8m0_exponent(a);
   if (!IS_Q && g.klsq) e = lsq_exponent(x, e);
   const float s = pow2_scale(e);
@@ -637,8 +643,7 @@ __device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int
       x[i] = x[i] - ((c & 8u) ? -d : d);
       a2 = fmaxf(a2, fabsf(x[i]));
     }
-    a2 = fmaxf(a2, __shfl_xor(a2, 1));
-    a2 = fmaxf(a2, __shfl_xor(a2, 2));
+    a2 = quad_max(a2);
     const int e2 = e8m0_exponent(a2);
     const float s2 = pow2_scale(e2);
     unsigned w2 = 0;
