@@ -329,38 +329,31 @@ __device__ void head_scale(float amax, float* gs, float* inv) {
 
 // Chunk statistics are read in batches of kFinBatch chunks with every load of
 // a batch in flight (the block is latency-bound: few blocks, short chains).
-constexpr int kFinBatch = 32;
+constexpr int kFinBatch = 16;
 
-// Per (b, kv-head): key mean, |K - kbar| max, V max, the K head scale (V's
-// is 1), and the tied Q scales of the group's query heads; with the weighted
-// hot test the mean value norm nu_bar (FP64: each thread sums a contiguous
-// run of tiles ascending, then the runs are added in thread order; a frozen
-// cache keeps its own) and the weight w_t = max(1, nu_t / nu_bar) of every
-// tile read (1 when nu_bar is 0).  Each block folds the non-finite flags of
-// its own K chunks, V items and Q tiles and ORs the result into the status
-// word (which the statistics pass cleared).  grid (B*Hkv), block 2D.
-__device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh, float* xch,
-                         float* red, float* nbs, double* part) {
+// Per (b, kv-head), in two parts.  The key part (after the statistics pass):
+// key mean, |K - kbar| max, the K head scale (V's is 1) and the tied Q scales
+// of the group's query heads, folding the non-finite flags of its K chunks
+// and Q tiles.  The value part (after the V coding): max |V|; with the
+// weighted hot test the mean value norm nu_bar (FP64: each thread sums a
+// contiguous run of tiles ascending, then the runs are added in thread order;
+// a frozen cache keeps its own) and the weight w_t = max(1, nu_t / nu_bar) of
+// every tile read (1 when nu_bar is 0), folding the flags of its V items.
+// Each ORs its flags into the status word (cleared before either runs).
+// Key part: block 2D threads; value part: any block size.
+__device__ void finalize_kq(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh,
+                            float* xch, float* red) {
   const int d = threadIdx.x, nthr = blockDim.x, D = g.D;
   const bool own = d < D;  // threads D .. 2D-1 fold min and max, and join the block reductions
   const size_t base = (size_t)bh * ws.nch * D + (own ? d : d - D);
   const int b = bh / g.Hkv, hk = bh % g.Hkv;
   // first the loads that do not wait on the key statistics, so that they are
   // in flight with them: this head's non-finite flags (its K chunks [ch0,
-  // ch1), its V items of tiles [qt0, qt1), the Q tiles of its query heads),
-  // max |V| and each query head's max |Q|
+  // ch1), the Q tiles of its query heads) and each query head's max |Q|
   unsigned badf = 0u;
-  float va = 0.0f;
   float qa[8];
   {
     for (int c = ws.ch0 + d; c < ws.ch1; c += nthr) badf |= ws.flags[(size_t)bh * ws.nch + c];
-    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
-    const int n = (g.qt1 - g.qt0) * ws.nvz;
-#pragma unroll 8
-    for (int i = d; i < n; i += nthr) {
-      va = fmaxf(va, ws.vamax[i0 + i]);
-      badf |= ws.flags[vflag0(g, ws) + i0 + i];
-    }
     const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G) * ws.nqt;
     for (int i = d; i < g.G * ws.nqt; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
 #pragma unroll
@@ -414,45 +407,15 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
   badf = __syncthreads_or(badf != 0u);
   if (d == 0 && badf) atomicOr(f.status, 1u);
   const float amax_k = block_max(dev, red);
-  const float amax_v = block_max(va, red);
   float gk, ik;
   head_scale(amax_k, &gk, &ik);
-  // V is coded at its own scale (per-head scale 1)
-  const float gv = 1.0f, iv = 1.0f;
   // frozen statistics: the K/V scales stay the cache's; Q's tie to its g_K
   if (g.frozen) gk = f.kv_head[(size_t)bh * 8 + 1];
-  if (g.vweight) {
-    if (!g.frozen) {
-      // thread d sums tiles [qt0 + d * run, qt0 + (d + 1) * run), ascending
-      const int n = g.qt1 - g.qt0, run = (n + nthr - 1) / nthr;
-      double sv = 0.0;
-      for (int i = d * run; i < min(n, (d + 1) * run); ++i)
-        sv += ws.vnst[(size_t)bh * g.NT + g.qt0 + i];
-      part[d] = sv;
-    }
-    __syncthreads();
-    if (d == 0) {
-      float nb = f.kv_head[(size_t)bh * 8 + 6];
-      if (!g.frozen) {
-        double sv = 0.0;
-        for (int i = 0; i < nthr; ++i) sv += part[i];
-        const int nk = stat_khi(g) - stat_t0(g) * kTile;
-        nb = nk > 0 ? (float)(sv / (double)nk) : 0.0f;
-      }
-      *nbs = nb;
-    }
-    __syncthreads();
-    const float nb = *nbs;
-    for (int t = g.qt0 + d; t < g.qt1; t += nthr) {
-      const float nt = ws.vnt[(size_t)bh * g.NT + t];
-      f.tile_w[(size_t)bh * g.NTc + t] = nb > 0.0f ? fmaxf(1.0f, nt / nb) : 1.0f;
-    }
-  }
   if (d == 0 && !g.frozen) {
+    // V is coded at its own scale (per-head scale 1); entries 3 and 6 are the
+    // value part's
     float* kh = f.kv_head + (size_t)bh * 8;
-    kh[0] = amax_k; kh[1] = gk; kh[2] = ik; kh[3] = amax_v; kh[4] = gv; kh[5] = iv;
-    kh[6] = g.vweight ? *nbs : 0.0f;
-    kh[7] = 0.0f;
+    kh[0] = amax_k; kh[1] = gk; kh[2] = ik; kh[4] = 1.0f; kh[5] = 1.0f; kh[7] = 0.0f;
   }
   // Q heads of this group: inv_q = w * 2^-j, w = fl32(sl * g_k), j the
   // smallest integer with amax_q * w <= 6 * 2^j.  The first eight heads' max
@@ -486,6 +449,57 @@ __device__ void finalize(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int
     float qv = 0.0f;
     for (int t = d; t < ws.nqt; t += nthr) qv = fmaxf(qv, ws.qamax[q0 + t]);
     q_scale(i, qv);
+  }
+}
+
+__device__ void finalize_v(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, int bh,
+                           float* red, float* nbs, double* part) {
+  const int d = threadIdx.x, nthr = blockDim.x;
+  unsigned badf = 0u;
+  float va = 0.0f;
+  {
+    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
+    const int n = (g.qt1 - g.qt0) * ws.nvz;
+#pragma unroll 4
+    for (int i = d; i < n; i += nthr) {
+      va = fmaxf(va, ws.vamax[i0 + i]);
+      badf |= ws.flags[vflag0(g, ws) + i0 + i];
+    }
+  }
+  badf = __syncthreads_or(badf != 0u);
+  if (d == 0 && badf) atomicOr(f.status, 1u);
+  const float amax_v = block_max(va, red);
+  if (g.vweight) {
+    if (!g.frozen) {
+      // thread d sums tiles [qt0 + d * run, qt0 + (d + 1) * run), ascending
+      const int n = g.qt1 - g.qt0, run = (n + nthr - 1) / nthr;
+      double sv = 0.0;
+      for (int i = d * run; i < min(n, (d + 1) * run); ++i)
+        sv += ws.vnst[(size_t)bh * g.NT + g.qt0 + i];
+      part[d] = sv;
+    }
+    __syncthreads();
+    if (d == 0) {
+      float nb = f.kv_head[(size_t)bh * 8 + 6];
+      if (!g.frozen) {
+        double sv = 0.0;
+        for (int i = 0; i < nthr; ++i) sv += part[i];
+        const int nk = stat_khi(g) - stat_t0(g) * kTile;
+        nb = nk > 0 ? (float)(sv / (double)nk) : 0.0f;
+      }
+      *nbs = nb;
+    }
+    __syncthreads();
+    const float nb = *nbs;
+    for (int t = g.qt0 + d; t < g.qt1; t += nthr) {
+      const float nt = ws.vnt[(size_t)bh * g.NT + t];
+      f.tile_w[(size_t)bh * g.NTc + t] = nb > 0.0f ? fmaxf(1.0f, nt / nb) : 1.0f;
+    }
+  }
+  if (d == 0 && !g.frozen) {
+    float* kh = f.kv_head + (size_t)bh * 8;
+    kh[3] = amax_v;
+    kh[6] = g.vweight ? *nbs : 0.0f;
   }
 }
 
@@ -683,27 +697,40 @@ __global__ __launch_bounds__(512) void k_stats(const T* __restrict__ Q, const T*
 
 // The V items of the tiles read, one block each (per kv-head, tile,
 // 128-channel slice), 2 * min(D, 128) threads.  Runs after k_stats, whose
-// block 0 cleared the status word.
+// block 0 cleared the status word.  Up to D = 128 (block = 2D threads) the
+// first nfin blocks are the key part of the finalize step, one per (b,
+// kv-head): it needs only the statistics pass, so it runs beside the V coding
+// rather than as a launch of its own; clear: the statistics pass did not run,
+// so block 0 clears the status word (there are then no flags to fold).
 template <typename T>
 __global__ __launch_bounds__(256) void k_vcode(const T* __restrict__ V, Geom g, QuantWs ws,
-                                               Fp4Ptrs f) {
+                                               Fp4Ptrs f, int nfin, int clear) {
   __shared__ T tile[kTile * (128 + 8)];
   __shared__ float red[16];
   __shared__ float knu[kTile];  // a tile's key norms
+  if ((int)blockIdx.x < nfin) {
+    float* xch = reinterpret_cast<float*>(tile);  // [2][D] (D <= 128)
+    if (clear && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+    finalize_kq(g, ws, f, blockIdx.x, xch, red);
+    return;
+  }
+  const int item = blockIdx.x - nfin;
   const int per_head = (g.qt1 - g.qt0) * ws.nvz;
-  const int r = blockIdx.x % per_head;
-  v_item<T>(V, g, ws, f, blockIdx.x / per_head, g.qt0 + r / ws.nvz, r % ws.nvz, tile, red, knu);
+  const int r = item % per_head;
+  v_item<T>(V, g, ws, f, item / per_head, g.qt0 + r / ws.nvz, r % ws.nvz, tile, red, knu);
 }
 
-// One block of 2*D threads per (b, kv-head).  clear: the statistics pass did
-// not run (nothing to check), so block 0 clears the status word itself.
+// Both finalize parts as a launch of their own (D > 128, where the V coding's
+// blocks are not 2D threads): one block of 2D threads per (b, kv-head).
 __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f, int clear) {
   extern __shared__ float xch[];  // [2][D]: min and max of each channel
   __shared__ float red[16];
   __shared__ float nbs;           // nu_bar
   __shared__ double part[1024];   // the threads' runs of tile norm sums
   if (clear && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
-  finalize(g, ws, f, blockIdx.x, xch, red, &nbs, part);
+  finalize_kq(g, ws, f, blockIdx.x, xch, red);
+  __syncthreads();
+  finalize_v(g, ws, f, blockIdx.x, red, &nbs, part);
 }
 
 // Quantisation in one launch: blocks for Q rows first, then per (b, kv-head),
@@ -712,10 +739,21 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f, int clear) {
 // sub-blocks of 256 threads (2048 elements each: 16 rows of 128 channels, or
 // the same at other D), their loads issued together before any is used.
 constexpr int kSubs = 4;
+// The first nfin blocks (D <= 128) are the value part of the finalize step,
+// one per (b, kv-head): it needs only the V coding before it.
 template <typename T>
 __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T* __restrict__ K,
-                                               Geom g, Fp4Ptrs f, int kpt, int qpb, int nq) {
+                                               Geom g, Fp4Ptrs f, QuantWs ws, int kpt, int qpb,
+                                               int nq, int nfin) {
   int b = blockIdx.x;
+  if (b < nfin) {
+    __shared__ float red[16];
+    __shared__ float nbs;
+    __shared__ double part[256];
+    finalize_v(g, ws, f, b, red, &nbs, part);
+    return;
+  }
+  b -= nfin;
   uint4 raw[kSubs];
   int row[kSubs];
   if (b < nq) {
@@ -764,19 +802,25 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(min(2 * g.D, 512)), stats_lds, s, q, k,
                        g, ws, f, nkb);
-  if (nvb > 0)
-    hipLaunchKernelGGL(k_vcode<T>, dim3(nvb), dim3(2 * min(g.D, 128)), 0, s, v, g, ws, f);
-  hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 2 * g.D * sizeof(float), s, g, ws, f,
-                     nkb + nqb > 0 ? 0 : 1);
+  const int clear = nkb + nqb > 0 ? 0 : 1;
+  // up to D = 128 the finalize parts ride in the V coding and K/Q coding launches
+  const bool fuse = g.D <= 128;
+  const int nfin = fuse ? nkvh : 0;
+  if (nvb + nfin > 0)
+    hipLaunchKernelGGL(k_vcode<T>, dim3(nvb + nfin), dim3(2 * min(g.D, 128)), 0, s, v, g, ws, f,
+                       nfin, clear);
+  if (!fuse)
+    hipLaunchKernelGGL(k_finalize, dim3(nkvh), dim3(2 * g.D), 2 * g.D * sizeof(float), s, g, ws,
+                       f, clear);
   // K rows: a 64-key tile of D channels is kTile * D / 8 threads, D / 32
   // sub-blocks of 256; Q: qpb sub-blocks per head
   const int kpt = g.D / 32;
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
   const long nq = (long)((qpb + kSubs - 1) / kSubs) * g.B * g.Hq;
-  const long nblk = nq + (long)(g.qt1 - g.qt0) * nkvh * ((kpt + kSubs - 1) / kSubs);
+  const long nblk = nfin + nq + (long)(g.qt1 - g.qt0) * nkvh * ((kpt + kSubs - 1) / kSubs);
   if (nblk > 0)
-    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, g, f, kpt, qpb,
-                       (int)nq);
+    hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, g, f, ws, kpt,
+                       qpb, (int)nq, nfin);
   return hipGetLastError();
 }
 
