@@ -152,7 +152,11 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *                          byte (2n + hh) * D/32 + db
  *   kbar     [B][Hkv][D] float       per-channel key mean
  *   kv_head  [B][Hkv][8] float       amax_K, g_K, inv_K, amax_V, 1, 1 (V's scale),
- *                                    nu_bar (with hot_weight, else 0), 0
+ *                                    nu_bar (with hot_weight, else 0), 0;
+ *                                    amax_V is max |V| over every key coded
+ *                                    (a call with frozen statistics raises it
+ *                                    to cover its tiles): the 16-bit pass
+ *                                    shifts bf16 V into the fp16 range by it
  *   tile_w   [B][Hkv][NTc] float     with hot_weight: the value-norm weight
  *                                    w_t of every tile some row sees (the
  *                                    rest untouched)

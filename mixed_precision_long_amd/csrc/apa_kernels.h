@@ -76,7 +76,7 @@ struct QuantWs {
   double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
   float* kmin;    // [B*Hkv][NCH][D]
   float* kmax;    // [B*Hkv][NCH][D]
-  float* vamax;   // [B*Hkv][NT][NVZ] max |V| over the statistics keys per V item
+  float* vamax;   // [B*Hkv][NT][NVZ] max |V| over the keys of each V item
   float* qamax;   // [B*Hq][NQT]
   unsigned* flags;  // [B*Hkv*NCH + B*Hkv*NT*NVZ + B*Hq*NQT]
   float* vnt;     // [B*Hkv][NT]  largest value norm of each tile read (weighted test)

@@ -172,8 +172,8 @@ __device__ void k_chunk_stats(const T* __restrict__ K, const Geom& g, const Quan
 // slice is staged in LDS (16-byte loads, zeros for keys past Nkv), then thread
 // (channel c, key half) takes one 32-key block: the smallest exponent that
 // fits its maximum under 6, E2M1 codes stored with the eight 4-key runs in
-// the order 0,2,4,6,1,3,5,7.  Also: the item's max |V| over the statistics
-// keys and its non-finite flag; with the weighted test and cz = 0, every
+// the order 0,2,4,6,1,3,5,7.  Also: the item's max |V| over its keys and its
+// non-finite flag; with the weighted test and cz = 0, every
 // key's value norm (squares in FP32 in channel order inside a thread, over
 // the threads of the key by an xor butterfly; from the staged slice when it
 // holds the whole row, D <= 128), the tile's largest norm and the FP64 sum of
@@ -221,7 +221,7 @@ __device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws
       x[i] = to_f32<T>(tile[(half * 32 + i) * ld + c]);
       bad |= !__builtin_isfinite(x[i]);
       a = fmaxf(a, fabsf(x[i]));
-      if (k0 + half * 32 + i < k1) as = fmaxf(as, fabsf(x[i]));
+      if (k0 + half * 32 + i < kend) as = fmaxf(as, fabsf(x[i]));
     }
     const int e = e8m0_exponent(a);
     const float sc = pow2_scale(e);
@@ -295,21 +295,35 @@ __device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws
   }
 }
 
-// max |Q| per (b, q-head, 64-row tile).  grid (NQT, B*Hq); a block of nh*D
-// threads (nh = 2, or 1 at D = 512): thread (half, d) takes rows r0 + half,
-// r0 + half + nh, ...
+// max |Q| and the non-finite check per (b, q-head, 64-row tile), any block
+// size.
 template <typename T>
 __device__ void q_stats(const T* __restrict__ Q, const Geom& g, const QuantWs& ws, int t, int bh,
                         float* red) {
-  const int d = threadIdx.x % g.D, half = threadIdx.x / g.D, nh = blockDim.x / g.D;
-  const size_t base = ((size_t)bh * g.Nq) * g.D;
-  const int r0 = t * 64, r1 = min(g.Nq, r0 + 64);
+  // the tile's rows are contiguous: 16-byte pieces, kQB per thread per round,
+  // every load of a round issued before the first is used
+  constexpr int kQB = 4;
+  const int r0 = t * 64, n = (min(g.Nq, r0 + 64) - r0) * (g.D / 8);
+  const T* src = Q + ((size_t)bh * g.Nq + r0) * g.D;
   float a = 0.0f;
   bool bad = false;
-  for (int r = r0 + half; r < r1; r += nh) {
-    float x = to_f32<T>(Q[base + (size_t)r * g.D + d]);
-    bad |= !__builtin_isfinite(x);
-    a = fmaxf(a, fabsf(x));
+  for (int i0 = threadIdx.x; i0 < n; i0 += kQB * (int)blockDim.x) {
+    uint4 r[kQB];
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      const int i = i0 + j * (int)blockDim.x;
+      r[j] = i < n ? *reinterpret_cast<const uint4*>(src + (size_t)i * 8) : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kQB; ++j) {
+      const T* e = reinterpret_cast<const T*>(&r[j]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = to_f32<T>(e[k]);
+        bad |= !__builtin_isfinite(x);
+        a = fmaxf(a, fabsf(x));
+      }
+    }
   }
   bad = __syncthreads_or(bad);
   float m = block_max(a, red);
@@ -496,10 +510,13 @@ __device__ void finalize_v(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, i
       f.tile_w[(size_t)bh * g.NTc + t] = nb > 0.0f ? fmaxf(1.0f, nt / nb) : 1.0f;
     }
   }
-  if (d == 0 && !g.frozen) {
+  if (d == 0) {
+    // max |V| over every key coded, for the 16-bit pass's range shift of
+    // bf16 V: with frozen statistics the cache's value grows to cover the
+    // new tiles too
     float* kh = f.kv_head + (size_t)bh * 8;
-    kh[3] = amax_v;
-    kh[6] = g.vweight ? *nbs : 0.0f;
+    kh[3] = g.frozen ? fmaxf(kh[3], amax_v) : amax_v;
+    if (!g.frozen) kh[6] = g.vweight ? *nbs : 0.0f;
   }
 }
 
@@ -734,10 +751,10 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f, int clear) {
 }
 
 // Quantisation in one launch: blocks for Q rows first, then per (b, kv-head),
-// last first, per 64-key tile its K rows -- the reverse of the order the
-// statistics pass read them (V^T was coded there).  A block takes up to 4
-// sub-blocks of 256 threads (2048 elements each: 16 rows of 128 channels, or
-// the same at other D), their loads issued together before any is used.
+// last first, its K rows -- the reverse of the order the statistics pass read
+// them.  A block takes up to kSubs consecutive sub-blocks of 256 threads (2048
+// elements each: 16 rows of 128 channels, or the same at other D), their
+// loads issued together before any is used.
 constexpr int kSubs = 4;
 // The first nfin blocks (D <= 128) are the value part of the finalize step,
 // one per (b, kv-head): it needs only the V coding before it.
@@ -769,15 +786,16 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
     return;
   }
   b -= nq;
-  const int bpt = (kpt + kSubs - 1) / kSubs;  // blocks per tile
-  const int per_head = (g.qt1 - g.qt0) * bpt;
+  // the head's sub-blocks [qt0 * kpt, qt1 * kpt) (16-row groups at D = 128),
+  // kSubs consecutive ones per block, across tile boundaries
+  const int s_lo = g.qt0 * kpt, s_hi = g.qt1 * kpt;
+  const int per_head = (s_hi - s_lo + kSubs - 1) / kSubs;
   const int bh = g.B * g.Hkv - 1 - b / per_head;
-  const int r = b % per_head, t = g.qt0 + r / bpt, s0 = (r % bpt) * kSubs;
-  const int ns = min(kSubs, kpt - s0);
+  const int s0 = s_lo + (b % per_head) * kSubs;
+  const int ns = min(kSubs, s_hi - s0);
 #pragma unroll
   for (int i = 0; i < kSubs; ++i)
-    raw[i] = i < ns ? load_row<T, false>(K, g, t * kpt + s0 + i, bh, &row[i])
-                    : uint4{0u, 0u, 0u, 0u};
+    raw[i] = i < ns ? load_row<T, false>(K, g, s0 + i, bh, &row[i]) : uint4{0u, 0u, 0u, 0u};
   const RowConst rc = row_const<false>(g, f, bh);
 #pragma unroll
   for (int i = 0; i < kSubs; ++i)
@@ -817,7 +835,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   const int kpt = g.D / 32;
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
   const long nq = (long)((qpb + kSubs - 1) / kSubs) * g.B * g.Hq;
-  const long nblk = nfin + nq + (long)(g.qt1 - g.qt0) * nkvh * ((kpt + kSubs - 1) / kSubs);
+  const long nblk = nfin + nq + (long)nkvh * (((g.qt1 - g.qt0) * kpt + kSubs - 1) / kSubs);
   if (nblk > 0)
     hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, g, f, ws, kpt,
                        qpb, (int)nq, nfin);

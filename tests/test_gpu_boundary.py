@@ -55,6 +55,36 @@ def test_bf16_v_beyond_fp16_range_apa(D):
     assert g["hot"].any() and (g["l"] > 0).any()
 
 
+def test_bf16_v_beyond_fp16_range_past_the_statistics_keys():
+    """Statistics over the first 2048 of 4096 keys, and bf16 V of the later
+    keys 2^16 times larger (beyond the fp16 range, unlike any statistics
+    key's): the per-head max |V| that pass 2 shifts V by covers every key
+    coded, so the output is finite and meets the usual bars against the
+    oracle, each row measured against its own largest magnitude.  With
+    eps = 0 every tile with any mass is hot, so pass 2 computes all of them
+    (a cold tile of the large values would carry FP4 differences 2^16 times
+    larger than the rest, whatever the range shift does)."""
+    w = small_workload(1, 4, 1, 96, 4096, 128, dtype="bf16", mode="gauss", seed=53)
+    Q, K, V = make_inputs(w)
+    V[:, :, 2048:] *= 2.0 ** 16
+    assert np.abs(V[:, :, :2048]).max() < 65504.0 < np.abs(V[:, :, 2048:]).max()
+    eps = 0.0
+    po = O.Params(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D, scale=w.scale, eps=eps, stat_keys=2048)
+    prep = O.quantize(po, Q, K, V)
+    r = O.run(po, Q, K, V, prep)
+    g = run_gpu(problem_for(w, stat_keys=2048), Q, K, V, eps, dtype="bf16")
+    assert g["fp4"]["status"] == 0
+    assert g["fp4"]["kv_head"][0, 0, 3] == np.float32(np.abs(V).max())
+    check_mask(g["hot"], r)
+    assert np.isfinite(g["out"]).all()
+    # the hot part ran in pass 2 on tiles of both ranges
+    hot_t = np.flatnonzero(g["hot"].any(axis=(0, 1, 2)))
+    assert (hot_t < 32).any() and (hot_t >= 32).any()
+    mag = np.abs(r["O"]).max(axis=-1, keepdims=True)
+    mag = np.where(mag > 0, mag, 1.0)
+    check_output(g["out"] / mag, r["O"] / mag, dtype="bf16")
+
+
 @pytest.mark.parametrize("where", ["q", "k", "v"])
 def test_nonfinite_input_sets_the_status_bit(where):
     """One NaN (or infinity) anywhere in Q, K or V sets bit 0 of the FP4
