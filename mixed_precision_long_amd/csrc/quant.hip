@@ -166,132 +166,147 @@ __device__ void k_chunk_stats(const T* __restrict__ K, const Geom& g, const Quan
   }
 }
 
-// V^T codes of one V item (b, kv-head, 64-key tile, 128-channel slice cz).
-// V enters at its own scale: its E8M0 block exponents carry the range, so its
-// codes need no statistics and are written here, in the statistics pass.  The
-// slice is staged in LDS (16-byte loads, zeros for keys past Nkv), then thread
-// (channel c, key half) takes one 32-key block: the smallest exponent that
-// fits its maximum under 6, E2M1 codes stored with the eight 4-key runs in
-// the order 0,2,4,6,1,3,5,7.  Also: the item's max |V| over its keys and its
-// non-finite flag; with the weighted test and cz = 0, every
-// key's value norm (squares in FP32 in channel order inside a thread, over
-// the threads of the key by an xor butterfly; from the staged slice when it
-// holds the whole row, D <= 128), the tile's largest norm and the FP64 sum of
-// its statistics keys' norms, keys ascending.
+// V^T codes of the V items (b, kv-head, 64-key tile, 128-channel slice cz)
+// of tiles t0 .. t0 + nt - 1.  V enters at its own scale: its E8M0 block
+// exponents carry the range, so its codes need no statistics.  Each tile's
+// slice is staged in LDS (16-byte loads, zeros for keys past Nkv), then
+// thread (channel c, key half) takes one 32-key block: the smallest exponent
+// that fits its maximum under 6, E2M1 codes stored with the eight 4-key runs
+// in the order 0,2,4,6,1,3,5,7.  Also: max |V| over the keys and the
+// non-finite flag (per block); with the weighted test and cz = 0, every key's
+// value norm (squares in FP32 in channel order inside a thread, over the
+// threads of the key by an xor butterfly; from the staged slice when it holds
+// the whole row, D <= 128), each tile's largest norm and the FP64 sum of its
+// statistics keys' norms, keys ascending.
 template <typename T>
-__device__ void v_item(const T* __restrict__ V, const Geom& g, const QuantWs& ws, const Fp4Ptrs& f,
-                       int bh, int t, int cz, T* tile, float* red, float* knu) {
-  constexpr int CH = 128, PADH = 8;
-  const int D = g.D, c0 = cz * CH, nch = min(CH, D - c0), ld = nch + PADH;
+__device__ void v_items(const T* __restrict__ V, const Geom& g, const QuantWs& ws,
+                        const Fp4Ptrs& f, int bh, int t0, int nt, int cz, T* tile, float* red,
+                        float* knu) {
+  // a staged row is ld elements apart whatever nch is, so that every column
+  // read below has a constant offset from one base
+  constexpr int CH = 128, PADH = 8, ld = CH + PADH;
+  const int D = g.D, c0 = cz * CH, nch = min(CH, D - c0);
   const int b = bh / g.Hkv, hk = bh % g.Hkv;
-  const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
-  const int k1 = max(k0, min(stat_khi(g), kend));
   const int per_row = nch / 8;
   // 64 rows x nch channels in 16-byte pieces, kStage per thread (the block has
-  // 2 * nch threads); the tile's rows are contiguous (flat or paged), rows
-  // past Nkv re-read the last key and are stored as zeros.  All loads are
-  // issued before the first is used.
+  // 2 * nch threads); a tile's rows are contiguous (flat or paged), rows past
+  // Nkv re-read the last key and are stored as zeros.  The next tile's loads
+  // are in flight while this tile is coded.
   constexpr int kStage = 4;
-  {
+  uint4 r[kStage];
+  auto load = [&](int t) {
+    const int k0 = t * kTile, last = min(g.Nkv, k0 + kTile) - 1 - k0;
     const T* src = V + kv_elem(g, b, hk, k0) + c0;
-    const int last = kend - 1 - k0;
-    uint4 r[kStage];
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
       const int i = threadIdx.x + j * (int)blockDim.x;
       const int kk = i / per_row, c = (i % per_row) * 8;
       r[j] = *reinterpret_cast<const uint4*>(src + (size_t)min(kk, last) * D + c);
     }
-#pragma unroll
-    for (int j = 0; j < kStage; ++j) {
-      const int i = threadIdx.x + j * (int)blockDim.x;
-      const int kk = i / per_row, c = (i % per_row) * 8;
-      *reinterpret_cast<uint4*>(&tile[kk * ld + c]) = kk <= last ? r[j] : uint4{0u, 0u, 0u, 0u};
-    }
-  }
-  __syncthreads();
+  };
   const int c = threadIdx.x % nch, half = threadIdx.x / nch;
   bool bad = false;
   float as = 0.0f;
-  if (half < 2) {
-    float x[32];
-    float a = 0.0f;
+  load(t0);
+  for (int it = 0; it < nt; ++it) {
+    const int t = t0 + it;
+    const int k0 = t * kTile, kend = min(g.Nkv, k0 + kTile);
+    const int k1 = max(k0, min(stat_khi(g), kend));
+    const int last = kend - 1 - k0;
+    if (it > 0) __syncthreads();  // every read of the previous tile is done
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = to_f32<T>(tile[(half * 32 + i) * ld + c]);
-      bad |= !__builtin_isfinite(x[i]);
-      a = fmaxf(a, fabsf(x[i]));
-      if (k0 + half * 32 + i < kend) as = fmaxf(as, fabsf(x[i]));
+    for (int j = 0; j < kStage; ++j) {
+      const int i = threadIdx.x + j * (int)blockDim.x;
+      const int kk = i / per_row, cc = (i % per_row) * 8;
+      *reinterpret_cast<uint4*>(&tile[kk * ld + cc]) = kk <= last ? r[j] : uint4{0u, 0u, 0u, 0u};
     }
-    const int e = e8m0_exponent(a);
-    const float sc = pow2_scale(e);
-    constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-    unsigned out[4];
+    __syncthreads();
+    if (it + 1 < nt) load(t + 1);
+    {
+      // two passes over the staged column (the block maximum, then the
+      // codes), so that the 32 values need not stay in registers
+      const T* col = tile + half * 32 * ld + c;
+      auto xv = [&](int i) { return to_f32<T>(col[i * ld]); };
+      float a = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      unsigned w = 0;
-      const int ra = perm[2 * j] * 4, rb = perm[2 * j + 1] * 4;
-      w = cvt_fp4x2(w, x[ra + 0], x[ra + 1], sc, 0);
-      w = cvt_fp4x2(w, x[ra + 2], x[ra + 3], sc, 1);
-      w = cvt_fp4x2(w, x[rb + 0], x[rb + 1], sc, 2);
-      w = cvt_fp4x2(w, x[rb + 2], x[rb + 3], sc, 3);
-      out[j] = w;
+      for (int i = 0; i < 32; ++i) {
+        const float x = xv(i);
+        bad |= !__builtin_isfinite(x);
+        a = fmaxf(a, fabsf(x));
+      }
+      as = fmaxf(as, a);  // rows past Nkv are zeros
+      const int e = e8m0_exponent(a);
+      const float sc = pow2_scale(e);
+      constexpr int perm[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+      unsigned out[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        unsigned w = 0;
+        const int ra = perm[2 * j] * 4, rb = perm[2 * j + 1] * 4;
+        w = cvt_fp4x2(w, xv(ra + 0), xv(ra + 1), sc, 0);
+        w = cvt_fp4x2(w, xv(ra + 2), xv(ra + 3), sc, 1);
+        w = cvt_fp4x2(w, xv(rb + 0), xv(rb + 1), sc, 2);
+        w = cvt_fp4x2(w, xv(rb + 2), xv(rb + 3), sc, 3);
+        out[j] = w;
+      }
+      const int ch = c0 + c;
+      uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(D);
+      *reinterpret_cast<uint4*>(blob + 34 * D + ch * 32 + half * 16) =
+          uint4{out[0], out[1], out[2], out[3]};
+      blob[66 * D + ((ch % 32) * 2 + half) * (D / 32) + ch / 32] = (uint8_t)(e + 127);
     }
-    const int ch = c0 + c;
-    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(D);
-    *reinterpret_cast<uint4*>(blob + 34 * D + ch * 32 + half * 16) =
-        uint4{out[0], out[1], out[2], out[3]};
-    blob[66 * D + ((ch % 32) * 2 + half) * (D / 32) + ch / 32] = (uint8_t)(e + 127);
+    if (g.vweight && cz == 0) {
+      // parts threads per key, each D / parts consecutive channels
+      const int parts = blockDim.x / kTile, cpp = D / parts;
+      const int kk = threadIdx.x / parts, part = threadIdx.x % parts;
+      float q = 0.0f;
+      if (nch == D) {
+        // the whole row is in the staged slice (zeros past Nkv)
+        const T* row = tile + kk * ld + part * cpp;
+        for (int c8 = 0; c8 < cpp; c8 += 8) {
+          const uint4 rr = *reinterpret_cast<const uint4*>(row + c8);
+          const T* e = reinterpret_cast<const T*>(&rr);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float y = to_f32<T>(e[i]);
+            q = fmaf(y, y, q);
+          }
+        }
+      } else if (k0 + kk < kend) {
+        const T* row = V + kv_elem(g, b, hk, k0 + kk) + part * cpp;
+        for (int c8 = 0; c8 < cpp; c8 += 8) {
+          const uint4 rr = *reinterpret_cast<const uint4*>(row + c8);
+          const T* e = reinterpret_cast<const T*>(&rr);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float y = to_f32<T>(e[i]);
+            q = fmaf(y, y, q);
+          }
+        }
+      }
+      for (int o = 1; o < parts; o <<= 1) q += __shfl_xor(q, o);
+      if (part == 0) knu[kk] = sqrtf(q);
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        float mx = 0.0f;
+        double sn = 0.0;
+        for (int i = 0; i < kTile; ++i) {
+          mx = fmaxf(mx, knu[i]);
+          if (k0 + i < k1) sn += (double)knu[i];
+        }
+        ws.vnt[(size_t)bh * g.NT + t] = mx;
+        ws.vnst[(size_t)bh * g.NT + t] = sn;
+      }
+    }
   }
+  // the block's max |V| and flag go to its first item, 0 to the others (the
+  // finalize step folds them per head)
   bad = __syncthreads_or(bad);
   const float m = block_max(as, red);
-  const size_t item = ((size_t)bh * g.NT + t) * ws.nvz + cz;
-  if (threadIdx.x == 0) {
-    ws.vamax[item] = m;
-    ws.flags[vflag0(g, ws) + item] = bad ? 1u : 0u;
-  }
-  if (g.vweight && cz == 0) {
-    // parts threads per key, each D / parts consecutive channels
-    const int parts = blockDim.x / kTile, cpp = D / parts;
-    const int kk = threadIdx.x / parts, part = threadIdx.x % parts;
-    float q = 0.0f;
-    if (nch == D) {
-      // the whole row is in the staged slice (zeros past Nkv)
-      const T* row = tile + kk * ld + part * cpp;
-      for (int c8 = 0; c8 < cpp; c8 += 8) {
-        const uint4 r = *reinterpret_cast<const uint4*>(row + c8);
-        const T* e = reinterpret_cast<const T*>(&r);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float y = to_f32<T>(e[i]);
-          q = fmaf(y, y, q);
-        }
-      }
-    } else if (k0 + kk < kend) {
-      const T* row = V + kv_elem(g, b, hk, k0 + kk) + part * cpp;
-      for (int c8 = 0; c8 < cpp; c8 += 8) {
-        const uint4 r = *reinterpret_cast<const uint4*>(row + c8);
-        const T* e = reinterpret_cast<const T*>(&r);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float y = to_f32<T>(e[i]);
-          q = fmaf(y, y, q);
-        }
-      }
-    }
-    for (int o = 1; o < parts; o <<= 1) q += __shfl_xor(q, o);
-    if (part == 0) knu[kk] = sqrtf(q);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float mx = 0.0f;
-      double sn = 0.0;
-      for (int i = 0; i < kTile; ++i) {
-        mx = fmaxf(mx, knu[i]);
-        if (k0 + i < k1) sn += (double)knu[i];
-      }
-      ws.vnt[(size_t)bh * g.NT + t] = mx;
-      ws.vnst[(size_t)bh * g.NT + t] = sn;
-    }
+  if (threadIdx.x < nt) {
+    const size_t item = ((size_t)bh * g.NT + t0 + threadIdx.x) * ws.nvz + cz;
+    ws.vamax[item] = threadIdx.x == 0 ? m : 0.0f;
+    ws.flags[vflag0(g, ws) + item] = (threadIdx.x == 0 && bad) ? 1u : 0u;
   }
 }
 
@@ -712,8 +727,11 @@ __global__ __launch_bounds__(512) void k_stats(const T* __restrict__ Q, const T*
   }
 }
 
-// The V items of the tiles read, one block each (per kv-head, tile,
-// 128-channel slice), 2 * min(D, 128) threads.  Runs after k_stats, whose
+// Tiles of V per V-coding block.
+constexpr int kVTiles = 4;
+
+// The V items of the tiles read (per kv-head, tile, 128-channel slice),
+// kVTiles consecutive tiles of one slice per block, 2 * min(D, 128) threads.  Runs after k_stats, whose
 // block 0 cleared the status word.  Up to D = 128 (block = 2D threads) the
 // first nfin blocks are the key part of the finalize step, one per (b,
 // kv-head): it needs only the statistics pass, so it runs beside the V coding
@@ -731,10 +749,13 @@ __global__ __launch_bounds__(256) void k_vcode(const T* __restrict__ V, Geom g, 
     finalize_kq(g, ws, f, blockIdx.x, xch, red);
     return;
   }
-  const int item = blockIdx.x - nfin;
-  const int per_head = (g.qt1 - g.qt0) * ws.nvz;
-  const int r = item % per_head;
-  v_item<T>(V, g, ws, f, item / per_head, g.qt0 + r / ws.nvz, r % ws.nvz, tile, red, knu);
+  const int blk = blockIdx.x - nfin;
+  const int ngrp = (g.qt1 - g.qt0 + kVTiles - 1) / kVTiles;
+  const int per_head = ngrp * ws.nvz;
+  const int r = blk % per_head;
+  const int t0 = g.qt0 + (r / ws.nvz) * kVTiles;
+  v_items<T>(V, g, ws, f, blk / per_head, t0, min(kVTiles, g.qt1 - t0), r % ws.nvz, tile, red,
+             knu);
 }
 
 // Both finalize parts as a launch of their own (D > 128, where the V coding's
@@ -815,7 +836,7 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
     stats_attr = true;
   }
   const int nkb = g.Nkv > 0 ? (ws.ch1 - ws.ch0) * nkvh : 0;
-  const int nvb = g.Nkv > 0 ? (g.qt1 - g.qt0) * ws.nvz * nkvh : 0;
+  const int nvb = g.Nkv > 0 ? (g.qt1 - g.qt0 + kVTiles - 1) / kVTiles * ws.nvz * nkvh : 0;
   const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(min(2 * g.D, 512)), stats_lds, s, q, k,
