@@ -126,6 +126,9 @@ struct Pass2Args {
   int32_t* list_tiles;   // [units][NT]  (units: see attn_units)
   uint32_t* list_masks;  // [units][NT]
   int32_t* list_count;   // [units]
+  // per (b, kv-head): its work groups by descending tile count (ties in
+  // ascending order), the order pass 2 takes them in; [units]
+  int32_t* list_order;
   // split states when a unit's keys run as S work groups: [S][rows] and
   // [S][rows][D] (rows = B*Hq*Nq)
   float *part_m, *part_l, *part_o;

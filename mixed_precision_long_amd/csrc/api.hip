@@ -175,11 +175,12 @@ size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
   const size_t units = (size_t)attn_units(g);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
-  const size_t t = take(units * g.NT * 4), m = take(units * g.NT * 4), c = take(units * 4);
+  const size_t t = take(units * g.NT * 4), m = take(units * g.NT * 4), c = take(units * 4),
+               r = take(units * 4);
   if (a && base) {
     uint8_t* bb = (uint8_t*)base;
     a->list_tiles = (int32_t*)(bb + t); a->list_masks = (uint32_t*)(bb + m);
-    a->list_count = (int32_t*)(bb + c);
+    a->list_count = (int32_t*)(bb + c); a->list_order = (int32_t*)(bb + r);
   }
   return split_ws(p, o, a, base);
 }

@@ -80,12 +80,25 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
   const int item = xcd_remap(blockIdx.x, gridDim.x);
   if (item >= nitems) return;  // uniform over the block
   const RowBlocks rb = row_blocks(g);
-  // exact: each (batch, kv-head, split) from its last query positions (the
-  // longest causal key ranges) down
-  const int wg = MODE == kExact ? rb.nwg - 1 - item % rb.nwg : item % rb.nwg;
-  int u = item / rb.nwg;
-  const int sp = u % S;
-  u /= S;
+  int wg, sp, u;
+  if (MODE == kExact) {
+    // each (batch, kv-head, split) from its last query positions (the
+    // longest causal key ranges) down
+    wg = rb.nwg - 1 - item % rb.nwg;
+    u = item / rb.nwg;
+    sp = u % S;
+    u /= S;
+  } else {
+    // per (batch, kv-head) and split, its work groups longest list first (a
+    // greedy longest-first schedule over the compute units its items land
+    // on); the splits stay in turn, so the work groups running together read
+    // the same part of their lists
+    const int per = rb.nwg * S;
+    u = item / per;
+    const int j = item % per;
+    wg = __builtin_amdgcn_readfirstlane(a.list_order[(size_t)u * rb.nwg + j % rb.nwg]);
+    sp = j / rb.nwg;
+  }
   const int hk = u % g.Hkv;
   const int b = u / g.Hkv;
   const int unit = (b * g.Hkv + hk) * rb.nwg + wg;
@@ -400,6 +413,34 @@ __device__ __forceinline__ void merge4(int m1i, float l1, v4f a1, float m2, floa
     *lse_out = Ls > 0.0f ? 0.69314718055994531f * (c0 + M + __log2f(Ls)) : -__builtin_inff();
 }
 
+// Per (b, kv-head), its pass-2 work groups ordered by descending tile count,
+// ties in ascending order (the rank of each among the head's counts, staged
+// in LDS); above kOrderMax work groups per head the order is the identity.
+// One block of 256 threads per (b, kv-head).  The order only schedules: every
+// work group computes the same values whenever it runs.
+constexpr int kOrderMax = 4096;
+__global__ __launch_bounds__(256) void k_order(const int32_t* __restrict__ count,
+                                               int32_t* __restrict__ order, int nwg) {
+  __shared__ int c[kOrderMax];
+  const int32_t* cnt = count + (size_t)blockIdx.x * nwg;
+  int32_t* ord = order + (size_t)blockIdx.x * nwg;
+  if (nwg > kOrderMax) {
+    for (int w = threadIdx.x; w < nwg; w += blockDim.x) ord[w] = w;
+    return;
+  }
+  for (int w = threadIdx.x; w < nwg; w += blockDim.x) c[w] = cnt[w];
+  __syncthreads();
+  for (int w = threadIdx.x; w < nwg; w += blockDim.x) {
+    const int x = c[w];
+    int r = 0;
+    for (int j = 0; j < nwg; ++j) {
+      const int y = c[j];
+      r += (y > x) | ((y == x) & (j < w));
+    }
+    ord[r] = w;
+  }
+}
+
 // Standalone merge of the cold and hot states; one thread per (row, 4 channels).
 template <int D, typename T>
 __global__ void k_merge(Geom g, Fp4Ptrs f, const int32_t* __restrict__ cm,
@@ -568,6 +609,10 @@ hipError_t launch_pass2(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a, hip
   hipLaunchKernelGGL(k_compact, dim3(nunits), dim3(64), 0, s, g, a.bits, a.list_tiles,
                      a.list_masks, a.list_count, nunits);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_order, dim3(g.B * g.Hkv), dim3(256), 0, s, a.list_count, a.list_order,
+                     row_blocks(g).nwg);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   return dispatch<kPass2>(g, a.q, a.k, a.v, f, a, attn_splits(g), s);
 }

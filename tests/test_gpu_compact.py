@@ -4,8 +4,9 @@ GPU's own hot mask: for work group (b, kv-head, four row blocks), every tile
 hot for any of its eight 16-row groups, ascending, with a mask whose bit
 2w + k says the tile is hot for wave w's k-th group.  Row blocks are
 numbered position-major, head-minor inside a kv-head (block j: query head
-hk * G + j % G, rows 32 * (j // G) ..).  Index work, so bit-exact; also at
-the 2048 x 122880 shape."""
+hk * G + j % G, rows 32 * (j // G) ..).  Also the order pass 2 takes a
+head's work groups in: by descending tile count, ties in ascending order.
+Index work, so bit-exact; also at the 2048 x 122880 shape."""
 import numpy as np
 import pytest
 import torch
@@ -54,7 +55,8 @@ def check(p, q, k, v, eps):
     want = expected_lists(p, hot)
     units, NT = len(want), hot.shape[3]
     # the pass-2 workspace starts with the lists: tiles [units][NT] int32,
-    # masks [units][NT] uint32, counts [units] int32, each 256-byte aligned
+    # masks [units][NT] uint32, counts [units] int32, then the order
+    # [units] int32, each 256-byte aligned
     ws = bufs.ws_p2.cpu().numpy()
     a = lambda n: (n + 255) // 256 * 256
     t_off, m_off = 0, a(units * NT * 4)
@@ -67,6 +69,12 @@ def check(p, q, k, v, eps):
         assert n == len(tl), (u, n, len(tl))
         assert np.array_equal(tiles[u, :n], tl), u
         assert np.array_equal(masks[u, :n], ml), u
+    o_off = c_off + a(units * 4)
+    order = ws[o_off:o_off + units * 4].view(np.int32).reshape(p.B * p.Hkv, -1)
+    for bk, ordk in enumerate(order):
+        cnt = count[bk * len(ordk):(bk + 1) * len(ordk)]
+        want_o = sorted(range(len(ordk)), key=lambda w: (-int(cnt[w]), w))
+        assert np.array_equal(ordk, want_o), bk
     return sum(len(t) for t, _ in want), units
 
 
