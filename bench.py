@@ -356,13 +356,14 @@ def main():
 
     def variant(p2, vv=None, ref=None):
         """One APA configuration on the same inputs (V replaced by vv if
-        given): 10 timed steps after 2, per-kernel times, hot cells, and its
-        output against `ref` (the exact output of the same inputs)."""
+        given): 10 timed steps after 20 (the clocks settle again after the
+        all-exact launches), per-kernel times, hot cells, and its output
+        against `ref` (the exact output of the same inputs)."""
         vv = v if vv is None else vv
         b2 = apa.alloc(p2)
         ev2 = []
-        for i in range(2 + 10):
-            step_eps(apa, p2, q, k, vv, b2, eps, stream, ev2 if i >= 2 else None)
+        for i in range(20 + 10):
+            step_eps(apa, p2, q, k, vv, b2, eps, stream, ev2 if i >= 20 else None)
         torch.cuda.synchronize()
         hot2 = apa_hot_mask(p2, b2.bits)
         c2, h2, _, _ = cell_counts(hot2, w.Nq, w.Nkv)
@@ -418,18 +419,20 @@ def main():
               flush=True)
 
     if w.eps_sweep and not args.no_sweep:
-        # each eps: the same step, warmed up, with its kernels timed apart
+        # each eps: the same step, warmed up (20 steps: after the all-exact
+        # launches the clocks take several steps to settle again), with its
+        # kernels timed apart over 20 steps
         sweep = {}
         for e2 in w.eps_sweep:
-            for _ in range(3):
+            for _ in range(20):
                 step_eps(apa, p, q, k, v, bufs, e2, stream, None)
             torch.cuda.synchronize()
             evs = []
             t0 = time.perf_counter()
-            for _ in range(10):
+            for _ in range(20):
                 step_eps(apa, p, q, k, v, bufs, e2, stream, evs)
             torch.cuda.synchronize()
-            ms2 = (time.perf_counter() - t0) * 1e3 / 10
+            ms2 = (time.perf_counter() - t0) * 1e3 / 20
             kms = [float(np.mean([x[a].elapsed_time(x[a + 1]) for x in evs])) for a in range(3)]
             hot2 = apa_hot_mask(p, bufs.bits)
             c2, h2, vp2, hp2 = cell_counts(hot2, w.Nq, w.Nkv)
