@@ -61,17 +61,19 @@ __host__ __device__ inline int first_key_tile(const Geom& g) {
   return g.causal && g.window > 0 && k > 0 ? k / 64 : 0;
 }
 
-// The statistics pass reads the K/V tiles a quantise call codes, [qt0,
-// qt1): for their non-finite check and value norms, and, up to the key
-// stat_khi, for the statistics, which start at tile stat_t0.  With frozen
+// A quantise call reads the K/V tiles it codes, [qt0, qt1): for their
+// non-finite check and value norms, and, up to the key stat_khi, for the
+// statistics, which start at tile stat_t0.  With frozen
 // statistics (quantising only tiles [qt0, qt1) of a persistent cache) none
 // are taken.
 __host__ __device__ inline int stat_t0(const Geom& g) { return g.frozen ? g.qt0 : first_key_tile(g); }
 __host__ __device__ inline int stat_khi(const Geom& g) { return g.frozen ? g.Nkv : g.stat_hi; }
 
-// Statistics scratch.  V items are (b, kv-head, tile, 128-channel slice): the
-// V^T coding blocks of the statistics pass.  flags: one word per statistics
-// block (a non-finite input seen), K chunks first, then V items, then Q tiles.
+// Statistics scratch.  V items are (b, kv-head, tile, 128-channel slice); a
+// V-coding block codes four consecutive items of one slice and keeps its max
+// |V| and flag in the first of them (zeros in the others).  flags: one word
+// per K chunk, V item and Q tile (a non-finite input seen), K chunks first,
+// then V items, then Q tiles.
 struct QuantWs {
   double* ksum;   // [B*Hkv][NCH][D]  per chunk of 16 tiles
   float* kmin;    // [B*Hkv][NCH][D]
