@@ -897,6 +897,9 @@ typedef struct {
   const int32_t* jq;
   const float *inv_q, *inv_k, *inv_v; /* per-head scales (unquantised operands) */
   const float* vw;   /* [B][Hkv][NT] value-norm weights (used with p->vweight) */
+  /* per (b, q-head) score factor when Q has a scale of its own (an ablation
+   * of the tied scale: Q normalised by 6 / max|Q|), or NULL: alpha = 2^jq */
+  const double* alpha_q;
   /* work list: triplets (b, h, g) */
   const int32_t* groups;
   int ngroups;
@@ -938,7 +941,7 @@ static void run_group(orc_job* J, int w) {
   ops.vc = J->vc + bk * D * (NkvP / 2);
   ops.vs = J->vs + bk * D * (NkvP / Bs);
   ops.NkvP = NkvP;
-  ops.alpha = ldexp(1.0, J->jq[bh]);
+  ops.alpha = J->alpha_q ? J->alpha_q[bh] : ldexp(1.0, J->jq[bh]);
   ops.g_v = J->g_v[bk];
   ops.Qh = J->Q + bh * p->Nq * D;
   ops.Kh = J->K + bk * p->Nkv * D;

@@ -59,7 +59,7 @@ class _Job(C.Structure):
     _fields_ = [("p", _P), ("Q", _P), ("K", _P), ("V", _P),
                 ("qc", _P), ("qs", _P), ("kc", _P), ("ks", _P), ("vc", _P), ("vs", _P),
                 ("qc2", _P), ("qs2", _P), ("kbar", _P), ("g_v", _P), ("jq", _P),
-                ("inv_q", _P), ("inv_k", _P), ("inv_v", _P), ("vw", _P),
+                ("inv_q", _P), ("inv_k", _P), ("inv_v", _P), ("vw", _P), ("alpha_q", _P),
                 ("groups", _P), ("ngroups", C.c_int),
                 ("hot", _P), ("margin", _P), ("m1", _P), ("l1", _P), ("lam", _P), ("o1", _P),
                 ("shift", _P), ("m2", _P), ("l2", _P), ("o2", _P), ("cr", _P), ("O", _P),
@@ -147,6 +147,8 @@ class Params:
                             # prefill: frozen at the last restat); 0: over all keys
     hot_weight: int = 0     # 1: the hot test weighs a tile's mass by its value-norm
                             # weight (see tile_weights); 0: mass only
+    q_scale: str = "tied"   # "own": an ablation of the tied Q scale -- Q normalised by
+                            # 6 / max|Q| of its head, the score factor sl * g_k * g_q
 
     def c(self) -> _Params:
         assert self.rg == 16, "the oracle keeps 16-row verdict groups"
@@ -157,6 +159,7 @@ class Params:
         assert self.window >= 0 and (self.window == 0 or self.causal)
         assert self.stat_keys == 0 or self.first_tile * self.tile < self.stat_keys <= self.Nkv
         assert self.hot_weight in (0, 1)
+        assert self.q_scale in ("tied", "own") and (self.q_scale == "tied" or self.fmt == MX)
         bs = 16 if self.fmt == NV else 32
         assert self.D % bs == 0
         return _Params(self.B, self.Hq, self.Hkv, self.Nq, self.Nkv, self.D, self.causal,
@@ -363,18 +366,25 @@ def quantize(p: Params, Q: np.ndarray, K: np.ndarray, V: np.ndarray) -> dict:
             L.orc_q_scale(C.c_float(aq), C.c_float(s_l), C.c_float(out["g_k"][b, h // G]), p.fmt,
                           _ptr(f[0:1]), _ptr(ji))
             out["inv_q"][b, h], out["jq"][b, h] = f[0], ji[0]
+            if p.q_scale == "own":
+                # Q at its own head scale, amax/6 like K's; the score factor
+                # then carries both head scales and sl (no longer a power of two)
+                L.orc_head_scale(C.c_float(aq), p.fmt, _ptr(f[0:1]), _ptr(f[1:2]))
+                out["inv_q"][b, h] = f[1]
+                out.setdefault("alpha_q", np.zeros((B, Hq), np.float64))[b, h] = (
+                    float(np.float32(s_l)) * float(out["g_k"][b, h // G]) * float(f[0]))
             qc = np.zeros((Nq, D // 2), np.uint8)
             qs = np.zeros((Nq, D // bs), np.uint8)
             if p.q_terms == 2:
                 qc2 = np.zeros((Nq, D // 2), np.uint8)
                 qs2 = np.zeros((Nq, D // bs), np.uint8)
-                L.orc_quant_rows2(_ptr(Qh), Nq, D, C.c_float(f[0]), p.fmt, _ptr(qc), _ptr(qs),
+                L.orc_quant_rows2(_ptr(Qh), Nq, D, C.c_float(out["inv_q"][b, h]), p.fmt, _ptr(qc), _ptr(qs),
                                   _ptr(qc2), _ptr(qs2))
                 out.setdefault("qc2", np.zeros((B, Hq, Nq, D // 2), np.uint8))[b, h] = qc2
                 out.setdefault("qs2", np.zeros((B, Hq, Nq, D // bs), np.uint8))[b, h] = qs2
             else:
-                L.orc_quant_rows(_ptr(Qh), Nq, D, None, C.c_float(f[0]), p.fmt, _ptr(qc),
-                                 _ptr(qs))
+                L.orc_quant_rows(_ptr(Qh), Nq, D, None, C.c_float(out["inv_q"][b, h]), p.fmt,
+                                 _ptr(qc), _ptr(qs))
             out["qc"][b, h], out["qs"][b, h] = qc, qs
     return out
 
@@ -428,6 +438,7 @@ def run(p: Params, Q, K, V, prep: dict | None = None, groups=None, nthreads: int
     job.jq = _ptr(prep["jq"])
     job.inv_q, job.inv_k, job.inv_v = (_ptr(prep[k]) for k in ("inv_q", "inv_k", "inv_v"))
     job.vw = _ptr(prep["vw"]) if p.hot_weight else None
+    job.alpha_q = _ptr(prep["alpha_q"]) if p.q_scale == "own" else None
     job.qc2 = _ptr(prep.get("qc2")) if p.q_terms == 2 else None
     job.qs2 = _ptr(prep.get("qs2")) if p.q_terms == 2 else None
     job.groups, job.ngroups = _ptr(groups), len(groups)

@@ -529,3 +529,38 @@ def test_nv_pass1_bitwise_vs_brute_force_on_flat_scores(eps, seed):
     assert np.array_equal((r["l1"][0] * sc).astype(np.float32), b["l"])
     assert np.array_equal((r["lam"][0] * sc).astype(np.float32), b["lam"])
     assert np.array_equal((r["o1"][0] * sc[..., None]).astype(np.float32), b["o"])
+
+
+@pytest.mark.parametrize("case", [
+    (8, 2, 128, 32768, 128, "path", 11, 0.005),
+    (8, 2, 128, 32768, 128, "gauss", 12, 0.005),
+    (4, 1, 64, 16384, 256, "path", 14, 0.02),
+], ids=["path_D128", "gauss_D128", "path_D256_eps0.02"])
+def test_tied_q_scale_costs_no_accuracy(case):
+    """Ablation of the tied Q scale (Q normalised so that the score factor is
+    a power of two) against Q at a head scale of its own (6 / max|Q|, like
+    K's): at long contexts, where most tiles are cold, the APA output's
+    distance from FP64 attention and the hot share are the same within the
+    spread of the inputs.  (A mis-scaled Q in either form shows as a many-fold
+    larger error.)"""
+    Hq, Hkv, Nq, Nkv, D, mode, seed, eps = case
+    w = small_workload(1, Hq, Hkv, Nq, Nkv, D, mode=mode, seed=seed)
+    Q, K, V = make_inputs(w)
+    Oe, _ = O.exact(O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale), Q, K, V)
+    e = Oe.reshape(-1, D)
+    res = {}
+    for qs in ("tied", "own"):
+        p = O.Params(1, Hq, Hkv, Nq, Nkv, D, scale=w.scale, eps=eps, q_scale=qs)
+        r = O.run(p, Q, K, V, O.quantize(p, Q, K, V))
+        o = r["O"].reshape(-1, D)
+        cos = (o * e).sum(1) / (np.linalg.norm(o, axis=1) * np.linalg.norm(e, axis=1))
+        vis = ~np.isnan(r["margin"])
+        res[qs] = dict(cos_min=cos.min(), cos_med=np.median(cos), mse=((o - e) ** 2).mean(),
+                       hot=r["hot"][vis].mean())
+    t, o = res["tied"], res["own"]
+    print("[tied Q scale]", {k: {kk: float("%.6g" % vv) for kk, vv in v.items()} for k, v in res.items()})
+    assert 0.05 < t["hot"] < 0.9  # most tiles are decided, some cold
+    assert abs(t["hot"] - o["hot"]) <= 0.02
+    assert t["mse"] <= 1.15 * o["mse"] and o["mse"] <= 1.15 * t["mse"]
+    assert abs(t["cos_min"] - o["cos_min"]) <= 0.01
+    assert abs(t["cos_med"] - o["cos_med"]) <= 2e-4
