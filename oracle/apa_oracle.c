@@ -47,7 +47,9 @@
  * planted tile, and the output-norm bound it gives; NVFP4 mode (blocks of 16
  * with UE4M3 scales, P in 16-key groups) bitwise against the brute force's own
  * NV quantisation on inputs whose P scales stay in UE4M3's normal range, and
- * its 2^-6 scale floor through the sink bug.  Parity unpinned: the
+ * its 2^-6 scale floor through the sink bug; the Q head-scale ablation
+ * (alpha_q: Q at a scale of its own) by its FP64 error matching the tied
+ * scale's, which a mis-scaled Q would multiply.  Parity unpinned: the
  * pages' measured numbers (they come from activation dumps that are not
  * available), listed as such in the design notes.
  */
