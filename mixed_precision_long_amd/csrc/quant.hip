@@ -740,7 +740,7 @@ constexpr int kVTiles = 4;
 template <typename T>
 __global__ __launch_bounds__(256) void k_vcode(const T* __restrict__ V, Geom g, QuantWs ws,
                                                Fp4Ptrs f, int nfin, int clear) {
-  __shared__ T tile[kTile * (128 + 8)];
+  __shared__ __attribute__((aligned(16))) T tile[kTile * (128 + 8)];
   __shared__ float red[16];
   __shared__ float knu[kTile];  // a tile's key norms
   if ((int)blockIdx.x < nfin) {
