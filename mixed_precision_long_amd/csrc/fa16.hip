@@ -415,10 +415,11 @@ __device__ __forceinline__ void merge4(int m1i, float l1, v4f a1, float m2, floa
 
 // Per (b, kv-head), its pass-2 work groups ordered by descending tile count,
 // ties in ascending order (the rank of each among the head's counts, staged
-// in LDS); above kOrderMax work groups per head the order is the identity.
+// in LDS: nwg^2 / 256 comparisons per thread, a few microseconds at 1024);
+// above kOrderMax work groups per head the order is the identity.
 // One block of 256 threads per (b, kv-head).  The order only schedules: every
 // work group computes the same values whenever it runs.
-constexpr int kOrderMax = 4096;
+constexpr int kOrderMax = 2048;
 __global__ __launch_bounds__(256) void k_order(const int32_t* __restrict__ count,
                                                int32_t* __restrict__ order, int nwg) {
   __shared__ int c[kOrderMax];
