@@ -122,6 +122,17 @@ typedef struct apa_problem {
                                      the weights into the FP4 buffer; every call
                                      on one FP4 buffer must name the same value.
                                      0: the mass test (0)                       */
+  int32_t ring_tiles;             /* KV window ring (the APA page's "What else
+                                     is in the box"): 0, or the key tiles R of
+                                     each of two ring halves, a multiple of 32
+                                     (the page uses 96).  The FP4 buffer then
+                                     holds 1 + 2R tile blobs per (b, kv-head):
+                                     the sink tile 0 and the halves, and only
+                                     apa_ring_pass1 fills and walks them;
+                                     apa_quantize, apa_quantize_tiles,
+                                     apa_quantize_static and apa_pass1 return
+                                     APA_ERR_UNSUPPORTED.  Needs D <= 256, no
+                                     window and the mass test (0)              */
 } apa_problem;
 
 /* Defaults: scale 1/sqrt(D), tile 64, row_group 16, MXFP4, tau 4, H 32,
@@ -181,7 +192,7 @@ size_t apa_fp4_bytes(const apa_problem* p);
 size_t apa_hotmask_bytes(const apa_problem* p);
 
 enum { APA_CALL_QUANTIZE = 0, APA_CALL_PASS1 = 1, APA_CALL_PASS2 = 2, APA_CALL_MERGE = 3,
-       APA_CALL_EXACT = 4 };
+       APA_CALL_EXACT = 4, APA_CALL_RING_PASS1 = 5 };
 /* Scratch bytes the given call needs in its `ws` argument (0: pass NULL). */
 size_t apa_workspace_bytes(const apa_problem* p, int32_t which_call);
 
@@ -291,6 +302,30 @@ apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* 
  * [0, 32)).  *records (may be NULL) receives the undecided tail tiles kept
  * per 32-row block (0 under APA_SCHED_WHOLE). */
 int32_t apa_pass1_split(const apa_problem* p, int32_t npos, int32_t* cut, int32_t* records);
+
+/* f3: pass 1 over a KV window ring ("What else is in the box": a sink tile
+ * plus two ring halves of R = p->ring_tiles FP4 tiles per KV head, the next
+ * key segment quantised while pass 1 walks the current one).  Does what
+ * apa_quantize then apa_pass1 do, with the FP4 K/V copy bounded to 1 + 2R
+ * tiles per KV head whatever Nkv is: the statistics over every key (one read
+ * of K and V), Q's codes, the sink tile; then, per segment of R tiles from the
+ * top down, that segment's FP4 codes into the ring half it alternates to (on
+ * a second stream the library keeps per device, ordered by events so that a
+ * half is rewritten only after the walk that reads it is done) and one launch
+ * of pass 1 over the segment for every 32-row block, carrying each block's
+ * state through the workspace.  Every row walks its tiles in the same order
+ * as apa_pass1 with one wave per block (APA_SCHED_WHOLE), so the outputs
+ * (cold state, hot mask, lambda) equal that call's bit for bit; apa_pass2
+ * then runs as usual on the same FP4 buffer (its Q frames and scales) and the
+ * 16-bit K/V.  The status word ORs the non-finite checks of every read.
+ * Arguments as apa_quantize and apa_pass1; ws: apa_workspace_bytes(p,
+ * APA_CALL_RING_PASS1) bytes (the quantise scratch, then per 32-row block
+ * and query head 128 D + 1040 bytes rounded up to 256).  Calls on one device
+ * must not overlap (they share its second stream's order). */
+apa_status apa_ring_pass1(const apa_problem* p, const void* q, const void* k, const void* v,
+                          void* fp4, float eps, int32_t* cold_m, float* cold_l, float* cold_o,
+                          uint32_t* hot_bits, float* lambda_out, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /* a8..a10: pass 2 ("Pass 2: exact FP16 on the hot tiles").  Compacts the hot
  * mask into per-work-group lists of tiles hot for any of its row groups, then

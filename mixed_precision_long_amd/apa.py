@@ -17,12 +17,12 @@ APA_OK, APA_ERR_INVALID_ARG, APA_ERR_UNSUPPORTED, APA_ERR_WORKSPACE, APA_ERR_HIP
 APA_F16, APA_BF16 = 0, 1
 APA_MXFP4, APA_NVFP4 = 0, 1
 SCHED_AUTO, SCHED_WHOLE, SCHED_PAIRS, SCHED_TRIPLES = range(4)
-CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT = range(5)
+CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT, CALL_RING_PASS1 = range(6)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
            "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize",
            "apa_quantize_static", "apa_quantize_tiles", "apa_pass1",
-           "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact"]
+           "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact", "apa_ring_pass1"]
 
 
 class ApaError(RuntimeError):
@@ -43,7 +43,7 @@ class Problem(C.Structure):
                 ("q_terms", C.c_int32), ("k_scale_lsq", C.c_int32), ("window", C.c_int32),
                 ("kv_capacity", C.c_int32), ("stat_keys", C.c_int32),
                 ("block_table", C.c_void_p), ("block_table_stride", C.c_int32),
-                ("hot_weight", C.c_int32)]
+                ("hot_weight", C.c_int32), ("ring_tiles", C.c_int32)]
 
 
 class Fp4Layout(C.Structure):
@@ -84,6 +84,7 @@ def lib() -> C.CDLL:
         L.apa_quantize_static.argtypes = [P, VP, VP, VP, VP, VP]
         L.apa_quantize_tiles.argtypes = [P, VP, VP, VP, VP, C.c_int32, C.c_int32, VP, S, VP]
         L.apa_pass1.argtypes = [P, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
+        L.apa_ring_pass1.argtypes = [P, VP, VP, VP, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
                                 VP, S, VP]
         L.apa_merge.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
@@ -98,9 +99,10 @@ def status_string(code: int) -> str:
 
 def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4.0, hoff=32.0,
             fmt=APA_MXFP4, sched=SCHED_AUTO, q_terms=1, k_lsq=0, window=0, kv_capacity=0,
-            stat_keys=0, block_table=None, hot_weight=0) -> Problem:
+            stat_keys=0, block_table=None, hot_weight=0, ring_tiles=0) -> Problem:
     """block_table: a device int32 tensor [B, stride] of page indices (paged
-    K/V), or None; hot_weight: 1 for the value-norm weighted hot test."""
+    K/V), or None; hot_weight: 1 for the value-norm weighted hot test;
+    ring_tiles: tiles per half of a KV window ring (0: none)."""
     p = Problem()
     lib().apa_problem_init(C.byref(p), B, Hq, Hkv, Nq, Nkv, D)
     p.dtype, p.is_causal, p.scale, p.tau, p.hot_frame_offset, p.fmt, p.pass1_schedule = (
@@ -111,6 +113,7 @@ def problem(B, Hq, Hkv, Nq, Nkv, D, *, dtype=APA_F16, causal=1, scale=0.0, tau=4
     p.kv_capacity = kv_capacity
     p.stat_keys = stat_keys
     p.hot_weight = hot_weight
+    p.ring_tiles = ring_tiles
     if block_table is not None:
         p.block_table = block_table.data_ptr()
         p.block_table_stride = block_table.shape[-1]
@@ -195,6 +198,18 @@ def pass1(p: Problem, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=Non
            "apa_pass1")
 
 
+def ring_pass1(p: Problem, q, k, v, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, lam=None,
+               ws=None, stream=None):
+    """Quantise and pass 1 over a KV window ring.  ws: workspace of
+    workspace_bytes(p, CALL_RING_PASS1) bytes."""
+    _check(lib().apa_ring_pass1(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), float(eps),
+                                _ptr(cold_m), _ptr(cold_l), _ptr(cold_o), _ptr(hot_bits),
+                                _ptr(lam), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)),
+           "apa_ring_pass1")
+
+
 def pass2(p: Problem, q, k, v, fp4, hot_bits, cold_m, cold_l, cold_o, fuse_merge: bool, out=None,
           lse=None, hot_m=None, hot_l=None, hot_o=None, ws=None, stream=None):
     _check(lib().apa_pass2(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), _ptr(hot_bits),
@@ -239,6 +254,7 @@ class Buffers:
     lam: object
     out: object
     lse: object
+    ws_ring: object = None  # KV window ring problems: the ring pass's workspace
 
 
 def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
@@ -259,7 +275,8 @@ def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
         bits=torch.empty(max(hotmask_bytes(p) // 4, 1), dtype=torch.int32, device=device),
         lam=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device) if with_lambda else None,
         out=torch.empty((B, Hq, Nq, D), dtype=odt, device=device),
-        lse=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device))
+        lse=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device),
+        ws_ring=u8(workspace_bytes(p, CALL_RING_PASS1)) if p.ring_tiles > 0 else None)
 
 
 def apa_forward(p: Problem, q, k, v, eps: float, bufs: Buffers, stream=None):

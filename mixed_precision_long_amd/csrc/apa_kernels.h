@@ -16,8 +16,15 @@ struct Geom {
               // keys r + off - window < k <= r + off); 0: none
   int NTc;    // key tiles per (b, kv-head) in the FP4 blob section (capacity >= NT)
   int stat_hi;  // K/V statistics cover keys [first_key_tile * 64, stat_hi)
-  int qt0, qt1; // K/V tiles whose codes a quantise call writes
+  int qt0, qt1; // K/V tiles a quantise call reads (statistics and checks)
+  int ct0, ct1; // K/V tiles whose codes it writes (within [qt0, qt1), or [0, 1))
   int frozen;   // 1: keep the FP4 buffer's K/V statistics (quantise only tiles)
+  int keep_status;  // 1: the call ORs into the status word without clearing it
+  int code_q;       // 1: the call reads and codes Q (0: Q's codes and scales stay)
+  // KV window ring: 0, or the tiles of each of its two halves; the blob
+  // section then holds 1 + 2 * ring slots per (b, kv-head), tile 0 in slot 0
+  // and tile t >= 1 of the segment in use at slot t + ring_delta
+  int ring, ring_delta;
   // paged 16-bit K/V: logical tile t of batch b is page bt[b * bts + t] of
   // pools [pages][Hkv][64][D]; nullptr: [B][Hkv][Nkv][D]
   const int32_t* bt;
@@ -52,6 +59,11 @@ struct Fp4Ptrs {
 };
 
 __host__ __device__ inline size_t blob_bytes(int D) { return (size_t)68 * D; }
+
+// The blob slot of key tile t (see Geom::ring).
+__host__ __device__ inline int blob_slot(const Geom& g, int t) {
+  return g.ring && t ? t + g.ring_delta : t;
+}
 
 // The first key tile any query row sees: 0, or with a sliding window the
 // tile of row 0's first key (Nkv - Nq - window + 1).  K/V statistics and
@@ -113,6 +125,13 @@ size_t pass1_ws_bytes(const Geom& g);
 // tail position of a visit order of npos positions under it (npos: walked
 // whole) and the undecided-tile records kept per unit.
 int pass1_split_info(const Geom& g, int npos, int* cut, int* cap);
+// KV window ring: bytes of the per-unit state kept between segment launches,
+// and one segment launch (tiles [t_lo, t_hi]; first: also tile 0 and the
+// initial state; last: writes the outputs).
+size_t pass1_seg_state_bytes(const Geom& g);
+hipError_t launch_pass1_segment(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                                const Pass1Out& o, void* state, int t_lo, int t_hi, int first,
+                                int last, hipStream_t s);
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                         const Pass1Out& o, void* ws, hipStream_t s);
 

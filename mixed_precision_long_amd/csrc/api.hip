@@ -51,6 +51,7 @@ bool valid_problem(const apa_problem* p) {
   if (p->stat_keys < 0 || p->stat_keys > p->Nkv) return false;
   if (p->block_table && (p->block_table_stride < (p->Nkv + 63) / 64)) return false;
   if (p->hot_weight != 0 && p->hot_weight != 1) return false;
+  if (p->ring_tiles < 0 || p->ring_tiles % 32 != 0) return false;
   return true;
 }
 
@@ -78,7 +79,14 @@ Geom geom(const apa_problem* p) {
   g.stat_hi = p->stat_keys > 0 ? p->stat_keys : p->Nkv;
   g.qt0 = first_key_tile(g);
   g.qt1 = g.NT;
+  g.ct0 = g.qt0;
+  g.ct1 = g.qt1;
   g.frozen = 0;
+  g.keep_status = 0;
+  g.code_q = 1;
+  g.ring = p->ring_tiles;
+  g.ring_delta = 0;
+  if (g.ring) g.NTc = 1 + 2 * g.ring;
   g.bt = p->block_table;
   g.bts = p->block_table_stride;
   g.vweight = p->hot_weight;
@@ -203,6 +211,10 @@ size_t exact_ws(const apa_problem* p, Pass2Args* a, void* base) {
 // D and dtype the device kernels implement for each call
 bool kernels_cover(const apa_problem* p, int call) {
   if (p->fmt != APA_MXFP4) return false;
+  // the ring's blobs are written and walked by apa_ring_pass1 only
+  if (p->ring_tiles > 0 && (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1)) return false;
+  if (call == APA_CALL_RING_PASS1)
+    return p->ring_tiles > 0 && p->D <= 256 && p->window == 0 && p->hot_weight == 0;
   if (p->q_terms == 2 && p->D > 256 && (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1))
     return false;
   if (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1 || call == APA_CALL_MERGE) return true;
@@ -270,6 +282,7 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
   p->block_table = nullptr;
   p->block_table_stride = 0;
   p->hot_weight = 0;
+  p->ring_tiles = 0;
 }
 
 const char* apa_last_hip_error(void) { return hipGetErrorString(g_last_hip); }
@@ -311,6 +324,10 @@ size_t apa_workspace_bytes(const apa_problem* p, int32_t which) {
     case APA_CALL_PASS1: return pass1_ws_bytes(geom(p));
     case APA_CALL_PASS2: return pass2_ws(p, nullptr, nullptr);
     case APA_CALL_EXACT: return exact_ws(p, nullptr, nullptr);
+    case APA_CALL_RING_PASS1:
+      return p->ring_tiles > 0 ? align256(quant_ws(p, nullptr, nullptr)) +
+                                     pass1_seg_state_bytes(geom(p))
+                               : 0;
     default: return 0;
   }
 }
@@ -342,8 +359,8 @@ apa_status apa_quantize_tiles(const apa_problem* p, const void* q, const void* k
   const size_t need = quant_ws(p, nullptr, nullptr);
   if (!ws || ws_bytes < need) return APA_ERR_WORKSPACE;
   g.frozen = 1;
-  g.qt0 = tile_begin;
-  g.qt1 = tile_end;
+  g.qt0 = g.ct0 = tile_begin;
+  g.qt1 = g.ct1 = tile_end;
   QuantWs w;
   quant_ws(p, &w, ws);
   w.ch0 = tile_begin / 16;
@@ -384,6 +401,102 @@ apa_status apa_pass1(const apa_problem* p, const void* fp4, float eps, int32_t* 
   return hip_status(launch_pass1(geom(p), fp4_ptrs(p, fp4), eps, p->tau,
                                  (int)p->hot_frame_offset, o, need > 0 ? ws : nullptr,
                                  (hipStream_t)stream));
+}
+
+namespace {
+
+// The stream each device's ring quantisation runs on (created on first use,
+// default priority, never blocking the null stream).
+std::mutex g_ring_mu;
+hipStream_t g_ring_stream[kMaxDevices] = {};
+
+hipError_t ring_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  if (!g_ring_stream[dev]) {
+    e = hipStreamCreateWithFlags(&g_ring_stream[dev], hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+  }
+  *out = g_ring_stream[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+apa_status apa_ring_pass1(const apa_problem* p, const void* q, const void* k, const void* v,
+                          void* fp4, float eps, int32_t* cold_m, float* cold_l, float* cold_o,
+                          uint32_t* hot_bits, float* lambda_out, void* ws, size_t ws_bytes,
+                          void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4 || !cold_m || !cold_l || !cold_o || !hot_bits)
+    return APA_ERR_INVALID_ARG;
+  if (isnan(eps) || eps < 0.0f) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_RING_PASS1)) return APA_ERR_UNSUPPORTED;
+  if (p->B == 0 || p->Hkv == 0) return APA_OK;
+  const size_t qbytes = align256(quant_ws(p, nullptr, nullptr));
+  const Geom g0 = geom(p);
+  if (!ws || ws_bytes < qbytes + pass1_seg_state_bytes(g0)) return APA_ERR_WORKSPACE;
+  QuantWs w;
+  quant_ws(p, &w, ws);
+  uint8_t* state = static_cast<uint8_t*>(ws) + qbytes;
+  const Fp4Ptrs f = fp4_ptrs(p, fp4);
+  const hipStream_t ps = (hipStream_t)stream;
+  clear_hip_error();
+  hipStream_t qs;
+  hipError_t e = ring_stream(&qs);
+  if (e != hipSuccess) return hip_status(e);
+  // 1. statistics over every key, Q's codes, the sink tile's codes
+  Geom gs = g0;
+  gs.ct0 = 0;
+  gs.ct1 = g0.NT > 0 ? 1 : 0;
+  e = launch_quantize(gs, q, k, v, f, w, ps);
+  if (e != hipSuccess || empty(p)) return hip_status(e);
+  // 2. the segments, top down: segment s holds tiles [s R, s R + R), tile 0
+  // excepted, in ring half s % 2; the walk of s waits for its codes, the codes
+  // of s wait for the walk of s + 2 (the last reader of that half)
+  const int R = p->ring_tiles;
+  const int top = (g0.NT - 1) / R;
+  hipEvent_t ev_stats = nullptr, ev_q[2] = {}, ev_p[2] = {};
+  auto make = [&](hipEvent_t* x) {
+    return e == hipSuccess ? (e = hipEventCreateWithFlags(x, hipEventDisableTiming)) : e;
+  };
+  for (hipEvent_t* x : {&ev_stats, &ev_q[0], &ev_q[1], &ev_p[0], &ev_p[1]}) (void)make(x);
+  if (e == hipSuccess) e = hipEventRecord(ev_stats, ps);
+  if (e == hipSuccess) e = hipStreamWaitEvent(qs, ev_stats, 0);
+  Pass1Out o = {cold_m, cold_l, cold_o, hot_bits, lambda_out};
+  for (int sgm = top; sgm >= 0 && e == hipSuccess; --sgm) {
+    const int h = sgm & 1;
+    Geom gq = g0;
+    gq.frozen = 1;
+    gq.keep_status = 1;
+    gq.code_q = 0;
+    gq.qt0 = sgm * R;
+    gq.qt1 = gq.ct1 = min(g0.NT, sgm * R + R);
+    // tile 0 stays in its sink slot from step 1 (the first walk may still be
+    // reading it while segment 0 is coded)
+    gq.ct0 = sgm == 0 ? min(1, gq.ct1) : sgm * R;
+    gq.ring_delta = 1 + h * R - sgm * R;
+    QuantWs wq = w;
+    wq.ch0 = gq.qt0 / 16;
+    wq.ch1 = (gq.qt1 + 15) / 16;
+    if ((e = hipStreamWaitEvent(qs, ev_p[h], 0)) != hipSuccess) break;
+    if ((e = launch_quantize(gq, q, k, v, f, wq, qs)) != hipSuccess) break;
+    if ((e = hipEventRecord(ev_q[h], qs)) != hipSuccess) break;
+    if ((e = hipStreamWaitEvent(ps, ev_q[h], 0)) != hipSuccess) break;
+    Geom gp = g0;
+    gp.ring_delta = gq.ring_delta;
+    if ((e = launch_pass1_segment(gp, f, eps, p->tau, (int)p->hot_frame_offset, o, state,
+                                  sgm * R, sgm * R + R - 1, sgm == top, sgm == 0, ps)) !=
+        hipSuccess)
+      break;
+    e = hipEventRecord(ev_p[h], ps);
+  }
+  for (hipEvent_t x : {ev_stats, ev_q[0], ev_q[1], ev_p[0], ev_p[1]})
+    if (x) (void)hipEventDestroy(x);
+  return hip_status(e);
 }
 
 int32_t apa_pass1_split(const apa_problem* p, int32_t npos, int32_t* cut, int32_t* records) {

@@ -294,6 +294,7 @@ struct CtxBase {
   float g_v;
   const cfloat* tw;  // value-norm weights of the kv-head's tiles (nullptr: mass test)
   uint32_t *bits0, *bits1;  // hot words of the two verdict groups
+  int ring_delta;  // window ring: blob slot of tile t >= 1 is t + ring_delta
   // the visit order: positions [0, npos()), position p at tile tile_of(p)
   __device__ __forceinline__ int npos() const { return dW + 1 - lo0; }
   __device__ __forceinline__ int tile_of(int p) const { return sh && p == 0 ? 0 : dW + sh - p; }
@@ -354,7 +355,8 @@ __device__ __forceinline__ void make_ctx(CtxBase<D>& c, const Geom& g, const Fp4
   c.g_v = f.kv_head[c.bhk * 8 + 4];
   c.tw = g.vweight ? (const cfloat*)(f.tile_w + c.bhk * (size_t)g.NTc) : nullptr;
   c.blobs = blob_rsrc(f.kv_blob + c.bhk * (size_t)g.NTc * Tile<D>::BLOB,
-                      (uint32_t)g.NT * Tile<D>::BLOB);
+                      (uint32_t)(g.ring ? g.NTc : g.NT) * Tile<D>::BLOB);
+  c.ring_delta = g.ring_delta;
   c.koff = n * (D / 2) + 16 * hh;
   c.ksoff = 32 * D + n * (D / 32);
   constexpr int NDO = Tile<D>::NDO;
@@ -665,7 +667,7 @@ __device__ __forceinline__ void assemble_words(const CtxBase<D>& c, Words& wd, c
 // return 0.  A head walk publishes its lambda from position nrep_tail on in
 // `pub_out`, in the state frame it had there (the frame the tail's replay ends
 // in).
-template <int D, bool LOG, bool TAIL, bool VW, int QT>
+template <int D, bool LOG, bool TAIL, bool VW, int QT, bool RING = false>
 __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& st, Words& wd, int nrep,
                                     int p0, int cnt, float eps, float tau, float Hf, const Cand& cr,
                                     int cap, const volatile lds_float* pub_in,
@@ -695,7 +697,10 @@ __device__ __forceinline__ int walk(const Geom& g, const Ctx<D, QT>& c, St<D>& s
   // into kn; once its P V product is issued, V^T of position i+1 is fetched
   // into va (prefetches past the last position re-read the last tile: in
   // bounds, unused)
-  auto next_blob = [&](int i) { return (uint32_t)(tile_at(min(i, cnt - 1)) * BLOB); };
+  auto next_blob = [&](int i) {
+    const int t = tile_at(min(i, cnt - 1));
+    return (uint32_t)((RING && t ? t + c.ring_delta : t) * BLOB);
+  };
   KOps<D> kn;
   v16f acc[2];
   v4i va[ND];
@@ -1325,6 +1330,62 @@ __global__ __launch_bounds__(64) void k_pass1_rewalk(Geom g, Fp4Ptrs f, float ep
   store_state<D>(g, c, out, st, lane);
 }
 
+// KV window ring ("What else is in the box": the FP4 copy of K and V kept to
+// a sink tile and two ring halves): the walk of every unit cut at fixed key
+// tile ranges [t_lo, t_hi], one launch per range from the top down, so that
+// only the range being walked needs FP4 blobs (the next one is coded into the
+// other half meanwhile).  A launch walks each unit's positions whose tiles lie
+// in the range (a contiguous run of its visit order: 0, d, d-1, ..., 1); the
+// first launch also takes tile 0 and starts the state, the last writes the
+// outputs; in between each unit's state waits in the workspace (the hand-off
+// layout of the split schedules).  The same walk over the same positions in
+// the same order as one unbroken walk: the same verdicts, state and outputs.
+// One wave per unit (no value-norm weights, no window, D <= 256).
+template <int D, bool LOG, int QT>
+__global__ __launch_bounds__(64) void k_pass1_seg(Geom g, Fp4Ptrs f, float eps, float tau,
+                                                  int hoff, Pass1Out out, uint8_t* state,
+                                                  int t_lo, int t_hi, int first, int last) {
+  const int lane = threadIdx.x;
+  Ctx<D, QT> c;
+  make_ctx<D>(c, g, f, out, unit_id(g, blockIdx.x), lane);
+  load_q2<D>(c, g, f, lane);
+  // the unit's positions of tiles [a, b]: dW + 1 - b .. dW + 1 - a; with
+  // tile 0 first in the first launch (then b == dW whenever a <= dW, since
+  // the first range holds the highest diagonal)
+  const int a = max(t_lo, 1), b = min(t_hi, c.dW);
+  int p0 = b >= a ? c.dW + 1 - b : 0;
+  int cnt = b >= a ? b - a + 1 : 0;
+  if (first) {
+    p0 = 0;
+    cnt += 1;
+  }
+  float* slot = reinterpret_cast<float*>(state + (size_t)blockIdx.x * handoff_bytes(D));
+  St<D> st;
+  Words wd = {-1, 0u, 0u, 0u, 0u};
+  if (first) {
+    init_state<D>(st, c.row_ok);
+    zero_outside<D>(g, c, lane);
+  } else {
+    load_state<D>(slot, st, wd, lane);
+    wd.wb = -1;
+  }
+  if (cnt > 0) {
+    __shared__ uint8_t vlog_sh[LOG ? kLogTiles : 1];
+    walk<D, LOG, false, false, QT, true>(g, c, st, wd, 0, p0, cnt, eps, tau, (float)hoff,
+                                         cand_of(f.kv_blob, 0, 0, D), 0, nullptr, nullptr,
+                                         (lds_u8*)vlog_sh, lane);
+  }
+  if (!last) {
+    save_state<D>(slot, st, wd, lane);
+    return;
+  }
+  if (lane == 0 && c.lead) {
+    c.bits0[0] = wd.p00;
+    if (c.has_g1) c.bits1[0] = wd.p01;
+  }
+  store_state<D>(g, c, out, st, lane);
+}
+
 // The schedule a launch with a workspace runs: the caller's, else two waves
 // per unit while those fit the GPU's wave slots at once, four waves per three
 // units while those do, else one wave per unit (then there is no workspace).
@@ -1427,7 +1488,46 @@ hipError_t run(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
   return run_qt<D, 1>(g, f, eps, tau, hoff, o, ws, s);
 }
 
+template <int D, int QT>
+hipError_t run_seg(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                   const Pass1Out& o, void* state, int t_lo, int t_hi, int first, int last,
+                   hipStream_t s) {
+  const int nunits = g.B * g.Hkv * (g.NqP / 32) * g.G;
+  if (nunits == 0) return hipSuccess;
+  uint8_t* st = static_cast<uint8_t*>(state);
+  if (g.NT <= kLogTiles)
+    hipLaunchKernelGGL((k_pass1_seg<D, true, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+                       hoff, o, st, t_lo, t_hi, first, last);
+  else
+    hipLaunchKernelGGL((k_pass1_seg<D, false, QT>), dim3(nunits), dim3(64), 0, s, g, f, eps, tau,
+                       hoff, o, st, t_lo, t_hi, first, last);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_seg_d(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                     const Pass1Out& o, void* state, int t_lo, int t_hi, int first, int last,
+                     hipStream_t s) {
+  if (g.qterms == 2) return run_seg<D, 2>(g, f, eps, tau, hoff, o, state, t_lo, t_hi, first, last, s);
+  return run_seg<D, 1>(g, f, eps, tau, hoff, o, state, t_lo, t_hi, first, last, s);
+}
+
 }  // namespace
+
+size_t pass1_seg_state_bytes(const Geom& g) {
+  return (size_t)g.B * g.Hkv * (g.NqP / 32) * g.G * handoff_bytes(g.D);
+}
+
+hipError_t launch_pass1_segment(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                                const Pass1Out& o, void* state, int t_lo, int t_hi, int first,
+                                int last, hipStream_t s) {
+  switch (g.D) {
+    case 64: return run_seg_d<64>(g, f, eps, tau, hoff, o, state, t_lo, t_hi, first, last, s);
+    case 128: return run_seg_d<128>(g, f, eps, tau, hoff, o, state, t_lo, t_hi, first, last, s);
+    case 256: return run_seg_d<256>(g, f, eps, tau, hoff, o, state, t_lo, t_hi, first, last, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_pass1(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                         const Pass1Out& o, void* ws, hipStream_t s) {

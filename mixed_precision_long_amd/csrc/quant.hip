@@ -250,7 +250,7 @@ __device__ void v_items(const T* __restrict__ V, const Geom& g, const QuantWs& w
         out[j] = w;
       }
       const int ch = c0 + c;
-      uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + t) * blob_bytes(D);
+      uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + blob_slot(g, t)) * blob_bytes(D);
       *reinterpret_cast<uint4*>(blob + 34 * D + ch * 32 + half * 16) =
           uint4{out[0], out[1], out[2], out[3]};
       blob[66 * D + ((ch % 32) * 2 + half) * (D / 32) + ch / 32] = (uint8_t)(e + 127);
@@ -384,11 +384,12 @@ __device__ void finalize_kq(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, 
   {
     for (int c = ws.ch0 + d; c < ws.ch1; c += nthr) badf |= ws.flags[(size_t)bh * ws.nch + c];
     const size_t q0 = ((size_t)b * g.Hq + (size_t)hk * g.G) * ws.nqt;
-    for (int i = d; i < g.G * ws.nqt; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
+    const int nq = g.code_q ? g.G * ws.nqt : 0;  // Q's flags and maxima, when Q was read
+    for (int i = d; i < nq; i += nthr) badf |= ws.flags[qflag0(g, ws) + q0 + i];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       qa[i] = 0.0f;
-      if (i < g.G)
+      if (i < g.G && g.code_q)
         for (int t = d; t < ws.nqt; t += nthr) qa[i] = fmaxf(qa[i], ws.qamax[q0 + (size_t)i * ws.nqt + t]);
     }
   }
@@ -449,6 +450,8 @@ __device__ void finalize_kq(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, 
   // Q heads of this group: inv_q = w * 2^-j, w = fl32(sl * g_k), j the
   // smallest integer with amax_q * w <= 6 * 2^j.  The first eight heads' max
   // |Q| were loaded above; further heads (groups above 8) load theirs here.
+  // A call that leaves Q as it is (the ring's later segments) keeps them.
+  if (!g.code_q) return;
   const float w = g.sl * gk;
   auto q_scale = [&](int i, float qv) {
     const size_t bq = (size_t)b * g.Hq + hk * g.G + i;
@@ -487,8 +490,8 @@ __device__ void finalize_v(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, i
   unsigned badf = 0u;
   float va = 0.0f;
   {
-    const size_t i0 = ((size_t)bh * g.NT + g.qt0) * ws.nvz;
-    const int n = (g.qt1 - g.qt0) * ws.nvz;
+    const size_t i0 = ((size_t)bh * g.NT + g.ct0) * ws.nvz;
+    const int n = (g.ct1 - g.ct0) * ws.nvz;
 #pragma unroll 4
     for (int i = d; i < n; i += nthr) {
       va = fmaxf(va, ws.vamax[i0 + i]);
@@ -501,10 +504,10 @@ __device__ void finalize_v(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, i
   if (g.vweight) {
     if (!g.frozen) {
       // thread d sums tiles [qt0 + d * run, qt0 + (d + 1) * run), ascending
-      const int n = g.qt1 - g.qt0, run = (n + nthr - 1) / nthr;
+      const int n = g.ct1 - g.ct0, run = (n + nthr - 1) / nthr;
       double sv = 0.0;
       for (int i = d * run; i < min(n, (d + 1) * run); ++i)
-        sv += ws.vnst[(size_t)bh * g.NT + g.qt0 + i];
+        sv += ws.vnst[(size_t)bh * g.NT + g.ct0 + i];
       part[d] = sv;
     }
     __syncthreads();
@@ -520,7 +523,7 @@ __device__ void finalize_v(const Geom& g, const QuantWs& ws, const Fp4Ptrs& f, i
     }
     __syncthreads();
     const float nb = *nbs;
-    for (int t = g.qt0 + d; t < g.qt1; t += nthr) {
+    for (int t = g.ct0 + d; t < g.ct1; t += nthr) {
       const float nt = ws.vnt[(size_t)bh * g.NT + t];
       f.tile_w[(size_t)bh * g.NTc + t] = nb > 0.0f ? fmaxf(1.0f, nt / nb) : 1.0f;
     }
@@ -672,7 +675,7 @@ __device__ void quant_rows(const uint4 raw, const Geom& g, const Fp4Ptrs& f, int
     crow = f.q_codes + r * (g.D / 2);
     srow = f.q_scales + r * (g.D / 32);
   } else {
-    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + row / kTile) * blob_bytes(g.D);
+    uint8_t* blob = f.kv_blob + ((size_t)bh * g.NTc + blob_slot(g, row / kTile)) * blob_bytes(g.D);
     crow = blob + (row % kTile) * (g.D / 2);
     srow = blob + 32 * g.D + (row % kTile) * (g.D / 32);
   }
@@ -716,7 +719,7 @@ __global__ __launch_bounds__(512) void k_stats(const T* __restrict__ Q, const T*
                                                Geom g, QuantWs ws, Fp4Ptrs f, int nkb) {
   extern __shared__ double sh[];
   __shared__ float red[16];
-  if (blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+  if (!g.keep_status && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
   const int bx = blockIdx.x;
   if (bx < nkb) {
     const int nc = ws.ch1 - ws.ch0;  // the chunks of the tiles read
@@ -745,16 +748,16 @@ __global__ __launch_bounds__(256) void k_vcode(const T* __restrict__ V, Geom g, 
   __shared__ float knu[kTile];  // a tile's key norms
   if ((int)blockIdx.x < nfin) {
     float* xch = reinterpret_cast<float*>(tile);  // [2][D] (D <= 128)
-    if (clear && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+    if (clear && !g.keep_status && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
     finalize_kq(g, ws, f, blockIdx.x, xch, red);
     return;
   }
   const int blk = blockIdx.x - nfin;
-  const int ngrp = (g.qt1 - g.qt0 + kVTiles - 1) / kVTiles;
+  const int ngrp = (g.ct1 - g.ct0 + kVTiles - 1) / kVTiles;
   const int per_head = ngrp * ws.nvz;
   const int r = blk % per_head;
-  const int t0 = g.qt0 + (r / ws.nvz) * kVTiles;
-  v_items<T>(V, g, ws, f, blk / per_head, t0, min(kVTiles, g.qt1 - t0), r % ws.nvz, tile, red,
+  const int t0 = g.ct0 + (r / ws.nvz) * kVTiles;
+  v_items<T>(V, g, ws, f, blk / per_head, t0, min(kVTiles, g.ct1 - t0), r % ws.nvz, tile, red,
              knu);
 }
 
@@ -765,7 +768,7 @@ __global__ void k_finalize(Geom g, QuantWs ws, Fp4Ptrs f, int clear) {
   __shared__ float red[16];
   __shared__ float nbs;           // nu_bar
   __shared__ double part[1024];   // the threads' runs of tile norm sums
-  if (clear && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
+  if (clear && !g.keep_status && blockIdx.x == 0 && threadIdx.x == 0) *f.status = 0u;
   finalize_kq(g, ws, f, blockIdx.x, xch, red);
   __syncthreads();
   finalize_v(g, ws, f, blockIdx.x, red, &nbs, part);
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(256) void k_quant(const T* __restrict__ Q, const T*
   b -= nq;
   // the head's sub-blocks [qt0 * kpt, qt1 * kpt) (16-row groups at D = 128),
   // kSubs consecutive ones per block, across tile boundaries
-  const int s_lo = g.qt0 * kpt, s_hi = g.qt1 * kpt;
+  const int s_lo = g.ct0 * kpt, s_hi = g.ct1 * kpt;
   const int per_head = (s_hi - s_lo + kSubs - 1) / kSubs;
   const int bh = g.B * g.Hkv - 1 - b / per_head;
   const int s0 = s_lo + (b % per_head) * kSubs;
@@ -836,8 +839,8 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
     stats_attr = true;
   }
   const int nkb = g.Nkv > 0 ? (ws.ch1 - ws.ch0) * nkvh : 0;
-  const int nvb = g.Nkv > 0 ? (g.qt1 - g.qt0 + kVTiles - 1) / kVTiles * ws.nvz * nkvh : 0;
-  const int nqb = g.Nq > 0 ? ws.nqt * g.B * g.Hq : 0;
+  const int nvb = g.Nkv > 0 ? (g.ct1 - g.ct0 + kVTiles - 1) / kVTiles * ws.nvz * nkvh : 0;
+  const int nqb = g.Nq > 0 && g.code_q ? ws.nqt * g.B * g.Hq : 0;
   if (nkb + nqb > 0)
     hipLaunchKernelGGL(k_stats<T>, dim3(nkb + nqb), dim3(min(2 * g.D, 512)), stats_lds, s, q, k,
                        g, ws, f, nkb);
@@ -855,8 +858,8 @@ hipError_t run_quantize(const Geom& g, const T* q, const T* k, const T* v, const
   // sub-blocks of 256; Q: qpb sub-blocks per head
   const int kpt = g.D / 32;
   const int qpb = (int)(((long)g.NqP * (g.D / 8) + 255) / 256);
-  const long nq = (long)((qpb + kSubs - 1) / kSubs) * g.B * g.Hq;
-  const long nblk = nfin + nq + (long)nkvh * (((g.qt1 - g.qt0) * kpt + kSubs - 1) / kSubs);
+  const long nq = g.code_q ? (long)((qpb + kSubs - 1) / kSubs) * g.B * g.Hq : 0;
+  const long nblk = nfin + nq + (long)nkvh * (((g.ct1 - g.ct0) * kpt + kSubs - 1) / kSubs);
   if (nblk > 0)
     hipLaunchKernelGGL(k_quant<T>, dim3((unsigned)nblk), dim3(256), 0, s, q, k, g, f, ws, kpt,
                        qpb, (int)nq, nfin);

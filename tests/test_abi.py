@@ -88,7 +88,8 @@ def test_sizes_and_layout():
     ("scale", float("nan")), ("fmt", 9), ("pass1_schedule", -1), ("pass1_schedule", 4),
     ("q_terms", 0), ("q_terms", 3), ("k_scale_lsq", 2), ("window", -1),
     ("window+noncausal", 4096), ("kv_capacity", 1000), ("kv_capacity", -1),
-    ("stat_keys", -1), ("stat_keys", 200000), ("block_table_stride", 1000)])
+    ("stat_keys", -1), ("stat_keys", 200000), ("block_table_stride", 1000),
+    ("ring_tiles", -32), ("ring_tiles", 96 + 16)])
 def test_invalid_problems_are_rejected(field, value):
     if field == "window+noncausal":
         p = prob(window=value, is_causal=0)  # a sliding window needs the causal mask
@@ -261,3 +262,37 @@ def test_quantize_tiles_validates_its_range():
     first = (122880 - 2048 - 4096 + 1) // 64
     assert L.apa_quantize_tiles(C.byref(pw), FAKE, FAKE, FAKE, FAKE, first - 1, 1920, FAKE,
                                 need, None) == apa.APA_ERR_INVALID_ARG
+
+
+def test_ring_problems():
+    """A KV window ring: the FP4 buffer holds 1 + 2R tile blobs per kv-head
+    whatever Nkv is; only apa_ring_pass1 fills and walks them; it needs
+    D <= 256, no window and the mass test; its workspace is the quantise
+    scratch and a hand-off state per 32-row block and query head."""
+    L = apa.lib()
+    p = prob()  # 2048 x 122880, 24 over 8 heads, D = 128
+    r = prob(ring_tiles=96)
+    lay, lr = apa.fp4_layout(p), apa.fp4_layout(r)
+    blob = 68 * 128
+    assert lr.kbar - lr.kv_blobs >= 8 * 193 * blob > lr.kbar - lr.kv_blobs - 256
+    assert apa.fp4_bytes(p) - apa.fp4_bytes(r) >= 8 * (1920 - 193) * blob - 4096
+    for call in (lambda x: L.apa_quantize(C.byref(x), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None),
+                 lambda x: L.apa_quantize_tiles(C.byref(x), FAKE, FAKE, FAKE, FAKE, 0, 1, FAKE,
+                                                1 << 40, None),
+                 lambda x: L.apa_pass1(C.byref(x), FAKE, 0.01, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                       1 << 40, None)):
+        assert call(r) == apa.APA_ERR_UNSUPPORTED
+    ring = lambda x, nbytes: L.apa_ring_pass1(C.byref(x), FAKE, FAKE, FAKE, FAKE, 0.01, FAKE, FAKE,
+                                              FAKE, FAKE, None, FAKE, nbytes, None)
+    assert ring(p, 1 << 40) == apa.APA_ERR_UNSUPPORTED  # no ring in the problem
+    for kw in ({"D": 512}, {"window": 4096}, {"hot_weight": 1}):
+        assert ring(prob(ring_tiles=96, **kw), 1 << 40) == apa.APA_ERR_UNSUPPORTED, kw
+    need = apa.workspace_bytes(r, apa.CALL_RING_PASS1)
+    units = 8 * 64 * 3
+    state = units * ((128 * 128 + 1040 + 255) // 256 * 256)
+    qneed = (apa.workspace_bytes(r, apa.CALL_QUANTIZE) + 255) // 256 * 256
+    assert need == qneed + state
+    assert apa.workspace_bytes(p, apa.CALL_RING_PASS1) == 0
+    assert ring(r, need - 1) == apa.APA_ERR_WORKSPACE
+    assert L.apa_ring_pass1(C.byref(r), FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, FAKE,
+                            FAKE, None, FAKE, need, None) == apa.APA_ERR_INVALID_ARG
