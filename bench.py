@@ -211,6 +211,8 @@ def main():
                     help="skip timing the accuracy variants (two-term Q, least-squares K scales)")
     ap.add_argument("--no-window", action="store_true",
                     help="skip timing the sliding-window variant (4096 keys)")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip timing the KV window ring (sink tile + two halves of 96 tiles)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="before warmup, run one plain device-to-device copy of MIB MiB (a "
                          "known-size kernel that scales the HBM byte counters)")
@@ -480,6 +482,44 @@ def main():
             "page_ms_window_vs_causal": [0.804, 6.053]}
         del bw
         print("[bench] window %d: %.3f ms (exact %.3f)" % (W, tot, ewms), file=sys.stderr,
+              flush=True)
+
+    if not args.no_ring and w.D <= 256:
+        # the page's KV window ring: the FP4 K/V copy held to a sink tile plus
+        # two halves of 96 tiles per KV head, segments coded on a second
+        # stream while pass 1 walks the previous one; the same step otherwise
+        R = 96
+        pr = apa.problem(w.B, w.Hq, w.Hkv, w.Nq, w.Nkv, w.D,
+                         dtype=apa.APA_F16 if w.dtype == "fp16" else apa.APA_BF16,
+                         scale=w.scale, ring_tiles=R)
+        br = apa.alloc(pr)
+        evr = []
+        for i in range(10 + 20):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            apa.ring_pass1(pr, q, k, v, br.fp4, eps, br.cold_m, br.cold_l, br.cold_o, br.bits,
+                           None, ws=br.ws_ring, stream=stream)
+            e[1].record(stream)
+            apa.pass2(pr, q, k, v, br.fp4, br.bits, br.cold_m, br.cold_l, br.cold_o, True,
+                      out=br.out, lse=br.lse, ws=br.ws_p2, stream=stream)
+            e[2].record(stream)
+            if i >= 10:
+                evr.append(e)
+        torch.cuda.synchronize()
+        cos_r = torch.nn.functional.cosine_similarity(br.out.float().reshape(-1, w.D),
+                                                      out.reshape(-1, w.D), dim=1)
+        res["kv_window_ring"] = {
+            "ring_tiles": R,
+            "ms": round(float(np.mean([x[0].elapsed_time(x[2]) for x in evr])), 4),
+            "kernels_ms": {"quantize+pass1": round(float(np.mean([x[0].elapsed_time(x[1])
+                                                                  for x in evr])), 4),
+                           "pass2": round(float(np.mean([x[1].elapsed_time(x[2]) for x in evr])),
+                                          4)},
+            "fp4_bytes": apa.fp4_bytes(pr), "fp4_bytes_without_ring": apa.fp4_bytes(p),
+            "page_fp4_mib": 13.6,
+            "vs_main_output_cos_min": round(float(cos_r.min()), 6)}
+        del br
+        print("[bench] ring %d: %.3f ms" % (R, res["kv_window_ring"]["ms"]), file=sys.stderr,
               flush=True)
 
     if not args.no_cpu:

@@ -1346,8 +1346,10 @@ __global__ __launch_bounds__(64) void k_pass1_seg(Geom g, Fp4Ptrs f, float eps, 
                                                   int hoff, Pass1Out out, uint8_t* state,
                                                   int t_lo, int t_hi, int first, int last) {
   const int lane = threadIdx.x;
+  // units of one kv-head on one XCD, so its L2 holds that head's segment
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
   Ctx<D, QT> c;
-  make_ctx<D>(c, g, f, out, unit_id(g, blockIdx.x), lane);
+  make_ctx<D>(c, g, f, out, unit_id(g, u), lane);
   load_q2<D>(c, g, f, lane);
   // the unit's positions of tiles [a, b]: dW + 1 - b .. dW + 1 - a; with
   // tile 0 first in the first launch (then b == dW whenever a <= dW, since
@@ -1359,7 +1361,7 @@ __global__ __launch_bounds__(64) void k_pass1_seg(Geom g, Fp4Ptrs f, float eps, 
     p0 = 0;
     cnt += 1;
   }
-  float* slot = reinterpret_cast<float*>(state + (size_t)blockIdx.x * handoff_bytes(D));
+  float* slot = reinterpret_cast<float*>(state + (size_t)u * handoff_bytes(D));
   St<D> st;
   Words wd = {-1, 0u, 0u, 0u, 0u};
   if (first) {
