@@ -16,9 +16,11 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are caller-owned DEVICE pointers.  The library never
- *     allocates, frees or synchronises; calls are enqueued on `stream` (a
- *     hipStream_t passed as void*, NULL = the null stream) and run in stream
- *     order.
+ *     allocates device memory, frees or synchronises; calls are enqueued on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream) and run
+ *     in stream order.  apa_ring_pass1 alone also enqueues work on a second
+ *     stream the library creates once per device, ordered against `stream`
+ *     by events it creates and releases within the call.
  *   - The return value is synchronous validation plus launch status.  On any
  *     non-APA_OK return nothing was enqueued, except APA_ERR_HIP, which reports
  *     a failed launch (earlier kernels of the same call may have run).
