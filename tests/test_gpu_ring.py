@@ -101,3 +101,39 @@ def test_ring_long3b():
     print("[ring long3b] FP4 buffer %d MB against %d MB" % (res["ring"]["fp4_bytes"] >> 20,
                                                            res["ref"]["fp4_bytes"] >> 20),
           flush=True)
+
+
+def test_ring_over_paged_kv():
+    """The ring reads its 16-bit K/V through a block table like every other
+    call: paged pools (unused slots NaN) give the flat ring's results bit for
+    bit, with a clean status word."""
+    from test_gpu_chunked import _pages
+    B, Hq, Hkv, Nq, Nkv, D, R = 2, 6, 2, 160, 7000, 128, 32
+    w = small_workload(B, Hq, Hkv, Nq, Nkv, D, seed=93)
+    Q, K, V = make_inputs(w)
+    NT = -(-Nkv // 64)
+    npages = B * NT + 3
+    perm = np.random.default_rng(4).permutation(npages)[:B * NT].reshape(B, NT).astype(np.int32)
+    bt = torch.from_numpy(np.ascontiguousarray(perm)).cuda()
+    kp, vp = (_pages(x, B, Hkv, Nkv, D, perm, npages, torch.float16) for x in (K, V))
+    q = torch.from_numpy(Q).half().cuda()
+    kf, vf = (torch.from_numpy(x).half().cuda() for x in (K, V))
+    eps = 0.01
+    outs = []
+    for kk, vv, table in ((kf, vf, None), (kp, vp, bt)):
+        p = apa.problem(B, Hq, Hkv, Nq, Nkv, D, scale=w.scale, ring_tiles=R, block_table=table)
+        b = apa.alloc(p, with_lambda=True)
+        apa.ring_pass1(p, q, kk, vv, b.fp4, eps, b.cold_m, b.cold_l, b.cold_o, b.bits, b.lam,
+                       ws=b.ws_ring)
+        apa.pass2(p, q, kk, vv, b.fp4, b.bits, b.cold_m, b.cold_l, b.cold_o, True, out=b.out,
+                  lse=b.lse, ws=b.ws_p2)
+        torch.cuda.synchronize()
+        outs.append(dict(m=b.cold_m.cpu().numpy(), o=b.cold_o.cpu().numpy(),
+                         bits=b.bits.cpu().numpy(), out=b.out.float().cpu().numpy(),
+                         sec=_sections(p, b.fp4)))
+    a, c = outs
+    for key in ("m", "o", "bits", "out"):
+        assert np.array_equal(np.nan_to_num(a[key]), np.nan_to_num(c[key])), key
+    for key in a["sec"]:
+        assert np.array_equal(a["sec"][key], c["sec"][key]), key
+    assert int(c["sec"]["status"].view(np.uint32)[0]) == 0
