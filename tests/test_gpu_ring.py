@@ -123,6 +123,7 @@ def test_ring_over_paged_kv():
     for kk, vv, table in ((kf, vf, None), (kp, vp, bt)):
         p = apa.problem(B, Hq, Hkv, Nq, Nkv, D, scale=w.scale, ring_tiles=R, block_table=table)
         b = apa.alloc(p, with_lambda=True)
+        b.fp4.zero_()  # the sections' alignment padding is never written
         apa.ring_pass1(p, q, kk, vv, b.fp4, eps, b.cold_m, b.cold_l, b.cold_o, b.bits, b.lam,
                        ws=b.ws_ring)
         apa.pass2(p, q, kk, vv, b.fp4, b.bits, b.cold_m, b.cold_l, b.cold_o, True, out=b.out,
