@@ -175,7 +175,8 @@ void apa_problem_init(apa_problem* p, int32_t B, int32_t Hq, int32_t Hkv, int32_
  *                                    rest untouched)
  *   q_head   [B][Hq][4]  float       amax_Q, inv_Q, j (as float: alpha = 2^j), 0
  *   q_frame  [B][Hq][NqP] float      c_r = sl * q.kbar, sl = fl32(scale*log2 e)
- *   status   uint32                  bit 0: a non-finite input was seen
+ *   status   uint32                  bit 0: a non-finite input was seen;
+ *                                    bit 1: a wait of apa_fused gave up
  *   q2_codes, q2_scales               with q_terms = 2: the residual term of Q,
  *            laid out as q_codes and q_scales: per 32-channel block, the
  *            FP32 residual of the normalised values after the first term's
@@ -194,7 +195,7 @@ size_t apa_fp4_bytes(const apa_problem* p);
 size_t apa_hotmask_bytes(const apa_problem* p);
 
 enum { APA_CALL_QUANTIZE = 0, APA_CALL_PASS1 = 1, APA_CALL_PASS2 = 2, APA_CALL_MERGE = 3,
-       APA_CALL_EXACT = 4, APA_CALL_RING_PASS1 = 5 };
+       APA_CALL_EXACT = 4, APA_CALL_RING_PASS1 = 5, APA_CALL_FUSED = 6 };
 /* Scratch bytes the given call needs in its `ws` argument (0: pass NULL). */
 size_t apa_workspace_bytes(const apa_problem* p, int32_t which_call);
 
@@ -342,6 +343,28 @@ apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const v
                      const void* fp4, const uint32_t* hot_bits, const int32_t* cold_m,
                      const float* cold_l, const float* cold_o, int32_t fuse_merge, void* out,
                      float* lse, float* hot_m, float* hot_l, float* hot_o, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* f1: pass 1 and pass 2 (with the fused merge) in one persistent launch
+ * ("Pass 2: exact FP16 on the hot tiles": one work group per compute unit
+ * takes ordered tickets, the pass-1 work first, then pass-2 work, whose waits
+ * are only on tickets that running work groups hold).  Does what apa_pass1
+ * (with its workspace) and then apa_pass2 with fuse_merge = 1 do, in one
+ * kernel launch (plus a clear of its control words): the same cold state,
+ * hot mask, lambda, output and lse, bit for bit.  A pass-2 work group starts
+ * as soon as the pass-1 units of its row blocks are done, while other work
+ * groups are still in pass 1.  Arguments as apa_pass1 and apa_pass2 (out is
+ * required); ws: apa_workspace_bytes(p, APA_CALL_FUSED) bytes (control
+ * words, the pass-1 workspace, the split states).  Covers D = 128, fp16,
+ * q_terms = 1, no value-norm weights and no ring, with the GQA groups of
+ * apa_pass2 and at most 4096 key tiles (Nkv <= 262144); other problems get
+ * APA_ERR_UNSUPPORTED.  Every wait inside the launch is bounded: one that
+ * gives up (it cannot while the GPU runs the launch's work groups) sets bit 1
+ * of the FP4 buffer's status word, and the outputs are then invalid.  Calls
+ * sharing a workspace must not overlap. */
+apa_status apa_fused(const apa_problem* p, const void* q, const void* k, const void* v,
+                     const void* fp4, float eps, int32_t* cold_m, float* cold_l, float* cold_o,
+                     uint32_t* hot_bits, float* lambda_out, void* out, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
 
 /* a10: exact merge of the cold and hot states ("The merge that makes it

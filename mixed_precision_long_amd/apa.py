@@ -17,12 +17,13 @@ APA_OK, APA_ERR_INVALID_ARG, APA_ERR_UNSUPPORTED, APA_ERR_WORKSPACE, APA_ERR_HIP
 APA_F16, APA_BF16 = 0, 1
 APA_MXFP4, APA_NVFP4 = 0, 1
 SCHED_AUTO, SCHED_WHOLE, SCHED_PAIRS, SCHED_TRIPLES = range(4)
-CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT, CALL_RING_PASS1 = range(6)
+CALL_QUANTIZE, CALL_PASS1, CALL_PASS2, CALL_MERGE, CALL_EXACT, CALL_RING_PASS1, CALL_FUSED = range(7)
 
 EXPORTS = ["apa_problem_init", "apa_fp4_layout_of", "apa_fp4_bytes", "apa_hotmask_bytes",
            "apa_workspace_bytes", "apa_status_string", "apa_last_hip_error", "apa_quantize",
            "apa_quantize_static", "apa_quantize_tiles", "apa_pass1",
-           "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact", "apa_ring_pass1"]
+           "apa_pass1_split", "apa_pass2", "apa_merge", "apa_exact", "apa_ring_pass1",
+           "apa_fused"]
 
 
 class ApaError(RuntimeError):
@@ -87,6 +88,8 @@ def lib() -> C.CDLL:
         L.apa_ring_pass1.argtypes = [P, VP, VP, VP, VP, C.c_float, VP, VP, VP, VP, VP, VP, S, VP]
         L.apa_pass2.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, C.c_int32, VP, VP, VP, VP, VP,
                                 VP, S, VP]
+        L.apa_fused.argtypes = [P, VP, VP, VP, VP, C.c_float, VP, VP, VP, VP, VP, VP, VP, VP, S,
+                                VP]
         L.apa_merge.argtypes = [P, VP, VP, VP, VP, VP, VP, VP, VP, VP, VP]
         L.apa_exact.argtypes = [P, VP, VP, VP, VP, VP, VP, S, VP]
         _lib = L
@@ -219,6 +222,17 @@ def pass2(p: Problem, q, k, v, fp4, hot_bits, cold_m, cold_l, cold_o, fuse_merge
            "apa_pass2")
 
 
+def fused(p: Problem, q, k, v, fp4, eps: float, cold_m, cold_l, cold_o, hot_bits, out, lse=None,
+          lam=None, ws=None, stream=None):
+    """Pass 1 and pass 2 (fused merge) in one persistent launch.  ws: workspace
+    of workspace_bytes(p, CALL_FUSED) bytes."""
+    _check(lib().apa_fused(C.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(fp4), float(eps),
+                           _ptr(cold_m), _ptr(cold_l), _ptr(cold_o), _ptr(hot_bits), _ptr(lam),
+                           _ptr(out), _ptr(lse), _ptr(ws),
+                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)),
+           "apa_fused")
+
+
 def merge(p: Problem, fp4, cold_m, cold_l, cold_o, hot_m, hot_l, hot_o, out, lse=None,
           stream=None):
     _check(lib().apa_merge(C.byref(p), _ptr(fp4), _ptr(cold_m), _ptr(cold_l), _ptr(cold_o),
@@ -255,9 +269,11 @@ class Buffers:
     out: object
     lse: object
     ws_ring: object = None  # KV window ring problems: the ring pass's workspace
+    ws_fused: object = None  # problems the single launch covers: its workspace
 
 
-def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
+def alloc(p: Problem, device="cuda", with_lambda: bool = False,
+          with_fused: bool = False) -> Buffers:
     import torch
     B, Hq, Nq, D = p.B, p.Hq, p.Nq, p.D
 
@@ -276,7 +292,9 @@ def alloc(p: Problem, device="cuda", with_lambda: bool = False) -> Buffers:
         lam=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device) if with_lambda else None,
         out=torch.empty((B, Hq, Nq, D), dtype=odt, device=device),
         lse=torch.empty((B, Hq, Nq), dtype=torch.float32, device=device),
-        ws_ring=u8(workspace_bytes(p, CALL_RING_PASS1)) if p.ring_tiles > 0 else None)
+        ws_ring=u8(workspace_bytes(p, CALL_RING_PASS1)) if p.ring_tiles > 0 else None,
+        ws_fused=(u8(workspace_bytes(p, CALL_FUSED))
+                  if with_fused and workspace_bytes(p, CALL_FUSED) > 0 else None))
 
 
 def apa_forward(p: Problem, q, k, v, eps: float, bufs: Buffers, stream=None):

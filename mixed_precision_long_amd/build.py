@@ -33,6 +33,7 @@ FLAGS = [
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {
     "pass1.hip": ["-mllvm", "-disable-machine-sink", *VGPR_FORM],
+    "fused.hip": ["-mllvm", "-disable-machine-sink", *VGPR_FORM],
     "fa16.hip": VGPR_FORM,
     "big16.hip": VGPR_FORM,
 }

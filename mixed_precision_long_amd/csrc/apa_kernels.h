@@ -169,6 +169,15 @@ hipError_t launch_merge(const Geom& g, const Fp4Ptrs& f, const int32_t* cold_m,
                         const float* cold_l, const float* cold_o, const float* hot_m,
                         const float* hot_l, const float* hot_o, void* out, float* lse,
                         hipStream_t s);
+// f1: pass 1 and pass 2 (fused merge) in one persistent launch.  The problems
+// it takes; the bytes of its control words (zeroed by the launch); the launch
+// (split: the pass-1 workspace or nullptr; a: pass 2's arguments with the
+// split states; ctl: the control words).
+bool fused_covers(const Geom& g);
+size_t fused_ctl_bytes(const Geom& g);
+hipError_t launch_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
+                        const Pass1Out& o, void* split, const Pass2Args& a, int32_t* ctl,
+                        hipStream_t s);
 hipError_t launch_exact(const Geom& g, const void* q, const void* k, const void* v, void* out,
                         float* lse, const Pass2Args& parts, hipStream_t s);
 

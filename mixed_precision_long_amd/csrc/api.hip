@@ -193,6 +193,23 @@ size_t pass2_ws(const apa_problem* p, Pass2Args* a, void* base) {
   return split_ws(p, o, a, base);
 }
 
+// The single launch's workspace: its control words, the pass-1 workspace,
+// then the split states.
+size_t fused_ws(const apa_problem* p, int32_t** ctl, void** split, Pass2Args* a, void* base) {
+  const Geom g = geom(p);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align256(o + bytes); return at; };
+  const size_t c = take(fused_ctl_bytes(g));
+  const size_t p1 = pass1_ws_bytes(g);
+  const size_t s1 = take(p1);
+  if (base) {
+    uint8_t* bb = (uint8_t*)base;
+    if (ctl) *ctl = (int32_t*)(bb + c);
+    if (split) *split = p1 ? (void*)(bb + s1) : nullptr;
+  }
+  return split_ws(p, o, a, base);
+}
+
 // The exact path's workspace: with bf16 inputs the per-(b, kv-head, key
 // chunk) maxima of |V|, then the split states.
 size_t exact_ws(const apa_problem* p, Pass2Args* a, void* base) {
@@ -215,6 +232,10 @@ bool kernels_cover(const apa_problem* p, int call) {
   if (p->ring_tiles > 0 && (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1)) return false;
   if (call == APA_CALL_RING_PASS1)
     return p->ring_tiles > 0 && p->D <= 256 && p->window == 0 && p->hot_weight == 0;
+  if (call == APA_CALL_FUSED) {
+    const int G = p->Hq / p->Hkv;
+    return (G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8) && fused_covers(geom(p));
+  }
   if (p->q_terms == 2 && p->D > 256 && (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1))
     return false;
   if (call == APA_CALL_QUANTIZE || call == APA_CALL_PASS1 || call == APA_CALL_MERGE) return true;
@@ -328,6 +349,8 @@ size_t apa_workspace_bytes(const apa_problem* p, int32_t which) {
       return p->ring_tiles > 0 ? align256(quant_ws(p, nullptr, nullptr)) +
                                      pass1_seg_state_bytes(geom(p))
                                : 0;
+    case APA_CALL_FUSED:
+      return kernels_cover(p, APA_CALL_FUSED) ? fused_ws(p, nullptr, nullptr, nullptr, nullptr) : 0;
     default: return 0;
   }
 }
@@ -530,6 +553,32 @@ apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const v
   pass2_ws(p, &a, ws);
   clear_hip_error();
   return hip_status(launch_pass2(geom(p), fp4_ptrs(p, fp4), a, (hipStream_t)stream));
+}
+
+apa_status apa_fused(const apa_problem* p, const void* q, const void* k, const void* v,
+                     const void* fp4, float eps, int32_t* cold_m, float* cold_l, float* cold_o,
+                     uint32_t* hot_bits, float* lambda_out, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!valid_problem(p)) return APA_ERR_INVALID_ARG;
+  if (!q || !k || !v || !fp4 || !cold_m || !cold_l || !cold_o || !hot_bits || !out)
+    return APA_ERR_INVALID_ARG;
+  if (isnan(eps) || eps < 0.0f) return APA_ERR_INVALID_ARG;
+  if (!kernels_cover(p, APA_CALL_FUSED)) return APA_ERR_UNSUPPORTED;
+  if (empty(p)) return APA_OK;
+  const size_t need = fused_ws(p, nullptr, nullptr, nullptr, nullptr);
+  if (!ws || ws_bytes < need) return APA_ERR_WORKSPACE;
+  Pass1Out o = {cold_m, cold_l, cold_o, hot_bits, lambda_out};
+  Pass2Args a = {};
+  a.q = q; a.k = k; a.v = v; a.bits = hot_bits;
+  a.cold_m = cold_m; a.cold_l = cold_l; a.cold_o = cold_o;
+  a.fuse = 1; a.out = out; a.lse = lse;
+  int32_t* ctl = nullptr;
+  void* split = nullptr;
+  fused_ws(p, &ctl, &split, &a, ws);
+  clear_hip_error();
+  return hip_status(launch_fused(geom(p), fp4_ptrs(p, fp4), eps, p->tau,
+                                 (int)p->hot_frame_offset, o, split, a, ctl,
+                                 (hipStream_t)stream));
 }
 
 apa_status apa_merge(const apa_problem* p, const void* fp4, const int32_t* cold_m,

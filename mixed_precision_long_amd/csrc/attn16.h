@@ -167,6 +167,39 @@ __device__ __forceinline__ float head_vamax(const Fp4Ptrs& f, const Pass2Args& a
   return m;
 }
 
+// Loads and stores of split and cold states.  COH: device-coherent (relaxed
+// agent-scope atomics, which bypass the per-XCD caches), for states another
+// work group of the same launch writes or reads; plain accesses otherwise.
+template <bool COH>
+__device__ __forceinline__ float ldf(const float* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool COH>
+__device__ __forceinline__ int32_t ldi(const int32_t* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return *p;
+}
+template <bool COH>
+__device__ __forceinline__ v4f ld4(const float* p) {
+  if constexpr (COH) return v4f{ldf<true>(p), ldf<true>(p + 1), ldf<true>(p + 2), ldf<true>(p + 3)};
+  return *reinterpret_cast<const v4f*>(p);
+}
+template <bool COH>
+__device__ __forceinline__ void stf(float* p, float v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH>
+__device__ __forceinline__ void st4(float* p, v4f v) {
+  if constexpr (COH) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) stf<true>(p + e, v[e]);
+  } else {
+    *reinterpret_cast<v4f*>(p) = v;
+  }
+}
+
 // The epilogue shared by both kernels: a split's partial state (S > 1 or an
 // unfused pass 2), else the output -- merged with the cold state in pass 2.
 // Lane (n, hh) holds row n's output channels ch0 + 32*db + 8*q + 4*hh + 0..3
@@ -174,7 +207,7 @@ __device__ __forceinline__ float head_vamax(const Fp4Ptrs& f, const Pass2Args& a
 // that holds part of them); l is already summed over both lane halves.  The
 // row scalars (partial m and l, LSE) are written when `scalars` is set.  o is
 // in units of 2^-vsh (bf16 V scaled into the fp16 range), scaled back here.
-template <int D, typename T, int MODE, int ND = D / 32>
+template <int D, typename T, int MODE, int ND = D / 32, bool COH = false>
 __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
                                            int S, int sp, size_t bhq, int row, int hh, float m,
                                            float l, float c_r, const v16f* o, int vsh,
@@ -189,8 +222,8 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
     float* pl = S > 1 ? a.part_l + (size_t)sp * rows : a.hot_l;
     float* po = S > 1 ? a.part_o + (size_t)sp * rows * D : a.hot_o;
     if (hh == 0 && scalars) {
-      pm[r] = l > 0.0f ? m : -__builtin_inff();
-      pl[r] = l;
+      stf<COH>(pm + r, l > 0.0f ? m : -__builtin_inff());
+      stf<COH>(pl + r, l);
     }
     float* orow = po + r * D + ch0;
 #pragma unroll
@@ -199,15 +232,15 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
       for (int q = 0; q < 4; ++q) {
         v4f x = {o[db][4 * q] * up, o[db][4 * q + 1] * up, o[db][4 * q + 2] * up,
                  o[db][4 * q + 3] * up};
-        *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
+        st4<COH>(orow + db * 32 + 8 * q + 4 * hh, x);
       }
     return;
   }
   float w1 = 0.0f, w2 = 0.0f, M = 0.0f, Lsum = 0.0f;
   const float* o1 = nullptr;
   if (MODE == kPass2) {
-    const int m1i = a.cold_m[r];
-    const float l1 = a.cold_l[r];
+    const int m1i = ldi<COH>(a.cold_m + r);
+    const float l1 = ldf<COH>(a.cold_l + r);
     const bool e1 = l1 > 0.0f && m1i != (int32_t)0x80000000, e2 = l > 0.0f;
     const float m1 = (float)m1i;
     M = -__builtin_inff();
@@ -231,7 +264,7 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
     for (int q = 0; q < 4; ++q) {
       const int ch = db * 32 + 8 * q + 4 * hh;
       v4f c1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (MODE == kPass2 && w1 != 0.0f) c1 = *reinterpret_cast<const v4f*>(o1 + ch);
+      if (MODE == kPass2 && w1 != 0.0f) c1 = ld4<COH>(o1 + ch);
       V4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = E::from((w1 * c1[e] + w2 * o[db][4 * q + e]) * inv);
