@@ -211,6 +211,8 @@ def main():
                     help="skip timing the accuracy variants (two-term Q, least-squares K scales)")
     ap.add_argument("--no-window", action="store_true",
                     help="skip timing the sliding-window variant (4096 keys)")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip timing the single persistent launch of both passes")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip timing the KV window ring (sink tile + two halves of 96 tiles)")
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -520,6 +522,47 @@ def main():
             "vs_main_output_cos_min": round(float(cos_r.min()), 6)}
         del br
         print("[bench] ring %d: %.3f ms" % (R, res["kv_window_ring"]["ms"]), file=sys.stderr,
+              flush=True)
+
+    if not args.no_fused and apa.workspace_bytes(p, apa.CALL_FUSED) > 0:
+        # both passes in one persistent launch (f1), interleaved step by step
+        # with the separate launches on the same inputs so both see the same
+        # clocks; its output must equal theirs bit for bit
+        bf = apa.alloc(p, with_fused=True)
+        evf, evs = [], []
+        for i in range(20 + 20):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            apa.quantize(p, q, k, v, bf.fp4, bf.ws_q, stream)
+            e[1].record(stream)
+            apa.fused(p, q, k, v, bf.fp4, eps, bf.cold_m, bf.cold_l, bf.cold_o, bf.bits, bf.out,
+                      lse=bf.lse, ws=bf.ws_fused, stream=stream)
+            e[2].record(stream)
+            s3 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            s3[0].record(stream)
+            step(False)
+            s3[1].record(stream)
+            if i >= 20:
+                evf.append(e)
+                evs.append(s3)
+        torch.cuda.synchronize()
+        L = apa.fp4_layout(p)
+        st_word = int(bf.fp4[L.status:L.status + 4].cpu().numpy().view(np.uint32)[0])
+        fms = float(np.mean([x[0].elapsed_time(x[2]) for x in evf]))
+        sms = float(np.mean([x[0].elapsed_time(x[1]) for x in evs]))
+        res["single_launch"] = {
+            "ms": round(fms, 4),
+            "kernels_ms": {"quantize": round(float(np.mean([x[0].elapsed_time(x[1])
+                                                             for x in evf])), 4),
+                           "pass1+pass2 (one launch)": round(float(np.mean(
+                               [x[1].elapsed_time(x[2]) for x in evf])), 4)},
+            "separate_launches_ms": round(sms, 4),
+            "tflops": round(flop / (fms * 1e-3) / 1e12, 3),
+            "output_equal_to_separate": bool(torch.equal(bf.out, bufs.out) and
+                                             torch.equal(bf.lse, bufs.lse)),
+            "wait_gave_up": bool(st_word & 2)}
+        del bf
+        print("[bench] single launch %.3f ms (separate %.3f)" % (fms, sms), file=sys.stderr,
               flush=True)
 
     if not args.no_cpu:

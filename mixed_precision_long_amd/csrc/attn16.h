@@ -200,6 +200,23 @@ __device__ __forceinline__ void st4(float* p, v4f v) {
   }
 }
 
+// 16-byte device-coherent accesses (cache policy SC1: agent scope, as the
+// relaxed atomics above) through a buffer resource over one 32-row block of
+// a [rows][D] float array (base: the block's first row; offsets in bytes).
+constexpr int kCpolSc1 = 16;
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rowblock_rsrc(const float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), (short)0, 32 * D * 4,
+                                           0x00020000);
+}
+__device__ __forceinline__ v4f coh_ld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
+}
+__device__ __forceinline__ void coh_st4(__amdgpu_buffer_rsrc_t r, uint32_t off, v4f v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), r, off, 0, kCpolSc1);
+}
+
 // The epilogue shared by both kernels: a split's partial state (S > 1 or an
 // unfused pass 2), else the output -- merged with the cold state in pass 2.
 // Lane (n, hh) holds row n's output channels ch0 + 32*db + 8*q + 4*hh + 0..3
@@ -226,13 +243,20 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
       stf<COH>(pl + r, l);
     }
     float* orow = po + r * D + ch0;
+    // COH: the row block's region (the wave's rows are one 32-row block)
+    const int n = threadIdx.x & 31;
+    const int r0w = COH ? __builtin_amdgcn_readfirstlane(row - n) : 0;
+    const auto rs = rowblock_rsrc<D>(po + (bhq * g.Nq + r0w) * D + ch0);
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v4f x = {o[db][4 * q] * up, o[db][4 * q + 1] * up, o[db][4 * q + 2] * up,
                  o[db][4 * q + 3] * up};
-        st4<COH>(orow + db * 32 + 8 * q + 4 * hh, x);
+        if constexpr (COH)
+          coh_st4(rs, (uint32_t)((n * D + db * 32 + 8 * q + 4 * hh) * 4), x);
+        else
+          *reinterpret_cast<v4f*>(orow + db * 32 + 8 * q + 4 * hh) = x;
       }
     return;
   }
@@ -264,7 +288,16 @@ __device__ __forceinline__ void finish_row(const Geom& g, const Fp4Ptrs& f, cons
     for (int q = 0; q < 4; ++q) {
       const int ch = db * 32 + 8 * q + 4 * hh;
       v4f c1 = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (MODE == kPass2 && w1 != 0.0f) c1 = ld4<COH>(o1 + ch);
+      if (MODE == kPass2 && w1 != 0.0f) {
+        if constexpr (COH) {
+          const int n = threadIdx.x & 31;
+          const int r0w = __builtin_amdgcn_readfirstlane(row - n);
+          c1 = coh_ld4(rowblock_rsrc<D>(a.cold_o + (bhq * g.Nq + r0w) * D + ch0),
+                       (uint32_t)((n * D + ch) * 4));
+        } else {
+          c1 = *reinterpret_cast<const v4f*>(o1 + ch);
+        }
+      }
       V4 y;
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[e] = E::from((w1 * c1[e] + w2 * o[db][4 * q + e]) * inv);

@@ -100,8 +100,8 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
     }
   }
   const GList<MODE> list = {base, tiles, masks};
-  fa_split<D, T, MODE, false, false>(g, Q, K, V, f, a, S, u, wg, sp, wave, fa_smem, lo, hi,
-                                     hi - lo, list);
+  fa_split<D, T, MODE, false, false>(g, Q, K, V, f, a, S, u, wg, sp, wave, wave, fa_smem, lo,
+                                     hi, hi - lo, list);
 }
 
 // Two work groups per compute unit up to D = 128 (registers <= 256 per

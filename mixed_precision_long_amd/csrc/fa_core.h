@@ -37,7 +37,9 @@ struct GList {
 
 // One split of one work group (four row blocks, one wave each) of the 16-bit
 // core: positions [lo, hi) of its tile list, staged through the double buffer
-// at smem (FaCfg<D>::BYTES of LDS); wave is the wave's index among the four.
+// at smem (FaCfg<D>::BYTES of LDS); wave is the wave's index among the four
+// (its share of the tile loads), rw the row block it computes (wave, or a
+// permutation of the four).
 // list.tile(it) and list.mask(it) give a position's key tile and the mask of
 // the verdict groups it is hot for (pass 2).  TEAM: two such splits share
 // the work group, one per four waves, and meet at every barrier: the loop
@@ -48,7 +50,8 @@ template <int D, typename T, int MODE, bool TEAM, bool COH, class List>
 __device__ __forceinline__ void fa_split(const Geom& g, const T* __restrict__ Q,
                                          const T* __restrict__ K, const T* __restrict__ V,
                                          const Fp4Ptrs& f, const Pass2Args& a, int S, int u,
-                                         int wg, int sp, int wave, uint8_t* smem, int lo, int hi,
+                                         int wg, int sp, int wave, int rw, uint8_t* smem, int lo,
+                                         int hi,
                                          int nit, const List& list) {
   using C = FaCfg<D>;
   using E = E16<T>;
@@ -62,7 +65,7 @@ __device__ __forceinline__ void fa_split(const Geom& g, const T* __restrict__ Q,
   const RowBlocks rb = row_blocks(g);
   const int hk = u % g.Hkv;
   const int b = u / g.Hkv;
-  const WaveRows wr = wave_rows(g, rb, wg, wave);
+  const WaveRows wr = wave_rows(g, rb, wg, rw);
   const int hq = hk * g.G + wr.gi;
   const size_t bhq = (size_t)b * g.Hq + hq, bhk = (size_t)b * g.Hkv + hk;
   const int r0 = wr.r0;
@@ -153,8 +156,8 @@ __device__ __forceinline__ void fa_split(const Geom& g, const T* __restrict__ Q,
     if (MODE == kExact) {
       on0 = on1 = t <= d_wave && t >= lo_wave;
     } else {
-      on0 = (mk >> (2 * wave)) & 1u;
-      on1 = (mk >> (2 * wave + 1)) & 1u;
+      on0 = (mk >> (2 * rw)) & 1u;
+      on1 = (mk >> (2 * rw + 1)) & 1u;
     }
     if (!(wr.live && (on0 || on1))) continue;
     const uint8_t* Ks = smem + sb * C::STAGE;

@@ -41,10 +41,11 @@ constexpr int kMaxLds = 160 * 1024;
 constexpr int kMaxSpin = 1 << 21;  // a few seconds of polls (a legitimate wait is < 2 ms)
 
 // The launch's control words (at the start of its workspace, cleared by
-// k_fused_init): the two ticket counters, the timeout flag, then per pass-2
-// work group the finished pass-1 units and the finished pass-2 tickets.
+// k_fused_init): per XCD a pass-1 and a pass-2 ticket counter, the timeout
+// flag, then per pass-2 work group the finished pass-1 units and the finished
+// pass-2 tickets.
 struct FusedCtl {
-  int t1, t2, timeout, pad[61];
+  int q1[8], q2[8], timeout, pad[47];
 };
 constexpr int kCtlWords = 64;
 
@@ -83,6 +84,14 @@ __device__ __forceinline__ int load_agent(const int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Tickets come from eight queues, one per XCD, holding the positions that
+// the XCD-contiguous numbering of the separate launches (xcd_remap) gives the
+// work groups dispatched to that XCD, so a work group first takes work whose
+// K/V its XCD's L2 already holds; an empty queue sends it to the next XCD's.
+// Called by all of wave 0: the position of a ticket in [0, n), or -1 once
+// every queue is empty.
+__device__ __forceinline__ int take_ticket(int* q, int n, int xcc, int lane);
+
 // Control flow around the barriers stays wave-uniform: the counters are
 // raised by every lane of wave 0 (lane 0 adds v, the others 0) and the value
 // lane 0 saw is taken with readfirstlane, so no branch on the lane index
@@ -91,6 +100,76 @@ __device__ __forceinline__ int load_agent(const int* p) {
 // other lanes re-enter the loop without it).
 __device__ __forceinline__ int wave_fetch_add(int* p, int v, int lane) {
   return __builtin_amdgcn_readfirstlane(atomic_add_agent(p, lane == 0 ? v : 0));
+}
+
+__device__ __forceinline__ int take_ticket(int* q, int n, int xcc, int lane) {
+  const int full = n & ~7, per = full >> 3;
+  for (int k = 0; k < 8; ++k) {
+    const int x = (xcc + k) & 7;
+    const int cnt = per + (x < n - full ? 1 : 0);
+    if (cnt == 0) continue;
+    const int i = wave_fetch_add(q + x, 1, lane);
+    if (i < cnt) return i < per ? x * per + i : full + x;
+  }
+  return -1;
+}
+
+// The last ticket's merge of a pass-2 work group's split states with the cold
+// state, for 16 rows of one row block (r0: its first query position) and one
+// wave: lane (h, c) takes row rlo + 2 i + h and channels 4 c .. 4 c + 3.  The
+// arithmetic of combine_row4 in the same order (the same results); the loads
+// of every split go out together, 16 bytes at a time, device-coherent.
+template <int D, typename T>
+__device__ __forceinline__ void combine_rows(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
+                                             int S, long nrows, size_t bhq, int r0, int rlo,
+                                             int lane) {
+  static_assert(D == 128, "one row per 32 lanes");
+  constexpr int kMaxS = 8;
+  const long rb0 = (long)bhq * g.Nq + r0;
+  const int c = lane & 31, h = lane >> 5;
+  const int ch = 4 * c;
+  __amdgpu_buffer_rsrc_t ro[kMaxS];
+#pragma unroll
+  for (int s = 0; s < kMaxS; ++s)
+    ro[s] = rowblock_rsrc<D>(a.part_o + ((long)min(s, S - 1) * nrows + rb0) * D);
+  const auto rc = rowblock_rsrc<D>(a.cold_o + rb0 * D);
+  for (int i = rlo + h; i < rlo + 16; i += 2) {
+    if (r0 + i >= g.Nq) break;
+    const long r = rb0 + i;
+    const uint32_t off = (uint32_t)((i * D + ch) * 4);
+    float ls[kMaxS], ms[kMaxS];
+    v4f os[kMaxS];
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < S) {
+        ls[s] = ldf<true>(a.part_l + s * nrows + r);
+        ms[s] = ldf<true>(a.part_m + s * nrows + r);
+        os[s] = coh_ld4(ro[s], off);
+      }
+    }
+    const float l1 = ldf<true>(a.cold_l + r);
+    const int m1 = ldi<true>(a.cold_m + r);
+    const v4f c1 = coh_ld4(rc, off);
+    float Mh = -__builtin_inff();
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s)
+      if (s < S && ls[s] > 0.0f) Mh = fmaxf(Mh, ms[s]);
+    float Lh = 0.0f;
+    v4f oh = {0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < kMaxS; ++s) {
+      if (s < S && ls[s] > 0.0f) {
+        const float w = fast_exp2(ms[s] - Mh);
+        Lh += w * ls[s];
+        for (int e = 0; e < 4; ++e) oh[e] += w * os[s][e];
+      }
+    }
+    const bool want_lse = a.lse && ch == 0;
+    const long bh = r / g.Nq, rr = r % g.Nq;
+    const float c0 = want_lse ? f.q_frame[bh * g.NqP + rr] : 0.0f;
+    merge4<T>(m1, l1, l1 > 0.0f ? c1 : v4f{0, 0, 0, 0}, Lh > 0.0f ? Mh : -__builtin_inff(), Lh,
+              oh, c0, reinterpret_cast<T*>(a.out) + r * D + ch, want_lse ? a.lse + r : nullptr);
+  }
 }
 
 template <int D, typename T, bool LOG, int QT, bool VW>
@@ -113,16 +192,19 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
                    : (sched == kSchedPairs ? kFusedWaves / 2 : kFusedWaves);
   const int nq32 = g.NqP / 32;
   const long nrows = (long)g.B * g.Hq * g.Nq;
+  // this work group's XCD (the hardware register; it only steers which
+  // queue is tried first)
+  const int xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)) & 7;
   // pass-1 tickets, until none is left
   for (;;) {
-    if (wave == 0) bc[0] = wave_fetch_add(&C->t1, 1, lane);
+    if (wave == 0) bc[0] = take_ticket(C->q1, n1, xcc, lane);
     __syncthreads();
     const int t = __builtin_amdgcn_readfirstlane(bc[0]);
     __syncthreads();
-    if (t >= n1) break;
+    if (t < 0) break;
     {
-      // ---- pass 1: the work group of the separate launch numbered t
-      const int blk = n1 - 1 - xcd_remap(t, n1);
+      // ---- pass 1: the work group of the separate launch at position t
+      const int blk = n1 - 1 - t;
       P1Lds<D, LOG>& L = *reinterpret_cast<P1Lds<D, LOG>*>(fsm);
       pass1_block<D, LOG, QT, VW>(g, f, eps, tau, hoff, out, split, cap, sched, nunits, blk, L);
       __builtin_amdgcn_s_setprio(0);
@@ -151,12 +233,11 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
 
   // pass-2 tickets: splits 2 pr and 2 pr + 1 of one work group
   for (;;) {
-    if (wave == 0) bc[0] = wave_fetch_add(&C->t2, 1, lane);
+    if (wave == 0) bc[0] = take_ticket(C->q2, n2, xcc, lane);
     __syncthreads();
-    const int t = __builtin_amdgcn_readfirstlane(bc[0]);
+    const int x = __builtin_amdgcn_readfirstlane(bc[0]);
     __syncthreads();
-    if (t >= n2) break;
-    const int x = xcd_remap(t, n2);
+    if (x < 0) break;
     const int per2 = rb.nwg * npairs;
     const int u = x / per2;  // (batch, kv-head)
     const int jx = x % per2;
@@ -236,8 +317,10 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
     const int nit = max(mid - lo0, hi1 - mid);
     const int lo = team ? mid : lo0, hi = team ? hi1 : mid;
     const LList list = {lst};
+    // the second half computes the row blocks two SIMDs over, so that each
+    // SIMD carries two different row blocks' hot tiles
     fa_split<D, T, kPass2, true, true>(g, (const T*)a.q, (const T*)a.k, (const T*)a.v, f, a, S,
-                                       u, wg, sp, wave & 3,
+                                       u, wg, sp, wave & 3, (wave & 3) ^ (team << 1),
                                        fsm + (size_t)team * FaCfg<D>::BYTES, lo, hi, nit, list);
     if (S == 1) continue;  // the split merged itself with the cold state
     // split states complete before the count; the last ticket merges them
@@ -246,16 +329,13 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
     if (wave == 0) bc[2] = wave_fetch_add(done + item, 1, lane) == npairs - 1;
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(bc[2])) continue;
-    const int nq4 = D / 4;
-    for (int idx = tid; idx < kWgWaves * 32 * nq4; idx += kFusedWaves * 64) {
-      const int w = idx / (32 * nq4);
-      const int n = (idx / nq4) % 32;
-      const int ch = (idx % nq4) * 4;
-      const WaveRows wr = wave_rows(g, rb, wg, w);
-      const int row = wr.r0 + n;
-      if (!wr.live || row >= g.Nq) continue;
-      const long r = ((long)(u / g.Hkv) * g.Hq + (u % g.Hkv) * g.G + wr.gi) * g.Nq + row;
-      combine_row4<D, T, kPass2, true>(g, f, a, S, nrows, r, ch);
+    // wave w merges rows 16 (w % 2) .. + 15 of row block w / 2
+    {
+      const WaveRows wr = wave_rows(g, rb, wg, wave >> 1);
+      if (wr.live) {
+        const size_t bhq = (size_t)(u / g.Hkv) * g.Hq + (u % g.Hkv) * g.G + wr.gi;
+        combine_rows<D, T>(g, f, a, S, nrows, bhq, wr.r0, 16 * (wave & 1), lane);
+      }
     }
   }
 }
