@@ -323,7 +323,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "k_pass1",
                      "achieved": round(p1_tflops, 3), "peak": PEAK_FP4_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(p1_tflops / PEAK_FP4_TFLOPS, 5),
-                     "traffic": traffic_for(["pass1.hip", "apa_device.h", "apa_kernels.h"], "k_pass1"),
+                     "traffic": traffic_for(["pass1.hip", "pass1_core.h", "apa_device.h", "apa_kernels.h"], "k_pass1"),
                      "algorithmic_fp4_flop_per_launch": w4},
         "weighted_roofline": {"t_roof_ms": round(t_roof_ms, 4),
                               "frac": round(t_roof_ms / ms, 4),
