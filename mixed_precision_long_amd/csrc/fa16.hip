@@ -100,7 +100,7 @@ __device__ __forceinline__ void fa_body(const Geom& g, const T* __restrict__ Q,
     }
   }
   const GList<MODE> list = {base, tiles, masks};
-  fa_split<D, T, MODE, false, false>(g, Q, K, V, f, a, S, u, wg, sp, wave, wave, fa_smem, lo,
+  fa_split<D, T, MODE, false, false, 0>(g, Q, K, V, f, a, S, u, wg, sp, wave, wave, fa_smem, lo,
                                      hi, hi - lo, list);
 }
 

@@ -46,7 +46,10 @@ struct GList {
 // runs nit >= hi - lo iterations, the extra ones only at the barrier.  COH:
 // split states and the cold state go through device-coherent accesses
 // (another work group of the same launch wrote or reads them).
-template <int D, typename T, int MODE, bool TEAM, bool COH, class List>
+// TAG only tells call sites apart: each kernel that calls the core directly
+// names its own specialization (the host pass of hipcc rejects a second
+// kernel specialization that calls the same one).
+template <int D, typename T, int MODE, bool TEAM, bool COH, int TAG, class List>
 __device__ __forceinline__ void fa_split(const Geom& g, const T* __restrict__ Q,
                                          const T* __restrict__ K, const T* __restrict__ V,
                                          const Fp4Ptrs& f, const Pass2Args& a, int S, int u,

@@ -319,7 +319,7 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
     const LList list = {lst};
     // the second half computes the row blocks two SIMDs over, so that each
     // SIMD carries two different row blocks' hot tiles
-    fa_split<D, T, kPass2, true, true>(g, (const T*)a.q, (const T*)a.k, (const T*)a.v, f, a, S,
+    fa_split<D, T, kPass2, true, true, 2 * QT + VW>(g, (const T*)a.q, (const T*)a.k, (const T*)a.v, f, a, S,
                                        u, wg, sp, wave & 3, (wave & 3) ^ (team << 1),
                                        fsm + (size_t)team * FaCfg<D>::BYTES, lo, hi, nit, list);
     if (S == 1) continue;  // the split merged itself with the cold state
@@ -340,7 +340,7 @@ void k_fused(Geom g, Fp4Ptrs f, float eps, float tau, int hoff, Pass1Out out, ui
   }
 }
 
-template <int D, typename T, int QT>
+template <int D, typename T, int QT, bool VW>
 hipError_t run_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int hoff,
                      const Pass1Out& o, void* split, const Pass2Args& a, int32_t* ctl,
                      hipStream_t s) {
@@ -357,7 +357,7 @@ hipError_t run_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int 
   hipLaunchKernelGGL(k_fused_init, dim3((nctl + 255) / 256), dim3(256), 0, s, ctl, nctl);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  auto kern = k_fused<D, T, true, QT, false>;
+  auto kern = k_fused<D, T, true, QT, VW>;
   constexpr size_t bytes = fused_lds<D, true>();
   static bool attr_done = false;
   if (!attr_done) {
@@ -380,7 +380,7 @@ hipError_t run_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int 
 }  // namespace
 
 bool fused_covers(const Geom& g) {
-  if (g.D != 128 || g.bf16 || g.qterms != 1 || g.vweight || g.ring) return false;
+  if (g.D != 128 || g.ring) return false;
   if (g.NT > kLogTiles) return false;
   return g.NT <= list_cap<128>();
 }
@@ -394,7 +394,21 @@ hipError_t launch_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, i
                         const Pass1Out& o, void* split, const Pass2Args& a, int32_t* ctl,
                         hipStream_t s) {
   if (!fused_covers(g)) return hipErrorInvalidValue;
-  return run_fused<128, _Float16, 1>(g, f, eps, tau, hoff, o, split, a, ctl, s);
+  // (input type, Q terms, value-norm weights) as the separate launches take them
+  auto go = [&](auto t, auto qt, auto vw) {
+    return run_fused<128, decltype(t), decltype(qt)::value, decltype(vw)::value>(
+        g, f, eps, tau, hoff, o, split, a, ctl, s);
+  };
+  using Q1 = std::integral_constant<int, 1>;
+  using Q2 = std::integral_constant<int, 2>;
+  using T = std::true_type;
+  using F = std::false_type;
+  if (g.bf16) {
+    if (g.qterms == 2) return g.vweight ? go(__bf16{}, Q2{}, T{}) : go(__bf16{}, Q2{}, F{});
+    return g.vweight ? go(__bf16{}, Q1{}, T{}) : go(__bf16{}, Q1{}, F{});
+  }
+  if (g.qterms == 2) return g.vweight ? go(_Float16{}, Q2{}, T{}) : go(_Float16{}, Q2{}, F{});
+  return g.vweight ? go(_Float16{}, Q1{}, T{}) : go(_Float16{}, Q1{}, F{});
 }
 
 }  // namespace apa

@@ -8,8 +8,9 @@ output and LSE, bit for bit, with bit 1 of the status word (a wait that gave
 up) clear.  The shapes cover the three pass-1 schedules, tails that give up
 and are walked again inside the launch, one key split (the split merges
 itself), an odd number of splits (the last ticket of a work group runs one
-split), GQA groups 1 and 3, batches, no causal mask, a sliding window, two
-calls in a row on one workspace, and the headline shape.  Checked against the
+split), GQA groups 1 and 3, batches, no causal mask, a sliding window, bf16
+inputs, two Q terms, the value-norm weighted test, two calls in a row on one
+workspace, and the headline shape.  Checked against the
 oracle once."""
 import numpy as np
 import pytest
@@ -17,7 +18,8 @@ import torch
 
 from gpu_util import pass1_schedule, problem_for, torch_inputs, unpack_bits
 from mixed_precision_long_amd import apa
-from mixed_precision_long_amd.inputs import WORKLOADS, make_inputs, small_workload
+from mixed_precision_long_amd.inputs import (WORKLOADS, make_inputs, outlier_value_tiles,
+                                             small_workload)
 from oracle import oracle as O
 from test_gpu_parity import check_mask, check_output
 from test_gpu_split import lift_key
@@ -89,6 +91,24 @@ def test_fused_equals_separate_launches(case):
     print("[fused] case", case, "schedule", pass1_schedule(p), flush=True)
     q, k, v = torch_inputs(Q, K, V, "fp16")
     ref, runs = run_pair(p, q, k, v, eps)
+    assert_same(ref, runs[0])
+
+
+@pytest.mark.parametrize("case", ["bf16", "two_term_q", "hot_weight", "bf16_two_term_weight"])
+def test_fused_variants(case):
+    """bf16 inputs (pass 2 converts V to fp16 in LDS), two Q terms in pass 1,
+    the value-norm weighted hot test, and all three together."""
+    bf = "bf16" in case
+    qt = 2 if "two_term" in case else 1
+    hw = 1 if "weight" in case else 0
+    w = small_workload(1, 6, 2, 200, 9000, 128, dtype="bf16" if bf else "fp16",
+                       mode="gauss" if bf else "path", seed=98)
+    Q, K, V = make_inputs(w)
+    if hw:
+        outlier_value_tiles(V, 4, 8.0, seed=98)
+    p = problem_for(w, q_terms=qt, hot_weight=hw)
+    q, k, v = torch_inputs(Q, K, V, "bf16" if bf else "fp16")
+    ref, runs = run_pair(p, q, k, v, 0.01)
     assert_same(ref, runs[0])
 
 
