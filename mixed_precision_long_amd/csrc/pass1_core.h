@@ -492,8 +492,9 @@ __host__ __device__ inline size_t cand_bytes(int cap) {
 }
 
 // After the records: room for the head's final state, which a tail that gave
-// up leaves there for the re-walk kernel (o in lane order, then the per-lane
-// scalars mf, mo, lambda, l, then the head's partial words).
+// up leaves there for the re-walk (k_pass1_rewalk, or the single launch's
+// re-walk step): o in lane order, then the per-lane scalars mf, mo, lambda,
+// l, then the head's partial words.
 __host__ __device__ inline size_t handoff_bytes(int D) {
   return ((size_t)128 * D + 1024 + 16 + 255) & ~(size_t)255;
 }
@@ -1026,7 +1027,7 @@ __device__ __forceinline__ void settle(const Geom& g, const Ctx<D, QT>& c, St<D>
 // mf, mo (its bits), lambda and l per lane, then the four partial hot words
 // (word k from lane k).  The tail of the triple schedule parks its state
 // there while it walks the next unit's tail; a tail that gave up leaves its
-// head's state there for the re-walk kernel.  Each lane reads back only
+// head's state there for the re-walk.  Each lane reads back only
 // what it wrote.
 template <int D>
 __device__ __forceinline__ float* handoff_of(uint8_t* split, int unit, int cap) {
@@ -1237,7 +1238,7 @@ __device__ __forceinline__ void pass1_block(const Geom& g, const Fp4Ptrs& f, flo
     const Cand cr = cand_of(split, u, cap, D);
     if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)oc, cr.r, 0u, 0u, 0);
     if (oc < 0) {
-      // gave up: leave the head's state for the re-walk kernel
+      // gave up: leave the head's state for the re-walk
 #pragma unroll 2
       for (int q = 0; q < ND * 4; ++q) reinterpret_cast<v4f*>(ho)[q * 64 + lane] = H.o[q][lane];
 #pragma unroll
