@@ -9,8 +9,8 @@ up) clear.  The shapes cover the three pass-1 schedules, tails that give up
 and are walked again inside the launch, one key split (the split merges
 itself), an odd number of splits (the last ticket of a work group runs one
 split), GQA groups 1 and 3, batches, no causal mask, a sliding window, bf16
-inputs, two Q terms, the value-norm weighted test, two calls in a row on one
-workspace, and the headline shape.  Checked against the
+inputs, two Q terms, the value-norm weighted test, paged K/V, two calls in a
+row on one workspace, and the headline shape.  Checked against the
 oracle once."""
 import numpy as np
 import pytest
@@ -110,6 +110,25 @@ def test_fused_variants(case):
     q, k, v = torch_inputs(Q, K, V, "bf16" if bf else "fp16")
     ref, runs = run_pair(p, q, k, v, 0.01)
     assert_same(ref, runs[0])
+
+
+def test_fused_over_paged_kv():
+    """16-bit K/V through a block table (unused page slots NaN): the same
+    results as the separate launches over the same pages, clean status."""
+    from test_gpu_chunked import _pages
+    B, Hq, Hkv, Nq, Nkv, D = 2, 6, 2, 160, 7000, 128
+    w = small_workload(B, Hq, Hkv, Nq, Nkv, D, seed=99)
+    Q, K, V = make_inputs(w)
+    NT = -(-Nkv // 64)
+    npages = B * NT + 3
+    perm = np.random.default_rng(5).permutation(npages)[:B * NT].reshape(B, NT).astype(np.int32)
+    bt = torch.from_numpy(np.ascontiguousarray(perm)).cuda()
+    kp, vp = (_pages(x, B, Hkv, Nkv, D, perm, npages, torch.float16) for x in (K, V))
+    q = torch.from_numpy(Q).half().cuda()
+    p = problem_for(w, block_table=bt)
+    ref, runs = run_pair(p, q, kp, vp, 0.01)
+    assert_same(ref, runs[0])
+    assert runs[0]["status"] == 0
 
 
 @pytest.mark.parametrize("sched", [apa.SCHED_PAIRS, apa.SCHED_TRIPLES])
