@@ -355,8 +355,9 @@ apa_status apa_pass2(const apa_problem* p, const void* q, const void* k, const v
  * as soon as the pass-1 units of its row blocks are done, while other work
  * groups are still in pass 1.  Arguments as apa_pass1 and apa_pass2 (out is
  * required); ws: apa_workspace_bytes(p, APA_CALL_FUSED) bytes (control
- * words, the pass-1 workspace, the split states).  Covers D = 128 (fp16 or
- * bf16, one or two Q terms, with or without value-norm weights; no ring),
+ * words, the pass-1 workspace, the split states).  Covers D = 64 and 128
+ * (fp16 or bf16, one or two Q terms, with or without value-norm weights; no
+ * ring),
  * the GQA groups of apa_pass2 and at most 4096 key tiles (Nkv <= 262144);
  * other problems get APA_ERR_UNSUPPORTED.  Every wait inside the launch is bounded: one that
  * gives up (it cannot while the GPU runs the launch's work groups) sets bit 1

@@ -116,24 +116,27 @@ __device__ __forceinline__ int take_ticket(int* q, int n, int xcc, int lane) {
 
 // The last ticket's merge of a pass-2 work group's split states with the cold
 // state, for 16 rows of one row block (r0: its first query position) and one
-// wave: lane (h, c) takes row rlo + 2 i + h and channels 4 c .. 4 c + 3.  The
+// wave: lane (h, c) takes row rlo + R i + h (R = 64 / (D / 4) rows at a time)
+// and channels 4 c .. 4 c + 3.  The
 // arithmetic of combine_row4 in the same order (the same results); the loads
 // of every split go out together, 16 bytes at a time, device-coherent.
 template <int D, typename T>
 __device__ __forceinline__ void combine_rows(const Geom& g, const Fp4Ptrs& f, const Pass2Args& a,
                                              int S, long nrows, size_t bhq, int r0, int rlo,
                                              int lane) {
-  static_assert(D == 128, "one row per 32 lanes");
+  static_assert(D == 64 || D == 128, "whole rows per wave");
+  constexpr int NQ = D / 4;       // lanes per row
+  constexpr int RPI = 64 / NQ;    // rows per pass of the wave
   constexpr int kMaxS = 8;
   const long rb0 = (long)bhq * g.Nq + r0;
-  const int c = lane & 31, h = lane >> 5;
+  const int c = lane % NQ, h = lane / NQ;
   const int ch = 4 * c;
   __amdgpu_buffer_rsrc_t ro[kMaxS];
 #pragma unroll
   for (int s = 0; s < kMaxS; ++s)
     ro[s] = rowblock_rsrc<D>(a.part_o + ((long)min(s, S - 1) * nrows + rb0) * D);
   const auto rc = rowblock_rsrc<D>(a.cold_o + rb0 * D);
-  for (int i = rlo + h; i < rlo + 16; i += 2) {
+  for (int i = rlo + h; i < rlo + 16; i += RPI) {
     if (r0 + i >= g.Nq) break;
     const long r = rb0 + i;
     const uint32_t off = (uint32_t)((i * D + ch) * 4);
@@ -380,9 +383,9 @@ hipError_t run_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, int 
 }  // namespace
 
 bool fused_covers(const Geom& g) {
-  if (g.D != 128 || g.ring) return false;
+  if ((g.D != 64 && g.D != 128) || g.ring) return false;
   if (g.NT > kLogTiles) return false;
-  return g.NT <= list_cap<128>();
+  return g.NT <= (g.D == 64 ? list_cap<64>() : list_cap<128>());
 }
 
 size_t fused_ctl_bytes(const Geom& g) {
@@ -394,21 +397,26 @@ hipError_t launch_fused(const Geom& g, const Fp4Ptrs& f, float eps, float tau, i
                         const Pass1Out& o, void* split, const Pass2Args& a, int32_t* ctl,
                         hipStream_t s) {
   if (!fused_covers(g)) return hipErrorInvalidValue;
-  // (input type, Q terms, value-norm weights) as the separate launches take them
-  auto go = [&](auto t, auto qt, auto vw) {
-    return run_fused<128, decltype(t), decltype(qt)::value, decltype(vw)::value>(
+  // (head size, input type, Q terms, value-norm weights) as the separate
+  // launches take them
+  auto go = [&](auto d, auto t, auto qt, auto vw) {
+    return run_fused<decltype(d)::value, decltype(t), decltype(qt)::value, decltype(vw)::value>(
         g, f, eps, tau, hoff, o, split, a, ctl, s);
+  };
+  auto by_d = [&](auto t, auto qt, auto vw) {
+    if (g.D == 64) return go(std::integral_constant<int, 64>{}, t, qt, vw);
+    return go(std::integral_constant<int, 128>{}, t, qt, vw);
   };
   using Q1 = std::integral_constant<int, 1>;
   using Q2 = std::integral_constant<int, 2>;
   using T = std::true_type;
   using F = std::false_type;
   if (g.bf16) {
-    if (g.qterms == 2) return g.vweight ? go(__bf16{}, Q2{}, T{}) : go(__bf16{}, Q2{}, F{});
-    return g.vweight ? go(__bf16{}, Q1{}, T{}) : go(__bf16{}, Q1{}, F{});
+    if (g.qterms == 2) return g.vweight ? by_d(__bf16{}, Q2{}, T{}) : by_d(__bf16{}, Q2{}, F{});
+    return g.vweight ? by_d(__bf16{}, Q1{}, T{}) : by_d(__bf16{}, Q1{}, F{});
   }
-  if (g.qterms == 2) return g.vweight ? go(_Float16{}, Q2{}, T{}) : go(_Float16{}, Q2{}, F{});
-  return g.vweight ? go(_Float16{}, Q1{}, T{}) : go(_Float16{}, Q1{}, F{});
+  if (g.qterms == 2) return g.vweight ? by_d(_Float16{}, Q2{}, T{}) : by_d(_Float16{}, Q2{}, F{});
+  return g.vweight ? by_d(_Float16{}, Q1{}, T{}) : by_d(_Float16{}, Q1{}, F{});
 }
 
 }  // namespace apa

@@ -112,6 +112,18 @@ def test_fused_variants(case):
     assert_same(ref, runs[0])
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_fused_d64(dtype):
+    """D = 64 (the merge takes four rows per wave pass): GQA 4, ragged."""
+    w = small_workload(1, 8, 2, 96, 12000, 64, dtype=dtype, mode="gauss" if dtype == "bf16" else "path",
+                       seed=100)
+    Q, K, V = make_inputs(w)
+    p = problem_for(w)
+    q, k, v = torch_inputs(Q, K, V, dtype)
+    ref, runs = run_pair(p, q, k, v, 0.005)
+    assert_same(ref, runs[0])
+
+
 def test_fused_over_paged_kv():
     """16-bit K/V through a block table (unused page slots NaN): the same
     results as the separate launches over the same pages, clean status."""
@@ -164,7 +176,7 @@ def test_fused_twice_on_one_workspace_and_oracle():
 
 
 def test_fused_uncovered_problems_are_refused():
-    w = small_workload(1, 4, 2, 64, 2000, 64, seed=97)
+    w = small_workload(1, 4, 2, 64, 2000, 256, seed=97)
     p = problem_for(w)
     assert apa.workspace_bytes(p, apa.CALL_FUSED) == 0
     b = apa.alloc(p, with_lambda=True)
