@@ -296,3 +296,32 @@ def test_ring_problems():
     assert ring(r, need - 1) == apa.APA_ERR_WORKSPACE
     assert L.apa_ring_pass1(C.byref(r), FAKE, FAKE, FAKE, FAKE, float("nan"), FAKE, FAKE, FAKE,
                             FAKE, None, FAKE, need, None) == apa.APA_ERR_INVALID_ARG
+
+
+def test_fused_problems():
+    """The single launch: covered problems (D 64 or 128, at most 4096 key
+    tiles, no ring, the GQA groups of pass 2) have a workspace of control
+    words, the pass-1 workspace and the split states; others report 0 bytes
+    and get APA_ERR_UNSUPPORTED before any device work; NULL required
+    pointers, a NaN eps and a short workspace are refused."""
+    L = apa.lib()
+    p = prob()  # 2048 x 122880, 24 over 8 heads, D = 128: 1920 tiles
+    need = apa.workspace_bytes(p, apa.CALL_FUSED)
+    nitems = 8 * ((3 * 64 + 3) // 4)
+    ctl = ((64 + 2 * nitems) * 4 + 255) // 256 * 256
+    S = 4
+    rows = 24 * 2048
+    split_states = sum((x + 255) // 256 * 256 for x in (S * rows * 4, S * rows * 4, S * rows * 128 * 4))
+    assert need == ctl + apa.workspace_bytes(p, apa.CALL_PASS1) + split_states
+    fused = lambda x, ws, nbytes, eps=0.01, out=FAKE: L.apa_fused(
+        C.byref(x), FAKE, FAKE, FAKE, FAKE, eps, FAKE, FAKE, FAKE, FAKE, None, out, None, ws,
+        nbytes, None)
+    for kw in ({"D": 256}, {"D": 512}, {"ring_tiles": 96}, {"Nkv": 4097 * 64}, {"Hq": 40}):
+        x = prob(**kw)
+        assert apa.workspace_bytes(x, apa.CALL_FUSED) == 0, kw
+        assert fused(x, FAKE, 1 << 40) == apa.APA_ERR_UNSUPPORTED, kw
+    assert apa.workspace_bytes(prob(D=64), apa.CALL_FUSED) > 0
+    assert fused(p, FAKE, need - 1) == apa.APA_ERR_WORKSPACE
+    assert fused(p, None, 1 << 40) == apa.APA_ERR_WORKSPACE
+    assert fused(p, FAKE, 1 << 40, out=None) == apa.APA_ERR_INVALID_ARG
+    assert fused(p, FAKE, 1 << 40, eps=float("nan")) == apa.APA_ERR_INVALID_ARG
